@@ -1,0 +1,89 @@
+"""An independent formulation of the drafter forward, built from torch library routines.
+
+Used only to pin the oracle. It keeps no ring at all: it holds the whole committed
+history of residual rows, recomputes every context K/V from it, and attends with an
+explicit boolean [queries, keys] mask over absolute positions, through
+torch.nn.functional.scaled_dot_product_attention (GQA via enable_gqa). RoPE is written
+as a complex rotation of the (i, i + hd/2) pairs. Everything runs in float64 on the CPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+
+def _t(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.float64))
+
+
+class TorchDrafter:
+    def __init__(self, shape, weights):
+        self.sh = shape
+        self.w = {k: _t(v) for k, v in weights.items() if not hasattr(v, "packed")}
+        self.bf16 = shape.act_dtype == "bf16"
+
+    def _c(self, x):
+        if not self.bf16:
+            return x
+        return x.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+    def _rms(self, x, name):
+        return F.rms_norm(x, (x.shape[-1],), weight=self.w[name], eps=self.sh.rms_eps)
+
+    def _rope(self, x, pos):
+        # x: [..., seq, heads, hd]; rotate pair (i, i+hd/2) by pos * theta^(-2i/hd)
+        hd = x.shape[-1]
+        half = hd // 2
+        freqs = torch.pow(torch.tensor(self.sh.rope_theta, dtype=torch.float64),
+                          -torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+        ang = torch.outer(torch.as_tensor(pos, dtype=torch.float64), freqs)  # [seq, half]
+        rot = torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        z = torch.complex(x[..., :half], x[..., half:]) * rot
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    def context_kv(self, history):
+        """K/V of every committed row, positions 0..n-1, per layer."""
+        sh = self.sh
+        r = self._c(_t(history))
+        c = self._c(self._rms(F.linear(r, self.w["fc"]), "enc_norm"))
+        pos = np.arange(r.shape[0])
+        out = []
+        for l in range(sh.layers):
+            p = f"layers.{l}."
+            k = F.linear(c, self.w[p + "k"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
+            v = F.linear(c, self.w[p + "v"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
+            k = self._rope(self._rms(k, p + "k_norm"), pos)
+            out.append((self._c(k), self._c(v)))
+        return out
+
+    def forward(self, history, anchor, block):
+        """Hidden rows [B+1, H] and logits [B, V] of the block drafted after `history`."""
+        sh = self.sh
+        e = len(history)
+        ctx = self.context_kv(history)
+        qpos = np.arange(e, e + block + 1)
+        kpos = np.arange(0, e + block + 1)
+        mask = torch.as_tensor(np.abs(qpos[:, None] - kpos[None, :]) <= sh.window)
+        ids = torch.tensor([anchor] + [sh.mask_id] * block)
+        x = F.embedding(ids, self.w["embed"])
+        for l in range(sh.layers):
+            p = f"layers.{l}."
+            h = self._c(self._rms(x, p + "in_norm"))
+            q = F.linear(h, self.w[p + "q"]).unflatten(-1, (sh.q_heads, sh.head_dim))
+            k = F.linear(h, self.w[p + "k"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
+            v = F.linear(h, self.w[p + "v"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
+            q = self._c(self._rope(self._rms(q, p + "q_norm"), qpos))
+            k = self._c(self._rope(self._rms(k, p + "k_norm"), qpos))
+            v = self._c(v)
+            kall = torch.cat([ctx[l][0], k], dim=0).transpose(0, 1)[None]  # [1, nkv, Nk, hd]
+            vall = torch.cat([ctx[l][1], v], dim=0).transpose(0, 1)[None]
+            o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], kall, vall,
+                                               attn_mask=mask, enable_gqa=True)
+            o = self._c(o[0].transpose(0, 1).flatten(-2))
+            x = x + F.linear(o, self.w[p + "o"])
+            h2 = self._c(self._rms(x, p + "post_norm"))
+            a = self._c(F.silu(F.linear(h2, self.w[p + "gate"])) * F.linear(h2, self.w[p + "up"]))
+            x = x + F.linear(a, self.w[p + "down"])
+        z = self._c(self._rms(x[1:], "final_norm"))
+        return x.numpy(), F.linear(z, self.w["lm_head"]).numpy()
