@@ -1,0 +1,256 @@
+"""Thin Python binding of libdflash.so (include/dflash.h): argument marshalling only.
+
+Every step of the round runs in the library's HIP kernels; PyTorch only provides device
+memory (weights, ring, workspace, inputs and outputs) and the stream. If the library is
+not built this module raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash.so")
+
+DFLASH_F32, DFLASH_BF16, DFLASH_Q4G64 = 0, 1, 2
+_DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
+
+EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
+           "dflash_draft_block", "dflash_lm_head_argmax", "dflash_verify_greedy", "dflash_cache_state",
+           "dflash_cache_read", "dflash_last_error", "dflash_status_string")
+
+
+class dflash_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden", "layers", "q_heads", "kv_heads", "head_dim", "intermediate", "vocab",
+        "target_streams", "target_width", "window", "max_block", "mask_token_id", "ring_phase")] + [
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("weight_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+
+
+class dflash_linear(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class dflash_layer(ctypes.Structure):
+    _fields_ = [(n, dflash_linear) for n in ("q", "k", "v", "o", "gate", "up", "down")] + [
+        (n, ctypes.c_void_p) for n in ("in_norm", "post_norm", "q_norm", "k_norm")]
+
+
+class dflash_weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", dflash_linear), ("fc", dflash_linear),
+                ("enc_norm", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(dflash_layer))]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "dflash_query_sizes": (i32, [P(dflash_config), P(sz), P(sz)]),
+        "dflash_create": (i32, [P(dflash_config), P(dflash_weights), vp, sz, vp, sz, vp, P(vp)]),
+        "dflash_destroy": (None, [vp]),
+        "dflash_cache_append": (i32, [vp, vp, i32, i32, vp]),
+        "dflash_cache_trim": (i32, [vp, i32]),
+        "dflash_draft_block": (i32, [vp, i32, i32, vp, vp, vp]),
+        "dflash_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
+        "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
+        "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
+        "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
+        "dflash_last_error": (ctypes.c_char_p, [vp]),
+        "dflash_status_string": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+def _check(status: int, ctx) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.dflash_last_error(ctx).decode() or L.dflash_status_string(status).decode()
+        raise DFlashError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_config(shape, max_block: int, phase: int = 0) -> dflash_config:
+    return dflash_config(
+        hidden=shape.hidden, layers=shape.layers, q_heads=shape.q_heads, kv_heads=shape.kv_heads,
+        head_dim=shape.head_dim, intermediate=shape.intermediate, vocab=shape.vocab,
+        target_streams=shape.target_streams, target_width=shape.target_width, window=shape.window,
+        max_block=max_block, mask_token_id=shape.mask_id, ring_phase=phase, rms_eps=shape.rms_eps,
+        rope_theta=shape.rope_theta, weight_dtype=_DTYPE[shape.weight_dtype], act_dtype=_DTYPE[shape.act_dtype])
+
+
+def act_torch_dtype(shape) -> torch.dtype:
+    return torch.float32 if shape.act_dtype == "f32" else torch.bfloat16
+
+
+def to_device(shape, weights: Dict[str, object], device="cuda") -> Dict[str, object]:
+    """Storage-form numpy weights -> device tensors (bf16-exact values become bfloat16)."""
+    dt = act_torch_dtype(shape)
+    out: Dict[str, object] = {}
+    for name, w in weights.items():
+        if hasattr(w, "packed"):
+            out[name] = (torch.from_numpy(w.packed.view(np.int32)).to(device),
+                         torch.from_numpy(w.scales).to(torch.bfloat16).to(device),
+                         torch.from_numpy(w.biases).to(torch.bfloat16).to(device))
+        else:
+            out[name] = torch.from_numpy(np.ascontiguousarray(w)).to(dt).to(device)
+    return out
+
+
+def query_sizes(cfg: dflash_config) -> Tuple[int, int]:
+    rb, wb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().dflash_query_sizes(ctypes.byref(cfg), ctypes.byref(rb), ctypes.byref(wb)), None)
+    return rb.value, wb.value
+
+
+class Drafter:
+    """One dflash_ctx: the drafter bound to device weights, its ring and its workspace."""
+
+    def __init__(self, shape, dev_weights: Dict[str, object], max_block: int, phase: int = 0,
+                 device="cuda", stream=None):
+        L = lib()
+        self.shape = shape
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.cfg = make_config(shape, max_block, phase)
+        self._w = dev_weights  # keeps every weight alive while the context is
+
+        def lin(name):
+            t = dev_weights[name]
+            if isinstance(t, tuple):
+                return dflash_linear(_ptr(t[0]), _ptr(t[1]), _ptr(t[2]))
+            return dflash_linear(_ptr(t), None, None)
+
+        layers = (dflash_layer * shape.layers)()
+        for l in range(shape.layers):
+            p = f"layers.{l}."
+            layers[l] = dflash_layer(*[lin(p + n) for n in ("q", "k", "v", "o", "gate", "up", "down")],
+                                     *[_ptr(dev_weights[p + n]) for n in ("in_norm", "post_norm", "q_norm", "k_norm")])
+        self._layers = layers
+        self.weights = dflash_weights(_ptr(dev_weights["embed"]), lin("lm_head"), lin("fc"),
+                                      _ptr(dev_weights["enc_norm"]), _ptr(dev_weights["final_norm"]),
+                                      ctypes.cast(layers, ctypes.POINTER(dflash_layer)))
+        ring_b, ws_b = query_sizes(self.cfg)
+        self.ring = torch.empty(max(ring_b, 256), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(L.dflash_create(ctypes.byref(self.cfg), ctypes.byref(self.weights), _ptr(self.ring), ring_b,
+                               _ptr(self.workspace), ws_b, _stream(stream), ctypes.byref(h)), None)
+        self.ctx = h
+        self.act_dtype = act_torch_dtype(shape)
+
+    def __del__(self):
+        ctx = getattr(self, "ctx", None)
+        if ctx and _lib is not None:
+            _lib.dflash_destroy(ctx)
+            self.ctx = None
+
+    # ---- the C-ABI calls, same names --------------------------------------------------
+    def cache_append(self, resid: torch.Tensor, commit: bool = False, stream=None) -> None:
+        self._dev(resid, self.act_dtype)
+        if resid.dim() != 2 or resid.shape[1] != self.shape.fc_in:
+            raise ValueError("residual rows must be [n, target_streams*target_width]")
+        _check(lib().dflash_cache_append(self.ctx, _ptr(resid), resid.shape[0], int(bool(commit)), _stream(stream)),
+               self.ctx)
+
+    def cache_trim(self, m: int) -> None:
+        _check(lib().dflash_cache_trim(self.ctx, int(m)), self.ctx)
+
+    def draft_block(self, anchor: int, block: int, tokens: Optional[torch.Tensor] = None,
+                    hidden: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if tokens is None:
+            tokens = torch.empty(block, dtype=torch.int32, device=self.device)
+        self._dev(tokens, torch.int32)
+        if hidden is not None:
+            self._dev(hidden, torch.float32)
+            if hidden.numel() < (block + 1) * self.shape.hidden:
+                raise ValueError("hidden output too small")
+        if tokens.numel() < block:
+            raise ValueError("token output too small")
+        _check(lib().dflash_draft_block(self.ctx, int(anchor), int(block), _ptr(tokens), _ptr(hidden),
+                                        _stream(stream)), self.ctx)
+        return tokens
+
+    def lm_head_argmax(self, rows: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        self._dev(rows, self.act_dtype)
+        if rows.dim() != 2 or rows.shape[1] != self.shape.hidden:
+            raise ValueError("rows must be [n, hidden]")
+        n = rows.shape[0]
+        if out is None:
+            out = torch.empty(n, dtype=torch.int32, device=self.device)
+        self._dev(out, torch.int32)
+        _check(lib().dflash_lm_head_argmax(self.ctx, _ptr(rows), n, _ptr(out), _stream(stream)), self.ctx)
+        return out
+
+    def verify_greedy(self, draft: torch.Tensor, target: torch.Tensor, block: int,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        self._dev(draft, torch.int32)
+        self._dev(target, torch.int32)
+        if draft.numel() < block or target.numel() < block + 1:
+            raise ValueError("draft needs block rows and target block + 1")
+        if out is None:
+            out = torch.empty(3, dtype=torch.int32, device=self.device)
+        self._dev(out, torch.int32)
+        _check(lib().dflash_verify_greedy(self.ctx, _ptr(draft), _ptr(target), int(block), _ptr(out),
+                                          _stream(stream)), self.ctx)
+        return out
+
+    def cache_state(self) -> Tuple[int, int, int, int]:
+        e, pend, s, c = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().dflash_cache_state(self.ctx, ctypes.byref(e), ctypes.byref(pend), ctypes.byref(s),
+                                        ctypes.byref(c)), self.ctx)
+        return e.value, pend.value, s.value, c.value
+
+    def cache_read(self, layer: int, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        e, _, _, _ = self.cache_state()
+        n_max = min(e, self.shape.window)
+        sh = (self.shape.kv_heads, max(n_max, 1), self.shape.head_dim)
+        k = torch.empty(sh, dtype=self.act_dtype, device=self.device)
+        v = torch.empty(sh, dtype=self.act_dtype, device=self.device)
+        n = ctypes.c_int32()
+        _check(lib().dflash_cache_read(self.ctx, int(layer), _ptr(k), _ptr(v), ctypes.byref(n), _stream(stream)),
+               self.ctx)
+        return k[:, :n.value], v[:, :n.value]
+
+    def _dev(self, t: torch.Tensor, dtype: torch.dtype) -> None:
+        if t.device != self.device or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {dtype} tensor on {self.device}, got {t.dtype} on {t.device}")

@@ -1,0 +1,323 @@
+// Attention side of the DFlash block forward: per-head q/k RMSNorm + RoPE, the ring
+// context cache writes, and bidirectional sliding-window attention over the ring plus the
+// block's own keys.
+//
+// The drafter attends with a bidirectional mask over absolute positions, |q - k| <= W,
+// and its context cache is a temporal window whose wrapped ring hands out slots in
+// physical order, so the mask must use absolute key positions (lablup/mlxcel #1762 "Muse
+// Glimmer DFlash assistant drafter on the round loop", What changed). Here the ring slot
+// of position p is (p + phase) mod C and the kernel walks keys in absolute-position order,
+// so the window never has to be rebuilt or rotated: context keys are positions
+// max(0, e-W)..e-1, followed by the block's transient keys at e..e+R-1.
+//
+// Work split: one work-group per (kv head, chunk of 64 keys) computes, for the kv
+// group's query vectors, the chunk's max logit m, sum of exp l and unnormalised output;
+// a combine kernel merges the chunks in chunk order (fixed, so results do not depend on
+// scheduling) and writes the attention output in the GEMM operand dtype.
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+// ---- q/k RMSNorm + RoPE on the block rows -----------------------------------------------
+// One wave per (row, head). Lane i < hd/2 owns the rotate-half pair (i, i + hd/2).
+template <bool BF>
+__global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float* __restrict__ qkv,
+                                                        const void* qnorm, const void* knorm, int R,
+                                                        int64_t pos0, void* qb, void* kb, void* vb) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = a.nq + 2 * a.nkv;
+  if (item >= R * heads) return;
+  const int r = item / heads, h = item - r * heads;
+  const int hd = a.hd, half = hd >> 1;
+  const float* src = qkv + (size_t)r * heads * hd + (size_t)h * hd;
+  const bool act = lane < half;
+  float x1 = act ? src[lane] : 0.f, x2 = act ? src[lane + half] : 0.f;
+  if (h >= a.nq + a.nkv) {  // v head: cast only
+    void* dst = vb;
+    const size_t o = ((size_t)r * a.nkv + (h - a.nq - a.nkv)) * hd;
+    if (act) {
+      act_st<BF>(dst, o + lane, x1);
+      act_st<BF>(dst, o + lane + half, x2);
+    }
+    return;
+  }
+  const bool is_q = h < a.nq;
+  const void* g = is_q ? qnorm : knorm;
+  const float ss = wave_sum(x1 * x1 + x2 * x2);
+  const float s = rsqrtf(ss / (float)hd + a.eps);
+  if (!act) return;
+  x1 = x1 * s * act_ld<BF>(g, lane);
+  x2 = x2 * s * act_ld<BF>(g, lane + half);
+  const double inv = pow((double)a.theta, -2.0 * (double)lane / (double)hd);
+  double sn, cs;
+  sincos((double)(pos0 + r) * inv, &sn, &cs);
+  const float c = (float)cs, sf = (float)sn;
+  const float y1 = x1 * c - x2 * sf, y2 = x2 * c + x1 * sf;
+  void* dst = is_q ? qb : kb;
+  const size_t o = is_q ? ((size_t)r * a.nq + h) * hd : ((size_t)r * a.nkv + (h - a.nq)) * hd;
+  act_st<BF>(dst, o + lane, y1);
+  act_st<BF>(dst, o + lane + half, y2);
+}
+
+// ---- context K/V into the ring ----------------------------------------------------------
+// kv: f32 [n, L, 2, nkv, hd] (k then v per layer). One wave per (row, layer, kv slot).
+// ring: act [L][2][nkv][C][hd].
+template <bool BF>
+__global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const float* __restrict__ kv,
+                                                         const void* const* knorms, int n, int64_t pos0,
+                                                         void* ring) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int per_row = a.L * 2 * a.nkv;
+  if (item >= n * per_row) return;
+  const int r = item / per_row;
+  int rem = item - r * per_row;
+  const int l = rem / (2 * a.nkv);
+  rem -= l * 2 * a.nkv;
+  const int isv = rem / a.nkv, h = rem - isv * a.nkv;
+  const int hd = a.hd, half = hd >> 1;
+  const float* src = kv + (size_t)item * hd;
+  const bool act = lane < half;
+  float x1 = act ? src[lane] : 0.f, x2 = act ? src[lane + half] : 0.f;
+  const int64_t pos = pos0 + r;
+  const int64_t slot = (pos + a.phase) % a.cap;
+  const size_t o = ((((size_t)l * 2 + isv) * a.nkv + h) * a.cap + (size_t)slot) * hd;
+  if (!isv) {
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float s = rsqrtf(ss / (float)hd + a.eps);
+    if (!act) return;
+    const void* g = knorms[l];
+    x1 = x1 * s * act_ld<BF>(g, lane);
+    x2 = x2 * s * act_ld<BF>(g, lane + half);
+    const double inv = pow((double)a.theta, -2.0 * (double)lane / (double)hd);
+    double sn, cs;
+    sincos((double)pos * inv, &sn, &cs);
+    const float c = (float)cs, sf = (float)sn;
+    const float y1 = x1 * c - x2 * sf, y2 = x2 * c + x1 * sf;
+    x1 = y1;
+    x2 = y2;
+  }
+  if (act) {
+    act_st<BF>(ring, o + lane, x1);
+    act_st<BF>(ring, o + lane + half, x2);
+  }
+}
+
+// ---- attention: partial softmax per (kv head, key chunk) --------------------------------
+// Query vector qi = r * G + hh (G = nq / nkv query heads of kv head g). part layout:
+// [nkv][nchunks][R*G][hd + 2] = (unnormalised output, m, l).
+template <bool BF>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const void* ring_layer, const void* qb,
+                                                           const void* kb, const void* vb, int R, int64_t e,
+                                                           int nchunks, float* __restrict__ part) {
+  extern __shared__ __align__(16) float sm[];
+  const int g = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hd = a.hd, G = a.nq / a.nkv, NQ = R * G;
+  const int KS = hd + 1;  // padded row stride of staged K (bank spread)
+  float* Ks = sm;                          // [64][hd+1]
+  float* Vs = Ks + ATTN_CHUNK * KS;        // [64][hd]
+  float* Qs = Vs + ATTN_CHUNK * hd;        // [ATTN_QG][hd]
+  float* Ss = Qs + ATTN_QG * hd;           // [ATTN_QG][64]
+  int64_t* kpos = (int64_t*)(Ss + ATTN_QG * ATTN_CHUNK);  // [64]
+
+  const int64_t lo = e > a.window ? e - a.window : 0;
+  const int nctx = (int)(e - lo);
+  const int nkeys = nctx + R;
+  const int k0 = c * ATTN_CHUNK;
+  const int kn = min(ATTN_CHUNK, nkeys - k0);
+  const size_t plane = (size_t)a.cap * hd;
+  const void* Kr = (const unsigned char*)ring_layer + ((size_t)(0 * a.nkv + g) * plane) * (BF ? 2 : 4);
+  const void* Vr = (const unsigned char*)ring_layer + ((size_t)(1 * a.nkv + g) * plane) * (BF ? 2 : 4);
+
+  // stage this chunk's keys and values (f32) and their absolute positions
+  for (int i = tid; i < kn * hd; i += blockDim.x) {
+    const int kj = i / hd, d = i - kj * hd;
+    const int key = k0 + kj;
+    float kvv, vvv;
+    if (key < nctx) {
+      const int64_t pos = lo + key;
+      const size_t off = (size_t)((pos + a.phase) % a.cap) * hd + d;
+      kvv = act_ld<BF>(Kr, off);
+      vvv = act_ld<BF>(Vr, off);
+    } else {
+      const int b = key - nctx;
+      const size_t off = ((size_t)b * a.nkv + g) * hd + d;
+      kvv = act_ld<BF>(kb, off);
+      vvv = act_ld<BF>(vb, off);
+    }
+    Ks[kj * KS + d] = kvv;
+    Vs[kj * hd + d] = vvv;
+  }
+  for (int kj = tid; kj < ATTN_CHUNK; kj += blockDim.x) {
+    const int key = k0 + kj;
+    kpos[kj] = key < nctx ? lo + key : e + (key - nctx);
+  }
+  const float scale = 1.0f / sqrtf((float)hd);
+
+  for (int q0 = 0; q0 < NQ; q0 += ATTN_QG) {
+    const int nq = min(ATTN_QG, NQ - q0);
+    __syncthreads();
+    for (int i = tid; i < nq * hd; i += blockDim.x) {
+      const int qi = i / hd, d = i - qi * hd;
+      const int gq = q0 + qi, r = gq / G, hh = gq - r * G;
+      Qs[qi * hd + d] = act_ld<BF>(qb, ((size_t)r * a.nq + (size_t)g * G + hh) * hd + d);
+    }
+    __syncthreads();
+    // scores: thread -> key lane, queries strided by waves
+    {
+      const int kj = lane;
+      for (int qi = w; qi < nq; qi += 4) {
+        float sc = -INFINITY;
+        if (kj < kn) {
+          const int r = (q0 + qi) / G;
+          const int64_t qp = e + r, kp = kpos[kj];
+          const int64_t dist = qp > kp ? qp - kp : kp - qp;
+          if (dist <= a.window) {
+            float s = 0.f;
+            const float* qv = Qs + qi * hd;
+            const float* kv = Ks + kj * KS;
+            for (int d = 0; d < hd; ++d) s += qv[d] * kv[d];
+            sc = s * scale;
+          }
+        }
+        Ss[qi * ATTN_CHUNK + kj] = sc;
+      }
+    }
+    __syncthreads();
+    // per-query max / exp / sum, one wave per query
+    for (int qi = w; qi < nq; qi += 4) {
+      const float s = Ss[qi * ATTN_CHUNK + lane];
+      const float m = wave_max(s);
+      const float pexp = (s == -INFINITY) ? 0.f : expf(s - m);
+      Ss[qi * ATTN_CHUNK + lane] = pexp;
+      const float l = wave_sum(pexp);
+      if (lane == 0) {
+        float* dst = part + (((size_t)g * nchunks + c) * NQ + q0 + qi) * (hd + 2);
+        dst[hd] = m;
+        dst[hd + 1] = l;
+      }
+    }
+    __syncthreads();
+    // unnormalised output: thread -> d, queries strided
+    for (int i = tid; i < nq * hd; i += blockDim.x) {
+      const int qi = i / hd, d = i - qi * hd;
+      float o = 0.f;
+      const float* pr = Ss + qi * ATTN_CHUNK;
+      for (int kj = 0; kj < kn; ++kj) o += pr[kj] * Vs[kj * hd + d];
+      part[(((size_t)g * nchunks + c) * NQ + q0 + qi) * (hd + 2) + d] = o;
+    }
+  }
+}
+
+// ---- combine chunks in chunk order --------------------------------------------------------
+// One work-group (hd threads) per (row, query head); out: act [R, nq*hd].
+template <bool BF>
+__global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part, int R, int nchunks, void* out) {
+  const int item = blockIdx.x;
+  const int r = item / a.nq, h = item - r * a.nq;
+  const int G = a.nq / a.nkv, g = h / G, hh = h - g * G;
+  const int NQ = R * G, qi = r * G + hh;
+  const int d = threadIdx.x, hd = a.hd;
+  float M = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part[(((size_t)g * nchunks + c) * NQ + qi) * (hd + 2) + hd]);
+  float L = 0.f, O = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float* p = part + (((size_t)g * nchunks + c) * NQ + qi) * (hd + 2);
+    const float m = p[hd];
+    if (m == -INFINITY) continue;
+    const float f = expf(m - M);
+    L += p[hd + 1] * f;
+    O += p[d] * f;
+  }
+  act_st<BF>(out, (size_t)r * a.nq * hd + (size_t)h * hd + d, O / L);
+}
+
+// ---- live window read-back (parity checks) -----------------------------------------------
+template <bool BF>
+__global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t lo, int n, void* kout, void* vout) {
+  const int hd = a.hd;
+  const size_t total = (size_t)a.nkv * n * hd;
+  const size_t plane = (size_t)a.cap * hd;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int d = (int)(i % hd);
+    const size_t t = i / hd;
+    const int j = (int)(t % n), h = (int)(t / n);
+    const size_t slot = (size_t)((lo + j + a.phase) % a.cap);
+    const size_t so = slot * hd + d;
+    if constexpr (BF) {
+      ((uint16_t*)kout)[i] = ((const uint16_t*)ring_layer)[(size_t)(0 * a.nkv + h) * plane + so];
+      ((uint16_t*)vout)[i] = ((const uint16_t*)ring_layer)[(size_t)(1 * a.nkv + h) * plane + so];
+    } else {
+      ((float*)kout)[i] = ((const float*)ring_layer)[(size_t)(0 * a.nkv + h) * plane + so];
+      ((float*)vout)[i] = ((const float*)ring_layer)[(size_t)(1 * a.nkv + h) * plane + so];
+    }
+  }
+}
+
+// ---- launchers ------------------------------------------------------------------------------
+hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
+                            int R, int64_t pos0, void* qb, void* kb, void* vb, hipStream_t s) {
+  const int items = R * (a.nq + 2 * a.nkv);
+  const int grid = (items + 3) / 4;
+  if (bf) hipLaunchKernelGGL(attn_prep_kernel<true>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, kb, vb);
+  else hipLaunchKernelGGL(attn_prep_kernel<false>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, kb, vb);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const void* const* knorms, int n,
+                             int64_t pos0, void* ring, hipStream_t s) {
+  const int items = n * a.L * 2 * a.nkv;
+  const int grid = (items + 3) / 4;
+  if (bf) hipLaunchKernelGGL(ring_write_kernel<true>, dim3(grid), dim3(256), 0, s, a, kv, knorms, n, pos0, ring);
+  else hipLaunchKernelGGL(ring_write_kernel<false>, dim3(grid), dim3(256), 0, s, a, kv, knorms, n, pos0, ring);
+  return hipGetLastError();
+}
+
+static int attn_nchunks(const AttnShape& a, int R, int64_t e) {
+  const int64_t lo = e > a.window ? e - a.window : 0;
+  const int nkeys = (int)(e - lo) + R;
+  return (nkeys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+}
+
+size_t attention_partial_floats(const AttnShape& a, int R) {
+  const int nch = (a.window + R + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * (a.hd + 2);
+}
+
+hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* kb,
+                            const void* vb, int R, int64_t e, float* part, void* out, hipStream_t s) {
+  const int nch = attn_nchunks(a, R, e);
+  const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4 +
+                     ATTN_CHUNK * 8;
+  dim3 grid(nch, a.nkv);
+  const void* fn = bf ? (const void*)attn_partial_kernel<true> : (const void*)attn_partial_kernel<false>;
+  static bool attr_set[2] = {false, false};
+  hipError_t err = hipSuccess;
+  if (!attr_set[bf ? 1 : 0]) {
+    err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    attr_set[bf ? 1 : 0] = true;
+  }
+  if (bf) hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, kb, vb, R, e, nch, part);
+  else hipLaunchKernelGGL(attn_partial_kernel<false>, grid, dim3(256), lds, s, a, ring_layer, qb, kb, vb, R, e, nch, part);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (bf) hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
+  else hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_read(int bf, const AttnShape& a, const void* ring_layer, int64_t lo, int n, void* kout,
+                             void* vout, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const size_t total = (size_t)a.nkv * n * a.hd;
+  const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  if (bf) hipLaunchKernelGGL(cache_read_kernel<true>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout);
+  else hipLaunchKernelGGL(cache_read_kernel<false>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

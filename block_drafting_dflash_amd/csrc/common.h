@@ -1,0 +1,70 @@
+// Device-side helpers shared by the DFlash kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+
+// ---- bf16 <-> f32 (bf16 stored as raw 16-bit words) -----------------------------------
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// nearest bf16, ties to even; NaN stays NaN, overflow rounds to inf
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// activation load/store in either f32 or bf16 storage
+template <bool BF16> __device__ __forceinline__ float act_ld(const void* p, int64_t i) {
+  if constexpr (BF16) return bf2f(((const uint16_t*)p)[i]);
+  else return ((const float*)p)[i];
+}
+template <bool BF16> __device__ __forceinline__ void act_st(void* p, int64_t i, float v) {
+  if constexpr (BF16) ((uint16_t*)p)[i] = f2bf(v);
+  else ((float*)p)[i] = v;
+}
+
+// ---- MFMA (A = activations [16 rows x k], B = weights [k x 16 cols]) ---------------------
+// 16x16x32 bf16: lane l supplies A[l%16][8*(l/16)+j] and B[8*(l/16)+j][l%16], j = 0..7;
+// result element q of lane l is D[4*(l/16)+q][l%16]. Products are exact, sums in f32.
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// 16x16x4 f32: lane l supplies A[l%16][l/16] and B[l/16][l%16]; same result layout.
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- wave reductions --------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, o, 64);
+  hi = __shfl_xor(hi, o, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// (value, index) key whose unsigned order is: larger value first, then lower index.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int32_t idx) {
+  uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);  // +0 and -0 compare equal
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)ord << 32) | (uint32_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ int32_t argmax_key_index(unsigned long long key) {
+  return (int32_t)(~(uint32_t)(key & 0xffffffffull));
+}

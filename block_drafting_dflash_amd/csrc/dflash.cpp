@@ -1,0 +1,521 @@
+// Host runtime of the DFlash round: the C-ABI declared in include/dflash.h.
+//
+// It validates the drafter shape, lays out the caller's workspace, keeps the ring's
+// bookkeeping (committed end e, pending rows, slack S, capacity C) and enqueues the
+// kernels of each call on the caller's stream. It never allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr int MAX_BLOCK_LIMIT = 256;
+constexpr int ARGMAX_GRID = 1024;
+
+struct Lin {
+  const void *w, *s, *b;
+};
+struct Layer {
+  Lin q, k, v, o, gate, up, down;
+  const void *in_norm, *post_norm, *q_norm, *k_norm;
+};
+
+struct Layout {  // byte offsets into the workspace
+  size_t keys, ticket, knorm_ptrs, x, qkv, qb, kb, vb, attn, mlp, part, app_fc, app_c, app_kv, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int64_t slack_rows(int64_t block) {
+  // clamp(block * 8, 32, 128) rows of speculative buffer, floored at the block size
+  // (lablup/mlxcel #1762, What changed; Pre-merge review round, second finding)
+  return std::max(std::min(std::max(block * 8, (int64_t)32), (int64_t)128), block);
+}
+
+struct Cfg {
+  dflash_config c;
+  int wt;       // WT_* of the linears
+  bool bf;      // act dtype bf16
+  int act_elt;  // bytes per activation / ring element
+  int R;        // max rows of a block forward = max_block + 1
+  int64_t S, C;
+  AttnShape a;
+};
+
+}  // namespace
+
+struct dflash_ctx {
+  Cfg cfg;
+  Layout lay;
+  Lin embed_lin, lm_head, fc;
+  const void *embed, *enc_norm, *final_norm;
+  std::vector<Layer> layers;
+  unsigned char* ring;
+  unsigned char* ws;
+  int64_t e = 0;        // committed context end (absolute position)
+  int64_t pending = 0;  // rows appended since the last trim
+  char err[512] = {0};
+};
+
+namespace {
+
+dflash_status fail(dflash_ctx* ctx, dflash_status st, const char* fmt, ...) {
+  if (ctx) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(ctx->err, sizeof ctx->err, fmt, ap);
+    va_end(ap);
+  }
+  return st;
+}
+
+thread_local char g_create_err[512];
+
+dflash_status cfg_fail(char* buf, dflash_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, 512, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int kstep(int wt) { return wt == WT_F32 ? 16 : 32; }
+
+// waves per work-group for a contraction of length K: the largest count <= 8 that splits
+// K into whole 8-step chunks. It depends on K only, never on the row count.
+int gemm_waves(int wt, int K) {
+  const int units = K / (chunk_steps(1) * kstep(wt));
+  for (int w = 8; w >= 1; --w)
+    if (units % w == 0) return w;
+  return 1;
+}
+
+dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
+  if (!c) return cfg_fail(err, DFLASH_E_ARG, "config is NULL");
+  const int32_t dims[] = {c->hidden, c->layers, c->q_heads, c->kv_heads, c->head_dim, c->intermediate,
+                          c->vocab, c->target_streams, c->target_width, c->window, c->max_block};
+  for (int32_t d : dims)
+    if (d <= 0) return cfg_fail(err, DFLASH_E_SHAPE, "every dimension must be positive");
+  int wt;
+  if (c->weight_dtype == DFLASH_F32) wt = WT_F32;
+  else if (c->weight_dtype == DFLASH_BF16) wt = WT_BF16;
+  else if (c->weight_dtype == DFLASH_Q4G64) return cfg_fail(err, DFLASH_E_ARG, "4-bit weights are not supported by this build");
+  else return cfg_fail(err, DFLASH_E_ARG, "unknown weight dtype %d", c->weight_dtype);
+  const bool bf = wt != WT_F32;
+  if (c->act_dtype != (bf ? DFLASH_BF16 : DFLASH_F32))
+    return cfg_fail(err, DFLASH_E_ARG, "act dtype must be f32 with f32 weights and bf16 otherwise");
+  if (c->max_block > MAX_BLOCK_LIMIT) return cfg_fail(err, DFLASH_E_RANGE, "max_block above %d", MAX_BLOCK_LIMIT);
+  if (c->q_heads % c->kv_heads) return cfg_fail(err, DFLASH_E_SHAPE, "q_heads must be a multiple of kv_heads");
+  if (c->head_dim % 2 || c->head_dim > 128 || c->head_dim % 16)
+    return cfg_fail(err, DFLASH_E_SHAPE, "head_dim must be a multiple of 16 and at most 128");
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab)
+    return cfg_fail(err, DFLASH_E_RANGE, "mask_token_id %d outside [0, %d)", c->mask_token_id, c->vocab);
+  if (c->vocab % 16) return cfg_fail(err, DFLASH_E_SHAPE, "vocab must be a multiple of 16");
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f) || !std::isfinite(c->rms_eps) || !std::isfinite(c->rope_theta))
+    return cfg_fail(err, DFLASH_E_ARG, "rms_eps and rope_theta must be positive and finite");
+  // every extent and element count handed to a kernel fits an int32
+  const int64_t qd = (int64_t)c->q_heads * c->head_dim, kvd = (int64_t)c->kv_heads * c->head_dim;
+  const int64_t fin = (int64_t)c->target_streams * c->target_width;
+  const int64_t H = c->hidden;
+  const int64_t products[] = {qd, kvd, fin, H * c->vocab, H * c->intermediate, H * fin, H * qd,
+                              (int64_t)c->layers * 2 * kvd * (c->window + 128 + c->max_block)};
+  for (int64_t v : products)
+    if (v > INT32_MAX) return cfg_fail(err, DFLASH_E_SHAPE, "a dimension product would wrap an int32");
+  const int unit = chunk_steps(1) * kstep(wt);
+  const int64_t ks[] = {H, c->intermediate, qd, fin};
+  for (int64_t k : ks)
+    if (k % unit) return cfg_fail(err, DFLASH_E_SHAPE, "hidden, intermediate, q_heads*head_dim and fc width must be multiples of %d", unit);
+  if (H % 16 || c->intermediate % 16 || qd % 16 || kvd % 16)
+    return cfg_fail(err, DFLASH_E_SHAPE, "output dimensions must be multiples of 16");
+  // the LDS-staged norm prologue must fit at least 16 rows of hidden
+  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden + 16 / (bf ? 2 : 4)) > (size_t)LDS_BYTES)
+    return cfg_fail(err, DFLASH_E_SHAPE, "hidden too large for the staged operand");
+  Cfg g;
+  g.c = *c;
+  g.wt = wt;
+  g.bf = bf;
+  g.act_elt = bf ? 2 : 4;
+  g.R = c->max_block + 1;
+  g.S = slack_rows(c->max_block);
+  g.C = c->window + g.S;
+  if (c->ring_phase < 0) return cfg_fail(err, DFLASH_E_ARG, "ring_phase must be >= 0");
+  g.a.nq = c->q_heads;
+  g.a.nkv = c->kv_heads;
+  g.a.hd = c->head_dim;
+  g.a.L = c->layers;
+  g.a.window = c->window;
+  g.a.cap = (int32_t)g.C;
+  g.a.phase = (int32_t)(c->ring_phase % g.C);
+  g.a.eps = c->rms_eps;
+  g.a.theta = c->rope_theta;
+  *out = g;
+  return DFLASH_OK;
+}
+
+Layout make_layout(const Cfg& g) {
+  const dflash_config& c = g.c;
+  const size_t H = c.hidden, R = g.R, ae = g.act_elt;
+  const size_t qd = (size_t)c.q_heads * c.head_dim, kvd = (size_t)c.kv_heads * c.head_dim;
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.keys = take(sizeof(unsigned long long) * GEMM_MAX_ROWS);
+  L.ticket = take(sizeof(unsigned int));
+  L.knorm_ptrs = take(sizeof(void*) * c.layers);
+  L.x = take(4 * R * H);
+  L.qkv = take(4 * R * (qd + 2 * kvd));
+  L.qb = take(ae * R * qd);
+  L.kb = take(ae * R * kvd);
+  L.vb = take(ae * R * kvd);
+  L.attn = take(ae * R * qd);
+  L.mlp = take(ae * R * c.intermediate);
+  L.part = take(4 * attention_partial_floats(g.a, (int)R));
+  L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
+  L.app_c = take(ae * (size_t)GEMM_MAX_ROWS * H);
+  L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
+  L.total = o;
+  return L;
+}
+
+size_t ring_bytes_of(const Cfg& g) {
+  return (size_t)g.act_elt * g.c.layers * 2 * g.c.kv_heads * (size_t)g.C * g.c.head_dim;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+dflash_status dev(dflash_ctx* ctx, hipError_t e, const char* what) {
+  if (e == hipSuccess) return DFLASH_OK;
+  return fail(ctx, DFLASH_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- GEMM driver: chunks rows, fills parameters, picks the grid -------------------------
+struct GemmCall {
+  int epi, xsrc;
+  std::vector<GemmSeg> segs;
+  int K;
+  const void* x;
+  int64_t ldx;  // elements
+  const void* gain;
+  void* y;
+  int64_t ldy;  // elements
+  int32_t* idx;
+};
+
+dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_t st) {
+  const Cfg& g = ctx->cfg;
+  const int wt = g.wt;
+  const int nb = gc.epi == EPI_SWIGLU ? 2 : 1;
+  const int waves = gemm_waves(wt, gc.K);
+  const int xstride = gc.K + 16 / g.act_elt;
+  const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;
+  const size_t y_elt = gc.epi == EPI_SWIGLU ? g.act_elt : 4;
+  int N = 0;
+  for (const auto& s : gc.segs) N = std::max(N, s.col0 + s.rows);
+  if (nb == 2) N = gc.segs[0].rows;
+  int r0 = 0;
+  while (r0 < rows) {
+    int rc = std::min(rows - r0, GEMM_MAX_ROWS);
+    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, 16 * waves);  // one finishing wave per row tile
+    if (gc.xsrc != XSRC_GLOBAL)
+      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride) > (size_t)LDS_BYTES) --rc;
+    GemmParams p{};
+    for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
+    p.nseg = (int)gc.segs.size();
+    p.ntiles = N / 16;
+    p.K = gc.K;
+    p.R = rc;
+    p.waves = waves;
+    p.nchunks = gc.K / (waves * chunk_steps((rc + 15) / 16) * kstep(wt));
+    p.x = (const unsigned char*)gc.x + (size_t)r0 * gc.ldx * x_elt;
+    p.ldx = gc.ldx;
+    p.gain = gc.gain;
+    p.eps = g.c.rms_eps;
+    p.xstride = xstride;
+    int grid = p.ntiles;
+    if (gc.epi == EPI_ARGMAX) {
+      p.keys = (unsigned long long*)(ctx->ws + ctx->lay.keys);
+      p.ticket = (unsigned int*)(ctx->ws + ctx->lay.ticket);
+      p.idx_out = gc.idx + r0;
+      grid = std::min(p.ntiles, ARGMAX_GRID);
+    } else {
+      p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
+      p.ldy = gc.ldy;
+    }
+    const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, p, grid, st);
+    if (le != hipSuccess)
+      return fail(ctx, DFLASH_E_DEVICE, "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, grid %d, lds %zu): %s",
+                  gc.epi, gc.xsrc, gc.K, rc, p.ntiles, waves, grid,
+                  gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride), hipGetErrorString(le));
+    r0 += rc;
+  }
+  return DFLASH_OK;
+}
+
+GemmSeg seg(const Lin& l, int col0, int rows) { return GemmSeg{l.w, l.s, l.b, col0, rows}; }
+
+}  // namespace
+
+// ======================================================================================
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_ARG: return "bad argument";
+    case DFLASH_E_SHAPE: return "bad shape";
+    case DFLASH_E_RANGE: return "value out of range";
+    case DFLASH_E_NO_CONTEXT: return "no committed context";
+    case DFLASH_E_REWIND: return "illegal rewind";
+    case DFLASH_E_STATE: return "uncommitted rows pending";
+    case DFLASH_E_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* dflash_last_error(const dflash_ctx* ctx) { return ctx ? ctx->err : g_create_err; }
+
+dflash_status dflash_query_sizes(const dflash_config* cfg, size_t* ring_bytes, size_t* workspace_bytes) {
+  Cfg g;
+  dflash_status s = check_cfg(cfg, &g, g_create_err);
+  if (s != DFLASH_OK) return s;
+  if (!ring_bytes || !workspace_bytes) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL size output");
+  *ring_bytes = ring_bytes_of(g);
+  *workspace_bytes = make_layout(g).total;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts, void* ring, size_t ring_bytes,
+                            void* workspace, size_t workspace_bytes, void* stream, dflash_ctx** out) {
+  g_create_err[0] = 0;
+  if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
+  *out = nullptr;
+  Cfg g;
+  dflash_status s = check_cfg(cfg, &g, g_create_err);
+  if (s != DFLASH_OK) return s;
+  if (!wts || !wts->layers) return cfg_fail(g_create_err, DFLASH_E_ARG, "weights or layer array is NULL");
+  if (!ring || !workspace) return cfg_fail(g_create_err, DFLASH_E_ARG, "ring or workspace is NULL");
+  if (((uintptr_t)ring & 255u) || ((uintptr_t)workspace & 255u))
+    return cfg_fail(g_create_err, DFLASH_E_ARG, "ring and workspace must be 256-byte aligned");
+  const Layout lay = make_layout(g);
+  if (ring_bytes < ring_bytes_of(g) || workspace_bytes < lay.total)
+    return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring or workspace smaller than dflash_query_sizes");
+  auto lin_ok = [&](const dflash_linear& l) { return l.w && aligned16(l.w); };
+  if (!wts->embed || !wts->enc_norm || !wts->final_norm || !lin_ok(wts->lm_head) || !lin_ok(wts->fc))
+    return cfg_fail(g_create_err, DFLASH_E_ARG, "a top-level weight is NULL or not 16-byte aligned");
+  for (int l = 0; l < g.c.layers; ++l) {
+    const dflash_layer& L = wts->layers[l];
+    if (!lin_ok(L.q) || !lin_ok(L.k) || !lin_ok(L.v) || !lin_ok(L.o) || !lin_ok(L.gate) || !lin_ok(L.up) ||
+        !lin_ok(L.down) || !L.in_norm || !L.post_norm || !L.q_norm || !L.k_norm)
+      return cfg_fail(g_create_err, DFLASH_E_ARG, "layer %d has a NULL or misaligned weight", l);
+  }
+  dflash_ctx* ctx = new (std::nothrow) dflash_ctx();
+  if (!ctx) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
+  ctx->cfg = g;
+  ctx->lay = lay;
+  auto cv = [](const dflash_linear& l) { return Lin{l.w, l.scales, l.biases}; };
+  ctx->lm_head = cv(wts->lm_head);
+  ctx->fc = cv(wts->fc);
+  ctx->embed = wts->embed;
+  ctx->enc_norm = wts->enc_norm;
+  ctx->final_norm = wts->final_norm;
+  ctx->layers.resize(g.c.layers);
+  std::vector<const void*> knorms(g.c.layers);
+  for (int l = 0; l < g.c.layers; ++l) {
+    const dflash_layer& L = wts->layers[l];
+    ctx->layers[l] = Layer{cv(L.q), cv(L.k), cv(L.v), cv(L.o), cv(L.gate), cv(L.up), cv(L.down),
+                           L.in_norm, L.post_norm, L.q_norm, L.k_norm};
+    knorms[l] = L.k_norm;
+  }
+  ctx->ring = (unsigned char*)ring;
+  ctx->ws = (unsigned char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(ctx->ws + lay.knorm_ptrs, knorms.data(), sizeof(void*) * knorms.size(),
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = launch_init_ws((unsigned long long*)(ctx->ws + lay.keys), GEMM_MAX_ROWS, (unsigned int*)(ctx->ws + lay.ticket), st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
+  if (e != hipSuccess) {
+    cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
+    delete ctx;
+    return DFLASH_E_DEVICE;
+  }
+  *out = ctx;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx* ctx) { delete ctx; }
+
+dflash_status dflash_cache_state(const dflash_ctx* ctx, int64_t* e, int32_t* pending, int32_t* slack,
+                                 int32_t* capacity) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (e) *e = ctx->e;
+  if (pending) *pending = (int32_t)ctx->pending;
+  if (slack) *slack = (int32_t)ctx->cfg.S;
+  if (capacity) *capacity = (int32_t)ctx->cfg.C;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_cache_trim(dflash_ctx* ctx, int32_t m) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (m < 0 || m > ctx->pending || m > ctx->cfg.S)
+    return fail(ctx, DFLASH_E_REWIND, "rewind of %d rows with %lld pending and slack %lld", m,
+                (long long)ctx->pending, (long long)ctx->cfg.S);
+  ctx->e += ctx->pending - m;
+  ctx->pending = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_cache_append(dflash_ctx* ctx, const void* resid, int32_t n, int32_t commit, void* stream) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (!resid || n <= 0) return fail(ctx, DFLASH_E_ARG, "append of %d rows: no residual stream captured", n);
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t start = ctx->e + ctx->pending, end = start + n;
+  const int64_t keep_from = commit ? end - c.window : end - g.C;
+  const int64_t first = std::max<int64_t>(0, keep_from - start);
+  const int64_t F = (int64_t)c.target_streams * c.target_width;
+  const int kvd = c.kv_heads * c.head_dim;
+  const int kv_cols = c.layers * 2 * kvd;
+  for (int64_t r0 = first; r0 < n; r0 += GEMM_MAX_ROWS) {
+    const int rc = (int)std::min<int64_t>(GEMM_MAX_ROWS, n - r0);
+    float* fc_out = (float*)(ctx->ws + ctx->lay.app_fc);
+    void* cbuf = ctx->ws + ctx->lay.app_c;
+    float* kv = (float*)(ctx->ws + ctx->lay.app_kv);
+    GemmCall f{EPI_STORE, XSRC_GLOBAL, {seg(ctx->fc, 0, c.hidden)}, (int)F,
+               (const unsigned char*)resid + (size_t)r0 * F * g.act_elt, F, nullptr, fc_out, c.hidden, nullptr};
+    dflash_status s = run_gemm(ctx, f, rc, st);
+    if (s != DFLASH_OK) return s;
+    s = dev(ctx, launch_rownorm(g.bf, fc_out, ctx->enc_norm, c.rms_eps, rc, c.hidden, cbuf, st), "encoder norm");
+    if (s != DFLASH_OK) return s;
+    // per-layer k/v projections of the encoder rows, six layers per launch
+    for (int l0 = 0; l0 < c.layers; l0 += GEMM_MAXSEG / 2) {
+      const int l1 = std::min(c.layers, l0 + GEMM_MAXSEG / 2);
+      GemmCall kvc{EPI_STORE, XSRC_GLOBAL, {}, c.hidden, cbuf, c.hidden, nullptr,
+                   kv + (size_t)l0 * 2 * kvd, kv_cols, nullptr};
+      for (int l = l0; l < l1; ++l) {
+        kvc.segs.push_back(seg(ctx->layers[l].k, (l - l0) * 2 * kvd, kvd));
+        kvc.segs.push_back(seg(ctx->layers[l].v, (l - l0) * 2 * kvd + kvd, kvd));
+      }
+      s = run_gemm(ctx, kvc, rc, st);
+      if (s != DFLASH_OK) return s;
+    }
+    s = dev(ctx, launch_ring_write(g.bf, g.a, kv, (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), rc,
+                                   start + r0, ctx->ring, st),
+            "ring write");
+    if (s != DFLASH_OK) return s;
+  }
+  if (commit) {
+    ctx->e = end;
+    ctx->pending = 0;
+  } else {
+    ctx->pending += n;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block, int32_t* d_tokens, float* d_hidden,
+                                 void* stream) {
+  if (!ctx) return DFLASH_E_ARG;
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  if (block < 1 || block > c.max_block) return fail(ctx, DFLASH_E_RANGE, "block %d outside 1..%d", block, c.max_block);
+  if (anchor < 0 || anchor >= c.vocab) return fail(ctx, DFLASH_E_RANGE, "anchor %d outside [0, %d)", anchor, c.vocab);
+  if (!d_tokens) return fail(ctx, DFLASH_E_ARG, "NULL token output");
+  if (ctx->e <= 0) return fail(ctx, DFLASH_E_NO_CONTEXT, "draft with an empty context");
+  if (ctx->pending) return fail(ctx, DFLASH_E_STATE, "%lld appended rows are not committed", (long long)ctx->pending);
+  hipStream_t st = (hipStream_t)stream;
+  const int R = block + 1;
+  const int H = c.hidden;
+  const int qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim;
+  float* x = (float*)(ctx->ws + ctx->lay.x);
+  float* qkv = (float*)(ctx->ws + ctx->lay.qkv);
+  void* qb = ctx->ws + ctx->lay.qb;
+  void* kb = ctx->ws + ctx->lay.kb;
+  void* vb = ctx->ws + ctx->lay.vb;
+  void* attn = ctx->ws + ctx->lay.attn;
+  void* mlp = ctx->ws + ctx->lay.mlp;
+  float* part = (float*)(ctx->ws + ctx->lay.part);
+  const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.C * c.head_dim;
+
+  dflash_status s = dev(ctx, launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, x, st), "embed");
+  if (s != DFLASH_OK) return s;
+  for (int l = 0; l < c.layers; ++l) {
+    const Layer& L = ctx->layers[l];
+    GemmCall q{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
+               L.in_norm, qkv, qd + 2 * kvd, nullptr};
+    if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
+    s = dev(ctx, launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, kb, vb, st), "attn prep");
+    if (s != DFLASH_OK) return s;
+    s = dev(ctx, launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, kb, vb, R, ctx->e, part, attn, st),
+            "attention");
+    if (s != DFLASH_OK) return s;
+    GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
+    if ((s = run_gemm(ctx, o, R, st)) != DFLASH_OK) return s;
+    GemmCall gu{EPI_SWIGLU, XSRC_NORM, {seg(L.gate, 0, c.intermediate), seg(L.up, 0, c.intermediate)}, H, x, H,
+                L.post_norm, mlp, c.intermediate, nullptr};
+    if ((s = run_gemm(ctx, gu, R, st)) != DFLASH_OK) return s;
+    GemmCall dn{EPI_RESID, XSRC_GLOBAL, {seg(L.down, 0, H)}, c.intermediate, mlp, c.intermediate, nullptr, x, H,
+                nullptr};
+    if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
+  }
+  if (d_hidden) {
+    s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
+    if (s != DFLASH_OK) return s;
+  }
+  GemmCall lm{EPI_ARGMAX, XSRC_NORM, {seg(ctx->lm_head, 0, c.vocab)}, H, x + H, H, ctx->final_norm, nullptr, 0,
+              d_tokens};
+  return run_gemm(ctx, lm, block, st);
+}
+
+dflash_status dflash_lm_head_argmax(dflash_ctx* ctx, const void* rows, int32_t n, int32_t* d_idx, void* stream) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (!rows || !d_idx) return fail(ctx, DFLASH_E_ARG, "NULL rows or output");
+  if (n < 1 || n > 4096) return fail(ctx, DFLASH_E_RANGE, "row count %d outside 1..4096", n);
+  const dflash_config& c = ctx->cfg.c;
+  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, c.hidden, rows, c.hidden, nullptr, nullptr, 0,
+              d_idx};
+  return run_gemm(ctx, lm, n, (hipStream_t)stream);
+}
+
+dflash_status dflash_verify_greedy(dflash_ctx* ctx, const int32_t* d_draft, const int32_t* d_target, int32_t block,
+                                   int32_t* d_out, void* stream) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (!d_draft || !d_target || !d_out) return fail(ctx, DFLASH_E_ARG, "NULL verify buffer");
+  if (block < 1 || block > ctx->cfg.c.max_block)
+    return fail(ctx, DFLASH_E_RANGE, "block %d outside 1..%d", block, ctx->cfg.c.max_block);
+  return dev(ctx, launch_verify(d_draft, d_target, block, ctx->cfg.c.vocab, d_out, (hipStream_t)stream), "verify");
+}
+
+dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, void* v_out, int32_t* n_out,
+                                void* stream) {
+  if (!ctx) return DFLASH_E_ARG;
+  const Cfg& g = ctx->cfg;
+  if (layer < 0 || layer >= g.c.layers) return fail(ctx, DFLASH_E_RANGE, "layer %d outside 0..%d", layer, g.c.layers - 1);
+  if (!n_out) return fail(ctx, DFLASH_E_ARG, "NULL count output");
+  const int64_t lo = std::max<int64_t>(0, ctx->e - g.c.window);
+  const int n = (int)(ctx->e - lo);
+  *n_out = n;
+  if (n == 0) return DFLASH_OK;
+  if (!k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL window output");
+  const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.C * g.c.head_dim;
+  return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),
+             "cache read");
+}
+
+}  // extern "C"

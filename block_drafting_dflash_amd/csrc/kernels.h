@@ -1,0 +1,82 @@
+// Internal launch interface between the runtime (dflash.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+enum { WT_F32 = 0, WT_BF16 = 1, WT_Q4 = 2 };  // weight storage (matches dflash_dtype)
+
+constexpr int GEMM_MAXSEG = 12;
+constexpr int GEMM_MAX_ROWS = 48;  // rows per GEMM launch (3 MFMA row tiles)
+constexpr int ATTN_CHUNK = 64;     // keys per attention work-group
+constexpr int ATTN_QG = 64;        // query vectors per attention pass
+
+enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2 };
+
+// MFMA steps per pipelined chunk (16-byte weight loads per lane per chunk): deeper for one
+// row tile, shallower when 2-3 row tiles of activations also sit in registers.
+__host__ __device__ constexpr int chunk_steps(int rt) { return rt == 1 ? 8 : 4; }
+constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per compute unit
+enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
+
+// One weight matrix [rows, K] (row-major) whose outputs occupy columns col0..col0+rows-1.
+struct GemmSeg {
+  const void* w;
+  const void* scales;  // q4 only: bf16 [rows, K/64]
+  const void* biases;  // q4 only
+  int32_t col0;
+  int32_t rows;
+};
+
+// Y[r, n] = sum_k X[r, k] W[n, k] for r < R over the concatenated segments.
+struct GemmParams {
+  GemmSeg seg[GEMM_MAXSEG];
+  int32_t nseg;
+  int32_t ntiles;   // 16-column output tiles
+  int32_t K;
+  int32_t R;        // rows of X (<= GEMM_MAX_ROWS)
+  int32_t waves;    // waves per work-group; each owns K/waves of every tile
+  int32_t nchunks;  // pipelined chunks per wave per tile
+  const void* x;    // XSRC_GLOBAL/LDS: act dtype [R, ldx]; XSRC_NORM: f32 [R, ldx]
+  int64_t ldx;
+  const void* gain;  // XSRC_NORM: act-dtype storage [K]
+  float eps;
+  int32_t xstride;  // staged X row stride in LDS (elements)
+  void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: act dtype [R, ldy]
+  int64_t ldy;
+  unsigned long long* keys;  // ARGMAX: per-row running keys (zero between launches)
+  unsigned int* ticket;      // ARGMAX: arrival counter (zero between launches)
+  int32_t* idx_out;          // ARGMAX: [R]
+};
+
+hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmParams& p, int grid, hipStream_t s);
+size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride);
+
+// ---- small kernels --------------------------------------------------------------------
+struct AttnShape {
+  int32_t nq, nkv, hd, L;
+  int32_t window;
+  int32_t cap, phase;  // ring capacity C and phase
+  float eps, theta;
+};
+
+hipError_t launch_init_ws(unsigned long long* keys, int nkeys, unsigned int* ticket, hipStream_t s);
+hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
+                        float* x, hipStream_t s);
+hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
+                          hipStream_t s);
+hipError_t launch_attn_prep(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
+                            const void* knorm, int R, int64_t pos0, void* qb, void* kb, void* vb, hipStream_t s);
+hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
+                             int n, int64_t pos0, void* ring, hipStream_t s);
+hipError_t launch_attention(int act_bf16, const AttnShape& a, const void* ring_layer, const void* qb,
+                            const void* kb, const void* vb, int R, int64_t e, float* part, void* out,
+                            hipStream_t s);
+size_t attention_partial_floats(const AttnShape& a, int R);
+hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
+                         hipStream_t s);
+hipError_t launch_cache_read(int act_bf16, const AttnShape& a, const void* ring_layer, int64_t lo, int n,
+                             void* kout, void* vout, hipStream_t s);
+
+}  // namespace dflash

@@ -1,0 +1,99 @@
+// Small kernels of the DFlash round: workspace init, block embedding gather, the encoder
+// RMSNorm, and the greedy verify scan.
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+__global__ void init_ws_kernel(unsigned long long* keys, int nkeys, unsigned int* ticket) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nkeys; i += gridDim.x * blockDim.x) keys[i] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+}
+
+hipError_t launch_init_ws(unsigned long long* keys, int nkeys, unsigned int* ticket, hipStream_t s) {
+  hipLaunchKernelGGL(init_ws_kernel, dim3(4), dim3(256), 0, s, keys, nkeys, ticket);
+  return hipGetLastError();
+}
+
+// Block rows [anchor, mask x (R-1)] from the target's raw embedding table (not the
+// embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows.
+template <bool BF>
+__global__ void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x) {
+  const int r = blockIdx.x;
+  const int64_t tok = r == 0 ? anchor : mask_id;
+  for (int i = threadIdx.x; i < hidden; i += blockDim.x) x[(size_t)r * hidden + i] = act_ld<BF>(table, tok * hidden + i);
+}
+
+hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
+                        hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(embed_kernel<true>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x);
+  else hipLaunchKernelGGL(embed_kernel<false>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x);
+  return hipGetLastError();
+}
+
+// out[r] = operand cast of RMSNorm(in[r]) * g; one 256-thread group per row. The sum of
+// squares is accumulated per lane in a fixed stride, then reduced wave by wave in order.
+template <bool BF>
+__global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ in, const void* gain, float eps, int H,
+                                                      void* out) {
+  __shared__ float part[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* x = in + (size_t)r * H;
+  float ss = 0.f;
+  for (int k = tid; k < H; k += 256) ss += x[k] * x[k];
+  ss = wave_sum(ss);
+  if (lane == 0) part[w] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float s = rsqrtf(tot / (float)H + eps);
+  for (int k = tid; k < H; k += 256) act_st<BF>(out, (size_t)r * H + k, x[k] * s * act_ld<BF>(gain, k));
+}
+
+hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, int R, int H, void* out,
+                          hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out);
+  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out);
+  return hipGetLastError();
+}
+
+// Greedy exact-match verify on one wave: the first row i with draft[i] != target[i]
+// (found by ballot over 64 rows at a time) is the accepted length k; bonus = target[k]
+// (lablup/mlxcel #1751, Implementation Review Summary: greedy exact-match verify rule).
+__global__ void verify_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ target, int B,
+                              int vocab, int32_t* out) {
+  const int lane = threadIdx.x;
+  bool bad = false;
+  for (int i = lane; i <= B; i += 64) {
+    const int32_t a = target[i];
+    bad |= (a < 0 || a >= vocab);
+  }
+  const bool any_bad = __any(bad);
+  int k = B;
+  for (int base = 0; base < B; base += 64) {
+    const int i = base + lane;
+    const bool mismatch = (i < B) && (draft[i] != target[i]);
+    const unsigned long long m = __ballot(mismatch);
+    if (m) {
+      k = base + __ffsll((long long)m) - 1;
+      break;
+    }
+  }
+  if (lane == 0) {
+    if (any_bad) {
+      out[0] = 0;
+      out[1] = -1;
+      out[2] = 1;
+    } else {
+      out[0] = k;
+      out[1] = target[k];
+      out[2] = 0;
+    }
+  }
+}
+
+hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(64), 0, s, draft, target, B, vocab, out);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

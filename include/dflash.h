@@ -1,0 +1,188 @@
+/*
+ * dflash.h -- C-ABI of one DFlash speculative round at batch 1 on one MI355X (gfx950).
+ *
+ * The round: the drafter's block forward (encoder.fc + output_norm_enc over the captured
+ * target residual streams, then Qwen3-shaped bidirectional sliding-window layers with
+ * per-head q/k RMSNorm and a SwiGLU MLP), the target's shared raw embedding table and
+ * untied lm_head with a per-row argmax, greedy exact-match verification, and the ring
+ * context cache with speculative slack and trim rollback.
+ *
+ * Sources: lablup/mlxcel #1762 "Muse Glimmer DFlash assistant drafter on the round loop"
+ * (What changed; Pre-merge review round), z-lab/dflash #168 "load Meta's
+ * Muse-Glimmer-30B-assistant DFlash head" (Why), lablup/mlxcel #1751 "LFM2 / LFM2.5
+ * DSpark drafter on the DFlash loop" (Security fixes; Implementation Review Summary).
+ *
+ * Conventions for every call:
+ *  - Device pointers point to device memory owned by the caller (PyTorch or hipMalloc).
+ *    The library never allocates device memory: the caller sizes the ring and the
+ *    workspace with dflash_query_sizes and keeps every buffer alive while the context is.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Device calls only enqueue
+ *    work; outputs are valid once the caller has synchronised the stream.
+ *  - Every call returns a status. On error nothing is enqueued and the context is
+ *    unchanged; dflash_last_error() describes the failure. Nothing throws or aborts.
+ *  - A context is used by one host thread and one stream at a time.
+ *  - Weight matrices are [out, in] row-major (y = x W^T). bf16 is raw 16-bit storage.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dflash_ctx dflash_ctx; /* opaque */
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_ARG = 1,        /* null pointer or malformed argument */
+  DFLASH_E_SHAPE = 2,      /* a dimension out of range, inconsistent, or a size overflow */
+  DFLASH_E_RANGE = 3,      /* a token id or a block width out of range */
+  DFLASH_E_NO_CONTEXT = 4, /* a draft before any committed context row */
+  DFLASH_E_REWIND = 5,     /* a trim deeper than the pending rows or than the slack */
+  DFLASH_E_STATE = 6,      /* a draft while appended rows are still uncommitted */
+  DFLASH_E_DEVICE = 7      /* a HIP call failed */
+} dflash_status;
+
+typedef enum {
+  DFLASH_F32 = 0,  /* float32 */
+  DFLASH_BF16 = 1, /* bfloat16 */
+  DFLASH_Q4G64 = 2 /* 4-bit affine, group 64 along the input dim (weights only, see below) */
+} dflash_dtype;
+
+/*
+ * Drafter shape. All dimensions are positive and bounded so that every extent and
+ * every element count fits an int32 (lablup/mlxcel #1762, Pre-merge review round, third
+ * finding: dimensions that would wrap an i32 are refused).
+ *   hidden, intermediate, q_heads*head_dim, target_streams*target_width: multiples of
+ *     128 (of 512 for DFLASH_Q4G64); each is either <= 2048 or a multiple of 2048.
+ *   head_dim: even, <= 256. q_heads a multiple of kv_heads.
+ *   window W >= 1: keys at absolute position p are visible to a query at q iff
+ *     |q - p| <= W (lablup/mlxcel #1762, What changed).
+ *   max_block: largest block a draft may use, 1..256. The ring's slack is
+ *     S = max(clamp(8*max_block, 32, 128), max_block) rows and its capacity C = W + S
+ *     (lablup/mlxcel #1762, What changed; Pre-merge review round, second finding).
+ *   mask_token_id: the token of the block's mask rows, in [0, vocab) (lablup/mlxcel
+ *     #1751, Review fixes: the mask id indexes the target's embedding table).
+ *   ring_phase: slot of absolute position p is (p + ring_phase) mod C.
+ *   weight_dtype: dtype of fc, every layer linear and the lm_head. With DFLASH_Q4G64
+ *     the embedding table and the norm gains are bf16; otherwise they use weight_dtype.
+ *   act_dtype: DFLASH_F32 with f32 weights, DFLASH_BF16 otherwise. It is the dtype of
+ *     the residual slab, of every GEMM operand, of the ring and of lm_head input rows.
+ */
+typedef struct {
+  int32_t hidden, layers, q_heads, kv_heads, head_dim, intermediate, vocab;
+  int32_t target_streams, target_width;
+  int32_t window, max_block, mask_token_id, ring_phase;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype; /* dflash_dtype */
+  int32_t act_dtype;    /* dflash_dtype */
+} dflash_config;
+
+/* A linear layer [out, in]. For DFLASH_Q4G64: w is uint32 [out, in/8] holding eight
+ * 4-bit codes per word along the input dim, lowest nibble first; scales and biases are
+ * bf16 [out, in/64]; the weight is scale*code + bias. Otherwise scales/biases are NULL. */
+typedef struct {
+  const void *w, *scales, *biases;
+} dflash_linear;
+
+typedef struct {
+  dflash_linear q, k, v, o, gate, up, down;
+  const void *in_norm, *post_norm; /* [hidden] */
+  const void *q_norm, *k_norm;     /* [head_dim] */
+} dflash_layer;
+
+/* embed and lm_head are the target's raw embedding table [vocab, hidden] and untied
+ * lm_head, shared with the drafter (lablup/mlxcel #1762, What changed). fc is
+ * encoder.fc [hidden, target_streams*target_width]; enc_norm is encoder.output_norm_enc.
+ * `layers` is a host array of cfg.layers entries; it is copied at create. */
+typedef struct {
+  const void *embed;
+  dflash_linear lm_head, fc;
+  const void *enc_norm, *final_norm;
+  const dflash_layer *layers;
+} dflash_weights;
+
+/* Bytes of ring and of workspace a context with this config needs. Host only. */
+dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, size_t *workspace_bytes);
+
+/* Validate cfg and the weight pointers, bind the caller's buffers and initialise the
+ * workspace on `stream`. ring and workspace must be at least the queried sizes and
+ * 256-byte aligned. The ring starts empty: e = 0, no pending rows. */
+dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *weights, void *ring,
+                            size_t ring_bytes, void *workspace, size_t workspace_bytes, void *stream,
+                            dflash_ctx **out);
+
+void dflash_destroy(dflash_ctx *ctx);
+
+/*
+ * Append n captured target residual rows (device, act_dtype, [n, target_streams *
+ * target_width] row-major) at the next absolute positions. Each row goes through
+ * encoder.fc and output_norm_enc, then every layer's k/v projection, k_norm and RoPE at
+ * its position, and is written to its ring slot. commit = 0: the rows are pending until
+ * dflash_cache_trim. commit != 0: all pending rows and these are committed now, and rows
+ * that the committed window can no longer see are dropped before the encoder
+ * (lablup/mlxcel #1762, Pre-merge review round, third finding). Errors: n <= 0 or a NULL
+ * slab ("no residual stream captured", lablup/mlxcel #1762, Pre-merge review round,
+ * second finding).
+ */
+dflash_status dflash_cache_append(dflash_ctx *ctx, const void *resid, int32_t n, int32_t commit, void *stream);
+
+/*
+ * Commit the pending rows except the last m: e += pending - m, pending = 0. Host
+ * bookkeeping only: the offsets rewind, no slot is restored (lablup/mlxcel #1762,
+ * Pre-merge review round: RotatingKVCache::trim). After a round of block B with k
+ * accepted, m = B - k (lablup/mlxcel #1751, Short-conv rollback: trim(block_size - n)
+ * with n = accepted + 1). DFLASH_E_REWIND unless 0 <= m <= min(pending, slack).
+ */
+dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
+
+/*
+ * Draft one block: rows [anchor, mask x block] at absolute positions e..e+block are
+ * embedded with the raw table, run through every layer over the ring's committed
+ * context and the block's own keys, and rows 1..block go through final_norm and the
+ * lm_head. d_tokens (device int32 [block]) receives the first index of each row's
+ * maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
+ * residual stream after the last layer. Errors: block outside 1..max_block or anchor
+ * outside [0, vocab) (DFLASH_E_RANGE); e == 0 (DFLASH_E_NO_CONTEXT); pending rows
+ * (DFLASH_E_STATE).
+ */
+dflash_status dflash_draft_block(dflash_ctx *ctx, int32_t anchor, int32_t block, int32_t *d_tokens,
+                                 float *d_hidden, void *stream);
+
+/* argmax over the vocabulary of rows (device, act_dtype [n, hidden]) times the shared
+ * lm_head, first index of the maximum f32 logit, into d_idx (device int32 [n]); the
+ * target's verify rows use this (lablup/mlxcel #1762, What changed: lm_head_module, no
+ * softcap). 1 <= n <= 4096. */
+dflash_status dflash_lm_head_argmax(dflash_ctx *ctx, const void *rows, int32_t n, int32_t *d_idx, void *stream);
+
+/*
+ * Greedy exact-match verify of one block (lablup/mlxcel #1751, Implementation Review
+ * Summary: greedy exact-match verify rule, verify width = block + 1). d_draft: device
+ * int32 [block] = d_1..d_block; d_target: device int32 [block+1] = the target's argmax
+ * at verify rows e..e+block. d_out (device int32 [3]) receives k = the number of leading
+ * rows with d_{i+1} == a_i (0..block), the bonus token a_k, and a status word: 0, or 1
+ * if any target id lies outside [0, vocab) (then k = 0 and bonus = -1).
+ */
+dflash_status dflash_verify_greedy(dflash_ctx *ctx, const int32_t *d_draft, const int32_t *d_target,
+                                   int32_t block, int32_t *d_out, void *stream);
+
+/* Committed end e, pending rows, slack S and capacity C. Host only. */
+dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pending, int32_t *slack,
+                                 int32_t *capacity);
+
+/* Copy one layer's live window, positions max(0, e-W)..e-1 in position order, into
+ * k_out and v_out (device, act_dtype [kv_heads, n, head_dim]); *n_out = n (host). */
+dflash_status dflash_cache_read(dflash_ctx *ctx, int32_t layer, void *k_out, void *v_out, int32_t *n_out,
+                                void *stream);
+
+/* Description of the last error on ctx (never NULL), and of a status code. */
+const char *dflash_last_error(const dflash_ctx *ctx);
+const char *dflash_status_string(dflash_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

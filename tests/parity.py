@@ -1,0 +1,201 @@
+"""Lock-step driver for the GPU parity tests: the HIP path (through the C-ABI) and the CPU
+oracle advance on identical seeded inputs and are compared after every call.
+
+Acceptance rule (exact vs tolerance):
+  * drafted tokens and target argmaxes: exact wherever the oracle's top-2 logit margin
+    exceeds 1e-2; a row at or below that margin is a near tie where either index is
+    correct, so both sides continue with the oracle's value;
+  * accepted length k, bonus token, cache offsets: exact;
+  * hidden rows and live ring K/V: per-vector relative L2 error <= 1e-4 (f32 shapes) or
+    2e-2 (bf16 shapes).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from block_drafting_dflash_amd import binding, synth
+from oracle import dflash_oracle as O
+
+MARGIN = 1e-2
+
+
+def rel_rows(g: np.ndarray, o: np.ndarray) -> np.ndarray:
+    g = g.reshape(-1, g.shape[-1]).astype(np.float64)
+    o = o.reshape(-1, o.shape[-1]).astype(np.float64)
+    den = np.maximum(np.linalg.norm(o, axis=1), 1e-30)
+    return np.linalg.norm(g - o, axis=1) / den
+
+
+@dataclasses.dataclass
+class Stats:
+    rows_checked: int = 0
+    near_ties: int = 0
+    near_tie_flips: int = 0
+    max_hidden_rel: float = 0.0
+    max_window_rel: float = 0.0
+
+
+class LockStep:
+    def __init__(self, shape, weights_np, max_block: int, phase: int = 0, dev_weights=None,
+                 check_windows: bool = True):
+        self.sh = shape
+        self.dev = dev_weights if dev_weights is not None else binding.to_device(shape, weights_np)
+        self.gpu = binding.Drafter(shape, self.dev, max_block, phase)
+        self.orc = O.OracleDrafter(shape, weights_np, max_block, phase)
+        self.tol = 1e-4 if shape.act_dtype == "f32" else 2e-2
+        self.dt = binding.act_torch_dtype(shape)
+        self.stats = Stats()
+        self.check_windows = check_windows
+
+    def _t(self, a: np.ndarray) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.dt).to(self.gpu.device)
+
+    def _agree(self, got: np.ndarray, want: np.ndarray, margins: np.ndarray, what: str) -> None:
+        for i in range(len(want)):
+            self.stats.rows_checked += 1
+            if margins[i] <= MARGIN:
+                self.stats.near_ties += 1
+                self.stats.near_tie_flips += int(got[i] != want[i])
+                continue
+            assert got[i] == want[i], f"{what} row {i}: gpu {got[i]} oracle {want[i]} (margin {margins[i]:.4g})"
+
+    def check_state(self) -> None:
+        e, pend, S, C = self.gpu.cache_state()
+        oe, ospan, oS, oC = self.orc.state()
+        assert (e, pend, S, C) == (oe, ospan, oS, oC), ((e, pend, S, C), (oe, ospan, oS, oC))
+
+    def check_window(self) -> None:
+        for l in range(self.sh.layers):
+            k, v = self.gpu.cache_read(l)
+            pos, ok, ov = self.orc.live_window(l)
+            assert k.shape[1] == len(pos)
+            kr = rel_rows(k.float().cpu().numpy(), ok)
+            vr = rel_rows(v.float().cpu().numpy(), ov)
+            m = float(max(kr.max(initial=0), vr.max(initial=0)))
+            self.stats.max_window_rel = max(self.stats.max_window_rel, m)
+            assert m <= self.tol, f"layer {l} window rel err {m}"
+
+    def append(self, rows: np.ndarray, commit: bool = False) -> None:
+        self.gpu.cache_append(self._t(rows), commit=commit)
+        self.orc.append(rows, commit=commit)
+        self.check_state()
+
+    def trim(self, m: int) -> None:
+        self.gpu.cache_trim(m)
+        self.orc.trim(m)
+        self.check_state()
+        if self.check_windows:
+            torch.cuda.synchronize()
+            self.check_window()
+
+    def draft(self, anchor: int, block: int) -> np.ndarray:
+        hidden = torch.empty((block + 1, self.sh.hidden), dtype=torch.float32, device=self.gpu.device)
+        toks = self.gpu.draft_block(anchor, block, hidden=hidden)
+        res = self.orc.draft(anchor, block)
+        torch.cuda.synchronize()
+        rel = rel_rows(hidden.cpu().numpy(), res.hidden)
+        self.stats.max_hidden_rel = max(self.stats.max_hidden_rel, float(rel.max()))
+        assert rel.max() <= self.tol, f"hidden rel err {rel.max()} > {self.tol}"
+        self._agree(toks.cpu().numpy(), res.tokens, res.margins, "draft token")
+        return res.tokens
+
+    def target_argmax(self, rows: np.ndarray) -> np.ndarray:
+        idx = self.gpu.lm_head_argmax(self._t(rows))
+        oi, om = self.orc.lm_head_argmax(rows)
+        torch.cuda.synchronize()
+        self._agree(idx.cpu().numpy(), oi, om, "target argmax")
+        return oi
+
+    def verify(self, d: np.ndarray, a: np.ndarray) -> tuple:
+        B = len(d)
+        dev = self.gpu.device
+        out = self.gpu.verify_greedy(torch.tensor(d, dtype=torch.int32, device=dev),
+                                     torch.tensor(a, dtype=torch.int32, device=dev), B)
+        k, bonus = O.verify_greedy(d, a)
+        got = out.cpu().tolist()
+        assert got == [k, bonus, 0], (got, k, bonus)
+        return k, bonus
+
+
+def run_lm_head_rounds(ls: LockStep, context: int, block: int, rounds: int, anchor_tag: int = 0) -> List[int]:
+    """Prefill + rounds whose verify rows go through the shared lm_head."""
+    sh = ls.sh
+    ls.append(synth.resid_rows(sh, context, 0), commit=True)
+    if ls.check_windows:
+        torch.cuda.synchronize()
+        ls.check_window()
+    anchor = synth.anchor_token(sh, tag=anchor_tag)
+    ks = []
+    for r in range(rounds):
+        d = ls.draft(anchor, block)
+        a = ls.target_argmax(synth.verify_hidden(sh, block + 1, r))
+        k, bonus = ls.verify(d, a)
+        ls.append(synth.resid_rows(sh, block + 1, r + 1))
+        ls.trim(block - k)
+        ks.append(k)
+        anchor = bonus
+    return ks
+
+
+def _prefill(ls: LockStep, context: int) -> None:
+    ls.append(synth.resid_rows(ls.sh, context, 0), commit=True)
+    if ls.check_windows:
+        torch.cuda.synchronize()
+        ls.check_window()
+
+
+def run_synthetic_rounds(ls: LockStep, context: int, block: int, rounds: int, p: float, tag: int = 0,
+                         prefill: bool = True) -> List[int]:
+    """Rounds whose target argmaxes come from the p-accept stand-in target."""
+    sh = ls.sh
+    if prefill:
+        _prefill(ls, context)
+    anchor = synth.anchor_token(sh, tag=tag)
+    ks = []
+    for r in range(rounds):
+        d = ls.draft(anchor, block)
+        a = synth.synthetic_target_argmax(d, synth.accept_draws(block, r, tag), p, sh.vocab)
+        k, bonus = ls.verify(d, a)
+        ls.append(synth.resid_rows(sh, block + 1, 1000 * tag + r + 1))
+        ls.trim(block - k)
+        ks.append(k)
+        anchor = bonus
+    return ks
+
+
+def target_with_accept_length(d: np.ndarray, k: int, vocab: int, tail: int) -> np.ndarray:
+    """Verify-row argmaxes that accept exactly k of the drafted tokens d."""
+    B = len(d)
+    a = np.empty(B + 1, dtype=np.int64)
+    a[:k] = d[:k]
+    if k < B:
+        a[k] = (int(d[k]) + 1) % vocab
+        a[k + 1:] = tail % vocab
+    else:
+        a[B] = tail % vocab
+    return a
+
+
+def run_random_depth_rounds(ls: LockStep, context: int, block: int, rounds: int, tag: int = 0,
+                            prefill: bool = True) -> List[int]:
+    """Rounds whose accepted length is drawn uniformly from 0..block (trims of random depth)."""
+    sh = ls.sh
+    if prefill:
+        _prefill(ls, context)
+    anchor = synth.anchor_token(sh, tag=tag)
+    ks = []
+    for r in range(rounds):
+        d = ls.draft(anchor, block)
+        kk = synth.random_depth_k(block, r, tag)
+        a = target_with_accept_length(d, kk, sh.vocab, tail=anchor + 7 * r)
+        k, bonus = ls.verify(d, a)
+        assert k == kk
+        ls.append(synth.resid_rows(sh, block + 1, 1000 * tag + r + 1))
+        ls.trim(block - k)
+        ks.append(k)
+        anchor = bonus
+    return ks

@@ -1,0 +1,109 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle, element by element."""
+import numpy as np
+import pytest
+import torch
+
+from block_drafting_dflash_amd import binding, synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+# small shapes that still span several MFMA tiles and ragged tails
+MICRO_F32 = synth.Shape(hidden=256, layers=2, q_heads=4, kv_heads=2, head_dim=64, intermediate=384,
+                        vocab=1040, target_streams=3, target_width=128, window=9,
+                        weight_dtype="f32", act_dtype="f32")
+MICRO_BF16 = synth.Shape(hidden=512, layers=2, q_heads=8, kv_heads=2, head_dim=64, intermediate=768,
+                         vocab=3008, target_streams=2, target_width=256, window=20,
+                         weight_dtype="bf16", act_dtype="bf16")
+
+
+@pytest.fixture(scope="module")
+def tiny_w():
+    return synth.make_weights(synth.TINY_F32)
+
+
+@pytest.fixture(scope="module")
+def micro_f32_w():
+    return synth.make_weights(MICRO_F32)
+
+
+@pytest.fixture(scope="module")
+def micro_bf16_w():
+    return synth.make_weights(MICRO_BF16)
+
+
+def test_tiny_f32_rounds_match_oracle(tiny_w):
+    wl = synth.WORKLOADS["tiny-f32-b4-ctx64"]
+    ls = P.LockStep(wl.shape, tiny_w, max_block=4)
+    P.run_lm_head_rounds(ls, wl.context, 4, wl.rounds)
+    assert ls.stats.max_hidden_rel <= 1e-4
+    print("tiny-f32 stats", ls.stats)
+
+
+@pytest.mark.parametrize("block,phase", [(1, 0), (3, 5), (8, -1)])
+def test_micro_f32_synthetic_accept(micro_f32_w, block, phase):
+    C = MICRO_F32.window + max(min(max(8 * block, 32), 128), block)
+    ls = P.LockStep(MICRO_F32, micro_f32_w, max_block=block, phase=phase % C)
+    ks = P.run_synthetic_rounds(ls, 23, block, 12, p=0.7, tag=block)
+    assert any(k > 0 for k in ks)
+
+
+@pytest.mark.parametrize("block,phase,context", [(4, 0, 50), (16, 3, 7), (17, 60, 33), (40, 0, 100)])
+def test_micro_bf16_random_depth(micro_bf16_w, block, phase, context):
+    ls = P.LockStep(MICRO_BF16, micro_bf16_w, max_block=block, phase=phase)
+    P.run_random_depth_rounds(ls, context, block, 10, tag=block)
+    print("micro-bf16 stats", block, ls.stats)
+
+
+def test_lm_head_argmax_is_width_invariant(micro_bf16_w):
+    sh = MICRO_BF16
+    dev = binding.to_device(sh, micro_bf16_w)
+    g = binding.Drafter(sh, dev, max_block=4)
+    rows = torch.from_numpy(synth.verify_hidden(sh, 40, 0)).to(torch.bfloat16).cuda()
+    full = g.lm_head_argmax(rows).cpu()
+    for w in (1, 4, 5, 16, 17, 33):
+        part = torch.cat([g.lm_head_argmax(rows[i:i + w].contiguous()).cpu() for i in range(0, 40, w)])
+        assert torch.equal(part, full), w
+
+
+def test_draft_is_bit_reproducible(micro_bf16_w):
+    sh = MICRO_BF16
+    dev = binding.to_device(sh, micro_bf16_w)
+    outs = []
+    for _ in range(2):
+        g = binding.Drafter(sh, dev, max_block=8)
+        g.cache_append(torch.from_numpy(synth.resid_rows(sh, 30, 0)).to(torch.bfloat16).cuda(), commit=True)
+        h = torch.empty((9, sh.hidden), dtype=torch.float32, device="cuda")
+        t = g.draft_block(5, 8, hidden=h)
+        outs.append((t.cpu(), h.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_boundary_errors_leave_state_unchanged(micro_f32_w):
+    sh = MICRO_F32
+    g = binding.Drafter(sh, binding.to_device(sh, micro_f32_w), max_block=4)
+    with pytest.raises(binding.DFlashError) as e:
+        g.draft_block(1, 4)
+    assert e.value.status == 4  # no context
+    g.cache_append(torch.from_numpy(synth.resid_rows(sh, 12, 0)).cuda(), commit=True)
+    st = g.cache_state()
+    for call, status in [(lambda: g.draft_block(1, 5), 3), (lambda: g.draft_block(1, 0), 3),
+                         (lambda: g.draft_block(sh.vocab, 2), 3), (lambda: g.cache_trim(1), 5)]:
+        with pytest.raises(binding.DFlashError) as e:
+            call()
+        assert e.value.status == status
+        assert g.cache_state() == st
+    g.cache_append(torch.from_numpy(synth.resid_rows(sh, 3, 1)).cuda())
+    with pytest.raises(binding.DFlashError) as e:
+        g.draft_block(1, 2)
+    assert e.value.status == 6
+    with pytest.raises(binding.DFlashError) as e:
+        g.cache_trim(4)
+    assert e.value.status == 5
+    g.cache_trim(2)
+    assert g.cache_state()[:2] == (13, 0)
+    # out-of-range target ids are reported by the verify status word
+    out = g.verify_greedy(torch.tensor([1, 2], dtype=torch.int32, device="cuda"),
+                          torch.tensor([1, sh.vocab, 0], dtype=torch.int32, device="cuda"), 2)
+    assert out.cpu().tolist() == [0, -1, 1]
