@@ -1,0 +1,259 @@
+"""Throughput of one DFlash speculative round at batch 1 on one MI355X.
+
+A step is one whole round over one block of synthetic input: the drafter's block forward
+(dflash_draft_block), the target verify rows through the shared lm_head
+(dflash_lm_head_argmax), greedy verify (dflash_verify_greedy), the append of the B+1
+verify residual rows (dflash_cache_append), one device->host copy of (k, bonus) and the
+trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts.
+
+Workload (timed as `value`): muse-bf16-b4-ctx1024 -- Muse-assistant-shaped bf16 drafter
+(hidden 2048, 5 layers, 32/4 heads x 128, intermediate 6144, vocab 202048, untied lm_head,
+fc 20480 -> 2048), context 1024, window 2048, block 4, verify rows N(0,1) through the
+lm_head. Also reported: the block-16 round (muse-bf16-b16-ctx4096, p = 0.6 synthetic
+target) and the CPU oracle timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
+    """Algorithmic bytes of one round: every weight read once, live K/V window, inputs."""
+    e = 2  # bf16
+    H, I, V, F = sh.hidden, sh.intermediate, sh.vocab, sh.fc_in
+    qd, kvd = sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim
+    layer = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * e
+    fc = H * F * e
+    lm = V * H * e
+    kv = sh.layers * 2 * min(ctx_visible, sh.window) * kvd * e
+    inputs = (block + 1) * F * e + (block + 1) * H * e
+    fwd = fc + sh.layers * layer + lm + kv + inputs
+    return {"fc": fc, "layers": sh.layers * layer, "lm_head": lm, "kv": kv, "block_forward": fwd,
+            "round_lm_verify": fwd + lm + (block + 1) * H * e}
+
+
+def run_gpu(args):
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    if not os.path.exists(binding.LIB_PATH):
+        from block_drafting_dflash_amd import build as _b
+        _b.build()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    wl = synth.WORKLOADS["muse-bf16-b4-ctx1024"]
+    sh = wl.shape
+    t0 = time.time()
+    weights = synth.make_weights(sh)
+    dw = binding.to_device(sh, weights)
+    torch.cuda.synchronize()
+    print(f"[bench] weights generated and resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    # ---------------- block 4, verify rows through the shared lm_head ------------------
+    B = 4
+    g = binding.Drafter(sh, dw, max_block=B)
+    g.cache_append(torch.from_numpy(synth.resid_rows(sh, wl.context, 0)).to(torch.bfloat16).to(dev), commit=True)
+    n = args.warmup + args.steps
+    vrows = torch.from_numpy(np.stack([synth.verify_hidden(sh, B + 1, r) for r in range(n)])).to(torch.bfloat16).to(dev)
+    resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, r + 1) for r in range(n)])).to(torch.bfloat16).to(dev)
+    toks = torch.empty(B, dtype=torch.int32, device=dev)
+    a = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    vout = torch.empty(3, dtype=torch.int32, device=dev)
+    host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    anchor = synth.anchor_token(sh)
+    ks = []
+    torch.cuda.synchronize()
+    t_start = None
+    for r in range(n):
+        if r == args.warmup:
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+        e = ev[r - args.warmup] if r >= args.warmup else None
+        if e: e[0].record(stream)
+        g.draft_block(anchor, B, tokens=toks)
+        if e: e[1].record(stream)
+        g.lm_head_argmax(vrows[r], out=a)
+        if e: e[2].record(stream)
+        g.verify_greedy(toks, a, B, out=vout)
+        if e: e[3].record(stream)
+        g.cache_append(resid[r])
+        if e: e[4].record(stream)
+        host.copy_(vout, non_blocking=True)
+        stream.synchronize()
+        k, bonus, status = host.tolist()
+        assert status == 0
+        g.cache_trim(B - k)
+        anchor = bonus
+        ks.append(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_draft = [x[0].elapsed_time(x[1]) for x in ev]
+    ms_lm = [x[1].elapsed_time(x[2]) for x in ev]
+    ms_append = [x[3].elapsed_time(x[4]) for x in ev]
+    e_end = g.cache_state()[0]
+    by = alg_bytes(sh, B, e_end)
+    rounds_s = args.steps / elapsed
+    lm_ms = float(np.mean(ms_lm))
+    fwd_ms = float(np.mean(ms_draft) + np.mean(ms_append))
+    res = {
+        "rounds_per_s": rounds_s, "ms_per_step": 1e3 * elapsed / args.steps, "drafted_tok_s": rounds_s * B,
+        "round_hbm_frac": by["round_lm_verify"] * rounds_s / (HBM_PEAK_GBS * 1e9),
+        "drafted_tok_s_hbm_frac": by["round_lm_verify"] * rounds_s / (HBM_PEAK_GBS * 1e9),
+        "block_forward_ms": fwd_ms, "block_forward_per_s": 1e3 / fwd_ms,
+        "block_forward_hbm_frac": by["block_forward"] / (fwd_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "draft_ms": float(np.mean(ms_draft)), "append_ms": float(np.mean(ms_append)),
+        "lm_head_ms": lm_ms, "lm_head_gbs": by["lm_head"] / (lm_ms * 1e-3) / 1e9,
+        "mean_accepted": float(np.mean(ks[args.warmup:])), "bytes": by,
+    }
+
+    # ---------------- block 16, p = 0.6 synthetic target --------------------------------
+    b16 = None
+    if args.block16_steps > 0:
+        wl2 = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
+        B2 = 16
+        del g
+        g2 = binding.Drafter(sh, dw, max_block=B2)
+        g2.cache_append(torch.from_numpy(synth.resid_rows(sh, wl2.context, 0)).to(torch.bfloat16).to(dev), commit=True)
+        n2 = args.warmup + args.block16_steps
+        resid2 = torch.from_numpy(np.stack([synth.resid_rows(sh, B2 + 1, 1000 + r) for r in range(n2)])).to(torch.bfloat16).to(dev)
+        u = torch.from_numpy(np.stack([synth.accept_draws(B2, r) for r in range(n2)])).to(dev)  # float64 [n2, 3, B2+1]
+        toks2 = torch.empty(B2, dtype=torch.int32, device=dev)
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.block16_steps)]
+        anchor = synth.anchor_token(sh)
+        V = sh.vocab
+        ks2 = []
+        torch.cuda.synchronize()
+        for r in range(n2):
+            if r == args.warmup:
+                torch.cuda.synchronize()
+                t2 = time.perf_counter()
+            e = ev2[r - args.warmup] if r >= args.warmup else None
+            if e: e[0].record(stream)
+            g2.draft_block(anchor, B2, tokens=toks2)
+            if e: e[1].record(stream)
+            # stand-in for the target's verify-row argmaxes (the target model is out of scope)
+            d = toks2.long()
+            other = (d + 1 + torch.floor(u[r, 1, :B2] * (V - 1)).long()) % V
+            tgt = torch.empty(B2 + 1, dtype=torch.int32, device=dev)
+            tgt[:B2] = torch.where(u[r, 0, :B2] < wl2.accept_p, d, other).int()
+            tgt[B2] = torch.floor(u[r, 2, B2] * V).int() % V
+            g2.verify_greedy(toks2, tgt, B2, out=vout)
+            if e: e[2].record(stream)
+            g2.cache_append(resid2[r])
+            if e: e[3].record(stream)
+            host.copy_(vout, non_blocking=True)
+            stream.synchronize()
+            k, bonus, status = host.tolist()
+            assert status == 0
+            g2.cache_trim(B2 - k)
+            anchor = bonus
+            ks2.append(k)
+        torch.cuda.synchronize()
+        el2 = time.perf_counter() - t2
+        by2 = alg_bytes(sh, B2, g2.cache_state()[0])
+        rs2 = args.block16_steps / el2
+        fwd2 = float(np.mean([x[0].elapsed_time(x[1]) + x[2].elapsed_time(x[3]) for x in ev2]))
+        b16 = {"workload": wl2.name, "rounds_per_s": rs2, "drafted_tok_s": rs2 * B2,
+               "round_hbm_frac": by2["block_forward"] * rs2 / (HBM_PEAK_GBS * 1e9),
+               "block_forward_ms": fwd2,
+               "block_forward_hbm_frac": by2["block_forward"] / (fwd2 * 1e-3) / (HBM_PEAK_GBS * 1e9),
+               "mean_accepted": float(np.mean(ks2[args.warmup:])), "steps": args.block16_steps}
+    return sh, weights, res, b16
+
+
+def cpu_baseline(sh, weights, budget_s: float) -> dict:
+    """The oracle as it stands, timed on the host cores over a bounded sample of rounds."""
+    from block_drafting_dflash_amd import synth
+    from oracle import dflash_oracle as O
+
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    B = 4
+    od = O.OracleDrafter(sh, weights, B)
+    t0 = time.time()
+    od.append(synth.resid_rows(sh, 1024, 0), commit=True)
+    od.draft(0, B)  # warms the f64 weight cache (not timed)
+    od.lm_head_argmax(synth.verify_hidden(sh, B + 1, 0))
+    setup = time.time() - t0
+    anchor = synth.anchor_token(sh)
+    done = 0
+    t1 = time.perf_counter()
+    while True:
+        d = od.draft(anchor, B).tokens
+        a, _ = od.lm_head_argmax(synth.verify_hidden(sh, B + 1, done))
+        k, bonus = O.verify_greedy(d, a)
+        od.append(synth.resid_rows(sh, B + 1, done + 1))
+        od.trim(B - k)
+        anchor = bonus
+        done += 1
+        if time.perf_counter() - t1 > budget_s or done >= 50:
+            break
+    el = time.perf_counter() - t1
+    return {"value": done / el, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} full block-4 rounds (draft, verify lm_head, verify, append, trim) of "
+                      f"muse-bf16-b4-ctx1024 after an untimed 1024-row prefill and f64 weight "
+                      f"conversion ({setup:.1f}s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--block16-steps", type=int, default=320)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the round at batch 1 is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    sh, weights, res, b16 = run_gpu(args)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(sh, weights, args.cpu_budget)
+    line = {
+        "metric": "DFlash rounds/s at block 4 (B=1), with drafted tok/s and % of HBM roofline",
+        "value": round(res["rounds_per_s"], 2), "unit": "rounds/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) residual/verify rows)",
+        "config": {"workload": "muse-bf16-b4-ctx1024", "block": 4, "context": 1024, "window": 2048,
+                   "hidden": 2048, "layers": 5, "vocab": 202048},
+        "drafted_tok_s": round(res["drafted_tok_s"], 1),
+        "round_hbm_frac": round(res["round_hbm_frac"], 4),
+        "block_forward": {"ms": round(res["block_forward_ms"], 4), "per_s": round(res["block_forward_per_s"], 1),
+                          "hbm_frac": round(res["block_forward_hbm_frac"], 4),
+                          "draft_ms": round(res["draft_ms"], 4), "append_ms": round(res["append_ms"], 4)},
+        "roofline": {"bound": "hbm", "kernel": "lm_head argmax GEMM (202048x2048 bf16, 5 verify rows)",
+                     "achieved": round(res["lm_head_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(res["lm_head_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(res["lm_head_ms"], 5)},
+        "block16": b16,
+        "cpu_baseline": cpu,
+        "mean_accepted": res["mean_accepted"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,8 +60,8 @@ def lib() -> ctypes.CDLL:
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     P = ctypes.POINTER
     sig = {
-        "dflash_query_sizes": (i32, [P(dflash_config), P(sz), P(sz)]),
-        "dflash_create": (i32, [P(dflash_config), P(dflash_weights), vp, sz, vp, sz, vp, P(vp)]),
+        "dflash_query_sizes": (i32, [P(dflash_config), P(sz), P(sz), P(sz)]),
+        "dflash_create": (i32, [P(dflash_config), P(dflash_weights), vp, sz, vp, sz, vp, sz, vp, P(vp)]),
         "dflash_destroy": (None, [vp]),
         "dflash_cache_append": (i32, [vp, vp, i32, i32, vp]),
         "dflash_cache_trim": (i32, [vp, i32]),
@@ -73,7 +73,7 @@ def lib() -> ctypes.CDLL:
         "dflash_last_error": (ctypes.c_char_p, [vp]),
         "dflash_status_string": (ctypes.c_char_p, [i32]),
     }
-    for name, (res, args) in sig.items():
+    for name, (res, args) in sig.items():  # every symbol include/dflash.h declares
         fn = getattr(L, name)
         fn.restype = res
         fn.argtypes = args
@@ -135,10 +135,10 @@ def to_device(shape, weights: Dict[str, object], device="cuda") -> Dict[str, obj
     return out
 
 
-def query_sizes(cfg: dflash_config) -> Tuple[int, int]:
-    rb, wb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib().dflash_query_sizes(ctypes.byref(cfg), ctypes.byref(rb), ctypes.byref(wb)), None)
-    return rb.value, wb.value
+def query_sizes(cfg: dflash_config) -> Tuple[int, int, int]:
+    rb, wb, pb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().dflash_query_sizes(ctypes.byref(cfg), ctypes.byref(rb), ctypes.byref(wb), ctypes.byref(pb)), None)
+    return rb.value, wb.value, pb.value
 
 
 class Drafter:
@@ -169,12 +169,14 @@ class Drafter:
         self.weights = dflash_weights(_ptr(dev_weights["embed"]), lin("lm_head"), lin("fc"),
                                       _ptr(dev_weights["enc_norm"]), _ptr(dev_weights["final_norm"]),
                                       ctypes.cast(layers, ctypes.POINTER(dflash_layer)))
-        ring_b, ws_b = query_sizes(self.cfg)
+        ring_b, ws_b, pk_b = query_sizes(self.cfg)
         self.ring = torch.empty(max(ring_b, 256), dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=self.device)
+        self.packed = torch.empty(max(pk_b, 256), dtype=torch.uint8, device=self.device)
         h = ctypes.c_void_p()
         _check(L.dflash_create(ctypes.byref(self.cfg), ctypes.byref(self.weights), _ptr(self.ring), ring_b,
-                               _ptr(self.workspace), ws_b, _stream(stream), ctypes.byref(h)), None)
+                               _ptr(self.workspace), ws_b, _ptr(self.packed), pk_b, _stream(stream),
+                               ctypes.byref(h)), None)
         self.ctx = h
         self.act_dtype = act_torch_dtype(shape)
 

@@ -212,6 +212,144 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
   }
 }
 
+// ---- attention on MFMA (bf16 operands): one work-group per (128-key chunk, kv head) -------
+// Scores are formed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, K rows from LDS, Q rows
+// from L2), so each lane ends up holding 4 keys x 1 query: exactly the B-operand layout of
+// the 16x16x16 MFMA that forms O^T = V^T P^T. P (in [0, 1]) enters as a bf16 pair
+// hi + lo, which keeps about 16 significant bits; V and K are bf16 already, products are
+// exact and sums are f32. Each wave owns query tiles w, w+4, ...
+constexpr int AM_CH = 128;  // keys per work-group
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
+                                                        const uint16_t* __restrict__ qb, const uint16_t* __restrict__ kb,
+                                                        const uint16_t* __restrict__ vb, int R, int64_t e, int nchunks,
+                                                        float* __restrict__ part) {
+  constexpr int KST = HD + 8;      // K row stride (elements): rows land 4 banks apart
+  constexpr int VST = AM_CH + 4;   // V^T row stride (elements)
+  __shared__ __align__(16) uint16_t Kl[AM_CH * KST];
+  __shared__ __align__(16) uint16_t Vt[HD * VST];
+  __shared__ int64_t kpos[AM_CH];
+  const int g = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int G = a.nq / a.nkv, NQ = R * G;
+  const int64_t lo = e > a.window ? e - a.window : 0;
+  const int nctx = (int)(e - lo);
+  const int nkeys = nctx + R;
+  const int k0 = c * AM_CH;
+  const int kn = min(AM_CH, nkeys - k0);
+  const size_t plane = (size_t)a.cap * HD;
+  const uint16_t* Kr = ring_layer + (size_t)g * plane;
+  const uint16_t* Vr = ring_layer + (size_t)(a.nkv + g) * plane;
+
+  constexpr int SEGS = HD / 8;  // 16-byte segments per row
+  for (int it = tid; it < AM_CH * SEGS; it += blockDim.x) {
+    const int kj = it / SEGS, sg = it - kj * SEGS;
+    u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (kj < kn) {
+      const int key = k0 + kj;
+      if (key < nctx) {
+        const size_t off = (size_t)((lo + key + a.phase) % a.cap) * HD + 8 * sg;
+        kv = *(const u32x4_t*)(Kr + off);
+        vv = *(const u32x4_t*)(Vr + off);
+      } else {
+        const size_t off = ((size_t)(key - nctx) * a.nkv + g) * HD + 8 * sg;
+        kv = *(const u32x4_t*)(kb + off);
+        vv = *(const u32x4_t*)(vb + off);
+      }
+    }
+    *(u32x4_t*)&Kl[kj * KST + 8 * sg] = kv;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) Vt[(8 * sg + t) * VST + kj] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
+  }
+  for (int kj = tid; kj < AM_CH; kj += blockDim.x) {
+    const int key = k0 + kj;
+    kpos[kj] = key < nctx ? lo + key : e + (key - nctx);
+  }
+  __syncthreads();
+
+  const float scale = 1.0f / sqrtf((float)HD);
+  const int nqt = (NQ + 15) / 16;
+  for (int qt = w; qt < nqt; qt += 4) {
+    const int qv = qt * 16 + li;
+    const bool qok = qv < NQ;
+    const int r = qok ? qv / G : 0, hh = qv - r * G;
+    const int64_t qpos = e + r;
+    u32x4_t qf[HD / 32];
+    const uint16_t* qrow = qb + ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s) {
+      qf[s] = u32x4_t{0u, 0u, 0u, 0u};
+      if (qok) qf[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * lg);
+    }
+    f32x4_t S[AM_CH / 16];
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < AM_CH / 16; ++kt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < HD / 32; ++s) {
+        const u32x4_t kf = *(const u32x4_t*)&Kl[(kt * 16 + li) * KST + 32 * s + 8 * lg];
+        acc = mfma_bf16(kf, qf[s], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kj = kt * 16 + 4 * lg + i;
+        const int64_t kp = kpos[kj];
+        const int64_t dist = qpos > kp ? qpos - kp : kp - qpos;
+        const bool vis = qok && kj < kn && dist <= a.window;
+        S[kt][i] = vis ? acc[i] * scale : -INFINITY;
+        m = fmaxf(m, S[kt][i]);
+      }
+    }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < AM_CH / 16; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = S[kt][i] == -INFINITY ? 0.f : expf(S[kt][i] - m);
+        S[kt][i] = pv;
+        l += pv;
+      }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    f32x4_t O[HD / 16];
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < AM_CH / 16; ++kt) {
+      s16x4_t phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t h = f2bf(S[kt][i]);
+        phi[i] = (short)h;
+        plo[i] = (short)f2bf(S[kt][i] - bf2f(h));
+      }
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt) {
+        const s16x4_t vf = *(const s16x4_t*)&Vt[(dt * 16 + li) * VST + kt * 16 + 4 * lg];
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, phi, O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, plo, O[dt], 0, 0, 0);
+      }
+    }
+    if (qok) {
+      float* dst = part + (((size_t)g * nchunks + c) * NQ + qv) * (HD + 2);
+#pragma unroll
+      for (int dt = 0; dt < HD / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * lg + i] = O[dt][i];
+      if (lg == 0) {
+        dst[HD] = m;
+        dst[HD + 1] = l;
+      }
+    }
+  }
+}
+
 // ---- combine chunks in chunk order --------------------------------------------------------
 // One work-group (hd threads) per (row, query head); out: act [R, nq*hd].
 template <bool BF>
@@ -276,10 +414,13 @@ hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const 
   return hipGetLastError();
 }
 
-static int attn_nchunks(const AttnShape& a, int R, int64_t e) {
+static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
+
+static int attn_nchunks(int bf, const AttnShape& a, int R, int64_t e) {
   const int64_t lo = e > a.window ? e - a.window : 0;
   const int nkeys = (int)(e - lo) + R;
-  return (nkeys + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  const int ch = use_mfma(bf, a) ? AM_CH : ATTN_CHUNK;
+  return (nkeys + ch - 1) / ch;
 }
 
 size_t attention_partial_floats(const AttnShape& a, int R) {
@@ -289,10 +430,23 @@ size_t attention_partial_floats(const AttnShape& a, int R) {
 
 hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* kb,
                             const void* vb, int R, int64_t e, float* part, void* out, hipStream_t s) {
-  const int nch = attn_nchunks(a, R, e);
+  const int nch = attn_nchunks(bf, a, R, e);
+  dim3 grid(nch, a.nkv);
+  if (use_mfma(bf, a)) {
+    const uint16_t* rl = (const uint16_t*)ring_layer;
+    if (a.hd == 128)
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)kb,
+                         (const uint16_t*)vb, R, e, nch, part);
+    else
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)kb,
+                         (const uint16_t*)vb, R, e, nch, part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
+    return hipGetLastError();
+  }
   const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4 +
                      ATTN_CHUNK * 8;
-  dim3 grid(nch, a.nkv);
   const void* fn = bf ? (const void*)attn_partial_kernel<true> : (const void*)attn_partial_kernel<false>;
   static bool attr_set[2] = {false, false};
   hipError_t err = hipSuccess;

@@ -21,7 +21,6 @@ using namespace dflash;
 namespace {
 
 constexpr int MAX_BLOCK_LIMIT = 256;
-constexpr int ARGMAX_GRID = 1024;
 
 struct Lin {
   const void *w, *s, *b;
@@ -63,6 +62,7 @@ struct dflash_ctx {
   std::vector<Layer> layers;
   unsigned char* ring;
   unsigned char* ws;
+  int cus = 256;        // compute units of the device the context was created on
   int64_t e = 0;        // committed context end (absolute position)
   int64_t pending = 0;  // rows appended since the last trim
   char err[512] = {0};
@@ -92,13 +92,42 @@ dflash_status cfg_fail(char* buf, dflash_status st, const char* fmt, ...) {
 
 int kstep(int wt) { return wt == WT_F32 ? 16 : 32; }
 
-// waves per work-group for a contraction of length K: the largest count <= 8 that splits
-// K into whole 8-step chunks. It depends on K only, never on the row count.
-int gemm_waves(int wt, int K) {
-  const int units = K / (chunk_steps(1) * kstep(wt));
-  for (int w = 8; w >= 1; --w)
-    if (units % w == 0) return w;
-  return 1;
+constexpr int ARGMAX_WAVES = 4;
+constexpr int ARGMAX_T[] = {1, 4, 8, 17, 25};
+constexpr int CHUNK_STEPS = 8;
+
+// Launch plan of a GEMM with contraction length K. Waves and chunking depend on K only.
+bool plan_gemm(int wt, int epi, int K, GemmPlan* pl) {
+  const int ks = kstep(wt);
+  if (epi == EPI_ARGMAX) {
+    if (K % (ARGMAX_WAVES * ks)) return false;
+    const int steps = K / (ARGMAX_WAVES * ks);
+    if (steps != 4 && steps != 8 && steps != 16) return false;
+    *pl = GemmPlan{ARGMAX_WAVES, steps, 1, 1, 0};
+    return gemm_plan_supported(*pl, epi);
+  }
+  if (K % (CHUNK_STEPS * ks)) return false;
+  const int units = K / (CHUNK_STEPS * ks);
+  for (int w = 8; w >= 1; --w) {
+    if (units % w) continue;
+    GemmPlan p{w, CHUNK_STEPS, units / w, 1, 0};
+    if (gemm_plan_supported(p, epi)) {
+      *pl = p;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Tiles per work-group of an argmax launch: the fewest that keep the whole grid resident
+// (about 200 VGPRs per lane leave 2 four-wave work-groups per CU; LDS may allow fewer).
+int argmax_tiles_per_wg(int ntiles, size_t lds, int cus, int rt) {
+  const int by_vgpr = rt == 1 ? 2 : 1;
+  const int by_lds = (int)std::max<size_t>(1, (size_t)LDS_BYTES / std::max<size_t>(lds, 1));
+  const int resident = cus * std::min(by_vgpr, by_lds);
+  for (int t : ARGMAX_T)
+    if ((ntiles + t - 1) / t <= resident) return t;
+  return ARGMAX_T[sizeof(ARGMAX_T) / sizeof(int) - 1];
 }
 
 dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
@@ -138,8 +167,15 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
     if (k % unit) return cfg_fail(err, DFLASH_E_SHAPE, "hidden, intermediate, q_heads*head_dim and fc width must be multiples of %d", unit);
   if (H % 16 || c->intermediate % 16 || qd % 16 || kvd % 16)
     return cfg_fail(err, DFLASH_E_SHAPE, "output dimensions must be multiples of 16");
-  // the LDS-staged norm prologue must fit at least 16 rows of hidden
-  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden + 16 / (bf ? 2 : 4)) > (size_t)LDS_BYTES)
+  // every contraction of the round needs a launch plan, and the LDS-staged norm prologue
+  // must fit at least 16 rows of hidden
+  GemmPlan pl;
+  const struct { int epi; int64_t K; } gemms[] = {{EPI_STORE, H}, {EPI_RESID, qd}, {EPI_SWIGLU, H},
+                                                  {EPI_RESID, c->intermediate}, {EPI_STORE, fin}, {EPI_ARGMAX, H}};
+  for (const auto& gm : gemms)
+    if (!plan_gemm(wt, gm.epi, (int)gm.K, &pl))
+      return cfg_fail(err, DFLASH_E_SHAPE, "no GEMM launch plan for a contraction of length %lld", (long long)gm.K);
+  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden + 16 / (bf ? 2 : 4), 1) > (size_t)LDS_BYTES)
     return cfg_fail(err, DFLASH_E_SHAPE, "hidden too large for the staged operand");
   Cfg g;
   g.c = *c;
@@ -196,6 +232,38 @@ size_t ring_bytes_of(const Cfg& g) {
   return (size_t)g.act_elt * g.c.layers * 2 * g.c.kv_heads * (size_t)g.C * g.c.head_dim;
 }
 
+// Fragment-major copies of every linear live in the caller's packed buffer, in this order:
+// fc, lm_head, then per layer q, k, v, o, gate, up, down.
+struct PackedLayout {
+  size_t total = 0;
+  std::vector<size_t> off;  // byte offset of each linear, in the order above
+};
+
+size_t linear_bytes(const Cfg& g, int64_t N, int64_t K) { return (size_t)N * K * (g.wt == WT_F32 ? 4 : 2); }
+
+PackedLayout make_packed_layout(const Cfg& g) {
+  const dflash_config& c = g.c;
+  const int64_t H = c.hidden, qd = (int64_t)c.q_heads * c.head_dim, kvd = (int64_t)c.kv_heads * c.head_dim;
+  const int64_t F = (int64_t)c.target_streams * c.target_width, I = c.intermediate;
+  PackedLayout P;
+  auto add = [&](int64_t N, int64_t K) {
+    P.off.push_back(P.total);
+    P.total = align256(P.total + linear_bytes(g, N, K));
+  };
+  add(H, F);
+  add(c.vocab, H);
+  for (int l = 0; l < c.layers; ++l) {
+    add(qd, H);
+    add(kvd, H);
+    add(kvd, H);
+    add(H, qd);
+    add(I, H);
+    add(I, H);
+    add(H, I);
+  }
+  return P;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 dflash_status dev(dflash_ctx* ctx, hipError_t e, const char* what) {
@@ -220,19 +288,22 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
   const Cfg& g = ctx->cfg;
   const int wt = g.wt;
   const int nb = gc.epi == EPI_SWIGLU ? 2 : 1;
-  const int waves = gemm_waves(wt, gc.K);
+  GemmPlan plan;
+  if (!plan_gemm(wt, gc.epi, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
+  const int waves = plan.waves;
   const int xstride = gc.K + 16 / g.act_elt;
   const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;
   const size_t y_elt = gc.epi == EPI_SWIGLU ? g.act_elt : 4;
   int N = 0;
   for (const auto& s : gc.segs) N = std::max(N, s.col0 + s.rows);
-  if (nb == 2) N = gc.segs[0].rows;
   int r0 = 0;
   while (r0 < rows) {
     int rc = std::min(rows - r0, GEMM_MAX_ROWS);
-    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, 16 * waves);  // one finishing wave per row tile
+    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, 32);  // two row tiles, one finishing wave each
     if (gc.xsrc != XSRC_GLOBAL)
-      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride) > (size_t)LDS_BYTES) --rc;
+      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride, gc.epi == EPI_ARGMAX ? 2 : 1) >
+                           (size_t)LDS_BYTES)
+        --rc;
     GemmParams p{};
     for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
     p.nseg = (int)gc.segs.size();
@@ -240,27 +311,30 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
     p.K = gc.K;
     p.R = rc;
     p.waves = waves;
-    p.nchunks = gc.K / (waves * chunk_steps((rc + 15) / 16) * kstep(wt));
     p.x = (const unsigned char*)gc.x + (size_t)r0 * gc.ldx * x_elt;
     p.ldx = gc.ldx;
     p.gain = gc.gain;
     p.eps = g.c.rms_eps;
     p.xstride = xstride;
-    int grid = p.ntiles;
+    GemmPlan pl = plan;
+    pl.grid = p.ntiles;
     if (gc.epi == EPI_ARGMAX) {
       p.keys = (unsigned long long*)(ctx->ws + ctx->lay.keys);
       p.ticket = (unsigned int*)(ctx->ws + ctx->lay.ticket);
       p.idx_out = gc.idx + r0;
-      grid = std::min(p.ntiles, ARGMAX_GRID);
+      const size_t lds = gemm_lds_bytes(wt, gc.xsrc, rc, waves, 1, xstride, 2);
+      pl.tiles_per_wg = argmax_tiles_per_wg(p.ntiles, lds, ctx->cus, (rc + 15) / 16);
+      pl.grid = (p.ntiles + pl.tiles_per_wg - 1) / pl.tiles_per_wg;
     } else {
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
       p.ldy = gc.ldy;
     }
-    const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, p, grid, st);
+    const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, pl, p, st);
     if (le != hipSuccess)
-      return fail(ctx, DFLASH_E_DEVICE, "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, grid %d, lds %zu): %s",
-                  gc.epi, gc.xsrc, gc.K, rc, p.ntiles, waves, grid,
-                  gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride), hipGetErrorString(le));
+      return fail(ctx, DFLASH_E_DEVICE,
+                  "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, ch %d x %d, tiles/wg %d, grid %d): %s",
+                  gc.epi, gc.xsrc, gc.K, rc, p.ntiles, waves, pl.ch, pl.nch, pl.tiles_per_wg, pl.grid,
+                  hipGetErrorString(le));
     r0 += rc;
   }
   return DFLASH_OK;
@@ -289,18 +363,21 @@ const char* dflash_status_string(dflash_status s) {
 
 const char* dflash_last_error(const dflash_ctx* ctx) { return ctx ? ctx->err : g_create_err; }
 
-dflash_status dflash_query_sizes(const dflash_config* cfg, size_t* ring_bytes, size_t* workspace_bytes) {
+dflash_status dflash_query_sizes(const dflash_config* cfg, size_t* ring_bytes, size_t* workspace_bytes,
+                                 size_t* packed_bytes) {
   Cfg g;
   dflash_status s = check_cfg(cfg, &g, g_create_err);
   if (s != DFLASH_OK) return s;
-  if (!ring_bytes || !workspace_bytes) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL size output");
+  if (!ring_bytes || !workspace_bytes || !packed_bytes) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL size output");
   *ring_bytes = ring_bytes_of(g);
   *workspace_bytes = make_layout(g).total;
+  *packed_bytes = make_packed_layout(g).total;
   return DFLASH_OK;
 }
 
 dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts, void* ring, size_t ring_bytes,
-                            void* workspace, size_t workspace_bytes, void* stream, dflash_ctx** out) {
+                            void* workspace, size_t workspace_bytes, void* packed, size_t packed_bytes, void* stream,
+                            dflash_ctx** out) {
   g_create_err[0] = 0;
   if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
   *out = nullptr;
@@ -308,12 +385,13 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   dflash_status s = check_cfg(cfg, &g, g_create_err);
   if (s != DFLASH_OK) return s;
   if (!wts || !wts->layers) return cfg_fail(g_create_err, DFLASH_E_ARG, "weights or layer array is NULL");
-  if (!ring || !workspace) return cfg_fail(g_create_err, DFLASH_E_ARG, "ring or workspace is NULL");
-  if (((uintptr_t)ring & 255u) || ((uintptr_t)workspace & 255u))
-    return cfg_fail(g_create_err, DFLASH_E_ARG, "ring and workspace must be 256-byte aligned");
+  if (!ring || !workspace || !packed) return cfg_fail(g_create_err, DFLASH_E_ARG, "ring, workspace or packed is NULL");
+  if (((uintptr_t)ring & 255u) || ((uintptr_t)workspace & 255u) || ((uintptr_t)packed & 255u))
+    return cfg_fail(g_create_err, DFLASH_E_ARG, "ring, workspace and packed must be 256-byte aligned");
   const Layout lay = make_layout(g);
-  if (ring_bytes < ring_bytes_of(g) || workspace_bytes < lay.total)
-    return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring or workspace smaller than dflash_query_sizes");
+  const PackedLayout pk = make_packed_layout(g);
+  if (ring_bytes < ring_bytes_of(g) || workspace_bytes < lay.total || packed_bytes < pk.total)
+    return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring, workspace or packed smaller than dflash_query_sizes");
   auto lin_ok = [&](const dflash_linear& l) { return l.w && aligned16(l.w); };
   if (!wts->embed || !wts->enc_norm || !wts->final_norm || !lin_ok(wts->lm_head) || !lin_ok(wts->fc))
     return cfg_fail(g_create_err, DFLASH_E_ARG, "a top-level weight is NULL or not 16-byte aligned");
@@ -343,9 +421,42 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   }
   ctx->ring = (unsigned char*)ring;
   ctx->ws = (unsigned char*)workspace;
+  {
+    int dev_id = 0, cus = 0;
+    if (hipGetDevice(&dev_id) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id) == hipSuccess && cus > 0)
+      ctx->cus = cus;
+  }
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hipMemcpyAsync(ctx->ws + lay.knorm_ptrs, knorms.data(), sizeof(void*) * knorms.size(),
-                                hipMemcpyHostToDevice, st);
+  // repack every linear into fragment-major blocks; the context reads only the packed copies
+  hipError_t e = hipSuccess;
+  {
+    const dflash_config& c = g.c;
+    const int H = c.hidden, qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim;
+    const int F = c.target_streams * c.target_width, I = c.intermediate;
+    unsigned char* base = (unsigned char*)packed;
+    size_t idx = 0;
+    auto pack = [&](Lin& l, int N, int K) {
+      void* dst = base + pk.off[idx++];
+      if (e == hipSuccess) e = launch_pack(g.wt, l.w, N, K, dst, st);
+      l.w = dst;
+    };
+    pack(ctx->fc, H, F);
+    pack(ctx->lm_head, c.vocab, H);
+    for (int l = 0; l < c.layers; ++l) {
+      Layer& L = ctx->layers[l];
+      pack(L.q, qd, H);
+      pack(L.k, kvd, H);
+      pack(L.v, kvd, H);
+      pack(L.o, H, qd);
+      pack(L.gate, I, H);
+      pack(L.up, I, H);
+      pack(L.down, H, I);
+    }
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ctx->ws + lay.knorm_ptrs, knorms.data(), sizeof(void*) * knorms.size(),
+                       hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = launch_init_ws((unsigned long long*)(ctx->ws + lay.keys), GEMM_MAX_ROWS, (unsigned int*)(ctx->ws + lay.ticket), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call

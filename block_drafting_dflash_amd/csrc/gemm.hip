@@ -4,18 +4,21 @@
 // The block forward multiplies B+1 (or B) rows by every drafter weight once, so each
 // weight byte is read exactly once per pass and the kernel is bound by HBM bandwidth. The
 // contraction uses MFMA tiles (A = 16 activation rows, B = 16 weight rows, 32 k per
-// bf16 instruction, 4 k per f32 instruction); the weights go straight from global memory
-// into the B operand with one 16-byte load per lane per step, and every wave prefetches
-// the next chunk of weights while it multiplies the current one.
+// bf16 instruction, 4 k per f32 instruction); weights go straight from global memory into
+// the B operand with one 16-byte load per lane per step.
 //
-// Work decomposition: a work-group owns 16 output columns (32 for the SwiGLU pair) and
-// all of K; its waves split K evenly and sum their partial tiles through LDS in a fixed
-// order, so every output's reduction order is the same whatever R is (a row gives
-// bit-identical results in a 4-row or a 16-row call). Activations come either straight
-// from global memory (L2-resident) or staged once in LDS, optionally through the RMSNorm
-// prologue y = x * rsqrt(mean(x^2) + eps) * g rounded to the operand dtype.
-// Epilogues: store, residual add, SwiGLU, and the fused argmax of the lm_head, which
-// reduces (value, index) keys with wavefront shuffles and one 64-bit atomicMax per row.
+// Work decomposition: a work-group owns T output tiles of 16 columns (32 weight rows for
+// the SwiGLU gate/up pair) and all of K for each; its waves split K evenly and sum their
+// partial tiles through LDS in a fixed order, so an output's reduction order never depends
+// on the row count (a row gives bit-identical results in a 4-row or a 16-row call). The
+// (tile, chunk) sequence of a work-group is a compile-time constant and fully unrolled:
+// every wave keeps the next chunk of weights in flight while it multiplies the current
+// one, and the compiler's wait counts stay exact (a loop back-edge would make it drain
+// the prefetch at every iteration). Activations come straight from global memory
+// (L2-resident) or are staged once in LDS, optionally through the RMSNorm prologue
+// y = x * rsqrt(mean(x^2) + eps) * g rounded to the operand dtype. Epilogues: store,
+// residual add, SwiGLU, and the fused lm_head argmax, which reduces (value, index) keys
+// with wavefront shuffles and one 64-bit atomicMax per row and work-group.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,65 +56,67 @@ __device__ __forceinline__ int find_seg(const GemmParams& p, int col) {
   return s;
 }
 
-template <int WT, int RT, int NB, int EPI, int XSRC>
-__global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
-  using T = WTr<WT>;
-  constexpr bool BF = T::BF;
-  constexpr int CH = chunk_steps(RT);
+// Single-chunk, single-tile launches run hundreds of work-groups, so they are held to two
+// resident work-groups per CU; the others keep the full register budget.
+template <int T, int NCH> constexpr int gemm_min_blocks() { return (T == 1 && NCH == 1) ? 2 : 1; }
+
+// T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
+__global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(const GemmParams p) {
+  using Tr = WTr<WT>;
+  constexpr bool BF = Tr::BF;
+  constexpr int NIT = T * NCH;
+  constexpr int NRED = T > 1 ? 2 : 1;  // reduction buffers (double-buffered across tiles)
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int nw = p.waves;
-  const int K = p.K, R = p.R, nch = p.nchunks;
-  const int kw = K / nw;  // k owned by this wave in every tile
+  const int K = p.K, R = p.R;
+  const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
 
-  float* red = (float*)smem;  // [nw][RT][NB][64 lanes][4]
-  unsigned char* xs = smem + (size_t)nw * RT * NB * 1024;
-  float* rinv = (float*)(xs + (size_t)R * p.xstride * T::ELT);
+  float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
+  unsigned char* xs = smem + (size_t)NRED * nw * RT * NB * 1024;
+  float* rinv = (float*)(xs + (size_t)R * p.xstride * Tr::ELT);
 
-  const int my_tiles = (p.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int nit = my_tiles * nch;
-
-  // byte pointers of this lane's weight rows for a tile
-  auto wrows = [&](int j, const unsigned char* (&wr)[NB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int s, row;
-      if constexpr (NB == 1) {
-        s = find_seg(p, 16 * j);
-        row = 16 * j - p.seg[s].col0 + li;
-      } else {
-        s = nb;
-        row = 16 * j + li;
-      }
-      wr[nb] = (const unsigned char*)p.seg[s].w + ((size_t)row * K + (size_t)w * kw + lg * T::EPL) * T::ELT;
-    }
+  // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
+  // the other epilogues always run with T == 1
+  auto tile_of = [&](int t) {
+    const int j = (int)blockIdx.x * T + t;
+    return j < p.ntiles ? j : p.ntiles - 1;
   };
 
   auto load = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], int it) {
-    const int ti = it / nch, c = it - ti * nch;
-    const int j = (int)blockIdx.x + ti * (int)gridDim.x;
-    const unsigned char* wr[NB];
-    wrows(j, wr);
-    const size_t kb = (size_t)c * CH * T::KSTEP * T::ELT;
+    const int j = tile_of(it / NCH), c = it % NCH;
+    const size_t kb = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP + lg * Tr::EPL) * Tr::ELT;
+    // fragment-major weights: one contiguous kilobyte per (16-row tile, KSTEP) block
+    const size_t kblocks = (size_t)K / Tr::KSTEP;
+    const size_t blk0 = (size_t)w * (kw / Tr::KSTEP) + (size_t)c * CH;
 #pragma unroll
-    for (int s = 0; s < CH; ++s)
+    for (int nb = 0; nb < NB; ++nb) {
+      int s, tj;
+      if constexpr (NB == 1) {
+        s = find_seg(p, 16 * j);
+        tj = (16 * j - p.seg[s].col0) >> 4;
+      } else {
+        s = nb;
+        tj = j;
+      }
+      const unsigned char* wr = (const unsigned char*)p.seg[s].w + ((size_t)tj * kblocks + blk0) * 1024 + lane * 16;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        wb[nb][s] = *(const u32x4_t*)(wr[nb] + kb + (size_t)s * T::KSTEP * T::ELT);
+      for (int st = 0; st < CH; ++st) wb[nb][st] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)st * 1024));
+    }
     if constexpr (XSRC == XSRC_GLOBAL) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int r = rt * 16 + li;
-        const unsigned char* xr = (const unsigned char*)p.x +
-            ((size_t)r * p.ldx + (size_t)w * kw + lg * T::EPL) * T::ELT + kb;
+        const unsigned char* xr = (const unsigned char*)p.x + (size_t)r * p.ldx * Tr::ELT + kb;
 #pragma unroll
-        for (int s = 0; s < CH; ++s) {
+        for (int st = 0; st < CH; ++st) {
           u32x4_t v = {0u, 0u, 0u, 0u};
-          if (r < R) v = *(const u32x4_t*)(xr + (size_t)s * T::KSTEP * T::ELT);
-          xb[rt][s] = v;
+          if (r < R) v = *(const u32x4_t*)(xr + (size_t)st * Tr::KSTEP * Tr::ELT);
+          xb[rt][st] = v;
         }
       }
     }
@@ -125,36 +130,36 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
     for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], int it) {
-    const int c = it % nch;
+    const int c = it % NCH;
 #pragma unroll
-    for (int s = 0; s < CH; ++s) {
+    for (int st = 0; st < CH; ++st) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         u32x4_t xf;
         if constexpr (XSRC == XSRC_GLOBAL) {
-          xf = xb[rt][s];
+          xf = xb[rt][st];
         } else {
           const int r = rt * 16 + li;
           xf = u32x4_t{0u, 0u, 0u, 0u};
           if (r < R) {
-            const int k = w * kw + (c * CH + s) * T::KSTEP + lg * T::EPL;
-            xf = *(const u32x4_t*)(xs + ((size_t)r * p.xstride + k) * T::ELT);
+            const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
+            xf = *(const u32x4_t*)(xs + ((size_t)r * p.xstride + k) * Tr::ELT);
           }
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = step_mfma<WT>(xf, wb[nb][s], acc[rt][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
       }
     }
   };
 
-  auto finalize = [&](int it) {
-    const int ti = it / nch;
-    const int j = (int)blockIdx.x + ti * (int)gridDim.x;
+  auto finalize = [&](int t) {
+    const int j = tile_of(t);
+    float* rb = red + (size_t)(t % NRED) * nw * RT * NB * 256;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        *(f32x4_t*)&red[((size_t)((w * RT + rt) * NB + nb) * 64 + lane) * 4] = acc[rt][nb];
+        *(f32x4_t*)&rb[((size_t)((w * RT + rt) * NB + nb) * 64 + lane) * 4] = acc[rt][nb];
         acc[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     __syncthreads();
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         v[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int ww = 0; ww < nw; ++ww) v[nb] += *(const f32x4_t*)&red[((size_t)((ww * RT + rt) * NB + nb) * 64 + lane) * 4];
+        for (int ww = 0; ww < nw; ++ww) v[nb] += *(const f32x4_t*)&rb[((size_t)((ww * RT + rt) * NB + nb) * 64 + lane) * 4];
       }
       const int col = 16 * j + li;
       if constexpr (EPI == EPI_ARGMAX) {
@@ -196,13 +201,13 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
         }
       }
     }
-    __syncthreads();
+    if constexpr (NRED == 1) __syncthreads();
   };
 
   // ---- issue the first weight chunk before staging activations -------------------------
-  u32x4_t wA[NB][CH], wB[NB][CH];
-  u32x4_t xA[RT][CH], xB[RT][CH];
-  if (nit > 0) load(wA, xA, 0);
+  u32x4_t wbuf[2][NB][CH];
+  u32x4_t xbuf[2][RT][CH];
+  load(wbuf[0], xbuf[0], 0);
 
   if constexpr (XSRC != XSRC_GLOBAL) {
     if constexpr (XSRC == XSRC_NORM) {
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = act_ld<BF>(p.x, (int64_t)r * p.ldx + k + e);
       }
-      unsigned char* dst = xs + ((size_t)r * p.xstride + k) * T::ELT;
+      unsigned char* dst = xs + ((size_t)r * p.xstride + k) * Tr::ELT;
       if constexpr (BF) {
         uint2 pk;
         pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
@@ -245,15 +250,12 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  // ---- main loop over (tile, chunk), two chunks per trip (register double buffer) -------
-  for (int it = 0; it < nit; it += 2) {
-    if (it + 1 < nit) load(wB, xB, it + 1);
-    compute(wA, xA, it);
-    if ((it + 1) % nch == 0) finalize(it);
-    if (it + 1 >= nit) break;
-    if (it + 2 < nit) load(wA, xA, it + 2);
-    compute(wB, xB, it + 1);
-    if ((it + 2) % nch == 0) finalize(it + 1);
+  // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (it + 1 < NIT) load(wbuf[(it + 1) & 1], xbuf[(it + 1) & 1], it + 1);
+    compute(wbuf[it & 1], xbuf[it & 1], it);
+    if (it % NCH == NCH - 1) finalize(it / NCH);
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
@@ -276,18 +278,19 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams p) {
   }
 }
 
-size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride) {
+size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, int tiles_per_wg) {
   const int rt = (R + 15) / 16;
   const size_t elt = wt == WT_F32 ? 4 : 2;
-  size_t b = (size_t)waves * rt * nb * 1024;
+  size_t b = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * rt * nb * 1024;
   if (xsrc != XSRC_GLOBAL) b += (size_t)R * xstride * elt + (size_t)R * 4;
   return b;
 }
 
-template <int WT, int RT, int NB, int EPI, int XSRC>
+// ---- instantiation tables -----------------------------------------------------------------
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
 static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(WT, XSRC, p.R, p.waves, NB, p.xstride);
-  auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC>;
+  const size_t lds = gemm_lds_bytes(WT, XSRC, p.R, p.waves, NB, p.xstride, T);
+  auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH>;
   static size_t attr_lds = 64 * 1024;  // dynamic LDS this kernel is cleared for
   if (lds > attr_lds) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -298,41 +301,80 @@ static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int WT, int RT, int EPI, int XSRC>
-static hipError_t dispatch_nb(const GemmParams& p, int grid, hipStream_t s) {
-  if constexpr (EPI == EPI_SWIGLU) return launch_t<WT, RT, 2, EPI, XSRC>(p, grid, s);
-  else return launch_t<WT, RT, 1, EPI, XSRC>(p, grid, s);
-}
-
-template <int WT, int EPI, int XSRC>
-static hipError_t dispatch_rt(const GemmParams& p, int grid, hipStream_t s) {
+template <int WT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
+static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
   const int rt = (p.R + 15) / 16;
-  if (rt == 1) return dispatch_nb<WT, 1, EPI, XSRC>(p, grid, s);
-  if (rt == 2) return dispatch_nb<WT, 2, EPI, XSRC>(p, grid, s);
-  return dispatch_nb<WT, 3, EPI, XSRC>(p, grid, s);
+  if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
+  if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
+  if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
+  else return launch_t<WT, 3, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
 }
 
-template <int WT, int EPI>
-static hipError_t dispatch_x(int xsrc, const GemmParams& p, int grid, hipStream_t s) {
-  if (xsrc == XSRC_GLOBAL) return dispatch_rt<WT, EPI, XSRC_GLOBAL>(p, grid, s);
-  if (xsrc == XSRC_LDS) return dispatch_rt<WT, EPI, XSRC_LDS>(p, grid, s);
-  return dispatch_rt<WT, EPI, XSRC_NORM>(p, grid, s);
-}
-
-template <int WT>
-static hipError_t dispatch_epi(int epi, int xsrc, const GemmParams& p, int grid, hipStream_t s) {
-  switch (epi) {
-    case EPI_STORE: return dispatch_x<WT, EPI_STORE>(xsrc, p, grid, s);
-    case EPI_RESID: return dispatch_x<WT, EPI_RESID>(xsrc, p, grid, s);
-    case EPI_SWIGLU: return dispatch_x<WT, EPI_SWIGLU>(xsrc, p, grid, s);
-    default: return dispatch_x<WT, EPI_ARGMAX>(xsrc, p, grid, s);
+// one-tile launches: CH = 8 steps per chunk, NCH chunks per wave
+template <int WT, int NB, int EPI, int XSRC>
+static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  switch (pl.nch) {
+    case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
+    case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
+    case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8>(p, pl.grid, s);
+    case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8>(p, pl.grid, s);
+    case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8>(p, pl.grid, s);
+    case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8>(p, pl.grid, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmParams& p, int grid, hipStream_t s) {
-  if (p.R < 1 || p.R > GEMM_MAX_ROWS || grid < 1) return hipErrorInvalidValue;
-  if (wt == WT_F32) return dispatch_epi<WT_F32>(epi, xsrc, p, grid, s);
-  if (wt == WT_BF16) return dispatch_epi<WT_BF16>(epi, xsrc, p, grid, s);
+// argmax launches: one chunk of CH = steps-per-wave, T tiles per work-group
+template <int WT, int XSRC, int CH>
+static hipError_t argmax_by_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  switch (pl.tiles_per_wg) {
+    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, 1, CH>(p, pl.grid, s);
+    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, 1, CH>(p, pl.grid, s);
+    case 8: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 8, 1, CH>(p, pl.grid, s);
+    case 17: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 17, 1, CH>(p, pl.grid, s);
+    case 25: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 25, 1, CH>(p, pl.grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WT, int XSRC>
+static hipError_t argmax_by_ch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  switch (pl.ch) {
+    case 4: return argmax_by_t<WT, XSRC, 4>(pl, p, s);
+    case 8: return argmax_by_t<WT, XSRC, 8>(pl, p, s);
+    case 16: return argmax_by_t<WT, XSRC, 16>(pl, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WT>
+static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s) {
+  if (epi == EPI_ARGMAX) {
+    if (xsrc == XSRC_NORM) return argmax_by_ch<WT, XSRC_NORM>(pl, p, s);
+    if (xsrc == XSRC_LDS) return argmax_by_ch<WT, XSRC_LDS>(pl, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (epi == EPI_STORE && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL>(pl, p, s);
+  if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM>(pl, p, s);
+  if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL>(pl, p, s);
+  if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM>(pl, p, s);
+  return hipErrorInvalidValue;
+}
+
+bool gemm_plan_supported(const GemmPlan& pl, int epi) {
+  if (epi == EPI_ARGMAX)
+    return pl.nch == 1 && (pl.ch == 4 || pl.ch == 8 || pl.ch == 16) &&
+           (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 8 || pl.tiles_per_wg == 17 ||
+            pl.tiles_per_wg == 25);
+  return pl.ch == 8 && pl.tiles_per_wg == 1 &&
+         (pl.nch == 1 || pl.nch == 2 || pl.nch == 3 || pl.nch == 4 || pl.nch == 5 || pl.nch == 10);
+}
+
+hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  if (p.R < 1 || p.R > GEMM_MAX_ROWS || pl.grid < 1 || p.waves != pl.waves || !gemm_plan_supported(pl, epi))
+    return hipErrorInvalidValue;
+  if (wt == WT_F32) return by_kind<WT_F32>(pl, epi, xsrc, p, s);
+  if (wt == WT_BF16) return by_kind<WT_BF16>(pl, epi, xsrc, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -20,7 +20,8 @@ __host__ __device__ constexpr int chunk_steps(int rt) { return rt == 1 ? 8 : 4; 
 constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per compute unit
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 
-// One weight matrix [rows, K] (row-major) whose outputs occupy columns col0..col0+rows-1.
+// One weight matrix [rows, K] in fragment-major blocks (launch_pack) whose outputs occupy
+// columns col0..col0+rows-1.
 struct GemmSeg {
   const void* w;
   const void* scales;  // q4 only: bf16 [rows, K/64]
@@ -37,7 +38,6 @@ struct GemmParams {
   int32_t K;
   int32_t R;        // rows of X (<= GEMM_MAX_ROWS)
   int32_t waves;    // waves per work-group; each owns K/waves of every tile
-  int32_t nchunks;  // pipelined chunks per wave per tile
   const void* x;    // XSRC_GLOBAL/LDS: act dtype [R, ldx]; XSRC_NORM: f32 [R, ldx]
   int64_t ldx;
   const void* gain;  // XSRC_NORM: act-dtype storage [K]
@@ -50,8 +50,15 @@ struct GemmParams {
   int32_t* idx_out;          // ARGMAX: [R]
 };
 
-hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmParams& p, int grid, hipStream_t s);
-size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride);
+// Launch shape of one GEMM: waves per work-group and, per wave and tile, nch chunks of ch
+// MFMA steps; tiles_per_wg output tiles per work-group; grid work-groups. It depends on K
+// (never on the row count) so that every output keeps one reduction order.
+struct GemmPlan {
+  int waves, ch, nch, tiles_per_wg, grid;
+};
+bool gemm_plan_supported(const GemmPlan& pl, int epi);
+hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
+size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, int tiles_per_wg);
 
 // ---- small kernels --------------------------------------------------------------------
 struct AttnShape {
@@ -61,6 +68,8 @@ struct AttnShape {
   float eps, theta;
 };
 
+// Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip).
+hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s);
 hipError_t launch_init_ws(unsigned long long* keys, int nkeys, unsigned int* ticket, hipStream_t s);
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
                         float* x, hipStream_t s);

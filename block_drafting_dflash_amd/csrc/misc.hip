@@ -97,3 +97,34 @@ hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int
 }
 
 }  // namespace dflash
+
+namespace dflash {
+
+// Repack a row-major linear W [N, K] into fragment-major 1 KiB blocks: block (j, s) holds
+// rows 16j..16j+15 and k in [s*KSTEP, (s+1)*KSTEP), and its lane l = li + 16*lg (li = row
+// offset, lg = 0..3) owns the 16 bytes W[16j + li][s*KSTEP + lg*EPL .. + EPL). Blocks of a
+// row tile are consecutive, so every 16-byte-per-lane wave load of the GEMM reads one
+// contiguous kilobyte and lands directly in the MFMA B-operand layout.
+__global__ void pack_kernel(const unsigned char* __restrict__ src, int64_t nblocks, int kblocks, int K, int elt,
+                            int epl, u32x4_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte lane slot
+  if (i >= nblocks * 64) return;
+  const int64_t blk = i >> 6;
+  const int lane = (int)(i & 63), li = lane & 15, lg = lane >> 4;
+  const int64_t j = blk / kblocks, s = blk - j * kblocks;
+  const int kstep = 4 * epl;
+  const size_t off = ((size_t)(16 * j + li) * K + (size_t)s * kstep + (size_t)lg * epl) * elt;
+  dst[i] = *(const u32x4_t*)(src + off);
+}
+
+hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s) {
+  const int elt = wt == WT_F32 ? 4 : 2, epl = 16 / elt;
+  const int kblocks = K / (4 * epl);
+  const int64_t nblocks = (int64_t)(N / 16) * kblocks;
+  const int64_t slots = nblocks * 64;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, (const unsigned char*)src,
+                     nblocks, kblocks, K, elt, epl, (u32x4_t*)dst);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -105,15 +105,23 @@ typedef struct {
   const dflash_layer *layers;
 } dflash_weights;
 
-/* Bytes of ring and of workspace a context with this config needs. Host only. */
-dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, size_t *workspace_bytes);
+/* Bytes of ring, of workspace and of packed weights a context with this config needs.
+ * Host only. */
+dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, size_t *workspace_bytes,
+                                 size_t *packed_bytes);
 
 /* Validate cfg and the weight pointers, bind the caller's buffers and initialise the
- * workspace on `stream`. ring and workspace must be at least the queried sizes and
- * 256-byte aligned. The ring starts empty: e = 0, no pending rows. */
+ * workspace on `stream`. ring, workspace and packed must be at least the queried sizes and
+ * 256-byte aligned. Every linear (fc, lm_head and the layer linears) is copied once into
+ * `packed` in a fragment-major order: each 16-row x 16-byte-per-lane block of the matrix
+ * becomes one contiguous kilobyte in the lane order of the MFMA operand, so that the
+ * weight streams of every later call read whole contiguous kilobytes. The call
+ * synchronises `stream`; afterwards the caller may free those row-major linears. The
+ * embedding table and the norm gains are read in place and must stay alive. The ring
+ * starts empty: e = 0, no pending rows. */
 dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *weights, void *ring,
-                            size_t ring_bytes, void *workspace, size_t workspace_bytes, void *stream,
-                            dflash_ctx **out);
+                            size_t ring_bytes, void *workspace, size_t workspace_bytes, void *packed,
+                            size_t packed_bytes, void *stream, dflash_ctx **out);
 
 void dflash_destroy(dflash_ctx *ctx);
 
