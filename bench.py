@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -44,6 +45,17 @@ def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
     fwd = fc + sh.layers * layer + lm + kv + inputs
     return {"fc": fc, "layers": sh.layers * layer, "lm_head": lm, "kv": kv, "block_forward": fwd,
             "round_lm_verify": fwd + lm + (block + 1) * H * e}
+
+
+def counted_traffic():
+    """HBM bytes per lm_head launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    (scaled by the same counters on a 1 GiB copy), or None if the kernel source changed since."""
+    try:
+        d = json.load(open(os.path.join(ROOT, "profiles", "lm_head_argmax_counters.json")))
+        src = open(os.path.join(ROOT, "block_drafting_dflash_amd", "csrc", "gemm.hip"), "rb").read()
+    except OSError:
+        return None
+    return d["traffic_bytes"] if d.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest() else None
 
 
 def run_gpu(args):
@@ -224,13 +236,26 @@ def main():
     ap.add_argument("--block16-steps", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB five times (counter reference) and exit")
     args = ap.parse_args()
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_mib": args.copy_probe_mib, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the round at batch 1 is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     sh, weights, res, b16 = run_gpu(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(sh, weights, args.cpu_budget)
+    traffic = counted_traffic()
     line = {
         "metric": "DFlash rounds/s at block 4 (B=1), with drafted tok/s and % of HBM roofline",
         "value": round(res["rounds_per_s"], 2), "unit": "rounds/s",
@@ -246,7 +271,9 @@ def main():
                           "draft_ms": round(res["draft_ms"], 4), "append_ms": round(res["append_ms"], 4)},
         "roofline": {"bound": "hbm", "kernel": "lm_head argmax GEMM (202048x2048 bf16, 5 verify rows)",
                      "achieved": round(res["lm_head_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["lm_head_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(res["lm_head_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic / (res["lm_head_ms"] * 1e-3) / 1e9, 1) if traffic else None),
+                     "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": res["bytes"]["lm_head"],
                      "avg_launch_ms": round(res["lm_head_ms"], 5)},
         "block16": b16,
         "cpu_baseline": cpu,

@@ -1,0 +1,115 @@
+"""Host-side tests of the C-ABI library: no GPU needed (no device call is made).
+
+They check that libdflash.so loads and exports every function include/dflash.h declares,
+that the binding describes each of them, and the host-side validation of
+dflash_query_sizes / dflash_create, including the ring size implied by the slack rule.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from block_drafting_dflash_amd import binding, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12, names
+    L = binding.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libdflash.so")
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(ImportError):
+        binding.lib()
+
+
+def sizes(shape, max_block=4, phase=0):
+    return binding.query_sizes(binding.make_config(shape, max_block, phase))
+
+
+def status_of(shape, max_block=4, **cfg_over):
+    cfg = binding.make_config(shape, max_block)
+    for k, v in cfg_over.items():
+        setattr(cfg, k, v)
+    try:
+        binding.query_sizes(cfg)
+        return 0
+    except binding.DFlashError as e:
+        return e.status
+
+
+def test_ring_size_follows_the_slack_rule():
+    """ring bytes = layers * 2 (K,V) * kv_heads * (W + S) * head_dim * element size, with
+    S read from the slack table the page states."""
+    table = json.load(open(os.path.join(ROOT, "tests", "golden", "slack_table.json")))["table"]
+    for sh in (synth.TINY_F32, synth.MUSE_BF16):
+        elt = 4 if sh.act_dtype == "f32" else 2
+        for b, S in table.items():
+            if int(b) > 256:
+                continue
+            ring, ws, packed = sizes(sh, int(b))
+            assert ring == sh.layers * 2 * sh.kv_heads * (sh.window + S) * sh.head_dim * elt, (sh, b)
+
+
+def test_packed_size_covers_every_linear_once():
+    sh = synth.MUSE_BF16
+    _, _, packed = sizes(sh)
+    H, qd, kvd = sh.hidden, sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim
+    n = H * sh.fc_in + sh.vocab * H + sh.layers * (qd * H + 2 * kvd * H + H * qd + 3 * sh.intermediate * H)
+    assert n * 2 <= packed <= n * 2 + 256 * (2 + 7 * sh.layers)
+
+
+def test_query_sizes_validation_statuses():
+    sh = synth.TINY_F32
+    E_ARG, E_SHAPE, E_RANGE = 1, 2, 3
+    assert status_of(sh) == 0
+    assert status_of(sh, head_dim=60) == E_SHAPE
+    assert status_of(sh, q_heads=3) == E_SHAPE  # not a multiple of kv_heads
+    assert status_of(sh, hidden=0) == E_SHAPE
+    assert status_of(sh, window=-1) == E_SHAPE
+    assert status_of(sh, mask_token_id=sh.vocab) == E_RANGE
+    assert status_of(sh, mask_token_id=-1) == E_RANGE
+    assert status_of(sh, max_block=257) == E_RANGE
+    assert status_of(sh, vocab=4100) == E_SHAPE  # not a multiple of 16
+    assert status_of(sh, act_dtype=binding.DFLASH_BF16) == E_ARG  # f32 weights need f32 activations
+    assert status_of(sh, weight_dtype=7) == E_ARG
+    assert status_of(sh, rms_eps=0.0) == E_ARG
+    assert status_of(sh, intermediate=200) == E_SHAPE  # no launch plan for this contraction
+    # a dimension product past the int32 range is refused, not wrapped
+    assert status_of(synth.MUSE_BF16, vocab=2 ** 20 + 16) == E_SHAPE
+
+
+def test_create_refuses_null_buffers_before_any_device_call():
+    sh = synth.TINY_F32
+    cfg = binding.make_config(sh, 4)
+    L = binding.lib()
+    h = ctypes.c_void_p()
+    st = L.dflash_create(ctypes.byref(cfg), None, None, 0, None, 0, None, 0, None, ctypes.byref(h))
+    assert st == 1 and not h.value
+    assert b"NULL" in L.dflash_last_error(None)
+    w = binding.dflash_weights()
+    st = L.dflash_create(ctypes.byref(cfg), ctypes.byref(w), None, 0, None, 0, None, 0, None, ctypes.byref(h))
+    assert st == 1
+
+
+def test_status_strings():
+    L = binding.lib()
+    for s in range(8):
+        assert L.dflash_status_string(s)
+    assert L.dflash_status_string(99) == b"unknown status"
