@@ -244,25 +244,39 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   const uint16_t* Kr = ring_layer + (size_t)g * plane;
   const uint16_t* Vr = ring_layer + (size_t)(a.nkv + g) * plane;
 
-  constexpr int SEGS = HD / 8;  // 16-byte segments per row
-  for (int it = tid; it < AM_CH * SEGS; it += blockDim.x) {
+  constexpr int SEGS = HD / 8;                 // 16-byte segments per row
+  constexpr int ITEMS = AM_CH * SEGS / 256;    // staging items per thread
+  // slot of the chunk's first context key; later keys wrap at most once (kj < nctx <= W < C)
+  const int64_t s0 = (lo + k0 + a.phase) % a.cap;
+  u32x4_t kv[ITEMS], vv[ITEMS];
+#pragma unroll
+  for (int u = 0; u < ITEMS; ++u) {
+    const int it = tid + u * 256;
     const int kj = it / SEGS, sg = it - kj * SEGS;
-    u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    kv[u] = u32x4_t{0u, 0u, 0u, 0u};
+    vv[u] = u32x4_t{0u, 0u, 0u, 0u};
     if (kj < kn) {
       const int key = k0 + kj;
       if (key < nctx) {
-        const size_t off = (size_t)((lo + key + a.phase) % a.cap) * HD + 8 * sg;
-        kv = *(const u32x4_t*)(Kr + off);
-        vv = *(const u32x4_t*)(Vr + off);
+        int64_t slot = s0 + kj;
+        if (slot >= a.cap) slot -= a.cap;
+        const size_t off = (size_t)slot * HD + 8 * sg;
+        kv[u] = *(const u32x4_t*)(Kr + off);
+        vv[u] = *(const u32x4_t*)(Vr + off);
       } else {
         const size_t off = ((size_t)(key - nctx) * a.nkv + g) * HD + 8 * sg;
-        kv = *(const u32x4_t*)(kb + off);
-        vv = *(const u32x4_t*)(vb + off);
+        kv[u] = *(const u32x4_t*)(kb + off);
+        vv[u] = *(const u32x4_t*)(vb + off);
       }
     }
-    *(u32x4_t*)&Kl[kj * KST + 8 * sg] = kv;
+  }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) Vt[(8 * sg + t) * VST + kj] = (uint16_t)(vv[t >> 1] >> (16 * (t & 1)));
+  for (int u = 0; u < ITEMS; ++u) {
+    const int it = tid + u * 256;
+    const int kj = it / SEGS, sg = it - kj * SEGS;
+    *(u32x4_t*)&Kl[kj * KST + 8 * sg] = kv[u];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) Vt[(8 * sg + t) * VST + kj] = (uint16_t)(vv[u][t >> 1] >> (16 * (t & 1)));
   }
   for (int kj = tid; kj < AM_CH; kj += blockDim.x) {
     const int key = k0 + kj;
@@ -351,24 +365,33 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
 }
 
 // ---- combine chunks in chunk order --------------------------------------------------------
-// One work-group (hd threads) per (row, query head); out: act [R, nq*hd].
+// One work-group (hd threads) per (row, query head); out: act [R, nq*hd]. The chunk maxima
+// and sums are staged in LDS first so the output loop issues independent loads.
+constexpr int COMBINE_MAX_CHUNKS = 80;
 template <bool BF>
 __global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part, int R, int nchunks, void* out) {
+  __shared__ float sm_m[COMBINE_MAX_CHUNKS], sm_l[COMBINE_MAX_CHUNKS];
   const int item = blockIdx.x;
   const int r = item / a.nq, h = item - r * a.nq;
   const int G = a.nq / a.nkv, g = h / G, hh = h - g * G;
   const int NQ = R * G, qi = r * G + hh;
   const int d = threadIdx.x, hd = a.hd;
+  const size_t stride = (size_t)NQ * (hd + 2);
+  const float* base = part + ((size_t)g * nchunks * NQ + qi) * (hd + 2);
+  for (int c = d; c < nchunks; c += blockDim.x) {
+    sm_m[c] = base[c * stride + hd];
+    sm_l[c] = base[c * stride + hd + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, part[(((size_t)g * nchunks + c) * NQ + qi) * (hd + 2) + hd]);
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, sm_m[c]);
   float L = 0.f, O = 0.f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
-    const float* p = part + (((size_t)g * nchunks + c) * NQ + qi) * (hd + 2);
-    const float m = p[hd];
-    if (m == -INFINITY) continue;
-    const float f = expf(m - M);
-    L += p[hd + 1] * f;
-    O += p[d] * f;
+    const float m = sm_m[c];
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    L += sm_l[c] * f;
+    O += base[c * stride + d] * f;
   }
   act_st<BF>(out, (size_t)r * a.nq * hd + (size_t)h * hd + d, O / L);
 }

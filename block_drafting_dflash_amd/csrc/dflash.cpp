@@ -31,7 +31,7 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t keys, ticket, knorm_ptrs, x, qkv, qb, kb, vb, attn, mlp, part, app_fc, app_c, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_c, app_kv, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -92,26 +92,17 @@ dflash_status cfg_fail(char* buf, dflash_status st, const char* fmt, ...) {
 
 int kstep(int wt) { return wt == WT_F32 ? 16 : 32; }
 
-constexpr int ARGMAX_WAVES = 4;
-constexpr int ARGMAX_T[] = {1, 4, 8, 17, 25};
 constexpr int CHUNK_STEPS = 8;
 
 // Launch plan of a GEMM with contraction length K. Waves and chunking depend on K only.
-bool plan_gemm(int wt, int epi, int K, GemmPlan* pl) {
+bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
   const int ks = kstep(wt);
-  if (epi == EPI_ARGMAX) {
-    if (K % (ARGMAX_WAVES * ks)) return false;
-    const int steps = K / (ARGMAX_WAVES * ks);
-    if (steps != 4 && steps != 8 && steps != 16) return false;
-    *pl = GemmPlan{ARGMAX_WAVES, steps, 1, 1, 0};
-    return gemm_plan_supported(*pl, epi);
-  }
   if (K % (CHUNK_STEPS * ks)) return false;
   const int units = K / (CHUNK_STEPS * ks);
   for (int w = 8; w >= 1; --w) {
     if (units % w) continue;
-    GemmPlan p{w, CHUNK_STEPS, units / w, 1, 0};
-    if (gemm_plan_supported(p, epi)) {
+    GemmPlan p{w, CHUNK_STEPS, units / w, epi == EPI_ARGMAX ? 4 : 1, 0};
+    if (gemm_plan_supported(p, epi, xsrc)) {
       *pl = p;
       return true;
     }
@@ -119,15 +110,13 @@ bool plan_gemm(int wt, int epi, int K, GemmPlan* pl) {
   return false;
 }
 
-// Tiles per work-group of an argmax launch: the fewest that keep the whole grid resident
-// (about 200 VGPRs per lane leave 2 four-wave work-groups per CU; LDS may allow fewer).
-int argmax_tiles_per_wg(int ntiles, size_t lds, int cus, int rt) {
-  const int by_vgpr = rt == 1 ? 2 : 1;
-  const int by_lds = (int)std::max<size_t>(1, (size_t)LDS_BYTES / std::max<size_t>(lds, 1));
-  const int resident = cus * std::min(by_vgpr, by_lds);
-  for (int t : ARGMAX_T)
-    if ((ntiles + t - 1) / t <= resident) return t;
-  return ARGMAX_T[sizeof(ARGMAX_T) / sizeof(int) - 1];
+// Tiles per work-group of an argmax launch: small work-groups keep the dispatcher
+// balancing the vocabulary stream; with many rows, more tiles per work-group bound how
+// often the operand rows are re-read from L2.
+int argmax_tiles_per_wg(int ntiles, int rows) {
+  if (ntiles < 1024) return 1;
+  if (ntiles < 8192) return 2;
+  return rows > 8 ? 16 : 4;
 }
 
 dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
@@ -145,6 +134,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   if (c->act_dtype != (bf ? DFLASH_BF16 : DFLASH_F32))
     return cfg_fail(err, DFLASH_E_ARG, "act dtype must be f32 with f32 weights and bf16 otherwise");
   if (c->max_block > MAX_BLOCK_LIMIT) return cfg_fail(err, DFLASH_E_RANGE, "max_block above %d", MAX_BLOCK_LIMIT);
+  if (c->window > MAX_WINDOW) return cfg_fail(err, DFLASH_E_SHAPE, "window above %d", MAX_WINDOW);
   if (c->q_heads % c->kv_heads) return cfg_fail(err, DFLASH_E_SHAPE, "q_heads must be a multiple of kv_heads");
   if (c->head_dim % 2 || c->head_dim > 128 || c->head_dim % 16)
     return cfg_fail(err, DFLASH_E_SHAPE, "head_dim must be a multiple of 16 and at most 128");
@@ -170,10 +160,12 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   // every contraction of the round needs a launch plan, and the LDS-staged norm prologue
   // must fit at least 16 rows of hidden
   GemmPlan pl;
-  const struct { int epi; int64_t K; } gemms[] = {{EPI_STORE, H}, {EPI_RESID, qd}, {EPI_SWIGLU, H},
-                                                  {EPI_RESID, c->intermediate}, {EPI_STORE, fin}, {EPI_ARGMAX, H}};
+  const struct { int epi, xsrc; int64_t K; } gemms[] = {
+      {EPI_STORE, XSRC_NORM, H},           {EPI_RESID, XSRC_GLOBAL, qd},  {EPI_SWIGLU, XSRC_NORM, H},
+      {EPI_RESID, XSRC_GLOBAL, c->intermediate}, {EPI_STORE, XSRC_GLOBAL, fin}, {EPI_STORE, XSRC_GLOBAL, H},
+      {EPI_ARGMAX, XSRC_LDS, H}};
   for (const auto& gm : gemms)
-    if (!plan_gemm(wt, gm.epi, (int)gm.K, &pl))
+    if (!plan_gemm(wt, gm.epi, gm.xsrc, (int)gm.K, &pl))
       return cfg_fail(err, DFLASH_E_SHAPE, "no GEMM launch plan for a contraction of length %lld", (long long)gm.K);
   if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden + 16 / (bf ? 2 : 4), 1) > (size_t)LDS_BYTES)
     return cfg_fail(err, DFLASH_E_SHAPE, "hidden too large for the staged operand");
@@ -210,8 +202,8 @@ Layout make_layout(const Cfg& g) {
     o = align256(o + bytes);
     return at;
   };
-  L.keys = take(sizeof(unsigned long long) * GEMM_MAX_ROWS);
-  L.ticket = take(sizeof(unsigned int));
+  // per-work-group argmax keys of one lm_head launch: <= 32 rows x <= V/16 work-groups
+  L.argmax_part = take(sizeof(unsigned long long) * 32 * (size_t)(c.vocab / 16));
   L.knorm_ptrs = take(sizeof(void*) * c.layers);
   L.x = take(4 * R * H);
   L.qkv = take(4 * R * (qd + 2 * kvd));
@@ -220,6 +212,7 @@ Layout make_layout(const Cfg& g) {
   L.vb = take(ae * R * kvd);
   L.attn = take(ae * R * qd);
   L.mlp = take(ae * R * c.intermediate);
+  L.zrows = take(ae * R * H);  // final-normed drafted rows (lm_head operand)
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_c = take(ae * (size_t)GEMM_MAX_ROWS * H);
@@ -289,7 +282,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
   const int wt = g.wt;
   const int nb = gc.epi == EPI_SWIGLU ? 2 : 1;
   GemmPlan plan;
-  if (!plan_gemm(wt, gc.epi, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
+  if (!plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
   const int waves = plan.waves;
   const int xstride = gc.K + 16 / g.act_elt;
   const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;
@@ -299,7 +292,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
   int r0 = 0;
   while (r0 < rows) {
     int rc = std::min(rows - r0, GEMM_MAX_ROWS);
-    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, 32);  // two row tiles, one finishing wave each
+    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, std::min(32, 16 * waves));  // one finishing wave per row tile
     if (gc.xsrc != XSRC_GLOBAL)
       while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride, gc.epi == EPI_ARGMAX ? 2 : 1) >
                            (size_t)LDS_BYTES)
@@ -319,11 +312,8 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
     GemmPlan pl = plan;
     pl.grid = p.ntiles;
     if (gc.epi == EPI_ARGMAX) {
-      p.keys = (unsigned long long*)(ctx->ws + ctx->lay.keys);
-      p.ticket = (unsigned int*)(ctx->ws + ctx->lay.ticket);
-      p.idx_out = gc.idx + r0;
-      const size_t lds = gemm_lds_bytes(wt, gc.xsrc, rc, waves, 1, xstride, 2);
-      pl.tiles_per_wg = argmax_tiles_per_wg(p.ntiles, lds, ctx->cus, (rc + 15) / 16);
+      p.part = (unsigned long long*)(ctx->ws + ctx->lay.argmax_part);
+      pl.tiles_per_wg = argmax_tiles_per_wg(p.ntiles, rc);
       pl.grid = (p.ntiles + pl.tiles_per_wg - 1) / pl.tiles_per_wg;
     } else {
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
@@ -335,6 +325,10 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
                   "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, ch %d x %d, tiles/wg %d, grid %d): %s",
                   gc.epi, gc.xsrc, gc.K, rc, p.ntiles, waves, pl.ch, pl.nch, pl.tiles_per_wg, pl.grid,
                   hipGetErrorString(le));
+    if (gc.epi == EPI_ARGMAX) {
+      const hipError_t fe = launch_argmax_finalize(p.part, pl.grid, rc, gc.idx + r0, st);
+      if (fe != hipSuccess) return dev(ctx, fe, "argmax finalize");
+    }
     r0 += rc;
   }
   return DFLASH_OK;
@@ -457,8 +451,6 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   if (e == hipSuccess)
     e = hipMemcpyAsync(ctx->ws + lay.knorm_ptrs, knorms.data(), sizeof(void*) * knorms.size(),
                        hipMemcpyHostToDevice, st);
-  if (e == hipSuccess)
-    e = launch_init_ws((unsigned long long*)(ctx->ws + lay.keys), GEMM_MAX_ROWS, (unsigned int*)(ctx->ws + lay.ticket), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
   if (e != hipSuccess) {
     cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
@@ -589,8 +581,11 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
   }
-  GemmCall lm{EPI_ARGMAX, XSRC_NORM, {seg(ctx->lm_head, 0, c.vocab)}, H, x + H, H, ctx->final_norm, nullptr, 0,
-              d_tokens};
+  // final RMSNorm of rows 1..B once, then the lm_head argmax over the bf16/f32 operand rows
+  void* zrows = ctx->ws + ctx->lay.zrows;
+  s = dev(ctx, launch_rownorm(g.bf, x + H, ctx->final_norm, c.rms_eps, block, H, zrows, st), "final norm");
+  if (s != DFLASH_OK) return s;
+  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
   return run_gemm(ctx, lm, block, st);
 }
 

@@ -18,7 +18,9 @@
 // (L2-resident) or are staged once in LDS, optionally through the RMSNorm prologue
 // y = x * rsqrt(mean(x^2) + eps) * g rounded to the operand dtype. Epilogues: store,
 // residual add, SwiGLU, and the fused lm_head argmax, which reduces (value, index) keys
-// with wavefront shuffles and one 64-bit atomicMax per row and work-group.
+// with wavefront shuffles and stores one key per row and work-group; a finalize kernel
+// reduces those (no fence or atomic in the streaming kernel: a device-scope fence per
+// work-group cost a third of the lm_head's time).
 #include "common.h"
 #include "kernels.h"
 
@@ -56,19 +58,19 @@ __device__ __forceinline__ int find_seg(const GemmParams& p, int col) {
   return s;
 }
 
-// Single-chunk, single-tile launches run hundreds of work-groups, so they are held to two
-// resident work-groups per CU; the others keep the full register budget.
-template <int T, int NCH> constexpr int gemm_min_blocks() { return (T == 1 && NCH == 1) ? 2 : 1; }
+// Minimum resident waves per SIMD (the second launch-bounds argument): single-chunk,
+// single-tile launches run hundreds of 8-wave work-groups and need two per CU (<= 128
+// VGPRs); the multi-tile argmax launches three; the rest keep the full register budget.
+template <int T, int NCH> constexpr int gemm_min_waves_per_simd() { return T > 1 ? 3 : (NCH == 1 ? 4 : 2); }
 
 // T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
 template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
-__global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm_kernel(const GemmParams p) {
   using Tr = WTr<WT>;
   constexpr bool BF = Tr::BF;
   constexpr int NIT = T * NCH;
   constexpr int NRED = T > 1 ? 2 : 1;  // reduction buffers (double-buffered across tiles)
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -77,8 +79,7 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
   const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
 
   float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
-  unsigned char* xs = smem + (size_t)NRED * nw * RT * NB * 1024;
-  float* rinv = (float*)(xs + (size_t)R * p.xstride * Tr::ELT);
+  float* rinv = red + (size_t)NRED * nw * RT * NB * 256;  // [R] (RMSNorm prologue)
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues always run with T == 1
@@ -129,6 +130,10 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // operand fragments of this wave's K slice, built once (staged sources only)
+  constexpr int XR = XSRC == XSRC_GLOBAL ? 1 : NCH;
+  u32x4_t xr[XR][RT][CH];
+
   auto compute = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], int it) {
     const int c = it % NCH;
 #pragma unroll
@@ -136,16 +141,8 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         u32x4_t xf;
-        if constexpr (XSRC == XSRC_GLOBAL) {
-          xf = xb[rt][st];
-        } else {
-          const int r = rt * 16 + li;
-          xf = u32x4_t{0u, 0u, 0u, 0u};
-          if (r < R) {
-            const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
-            xf = *(const u32x4_t*)(xs + ((size_t)r * p.xstride + k) * Tr::ELT);
-          }
-        }
+        if constexpr (XSRC == XSRC_GLOBAL) xf = xb[rt][st];
+        else xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
       }
@@ -214,6 +211,7 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
       const float* xf = (const float*)p.x;
       for (int r = w; r < R; r += nw) {
         float ss = 0.f;
+#pragma unroll 8
         for (int k = lane * 4; k < K; k += 256) {
           const float4 v = *(const float4*)(xf + (size_t)r * p.ldx + k);
           ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -223,31 +221,43 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
       }
       __syncthreads();
     }
-    for (int i = tid * 4; i < R * K; i += blockDim.x * 4) {
-      const int r = i / K, k = i - r * K;
-      float v[4];
-      if constexpr (XSRC == XSRC_NORM) {
-        const float4 t = *(const float4*)((const float*)p.x + (size_t)r * p.ldx + k);
-        const float s = rinv[r];
-        v[0] = t.x * s * act_ld<BF>(p.gain, k + 0);
-        v[1] = t.y * s * act_ld<BF>(p.gain, k + 1);
-        v[2] = t.z * s * act_ld<BF>(p.gain, k + 2);
-        v[3] = t.w * s * act_ld<BF>(p.gain, k + 3);
-      } else {
+    // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = act_ld<BF>(p.x, (int64_t)r * p.ldx + k + e);
-      }
-      unsigned char* dst = xs + ((size_t)r * p.xstride + k) * Tr::ELT;
-      if constexpr (BF) {
-        uint2 pk;
-        pk.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-        pk.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-        *(uint2*)dst = pk;
-      } else {
-        *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
-      }
-    }
-    __syncthreads();
+    for (int c = 0; c < XR; ++c)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int st = 0; st < CH; ++st) {
+          const int r = rt * 16 + li;
+          const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
+          u32x4_t f = {0u, 0u, 0u, 0u};
+          if (r < R) {
+            if constexpr (XSRC == XSRC_LDS) {
+              f = *(const u32x4_t*)((const unsigned char*)p.x + ((size_t)r * p.ldx + k) * Tr::ELT);
+            } else {
+              const float* src = (const float*)p.x + (size_t)r * p.ldx + k;
+              const float s = rinv[r];
+              if constexpr (BF) {
+                const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+                const u32x4_t gb = *(const u32x4_t*)((const uint16_t*)p.gain + k);
+                float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                  const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
+                  f[e2] = (uint32_t)f2bf(v[2 * e2] * s * g0) | ((uint32_t)f2bf(v[2 * e2 + 1] * s * g1) << 16);
+                }
+              } else {
+                const float4 a0 = *(const float4*)src;
+                const float4 g = *(const float4*)((const float*)p.gain + k);
+                f[0] = __float_as_uint(a0.x * s * g.x);
+                f[1] = __float_as_uint(a0.y * s * g.y);
+                f[2] = __float_as_uint(a0.z * s * g.z);
+                f[3] = __float_as_uint(a0.w * s * g.w);
+              }
+            }
+          }
+          xr[c][rt][st] = f;
+        }
   }
 
   // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
@@ -263,26 +273,18 @@ __global__ __launch_bounds__(512, (gemm_min_blocks<T, NCH>())) void gemm_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = w * 16 + 4 * lg + q;
-        if (r < R && best[q] != 0ull) atomicMax(&p.keys[r], best[q]);
+        if (r < R) p.part[(size_t)r * gridDim.x + blockIdx.x] = best[q];
       }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(p.ticket, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      for (int r = tid; r < R; r += blockDim.x) p.idx_out[r] = argmax_key_index(atomicExch(&p.keys[r], 0ull));
-      if (tid == 0) atomicExch(p.ticket, 0u);
     }
   }
 }
 
 size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, int tiles_per_wg) {
+  (void)wt;
+  (void)xstride;
   const int rt = (R + 15) / 16;
-  const size_t elt = wt == WT_F32 ? 4 : 2;
   size_t b = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * rt * nb * 1024;
-  if (xsrc != XSRC_GLOBAL) b += (size_t)R * xstride * elt + (size_t)R * 4;
+  if (xsrc == XSRC_NORM) b += (size_t)R * 4;
   return b;
 }
 
@@ -310,39 +312,46 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
   else return launch_t<WT, 3, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
 }
 
-// one-tile launches: CH = 8 steps per chunk, NCH chunks per wave
+// one-tile launches: CH = 8 steps per chunk, NCH chunks per wave (staged operands hold
+// every chunk in registers, so they stop at two chunks)
 template <int WT, int NB, int EPI, int XSRC>
 static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  switch (pl.nch) {
-    case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
-    case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
-    case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8>(p, pl.grid, s);
-    case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8>(p, pl.grid, s);
-    case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8>(p, pl.grid, s);
-    case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8>(p, pl.grid, s);
-    default: return hipErrorInvalidValue;
+  if constexpr (XSRC != XSRC_GLOBAL) {
+    switch (pl.nch) {
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (pl.nch) {
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
+      case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8>(p, pl.grid, s);
+      case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8>(p, pl.grid, s);
+      case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8>(p, pl.grid, s);
+      case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8>(p, pl.grid, s);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
-// argmax launches: one chunk of CH = steps-per-wave, T tiles per work-group
-template <int WT, int XSRC, int CH>
+// argmax launches: T tiles per work-group, NCH chunks of 8 steps per wave and tile
+template <int WT, int XSRC, int NCH>
 static hipError_t argmax_by_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   switch (pl.tiles_per_wg) {
-    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, 1, CH>(p, pl.grid, s);
-    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, 1, CH>(p, pl.grid, s);
-    case 8: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 8, 1, CH>(p, pl.grid, s);
-    case 17: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 17, 1, CH>(p, pl.grid, s);
-    case 25: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 25, 1, CH>(p, pl.grid, s);
+    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, NCH, 8>(p, pl.grid, s);
+    case 2: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 2, NCH, 8>(p, pl.grid, s);
+    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, NCH, 8>(p, pl.grid, s);
+    case 16: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 16, NCH, 8>(p, pl.grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int WT, int XSRC>
 static hipError_t argmax_by_ch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  switch (pl.ch) {
-    case 4: return argmax_by_t<WT, XSRC, 4>(pl, p, s);
-    case 8: return argmax_by_t<WT, XSRC, 8>(pl, p, s);
-    case 16: return argmax_by_t<WT, XSRC, 16>(pl, p, s);
+  switch (pl.nch) {
+    case 1: return argmax_by_t<WT, XSRC, 1>(pl, p, s);
+    case 2: return argmax_by_t<WT, XSRC, 2>(pl, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -350,7 +359,6 @@ static hipError_t argmax_by_ch(const GemmPlan& pl, const GemmParams& p, hipStrea
 template <int WT>
 static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s) {
   if (epi == EPI_ARGMAX) {
-    if (xsrc == XSRC_NORM) return argmax_by_ch<WT, XSRC_NORM>(pl, p, s);
     if (xsrc == XSRC_LDS) return argmax_by_ch<WT, XSRC_LDS>(pl, p, s);
     return hipErrorInvalidValue;
   }
@@ -361,17 +369,17 @@ static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParam
   return hipErrorInvalidValue;
 }
 
-bool gemm_plan_supported(const GemmPlan& pl, int epi) {
+bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {
   if (epi == EPI_ARGMAX)
-    return pl.nch == 1 && (pl.ch == 4 || pl.ch == 8 || pl.ch == 16) &&
-           (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 8 || pl.tiles_per_wg == 17 ||
-            pl.tiles_per_wg == 25);
+    return xsrc == XSRC_LDS && pl.ch == 8 && (pl.nch == 1 || pl.nch == 2) &&
+           (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 16);
+  if (xsrc != XSRC_GLOBAL) return pl.ch == 8 && pl.tiles_per_wg == 1 && (pl.nch == 1 || pl.nch == 2);
   return pl.ch == 8 && pl.tiles_per_wg == 1 &&
          (pl.nch == 1 || pl.nch == 2 || pl.nch == 3 || pl.nch == 4 || pl.nch == 5 || pl.nch == 10);
 }
 
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  if (p.R < 1 || p.R > GEMM_MAX_ROWS || pl.grid < 1 || p.waves != pl.waves || !gemm_plan_supported(pl, epi))
+  if (p.R < 1 || p.R > GEMM_MAX_ROWS || pl.grid < 1 || p.waves != pl.waves || !gemm_plan_supported(pl, epi, xsrc))
     return hipErrorInvalidValue;
   if (wt == WT_F32) return by_kind<WT_F32>(pl, epi, xsrc, p, s);
   if (wt == WT_BF16) return by_kind<WT_BF16>(pl, epi, xsrc, p, s);

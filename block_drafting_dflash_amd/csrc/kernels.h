@@ -11,6 +11,7 @@ constexpr int GEMM_MAXSEG = 12;
 constexpr int GEMM_MAX_ROWS = 48;  // rows per GEMM launch (3 MFMA row tiles)
 constexpr int ATTN_CHUNK = 64;     // keys per attention work-group
 constexpr int ATTN_QG = 64;        // query vectors per attention pass
+constexpr int MAX_WINDOW = 4096;   // attention chunks of one query stay within the combine's LDS
 
 enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2 };
 
@@ -45,9 +46,7 @@ struct GemmParams {
   int32_t xstride;  // staged X row stride in LDS (elements)
   void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: act dtype [R, ldy]
   int64_t ldy;
-  unsigned long long* keys;  // ARGMAX: per-row running keys (zero between launches)
-  unsigned int* ticket;      // ARGMAX: arrival counter (zero between launches)
-  int32_t* idx_out;          // ARGMAX: [R]
+  unsigned long long* part;  // ARGMAX: per-work-group best keys, [R][grid]
 };
 
 // Launch shape of one GEMM: waves per work-group and, per wave and tile, nch chunks of ch
@@ -56,7 +55,7 @@ struct GemmParams {
 struct GemmPlan {
   int waves, ch, nch, tiles_per_wg, grid;
 };
-bool gemm_plan_supported(const GemmPlan& pl, int epi);
+bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc);
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, int tiles_per_wg);
 
@@ -70,7 +69,8 @@ struct AttnShape {
 
 // Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip).
 hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s);
-hipError_t launch_init_ws(unsigned long long* keys, int nkeys, unsigned int* ticket, hipStream_t s);
+// idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
+hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
                         float* x, hipStream_t s);
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,

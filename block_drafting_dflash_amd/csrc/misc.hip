@@ -5,13 +5,35 @@
 
 namespace dflash {
 
-__global__ void init_ws_kernel(unsigned long long* keys, int nkeys, unsigned int* ticket) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nkeys; i += gridDim.x * blockDim.x) keys[i] = 0ull;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+// One work-group per row: the largest (value, index) key over the lm_head work-groups'
+// partial keys; the key order puts the larger logit first and then the lower index.
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* __restrict__ part, int groups,
+                                                             int32_t* idx) {
+  __shared__ unsigned long long red[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const unsigned long long* row = part + (size_t)r * groups;
+  unsigned long long best = 0ull;
+#pragma unroll 4
+  for (int g = tid; g < groups; g += 256) {
+    const unsigned long long k = row[g];
+    best = k > best ? k : best;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long k = shfl_xor_u64(best, o);
+    best = k > best ? k : best;
+  }
+  if (lane == 0) red[w] = best;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long b = red[0];
+    for (int i = 1; i < 4; ++i) b = red[i] > b ? red[i] : b;
+    idx[r] = argmax_key_index(b);
+  }
 }
 
-hipError_t launch_init_ws(unsigned long long* keys, int nkeys, unsigned int* ticket, hipStream_t s) {
-  hipLaunchKernelGGL(init_ws_kernel, dim3(4), dim3(256), 0, s, keys, nkeys, ticket);
+hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s) {
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(R), dim3(256), 0, s, part, groups, idx);
   return hipGetLastError();
 }
 

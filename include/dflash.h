@@ -14,8 +14,9 @@
  *
  * Conventions for every call:
  *  - Device pointers point to device memory owned by the caller (PyTorch or hipMalloc).
- *    The library never allocates device memory: the caller sizes the ring and the
- *    workspace with dflash_query_sizes and keeps every buffer alive while the context is.
+ *    The library never allocates device memory: the caller sizes the ring, the workspace
+ *    and the packed weights with dflash_query_sizes and keeps them alive while the
+ *    context is.
  *  - `stream` is a hipStream_t (NULL = the default stream). Device calls only enqueue
  *    work; outputs are valid once the caller has synchronised the stream.
  *  - Every call returns a status. On error nothing is enqueued and the context is
@@ -57,9 +58,10 @@ typedef enum {
  * every element count fits an int32 (lablup/mlxcel #1762, Pre-merge review round, third
  * finding: dimensions that would wrap an i32 are refused).
  *   hidden, intermediate, q_heads*head_dim, target_streams*target_width: multiples of
- *     128 (of 512 for DFLASH_Q4G64); each is either <= 2048 or a multiple of 2048.
- *   head_dim: even, <= 256. q_heads a multiple of kv_heads.
- *   window W >= 1: keys at absolute position p are visible to a query at q iff
+ *     256 for bf16 weights (128 for f32) with a launch plan (every C1-style shape has
+ *     one); hidden, intermediate, q/kv_heads*head_dim and vocab multiples of 16.
+ *   head_dim: a multiple of 16, at most 128. q_heads a multiple of kv_heads.
+ *   window W, 1..4096: keys at absolute position p are visible to a query at q iff
  *     |q - p| <= W (lablup/mlxcel #1762, What changed).
  *   max_block: largest block a draft may use, 1..256. The ring's slack is
  *     S = max(clamp(8*max_block, 32, 128), max_block) rows and its capacity C = W + S
