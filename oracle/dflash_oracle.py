@@ -39,10 +39,15 @@ What the round computes (readings where the pages are silent are marked READING)
     trim(block_size - n)].
   * ring slack S = max(clamp(8 B, 32, 128), B) and trim = offset rewind with no restore
     [muse, What changed; Pre-merge review round, second finding].
-  * READING (precision): C0-style f32 shapes have no casts. bf16 shapes round to bf16
-    (nearest, ties to even) at: every GEMM operand (residual slab, encoder output, norm
-    outputs, attention output, SwiGLU output, verify rows), K/V written to the ring, and
-    the block's q/k/v before attention. Everything else is exact f64 here.
+  * READING (precision): activations are real numbers (f64 here). bf16 shapes round to
+    bf16 (nearest, ties to even) only where a value is stored in the cache dtype: the
+    context K/V written to the ring and the block's own k/v, which are attended next to
+    them. Inputs arrive in their storage dtype (the residual slab, the verify rows, the
+    embedding table and the weights are bf16 values already). f32 shapes round nothing.
+    Rounding computed activations to bf16 before every contraction would make any two
+    correct implementations drift apart by about 1e-2 in the logits at the Muse-shaped
+    sizes (each differently rounded operand flips further roundings downstream), so the
+    argmax could not be compared exactly above a 1e-2 margin.
 """
 from __future__ import annotations
 
@@ -219,14 +224,15 @@ class OracleDrafter:
         return np.asarray(self.w[name], dtype=F64)
 
     def _act(self, x):
+        """Rounding to the storage dtype (cache K/V; inputs given in that dtype)."""
         return cast(x, self.sh.act_dtype)
 
     # -- pieces --------------------------------------------------------------------------
     def encode(self, resid: np.ndarray) -> np.ndarray:
-        """encoder.fc then encoder.output_norm_enc, per row; returns the bf16/f32 operand."""
+        """encoder.fc then encoder.output_norm_enc, per row (rows given in the storage dtype)."""
         r = self._act(np.asarray(resid, dtype=F64))
         h = r @ self._lin("fc").T
-        return self._act(rms_norm(h, self._gain("enc_norm"), self.sh.rms_eps))
+        return rms_norm(h, self._gain("enc_norm"), self.sh.rms_eps)
 
     def context_kv(self, c: np.ndarray, pos: np.ndarray, layer: int) -> Tuple[np.ndarray, np.ndarray]:
         """Per-layer context K/V of encoder rows c at absolute positions pos (ring dtype)."""
@@ -239,11 +245,11 @@ class OracleDrafter:
         return self._act(k), self._act(v)
 
     def lm_head_logits(self, rows: np.ndarray, chunk: int = 16384) -> np.ndarray:
-        """f64 logits of operand rows through the untied lm_head (no softcap)."""
-        z = self._act(np.asarray(rows, dtype=F64))
+        """f64 logits of rows through the untied lm_head (no softcap)."""
+        z = np.asarray(rows, dtype=F64)
         V = self.sh.vocab
         out = np.empty((z.shape[0], V), dtype=F64)
-        if "lm_head" in self._cache or V <= chunk:
+        if "lm_head" in self._cache or V <= chunk or self._cache_f64:
             out[:] = z @ self._lin("lm_head").T
             return out
         for s in range(0, V, chunk):
@@ -327,15 +333,15 @@ class OracleDrafter:
         kpos = np.concatenate([ctx_pos, qpos])
         out = np.zeros((R, sh.q_heads, sh.head_dim), dtype=F64)
         scale = 1.0 / np.sqrt(sh.head_dim)
+        # vis[j, i]: key i is visible to query row j; an invisible key gets weight exactly 0
+        vis = np.abs(qpos[:, None] - kpos[None, :]) <= self.W
         for h in range(sh.q_heads):
             g = h // group
             keys = np.concatenate([self.K[layer, g, ctx_slots, :], kb[:, g, :]], axis=0)
             vals = np.concatenate([self.V[layer, g, ctx_slots, :], vb[:, g, :]], axis=0)
-            for j in range(R):
-                vis = np.abs(qpos[j] - kpos) <= self.W
-                s = (keys[vis] @ q[j, h]) * scale
-                p = np.exp(s - s.max())
-                out[j, h] = (p / p.sum()) @ vals[vis]
+            s = np.where(vis, (q[:, h, :] @ keys.T) * scale, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[:, h] = (p / p.sum(axis=1, keepdims=True)) @ vals
         return out
 
     def draft(self, anchor: int, block: int) -> DraftResult:
@@ -355,17 +361,17 @@ class OracleDrafter:
         nq, nkv, hd = sh.q_heads, sh.kv_heads, sh.head_dim
         for l in range(sh.layers):
             p = f"layers.{l}."
-            h = self._act(rms_norm(x, self._gain(p + "in_norm"), sh.rms_eps))
+            h = rms_norm(x, self._gain(p + "in_norm"), sh.rms_eps)
             q = (h @ self._lin(p + "q").T).reshape(R, nq, hd)
             kb = (h @ self._lin(p + "k").T).reshape(R, nkv, hd)
             vb = (h @ self._lin(p + "v").T).reshape(R, nkv, hd)
-            q = self._act(rope_neox(rms_norm(q, self._gain(p + "q_norm"), sh.rms_eps), qpos, sh.rope_theta))
+            q = rope_neox(rms_norm(q, self._gain(p + "q_norm"), sh.rms_eps), qpos, sh.rope_theta)
             kb = self._act(rope_neox(rms_norm(kb, self._gain(p + "k_norm"), sh.rms_eps), qpos, sh.rope_theta))
             vb = self._act(vb)
-            o = self._act(self._attention(l, q, kb, vb, qpos).reshape(R, nq * hd))
+            o = self._attention(l, q, kb, vb, qpos).reshape(R, nq * hd)
             x = x + o @ self._lin(p + "o").T
-            h2 = self._act(rms_norm(x, self._gain(p + "post_norm"), sh.rms_eps))
-            a = self._act(silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T))
+            h2 = rms_norm(x, self._gain(p + "post_norm"), sh.rms_eps)
+            a = silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)
             x = x + a @ self._lin(p + "down").T
         z = rms_norm(x[1:], self._gain("final_norm"), sh.rms_eps)
         logits = self.lm_head_logits(z)
@@ -374,8 +380,9 @@ class OracleDrafter:
                            logits_top=logits[np.arange(block), idx])
 
     def lm_head_argmax(self, rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-        """argmax over the vocabulary of rows through the shared lm_head, and margins."""
-        logits = self.lm_head_logits(rows)
+        """argmax over the vocabulary of rows (given in the storage dtype) through the shared
+        lm_head, and margins."""
+        logits = self.lm_head_logits(self._act(np.asarray(rows, dtype=F64)))
         idx, margin = argmax_with_margin(logits)
         return idx.astype(np.int64), margin
 

@@ -1,0 +1,77 @@
+"""GPU parity at the Muse-shaped full sizes (hidden 2048, 5 layers, 32q/4kv x 128, I 6144,
+vocab 202048, fc 5 x 4096 -> 2048, window 2048), in the launch configuration the bench
+times, in lock-step with the CPU oracle.
+
+Every round compares every drafted token (exact above the 1e-2 near-tie margin), the
+final hidden rows (2e-2 relative per row), the verify result, the cache offsets, and after
+every trim the whole live K/V window of all five layers. Round counts are bounded so each
+test stays within about a minute of oracle time on 16 host cores.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_drafting_dflash_amd import binding, synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+SH = synth.MUSE_BF16
+
+
+@pytest.fixture(scope="module")
+def muse():
+    w = synth.make_weights(SH)
+    dev = binding.to_device(SH, w)
+    # the oracle reads linears in f64: convert them once for all tests of this module
+    w64 = {k: (np.asarray(v, dtype=np.float64) if k != "embed" and getattr(v, "ndim", 0) == 2 else v)
+           for k, v in w.items()}
+    del w
+    return w64, dev
+
+
+def _report(name, ls, ks):
+    print(f"{name}: rounds {len(ks)} mean k {np.mean(ks):.3f} stats {ls.stats}", flush=True)
+
+
+def test_block4_ctx1024_lm_head_verify(muse):
+    """Block 4 after a 1024-row context; verify rows N(0,1) through the shared lm_head."""
+    w64, dev = muse
+    wl = synth.WORKLOADS["muse-bf16-b4-ctx1024"]
+    ls = P.LockStep(SH, w64, max_block=4, dev_weights=dev)
+    ks = P.run_lm_head_rounds(ls, wl.context, 4, wl.rounds)
+    _report(wl.name, ls, ks)
+    assert ls.stats.rows_checked == wl.rounds * (4 + 5)
+
+
+def test_block16_ctx4096_synthetic_accept(muse):
+    """Block 16 after a 4096-row prefill (2048 kept); p = 0.6 prefix-broken stand-in target."""
+    w64, dev = muse
+    wl = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
+    ls = P.LockStep(SH, w64, max_block=16, dev_weights=dev)
+    ks = P.run_synthetic_rounds(ls, wl.context, 16, 48, p=wl.accept_p)
+    _report(wl.name, ls, ks)
+    assert any(k > 0 for k in ks)
+    assert ls.gpu.cache_state()[0] == wl.context + sum(k + 1 for k in ks)
+
+
+@pytest.mark.parametrize("block,rounds", [(8, 48), (32, 24)])
+def test_ctx16384_forced_wraps_random_depth(muse, block, rounds):
+    """16384-row prefill slab (drop-then-project keeps 2048), a ring phase that puts the
+    first round's append across the last slot, trims of random depth, then the deepest
+    legal rewind (S rows appended and all rewound) and one more round."""
+    w64, dev = muse
+    wl = synth.WORKLOADS["muse-bf16-ctx16384-wrap"]
+    S = max(min(max(8 * block, 32), 128), block)
+    C = SH.window + S
+    phase = synth.ring_phase_for_wrap(C, wl.context, block + 1)
+    ls = P.LockStep(SH, w64, max_block=block, phase=phase, dev_weights=dev)
+    ks = P.run_random_depth_rounds(ls, wl.context, block, rounds, tag=block)
+    e0 = ls.gpu.cache_state()[0]
+    ls.append(synth.resid_rows(SH, S, 90_000 + block))
+    ls.trim(S)
+    assert ls.gpu.cache_state()[:2] == (e0, 0)
+    ks += P.run_random_depth_rounds(ls, 0, block, 2, tag=500 + block, prefill=False)
+    _report(f"{wl.name} block {block}", ls, ks)
+    first_slot = (wl.context + phase) % C
+    assert first_slot + block + 1 > C  # the first append did straddle the ring end

@@ -107,3 +107,35 @@ def test_boundary_errors_leave_state_unchanged(micro_f32_w):
     out = g.verify_greedy(torch.tensor([1, 2], dtype=torch.int32, device="cuda"),
                           torch.tensor([1, sh.vocab, 0], dtype=torch.int32, device="cuda"), 2)
     assert out.cpu().tolist() == [0, -1, 1]
+
+
+def test_outputs_do_not_depend_on_ring_phase(micro_bf16_w):
+    """Drafted tokens, hidden rows and the live window are bit-identical for ring phases
+    0, 1, C-1 and a random one: the slot of a position never changes what is computed."""
+    sh, block, context, rounds = MICRO_BF16, 8, 50, 12
+    C = sh.window + max(min(max(8 * block, 32), 128), block)
+    dev = binding.to_device(sh, micro_bf16_w)
+    phases = (0, 1, C - 1, int(np.random.default_rng(synth.SEED_PHASE).integers(2, C - 1)))
+    runs = []
+    for phase in phases:
+        g = binding.Drafter(sh, dev, max_block=block, phase=phase)
+        g.cache_append(torch.from_numpy(synth.resid_rows(sh, context, 0)).to(torch.bfloat16).cuda(), commit=True)
+        anchor, outs = synth.anchor_token(sh), []
+        for r in range(rounds):
+            h = torch.empty((block + 1, sh.hidden), dtype=torch.float32, device="cuda")
+            d = g.draft_block(anchor, block, hidden=h).cpu().numpy()
+            a = P.target_with_accept_length(d, synth.random_depth_k(block, r), sh.vocab, tail=r)
+            out = g.verify_greedy(torch.from_numpy(d).cuda(), torch.from_numpy(a.astype(np.int32)).cuda(), block)
+            k, bonus, _ = out.cpu().tolist()
+            g.cache_append(torch.from_numpy(synth.resid_rows(sh, block + 1, r + 1)).to(torch.bfloat16).cuda())
+            g.cache_trim(block - k)
+            outs.append((d, h.cpu(), k))
+            anchor = bonus
+        kv = [g.cache_read(l) for l in range(sh.layers)]
+        runs.append((outs, [(k.cpu(), v.cpu()) for k, v in kv], g.cache_state()))
+    for phase, (outs, kv, st) in zip(phases[1:], runs[1:]):
+        assert st == runs[0][2], phase
+        for (d0, h0, k0), (d1, h1, k1) in zip(runs[0][0], outs):
+            assert np.array_equal(d0, d1) and k0 == k1 and torch.equal(h0, h1), phase
+        for (k0, v0), (k1, v1) in zip(runs[0][1], kv):
+            assert torch.equal(k0, k1) and torch.equal(v0, v1), phase

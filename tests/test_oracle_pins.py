@@ -236,12 +236,12 @@ def test_forward_bf16_matches_torch_formulation(micro_bf16_w):
     od, hist, anchor = _run_rounds(sh, micro_bf16_w, 17, 4, rounds=5, phase=3, seed=5)
     res = od.draft(anchor, 4)
     hid, logits = TorchDrafter(sh, micro_bf16_w).forward(hist, anchor, 4)
-    # the torch cast goes f64 -> f32 -> bf16 (rare double rounding), hence a loose bound
-    rel = np.linalg.norm(res.hidden - hid, axis=1) / np.linalg.norm(hid, axis=1)
-    assert rel.max() < 1e-3
+    # only the cached K/V are rounded to bf16; on these seeded inputs torch's f64 -> f32 ->
+    # bf16 conversion rounds every one of them as the oracle's direct rounding does
+    np.testing.assert_allclose(res.hidden, hid, rtol=1e-12, atol=1e-12)
     idx = np.argmax(logits, axis=1)
-    ok = res.margins > 1e-3
-    assert np.array_equal(res.tokens[ok], idx[ok])
+    assert np.array_equal(res.tokens, idx)
+    np.testing.assert_allclose(res.logits_top, logits[np.arange(4), idx], rtol=1e-12)
 
 
 def test_uniform_query_attention_counts_the_inclusive_window(micro_w):

@@ -4,7 +4,9 @@ Used only to pin the oracle. It keeps no ring at all: it holds the whole committ
 history of residual rows, recomputes every context K/V from it, and attends with an
 explicit boolean [queries, keys] mask over absolute positions, through
 torch.nn.functional.scaled_dot_product_attention (GQA via enable_gqa). RoPE is written
-as a complex rotation of the (i, i + hd/2) pairs. Everything runs in float64 on the CPU.
+as a complex rotation of the (i, i + hd/2) pairs. Everything runs in float64 on the CPU;
+bf16 shapes round the inputs and the cached K/V (context and block) to bf16 through torch's
+own conversion.
 """
 from __future__ import annotations
 
@@ -46,7 +48,7 @@ class TorchDrafter:
         """K/V of every committed row, positions 0..n-1, per layer."""
         sh = self.sh
         r = self._c(_t(history))
-        c = self._c(self._rms(F.linear(r, self.w["fc"]), "enc_norm"))
+        c = self._rms(F.linear(r, self.w["fc"]), "enc_norm")
         pos = np.arange(r.shape[0])
         out = []
         for l in range(sh.layers):
@@ -69,21 +71,21 @@ class TorchDrafter:
         x = F.embedding(ids, self.w["embed"])
         for l in range(sh.layers):
             p = f"layers.{l}."
-            h = self._c(self._rms(x, p + "in_norm"))
+            h = self._rms(x, p + "in_norm")
             q = F.linear(h, self.w[p + "q"]).unflatten(-1, (sh.q_heads, sh.head_dim))
             k = F.linear(h, self.w[p + "k"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
             v = F.linear(h, self.w[p + "v"]).unflatten(-1, (sh.kv_heads, sh.head_dim))
-            q = self._c(self._rope(self._rms(q, p + "q_norm"), qpos))
+            q = self._rope(self._rms(q, p + "q_norm"), qpos)
             k = self._c(self._rope(self._rms(k, p + "k_norm"), qpos))
             v = self._c(v)
             kall = torch.cat([ctx[l][0], k], dim=0).transpose(0, 1)[None]  # [1, nkv, Nk, hd]
             vall = torch.cat([ctx[l][1], v], dim=0).transpose(0, 1)[None]
             o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], kall, vall,
                                                attn_mask=mask, enable_gqa=True)
-            o = self._c(o[0].transpose(0, 1).flatten(-2))
+            o = o[0].transpose(0, 1).flatten(-2)
             x = x + F.linear(o, self.w[p + "o"])
-            h2 = self._c(self._rms(x, p + "post_norm"))
-            a = self._c(F.silu(F.linear(h2, self.w[p + "gate"])) * F.linear(h2, self.w[p + "up"]))
+            h2 = self._rms(x, p + "post_norm")
+            a = F.silu(F.linear(h2, self.w[p + "gate"])) * F.linear(h2, self.w[p + "up"])
             x = x + F.linear(a, self.w[p + "down"])
-        z = self._c(self._rms(x[1:], "final_norm"))
+        z = self._rms(x[1:], "final_norm")
         return x.numpy(), F.linear(z, self.w["lm_head"]).numpy()
