@@ -21,10 +21,12 @@ namespace dflash {
 
 // ---- q/k RMSNorm + RoPE on the block rows -----------------------------------------------
 // One wave per (row, head). Lane i < hd/2 owns the rotate-half pair (i, i + hd/2).
+// q leaves as an attention operand (hi/lo bf16 planes, or f32); k and v are rounded to the
+// cache dtype, as they sit next to the ring's keys and values.
 template <bool BF>
 __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float* __restrict__ qkv,
                                                         const void* qnorm, const void* knorm, int R,
-                                                        int64_t pos0, void* qb, void* kb, void* vb) {
+                                                        int64_t pos0, void* qb, void* qlo, void* kb, void* vb) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int heads = a.nq + 2 * a.nkv;
@@ -55,10 +57,15 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float
   sincos((double)(pos0 + r) * inv, &sn, &cs);
   const float c = (float)cs, sf = (float)sn;
   const float y1 = x1 * c - x2 * sf, y2 = x2 * c + x1 * sf;
-  void* dst = is_q ? qb : kb;
-  const size_t o = is_q ? ((size_t)r * a.nq + h) * hd : ((size_t)r * a.nkv + (h - a.nq)) * hd;
-  act_st<BF>(dst, o + lane, y1);
-  act_st<BF>(dst, o + lane + half, y2);
+  if (is_q) {
+    const size_t o = ((size_t)r * a.nq + h) * hd;
+    op_st<BF>(qb, qlo, o + lane, y1);
+    op_st<BF>(qb, qlo, o + lane + half, y2);
+  } else {
+    const size_t o = ((size_t)r * a.nkv + (h - a.nq)) * hd;
+    act_st<BF>(kb, o + lane, y1);
+    act_st<BF>(kb, o + lane + half, y2);
+  }
 }
 
 // ---- context K/V into the ring ----------------------------------------------------------
@@ -110,8 +117,8 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
 // [nkv][nchunks][R*G][hd + 2] = (unnormalised output, m, l).
 template <bool BF>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const void* ring_layer, const void* qb,
-                                                           const void* kb, const void* vb, int R, int64_t e,
-                                                           int nchunks, float* __restrict__ part) {
+                                                           const void* qlo, const void* kb, const void* vb, int R,
+                                                           int64_t e, int nchunks, float* __restrict__ part) {
   extern __shared__ __align__(16) float sm[];
   const int g = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -163,7 +170,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
     for (int i = tid; i < nq * hd; i += blockDim.x) {
       const int qi = i / hd, d = i - qi * hd;
       const int gq = q0 + qi, r = gq / G, hh = gq - r * G;
-      Qs[qi * hd + d] = act_ld<BF>(qb, ((size_t)r * a.nq + (size_t)g * G + hh) * hd + d);
+      const size_t qo = ((size_t)r * a.nq + (size_t)g * G + hh) * hd + d;
+      if constexpr (BF) Qs[qi * hd + d] = bf2f(((const uint16_t*)qb)[qo]) + bf2f(((const uint16_t*)qlo)[qo]);
+      else Qs[qi * hd + d] = ((const float*)qb)[qo];
     }
     __syncthreads();
     // scores: thread -> key lane, queries strided by waves
@@ -215,17 +224,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
 // ---- attention on MFMA (bf16 operands): one work-group per (128-key chunk, kv head) -------
 // Scores are formed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, K rows from LDS, Q rows
 // from L2), so each lane ends up holding 4 keys x 1 query: exactly the B-operand layout of
-// the 16x16x16 MFMA that forms O^T = V^T P^T. P (in [0, 1]) enters as a bf16 pair
-// hi + lo, which keeps about 16 significant bits; V and K are bf16 already, products are
-// exact and sums are f32. Each wave owns query tiles w, w+4, ...
+// the 16x16x16 MFMA that forms O^T = V^T P^T. Q (an f32 activation) and P (in [0, 1])
+// enter as bf16 pairs hi + lo, which keep about 16 significant bits; V and K are bf16
+// already, products are exact and sums are f32. Each wave owns query tiles w, w+4, ...
 constexpr int AM_CH = 128;  // keys per work-group
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
-                                                        const uint16_t* __restrict__ qb, const uint16_t* __restrict__ kb,
-                                                        const uint16_t* __restrict__ vb, int R, int64_t e, int nchunks,
-                                                        float* __restrict__ part) {
+                                                        const uint16_t* __restrict__ qb, const uint16_t* __restrict__ qlo,
+                                                        const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                                        int R, int64_t e, int nchunks, float* __restrict__ part) {
   constexpr int KST = HD + 8;      // K row stride (elements): rows land 4 banks apart
   constexpr int VST = AM_CH + 4;   // V^T row stride (elements)
   __shared__ __align__(16) uint16_t Kl[AM_CH * KST];
@@ -291,12 +300,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
     const bool qok = qv < NQ;
     const int r = qok ? qv / G : 0, hh = qv - r * G;
     const int64_t qpos = e + r;
-    u32x4_t qf[HD / 32];
-    const uint16_t* qrow = qb + ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
+    u32x4_t qf[HD / 32], qfl[HD / 32];
+    const size_t qo = ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s) {
       qf[s] = u32x4_t{0u, 0u, 0u, 0u};
-      if (qok) qf[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * lg);
+      qfl[s] = u32x4_t{0u, 0u, 0u, 0u};
+      if (qok) {
+        qf[s] = *(const u32x4_t*)(qb + qo + 32 * s + 8 * lg);
+        qfl[s] = *(const u32x4_t*)(qlo + qo + 32 * s + 8 * lg);
+      }
     }
     f32x4_t S[AM_CH / 16];
     float m = -INFINITY;
@@ -307,6 +320,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
       for (int s = 0; s < HD / 32; ++s) {
         const u32x4_t kf = *(const u32x4_t*)&Kl[(kt * 16 + li) * KST + 32 * s + 8 * lg];
         acc = mfma_bf16(kf, qf[s], acc);
+        acc = mfma_bf16(kf, qfl[s], acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -365,11 +379,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
 }
 
 // ---- combine chunks in chunk order --------------------------------------------------------
-// One work-group (hd threads) per (row, query head); out: act [R, nq*hd]. The chunk maxima
-// and sums are staged in LDS first so the output loop issues independent loads.
+// One work-group (hd threads) per (row, query head); out: the O-projection operand [R,
+// nq*hd] (hi/lo bf16 planes, or f32). The chunk maxima and sums are staged in LDS first so
+// the output loop issues independent loads.
 constexpr int COMBINE_MAX_CHUNKS = 80;
 template <bool BF>
-__global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part, int R, int nchunks, void* out) {
+__global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part, int R, int nchunks, void* out,
+                                    void* out_lo) {
   __shared__ float sm_m[COMBINE_MAX_CHUNKS], sm_l[COMBINE_MAX_CHUNKS];
   const int item = blockIdx.x;
   const int r = item / a.nq, h = item - r * a.nq;
@@ -393,7 +409,7 @@ __global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part,
     L += sm_l[c] * f;
     O += base[c * stride + d] * f;
   }
-  act_st<BF>(out, (size_t)r * a.nq * hd + (size_t)h * hd + d, O / L);
+  op_st<BF>(out, out_lo, (size_t)r * a.nq * hd + (size_t)h * hd + d, O / L);
 }
 
 // ---- live window read-back (parity checks) -----------------------------------------------
@@ -420,11 +436,13 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
 
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
-                            int R, int64_t pos0, void* qb, void* kb, void* vb, hipStream_t s) {
+                            int R, int64_t pos0, void* qb, void* qlo, void* kb, void* vb, hipStream_t s) {
   const int items = R * (a.nq + 2 * a.nkv);
   const int grid = (items + 3) / 4;
-  if (bf) hipLaunchKernelGGL(attn_prep_kernel<true>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, kb, vb);
-  else hipLaunchKernelGGL(attn_prep_kernel<false>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, kb, vb);
+  if (bf)
+    hipLaunchKernelGGL(attn_prep_kernel<true>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo, kb, vb);
+  else
+    hipLaunchKernelGGL(attn_prep_kernel<false>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo, kb, vb);
   return hipGetLastError();
 }
 
@@ -451,21 +469,22 @@ size_t attention_partial_floats(const AttnShape& a, int R) {
   return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * (a.hd + 2);
 }
 
-hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* kb,
-                            const void* vb, int R, int64_t e, float* part, void* out, hipStream_t s) {
+hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* qlo,
+                            const void* kb, const void* vb, int R, int64_t e, float* part, void* out, void* out_lo,
+                            hipStream_t s) {
   const int nch = attn_nchunks(bf, a, R, e);
   dim3 grid(nch, a.nkv);
   if (use_mfma(bf, a)) {
     const uint16_t* rl = (const uint16_t*)ring_layer;
     if (a.hd == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)kb,
-                         (const uint16_t*)vb, R, e, nch, part);
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
+                         (const uint16_t*)kb, (const uint16_t*)vb, R, e, nch, part);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)kb,
-                         (const uint16_t*)vb, R, e, nch, part);
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
+                         (const uint16_t*)kb, (const uint16_t*)vb, R, e, nch, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
+    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
     return hipGetLastError();
   }
   const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4 +
@@ -478,12 +497,14 @@ hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, 
     if (err != hipSuccess) return err;
     attr_set[bf ? 1 : 0] = true;
   }
-  if (bf) hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, kb, vb, R, e, nch, part);
-  else hipLaunchKernelGGL(attn_partial_kernel<false>, grid, dim3(256), lds, s, a, ring_layer, qb, kb, vb, R, e, nch, part);
+  if (bf)
+    hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, kb, vb, R, e, nch, part);
+  else
+    hipLaunchKernelGGL(attn_partial_kernel<false>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, kb, vb, R, e, nch, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (bf) hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
-  else hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out);
+  if (bf) hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
+  else hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
   return hipGetLastError();
 }
 

@@ -29,6 +29,26 @@ template <bool BF16> __device__ __forceinline__ void act_st(void* p, int64_t i, 
   else ((float*)p)[i] = v;
 }
 
+// ---- f32 operands for bf16 MFMA ---------------------------------------------------------
+// An f32 value v travels as the bf16 pair hi = bf16(v), lo = bf16(v - hi): v - hi is exact
+// in f32, so hi + lo carries about 16 significant bits (relative error <= 2^-17) and a
+// product with a bf16 weight costs two exact MFMA products instead of one rounded operand.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+// Store of an activation operand: two bf16 planes (SPLIT) or f32.
+template <bool SPLIT> __device__ __forceinline__ void op_st(void* hi, void* lo, int64_t i, float v) {
+  if constexpr (SPLIT) {
+    uint16_t h, l;
+    split_bf16(v, h, l);
+    ((uint16_t*)hi)[i] = h;
+    ((uint16_t*)lo)[i] = l;
+  } else {
+    ((float*)hi)[i] = v;
+  }
+}
+
 // ---- MFMA (A = activations [16 rows x k], B = weights [k x 16 cols]) ---------------------
 // 16x16x32 bf16: lane l supplies A[l%16][8*(l/16)+j] and B[8*(l/16)+j][l%16], j = 0..7;
 // result element q of lane l is D[4*(l/16)+q][l%16]. Products are exact, sums in f32.

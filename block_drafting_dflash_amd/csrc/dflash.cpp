@@ -31,7 +31,7 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t argmax_part, knorm_ptrs, x, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_c, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_c, app_kv, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -162,6 +162,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   GemmPlan pl;
   const struct { int epi, xsrc; int64_t K; } gemms[] = {
       {EPI_STORE, XSRC_NORM, H},           {EPI_RESID, XSRC_GLOBAL, qd},  {EPI_SWIGLU, XSRC_NORM, H},
+      {EPI_SWIGLU, XSRC_GLOBAL, H},
       {EPI_RESID, XSRC_GLOBAL, c->intermediate}, {EPI_STORE, XSRC_GLOBAL, fin}, {EPI_STORE, XSRC_GLOBAL, H},
       {EPI_ARGMAX, XSRC_LDS, H}};
   for (const auto& gm : gemms)
@@ -205,17 +206,20 @@ Layout make_layout(const Cfg& g) {
   // per-work-group argmax keys of one lm_head launch: <= 32 rows x <= V/16 work-groups
   L.argmax_part = take(sizeof(unsigned long long) * 32 * (size_t)(c.vocab / 16));
   L.knorm_ptrs = take(sizeof(void*) * c.layers);
+  // operand buffers (q, attention output, SwiGLU output, normed rows) hold 4 bytes per
+  // element: f32, or for bf16 shapes a hi plane followed by a lo plane (see lo_plane)
   L.x = take(4 * R * H);
+  L.hn = take(4 * R * H);  // normed rows of launches past one row tile
   L.qkv = take(4 * R * (qd + 2 * kvd));
-  L.qb = take(ae * R * qd);
+  L.qb = take(4 * R * qd);
   L.kb = take(ae * R * kvd);
   L.vb = take(ae * R * kvd);
-  L.attn = take(ae * R * qd);
-  L.mlp = take(ae * R * c.intermediate);
-  L.zrows = take(ae * R * H);  // final-normed drafted rows (lm_head operand)
+  L.attn = take(4 * R * qd);
+  L.mlp = take(4 * R * c.intermediate);
+  L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
-  L.app_c = take(ae * (size_t)GEMM_MAX_ROWS * H);
+  L.app_c = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
   L.total = o;
   return L;
@@ -259,6 +263,11 @@ PackedLayout make_packed_layout(const Cfg& g) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// lo plane of an operand buffer of rows x ld elements (bf16 shapes), or NULL (f32 shapes)
+void* lo_plane(const Cfg& g, void* base, size_t rows, size_t ld) {
+  return g.bf ? (unsigned char*)base + rows * ld * 2 : nullptr;
+}
+
 dflash_status dev(dflash_ctx* ctx, hipError_t e, const char* what) {
   if (e == hipSuccess) return DFLASH_OK;
   return fail(ctx, DFLASH_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -275,17 +284,35 @@ struct GemmCall {
   void* y;
   int64_t ldy;  // elements
   int32_t* idx;
+  int split = 0;  // operands are hi/lo bf16 pairs (x/xlo planes, or formed by the norm prologue)
+  const void* xlo = nullptr;
+  void* ylo = nullptr;
 };
 
-dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_t st) {
+dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
   const Cfg& g = ctx->cfg;
+  GemmCall gc = gc_in;
+  if (gc.xsrc == XSRC_NORM && gc.split && rows > 16) {
+    // hi/lo operand pairs of more than one row tile would not stay in registers: normalise
+    // the rows once into planes (the same bits as the fused prologue) and stream them
+    void* hn = ctx->ws + ctx->lay.hn;
+    void* hn_lo = lo_plane(g, hn, g.R, gc.K);
+    const dflash_status s0 =
+        dev(ctx, launch_rownorm(1, (const float*)gc.x, gc.gain, g.c.rms_eps, rows, gc.K, hn, hn_lo, st), "row norm");
+    if (s0 != DFLASH_OK) return s0;
+    gc.xsrc = XSRC_GLOBAL;
+    gc.x = hn;
+    gc.xlo = hn_lo;
+    gc.ldx = gc.K;
+    gc.gain = nullptr;
+  }
   const int wt = g.wt;
   const int nb = gc.epi == EPI_SWIGLU ? 2 : 1;
   GemmPlan plan;
   if (!plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
   const int waves = plan.waves;
   const int xstride = gc.K + 16 / g.act_elt;
-  const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;
+  const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;  // a split operand is two bf16 planes
   const size_t y_elt = gc.epi == EPI_SWIGLU ? g.act_elt : 4;
   int N = 0;
   for (const auto& s : gc.segs) N = std::max(N, s.col0 + s.rows);
@@ -304,19 +331,27 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc, int rows, hipStream_
     p.K = gc.K;
     p.R = rc;
     p.waves = waves;
+    p.split = gc.split;
     p.x = (const unsigned char*)gc.x + (size_t)r0 * gc.ldx * x_elt;
+    p.xlo = gc.xlo ? (const unsigned char*)gc.xlo + (size_t)r0 * gc.ldx * x_elt : nullptr;
     p.ldx = gc.ldx;
     p.gain = gc.gain;
     p.eps = g.c.rms_eps;
     p.xstride = xstride;
     GemmPlan pl = plan;
     pl.grid = p.ntiles;
+    if (gc.xsrc == XSRC_NORM && gc.split && nb == 2 && p.ntiles % 2 == 0) {
+      // the normed gate/up pair with hi/lo operands: two tiles per work-group
+      pl.tiles_per_wg = 2;
+      pl.grid = p.ntiles / 2;
+    }
     if (gc.epi == EPI_ARGMAX) {
       p.part = (unsigned long long*)(ctx->ws + ctx->lay.argmax_part);
       pl.tiles_per_wg = argmax_tiles_per_wg(p.ntiles, rc);
       pl.grid = (p.ntiles + pl.tiles_per_wg - 1) / pl.tiles_per_wg;
     } else {
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
+      p.ylo = gc.ylo ? (unsigned char*)gc.ylo + (size_t)r0 * gc.ldy * y_elt : nullptr;
       p.ldy = gc.ldy;
     }
     const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, pl, p, st);
@@ -499,18 +534,22 @@ dflash_status dflash_cache_append(dflash_ctx* ctx, const void* resid, int32_t n,
     const int rc = (int)std::min<int64_t>(GEMM_MAX_ROWS, n - r0);
     float* fc_out = (float*)(ctx->ws + ctx->lay.app_fc);
     void* cbuf = ctx->ws + ctx->lay.app_c;
+    void* cbuf_lo = lo_plane(g, cbuf, GEMM_MAX_ROWS, c.hidden);
     float* kv = (float*)(ctx->ws + ctx->lay.app_kv);
     GemmCall f{EPI_STORE, XSRC_GLOBAL, {seg(ctx->fc, 0, c.hidden)}, (int)F,
                (const unsigned char*)resid + (size_t)r0 * F * g.act_elt, F, nullptr, fc_out, c.hidden, nullptr};
     dflash_status s = run_gemm(ctx, f, rc, st);
     if (s != DFLASH_OK) return s;
-    s = dev(ctx, launch_rownorm(g.bf, fc_out, ctx->enc_norm, c.rms_eps, rc, c.hidden, cbuf, st), "encoder norm");
+    s = dev(ctx, launch_rownorm(g.bf, fc_out, ctx->enc_norm, c.rms_eps, rc, c.hidden, cbuf, cbuf_lo, st),
+            "encoder norm");
     if (s != DFLASH_OK) return s;
     // per-layer k/v projections of the encoder rows, six layers per launch
     for (int l0 = 0; l0 < c.layers; l0 += GEMM_MAXSEG / 2) {
       const int l1 = std::min(c.layers, l0 + GEMM_MAXSEG / 2);
       GemmCall kvc{EPI_STORE, XSRC_GLOBAL, {}, c.hidden, cbuf, c.hidden, nullptr,
                    kv + (size_t)l0 * 2 * kvd, kv_cols, nullptr};
+      kvc.split = g.bf;
+      kvc.xlo = cbuf_lo;
       for (int l = l0; l < l1; ++l) {
         kvc.segs.push_back(seg(ctx->layers[l].k, (l - l0) * 2 * kvd, kvd));
         kvc.segs.push_back(seg(ctx->layers[l].v, (l - l0) * 2 * kvd + kvd, kvd));
@@ -553,6 +592,9 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   void* vb = ctx->ws + ctx->lay.vb;
   void* attn = ctx->ws + ctx->lay.attn;
   void* mlp = ctx->ws + ctx->lay.mlp;
+  void* qb_lo = lo_plane(g, qb, g.R, qd);
+  void* attn_lo = lo_plane(g, attn, g.R, qd);
+  void* mlp_lo = lo_plane(g, mlp, g.R, c.intermediate);
   float* part = (float*)(ctx->ws + ctx->lay.part);
   const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.C * c.head_dim;
 
@@ -562,30 +604,42 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     const Layer& L = ctx->layers[l];
     GemmCall q{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
                L.in_norm, qkv, qd + 2 * kvd, nullptr};
+    q.split = g.bf;
     if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
-    s = dev(ctx, launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, kb, vb, st), "attn prep");
+    s = dev(ctx, launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, qb_lo, kb, vb, st), "attn prep");
     if (s != DFLASH_OK) return s;
-    s = dev(ctx, launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, kb, vb, R, ctx->e, part, attn, st),
+    s = dev(ctx,
+            launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, qb_lo, kb, vb, R, ctx->e, part, attn, attn_lo,
+                             st),
             "attention");
     if (s != DFLASH_OK) return s;
     GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
+    o.split = g.bf;
+    o.xlo = attn_lo;
     if ((s = run_gemm(ctx, o, R, st)) != DFLASH_OK) return s;
     GemmCall gu{EPI_SWIGLU, XSRC_NORM, {seg(L.gate, 0, c.intermediate), seg(L.up, 0, c.intermediate)}, H, x, H,
                 L.post_norm, mlp, c.intermediate, nullptr};
+    gu.split = g.bf;
+    gu.ylo = mlp_lo;
     if ((s = run_gemm(ctx, gu, R, st)) != DFLASH_OK) return s;
     GemmCall dn{EPI_RESID, XSRC_GLOBAL, {seg(L.down, 0, H)}, c.intermediate, mlp, c.intermediate, nullptr, x, H,
                 nullptr};
+    dn.split = g.bf;
+    dn.xlo = mlp_lo;
     if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
   }
   if (d_hidden) {
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
   }
-  // final RMSNorm of rows 1..B once, then the lm_head argmax over the bf16/f32 operand rows
+  // final RMSNorm of rows 1..B once, then the lm_head argmax over the operand rows
   void* zrows = ctx->ws + ctx->lay.zrows;
-  s = dev(ctx, launch_rownorm(g.bf, x + H, ctx->final_norm, c.rms_eps, block, H, zrows, st), "final norm");
+  void* zrows_lo = lo_plane(g, zrows, block, H);
+  s = dev(ctx, launch_rownorm(g.bf, x + H, ctx->final_norm, c.rms_eps, block, H, zrows, zrows_lo, st), "final norm");
   if (s != DFLASH_OK) return s;
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
+  lm.split = g.bf;
+  lm.xlo = zrows_lo;
   return run_gemm(ctx, lm, block, st);
 }
 

@@ -15,8 +15,10 @@
 // every wave keeps the next chunk of weights in flight while it multiplies the current
 // one, and the compiler's wait counts stay exact (a loop back-edge would make it drain
 // the prefetch at every iteration). Activations come straight from global memory
-// (L2-resident) or are staged once in LDS, optionally through the RMSNorm prologue
-// y = x * rsqrt(mean(x^2) + eps) * g rounded to the operand dtype. Epilogues: store,
+// (L2-resident) or are formed once per wave in registers, optionally through the RMSNorm
+// prologue y = x * rsqrt(mean(x^2) + eps) * g. With bf16 weights an f32 activation enters
+// as a bf16 pair hi + lo and costs two MFMA products (SPLIT); activations given in bf16
+// (the residual slab, verify rows) take one. Epilogues: store,
 // residual add, SwiGLU, and the fused lm_head argmax, which reduces (value, index) keys
 // with wavefront shuffles and stores one key per row and work-group; a finalize kernel
 // reduces those (no fence or atomic in the streaming kernel: a device-scope fence per
@@ -58,16 +60,28 @@ __device__ __forceinline__ int find_seg(const GemmParams& p, int col) {
   return s;
 }
 
-// Minimum resident waves per SIMD (the second launch-bounds argument): single-chunk,
-// single-tile launches run hundreds of 8-wave work-groups and need two per CU (<= 128
-// VGPRs); the multi-tile argmax launches three; the rest keep the full register budget.
-template <int T, int NCH> constexpr int gemm_min_waves_per_simd() { return T > 1 ? 3 : (NCH == 1 ? 4 : 2); }
+// Minimum resident waves per SIMD (the second launch-bounds argument), sized so that the
+// live registers (weights in flight, operand fragments, accumulators) never spill:
+// single-chunk single-tile launches of one row tile run hundreds of 8-wave work-groups
+// and get two per CU (<= 128 VGPRs); launches with more row tiles, hi/lo operand pairs
+// across several chunks, or the two-tile normed gate/up pair take the full budget and
+// fewer, larger work-groups; the multi-tile argmax launches three.
+template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int gemm_min_waves_per_simd() {
+  if (RT > 1) return 2;
+  if (T > 1) return XSRC == XSRC_NORM ? 2 : 3;
+  if (SPLIT && (NCH > 1 || NB > 1)) return NB > 1 ? 3 : 2;
+  return NCH == 1 ? 4 : 2;
+}
 
 // T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
-template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
-__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm_kernel(const GemmParams p) {
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>())) void gemm_kernel(
+    const GemmParams p) {
   using Tr = WTr<WT>;
   constexpr bool BF = Tr::BF;
+  static_assert(!SPLIT || BF, "hi/lo operand pairs feed bf16 MFMA only");
+  static_assert(!(BF && XSRC == XSRC_NORM && !SPLIT), "a normed bf16 operand is always a hi/lo pair");
+  constexpr int SR = SPLIT ? RT : 1;  // row tiles of lo fragments held (1 = unused)
   constexpr int NIT = T * NCH;
   constexpr int NRED = T > 1 ? 2 : 1;  // reduction buffers (double-buffered across tiles)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -82,13 +96,13 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
   float* rinv = red + (size_t)NRED * nw * RT * NB * 256;  // [R] (RMSNorm prologue)
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
-  // the other epilogues always run with T == 1
+  // the other epilogues run with T dividing the tile count
   auto tile_of = [&](int t) {
     const int j = (int)blockIdx.x * T + t;
     return j < p.ntiles ? j : p.ntiles - 1;
   };
 
-  auto load = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], int it) {
+  auto load = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH], int it) {
     const int j = tile_of(it / NCH), c = it % NCH;
     const size_t kb = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP + lg * Tr::EPL) * Tr::ELT;
     // fragment-major weights: one contiguous kilobyte per (16-row tile, KSTEP) block
@@ -112,12 +126,22 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int r = rt * 16 + li;
-        const unsigned char* xr = (const unsigned char*)p.x + (size_t)r * p.ldx * Tr::ELT + kb;
+        const size_t xo = (size_t)r * p.ldx * Tr::ELT + kb;
+        const unsigned char* xr = (const unsigned char*)p.x + xo;
 #pragma unroll
         for (int st = 0; st < CH; ++st) {
           u32x4_t v = {0u, 0u, 0u, 0u};
           if (r < R) v = *(const u32x4_t*)(xr + (size_t)st * Tr::KSTEP * Tr::ELT);
           xb[rt][st] = v;
+        }
+        if constexpr (SPLIT) {
+          const unsigned char* xl = (const unsigned char*)p.xlo + xo;
+#pragma unroll
+          for (int st = 0; st < CH; ++st) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (r < R) v = *(const u32x4_t*)(xl + (size_t)st * Tr::KSTEP * Tr::ELT);
+            xlb[rt][st] = v;
+          }
         }
       }
     }
@@ -133,18 +157,27 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
   // operand fragments of this wave's K slice, built once (staged sources only)
   constexpr int XR = XSRC == XSRC_GLOBAL ? 1 : NCH;
   u32x4_t xr[XR][RT][CH];
+  u32x4_t xrl[SPLIT ? XR : 1][SR][CH];  // lo halves of staged pairs
 
-  auto compute = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], int it) {
+  auto compute = [&](u32x4_t (&wb)[NB][CH], u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH], int it) {
     const int c = it % NCH;
 #pragma unroll
     for (int st = 0; st < CH; ++st) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        u32x4_t xf;
-        if constexpr (XSRC == XSRC_GLOBAL) xf = xb[rt][st];
-        else xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+        u32x4_t xf, xl;
+        if constexpr (XSRC == XSRC_GLOBAL) {
+          xf = xb[rt][st];
+          if constexpr (SPLIT) xl = xlb[rt][st];
+        } else {
+          xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+          if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+        }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
+          if constexpr (SPLIT) acc[rt][nb] = step_mfma<WT>(xl, wb[nb][st], acc[rt][nb]);
+        }
       }
     }
   };
@@ -193,7 +226,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
             ((float*)p.y)[o] += v[0][q];
           } else if constexpr (EPI == EPI_SWIGLU) {
             const float g = v[0][q], u = v[NB - 1][q];
-            act_st<BF>(p.y, o, g / (1.0f + expf(-g)) * u);
+            op_st<SPLIT>(p.y, p.ylo, o, g / (1.0f + expf(-g)) * u);
           }
         }
       }
@@ -204,20 +237,26 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
   // ---- issue the first weight chunk before staging activations -------------------------
   u32x4_t wbuf[2][NB][CH];
   u32x4_t xbuf[2][RT][CH];
-  load(wbuf[0], xbuf[0], 0);
+  u32x4_t xlbuf[2][SR][CH];
+  load(wbuf[0], xbuf[0], xlbuf[0], 0);
 
   if constexpr (XSRC != XSRC_GLOBAL) {
     if constexpr (XSRC == XSRC_NORM) {
+      // one wave per row replays the row RMSNorm kernel's sum of squares operation for
+      // operation (256 strided partial sums, wave butterflies, the four wave sums in
+      // order), so a row normalised here or there yields the same bits
       const float* xf = (const float*)p.x;
       for (int r = w; r < R; r += nw) {
-        float ss = 0.f;
+        const float* xrow = xf + (size_t)r * p.ldx;
+        float q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ss = 0.f;
 #pragma unroll 8
-        for (int k = lane * 4; k < K; k += 256) {
-          const float4 v = *(const float4*)(xf + (size_t)r * p.ldx + k);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          for (int k = j * 64 + lane; k < K; k += 256) ss = fmaf(xrow[k], xrow[k], ss);
+          q[j] = wave_sum(ss);
         }
-        ss = wave_sum(ss);
-        if (lane == 0) rinv[r] = rsqrtf(ss / (float)K + p.eps);
+        if (lane == 0) rinv[r] = rsqrtf((((q[0] + q[1]) + q[2]) + q[3]) / (float)K + p.eps);
       }
       __syncthreads();
     }
@@ -230,10 +269,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
         for (int st = 0; st < CH; ++st) {
           const int r = rt * 16 + li;
           const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
-          u32x4_t f = {0u, 0u, 0u, 0u};
+          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
           if (r < R) {
             if constexpr (XSRC == XSRC_LDS) {
-              f = *(const u32x4_t*)((const unsigned char*)p.x + ((size_t)r * p.ldx + k) * Tr::ELT);
+              const size_t xo = ((size_t)r * p.ldx + k) * Tr::ELT;
+              f = *(const u32x4_t*)((const unsigned char*)p.x + xo);
+              if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
             } else {
               const float* src = (const float*)p.x + (size_t)r * p.ldx + k;
               const float s = rinv[r];
@@ -244,7 +285,11 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                   const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
-                  f[e2] = (uint32_t)f2bf(v[2 * e2] * s * g0) | ((uint32_t)f2bf(v[2 * e2 + 1] * s * g1) << 16);
+                  uint16_t h0, l0, h1, l1;
+                  split_bf16(v[2 * e2] * s * g0, h0, l0);
+                  split_bf16(v[2 * e2 + 1] * s * g1, h1, l1);
+                  f[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                  fl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
                 }
               } else {
                 const float4 a0 = *(const float4*)src;
@@ -257,14 +302,15 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<T, NCH>())) void gemm
             }
           }
           xr[c][rt][st] = f;
+          if constexpr (SPLIT) xrl[c][rt][st] = fl;
         }
   }
 
   // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    if (it + 1 < NIT) load(wbuf[(it + 1) & 1], xbuf[(it + 1) & 1], it + 1);
-    compute(wbuf[it & 1], xbuf[it & 1], it);
+    if (it + 1 < NIT) load(wbuf[(it + 1) & 1], xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
+    compute(wbuf[it & 1], xbuf[it & 1], xlbuf[it & 1], it);
     if (it % NCH == NCH - 1) finalize(it / NCH);
   }
 
@@ -289,10 +335,10 @@ size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, i
 }
 
 // ---- instantiation tables -----------------------------------------------------------------
-template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
   const size_t lds = gemm_lds_bytes(WT, XSRC, p.R, p.waves, NB, p.xstride, T);
-  auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH>;
+  auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>;
   static size_t attr_lds = 64 * 1024;  // dynamic LDS this kernel is cleared for
   if (lds > attr_lds) {
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -303,77 +349,108 @@ static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int WT, int NB, int EPI, int XSRC, int T, int NCH, int CH>
+// The plan counts NCH chunks of 8 steps per wave; launches with two or three row tiles
+// run twice as many chunks of chunk_steps(rt) = 4 steps (same k order per wave, so the
+// same sums) to halve the weight and operand buffers in flight.
+template <int WT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
+  static_assert(CH == 8, "plans count 8-step chunks");
+  static_assert(chunk_steps(1) == 8 && chunk_steps(2) == 4 && chunk_steps(3) == 4, "chunk depth by row tiles");
   const int rt = (p.R + 15) / 16;
-  if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
-  if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
+  if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+  if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
   if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
-  else return launch_t<WT, 3, NB, EPI, XSRC, T, NCH, CH>(p, grid, s);
+  else return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
 }
 
 // one-tile launches: CH = 8 steps per chunk, NCH chunks per wave (staged operands hold
 // every chunk in registers, so they stop at two chunks)
-template <int WT, int NB, int EPI, int XSRC>
+template <int WT, int NB, int EPI, int XSRC, bool SPLIT>
 static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if constexpr (XSRC != XSRC_GLOBAL) {
+    // normed operands: one tile per work-group, or two (the registers holding the
+    // operand pairs then serve both tiles)
+    if (pl.tiles_per_wg == 2) {
+      switch (pl.nch) {
+        case 1: return by_rt<WT, NB, EPI, XSRC, 2, 1, 8, SPLIT>(p, pl.grid, s);
+        case 2: return by_rt<WT, NB, EPI, XSRC, 2, 2, 8, SPLIT>(p, pl.grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (pl.nch) {
-      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
-      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8, SPLIT>(p, pl.grid, s);
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (pl.nch) {
-      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8>(p, pl.grid, s);
-      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8>(p, pl.grid, s);
-      case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8>(p, pl.grid, s);
-      case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8>(p, pl.grid, s);
-      case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8>(p, pl.grid, s);
-      case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8>(p, pl.grid, s);
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8, SPLIT>(p, pl.grid, s);
+      case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8, SPLIT>(p, pl.grid, s);
+      case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8, SPLIT>(p, pl.grid, s);
+      case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8, SPLIT>(p, pl.grid, s);
+      case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8, SPLIT>(p, pl.grid, s);
       default: return hipErrorInvalidValue;
     }
   }
 }
 
 // argmax launches: T tiles per work-group, NCH chunks of 8 steps per wave and tile
-template <int WT, int XSRC, int NCH>
+template <int WT, int XSRC, int NCH, bool SPLIT>
 static hipError_t argmax_by_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   switch (pl.tiles_per_wg) {
-    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, NCH, 8>(p, pl.grid, s);
-    case 2: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 2, NCH, 8>(p, pl.grid, s);
-    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, NCH, 8>(p, pl.grid, s);
-    case 16: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 16, NCH, 8>(p, pl.grid, s);
+    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 2: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 2, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 16: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 16, NCH, 8, SPLIT>(p, pl.grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int WT, int XSRC>
+template <int WT, int XSRC, bool SPLIT>
 static hipError_t argmax_by_ch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   switch (pl.nch) {
-    case 1: return argmax_by_t<WT, XSRC, 1>(pl, p, s);
-    case 2: return argmax_by_t<WT, XSRC, 2>(pl, p, s);
+    case 1: return argmax_by_t<WT, XSRC, 1, SPLIT>(pl, p, s);
+    case 2: return argmax_by_t<WT, XSRC, 2, SPLIT>(pl, p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// f32 weights take f32 operands (one f32 MFMA product). bf16 weights take a hi/lo pair for
+// every computed activation (normed rows, attention output, SwiGLU output, encoder rows)
+// and a single plane only where the rows are given in bf16 (fc over the residual slab,
+// the lm_head over verify rows).
 template <int WT>
 static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s) {
-  if (epi == EPI_ARGMAX) {
-    if (xsrc == XSRC_LDS) return argmax_by_ch<WT, XSRC_LDS>(pl, p, s);
-    return hipErrorInvalidValue;
+  if constexpr (WT == WT_F32) {
+    if (p.split) return hipErrorInvalidValue;
+    if (epi == EPI_ARGMAX) return xsrc == XSRC_LDS ? argmax_by_ch<WT, XSRC_LDS, false>(pl, p, s) : hipErrorInvalidValue;
+    if (epi == EPI_STORE && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, false>(pl, p, s);
+    if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, false>(pl, p, s);
+    if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, false>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, false>(pl, p, s);
+  } else {
+    if (epi == EPI_ARGMAX) {
+      if (xsrc != XSRC_LDS) return hipErrorInvalidValue;
+      return p.split ? argmax_by_ch<WT, XSRC_LDS, true>(pl, p, s) : argmax_by_ch<WT, XSRC_LDS, false>(pl, p, s);
+    }
+    if (epi == EPI_STORE && xsrc == XSRC_GLOBAL)
+      return p.split ? by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, true>(pl, p, s)
+                     : by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, false>(pl, p, s);
+    if (!p.split) return hipErrorInvalidValue;
+    if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, true>(pl, p, s);
+    if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, true>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, true>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_GLOBAL) return by_nch<WT, 2, EPI_SWIGLU, XSRC_GLOBAL, true>(pl, p, s);
   }
-  if (epi == EPI_STORE && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL>(pl, p, s);
-  if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM>(pl, p, s);
-  if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL>(pl, p, s);
-  if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM>(pl, p, s);
   return hipErrorInvalidValue;
 }
-
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {
   if (epi == EPI_ARGMAX)
     return xsrc == XSRC_LDS && pl.ch == 8 && (pl.nch == 1 || pl.nch == 2) &&
            (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 16);
-  if (xsrc != XSRC_GLOBAL) return pl.ch == 8 && pl.tiles_per_wg == 1 && (pl.nch == 1 || pl.nch == 2);
+  if (xsrc != XSRC_GLOBAL)
+    return pl.ch == 8 && (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2) && (pl.nch == 1 || pl.nch == 2);
   return pl.ch == 8 && pl.tiles_per_wg == 1 &&
          (pl.nch == 1 || pl.nch == 2 || pl.nch == 3 || pl.nch == 4 || pl.nch == 5 || pl.nch == 10);
 }

@@ -39,12 +39,20 @@ struct GemmParams {
   int32_t K;
   int32_t R;        // rows of X (<= GEMM_MAX_ROWS)
   int32_t waves;    // waves per work-group; each owns K/waves of every tile
-  const void* x;    // XSRC_GLOBAL/LDS: act dtype [R, ldx]; XSRC_NORM: f32 [R, ldx]
+  // split != 0 (bf16 weights only): operands are f32 values carried as bf16 hi/lo pairs,
+  // two MFMA products per weight fragment. XSRC_GLOBAL/LDS read the hi plane at x and the
+  // lo plane at xlo; XSRC_NORM forms the pair in registers; SWIGLU writes y (hi) and ylo.
+  // split == 0: XSRC_GLOBAL/LDS read one plane of the weight dtype (inputs given in bf16
+  // or f32 shapes).
+  int32_t split;
+  const void* x;    // XSRC_GLOBAL/LDS: [R, ldx] (see split); XSRC_NORM: f32 [R, ldx]
+  const void* xlo;
   int64_t ldx;
   const void* gain;  // XSRC_NORM: act-dtype storage [K]
   float eps;
   int32_t xstride;  // staged X row stride in LDS (elements)
-  void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: act dtype [R, ldy]
+  void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: hi/lo planes (split) or f32
+  void* ylo;
   int64_t ldy;
   unsigned long long* part;  // ARGMAX: per-work-group best keys, [R][grid]
 };
@@ -73,15 +81,18 @@ hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStre
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
                         float* x, hipStream_t s);
+// RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          hipStream_t s);
+                          void* out_lo, hipStream_t s);
+// q/k RMSNorm + RoPE: q as an operand (hi/lo planes qb/qlo, or f32), k/v in the cache dtype.
 hipError_t launch_attn_prep(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
-                            const void* knorm, int R, int64_t pos0, void* qb, void* kb, void* vb, hipStream_t s);
+                            const void* knorm, int R, int64_t pos0, void* qb, void* qlo, void* kb, void* vb,
+                            hipStream_t s);
 hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
                              int n, int64_t pos0, void* ring, hipStream_t s);
 hipError_t launch_attention(int act_bf16, const AttnShape& a, const void* ring_layer, const void* qb,
-                            const void* kb, const void* vb, int R, int64_t e, float* part, void* out,
-                            hipStream_t s);
+                            const void* qlo, const void* kb, const void* vb, int R, int64_t e, float* part,
+                            void* out, void* out_lo, hipStream_t s);
 size_t attention_partial_floats(const AttnShape& a, int R);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);

@@ -1,5 +1,5 @@
-// Small kernels of the DFlash round: workspace init, block embedding gather, the encoder
-// RMSNorm, and the greedy verify scan.
+// Small kernels of the DFlash round: the argmax finish, block embedding gather, row
+// RMSNorm, the greedy verify scan and the weight repack.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,28 +53,29 @@ hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, i
   return hipGetLastError();
 }
 
-// out[r] = operand cast of RMSNorm(in[r]) * g; one 256-thread group per row. The sum of
-// squares is accumulated per lane in a fixed stride, then reduced wave by wave in order.
+// out[r] = RMSNorm(in[r]) * g as a GEMM operand (hi/lo bf16 planes for bf16 shapes, f32
+// otherwise); one 256-thread group per row. The sum of squares is accumulated per lane in
+// a fixed stride, then reduced wave by wave in order.
 template <bool BF>
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ in, const void* gain, float eps, int H,
-                                                      void* out) {
+                                                      void* out, void* out_lo) {
   __shared__ float part[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* x = in + (size_t)r * H;
   float ss = 0.f;
-  for (int k = tid; k < H; k += 256) ss += x[k] * x[k];
+  for (int k = tid; k < H; k += 256) ss = fmaf(x[k], x[k], ss);
   ss = wave_sum(ss);
   if (lane == 0) part[w] = ss;
   __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float s = rsqrtf(tot / (float)H + eps);
-  for (int k = tid; k < H; k += 256) act_st<BF>(out, (size_t)r * H + k, x[k] * s * act_ld<BF>(gain, k));
+  for (int k = tid; k < H; k += 256) op_st<BF>(out, out_lo, (size_t)r * H + k, x[k] * s * act_ld<BF>(gain, k));
 }
 
 hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out);
-  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out);
+                          void* out_lo, hipStream_t s) {
+  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
+  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
   return hipGetLastError();
 }
 
