@@ -128,7 +128,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   int wt;
   if (c->weight_dtype == DFLASH_F32) wt = WT_F32;
   else if (c->weight_dtype == DFLASH_BF16) wt = WT_BF16;
-  else if (c->weight_dtype == DFLASH_Q4G64) return cfg_fail(err, DFLASH_E_ARG, "4-bit weights are not supported by this build");
+  else if (c->weight_dtype == DFLASH_Q4G64) wt = WT_Q4;
   else return cfg_fail(err, DFLASH_E_ARG, "unknown weight dtype %d", c->weight_dtype);
   const bool bf = wt != WT_F32;
   if (c->act_dtype != (bf ? DFLASH_BF16 : DFLASH_F32))
@@ -168,7 +168,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   for (const auto& gm : gemms)
     if (!plan_gemm(wt, gm.epi, gm.xsrc, (int)gm.K, &pl))
       return cfg_fail(err, DFLASH_E_SHAPE, "no GEMM launch plan for a contraction of length %lld", (long long)gm.K);
-  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden + 16 / (bf ? 2 : 4), 1) > (size_t)LDS_BYTES)
+  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden, 1) > (size_t)LDS_BYTES)
     return cfg_fail(err, DFLASH_E_SHAPE, "hidden too large for the staged operand");
   Cfg g;
   g.c = *c;
@@ -236,7 +236,13 @@ struct PackedLayout {
   std::vector<size_t> off;  // byte offset of each linear, in the order above
 };
 
-size_t linear_bytes(const Cfg& g, int64_t N, int64_t K) { return (size_t)N * K * (g.wt == WT_F32 ? 4 : 2); }
+// f32/bf16: the fragment-major matrix; q4: code blocks (K/2 bytes per row) followed by
+// scale blocks (K/16 bytes per row)
+size_t q4_code_bytes(int64_t N, int64_t K) { return (size_t)N * K / 2; }
+size_t linear_bytes(const Cfg& g, int64_t N, int64_t K) {
+  if (g.wt == WT_Q4) return q4_code_bytes(N, K) + (size_t)N * K / 16;
+  return (size_t)N * K * (g.wt == WT_F32 ? 4 : 2);
+}
 
 PackedLayout make_packed_layout(const Cfg& g) {
   const dflash_config& c = g.c;
@@ -311,7 +317,6 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   GemmPlan plan;
   if (!plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
   const int waves = plan.waves;
-  const int xstride = gc.K + 16 / g.act_elt;
   const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;  // a split operand is two bf16 planes
   const size_t y_elt = gc.epi == EPI_SWIGLU ? g.act_elt : 4;
   int N = 0;
@@ -321,7 +326,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     int rc = std::min(rows - r0, GEMM_MAX_ROWS);
     if (gc.epi == EPI_ARGMAX) rc = std::min(rc, std::min(32, 16 * waves));  // one finishing wave per row tile
     if (gc.xsrc != XSRC_GLOBAL)
-      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, xstride, gc.epi == EPI_ARGMAX ? 2 : 1) >
+      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, gc.K, gc.epi == EPI_ARGMAX ? 2 : 1) >
                            (size_t)LDS_BYTES)
         --rc;
     GemmParams p{};
@@ -337,7 +342,6 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     p.ldx = gc.ldx;
     p.gain = gc.gain;
     p.eps = g.c.rms_eps;
-    p.xstride = xstride;
     GemmPlan pl = plan;
     pl.grid = p.ntiles;
     if (gc.xsrc == XSRC_NORM && gc.split && nb == 2 && p.ntiles % 2 == 0) {
@@ -421,7 +425,11 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   const PackedLayout pk = make_packed_layout(g);
   if (ring_bytes < ring_bytes_of(g) || workspace_bytes < lay.total || packed_bytes < pk.total)
     return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring, workspace or packed smaller than dflash_query_sizes");
-  auto lin_ok = [&](const dflash_linear& l) { return l.w && aligned16(l.w); };
+  auto lin_ok = [&](const dflash_linear& l) {
+    if (!l.w || !aligned16(l.w)) return false;
+    if (g.wt == WT_Q4) return l.scales && l.biases && ((uintptr_t)l.scales & 1u) == 0 && ((uintptr_t)l.biases & 1u) == 0;
+    return true;
+  };
   if (!wts->embed || !wts->enc_norm || !wts->final_norm || !lin_ok(wts->lm_head) || !lin_ok(wts->fc))
     return cfg_fail(g_create_err, DFLASH_E_ARG, "a top-level weight is NULL or not 16-byte aligned");
   for (int l = 0; l < g.c.layers; ++l) {
@@ -466,8 +474,15 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
     unsigned char* base = (unsigned char*)packed;
     size_t idx = 0;
     auto pack = [&](Lin& l, int N, int K) {
-      void* dst = base + pk.off[idx++];
-      if (e == hipSuccess) e = launch_pack(g.wt, l.w, N, K, dst, st);
+      unsigned char* dst = base + pk.off[idx++];
+      if (g.wt == WT_Q4) {
+        unsigned char* sdst = dst + q4_code_bytes(N, K);
+        if (e == hipSuccess) e = launch_pack_q4(l.w, l.s, l.b, N, K, dst, sdst, st);
+        l.s = sdst;
+        l.b = nullptr;
+      } else if (e == hipSuccess) {
+        e = launch_pack(g.wt, l.w, N, K, dst, st);
+      }
       l.w = dst;
     };
     pack(ctx->fc, H, F);

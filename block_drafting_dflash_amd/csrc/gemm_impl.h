@@ -1,0 +1,603 @@
+// Skinny weight-streaming GEMM for the DFlash block forward: Y[r, n] = sum_k X[r, k] W[n, k]
+// with at most 48 activation rows against weight matrices of up to 202048 rows.
+//
+// The block forward multiplies B+1 (or B) rows by every drafter weight once, so each
+// weight byte is read exactly once per pass and the kernel is bound by HBM bandwidth. The
+// contraction uses MFMA tiles (A = 16 activation rows, B = 16 weight rows, 32 k per
+// bf16 instruction, 4 k per f32 instruction); weights go straight from global memory into
+// the B operand with one 16-byte load per lane per step.
+//
+// Work decomposition: a work-group owns T output tiles of 16 columns (32 weight rows for
+// the SwiGLU gate/up pair) and all of K for each; its waves split K evenly and sum their
+// partial tiles through LDS in a fixed order, so an output's reduction order never depends
+// on the row count (a row gives bit-identical results in a 4-row or a 16-row call). The
+// (tile, chunk) sequence of a work-group is a compile-time constant and fully unrolled:
+// every wave keeps the next chunk of weights in flight while it multiplies the current
+// one, and the compiler's wait counts stay exact (a loop back-edge would make it drain
+// the prefetch at every iteration). Activations come straight from global memory
+// (L2-resident) or are formed once per wave in registers, optionally through the RMSNorm
+// prologue y = x * rsqrt(mean(x^2) + eps) * g. With bf16 weights an f32 activation enters
+// as a bf16 pair hi + lo and costs two MFMA products (SPLIT); activations given in bf16
+// (the residual slab, verify rows) take one. Epilogues: store,
+// residual add, SwiGLU, and the fused lm_head argmax, which reduces (value, index) keys
+// with wavefront shuffles and stores one key per row and work-group; a finalize kernel
+// reduces those (no fence or atomic in the streaming kernel: a device-scope fence per
+// work-group cost a third of the lm_head's time).
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+template <int WT> struct WTr;
+template <> struct WTr<WT_F32> {
+  static constexpr int KSTEP = 16;  // k covered by one 16-byte lane load across the wave
+  static constexpr int EPL = 4;     // elements per lane per step
+  static constexpr int ELT = 4;     // bytes per weight/activation element
+  static constexpr bool BF = false;
+};
+template <> struct WTr<WT_BF16> {
+  static constexpr int KSTEP = 32;
+  static constexpr int EPL = 8;
+  static constexpr int ELT = 2;
+  static constexpr bool BF = true;
+};
+// 4-bit weights: bf16 activation steps of 32 k; one 16-byte lane load of codes covers four
+// steps (a 128-k block), see launch_pack_q4.
+template <> struct WTr<WT_Q4> {
+  static constexpr int KSTEP = 32;
+  static constexpr int EPL = 8;
+  static constexpr int ELT = 2;
+  static constexpr bool BF = true;
+};
+
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// Eight reordered 4-bit codes -> the bf16 values 128 + q in MFMA operand order (element
+// 2e in the low half of word e): bf16 0x4300 is 128 and its 7 mantissa bits count units.
+__device__ __forceinline__ u32x4_t q4_expand(uint32_t w) {
+  u32x4_t f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = ((w >> (4 * e)) & 0x000F000Fu) | 0x43004300u;
+  return f;
+}
+
+template <int WT>
+__device__ __forceinline__ f32x4_t step_mfma(u32x4_t x, u32x4_t w, f32x4_t acc) {
+  if constexpr (WT == WT_BF16) {
+    return mfma_bf16(x, w, acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = mfma_f32(__uint_as_float(x[e]), __uint_as_float(w[e]), acc);
+    return acc;
+  }
+}
+
+__device__ __forceinline__ int find_seg(const GemmParams& p, int col) {
+  int s = 0;
+  for (int i = 1; i < p.nseg; ++i)
+    if (col >= p.seg[i].col0) s = i;
+  return s;
+}
+
+// Minimum resident waves per SIMD (the second launch-bounds argument), sized so that the
+// live registers (weights in flight, operand fragments, accumulators) never spill:
+// single-chunk single-tile launches of one row tile run hundreds of 8-wave work-groups
+// and get two per CU (<= 128 VGPRs); launches with more row tiles, hi/lo operand pairs
+// across several chunks, or the two-tile normed gate/up pair take the full budget and
+// fewer, larger work-groups; the multi-tile argmax launches three.
+template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int gemm_min_waves_per_simd() {
+  if (RT > 1) return 2;
+  if (T > 1) return XSRC == XSRC_NORM ? 2 : 3;
+  if (SPLIT && (NCH > 1 || NB > 1)) return NB > 1 ? 3 : 2;
+  return NCH == 1 ? 4 : 2;
+}
+
+// T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>())) void gemm_kernel(
+    const GemmParams p) {
+  using Tr = WTr<WT>;
+  constexpr bool BF = Tr::BF;
+  static_assert(!SPLIT || BF, "hi/lo operand pairs feed bf16 MFMA only");
+  constexpr bool Q4 = WT == WT_Q4;
+  constexpr int CB = Q4 ? CH / 4 : 1;  // 128-k code blocks per chunk
+  static_assert(!Q4 || CH % 4 == 0, "a q4 chunk is whole code blocks");
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  static_assert(!(BF && XSRC == XSRC_NORM && !SPLIT), "a normed bf16 operand is always a hi/lo pair");
+  constexpr int SR = SPLIT ? RT : 1;  // row tiles of lo fragments held (1 = unused)
+  constexpr int NIT = T * NCH;
+  constexpr int NRED = T > 1 ? 2 : 1;  // reduction buffers (double-buffered across tiles)
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nw = p.waves;
+  const int K = p.K, R = p.R;
+  const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
+
+  float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
+  float* rinv = red + (size_t)NRED * nw * RT * NB * 256;  // [R] (RMSNorm prologue)
+  // q4 with streamed operands: per wave, the operand sum of each (64-k group, row) of its
+  // k range, [kw/64][RT][16] (written by the prologue, read back by the same wave)
+  float* xsw = (float*)(smem + gemm_lds_red_bytes(XSRC, R, nw, RT * 16, NB, T)) + (size_t)w * (kw / 64) * RT * 16;
+
+  // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
+  // the other epilogues run with T dividing the tile count
+  auto tile_of = [&](int t) {
+    const int j = (int)blockIdx.x * T + t;
+    return j < p.ntiles ? j : p.ntiles - 1;
+  };
+
+  auto load = [&](u32x4_t (&wb)[NB][CH], u32x2_t (&sb)[NB][CB], u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH],
+                  int it) {
+    const int j = tile_of(it / NCH), c = it % NCH;
+    const size_t kb = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP + lg * Tr::EPL) * Tr::ELT;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int s, tj;
+      if constexpr (NB == 1) {
+        s = find_seg(p, 16 * j);
+        tj = (16 * j - p.seg[s].col0) >> 4;
+      } else {
+        s = nb;
+        tj = j;
+      }
+      if constexpr (Q4) {
+        // one kilobyte of codes and 128 bytes of (scale, bias) per (16-row tile, 128 k)
+        const size_t kblocks = (size_t)K / 128;
+        const size_t blk0 = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP) / 128;
+        const size_t bo = (size_t)tj * kblocks + blk0;
+        const unsigned char* wr = (const unsigned char*)p.seg[s].w + bo * 1024 + lane * 16;
+        const unsigned char* sr = (const unsigned char*)p.seg[s].scales + bo * 128 + li * 8;
+#pragma unroll
+        for (int b = 0; b < CB; ++b) {
+          wb[nb][b] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)b * 1024));
+          sb[nb][b] = __builtin_nontemporal_load((const u32x2_t*)(sr + (size_t)b * 128));
+        }
+      } else {
+        // fragment-major weights: one contiguous kilobyte per (16-row tile, KSTEP) block
+        const size_t kblocks = (size_t)K / Tr::KSTEP;
+        const size_t blk0 = (size_t)w * (kw / Tr::KSTEP) + (size_t)c * CH;
+        const unsigned char* wr = (const unsigned char*)p.seg[s].w + ((size_t)tj * kblocks + blk0) * 1024 + lane * 16;
+#pragma unroll
+        for (int st = 0; st < CH; ++st)
+          wb[nb][st] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)st * 1024));
+      }
+    }
+    if constexpr (XSRC == XSRC_GLOBAL) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + li;
+        const size_t xo = (size_t)r * p.ldx * Tr::ELT + kb;
+        const unsigned char* xr = (const unsigned char*)p.x + xo;
+#pragma unroll
+        for (int st = 0; st < CH; ++st) {
+          u32x4_t v = {0u, 0u, 0u, 0u};
+          if (r < R) v = *(const u32x4_t*)(xr + (size_t)st * Tr::KSTEP * Tr::ELT);
+          xb[rt][st] = v;
+        }
+        if constexpr (SPLIT) {
+          const unsigned char* xl = (const unsigned char*)p.xlo + xo;
+#pragma unroll
+          for (int st = 0; st < CH; ++st) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (r < R) v = *(const u32x4_t*)(xl + (size_t)st * Tr::KSTEP * Tr::ELT);
+            xlb[rt][st] = v;
+          }
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[RT][NB];
+  unsigned long long best[4] = {0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // operand fragments of this wave's K slice, built once (staged sources only)
+  constexpr int XR = XSRC == XSRC_GLOBAL ? 1 : NCH;
+  u32x4_t xr[XR][RT][CH];
+  u32x4_t xrl[SPLIT ? XR : 1][SR][CH];  // lo halves of staged pairs
+  // q4: per 64-k group, the sum of the operand values of each accumulator row (staged
+  // sources: built once from the staged fragments)
+  constexpr int NG = (Q4 && XSRC != XSRC_GLOBAL) ? XR * CH / 2 : 1;
+  f32x4_t xg[NG][RT];
+
+  auto compute = [&](u32x4_t (&wb)[NB][CH], u32x2_t (&sb)[NB][CB], u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH],
+                     int it) {
+    const int c = it % NCH;
+    auto xfrag = [&](int rt, int st, u32x4_t& xf, u32x4_t& xl) {
+      if constexpr (XSRC == XSRC_GLOBAL) {
+        xf = xb[rt][st];
+        if constexpr (SPLIT) xl = xlb[rt][st];
+      } else {
+        xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+        if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+      }
+    };
+    if constexpr (Q4) {
+      // y += s * sum(x (128 + q)) + (b - 128 s) * sum(x) per 64-k group: the codes enter the
+      // MFMA as exact bf16 integers and the 128 offset cancels against the operand sums
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        float sc[NB][2], cc[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const uint32_t v = sb[nb][b][g2];
+            sc[nb][g2] = __uint_as_float(v << 16);
+            cc[nb][g2] = __uint_as_float(v & 0xffff0000u) - 128.0f * sc[nb][g2];
+          }
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          f32x4_t ag[RT][NB];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) ag[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * g2 + tt, st = 4 * b + t;
+            u32x4_t fr[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) fr[nb] = q4_expand(wb[nb][b][t]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              u32x4_t xf, xl;
+              xfrag(rt, st, xf, xl);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                ag[rt][nb] = mfma_bf16(xf, fr[nb], ag[rt][nb]);
+                if constexpr (SPLIT) ag[rt][nb] = mfma_bf16(xl, fr[nb], ag[rt][nb]);
+              }
+            }
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int gi = (c * CH + 4 * b) / 2 + g2;  // group within this wave's k range
+            f32x4_t xs;
+            if constexpr (XSRC == XSRC_GLOBAL) xs = *(const f32x4_t*)&xsw[(gi * RT + rt) * 16 + 4 * lg];
+            else xs = xg[XSRC == XSRC_GLOBAL ? 0 : gi][rt];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                acc[rt][nb][q] = fmaf(sc[nb][g2], ag[rt][nb][q], acc[rt][nb][q]);
+                acc[rt][nb][q] = fmaf(cc[nb][g2], xs[q], acc[rt][nb][q]);
+              }
+              // the accumulator's only reader is the final reduction: without this empty
+              // read-write the compiler sinks every group's update there and keeps all the
+              // group partials, scales and sums alive across the stream
+              asm volatile("" : "+v"(acc[rt][nb]));
+            }
+          }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int st = 0; st < CH; ++st) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        u32x4_t xf, xl;
+        if constexpr (XSRC == XSRC_GLOBAL) {
+          xf = xb[rt][st];
+          if constexpr (SPLIT) xl = xlb[rt][st];
+        } else {
+          xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+          if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
+          if constexpr (SPLIT) acc[rt][nb] = step_mfma<WT>(xl, wb[nb][st], acc[rt][nb]);
+        }
+      }
+    }
+  };
+
+  auto finalize = [&](int t) {
+    const int j = tile_of(t);
+    float* rb = red + (size_t)(t % NRED) * nw * RT * NB * 256;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        *(f32x4_t*)&rb[((size_t)((w * RT + rt) * NB + nb) * 64 + lane) * 4] = acc[rt][nb];
+        acc[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    __syncthreads();
+    // wave w finishes row tiles w, w+nw, ... (the argmax launch guarantees nw >= RT)
+    for (int rt = w; rt < RT; rt += nw) {
+      f32x4_t v[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        v[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ww = 0; ww < nw; ++ww) v[nb] += *(const f32x4_t*)&rb[((size_t)((ww * RT + rt) * NB + nb) * 64 + lane) * 4];
+      }
+      const int col = 16 * j + li;
+      if constexpr (EPI == EPI_ARGMAX) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rt * 16 + 4 * lg + q;
+          unsigned long long key = (r < R) ? argmax_key(v[0][q], col) : 0ull;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            unsigned long long other = shfl_xor_u64(key, o);
+            key = other > key ? other : key;
+          }
+          best[q] = key > best[q] ? key : best[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rt * 16 + 4 * lg + q;
+          if (r >= R) continue;
+          const size_t o = (size_t)r * p.ldy + col;
+          if constexpr (EPI == EPI_STORE) {
+            ((float*)p.y)[o] = v[0][q];
+          } else if constexpr (EPI == EPI_RESID) {
+            ((float*)p.y)[o] += v[0][q];
+          } else if constexpr (EPI == EPI_SWIGLU) {
+            const float g = v[0][q], u = v[NB - 1][q];
+            op_st<SPLIT>(p.y, p.ylo, o, g / (1.0f + expf(-g)) * u);
+          }
+        }
+      }
+    }
+    if constexpr (NRED == 1) __syncthreads();
+  };
+
+  // ---- issue the first weight chunk before staging activations -------------------------
+  u32x4_t wbuf[2][NB][CH];
+  u32x2_t sbuf[2][NB][CB];
+  u32x4_t xbuf[2][RT][CH];
+  u32x4_t xlbuf[2][SR][CH];
+  load(wbuf[0], sbuf[0], xbuf[0], xlbuf[0], 0);
+
+  if constexpr (Q4 && XSRC == XSRC_GLOBAL) {
+    // operand sums per (group, row) by MFMA against a ones fragment (the D layout gives
+    // rows 4*lg .. 4*lg+3 in every column; the li == 0 lanes store them)
+    for (int gi = 0; gi < kw / 64; ++gi) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + li;
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const size_t xo = ((size_t)r * p.ldx + (size_t)w * kw + gi * 64 + tt * 32 + lg * 8) * 2;
+          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
+          if (r < R) {
+            f = *(const u32x4_t*)((const unsigned char*)p.x + xo);
+            if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
+          }
+          a = mfma_bf16(f, ones, a);
+          if constexpr (SPLIT) a = mfma_bf16(fl, ones, a);
+        }
+        if (li == 0) *(f32x4_t*)&xsw[(gi * RT + rt) * 16 + 4 * lg] = a;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (XSRC != XSRC_GLOBAL) {
+    if constexpr (XSRC == XSRC_NORM) {
+      // one wave per row replays the row RMSNorm kernel's sum of squares operation for
+      // operation (256 strided partial sums, wave butterflies, the four wave sums in
+      // order), so a row normalised here or there yields the same bits
+      const float* xf = (const float*)p.x;
+      for (int r = w; r < R; r += nw) {
+        const float* xrow = xf + (size_t)r * p.ldx;
+        float q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ss = 0.f;
+#pragma unroll 8
+          for (int k = j * 64 + lane; k < K; k += 256) ss = fmaf(xrow[k], xrow[k], ss);
+          q[j] = wave_sum(ss);
+        }
+        if (lane == 0) rinv[r] = rsqrtf((((q[0] + q[1]) + q[2]) + q[3]) / (float)K + p.eps);
+      }
+      __syncthreads();
+    }
+    // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
+#pragma unroll
+    for (int c = 0; c < XR; ++c)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int st = 0; st < CH; ++st) {
+          const int r = rt * 16 + li;
+          const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
+          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
+          if (r < R) {
+            if constexpr (XSRC == XSRC_LDS) {
+              const size_t xo = ((size_t)r * p.ldx + k) * Tr::ELT;
+              f = *(const u32x4_t*)((const unsigned char*)p.x + xo);
+              if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
+            } else {
+              const float* src = (const float*)p.x + (size_t)r * p.ldx + k;
+              const float s = rinv[r];
+              if constexpr (BF) {
+                const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+                const u32x4_t gb = *(const u32x4_t*)((const uint16_t*)p.gain + k);
+                float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                  const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
+                  uint16_t h0, l0, h1, l1;
+                  split_bf16(v[2 * e2] * s * g0, h0, l0);
+                  split_bf16(v[2 * e2 + 1] * s * g1, h1, l1);
+                  f[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                  fl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                }
+              } else {
+                const float4 a0 = *(const float4*)src;
+                const float4 g = *(const float4*)((const float*)p.gain + k);
+                f[0] = __float_as_uint(a0.x * s * g.x);
+                f[1] = __float_as_uint(a0.y * s * g.y);
+                f[2] = __float_as_uint(a0.z * s * g.z);
+                f[3] = __float_as_uint(a0.w * s * g.w);
+              }
+            }
+          }
+          xr[c][rt][st] = f;
+          if constexpr (SPLIT) xrl[c][rt][st] = fl;
+        }
+    if constexpr (Q4) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int st = 2 * gi + tt;
+            a = mfma_bf16(xr[st / CH][rt][st % CH], ones, a);
+            if constexpr (SPLIT) a = mfma_bf16(xrl[st / CH][rt][st % CH], ones, a);
+          }
+          xg[gi][rt] = a;
+        }
+    }
+  }
+
+  // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (it + 1 < NIT) load(wbuf[(it + 1) & 1], sbuf[(it + 1) & 1], xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
+    compute(wbuf[it & 1], sbuf[it & 1], xbuf[it & 1], xlbuf[it & 1], it);
+    if (it % NCH == NCH - 1) finalize(it / NCH);
+  }
+
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (w < RT && li == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = w * 16 + 4 * lg + q;
+        if (r < R) p.part[(size_t)r * gridDim.x + blockIdx.x] = best[q];
+      }
+    }
+  }
+}
+
+// ---- instantiation tables -----------------------------------------------------------------
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
+  const size_t lds = gemm_lds_bytes(WT, XSRC, p.R, p.waves, NB, p.K, T);
+  auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>;
+  static size_t attr_lds = 64 * 1024;  // dynamic LDS this kernel is cleared for
+  if (lds > attr_lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_lds = lds;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(p.waves * 64), lds, s, p);
+  return hipGetLastError();
+}
+
+// The plan counts NCH chunks of 8 steps per wave; launches with two or three row tiles
+// run twice as many chunks of chunk_steps(rt) = 4 steps (same k order per wave, so the
+// same sums) to halve the weight and operand buffers in flight.
+template <int WT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
+  static_assert(CH == 8, "plans count 8-step chunks");
+  static_assert(chunk_steps(1) == 8 && chunk_steps(2) == 4 && chunk_steps(3) == 4, "chunk depth by row tiles");
+  const int rt = (p.R + 15) / 16;
+  if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+  if constexpr (XSRC == XSRC_NORM && SPLIT) {
+    return hipErrorInvalidValue;  // normed hi/lo operands of more rows go through planes (run_gemm)
+  } else {
+    if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+    if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
+    else return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+  }
+}
+
+// one-tile launches: CH = 8 steps per chunk, NCH chunks per wave (staged operands hold
+// every chunk in registers, so they stop at two chunks)
+template <int WT, int NB, int EPI, int XSRC, bool SPLIT>
+static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  if constexpr (XSRC != XSRC_GLOBAL) {
+    // normed operands: one tile per work-group, or two (the registers holding the
+    // operand pairs then serve both tiles)
+    if (pl.tiles_per_wg == 2) {
+      switch (pl.nch) {
+        case 1: return by_rt<WT, NB, EPI, XSRC, 2, 1, 8, SPLIT>(p, pl.grid, s);
+        case 2: return by_rt<WT, NB, EPI, XSRC, 2, 2, 8, SPLIT>(p, pl.grid, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    switch (pl.nch) {
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8, SPLIT>(p, pl.grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (pl.nch) {
+      case 1: return by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
+      case 2: return by_rt<WT, NB, EPI, XSRC, 1, 2, 8, SPLIT>(p, pl.grid, s);
+      case 3: return by_rt<WT, NB, EPI, XSRC, 1, 3, 8, SPLIT>(p, pl.grid, s);
+      case 4: return by_rt<WT, NB, EPI, XSRC, 1, 4, 8, SPLIT>(p, pl.grid, s);
+      case 5: return by_rt<WT, NB, EPI, XSRC, 1, 5, 8, SPLIT>(p, pl.grid, s);
+      case 10: return by_rt<WT, NB, EPI, XSRC, 1, 10, 8, SPLIT>(p, pl.grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+}
+
+// argmax launches: T tiles per work-group, NCH chunks of 8 steps per wave and tile
+template <int WT, int XSRC, int NCH, bool SPLIT>
+static hipError_t argmax_by_t(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  switch (pl.tiles_per_wg) {
+    case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 2: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 2, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 16: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 16, NCH, 8, SPLIT>(p, pl.grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WT, int XSRC, bool SPLIT>
+static hipError_t argmax_by_ch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
+  switch (pl.nch) {
+    case 1: return argmax_by_t<WT, XSRC, 1, SPLIT>(pl, p, s);
+    case 2: return argmax_by_t<WT, XSRC, 2, SPLIT>(pl, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// f32 weights take f32 operands (one f32 MFMA product). bf16 weights take a hi/lo pair for
+// every computed activation (normed rows, attention output, SwiGLU output, encoder rows)
+// and a single plane only where the rows are given in bf16 (fc over the residual slab,
+// the lm_head over verify rows).
+template <int WT>
+static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s) {
+  if constexpr (WT == WT_F32) {
+    if (p.split) return hipErrorInvalidValue;
+    if (epi == EPI_ARGMAX) return xsrc == XSRC_LDS ? argmax_by_ch<WT, XSRC_LDS, false>(pl, p, s) : hipErrorInvalidValue;
+    if (epi == EPI_STORE && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, false>(pl, p, s);
+    if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, false>(pl, p, s);
+    if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, false>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, false>(pl, p, s);
+  } else {
+    if (epi == EPI_ARGMAX) {
+      if (xsrc != XSRC_LDS) return hipErrorInvalidValue;
+      return p.split ? argmax_by_ch<WT, XSRC_LDS, true>(pl, p, s) : argmax_by_ch<WT, XSRC_LDS, false>(pl, p, s);
+    }
+    if (epi == EPI_STORE && xsrc == XSRC_GLOBAL)
+      return p.split ? by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, true>(pl, p, s)
+                     : by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, false>(pl, p, s);
+    if (!p.split) return hipErrorInvalidValue;
+    if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, true>(pl, p, s);
+    if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, true>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, true>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_GLOBAL) return by_nch<WT, 2, EPI_SWIGLU, XSRC_GLOBAL, true>(pl, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dflash

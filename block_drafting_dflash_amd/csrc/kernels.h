@@ -25,8 +25,8 @@ enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 // columns col0..col0+rows-1.
 struct GemmSeg {
   const void* w;
-  const void* scales;  // q4 only: bf16 [rows, K/64]
-  const void* biases;  // q4 only
+  const void* scales;  // q4 only: the packed scale blocks (launch_pack_q4)
+  const void* biases;  // unused
   int32_t col0;
   int32_t rows;
 };
@@ -50,7 +50,6 @@ struct GemmParams {
   int64_t ldx;
   const void* gain;  // XSRC_NORM: act-dtype storage [K]
   float eps;
-  int32_t xstride;  // staged X row stride in LDS (elements)
   void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: hi/lo planes (split) or f32
   void* ylo;
   int64_t ldy;
@@ -65,7 +64,17 @@ struct GemmPlan {
 };
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc);
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
-size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int xstride, int tiles_per_wg);
+// LDS of a GEMM work-group, first part: the cross-wave reduction buffers (double-buffered
+// across tiles when a work-group owns several) and the RMSNorm row scales (XSRC_NORM).
+__host__ __device__ inline size_t gemm_lds_red_bytes(int xsrc, int R, int waves, int rows_pad, int nb,
+                                                     int tiles_per_wg) {
+  size_t b = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * (rows_pad / 16) * nb * 1024;
+  if (xsrc == XSRC_NORM) b += (size_t)R * 4;
+  return (b + 15) & ~(size_t)15;
+}
+// Whole LDS of a GEMM work-group: the part above plus, for 4-bit weights with streamed
+// operands, the operand sums per (64-k group, padded row): K/64 * rows_pad floats.
+size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int tiles_per_wg);
 
 // ---- small kernels --------------------------------------------------------------------
 struct AttnShape {
@@ -77,6 +86,10 @@ struct AttnShape {
 
 // Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip).
 hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s);
+// 4-bit linear (codes uint32 [N, K/8], bf16 scales/biases [N, K/64]) -> fragment-major
+// code blocks (N*K/2 bytes) and scale blocks (N*K/16 bytes), see misc.hip.
+hipError_t launch_pack_q4(const void* codes, const void* scales, const void* biases, int N, int K, void* dst_codes,
+                          void* dst_scales, hipStream_t s);
 // idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,

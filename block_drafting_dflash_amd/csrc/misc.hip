@@ -150,4 +150,57 @@ hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStre
   return hipGetLastError();
 }
 
+
+// 4-bit affine weights (w = s * q + b, group 64 along k) into fragment-major form.
+// Codes: block (j, s4) holds rows 16j..16j+15 and k in [128*s4, 128*s4 + 128); lane
+// l = li + 16*lg owns four words, word t carrying the eight codes of row 16j + li at
+// k = 128*s4 + 32*t + 8*lg .. + 8. Inside a word the nibbles are reordered so that k0, k2,
+// k4, k6 sit in bits 0-15 and k1, k3, k5, k7 in bits 16-31: (word >> 4e) & 0x000F000F then
+// holds the codes of k = 2e and 2e + 1 in the two 16-bit halves, which become the bf16
+// values 128 + q with one OR (the GEMM subtracts the 128 per group). Scales: a 128-byte
+// block per (j, s4) with 8 bytes per row li: (s, b) of groups 2*s4 and 2*s4 + 1, bf16.
+__device__ __forceinline__ uint32_t q4_reorder(uint32_t w) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r |= ((w >> (8 * e)) & 0xFu) << (4 * e);             // k = 2e
+    r |= ((w >> (8 * e + 4)) & 0xFu) << (16 + 4 * e);    // k = 2e + 1
+  }
+  return r;
+}
+
+__global__ void pack_q4_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                               const uint16_t* __restrict__ biases, int64_t nblocks, int kblocks, int K,
+                               u32x4_t* __restrict__ dst_codes, uint32_t* __restrict__ dst_scales) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte lane slot
+  if (i >= nblocks * 64) return;
+  const int64_t blk = i >> 6;
+  const int lane = (int)(i & 63), li = lane & 15, lg = lane >> 4;
+  const int64_t j = blk / kblocks, s4 = blk - j * kblocks;
+  const int64_t row = 16 * j + li;
+  const uint32_t* src = codes + row * (K / 8) + (128 * s4 + 8 * lg) / 8;
+  u32x4_t v;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = q4_reorder(src[4 * t]);  // k advances 32 per word = 4 words
+  dst_codes[i] = v;
+  if (lg == 0) {
+    const int groups = K / 64;
+    const int64_t g0 = row * groups + 2 * s4;
+    uint32_t* d = dst_scales + blk * 32 + li * 2;
+    d[0] = (uint32_t)scales[g0] | ((uint32_t)biases[g0] << 16);
+    d[1] = (uint32_t)scales[g0 + 1] | ((uint32_t)biases[g0 + 1] << 16);
+  }
+}
+
+hipError_t launch_pack_q4(const void* codes, const void* scales, const void* biases, int N, int K, void* dst_codes,
+                          void* dst_scales, hipStream_t s) {
+  const int kblocks = K / 128;
+  const int64_t nblocks = (int64_t)(N / 16) * kblocks;
+  const int64_t slots = nblocks * 64;
+  hipLaunchKernelGGL(pack_q4_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, (const uint32_t*)codes,
+                     (const uint16_t*)scales, (const uint16_t*)biases, nblocks, kblocks, K, (u32x4_t*)dst_codes,
+                     (uint32_t*)dst_scales);
+  return hipGetLastError();
+}
+
 }  // namespace dflash

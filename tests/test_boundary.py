@@ -75,6 +75,17 @@ def test_packed_size_covers_every_linear_once():
     assert n * 2 <= packed <= n * 2 + 256 * (2 + 7 * sh.layers)
 
 
+def test_packed_size_of_4bit_linears():
+    """q4: codes (K/2 bytes per row) plus one (scale, bias) pair per 64-k group (4 bytes),
+    for every linear once; the ring stays bf16."""
+    sh = synth.MUSE_Q4
+    ring, _, packed = sizes(sh)
+    H, qd, kvd = sh.hidden, sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim
+    n = H * sh.fc_in + sh.vocab * H + sh.layers * (qd * H + 2 * kvd * H + H * qd + 3 * sh.intermediate * H)
+    assert n * 9 // 16 <= packed <= n * 9 // 16 + 256 * (2 + 7 * sh.layers)
+    assert ring == sizes(synth.MUSE_BF16)[0]
+
+
 def test_query_sizes_validation_statuses():
     sh = synth.TINY_F32
     E_ARG, E_SHAPE, E_RANGE = 1, 2, 3

@@ -75,3 +75,25 @@ def test_ctx16384_forced_wraps_random_depth(muse, block, rounds):
     _report(f"{wl.name} block {block}", ls, ks)
     first_slot = (wl.context + phase) % C
     assert first_slot + block + 1 > C  # the first append did straddle the ring end
+
+
+@pytest.fixture(scope="module")
+def muse_q4():
+    sh = synth.MUSE_Q4
+    w = synth.make_weights(sh)
+    dev = binding.to_device(sh, w)
+    return w, dev
+
+
+@pytest.mark.parametrize("block", [4, 5, 8, 16])
+def test_q4_ctx2048_width_sweep(muse_q4, block):
+    """4-bit Muse-shaped drafter (fc, layers and lm_head in q4, group 64; embedding bf16)
+    after a 2048-row context, one ring per width, p-accept stand-in target with the
+    width's own p."""
+    w, dev = muse_q4
+    wl = synth.WORKLOADS["muse-q4-sweep-ctx2048"]
+    p = synth.width_accept_p(wl.blocks)[block]
+    ls = P.LockStep(wl.shape, w, max_block=block, dev_weights=dev)
+    ks = P.run_synthetic_rounds(ls, wl.context, block, 24, p=p, tag=block)
+    _report(f"{wl.name} block {block} p {p:.3f}", ls, ks)
+    assert ls.stats.max_hidden_rel <= 2e-3

@@ -17,6 +17,14 @@ MICRO_BF16 = synth.Shape(hidden=512, layers=2, q_heads=8, kv_heads=2, head_dim=6
                          weight_dtype="bf16", act_dtype="bf16")
 
 
+MICRO_Q4 = MICRO_BF16.with_(weight_dtype="q4")
+
+
+@pytest.fixture(scope="module")
+def micro_q4_w():
+    return synth.make_weights(MICRO_Q4)
+
+
 @pytest.fixture(scope="module")
 def tiny_w():
     return synth.make_weights(synth.TINY_F32)
@@ -139,3 +147,23 @@ def test_outputs_do_not_depend_on_ring_phase(micro_bf16_w):
             assert np.array_equal(d0, d1) and k0 == k1 and torch.equal(h0, h1), phase
         for (k0, v0), (k1, v1) in zip(runs[0][1], kv):
             assert torch.equal(k0, k1) and torch.equal(v0, v1), phase
+
+
+@pytest.mark.parametrize("block,phase,context", [(4, 0, 50), (16, 7, 30), (17, 0, 9), (40, 3, 64)])
+def test_micro_q4_random_depth(micro_q4_w, block, phase, context):
+    """4-bit fc, layer linears and lm_head (group 64): the codes enter the MFMA as exact
+    integers and each group is rescaled; the oracle dequantizes w = s q + b exactly."""
+    ls = P.LockStep(MICRO_Q4, micro_q4_w, max_block=block, phase=phase)
+    P.run_random_depth_rounds(ls, context, block, 10, tag=block)
+    assert ls.stats.max_hidden_rel <= 2e-3, ls.stats
+    print("micro-q4 stats", block, ls.stats)
+
+
+def test_q4_lm_head_argmax_is_width_invariant(micro_q4_w):
+    sh = MICRO_Q4
+    g = binding.Drafter(sh, binding.to_device(sh, micro_q4_w), max_block=4)
+    rows = torch.from_numpy(synth.verify_hidden(sh, 40, 0)).to(torch.bfloat16).cuda()
+    full = g.lm_head_argmax(rows).cpu()
+    for w in (1, 5, 16, 17):
+        part = torch.cat([g.lm_head_argmax(rows[i:i + w].contiguous()).cpu() for i in range(0, 40, w)])
+        assert torch.equal(part, full), w
