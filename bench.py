@@ -10,7 +10,8 @@ Workload (timed as `value`): muse-bf16-b4-ctx1024 -- Muse-assistant-shaped bf16 
 (hidden 2048, 5 layers, 32/4 heads x 128, intermediate 6144, vocab 202048, untied lm_head,
 fc 20480 -> 2048), context 1024, window 2048, block 4, verify rows N(0,1) through the
 lm_head. Also reported: the block-16 round (muse-bf16-b16-ctx4096, p = 0.6 synthetic
-target) and the CPU oracle timed on the host cores.
+target), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16) and the CPU oracle
+timed on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -33,13 +34,17 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
 def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
-    """Algorithmic bytes of one round: every weight read once, live K/V window, inputs."""
+    """Algorithmic bytes of one round: every weight read once, live K/V window, inputs.
+
+    Weights cost 2 bytes per parameter in bf16 and 9/16 in q4 (a 4-bit code plus a bf16
+    scale and bias per 64 inputs); activations, the ring and the embedding rows are bf16."""
     e = 2  # bf16
+    we = 9 / 16 if sh.weight_dtype == "q4" else 2
     H, I, V, F = sh.hidden, sh.intermediate, sh.vocab, sh.fc_in
     qd, kvd = sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim
-    layer = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * e
-    fc = H * F * e
-    lm = V * H * e
+    layer = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * we
+    fc = H * F * we
+    lm = V * H * we
     kv = sh.layers * 2 * min(ctx_visible, sh.window) * kvd * e
     inputs = (block + 1) * F * e + (block + 1) * H * e
     fwd = fc + sh.layers * layer + lm + kv + inputs
@@ -52,10 +57,10 @@ def counted_traffic():
     (scaled by the same counters on a 1 GiB copy), or None if the kernel source changed since."""
     try:
         d = json.load(open(os.path.join(ROOT, "profiles", "lm_head_argmax_counters.json")))
-        src = open(os.path.join(ROOT, "block_drafting_dflash_amd", "csrc", "gemm.hip"), "rb").read()
+        src = open(os.path.join(ROOT, "block_drafting_dflash_amd", "csrc", "gemm_impl.h"), "rb").read()
     except OSError:
         return None
-    return d["traffic_bytes"] if d.get("gemm_hip_sha256") == hashlib.sha256(src).hexdigest() else None
+    return d["traffic_bytes"] if d.get("kernel_source_sha256") == hashlib.sha256(src).hexdigest() else None
 
 
 def run_gpu(args):
@@ -138,56 +143,92 @@ def run_gpu(args):
     # ---------------- block 16, p = 0.6 synthetic target --------------------------------
     b16 = None
     if args.block16_steps > 0:
-        wl2 = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
-        B2 = 16
         del g
-        g2 = binding.Drafter(sh, dw, max_block=B2)
-        g2.cache_append(torch.from_numpy(synth.resid_rows(sh, wl2.context, 0)).to(torch.bfloat16).to(dev), commit=True)
-        n2 = args.warmup + args.block16_steps
-        resid2 = torch.from_numpy(np.stack([synth.resid_rows(sh, B2 + 1, 1000 + r) for r in range(n2)])).to(torch.bfloat16).to(dev)
-        u = torch.from_numpy(np.stack([synth.accept_draws(B2, r) for r in range(n2)])).to(dev)  # float64 [n2, 3, B2+1]
-        toks2 = torch.empty(B2, dtype=torch.int32, device=dev)
-        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.block16_steps)]
-        anchor = synth.anchor_token(sh)
-        V = sh.vocab
-        ks2 = []
-        torch.cuda.synchronize()
-        for r in range(n2):
-            if r == args.warmup:
-                torch.cuda.synchronize()
-                t2 = time.perf_counter()
-            e = ev2[r - args.warmup] if r >= args.warmup else None
-            if e: e[0].record(stream)
-            g2.draft_block(anchor, B2, tokens=toks2)
-            if e: e[1].record(stream)
-            # stand-in for the target's verify-row argmaxes (the target model is out of scope)
-            d = toks2.long()
-            other = (d + 1 + torch.floor(u[r, 1, :B2] * (V - 1)).long()) % V
-            tgt = torch.empty(B2 + 1, dtype=torch.int32, device=dev)
-            tgt[:B2] = torch.where(u[r, 0, :B2] < wl2.accept_p, d, other).int()
-            tgt[B2] = torch.floor(u[r, 2, B2] * V).int() % V
-            g2.verify_greedy(toks2, tgt, B2, out=vout)
-            if e: e[2].record(stream)
-            g2.cache_append(resid2[r])
-            if e: e[3].record(stream)
-            host.copy_(vout, non_blocking=True)
-            stream.synchronize()
-            k, bonus, status = host.tolist()
-            assert status == 0
-            g2.cache_trim(B2 - k)
-            anchor = bonus
-            ks2.append(k)
-        torch.cuda.synchronize()
-        el2 = time.perf_counter() - t2
-        by2 = alg_bytes(sh, B2, g2.cache_state()[0])
-        rs2 = args.block16_steps / el2
-        fwd2 = float(np.mean([x[0].elapsed_time(x[1]) + x[2].elapsed_time(x[3]) for x in ev2]))
-        b16 = {"workload": wl2.name, "rounds_per_s": rs2, "drafted_tok_s": rs2 * B2,
-               "round_hbm_frac": by2["block_forward"] * rs2 / (HBM_PEAK_GBS * 1e9),
-               "block_forward_ms": fwd2,
-               "block_forward_hbm_frac": by2["block_forward"] / (fwd2 * 1e-3) / (HBM_PEAK_GBS * 1e9),
-               "mean_accepted": float(np.mean(ks2[args.warmup:])), "steps": args.block16_steps}
-    return sh, weights, res, b16
+        wl2 = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
+        b16 = synthetic_rounds(sh, dw, 16, wl2.context, args.warmup, args.block16_steps, wl2.accept_p, tag=0)
+        b16 = {"workload": wl2.name, **b16}
+    return sh, weights, dw, res, b16
+
+
+def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: float, tag: int) -> dict:
+    """Rounds of block B whose verify-row argmaxes come from the p-accept stand-in target
+    (computed on the device from pre-drawn uniforms): draft, verify, append, one D2H copy of
+    (k, bonus), trim. The block forward is the event-timed draft plus append."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    g = binding.Drafter(sh, dw, max_block=B)
+    g.cache_append(torch.from_numpy(synth.resid_rows(sh, context, 0)).to(torch.bfloat16).to(dev), commit=True)
+    n = warmup + steps
+    resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, 1000 * (tag + 1) + r) for r in range(n)]))
+    resid = resid.to(torch.bfloat16).to(dev)
+    u = torch.from_numpy(np.stack([synth.accept_draws(B, r, tag) for r in range(n)])).to(dev)  # f64 [n, 3, B+1]
+    toks = torch.empty(B, dtype=torch.int32, device=dev)
+    tgt = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    vout = torch.empty(3, dtype=torch.int32, device=dev)
+    host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    anchor = synth.anchor_token(sh, tag=tag)
+    V = sh.vocab
+    ks = []
+    torch.cuda.synchronize()
+    t0 = None
+    for r in range(n):
+        if r == warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        e = ev[r - warmup] if r >= warmup else None
+        if e: e[0].record(stream)
+        g.draft_block(anchor, B, tokens=toks)
+        if e: e[1].record(stream)
+        # stand-in for the target's verify-row argmaxes (the target model is out of scope)
+        d = toks.long()
+        other = (d + 1 + torch.floor(u[r, 1, :B] * (V - 1)).long()) % V
+        tgt[:B] = torch.where(u[r, 0, :B] < p, d, other).int()
+        tgt[B] = torch.floor(u[r, 2, B] * V).int() % V
+        g.verify_greedy(toks, tgt, B, out=vout)
+        if e: e[2].record(stream)
+        g.cache_append(resid[r])
+        if e: e[3].record(stream)
+        host.copy_(vout, non_blocking=True)
+        stream.synchronize()
+        k, bonus, status = host.tolist()
+        assert status == 0
+        g.cache_trim(B - k)
+        anchor = bonus
+        ks.append(k)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    by = alg_bytes(sh, B, g.cache_state()[0])
+    rs = steps / el
+    fwd = float(np.mean([x[0].elapsed_time(x[1]) + x[2].elapsed_time(x[3]) for x in ev]))
+    return {"block": B, "accept_p": round(p, 4), "rounds_per_s": round(rs, 2), "drafted_tok_s": round(rs * B, 1),
+            "round_hbm_frac": round(by["block_forward"] * rs / (HBM_PEAK_GBS * 1e9), 4),
+            "block_forward_ms": round(fwd, 4),
+            "block_forward_hbm_frac": round(by["block_forward"] / (fwd * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "mean_accepted": round(float(np.mean(ks[warmup:])), 4), "steps": steps}
+
+
+def run_q4(args) -> dict:
+    """The 4-bit Muse-shaped drafter (fc, layers and lm_head in q4, group 64) after a
+    2048-row context, one ring per width, each width with its own accept probability."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    wl = synth.WORKLOADS["muse-q4-sweep-ctx2048"]
+    sh = wl.shape
+    t0 = time.time()
+    dw = binding.to_device(sh, synth.make_weights(sh))
+    torch.cuda.synchronize()
+    print(f"[bench] q4 weights generated and resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    ps = synth.width_accept_p(wl.blocks)
+    widths = [synthetic_rounds(sh, dw, B, wl.context, args.warmup, args.q4_steps, ps[B], tag=B) for B in wl.blocks]
+    return {"workload": wl.name, "widths": widths}
+
 
 
 def cpu_baseline(sh, weights, budget_s: float) -> dict:
@@ -219,7 +260,7 @@ def cpu_baseline(sh, weights, budget_s: float) -> dict:
         od.trim(B - k)
         anchor = bonus
         done += 1
-        if time.perf_counter() - t1 > budget_s or done >= 50:
+        if time.perf_counter() - t1 > budget_s or done >= 400:
             break
     el = time.perf_counter() - t1
     return {"value": done / el, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
@@ -234,6 +275,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--block16-steps", type=int, default=320)
+    ap.add_argument("--q4-steps", type=int, default=200, help="timed rounds per width of the q4 sweep (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -253,7 +295,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the round at batch 1 is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
-    sh, weights, res, b16 = run_gpu(args)
+    sh, weights, dw, res, b16 = run_gpu(args)
+    del dw
+    q4 = run_q4(args) if args.q4_steps > 0 else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(sh, weights, args.cpu_budget)
     traffic = counted_traffic()
     line = {
@@ -276,6 +320,7 @@ def main():
                      "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": res["bytes"]["lm_head"],
                      "avg_launch_ms": round(res["lm_head_ms"], 5)},
         "block16": b16,
+        "q4": q4,
         "cpu_baseline": cpu,
         "mean_accepted": res["mean_accepted"],
     }
