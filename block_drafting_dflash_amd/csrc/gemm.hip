@@ -11,9 +11,9 @@ hipError_t launch_gemm_q4(const GemmPlan& pl, int epi, int xsrc, const GemmParam
 
 size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int tiles_per_wg) {
   const int rows_pad = 16 * ((R + 15) / 16);
-  size_t b = gemm_lds_red_bytes(xsrc, R, waves, rows_pad, nb, tiles_per_wg);
-  if (wt == WT_Q4 && xsrc == XSRC_GLOBAL) b += (size_t)(K / 64) * rows_pad * 4;
-  return b;
+  (void)wt;
+  (void)K;
+  return gemm_lds_red_bytes(xsrc, R, waves, rows_pad, nb, tiles_per_wg);
 }
 
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {

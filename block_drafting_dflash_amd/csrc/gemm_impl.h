@@ -118,9 +118,6 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 
   float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
   float* rinv = red + (size_t)NRED * nw * RT * NB * 256;  // [R] (RMSNorm prologue)
-  // q4 with streamed operands: per wave, the operand sum of each (64-k group, row) of its
-  // k range, [kw/64][RT][16] (written by the prologue, read back by the same wave)
-  float* xsw = (float*)(smem + gemm_lds_red_bytes(XSRC, R, nw, RT * 16, NB, T)) + (size_t)w * (kw / 64) * RT * 16;
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues run with T dividing the tile count
@@ -129,10 +126,9 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     return j < p.ntiles ? j : p.ntiles - 1;
   };
 
-  auto load = [&](u32x4_t (&wb)[NB][CH], u32x2_t (&sb)[NB][CB], u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH],
-                  int it) {
+  // weights of (tile, chunk) it: the fragment-major blocks of every segment
+  auto load_w = [&](u32x4_t (&wb)[NB][CH], u32x2_t (&sb)[NB][CB], int it) {
     const int j = tile_of(it / NCH), c = it % NCH;
-    const size_t kb = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP + lg * Tr::EPL) * Tr::ELT;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       int s, tj;
@@ -165,6 +161,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           wb[nb][st] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)st * 1024));
       }
     }
+  };
+
+  // streamed operand fragments of chunk it (hi and, for pairs, lo planes)
+  auto load_x = [&](u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH], int it) {
+    const int c = it % NCH;
+    const size_t kb = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP + lg * Tr::EPL) * Tr::ELT;
     if constexpr (XSRC == XSRC_GLOBAL) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -234,11 +236,13 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           }
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
-          f32x4_t ag[RT][NB];
+          f32x4_t ag[RT][NB], ax[RT];
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
+          for (int rt = 0; rt < RT; ++rt) {
+            ax[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) ag[rt][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
             const int t = 2 * g2 + tt, st = 4 * b + t;
@@ -254,13 +258,17 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
                 ag[rt][nb] = mfma_bf16(xf, fr[nb], ag[rt][nb]);
                 if constexpr (SPLIT) ag[rt][nb] = mfma_bf16(xl, fr[nb], ag[rt][nb]);
               }
+              if constexpr (XSRC == XSRC_GLOBAL) {  // streamed operands: their group sums here
+                ax[rt] = mfma_bf16(xf, ones, ax[rt]);
+                if constexpr (SPLIT) ax[rt] = mfma_bf16(xl, ones, ax[rt]);
+              }
             }
           }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             const int gi = (c * CH + 4 * b) / 2 + g2;  // group within this wave's k range
             f32x4_t xs;
-            if constexpr (XSRC == XSRC_GLOBAL) xs = *(const f32x4_t*)&xsw[(gi * RT + rt) * 16 + 4 * lg];
+            if constexpr (XSRC == XSRC_GLOBAL) xs = ax[rt];
             else xs = xg[XSRC == XSRC_GLOBAL ? 0 : gi][rt];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -353,36 +361,17 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   };
 
   // ---- issue the first weight chunk before staging activations -------------------------
-  u32x4_t wbuf[2][NB][CH];
-  u32x2_t sbuf[2][NB][CB];
+  // weights run PDW - 1 chunks ahead (q4 chunks carry a quarter of the bytes, so more
+  // of them stay in flight); streamed operands, from L2, one chunk ahead
+  constexpr int PDW = Q4 ? 4 : 2;
+  u32x4_t wbuf[PDW][NB][CH];
+  u32x2_t sbuf[PDW][NB][CB];
   u32x4_t xbuf[2][RT][CH];
   u32x4_t xlbuf[2][SR][CH];
-  load(wbuf[0], sbuf[0], xbuf[0], xlbuf[0], 0);
-
-  if constexpr (Q4 && XSRC == XSRC_GLOBAL) {
-    // operand sums per (group, row) by MFMA against a ones fragment (the D layout gives
-    // rows 4*lg .. 4*lg+3 in every column; the li == 0 lanes store them)
-    for (int gi = 0; gi < kw / 64; ++gi) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + li;
-        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const size_t xo = ((size_t)r * p.ldx + (size_t)w * kw + gi * 64 + tt * 32 + lg * 8) * 2;
-          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
-          if (r < R) {
-            f = *(const u32x4_t*)((const unsigned char*)p.x + xo);
-            if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
-          }
-          a = mfma_bf16(f, ones, a);
-          if constexpr (SPLIT) a = mfma_bf16(fl, ones, a);
-        }
-        if (li == 0) *(f32x4_t*)&xsw[(gi * RT + rt) * 16 + 4 * lg] = a;
-      }
-    }
-    __syncthreads();
-  }
+  for (int i = 0; i < PDW - 1; ++i)
+    if (i < NIT) load_w(wbuf[i], sbuf[i], i);
+  if constexpr (XSRC == XSRC_GLOBAL) load_x(xbuf[0], xlbuf[0], 0);
 
   if constexpr (XSRC != XSRC_GLOBAL) {
     if constexpr (XSRC == XSRC_NORM) {
@@ -468,8 +457,10 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    if (it + 1 < NIT) load(wbuf[(it + 1) & 1], sbuf[(it + 1) & 1], xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
-    compute(wbuf[it & 1], sbuf[it & 1], xbuf[it & 1], xlbuf[it & 1], it);
+    if (it + PDW - 1 < NIT) load_w(wbuf[(it + PDW - 1) % PDW], sbuf[(it + PDW - 1) % PDW], it + PDW - 1);
+    if constexpr (XSRC == XSRC_GLOBAL)
+      if (it + 1 < NIT) load_x(xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
+    compute(wbuf[it % PDW], sbuf[it % PDW], xbuf[it & 1], xlbuf[it & 1], it);
     if (it % NCH == NCH - 1) finalize(it / NCH);
   }
 

@@ -72,8 +72,7 @@ __host__ __device__ inline size_t gemm_lds_red_bytes(int xsrc, int R, int waves,
   if (xsrc == XSRC_NORM) b += (size_t)R * 4;
   return (b + 15) & ~(size_t)15;
 }
-// Whole LDS of a GEMM work-group: the part above plus, for 4-bit weights with streamed
-// operands, the operand sums per (64-k group, padded row): K/64 * rows_pad floats.
+// Whole LDS of a GEMM work-group (today the part above for every weight type).
 size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int tiles_per_wg);
 
 // ---- small kernels --------------------------------------------------------------------
