@@ -10,6 +10,10 @@
 // so the window never has to be rebuilt or rotated: context keys are positions
 // max(0, e-W)..e-1, followed by the block's transient keys at e..e+R-1.
 //
+// Ring layout per layer: K as [kv head][slot][head dim] and V transposed, [kv head][head
+// dim][slot], so that both MFMA operands of the attention read consecutive elements: a key
+// row for the scores, a run of consecutive keys at one dim for the output.
+//
 // Work split: one work-group per (kv head, chunk of 64 keys) computes, for the kv
 // group's query vectors, the chunk's max logit m, sum of exp l and unnormalised output;
 // a combine kernel merges the chunks in chunk order (fixed, so results do not depend on
@@ -18,6 +22,10 @@
 #include "kernels.h"
 
 namespace dflash {
+
+// floats per (chunk, query) partial: the unnormalised output [hd], then m and l, padded to a
+// multiple of four so that output rows stay 16-byte aligned
+#define PART_STRIDE(hd) ((hd) + 4)
 
 // ---- q/k RMSNorm + RoPE on the block rows -----------------------------------------------
 // One wave per (row, head). Lane i < hd/2 owns the rotate-half pair (i, i + hd/2).
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float
 
 // ---- context K/V into the ring ----------------------------------------------------------
 // kv: f32 [n, L, 2, nkv, hd] (k then v per layer). One wave per (row, layer, kv slot).
-// ring: act [L][2][nkv][C][hd].
+// ring: act, per layer K [nkv][C][hd] then V^T [nkv][hd][C].
 template <bool BF>
 __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const float* __restrict__ kv,
                                                          const void* const* knorms, int n, int64_t pos0,
@@ -90,7 +98,8 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
   float x1 = act ? src[lane] : 0.f, x2 = act ? src[lane + half] : 0.f;
   const int64_t pos = pos0 + r;
   const int64_t slot = (pos + a.phase) % a.cap;
-  const size_t o = ((((size_t)l * 2 + isv) * a.nkv + h) * a.cap + (size_t)slot) * hd;
+  // K row at (l, 0, h, slot); V element d at (l, 1, h, d, slot)
+  const size_t plane = (((size_t)l * 2 + isv) * a.nkv + h) * (size_t)a.cap * hd;
   if (!isv) {
     const float ss = wave_sum(x1 * x1 + x2 * x2);
     const float s = rsqrtf(ss / (float)hd + a.eps);
@@ -107,8 +116,13 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
     x2 = y2;
   }
   if (act) {
-    act_st<BF>(ring, o + lane, x1);
-    act_st<BF>(ring, o + lane + half, x2);
+    if (!isv) {
+      act_st<BF>(ring, plane + (size_t)slot * hd + lane, x1);
+      act_st<BF>(ring, plane + (size_t)slot * hd + lane + half, x2);
+    } else {
+      act_st<BF>(ring, plane + (size_t)lane * a.cap + slot, x1);
+      act_st<BF>(ring, plane + (size_t)(lane + half) * a.cap + slot, x2);
+    }
   }
 }
 
@@ -146,9 +160,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
     float kvv, vvv;
     if (key < nctx) {
       const int64_t pos = lo + key;
-      const size_t off = (size_t)((pos + a.phase) % a.cap) * hd + d;
-      kvv = act_ld<BF>(Kr, off);
-      vvv = act_ld<BF>(Vr, off);
+      const size_t slot = (size_t)((pos + a.phase) % a.cap);
+      kvv = act_ld<BF>(Kr, slot * hd + d);
+      vvv = act_ld<BF>(Vr, (size_t)d * a.cap + slot);
     } else {
       const int b = key - nctx;
       const size_t off = ((size_t)b * a.nkv + g) * hd + d;
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
       Ss[qi * ATTN_CHUNK + lane] = pexp;
       const float l = wave_sum(pexp);
       if (lane == 0) {
-        float* dst = part + (((size_t)g * nchunks + c) * NQ + q0 + qi) * (hd + 2);
+        float* dst = part + (((size_t)g * nchunks + c) * NQ + q0 + qi) * PART_STRIDE(hd);
         dst[hd] = m;
         dst[hd + 1] = l;
       }
@@ -216,94 +230,101 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
       float o = 0.f;
       const float* pr = Ss + qi * ATTN_CHUNK;
       for (int kj = 0; kj < kn; ++kj) o += pr[kj] * Vs[kj * hd + d];
-      part[(((size_t)g * nchunks + c) * NQ + q0 + qi) * (hd + 2) + d] = o;
+      part[(((size_t)g * nchunks + c) * NQ + q0 + qi) * PART_STRIDE(hd) + d] = o;
     }
   }
 }
 
-// ---- attention on MFMA (bf16 operands): one work-group per (128-key chunk, kv head) -------
-// Scores are formed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, K rows from LDS, Q rows
-// from L2), so each lane ends up holding 4 keys x 1 query: exactly the B-operand layout of
-// the 16x16x16 MFMA that forms O^T = V^T P^T. Q (an f32 activation) and P (in [0, 1])
-// enter as bf16 pairs hi + lo, which keep about 16 significant bits; V and K are bf16
-// already, products are exact and sums are f32. Each wave owns query tiles w, w+4, ...
-constexpr int AM_CH = 128;  // keys per work-group
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-
+// ---- attention on MFMA (bf16 operands): one work-group per (64-key chunk, kv head) ------
+// Each wave takes query tiles w, w+4, ... and reads its operands straight from memory (no
+// LDS): scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16 key rows, B = 16 queries), then
+// O^T = V^T P^T (A = 16 dims x 32 keys from the transposed V, B = P). The key rows of the
+// two score tiles of each 32-key half are ordered so that lane (li, lg) ends up with keys
+// 8*lg .. 8*lg+7 of the half for query li, exactly its B operand of the output product,
+// and the matching V^T run is one 16-byte load (per-key loads where the run wraps the ring
+// or reaches the block's own keys). Q (an f32 activation) and P (in [0, 1]) enter as bf16
+// pairs hi + lo, about 16 significant bits; K and V are bf16 already, products are exact
+// and sums f32.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
                                                         const uint16_t* __restrict__ qb, const uint16_t* __restrict__ qlo,
                                                         const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                                         int R, int64_t e, int nchunks, float* __restrict__ part) {
-  constexpr int KST = HD + 8;      // K row stride (elements): rows land 4 banks apart
-  constexpr int VST = AM_CH + 4;   // V^T row stride (elements)
-  __shared__ __align__(16) uint16_t Kl[AM_CH * KST];
-  __shared__ __align__(16) uint16_t Vt[HD * VST];
-  __shared__ int64_t kpos[AM_CH];
+  constexpr int KC = ATTN_CHUNK;  // 64 keys = two halves of 32
+  constexpr int DS = HD / 32, DT = HD / 16;
+  static_assert(KC == 64, "two 32-key halves per work-group");
   const int g = blockIdx.y, c = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int G = a.nq / a.nkv, NQ = R * G;
+  const int G = a.nq / a.nkv, NQ = R * G, nqt = (NQ + 15) / 16;
+  if (w >= nqt) return;  // no barrier below: an idle wave may leave
   const int64_t lo = e > a.window ? e - a.window : 0;
-  const int nctx = (int)(e - lo);
-  const int nkeys = nctx + R;
-  const int k0 = c * AM_CH;
-  const int kn = min(AM_CH, nkeys - k0);
-  const size_t plane = (size_t)a.cap * HD;
-  const uint16_t* Kr = ring_layer + (size_t)g * plane;
-  const uint16_t* Vr = ring_layer + (size_t)(a.nkv + g) * plane;
+  const int nctx = (int)(e - lo), nkeys = nctx + R;
+  const int k0 = c * KC;
+  const int C = a.cap;
+  const uint16_t* Kp = ring_layer + (size_t)g * C * HD;
+  const uint16_t* VTp = ring_layer + (size_t)(a.nkv + g) * HD * C;
+  // slot of context key kk (0 <= kk < nctx <= W < C: at most one wrap)
+  const int s_base = (int)((lo + a.phase) % C);
+  auto slot_of = [&](int kk) { const int sl = s_base + kk; return sl >= C ? sl - C : sl; };
 
-  constexpr int SEGS = HD / 8;                 // 16-byte segments per row
-  constexpr int ITEMS = AM_CH * SEGS / 256;    // staging items per thread
-  // slot of the chunk's first context key; later keys wrap at most once (kj < nctx <= W < C)
-  const int64_t s0 = (lo + k0 + a.phase) % a.cap;
-  u32x4_t kv[ITEMS], vv[ITEMS];
+  // ---- K rows: half h, tile tb, row li <-> key 32h + 8*(li/4) + 4*tb + li%4 --------------
+  u32x4_t kf[2][2][DS];
 #pragma unroll
-  for (int u = 0; u < ITEMS; ++u) {
-    const int it = tid + u * 256;
-    const int kj = it / SEGS, sg = it - kj * SEGS;
-    kv[u] = u32x4_t{0u, 0u, 0u, 0u};
-    vv[u] = u32x4_t{0u, 0u, 0u, 0u};
-    if (kj < kn) {
-      const int key = k0 + kj;
-      if (key < nctx) {
-        int64_t slot = s0 + kj;
-        if (slot >= a.cap) slot -= a.cap;
-        const size_t off = (size_t)slot * HD + 8 * sg;
-        kv[u] = *(const u32x4_t*)(Kr + off);
-        vv[u] = *(const u32x4_t*)(Vr + off);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int key = k0 + 32 * h + 8 * (li >> 2) + 4 * tb + (li & 3);
+      const uint16_t* row = nullptr;
+      if (key < nctx) row = Kp + (size_t)slot_of(key) * HD;
+      else if (key < nkeys) row = kb + ((size_t)(key - nctx) * a.nkv + g) * HD;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        kf[h][tb][s] = u32x4_t{0u, 0u, 0u, 0u};
+        if (row) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
+      }
+    }
+  // ---- V^T runs: half h, dim tile dt: dim dt*16 + li, keys 32h + 8*lg .. + 8 ------------
+  u32x4_t vf[2][DT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int kr = k0 + 32 * h + 8 * lg;
+    const bool run = kr + 7 < nctx && slot_of(kr) + 7 < C;  // eight context keys in consecutive slots
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int dim = dt * 16 + li;
+      if (run) {
+        __builtin_memcpy(&vf[h][dt], VTp + (size_t)dim * C + slot_of(kr), 16);  // 2-byte aligned run
       } else {
-        const size_t off = ((size_t)(key - nctx) * a.nkv + g) * HD + 8 * sg;
-        kv[u] = *(const u32x4_t*)(kb + off);
-        vv[u] = *(const u32x4_t*)(vb + off);
+        uint32_t wv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int key = kr + 2 * t + u;
+            uint32_t bits = 0;
+            if (key < nctx) bits = VTp[(size_t)dim * C + slot_of(key)];
+            else if (key < nkeys) bits = vb[((size_t)(key - nctx) * a.nkv + g) * HD + dim];
+            pair |= bits << (16 * u);
+          }
+          wv[t] = pair;
+        }
+        vf[h][dt] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
       }
     }
   }
-#pragma unroll
-  for (int u = 0; u < ITEMS; ++u) {
-    const int it = tid + u * 256;
-    const int kj = it / SEGS, sg = it - kj * SEGS;
-    *(u32x4_t*)&Kl[kj * KST + 8 * sg] = kv[u];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) Vt[(8 * sg + t) * VST + kj] = (uint16_t)(vv[u][t >> 1] >> (16 * (t & 1)));
-  }
-  for (int kj = tid; kj < AM_CH; kj += blockDim.x) {
-    const int key = k0 + kj;
-    kpos[kj] = key < nctx ? lo + key : e + (key - nctx);
-  }
-  __syncthreads();
 
   const float scale = 1.0f / sqrtf((float)HD);
-  const int nqt = (NQ + 15) / 16;
   for (int qt = w; qt < nqt; qt += 4) {
     const int qv = qt * 16 + li;
     const bool qok = qv < NQ;
     const int r = qok ? qv / G : 0, hh = qv - r * G;
     const int64_t qpos = e + r;
-    u32x4_t qf[HD / 32], qfl[HD / 32];
+    u32x4_t qf[DS], qfl[DS];
     const size_t qo = ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
 #pragma unroll
-    for (int s = 0; s < HD / 32; ++s) {
+    for (int s = 0; s < DS; ++s) {
       qf[s] = u32x4_t{0u, 0u, 0u, 0u};
       qfl[s] = u32x4_t{0u, 0u, 0u, 0u};
       if (qok) {
@@ -311,69 +332,66 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
         qfl[s] = *(const u32x4_t*)(qlo + qo + 32 * s + 8 * lg);
       }
     }
-    f32x4_t S[AM_CH / 16];
+    // scores: element i of tile (h, tb) is key 32h + 8*lg + 4*tb + i for query li
+    float S[2][2][4];
     float m = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < AM_CH / 16; ++kt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int s = 0; s < HD / 32; ++s) {
-        const u32x4_t kf = *(const u32x4_t*)&Kl[(kt * 16 + li) * KST + 32 * s + 8 * lg];
-        acc = mfma_bf16(kf, qf[s], acc);
-        acc = mfma_bf16(kf, qfl[s], acc);
-      }
+      for (int tb = 0; tb < 2; ++tb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = kt * 16 + 4 * lg + i;
-        const int64_t kp = kpos[kj];
-        const int64_t dist = qpos > kp ? qpos - kp : kp - qpos;
-        const bool vis = qok && kj < kn && dist <= a.window;
-        S[kt][i] = vis ? acc[i] * scale : -INFINITY;
-        m = fmaxf(m, S[kt][i]);
+        for (int s = 0; s < DS; ++s) {
+          acc = mfma_bf16(kf[h][tb][s], qf[s], acc);
+          acc = mfma_bf16(kf[h][tb][s], qfl[s], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 32 * h + 8 * lg + 4 * tb + i;
+          const int64_t kp = key < nctx ? lo + key : e + (key - nctx);
+          const int64_t dist = qpos > kp ? qpos - kp : kp - qpos;
+          const bool vis = qok && key < nkeys && dist <= a.window;
+          S[h][tb][i] = vis ? acc[i] * scale : -INFINITY;
+          m = fmaxf(m, S[h][tb][i]);
+        }
       }
-    }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     float l = 0.f;
+    u32x4_t phi[2], plo[2];
 #pragma unroll
-    for (int kt = 0; kt < AM_CH / 16; ++kt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = S[kt][i] == -INFINITY ? 0.f : expf(S[kt][i] - m);
-        S[kt][i] = pv;
-        l += pv;
+      for (int t = 0; t < 4; ++t) {  // word t holds keys 8*lg + 2t, 2t + 1 of the half
+        float pv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * t + u, tb = j >> 2, i = j & 3;
+          const float sv = S[h][tb][i];
+          pv[u] = sv == -INFINITY ? 0.f : expf(sv - m);
+          l += pv[u];
+        }
+        uint32_t hp, lp;
+        split2_bf16(pv[0], pv[1], hp, lp);
+        phi[h][t] = hp;
+        plo[h][t] = lp;
       }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    f32x4_t O[HD / 16];
+    float* dst = part + (((size_t)g * nchunks + c) * NQ + qv) * PART_STRIDE(HD);
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) O[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < AM_CH / 16; ++kt) {
-      s16x4_t phi, plo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t h = f2bf(S[kt][i]);
-        phi[i] = (short)h;
-        plo[i] = (short)f2bf(S[kt][i] - bf2f(h));
+      for (int h = 0; h < 2; ++h) {
+        o = mfma_bf16(vf[h][dt], phi[h], o);
+        o = mfma_bf16(vf[h][dt], plo[h], o);
       }
-#pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt) {
-        const s16x4_t vf = *(const s16x4_t*)&Vt[(dt * 16 + li) * VST + kt * 16 + 4 * lg];
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, phi, O[dt], 0, 0, 0);
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, plo, O[dt], 0, 0, 0);
-      }
+      if (qok) *(f32x4_t*)&dst[dt * 16 + 4 * lg] = o;  // dims dt*16 + 4*lg .. + 4 of query qv
     }
-    if (qok) {
-      float* dst = part + (((size_t)g * nchunks + c) * NQ + qv) * (HD + 2);
-#pragma unroll
-      for (int dt = 0; dt < HD / 16; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[dt * 16 + 4 * lg + i] = O[dt][i];
-      if (lg == 0) {
-        dst[HD] = m;
-        dst[HD + 1] = l;
-      }
+    if (qok && lg == 0) {
+      dst[HD] = m;
+      dst[HD + 1] = l;
     }
   }
 }
@@ -392,8 +410,8 @@ __global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part,
   const int G = a.nq / a.nkv, g = h / G, hh = h - g * G;
   const int NQ = R * G, qi = r * G + hh;
   const int d = threadIdx.x, hd = a.hd;
-  const size_t stride = (size_t)NQ * (hd + 2);
-  const float* base = part + ((size_t)g * nchunks * NQ + qi) * (hd + 2);
+  const size_t stride = (size_t)NQ * PART_STRIDE(hd);
+  const float* base = part + ((size_t)g * nchunks * NQ + qi) * PART_STRIDE(hd);
   for (int c = d; c < nchunks; c += blockDim.x) {
     sm_m[c] = base[c * stride + hd];
     sm_l[c] = base[c * stride + hd + 1];
@@ -423,13 +441,14 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
     const size_t t = i / hd;
     const int j = (int)(t % n), h = (int)(t / n);
     const size_t slot = (size_t)((lo + j + a.phase) % a.cap);
-    const size_t so = slot * hd + d;
+    const size_t ko = (size_t)h * plane + slot * hd + d;               // K [h][slot][d]
+    const size_t vo = (size_t)(a.nkv + h) * plane + (size_t)d * a.cap + slot;  // V^T [h][d][slot]
     if constexpr (BF) {
-      ((uint16_t*)kout)[i] = ((const uint16_t*)ring_layer)[(size_t)(0 * a.nkv + h) * plane + so];
-      ((uint16_t*)vout)[i] = ((const uint16_t*)ring_layer)[(size_t)(1 * a.nkv + h) * plane + so];
+      ((uint16_t*)kout)[i] = ((const uint16_t*)ring_layer)[ko];
+      ((uint16_t*)vout)[i] = ((const uint16_t*)ring_layer)[vo];
     } else {
-      ((float*)kout)[i] = ((const float*)ring_layer)[(size_t)(0 * a.nkv + h) * plane + so];
-      ((float*)vout)[i] = ((const float*)ring_layer)[(size_t)(1 * a.nkv + h) * plane + so];
+      ((float*)kout)[i] = ((const float*)ring_layer)[ko];
+      ((float*)vout)[i] = ((const float*)ring_layer)[vo];
     }
   }
 }
@@ -460,13 +479,13 @@ static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a
 static int attn_nchunks(int bf, const AttnShape& a, int R, int64_t e) {
   const int64_t lo = e > a.window ? e - a.window : 0;
   const int nkeys = (int)(e - lo) + R;
-  const int ch = use_mfma(bf, a) ? AM_CH : ATTN_CHUNK;
-  return (nkeys + ch - 1) / ch;
+  (void)bf;
+  return (nkeys + ATTN_CHUNK - 1) / ATTN_CHUNK;
 }
 
 size_t attention_partial_floats(const AttnShape& a, int R) {
   const int nch = (a.window + R + ATTN_CHUNK - 1) / ATTN_CHUNK;
-  return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * (a.hd + 2);
+  return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * PART_STRIDE(a.hd);
 }
 
 hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* qlo,

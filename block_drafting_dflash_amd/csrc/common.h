@@ -11,12 +11,14 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 // ---- bf16 <-> f32 (bf16 stored as raw 16-bit words) -----------------------------------
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// nearest bf16, ties to even; NaN stays NaN, overflow rounds to inf
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// nearest bf16, ties to even; NaN stays NaN, overflow rounds to inf (gfx950 converts in
+// hardware, v_cvt_pk_bf16_f32, two values per instruction)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // activation load/store in either f32 or bf16 storage
@@ -36,6 +38,11 @@ template <bool BF16> __device__ __forceinline__ void act_st(void* p, int64_t i, 
 __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
   hi = f2bf(v);
   lo = f2bf(v - bf2f(hi));
+}
+// the same for two values at once: packed hi pair and packed lo pair (a in the low halves)
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = f2bf2(a, b);
+  lo = f2bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 // Store of an activation operand: two bf16 planes (SPLIT) or f32.
 template <bool SPLIT> __device__ __forceinline__ void op_st(void* hi, void* lo, int64_t i, float v) {

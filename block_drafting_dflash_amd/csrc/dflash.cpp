@@ -31,7 +31,7 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_c, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_kv, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -192,6 +192,9 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   return DFLASH_OK;
 }
 
+// rows of the normed-operand planes: a draft's rows or one append chunk, whichever is more
+size_t hn_rows(const Cfg& g) { return std::max<size_t>((size_t)g.R, (size_t)GEMM_MAX_ROWS); }
+
 Layout make_layout(const Cfg& g) {
   const dflash_config& c = g.c;
   const size_t H = c.hidden, R = g.R, ae = g.act_elt;
@@ -209,7 +212,7 @@ Layout make_layout(const Cfg& g) {
   // operand buffers (q, attention output, SwiGLU output, normed rows) hold 4 bytes per
   // element: f32, or for bf16 shapes a hi plane followed by a lo plane (see lo_plane)
   L.x = take(4 * R * H);
-  L.hn = take(4 * R * H);  // normed rows of launches past one row tile
+  L.hn = take(4 * hn_rows(g) * H);  // normed rows of launches past one row tile
   L.qkv = take(4 * R * (qd + 2 * kvd));
   L.qb = take(4 * R * qd);
   L.kb = take(ae * R * kvd);
@@ -219,7 +222,6 @@ Layout make_layout(const Cfg& g) {
   L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
-  L.app_c = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
   L.total = o;
   return L;
@@ -300,9 +302,9 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   GemmCall gc = gc_in;
   if (gc.xsrc == XSRC_NORM && gc.split && rows > 16) {
     // hi/lo operand pairs of more than one row tile would not stay in registers: normalise
-    // the rows once into planes (the same bits as the fused prologue) and stream them
+    // the rows once into planes and stream them
     void* hn = ctx->ws + ctx->lay.hn;
-    void* hn_lo = lo_plane(g, hn, g.R, gc.K);
+    void* hn_lo = lo_plane(g, hn, hn_rows(g), gc.K);
     const dflash_status s0 =
         dev(ctx, launch_rownorm(1, (const float*)gc.x, gc.gain, g.c.rms_eps, rows, gc.K, hn, hn_lo, st), "row norm");
     if (s0 != DFLASH_OK) return s0;
@@ -344,8 +346,9 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     p.eps = g.c.rms_eps;
     GemmPlan pl = plan;
     pl.grid = p.ntiles;
-    if (gc.xsrc == XSRC_NORM && gc.split && nb == 2 && p.ntiles % 2 == 0) {
-      // the normed gate/up pair with hi/lo operands: two tiles per work-group
+    if (gc.xsrc == XSRC_NORM && gc.split && p.ntiles % 2 == 0) {
+      // normed hi/lo operands: two tiles per work-group share the operand registers and
+      // halve the operand reads from L2
       pl.tiles_per_wg = 2;
       pl.grid = p.ntiles / 2;
     }
@@ -548,23 +551,18 @@ dflash_status dflash_cache_append(dflash_ctx* ctx, const void* resid, int32_t n,
   for (int64_t r0 = first; r0 < n; r0 += GEMM_MAX_ROWS) {
     const int rc = (int)std::min<int64_t>(GEMM_MAX_ROWS, n - r0);
     float* fc_out = (float*)(ctx->ws + ctx->lay.app_fc);
-    void* cbuf = ctx->ws + ctx->lay.app_c;
-    void* cbuf_lo = lo_plane(g, cbuf, GEMM_MAX_ROWS, c.hidden);
     float* kv = (float*)(ctx->ws + ctx->lay.app_kv);
     GemmCall f{EPI_STORE, XSRC_GLOBAL, {seg(ctx->fc, 0, c.hidden)}, (int)F,
                (const unsigned char*)resid + (size_t)r0 * F * g.act_elt, F, nullptr, fc_out, c.hidden, nullptr};
     dflash_status s = run_gemm(ctx, f, rc, st);
     if (s != DFLASH_OK) return s;
-    s = dev(ctx, launch_rownorm(g.bf, fc_out, ctx->enc_norm, c.rms_eps, rc, c.hidden, cbuf, cbuf_lo, st),
-            "encoder norm");
-    if (s != DFLASH_OK) return s;
-    // per-layer k/v projections of the encoder rows, six layers per launch
+    // per-layer k/v projections of the encoder rows (output_norm_enc fused as the operand
+    // norm), six layers per launch
     for (int l0 = 0; l0 < c.layers; l0 += GEMM_MAXSEG / 2) {
       const int l1 = std::min(c.layers, l0 + GEMM_MAXSEG / 2);
-      GemmCall kvc{EPI_STORE, XSRC_GLOBAL, {}, c.hidden, cbuf, c.hidden, nullptr,
+      GemmCall kvc{EPI_STORE, XSRC_NORM, {}, c.hidden, fc_out, c.hidden, ctx->enc_norm,
                    kv + (size_t)l0 * 2 * kvd, kv_cols, nullptr};
       kvc.split = g.bf;
-      kvc.xlo = cbuf_lo;
       for (int l = l0; l < l1; ++l) {
         kvc.segs.push_back(seg(ctx->layers[l].k, (l - l0) * 2 * kvd, kvd));
         kvc.segs.push_back(seg(ctx->layers[l].v, (l - l0) * 2 * kvd + kvd, kvd));

@@ -117,7 +117,8 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
 
   float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
-  float* rinv = red + (size_t)NRED * nw * RT * NB * 256;  // [R] (RMSNorm prologue)
+  // XSRC_NORM: per wave, the sum of squares of each row over the wave's k range [nw][RT*16]
+  float* ssq = red + (size_t)NRED * nw * RT * NB * 256;
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues run with T dividing the tile count
@@ -327,6 +328,17 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
         v[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int ww = 0; ww < nw; ++ww) v[nb] += *(const f32x4_t*)&rb[((size_t)((ww * RT + rt) * NB + nb) * 64 + lane) * 4];
       }
+      if constexpr (XSRC == XSRC_NORM) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rt * 16 + 4 * lg + q;
+          float tot = 0.f;
+          for (int ww = 0; ww < nw; ++ww) tot += ssq[ww * RT * 16 + r];
+          const float rs = rsqrtf(tot / (float)K + p.eps);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) v[nb][q] *= rs;
+        }
+      }
       const int col = 16 * j + li;
       if constexpr (EPI == EPI_ARGMAX) {
 #pragma unroll
@@ -374,25 +386,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   if constexpr (XSRC == XSRC_GLOBAL) load_x(xbuf[0], xlbuf[0], 0);
 
   if constexpr (XSRC != XSRC_GLOBAL) {
-    if constexpr (XSRC == XSRC_NORM) {
-      // one wave per row replays the row RMSNorm kernel's sum of squares operation for
-      // operation (256 strided partial sums, wave butterflies, the four wave sums in
-      // order), so a row normalised here or there yields the same bits
-      const float* xf = (const float*)p.x;
-      for (int r = w; r < R; r += nw) {
-        const float* xrow = xf + (size_t)r * p.ldx;
-        float q[4];
+    // RMSNorm operands: the row scale rsqrt(mean(x^2) + eps) is one number per row, so the
+    // operand is x * g and the scale multiplies the finished dot products (finalize); the
+    // sums of squares come from the same loads, per lane, then per wave, then across waves
+    float ssl[RT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float ss = 0.f;
-#pragma unroll 8
-          for (int k = j * 64 + lane; k < K; k += 256) ss = fmaf(xrow[k], xrow[k], ss);
-          q[j] = wave_sum(ss);
-        }
-        if (lane == 0) rinv[r] = rsqrtf((((q[0] + q[1]) + q[2]) + q[3]) / (float)K + p.eps);
-      }
-      __syncthreads();
-    }
+    for (int rt = 0; rt < RT; ++rt) ssl[rt] = 0.f;
     // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
 #pragma unroll
     for (int c = 0; c < XR; ++c)
@@ -410,33 +409,46 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
               if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
             } else {
               const float* src = (const float*)p.x + (size_t)r * p.ldx + k;
-              const float s = rinv[r];
               if constexpr (BF) {
                 const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
                 const u32x4_t gb = *(const u32x4_t*)((const uint16_t*)p.gain + k);
                 float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
+                for (int e = 0; e < 8; ++e) ssl[rt] = fmaf(v[e], v[e], ssl[rt]);
+#pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                   const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
-                  uint16_t h0, l0, h1, l1;
-                  split_bf16(v[2 * e2] * s * g0, h0, l0);
-                  split_bf16(v[2 * e2 + 1] * s * g1, h1, l1);
-                  f[e2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                  fl[e2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+                  uint32_t hp, lp;
+                  split2_bf16(v[2 * e2] * g0, v[2 * e2 + 1] * g1, hp, lp);
+                  f[e2] = hp;
+                  fl[e2] = lp;
                 }
               } else {
                 const float4 a0 = *(const float4*)src;
                 const float4 g = *(const float4*)((const float*)p.gain + k);
-                f[0] = __float_as_uint(a0.x * s * g.x);
-                f[1] = __float_as_uint(a0.y * s * g.y);
-                f[2] = __float_as_uint(a0.z * s * g.z);
-                f[3] = __float_as_uint(a0.w * s * g.w);
+                ssl[rt] = fmaf(a0.x, a0.x, ssl[rt]);
+                ssl[rt] = fmaf(a0.y, a0.y, ssl[rt]);
+                ssl[rt] = fmaf(a0.z, a0.z, ssl[rt]);
+                ssl[rt] = fmaf(a0.w, a0.w, ssl[rt]);
+                f[0] = __float_as_uint(a0.x * g.x);
+                f[1] = __float_as_uint(a0.y * g.y);
+                f[2] = __float_as_uint(a0.z * g.z);
+                f[3] = __float_as_uint(a0.w * g.w);
               }
             }
           }
           xr[c][rt][st] = f;
           if constexpr (SPLIT) xrl[c][rt][st] = fl;
         }
+    if constexpr (XSRC == XSRC_NORM) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float v = ssl[rt];
+        v += __shfl_xor(v, 16, 64);  // the four lanes of row li, in a fixed order
+        v += __shfl_xor(v, 32, 64);
+        if (lg == 0) ssq[w * RT * 16 + rt * 16 + li] = v;
+      }
+    }
     if constexpr (Q4) {
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi)

@@ -65,11 +65,13 @@ struct GemmPlan {
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc);
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 // LDS of a GEMM work-group, first part: the cross-wave reduction buffers (double-buffered
-// across tiles when a work-group owns several) and the RMSNorm row scales (XSRC_NORM).
+// across tiles when a work-group owns several) and the per-wave row sums of squares of the
+// RMSNorm operands (XSRC_NORM).
 __host__ __device__ inline size_t gemm_lds_red_bytes(int xsrc, int R, int waves, int rows_pad, int nb,
                                                      int tiles_per_wg) {
+  (void)R;
   size_t b = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * (rows_pad / 16) * nb * 1024;
-  if (xsrc == XSRC_NORM) b += (size_t)R * 4;
+  if (xsrc == XSRC_NORM) b += (size_t)waves * rows_pad * 4;
   return (b + 15) & ~(size_t)15;
 }
 // Whole LDS of a GEMM work-group (today the part above for every weight type).
