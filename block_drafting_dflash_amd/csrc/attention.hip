@@ -1,23 +1,29 @@
 // Attention side of the DFlash block forward: per-head q/k RMSNorm + RoPE, the ring
-// context cache writes, and bidirectional sliding-window attention over the ring plus the
-// block's own keys.
+// context cache writes, and bidirectional sliding-window attention over the ring.
 //
 // The drafter attends with a bidirectional mask over absolute positions, |q - k| <= W,
 // and its context cache is a temporal window whose wrapped ring hands out slots in
 // physical order, so the mask must use absolute key positions (lablup/mlxcel #1762 "Muse
-// Glimmer DFlash assistant drafter on the round loop", What changed). Here the ring slot
-// of position p is (p + phase) mod C and the kernel walks keys in absolute-position order,
-// so the window never has to be rebuilt or rotated: context keys are positions
-// max(0, e-W)..e-1, followed by the block's transient keys at e..e+R-1.
+// Glimmer DFlash assistant drafter on the round loop", What changed). The block's own keys
+// follow the context keys (lablup/mlxcel #1751 "LFM2 / LFM2.5 DSpark drafter on the DFlash
+// loop", Verified against the issue: proposal K/V concatenated after the context K/V).
 //
-// Ring layout per layer: K as [kv head][slot][head dim] and V transposed, [kv head][head
-// dim][slot], so that both MFMA operands of the attention read consecutive elements: a key
-// row for the scores, a run of consecutive keys at one dim for the output.
+// Ring: the slot of absolute position p is (p + phase) mod Cs, with the storage capacity
+// Cs and the phase multiples of 8 (AttnShape cap / phase). Per layer, K is stored as
+// [kv head][slot][head dim] and V transposed, [kv head][head dim][slot], so that both MFMA
+// operands of the attention read consecutive elements: a key row for the scores, a run of
+// eight consecutive keys at one dim for the output. The draft writes the block's own k/v
+// into the slots of positions e..e+R-1 (past the committed window; the append of the
+// verified rows overwrites them), so all keys of a query, positions max(0, e-W)..e+R-1,
+// come from the ring. The ring is zeroed when the context is created, so every slot holds
+// finite values and keys outside a query's window can be read and given weight exactly 0.
 //
-// Work split: one work-group per (kv head, chunk of 64 keys) computes, for the kv
-// group's query vectors, the chunk's max logit m, sum of exp l and unnormalised output;
-// a combine kernel merges the chunks in chunk order (fixed, so results do not depend on
-// scheduling) and writes the attention output in the GEMM operand dtype.
+// Work split: keys are cut into chunks of 64 absolute positions (aligned to multiples of
+// 64, so the cut never depends on the phase and every 8-key run is one aligned 16-byte
+// load). One work-group per (chunk, kv head) computes, for the kv group's query vectors,
+// the chunk's max logit m, sum of exp l and unnormalised output; a combine kernel merges
+// the chunks in chunk order (fixed, so results do not depend on scheduling) and writes the
+// attention output as the O-projection operand.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,14 +33,16 @@ namespace dflash {
 // multiple of four so that output rows stay 16-byte aligned
 #define PART_STRIDE(hd) ((hd) + 4)
 
+__device__ __forceinline__ int64_t ring_slot(const AttnShape& a, int64_t pos) { return (pos + a.phase) % a.cap; }
+
 // ---- q/k RMSNorm + RoPE on the block rows -----------------------------------------------
-// One wave per (row, head). Lane i < hd/2 owns the rotate-half pair (i, i + hd/2).
-// q leaves as an attention operand (hi/lo bf16 planes, or f32); k and v are rounded to the
-// cache dtype, as they sit next to the ring's keys and values.
+// One wave per (row, head). Lane i < hd/2 owns the rotate-half pair (i, i + hd/2). q leaves
+// as an attention operand (hi/lo bf16 planes, or f32); k and v go to the ring slots of
+// positions pos0 + r in the cache dtype.
 template <bool BF>
 __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float* __restrict__ qkv,
                                                         const void* qnorm, const void* knorm, int R,
-                                                        int64_t pos0, void* qb, void* qlo, void* kb, void* vb) {
+                                                        int64_t pos0, void* qb, void* qlo, void* ring_layer) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int heads = a.nq + 2 * a.nkv;
@@ -44,12 +52,13 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float
   const float* src = qkv + (size_t)r * heads * hd + (size_t)h * hd;
   const bool act = lane < half;
   float x1 = act ? src[lane] : 0.f, x2 = act ? src[lane + half] : 0.f;
-  if (h >= a.nq + a.nkv) {  // v head: cast only
-    void* dst = vb;
-    const size_t o = ((size_t)r * a.nkv + (h - a.nq - a.nkv)) * hd;
+  const size_t slot = (size_t)ring_slot(a, pos0 + r);
+  const size_t plane = (size_t)a.cap * hd;
+  if (h >= a.nq + a.nkv) {  // v head: cast into V^T [head][dim][slot]
+    const size_t vbase = (size_t)(a.nkv + (h - a.nq - a.nkv)) * plane;
     if (act) {
-      act_st<BF>(dst, o + lane, x1);
-      act_st<BF>(dst, o + lane + half, x2);
+      act_st<BF>(ring_layer, vbase + (size_t)lane * a.cap + slot, x1);
+      act_st<BF>(ring_layer, vbase + (size_t)(lane + half) * a.cap + slot, x2);
     }
     return;
   }
@@ -70,15 +79,15 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float
     op_st<BF>(qb, qlo, o + lane, y1);
     op_st<BF>(qb, qlo, o + lane + half, y2);
   } else {
-    const size_t o = ((size_t)r * a.nkv + (h - a.nq)) * hd;
-    act_st<BF>(kb, o + lane, y1);
-    act_st<BF>(kb, o + lane + half, y2);
+    const size_t kbase = (size_t)(h - a.nq) * plane + slot * hd;
+    act_st<BF>(ring_layer, kbase + lane, y1);
+    act_st<BF>(ring_layer, kbase + lane + half, y2);
   }
 }
 
 // ---- context K/V into the ring ----------------------------------------------------------
 // kv: f32 [n, L, 2, nkv, hd] (k then v per layer). One wave per (row, layer, kv slot).
-// ring: act, per layer K [nkv][C][hd] then V^T [nkv][hd][C].
+// ring: act, per layer K [nkv][Cs][hd] then V^T [nkv][hd][Cs].
 template <bool BF>
 __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const float* __restrict__ kv,
                                                          const void* const* knorms, int n, int64_t pos0,
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
   const bool act = lane < half;
   float x1 = act ? src[lane] : 0.f, x2 = act ? src[lane + half] : 0.f;
   const int64_t pos = pos0 + r;
-  const int64_t slot = (pos + a.phase) % a.cap;
+  const size_t slot = (size_t)ring_slot(a, pos);
   // K row at (l, 0, h, slot); V element d at (l, 1, h, d, slot)
   const size_t plane = (((size_t)l * 2 + isv) * a.nkv + h) * (size_t)a.cap * hd;
   if (!isv) {
@@ -117,8 +126,8 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
   }
   if (act) {
     if (!isv) {
-      act_st<BF>(ring, plane + (size_t)slot * hd + lane, x1);
-      act_st<BF>(ring, plane + (size_t)slot * hd + lane + half, x2);
+      act_st<BF>(ring, plane + slot * hd + lane, x1);
+      act_st<BF>(ring, plane + slot * hd + lane + half, x2);
     } else {
       act_st<BF>(ring, plane + (size_t)lane * a.cap + slot, x1);
       act_st<BF>(ring, plane + (size_t)(lane + half) * a.cap + slot, x2);
@@ -126,13 +135,21 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
   }
 }
 
-// ---- attention: partial softmax per (kv head, key chunk) --------------------------------
-// Query vector qi = r * G + hh (G = nq / nkv query heads of kv head g). part layout:
-// [nkv][nchunks][R*G][hd + 2] = (unnormalised output, m, l).
+// Keys of a query: absolute positions lo..e+R-1 (lo = max(0, e - W)); chunk c of a launch
+// covers positions (lo/64 + c)*64 .. + 64.
+__host__ __device__ inline int64_t attn_lo(const AttnShape& a, int64_t e) { return e > a.window ? e - a.window : 0; }
+__host__ __device__ inline int attn_nchunks(const AttnShape& a, int R, int64_t e) {
+  return (int)((e + R - 1) / ATTN_CHUNK - attn_lo(a, e) / ATTN_CHUNK + 1);
+}
+
+// ---- attention: partial softmax per (kv head, key chunk), VALU path ---------------------
+// (f32 shapes and head dims without an MFMA kernel.) Query vector qi = r * G + hh (G = nq
+// / nkv query heads of kv head g). part layout: [nkv][nchunks][R*G][PART_STRIDE(hd)] =
+// (unnormalised output, m, l).
 template <bool BF>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const void* ring_layer, const void* qb,
-                                                           const void* qlo, const void* kb, const void* vb, int R,
-                                                           int64_t e, int nchunks, float* __restrict__ part) {
+                                                           const void* qlo, int R, int64_t e, int nchunks,
+                                                           float* __restrict__ part) {
   extern __shared__ __align__(16) float sm[];
   const int g = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -142,39 +159,19 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
   float* Vs = Ks + ATTN_CHUNK * KS;        // [64][hd]
   float* Qs = Vs + ATTN_CHUNK * hd;        // [ATTN_QG][hd]
   float* Ss = Qs + ATTN_QG * hd;           // [ATTN_QG][64]
-  int64_t* kpos = (int64_t*)(Ss + ATTN_QG * ATTN_CHUNK);  // [64]
 
-  const int64_t lo = e > a.window ? e - a.window : 0;
-  const int nctx = (int)(e - lo);
-  const int nkeys = nctx + R;
-  const int k0 = c * ATTN_CHUNK;
-  const int kn = min(ATTN_CHUNK, nkeys - k0);
+  const int64_t lo = attn_lo(a, e), hi = e + R;
+  const int64_t p0 = (lo / ATTN_CHUNK + c) * ATTN_CHUNK;
   const size_t plane = (size_t)a.cap * hd;
-  const void* Kr = (const unsigned char*)ring_layer + ((size_t)(0 * a.nkv + g) * plane) * (BF ? 2 : 4);
-  const void* Vr = (const unsigned char*)ring_layer + ((size_t)(1 * a.nkv + g) * plane) * (BF ? 2 : 4);
+  const void* Kr = (const unsigned char*)ring_layer + ((size_t)g * plane) * (BF ? 2 : 4);
+  const void* Vr = (const unsigned char*)ring_layer + ((size_t)(a.nkv + g) * plane) * (BF ? 2 : 4);
 
-  // stage this chunk's keys and values (f32) and their absolute positions
-  for (int i = tid; i < kn * hd; i += blockDim.x) {
+  // stage this chunk's keys and values (f32); every slot holds finite values
+  for (int i = tid; i < ATTN_CHUNK * hd; i += blockDim.x) {
     const int kj = i / hd, d = i - kj * hd;
-    const int key = k0 + kj;
-    float kvv, vvv;
-    if (key < nctx) {
-      const int64_t pos = lo + key;
-      const size_t slot = (size_t)((pos + a.phase) % a.cap);
-      kvv = act_ld<BF>(Kr, slot * hd + d);
-      vvv = act_ld<BF>(Vr, (size_t)d * a.cap + slot);
-    } else {
-      const int b = key - nctx;
-      const size_t off = ((size_t)b * a.nkv + g) * hd + d;
-      kvv = act_ld<BF>(kb, off);
-      vvv = act_ld<BF>(vb, off);
-    }
-    Ks[kj * KS + d] = kvv;
-    Vs[kj * hd + d] = vvv;
-  }
-  for (int kj = tid; kj < ATTN_CHUNK; kj += blockDim.x) {
-    const int key = k0 + kj;
-    kpos[kj] = key < nctx ? lo + key : e + (key - nctx);
+    const size_t slot = (size_t)ring_slot(a, p0 + kj);
+    Ks[kj * KS + d] = act_ld<BF>(Kr, slot * hd + d);
+    Vs[kj * hd + d] = act_ld<BF>(Vr, (size_t)d * a.cap + slot);
   }
   const float scale = 1.0f / sqrtf((float)hd);
 
@@ -192,19 +189,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
     // scores: thread -> key lane, queries strided by waves
     {
       const int kj = lane;
+      const int64_t kp = p0 + kj;
       for (int qi = w; qi < nq; qi += 4) {
         float sc = -INFINITY;
-        if (kj < kn) {
-          const int r = (q0 + qi) / G;
-          const int64_t qp = e + r, kp = kpos[kj];
-          const int64_t dist = qp > kp ? qp - kp : kp - qp;
-          if (dist <= a.window) {
-            float s = 0.f;
-            const float* qv = Qs + qi * hd;
-            const float* kv = Ks + kj * KS;
-            for (int d = 0; d < hd; ++d) s += qv[d] * kv[d];
-            sc = s * scale;
-          }
+        const int64_t qp = e + (q0 + qi) / G;
+        const int64_t dist = qp > kp ? qp - kp : kp - qp;
+        if (kp >= lo && kp < hi && dist <= a.window) {
+          float s = 0.f;
+          const float* qv = Qs + qi * hd;
+          const float* kv = Ks + kj * KS;
+          for (int d = 0; d < hd; ++d) s += qv[d] * kv[d];
+          sc = s * scale;
         }
         Ss[qi * ATTN_CHUNK + kj] = sc;
       }
@@ -229,28 +224,26 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
       const int qi = i / hd, d = i - qi * hd;
       float o = 0.f;
       const float* pr = Ss + qi * ATTN_CHUNK;
-      for (int kj = 0; kj < kn; ++kj) o += pr[kj] * Vs[kj * hd + d];
+      for (int kj = 0; kj < ATTN_CHUNK; ++kj) o += pr[kj] * Vs[kj * hd + d];
       part[(((size_t)g * nchunks + c) * NQ + q0 + qi) * PART_STRIDE(hd) + d] = o;
     }
   }
 }
 
 // ---- attention on MFMA (bf16 operands): one work-group per (64-key chunk, kv head) ------
-// Each wave takes query tiles w, w+4, ... and reads its operands straight from memory (no
+// Each wave takes query tiles w, w+4, ... and reads its operands straight from the ring (no
 // LDS): scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16 key rows, B = 16 queries), then
 // O^T = V^T P^T (A = 16 dims x 32 keys from the transposed V, B = P). The key rows of the
 // two score tiles of each 32-key half are ordered so that lane (li, lg) ends up with keys
 // 8*lg .. 8*lg+7 of the half for query li, exactly its B operand of the output product,
-// and the matching V^T run is one 16-byte load (per-key loads where the run wraps the ring
-// or reaches the block's own keys). Q (an f32 activation) and P (in [0, 1]) enter as bf16
-// pairs hi + lo, about 16 significant bits; K and V are bf16 already, products are exact
-// and sums f32.
+// and the matching V^T run is one aligned 16-byte load. Q (an f32 activation) and P (in
+// [0, 1]) enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16
+// already, products are exact and sums f32.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
                                                         const uint16_t* __restrict__ qb, const uint16_t* __restrict__ qlo,
-                                                        const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
                                                         int R, int64_t e, int nchunks, float* __restrict__ part) {
-  constexpr int KC = ATTN_CHUNK;  // 64 keys = two halves of 32
+  constexpr int KC = ATTN_CHUNK;  // 64 positions = two halves of 32
   constexpr int DS = HD / 32, DT = HD / 16;
   static_assert(KC == 64, "two 32-key halves per work-group");
   const int g = blockIdx.y, c = blockIdx.x;
@@ -258,61 +251,33 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   const int li = lane & 15, lg = lane >> 4;
   const int G = a.nq / a.nkv, NQ = R * G, nqt = (NQ + 15) / 16;
   if (w >= nqt) return;  // no barrier below: an idle wave may leave
-  const int64_t lo = e > a.window ? e - a.window : 0;
-  const int nctx = (int)(e - lo), nkeys = nctx + R;
-  const int k0 = c * KC;
+  const int64_t lo = attn_lo(a, e), hi = e + R;
+  const int64_t p0 = (lo / KC + c) * KC;
   const int C = a.cap;
   const uint16_t* Kp = ring_layer + (size_t)g * C * HD;
   const uint16_t* VTp = ring_layer + (size_t)(a.nkv + g) * HD * C;
-  // slot of context key kk (0 <= kk < nctx <= W < C: at most one wrap)
-  const int s_base = (int)((lo + a.phase) % C);
-  auto slot_of = [&](int kk) { const int sl = s_base + kk; return sl >= C ? sl - C : sl; };
+  // slot of the chunk's first position: a multiple of 8 (p0, phase and Cs are), so the
+  // runs p0 + 8j .. + 8 sit in consecutive slots s0 + 8j (mod Cs) that never wrap
+  const int s0 = (int)ring_slot(a, p0);
+  auto slot_at = [&](int kk) { const int sl = s0 + kk; return sl >= C ? sl - C : sl; };
 
-  // ---- K rows: half h, tile tb, row li <-> key 32h + 8*(li/4) + 4*tb + li%4 --------------
+  // ---- K rows: half h, tile tb, row li <-> position p0 + 32h + 8*(li/4) + 4*tb + li%4 -----
   u32x4_t kf[2][2][DS];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int key = k0 + 32 * h + 8 * (li >> 2) + 4 * tb + (li & 3);
-      const uint16_t* row = nullptr;
-      if (key < nctx) row = Kp + (size_t)slot_of(key) * HD;
-      else if (key < nkeys) row = kb + ((size_t)(key - nctx) * a.nkv + g) * HD;
+      const uint16_t* row = Kp + (size_t)slot_at(32 * h + 8 * (li >> 2) + 4 * tb + (li & 3)) * HD;
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        kf[h][tb][s] = u32x4_t{0u, 0u, 0u, 0u};
-        if (row) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
-      }
+      for (int s = 0; s < DS; ++s) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
     }
-  // ---- V^T runs: half h, dim tile dt: dim dt*16 + li, keys 32h + 8*lg .. + 8 ------------
+  // ---- V^T runs: half h, dim tile dt: dim dt*16 + li, positions p0 + 32h + 8*lg .. + 8 ----
   u32x4_t vf[2][DT];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int kr = k0 + 32 * h + 8 * lg;
-    const bool run = kr + 7 < nctx && slot_of(kr) + 7 < C;  // eight context keys in consecutive slots
+    const int sl = slot_at(32 * h + 8 * lg);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int dim = dt * 16 + li;
-      if (run) {
-        __builtin_memcpy(&vf[h][dt], VTp + (size_t)dim * C + slot_of(kr), 16);  // 2-byte aligned run
-      } else {
-        uint32_t wv[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint32_t pair = 0;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int key = kr + 2 * t + u;
-            uint32_t bits = 0;
-            if (key < nctx) bits = VTp[(size_t)dim * C + slot_of(key)];
-            else if (key < nkeys) bits = vb[((size_t)(key - nctx) * a.nkv + g) * HD + dim];
-            pair |= bits << (16 * u);
-          }
-          wv[t] = pair;
-        }
-        vf[h][dt] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
-      }
-    }
+    for (int dt = 0; dt < DT; ++dt) vf[h][dt] = *(const u32x4_t*)(VTp + (size_t)(dt * 16 + li) * C + sl);
   }
 
   const float scale = 1.0f / sqrtf((float)HD);
@@ -325,14 +290,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
     const size_t qo = ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      qf[s] = u32x4_t{0u, 0u, 0u, 0u};
-      qfl[s] = u32x4_t{0u, 0u, 0u, 0u};
-      if (qok) {
-        qf[s] = *(const u32x4_t*)(qb + qo + 32 * s + 8 * lg);
-        qfl[s] = *(const u32x4_t*)(qlo + qo + 32 * s + 8 * lg);
-      }
+      qf[s] = *(const u32x4_t*)(qb + qo + 32 * s + 8 * lg);
+      qfl[s] = *(const u32x4_t*)(qlo + qo + 32 * s + 8 * lg);
     }
-    // scores: element i of tile (h, tb) is key 32h + 8*lg + 4*tb + i for query li
+    // scores: element i of tile (h, tb) is position p0 + 32h + 8*lg + 4*tb + i for query li
     float S[2][2][4];
     float m = -INFINITY;
 #pragma unroll
@@ -347,10 +308,9 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 32 * h + 8 * lg + 4 * tb + i;
-          const int64_t kp = key < nctx ? lo + key : e + (key - nctx);
+          const int64_t kp = p0 + 32 * h + 8 * lg + 4 * tb + i;
           const int64_t dist = qpos > kp ? qpos - kp : kp - qpos;
-          const bool vis = qok && key < nkeys && dist <= a.window;
+          const bool vis = qok && kp >= lo && kp < hi && dist <= a.window;
           S[h][tb][i] = vis ? acc[i] * scale : -INFINITY;
           m = fmaxf(m, S[h][tb][i]);
         }
@@ -440,8 +400,8 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
     const int d = (int)(i % hd);
     const size_t t = i / hd;
     const int j = (int)(t % n), h = (int)(t / n);
-    const size_t slot = (size_t)((lo + j + a.phase) % a.cap);
-    const size_t ko = (size_t)h * plane + slot * hd + d;               // K [h][slot][d]
+    const size_t slot = (size_t)ring_slot(a, lo + j);
+    const size_t ko = (size_t)h * plane + slot * hd + d;                       // K [h][slot][d]
     const size_t vo = (size_t)(a.nkv + h) * plane + (size_t)d * a.cap + slot;  // V^T [h][d][slot]
     if constexpr (BF) {
       ((uint16_t*)kout)[i] = ((const uint16_t*)ring_layer)[ko];
@@ -455,13 +415,15 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
 
 // ---- launchers ------------------------------------------------------------------------------
 hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
-                            int R, int64_t pos0, void* qb, void* qlo, void* kb, void* vb, hipStream_t s) {
+                            int R, int64_t pos0, void* qb, void* qlo, void* ring_layer, hipStream_t s) {
   const int items = R * (a.nq + 2 * a.nkv);
   const int grid = (items + 3) / 4;
   if (bf)
-    hipLaunchKernelGGL(attn_prep_kernel<true>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo, kb, vb);
+    hipLaunchKernelGGL(attn_prep_kernel<true>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo,
+                       ring_layer);
   else
-    hipLaunchKernelGGL(attn_prep_kernel<false>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo, kb, vb);
+    hipLaunchKernelGGL(attn_prep_kernel<false>, dim3(grid), dim3(256), 0, s, a, qkv, qnorm, knorm, R, pos0, qb, qlo,
+                       ring_layer);
   return hipGetLastError();
 }
 
@@ -476,38 +438,33 @@ hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const 
 
 static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
 
-static int attn_nchunks(int bf, const AttnShape& a, int R, int64_t e) {
-  const int64_t lo = e > a.window ? e - a.window : 0;
-  const int nkeys = (int)(e - lo) + R;
-  (void)bf;
-  return (nkeys + ATTN_CHUNK - 1) / ATTN_CHUNK;
-}
-
 size_t attention_partial_floats(const AttnShape& a, int R) {
-  const int nch = (a.window + R + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  // chunks of a launch: positions lo..e+R-1 (at most W + R of them) cut at multiples of 64
+  const int nch = (a.window + R + 2 * ATTN_CHUNK - 2) / ATTN_CHUNK;
   return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * PART_STRIDE(a.hd);
 }
 
+int attention_max_chunks() { return COMBINE_MAX_CHUNKS; }
+
 hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* qlo,
-                            const void* kb, const void* vb, int R, int64_t e, float* part, void* out, void* out_lo,
-                            hipStream_t s) {
-  const int nch = attn_nchunks(bf, a, R, e);
+                            int R, int64_t e, float* part, void* out, void* out_lo, hipStream_t s) {
+  const int nch = attn_nchunks(a, R, e);
+  if (nch > COMBINE_MAX_CHUNKS) return hipErrorInvalidValue;
   dim3 grid(nch, a.nkv);
   if (use_mfma(bf, a)) {
     const uint16_t* rl = (const uint16_t*)ring_layer;
     if (a.hd == 128)
       hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
-                         (const uint16_t*)kb, (const uint16_t*)vb, R, e, nch, part);
+                         R, e, nch, part);
     else
       hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
-                         (const uint16_t*)kb, (const uint16_t*)vb, R, e, nch, part);
+                         R, e, nch, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4 +
-                     ATTN_CHUNK * 8;
+  const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4;
   const void* fn = bf ? (const void*)attn_partial_kernel<true> : (const void*)attn_partial_kernel<false>;
   static bool attr_set[2] = {false, false};
   hipError_t err = hipSuccess;
@@ -517,9 +474,9 @@ hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, 
     attr_set[bf ? 1 : 0] = true;
   }
   if (bf)
-    hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, kb, vb, R, e, nch, part);
+    hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, R, e, nch, part);
   else
-    hipLaunchKernelGGL(attn_partial_kernel<false>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, kb, vb, R, e, nch, part);
+    hipLaunchKernelGGL(attn_partial_kernel<false>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, R, e, nch, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (bf) hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);

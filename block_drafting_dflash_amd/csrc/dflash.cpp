@@ -31,7 +31,7 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, kb, vb, attn, mlp, zrows, part, app_fc, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, app_fc, app_kv, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -48,7 +48,8 @@ struct Cfg {
   bool bf;      // act dtype bf16
   int act_elt;  // bytes per activation / ring element
   int R;        // max rows of a block forward = max_block + 1
-  int64_t S, C;
+  int64_t S, C;  // slack and capacity of the window (C = W + S)
+  int64_t Cs;    // slots stored: C rounded up to a multiple of 8, at least W + R and 64
   AttnShape a;
 };
 
@@ -148,7 +149,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   const int64_t fin = (int64_t)c->target_streams * c->target_width;
   const int64_t H = c->hidden;
   const int64_t products[] = {qd, kvd, fin, H * c->vocab, H * c->intermediate, H * fin, H * qd,
-                              (int64_t)c->layers * 2 * kvd * (c->window + 128 + c->max_block)};
+                              (int64_t)c->layers * 2 * kvd * (c->window + 128 + c->max_block + 72)};
   for (int64_t v : products)
     if (v > INT32_MAX) return cfg_fail(err, DFLASH_E_SHAPE, "a dimension product would wrap an int32");
   const int unit = chunk_steps(1) * kstep(wt);
@@ -178,14 +179,18 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   g.R = c->max_block + 1;
   g.S = slack_rows(c->max_block);
   g.C = c->window + g.S;
+  // storage: the block's own keys (positions e..e+R-1) get slots of their own past the
+  // window, and the slot grid is 8-aligned so that attention reads aligned 8-key runs
+  g.Cs = std::max<int64_t>({g.C, (int64_t)c->window + g.R, (int64_t)64});
+  g.Cs = (g.Cs + 7) & ~(int64_t)7;
   if (c->ring_phase < 0) return cfg_fail(err, DFLASH_E_ARG, "ring_phase must be >= 0");
   g.a.nq = c->q_heads;
   g.a.nkv = c->kv_heads;
   g.a.hd = c->head_dim;
   g.a.L = c->layers;
   g.a.window = c->window;
-  g.a.cap = (int32_t)g.C;
-  g.a.phase = (int32_t)(c->ring_phase % g.C);
+  g.a.cap = (int32_t)g.Cs;
+  g.a.phase = (int32_t)((c->ring_phase % g.Cs) & ~(int64_t)7);
   g.a.eps = c->rms_eps;
   g.a.theta = c->rope_theta;
   *out = g;
@@ -215,8 +220,6 @@ Layout make_layout(const Cfg& g) {
   L.hn = take(4 * hn_rows(g) * H);  // normed rows of launches past one row tile
   L.qkv = take(4 * R * (qd + 2 * kvd));
   L.qb = take(4 * R * qd);
-  L.kb = take(ae * R * kvd);
-  L.vb = take(ae * R * kvd);
   L.attn = take(4 * R * qd);
   L.mlp = take(4 * R * c.intermediate);
   L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
@@ -228,7 +231,7 @@ Layout make_layout(const Cfg& g) {
 }
 
 size_t ring_bytes_of(const Cfg& g) {
-  return (size_t)g.act_elt * g.c.layers * 2 * g.c.kv_heads * (size_t)g.C * g.c.head_dim;
+  return (size_t)g.act_elt * g.c.layers * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
 }
 
 // Fragment-major copies of every linear live in the caller's packed buffer, in this order:
@@ -504,6 +507,9 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   if (e == hipSuccess)
     e = hipMemcpyAsync(ctx->ws + lay.knorm_ptrs, knorms.data(), sizeof(void*) * knorms.size(),
                        hipMemcpyHostToDevice, st);
+  // every slot starts finite (zero): attention reads whole aligned runs of slots, including
+  // keys outside a query's window that then get weight 0
+  if (e == hipSuccess) e = hipMemsetAsync(ring, 0, ring_bytes_of(g), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
   if (e != hipSuccess) {
     cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
@@ -601,15 +607,13 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   float* x = (float*)(ctx->ws + ctx->lay.x);
   float* qkv = (float*)(ctx->ws + ctx->lay.qkv);
   void* qb = ctx->ws + ctx->lay.qb;
-  void* kb = ctx->ws + ctx->lay.kb;
-  void* vb = ctx->ws + ctx->lay.vb;
   void* attn = ctx->ws + ctx->lay.attn;
   void* mlp = ctx->ws + ctx->lay.mlp;
   void* qb_lo = lo_plane(g, qb, g.R, qd);
   void* attn_lo = lo_plane(g, attn, g.R, qd);
   void* mlp_lo = lo_plane(g, mlp, g.R, c.intermediate);
   float* part = (float*)(ctx->ws + ctx->lay.part);
-  const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.C * c.head_dim;
+  const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * c.head_dim;
 
   dflash_status s = dev(ctx, launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, x, st), "embed");
   if (s != DFLASH_OK) return s;
@@ -619,11 +623,12 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
                L.in_norm, qkv, qd + 2 * kvd, nullptr};
     q.split = g.bf;
     if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
-    s = dev(ctx, launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, qb_lo, kb, vb, st), "attn prep");
-    if (s != DFLASH_OK) return s;
+    // q as an operand; the block's own k/v into the ring slots of positions e..e+R-1
     s = dev(ctx,
-            launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, qb_lo, kb, vb, R, ctx->e, part, attn, attn_lo,
-                             st),
+            launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, qb_lo, ctx->ring + l * ring_layer, st),
+            "attn prep");
+    if (s != DFLASH_OK) return s;
+    s = dev(ctx, launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, qb_lo, R, ctx->e, part, attn, attn_lo, st),
             "attention");
     if (s != DFLASH_OK) return s;
     GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
@@ -686,7 +691,7 @@ dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, voi
   *n_out = n;
   if (n == 0) return DFLASH_OK;
   if (!k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL window output");
-  const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.C * g.c.head_dim;
+  const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
   return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),
              "cache read");
 }

@@ -81,7 +81,7 @@ size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int til
 struct AttnShape {
   int32_t nq, nkv, hd, L;
   int32_t window;
-  int32_t cap, phase;  // ring capacity C and phase
+  int32_t cap, phase;  // ring slots stored (a multiple of 8, >= 64) and phase (a multiple of 8)
   float eps, theta;
 };
 
@@ -98,15 +98,18 @@ hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anc
 // RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
                           void* out_lo, hipStream_t s);
-// q/k RMSNorm + RoPE: q as an operand (hi/lo planes qb/qlo, or f32), k/v in the cache dtype.
+// q/k RMSNorm + RoPE: q as an operand (hi/lo planes qb/qlo, or f32); k and v of the block
+// rows into the ring slots of positions pos0.. (cache dtype).
 hipError_t launch_attn_prep(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
-                            const void* knorm, int R, int64_t pos0, void* qb, void* qlo, void* kb, void* vb,
+                            const void* knorm, int R, int64_t pos0, void* qb, void* qlo, void* ring_layer,
                             hipStream_t s);
 hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
                              int n, int64_t pos0, void* ring, hipStream_t s);
+// Attention of R block rows (positions e..e+R-1) over positions max(0, e-W)..e+R-1 of the
+// ring layer; writes the O-projection operand out/out_lo.
 hipError_t launch_attention(int act_bf16, const AttnShape& a, const void* ring_layer, const void* qb,
-                            const void* qlo, const void* kb, const void* vb, int R, int64_t e, float* part,
-                            void* out, void* out_lo, hipStream_t s);
+                            const void* qlo, int R, int64_t e, float* part, void* out, void* out_lo,
+                            hipStream_t s);
 size_t attention_partial_floats(const AttnShape& a, int R);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);

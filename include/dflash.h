@@ -65,10 +65,15 @@ typedef enum {
  *     |q - p| <= W (lablup/mlxcel #1762, What changed).
  *   max_block: largest block a draft may use, 1..256. The ring's slack is
  *     S = max(clamp(8*max_block, 32, 128), max_block) rows and its capacity C = W + S
- *     (lablup/mlxcel #1762, What changed; Pre-merge review round, second finding).
+ *     (lablup/mlxcel #1762, What changed; Pre-merge review round, second finding). The
+ *     ring stores Cs = max(C, W + max_block + 1, 64) rounded up to a multiple of 8 slots
+ *     per layer and kv head, so that the draft's own block rows have slots of their own
+ *     past the window and attention reads 8-aligned runs of slots.
  *   mask_token_id: the token of the block's mask rows, in [0, vocab) (lablup/mlxcel
  *     #1751, Review fixes: the mask id indexes the target's embedding table).
- *   ring_phase: slot of absolute position p is (p + ring_phase) mod C.
+ *   ring_phase: slot of absolute position p is (p + phi) mod Cs, with phi = ring_phase
+ *     mod Cs rounded down to a multiple of 8. Nothing the calls return depends on it; it
+ *     places the ring's wrap point (tests force wraps with it).
  *   weight_dtype: dtype of fc, every layer linear and the lm_head. With DFLASH_Q4G64
  *     the embedding table and the norm gains are bf16; otherwise they use weight_dtype.
  *   act_dtype: DFLASH_F32 with f32 weights, DFLASH_BF16 otherwise. It is the dtype of
@@ -107,8 +112,8 @@ typedef struct {
   const dflash_layer *layers;
 } dflash_weights;
 
-/* Bytes of ring, of workspace and of packed weights a context with this config needs.
- * Host only. */
+/* Bytes of ring (layers * 2 * kv_heads * Cs * head_dim * act element size), of workspace
+ * and of packed weights a context with this config needs. Host only. */
 dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, size_t *workspace_bytes,
                                  size_t *packed_bytes);
 
@@ -120,7 +125,7 @@ dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, s
  * weight streams of every later call read whole contiguous kilobytes. The call
  * synchronises `stream`; afterwards the caller may free those row-major linears. The
  * embedding table and the norm gains are read in place and must stay alive. The ring
- * starts empty: e = 0, no pending rows. */
+ * zero-filled and starts empty: e = 0, no pending rows. */
 dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *weights, void *ring,
                             size_t ring_bytes, void *workspace, size_t workspace_bytes, void *packed,
                             size_t packed_bytes, void *stream, dflash_ctx **out);
@@ -153,7 +158,9 @@ dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
  * Draft one block: rows [anchor, mask x block] at absolute positions e..e+block are
  * embedded with the raw table, run through every layer over the ring's committed
  * context and the block's own keys, and rows 1..block go through final_norm and the
- * lm_head. d_tokens (device int32 [block]) receives the first index of each row's
+ * lm_head. Each layer writes the block's own k/v into the ring slots of positions
+ * e..e+block, which lie past the committed window (dflash_cache_read never returns them
+ * and the next append overwrites them). d_tokens (device int32 [block]) receives the first index of each row's
  * maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
  * residual stream after the last layer. Errors: block outside 1..max_block or anchor
  * outside [0, vocab) (DFLASH_E_RANGE); e == 0 (DFLASH_E_NO_CONTEXT); pending rows

@@ -55,16 +55,20 @@ def status_of(shape, max_block=4, **cfg_over):
 
 
 def test_ring_size_follows_the_slack_rule():
-    """ring bytes = layers * 2 (K,V) * kv_heads * (W + S) * head_dim * element size, with
-    S read from the slack table the page states."""
+    """ring bytes = layers * 2 (K,V) * kv_heads * Cs * head_dim * element size, where the
+    stored slots Cs are the capacity W + S (S from the slack table the page states), raised
+    to W + block + 1 and 64 at least, rounded up to a multiple of 8."""
     table = json.load(open(os.path.join(ROOT, "tests", "golden", "slack_table.json")))["table"]
-    for sh in (synth.TINY_F32, synth.MUSE_BF16):
+    for sh in (synth.TINY_F32, synth.MUSE_BF16, synth.TINY_F32.with_(window=9)):
         elt = 4 if sh.act_dtype == "f32" else 2
         for b, S in table.items():
             if int(b) > 256:
                 continue
+            cs = max(sh.window + S, sh.window + int(b) + 1, 64)
+            cs = (cs + 7) // 8 * 8
             ring, ws, packed = sizes(sh, int(b))
-            assert ring == sh.layers * 2 * sh.kv_heads * (sh.window + S) * sh.head_dim * elt, (sh, b)
+            assert ring == sh.layers * 2 * sh.kv_heads * cs * sh.head_dim * elt, (sh, b)
+            assert cs >= sh.window + S  # the capacity the slack rule asks for is there
 
 
 def test_packed_size_covers_every_linear_once():

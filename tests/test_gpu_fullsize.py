@@ -63,8 +63,11 @@ def test_ctx16384_forced_wraps_random_depth(muse, block, rounds):
     w64, dev = muse
     wl = synth.WORKLOADS["muse-bf16-ctx16384-wrap"]
     S = max(min(max(8 * block, 32), 128), block)
-    C = SH.window + S
-    phase = synth.ring_phase_for_wrap(C, wl.context, block + 1)
+    # the library stores Cs slots (8-aligned) and rounds the phase down to a multiple of 8:
+    # put the first round's append at slot Cs - 8 so its block + 1 >= 9 rows straddle the end
+    Cs = (max(SH.window + S, SH.window + block + 1, 64) + 7) // 8 * 8
+    phase = (Cs - 8 - wl.context) % Cs
+    assert phase % 8 == 0
     ls = P.LockStep(SH, w64, max_block=block, phase=phase, dev_weights=dev)
     ks = P.run_random_depth_rounds(ls, wl.context, block, rounds, tag=block)
     e0 = ls.gpu.cache_state()[0]
@@ -73,8 +76,8 @@ def test_ctx16384_forced_wraps_random_depth(muse, block, rounds):
     assert ls.gpu.cache_state()[:2] == (e0, 0)
     ks += P.run_random_depth_rounds(ls, 0, block, 2, tag=500 + block, prefill=False)
     _report(f"{wl.name} block {block}", ls, ks)
-    first_slot = (wl.context + phase) % C
-    assert first_slot + block + 1 > C  # the first append did straddle the ring end
+    first_slot = (wl.context + phase) % Cs
+    assert first_slot + block + 1 > Cs  # the first append did straddle the ring end
 
 
 @pytest.fixture(scope="module")
