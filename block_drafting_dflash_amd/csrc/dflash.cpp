@@ -169,7 +169,7 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   for (const auto& gm : gemms)
     if (!plan_gemm(wt, gm.epi, gm.xsrc, (int)gm.K, &pl))
       return cfg_fail(err, DFLASH_E_SHAPE, "no GEMM launch plan for a contraction of length %lld", (long long)gm.K);
-  if (gemm_lds_bytes(wt, XSRC_NORM, 16, 8, 2, c->hidden, 1) > (size_t)LDS_BYTES)
+  if (gemm_lds_bytes(wt, XSRC_NORM, 1, 16, 8, 2, c->hidden, 2) > (size_t)LDS_BYTES)
     return cfg_fail(err, DFLASH_E_SHAPE, "hidden too large for the staged operand");
   Cfg g;
   g.c = *c;
@@ -328,12 +328,15 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   for (const auto& s : gc.segs) N = std::max(N, s.col0 + s.rows);
   int r0 = 0;
   while (r0 < rows) {
-    int rc = std::min(rows - r0, GEMM_MAX_ROWS);
+    // bf16 and 4-bit weights take at most two row tiles per launch: their operand rows are
+    // staged through LDS there, while a three-tile launch loads 48-row fragments per wave
+    // (measured slower than two staged launches over the same rows)
+    int rc = std::min(rows - r0, g.bf ? 32 : GEMM_MAX_ROWS);
     if (gc.epi == EPI_ARGMAX) rc = std::min(rc, std::min(32, 16 * waves));  // one finishing wave per row tile
-    if (gc.xsrc != XSRC_GLOBAL)
-      while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, rc, waves, nb, gc.K, gc.epi == EPI_ARGMAX ? 2 : 1) >
-                           (size_t)LDS_BYTES)
-        --rc;
+    // tiles per work-group that size the reduction buffers: two or more for the argmax, two
+    // for normed hi/lo operands over an even tile count (the launch below)
+    const int tpw_lds = gc.epi == EPI_ARGMAX || (gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0) ? 2 : 1;
+    while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
     GemmParams p{};
     for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
     p.nseg = (int)gc.segs.size();

@@ -9,11 +9,8 @@ hipError_t launch_gemm_f32(const GemmPlan& pl, int epi, int xsrc, const GemmPara
 hipError_t launch_gemm_bf16(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_q4(const GemmPlan& pl, int epi, int xsrc, const GemmParams& p, hipStream_t s);
 
-size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int tiles_per_wg) {
-  const int rows_pad = 16 * ((R + 15) / 16);
-  (void)wt;
-  (void)K;
-  return gemm_lds_red_bytes(xsrc, R, waves, rows_pad, nb, tiles_per_wg);
+size_t gemm_lds_bytes(int wt, int xsrc, int split, int R, int waves, int nb, int K, int tiles_per_wg) {
+  return gemm_lds_layout(wt, xsrc, split, R, waves, nb, K, tiles_per_wg).total;
 }
 
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {
@@ -29,6 +26,8 @@ bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
   if (p.R < 1 || p.R > GEMM_MAX_ROWS || pl.grid < 1 || p.waves != pl.waves || !gemm_plan_supported(pl, epi, xsrc))
     return hipErrorInvalidValue;
+  if (p.nseg < 1 || p.nseg > GEMM_MAXSEG || (epi == EPI_ARGMAX && (p.nseg != 1 || p.seg[0].col0 != 0)))
+    return hipErrorInvalidValue;  // the argmax kernel reads one matrix
   if (wt == WT_F32) return launch_gemm_f32(pl, epi, xsrc, p, s);
   if (wt == WT_BF16) return launch_gemm_bf16(pl, epi, xsrc, p, s);
   if (wt == WT_Q4) return launch_gemm_q4(pl, epi, xsrc, p, s);

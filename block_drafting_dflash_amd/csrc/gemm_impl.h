@@ -73,24 +73,70 @@ __device__ __forceinline__ f32x4_t step_mfma(u32x4_t x, u32x4_t w, f32x4_t acc) 
   }
 }
 
-__device__ __forceinline__ int find_seg(const GemmParams& p, int col) {
-  int s = 0;
-  for (int i = 1; i < p.nseg; ++i)
-    if (col >= p.seg[i].col0) s = i;
-  return s;
+// The segment holding output column col: its weight and scale blocks and the column's tile
+// within it. Every segment entry is read in one batch of scalar loads and picked by
+// selects, so the first weight address waits for one kernel-argument fetch, not a chain.
+struct SegSel {
+  const unsigned char* w;
+  const unsigned char* sc;
+  int tj;
+};
+__device__ __forceinline__ SegSel select_seg(const GemmParams& p, int col) {
+  const unsigned char* w = (const unsigned char*)p.seg[0].w;
+  const unsigned char* sc = (const unsigned char*)p.seg[0].scales;
+  int c0 = p.seg[0].col0;
+#pragma unroll
+  for (int i = 1; i < GEMM_MAXSEG; ++i) {
+    const bool take = i < p.nseg && col >= p.seg[i].col0;
+    w = take ? (const unsigned char*)p.seg[i].w : w;
+    sc = take ? (const unsigned char*)p.seg[i].scales : sc;
+    c0 = take ? p.seg[i].col0 : c0;
+  }
+  return SegSel{w, sc, (col - c0) >> 4};
 }
 
 // Minimum resident waves per SIMD (the second launch-bounds argument), sized so that the
 // live registers (weights in flight, operand fragments, accumulators) never spill:
 // single-chunk single-tile launches of one row tile run hundreds of 8-wave work-groups
-// and get two per CU (<= 128 VGPRs); launches with more row tiles, hi/lo operand pairs
-// across several chunks, or the two-tile normed gate/up pair take the full budget and
+// and get two per CU (<= 128 VGPRs); launches with more row tiles, normed operands, or
+// hi/lo operand pairs across several chunks or weight blocks take the full budget and
 // fewer, larger work-groups; the multi-tile argmax launches three.
 template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int gemm_min_waves_per_simd() {
-  if (RT > 1) return 2;
-  if (T > 1) return XSRC == XSRC_NORM ? 2 : 3;
-  if (SPLIT && (NCH > 1 || NB > 1)) return NB > 1 ? 3 : 2;
+  if (RT > 1 || XSRC == XSRC_NORM) return 2;
+  if (T > 1) return 3;
+  if (SPLIT && (NCH > 1 || NB > 1)) return 2;
   return NCH == 1 ? 4 : 2;
+}
+
+// Weight chunks a wave issues before its first product. The layer GEMMs put every chunk of
+// the launch in flight at once (a launch is one round trip, not a pipeline) as far as the
+// registers beside the operands allow: streamed operands staged through LDS hold one chunk
+// of compact rows plus the fragments read back; unstaged streamed operands two chunks of
+// fragments; staged (LDS-source) operands every chunk; normed operands their raw rows while
+// the pairs are formed; and about 48 registers go to accumulators, addresses and sums. The
+// vocabulary argmax keeps shallow look-ahead: it runs thousands of work-groups, several per
+// CU, which keep the stream busy between them. f32 weights (the exact-arithmetic shapes)
+// keep one chunk ahead.
+template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+constexpr int gemm_chunks_ahead() {
+  constexpr bool Q4 = WT == WT_Q4, BF = WT != WT_F32;
+  constexpr int nit = T * NCH;
+  if (EPI == EPI_ARGMAX || !BF) return nit < (Q4 ? 3 : 1) ? nit : (Q4 ? 3 : 1);
+  constexpr int budget = 512 / gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>();
+  constexpr int planes = SPLIT ? 2 : 1;
+  constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
+  constexpr int raw = XSRC == XSRC_NORM ? RT * CH * 4 * 2 + CH * 4 : 0;
+  constexpr int gupi = 64 / (CH * 32 * 2 / 16);  // staged rows per load instruction
+  constexpr int staged = planes * ((16 * RT + gupi - 1) / gupi) * 4 + 32;
+  // normed rows of a later chunk are loaded while the earlier chunks' pairs are held
+  constexpr int opnd = XSRC == XSRC_GLOBAL ? (RT <= 2 ? staged : 2 * frag)
+                       : XSRC == XSRC_LDS  ? NCH * frag
+                       : NCH == 1          ? (raw > frag ? raw : frag)
+                                           : NCH * frag + raw;
+  constexpr int wreg = Q4 ? NB * (CH / 4) * 6 : NB * CH * 4;
+  constexpr int fit = (budget - opnd - 48) / wreg;
+  // a launch with more chunks than fit streams the rest: one more chunk buffer is live
+  return fit >= nit ? nit : (fit - 1 < 1 ? 1 : (fit - 1 > 8 ? 8 : fit - 1));
 }
 
 // T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
@@ -116,9 +162,22 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   const int K = p.K, R = p.R;
   const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
 
+  const GemmLds lds = gemm_lds_layout(WT, XSRC, SPLIT ? 1 : 0, R, nw, NB, K, T);
   float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
   // XSRC_NORM: per wave, the sum of squares of each row over the wave's k range [nw][RT*16]
-  float* ssq = red + (size_t)NRED * nw * RT * NB * 256;
+  float* ssq = (float*)(smem + lds.ssq_off);
+  // this wave's operand staging slot (see gemm_lds_layout)
+  unsigned char* xs = smem + lds.xs_off + (size_t)w * lds.xs_wave;
+  // staged operands: streamed rows (STG_G) of one chunk, [plane][row][CH * KSTEP] bf16; or the
+  // normed raw rows (STG_N) of the wave's whole k range, [row][CH * KSTEP] f32 then the gains
+  constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RT <= 2;
+  constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT == 1 && NCH == 1;
+  constexpr int SP = SPLIT ? 2 : 1;          // operand planes
+  constexpr int LK = CH * Tr::KSTEP;          // k of one chunk
+  constexpr int GU = LK * 2 / 16;             // lanes per staged bf16 row (32 or 16)
+  constexpr int GUPI = 64 / GU;               // staged rows per load instruction
+  constexpr int GIMAX = (16 * RT + GUPI - 1) / GUPI;
+  static_assert(!STG_N || LK * 4 == 1024, "a normed row of one chunk is one wave load");
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues run with T dividing the tile count
@@ -132,21 +191,22 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     const int j = tile_of(it / NCH), c = it % NCH;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      int s, tj;
-      if constexpr (NB == 1) {
-        s = find_seg(p, 16 * j);
-        tj = (16 * j - p.seg[s].col0) >> 4;
+      SegSel sel;
+      if constexpr (EPI == EPI_ARGMAX) {  // one matrix (checked at launch)
+        sel = SegSel{(const unsigned char*)p.seg[0].w, (const unsigned char*)p.seg[0].scales, j};
+      } else if constexpr (NB == 1) {
+        sel = select_seg(p, 16 * j);
       } else {
-        s = nb;
-        tj = j;
+        sel = SegSel{(const unsigned char*)p.seg[nb].w, (const unsigned char*)p.seg[nb].scales, j};
       }
+      const int tj = sel.tj;
       if constexpr (Q4) {
         // one kilobyte of codes and 128 bytes of (scale, bias) per (16-row tile, 128 k)
         const size_t kblocks = (size_t)K / 128;
         const size_t blk0 = ((size_t)w * kw + (size_t)c * CH * Tr::KSTEP) / 128;
         const size_t bo = (size_t)tj * kblocks + blk0;
-        const unsigned char* wr = (const unsigned char*)p.seg[s].w + bo * 1024 + lane * 16;
-        const unsigned char* sr = (const unsigned char*)p.seg[s].scales + bo * 128 + li * 8;
+        const unsigned char* wr = sel.w + bo * 1024 + lane * 16;
+        const unsigned char* sr = sel.sc + bo * 128 + li * 8;
 #pragma unroll
         for (int b = 0; b < CB; ++b) {
           wb[nb][b] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)b * 1024));
@@ -156,13 +216,18 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
         // fragment-major weights: one contiguous kilobyte per (16-row tile, KSTEP) block
         const size_t kblocks = (size_t)K / Tr::KSTEP;
         const size_t blk0 = (size_t)w * (kw / Tr::KSTEP) + (size_t)c * CH;
-        const unsigned char* wr = (const unsigned char*)p.seg[s].w + ((size_t)tj * kblocks + blk0) * 1024 + lane * 16;
+        const unsigned char* wr = sel.w + ((size_t)tj * kblocks + blk0) * 1024 + lane * 16;
 #pragma unroll
         for (int st = 0; st < CH; ++st)
           wb[nb][st] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)st * 1024));
       }
     }
   };
+
+  // Operand rows past R load row R - 1 instead of branching around the load (a divergent
+  // branch makes the compiler wait for every load in flight): MFMA output row r depends on
+  // operand row r alone, and rows past R are never stored.
+  auto xrow = [&](int rt) { return min(rt * 16 + li, R - 1); };
 
   // streamed operand fragments of chunk it (hi and, for pairs, lo planes)
   auto load_x = [&](u32x4_t (&xb)[RT][CH], u32x4_t (&xlb)[SR][CH], int it) {
@@ -171,26 +236,55 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     if constexpr (XSRC == XSRC_GLOBAL) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int r = rt * 16 + li;
-        const size_t xo = (size_t)r * p.ldx * Tr::ELT + kb;
+        const size_t xo = (size_t)xrow(rt) * p.ldx * Tr::ELT + kb;
         const unsigned char* xr = (const unsigned char*)p.x + xo;
 #pragma unroll
-        for (int st = 0; st < CH; ++st) {
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (r < R) v = *(const u32x4_t*)(xr + (size_t)st * Tr::KSTEP * Tr::ELT);
-          xb[rt][st] = v;
-        }
+        for (int st = 0; st < CH; ++st) xb[rt][st] = *(const u32x4_t*)(xr + (size_t)st * Tr::KSTEP * Tr::ELT);
         if constexpr (SPLIT) {
           const unsigned char* xl = (const unsigned char*)p.xlo + xo;
 #pragma unroll
-          for (int st = 0; st < CH; ++st) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (r < R) v = *(const u32x4_t*)(xl + (size_t)st * Tr::KSTEP * Tr::ELT);
-            xlb[rt][st] = v;
-          }
+          for (int st = 0; st < CH; ++st) xlb[rt][st] = *(const u32x4_t*)(xl + (size_t)st * Tr::KSTEP * Tr::ELT);
         }
       }
     }
+  };
+
+  // STG_G: the R rows of each plane for chunk it, GU lanes of 16 bytes per row, rows past
+  // R-1 repeating row R-1 in the last instruction; then stored to the staging slot
+  u32x4_t xc[STG_G ? SP : 1][STG_G ? GIMAX : 1];
+  const int gipp = (R + GUPI - 1) / GUPI;  // load instructions per plane
+  auto load_xc = [&](int it) {
+    if constexpr (STG_G) {
+      const size_t k0 = (size_t)w * kw + (size_t)(it % NCH) * LK;
+      const int piece = lane % GU;
+#pragma unroll
+      for (int pl = 0; pl < SP; ++pl)
+#pragma unroll
+        for (int i = 0; i < GIMAX; ++i)
+          if (i < gipp) {
+            const int r = min(i * GUPI + lane / GU, R - 1);
+            const unsigned char* src = (const unsigned char*)(pl ? p.xlo : p.x);
+            xc[pl][i] = *(const u32x4_t*)(src + ((size_t)r * p.ldx + k0) * 2 + piece * 16);
+          }
+    }
+  };
+  auto stage_xc = [&]() {
+    if constexpr (STG_G) {
+      const int piece = lane % GU;
+#pragma unroll
+      for (int pl = 0; pl < SP; ++pl)
+#pragma unroll
+        for (int i = 0; i < GIMAX; ++i)
+          if (i < gipp) {
+            const int r = min(i * GUPI + lane / GU, R - 1);
+            *(u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + piece * 16) = xc[pl][i];
+          }
+    }
+  };
+  // MFMA fragment (row tile rt, step st) of plane pl from the staged rows
+  auto frag_xs = [&](int rt, int st, int pl) {
+    const int r = min(rt * 16 + li, R - 1);
+    return *(const u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2);
   };
 
   f32x4_t acc[RT][NB];
@@ -213,7 +307,10 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
                      int it) {
     const int c = it % NCH;
     auto xfrag = [&](int rt, int st, u32x4_t& xf, u32x4_t& xl) {
-      if constexpr (XSRC == XSRC_GLOBAL) {
+      if constexpr (STG_G) {
+        xf = frag_xs(rt, st, 0);
+        if constexpr (SPLIT) xl = frag_xs(rt, st, 1);
+      } else if constexpr (XSRC == XSRC_GLOBAL) {
         xf = xb[rt][st];
         if constexpr (SPLIT) xl = xlb[rt][st];
       } else {
@@ -293,17 +390,29 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         u32x4_t xf, xl;
-        if constexpr (XSRC == XSRC_GLOBAL) {
-          xf = xb[rt][st];
-          if constexpr (SPLIT) xl = xlb[rt][st];
-        } else {
-          xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
-          if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
-        }
+        xfrag(rt, st, xf, xl);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           acc[rt][nb] = step_mfma<WT>(xf, wb[nb][st], acc[rt][nb]);
           if constexpr (SPLIT) acc[rt][nb] = step_mfma<WT>(xl, wb[nb][st], acc[rt][nb]);
+        }
+      }
+    }
+  };
+
+  // EPI_RESID: the residual values of the first row tile this wave finishes (row tile w:
+  // all of them when the work-group has at least RT waves), fetched with the operands so
+  // that the epilogue only stores; every output is read and written by one lane
+  static_assert(EPI != EPI_RESID || T == 1, "residual launches own one tile per work-group");
+  float yres[4] = {0.f, 0.f, 0.f, 0.f};
+  auto load_resid = [&]() {
+    if constexpr (EPI == EPI_RESID) {
+      if (w < RT) {
+        const int col = 16 * tile_of(0) + li;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = min(w * 16 + 4 * lg + q, R - 1);
+          yres[q] = ((const float*)p.y)[(size_t)r * p.ldy + col];
         }
       }
     }
@@ -361,7 +470,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           if constexpr (EPI == EPI_STORE) {
             ((float*)p.y)[o] = v[0][q];
           } else if constexpr (EPI == EPI_RESID) {
-            ((float*)p.y)[o] += v[0][q];
+            ((float*)p.y)[o] = (rt == w ? yres[q] : ((const float*)p.y)[o]) + v[0][q];
           } else if constexpr (EPI == EPI_SWIGLU) {
             const float g = v[0][q], u = v[NB - 1][q];
             op_st<SPLIT>(p.y, p.ylo, o, g / (1.0f + expf(-g)) * u);
@@ -372,27 +481,87 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     if constexpr (NRED == 1) __syncthreads();
   };
 
-  // ---- issue the first weight chunk before staging activations -------------------------
-  // weights run PDW - 1 chunks ahead (q4 chunks carry a quarter of the bytes, so more
-  // of them stay in flight); streamed operands, from L2, one chunk ahead
-  constexpr int PDW = Q4 ? 4 : 2;
+  // ---- issue order: operands, the weight stream, then operand arithmetic ---------------
+  // The memory counter retires loads in issue order, so a value can be used only once
+  // every load issued before it has arrived. The small L2-resident operands therefore go
+  // first and the weights right behind them, before any arithmetic: the normed operands
+  // are ready when their own loads land, and every weight chunk the register budget holds
+  // (all of them for the layer GEMMs) is in flight from the start.
+  constexpr int AHEAD = gemm_chunks_ahead<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>();
+  constexpr int PDW = AHEAD + 1;
   u32x4_t wbuf[PDW][NB][CH];
   u32x2_t sbuf[PDW][NB][CB];
-  u32x4_t xbuf[2][RT][CH];
+  u32x4_t xbuf[2][RT][CH];  // streamed fragments (not STG_G)
   u32x4_t xlbuf[2][SR][CH];
-#pragma unroll
-  for (int i = 0; i < PDW - 1; ++i)
-    if (i < NIT) load_w(wbuf[i], sbuf[i], i);
-  if constexpr (XSRC == XSRC_GLOBAL) load_x(xbuf[0], xlbuf[0], 0);
 
-  if constexpr (XSRC != XSRC_GLOBAL) {
-    // RMSNorm operands: the row scale rsqrt(mean(x^2) + eps) is one number per row, so the
-    // operand is x * g and the scale multiplies the finished dot products (finalize); the
-    // sums of squares come from the same loads, per lane, then per wave, then across waves
-    float ssl[RT];
+  // normed operands: raw f32 rows and gains. A single-chunk launch loads them ahead of the
+  // weights (NORM_FIRST). With more chunks, each value is loaded behind the weights and
+  // formed at once, under a row guard: without the branch the scheduler hoists the loads of
+  // every chunk and holds them beside the formed pairs.
+  constexpr int XRAW = BF ? 2 : 1;  // 16-byte f32 loads per (row tile, step)
+  constexpr bool NORM_FIRST = XSRC == XSRC_NORM && XR == 1;
+  f32x4_t xa[STG_N ? 1 : RT][CH][XRAW];
+  u32x4_t ga[CH];
+  // STG_N: raw row i of the wave's k range in load i (64 lanes x 4 f32), the gains in the last
+  u32x4_t xn[STG_N ? 17 : 1];
+  auto kof = [&](int c, int st) { return w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL; };
+  auto raw_ld = [&](int c, int rt, int st, int h) {
+    return *(const f32x4_t*)((const float*)p.x + (size_t)xrow(rt) * p.ldx + kof(c, st) + 4 * h);
+  };
+  auto gain_ld = [&](int c, int st) {
+    if constexpr (BF) return *(const u32x4_t*)((const uint16_t*)p.gain + kof(c, st));
+    else return *(const u32x4_t*)((const float*)p.gain + kof(c, st));
+  };
+  // one normed operand fragment: sums of squares from the raw values, and x * g as a hi/lo
+  // bf16 pair (bf16 weights) or f32
+  auto form = [&](const f32x4_t a0, const f32x4_t a1, const u32x4_t gb, float& ss, u32x4_t& f, u32x4_t& fl) {
+    if constexpr (BF) {
+      const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ssl[rt] = 0.f;
-    // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
+        uint32_t hp, lp;
+        split2_bf16(v[2 * e2] * g0, v[2 * e2 + 1] * g1, hp, lp);
+        f[e2] = hp;
+        fl[e2] = lp;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss = fmaf(a0[e], a0[e], ss);
+        f[e] = __float_as_uint(a0[e] * __uint_as_float(gb[e]));
+      }
+    }
+  };
+  if constexpr (STG_G) {
+    load_xc(0);
+  } else if constexpr (XSRC == XSRC_GLOBAL) {
+    load_x(xbuf[0], xlbuf[0], 0);
+  } else if constexpr (STG_N) {
+    const size_t k0 = (size_t)w * kw;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < R) xn[i] = *(const u32x4_t*)((const float*)p.x + (size_t)i * p.ldx + k0 + lane * 4);
+    xn[16] = *(const u32x4_t*)((const uint16_t*)p.gain + k0 + (lane & 31) * 8);
+  } else if constexpr (NORM_FIRST) {
+#pragma unroll
+    for (int st = 0; st < CH; ++st) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int h = 0; h < XRAW; ++h) xa[rt][st][h] = raw_ld(0, rt, st, h);
+      ga[st] = gain_ld(0, st);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) load_w(wbuf[i], sbuf[i], i);
+  load_resid();
+  if constexpr (XSRC == XSRC_LDS) {
+    // LDS-source planes (the argmax rows): every chunk into the operand fragments, behind
+    // the first weight chunk and only for the real rows (measured faster for the
+    // vocabulary stream, where each work-group is one of many on its CU)
 #pragma unroll
     for (int c = 0; c < XR; ++c)
 #pragma unroll
@@ -400,78 +569,90 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 #pragma unroll
         for (int st = 0; st < CH; ++st) {
           const int r = rt * 16 + li;
-          const int k = w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;
-          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
+          const size_t xo = ((size_t)r * p.ldx + kof(c, st)) * Tr::ELT;
+          u32x4_t v = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
           if (r < R) {
-            if constexpr (XSRC == XSRC_LDS) {
-              const size_t xo = ((size_t)r * p.ldx + k) * Tr::ELT;
-              f = *(const u32x4_t*)((const unsigned char*)p.x + xo);
-              if constexpr (SPLIT) fl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
-            } else {
-              const float* src = (const float*)p.x + (size_t)r * p.ldx + k;
-              if constexpr (BF) {
-                const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
-                const u32x4_t gb = *(const u32x4_t*)((const uint16_t*)p.gain + k);
-                float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            v = *(const u32x4_t*)((const unsigned char*)p.x + xo);
+            if constexpr (SPLIT) vl = *(const u32x4_t*)((const unsigned char*)p.xlo + xo);
+          }
+          xr[c][rt][st] = v;
+          if constexpr (SPLIT) xrl[c][rt][st] = vl;
+        }
+  }
+
+  if constexpr (XSRC == XSRC_NORM) {
+    // RMSNorm operands: the row scale rsqrt(mean(x^2) + eps) is one number per row, so the
+    // operand is x * g and the scale multiplies the finished dot products (finalize); the
+    // sums of squares come from the same loads, per lane, then per wave, then across waves
+    float ssl[RT];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ssl[rt] = fmaf(v[e], v[e], ssl[rt]);
+    for (int rt = 0; rt < RT; ++rt) ssl[rt] = 0.f;
+    if constexpr (STG_N) {
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                  const float g0 = __uint_as_float(gb[e2] << 16), g1 = __uint_as_float(gb[e2] & 0xffff0000u);
-                  uint32_t hp, lp;
-                  split2_bf16(v[2 * e2] * g0, v[2 * e2 + 1] * g1, hp, lp);
-                  f[e2] = hp;
-                  fl[e2] = lp;
-                }
-              } else {
-                const float4 a0 = *(const float4*)src;
-                const float4 g = *(const float4*)((const float*)p.gain + k);
-                ssl[rt] = fmaf(a0.x, a0.x, ssl[rt]);
-                ssl[rt] = fmaf(a0.y, a0.y, ssl[rt]);
-                ssl[rt] = fmaf(a0.z, a0.z, ssl[rt]);
-                ssl[rt] = fmaf(a0.w, a0.w, ssl[rt]);
-                f[0] = __float_as_uint(a0.x * g.x);
-                f[1] = __float_as_uint(a0.y * g.y);
-                f[2] = __float_as_uint(a0.z * g.z);
-                f[3] = __float_as_uint(a0.w * g.w);
-              }
-            }
+      for (int i = 0; i < 16; ++i)
+        if (i < R) *(u32x4_t*)(xs + (size_t)i * lds.row_bytes + lane * 16) = xn[i];
+      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (lane & 31) * 16) = xn[16];
+    }
+    // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
+#pragma unroll
+    for (int c = 0; c < XR; ++c) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int st = 0; st < CH; ++st) {
+          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
+          if constexpr (STG_N) {
+            const unsigned char* xrw = xs + (size_t)min(li, R - 1) * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 4;
+            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2);
+            form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
+          } else if constexpr (NORM_FIRST) {
+            form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
+          } else if (rt * 16 + li < R) {
+            const float* src = (const float*)p.x + (size_t)(rt * 16 + li) * p.ldx + kof(c, st);
+            form(*(const f32x4_t*)src, *(const f32x4_t*)(src + 4 * (XRAW - 1)), gain_ld(c, st), ssl[rt], f, fl);
           }
           xr[c][rt][st] = f;
           if constexpr (SPLIT) xrl[c][rt][st] = fl;
         }
-    if constexpr (XSRC == XSRC_NORM) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float v = ssl[rt];
-        v += __shfl_xor(v, 16, 64);  // the four lanes of row li, in a fixed order
-        v += __shfl_xor(v, 32, 64);
-        if (lg == 0) ssq[w * RT * 16 + rt * 16 + li] = v;
-      }
     }
-    if constexpr (Q4) {
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int st = 2 * gi + tt;
-            a = mfma_bf16(xr[st / CH][rt][st % CH], ones, a);
-            if constexpr (SPLIT) a = mfma_bf16(xrl[st / CH][rt][st % CH], ones, a);
-          }
-          xg[gi][rt] = a;
-        }
+    for (int rt = 0; rt < RT; ++rt) {
+      float v = ssl[rt];
+      v += __shfl_xor(v, 16, 64);  // the four lanes of row li, in a fixed order
+      v += __shfl_xor(v, 32, 64);
+      if (lg == 0) ssq[w * RT * 16 + rt * 16 + li] = v;
     }
   }
+  if constexpr (Q4 && XSRC != XSRC_GLOBAL) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int st = 2 * gi + tt;
+          a = mfma_bf16(xr[st / CH][rt][st % CH], ones, a);
+          if constexpr (SPLIT) a = mfma_bf16(xrl[st / CH][rt][st % CH], ones, a);
+        }
+        xg[gi][rt] = a;
+      }
+  }
+  // the normed staging slots share their bytes with the reduction buffers
+  if constexpr (STG_N) __syncthreads();
 
   // ---- straight-line (tile, chunk) pipeline ---------------------------------------------
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     if (it + PDW - 1 < NIT) load_w(wbuf[(it + PDW - 1) % PDW], sbuf[(it + PDW - 1) % PDW], it + PDW - 1);
-    if constexpr (XSRC == XSRC_GLOBAL)
+    if constexpr (STG_G) {
+      // this chunk's rows into the staging slot, then the next chunk's loads into the
+      // registers they free (behind the weights in flight)
+      stage_xc();
+      if (it + 1 < NIT) load_xc(it + 1);
+    } else if constexpr (XSRC == XSRC_GLOBAL) {
       if (it + 1 < NIT) load_x(xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
+    }
     compute(wbuf[it % PDW], sbuf[it % PDW], xbuf[it & 1], xlbuf[it & 1], it);
     if (it % NCH == NCH - 1) finalize(it / NCH);
   }
@@ -490,7 +671,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 // ---- instantiation tables -----------------------------------------------------------------
 template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(WT, XSRC, p.R, p.waves, NB, p.K, T);
+  const size_t lds = gemm_lds_layout(WT, XSRC, SPLIT ? 1 : 0, p.R, p.waves, NB, p.K, T).total;
   auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>;
   static size_t attr_lds = 64 * 1024;  // dynamic LDS this kernel is cleared for
   if (lds > attr_lds) {

@@ -64,18 +64,54 @@ struct GemmPlan {
 };
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc);
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
-// LDS of a GEMM work-group, first part: the cross-wave reduction buffers (double-buffered
-// across tiles when a work-group owns several) and the per-wave row sums of squares of the
-// RMSNorm operands (XSRC_NORM).
-__host__ __device__ inline size_t gemm_lds_red_bytes(int xsrc, int R, int waves, int rows_pad, int nb,
-                                                     int tiles_per_wg) {
-  (void)R;
-  size_t b = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * (rows_pad / 16) * nb * 1024;
-  if (xsrc == XSRC_NORM) b += (size_t)waves * rows_pad * 4;
-  return (b + 15) & ~(size_t)15;
+// LDS of a GEMM work-group: the cross-wave reduction buffers (double-buffered across tiles
+// when a work-group owns several), the per-wave row sums of squares of the RMSNorm operands
+// (XSRC_NORM), and, for bf16 and 4-bit weights, a per-wave slot that stages the operand
+// rows of one chunk of the wave's k range (XSRC_GLOBAL with at most two row tiles: R rows
+// of each plane; XSRC_NORM with one row tile and one chunk: R raw f32 rows and the gains).
+// Staging loads only the R real rows with every lane busy, where the MFMA fragments would
+// load 16 rows per row tile; the fragments are then read from LDS. The normed slot is dead
+// once the operand pairs are formed and shares its bytes with the reduction buffers.
+struct GemmLds {
+  int stage;       // 0 none, 1 streamed rows, 2 normed rows
+  int row_bytes;   // staged bytes per row and plane, padded by 16 against bank conflicts
+  size_t ssq_off;  // byte offsets in the work-group's LDS
+  size_t xs_off;
+  size_t xs_wave;  // staged bytes per wave
+  size_t total;
+};
+__host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, int R, int waves, int nb, int K,
+                                                   int tiles_per_wg) {
+  const int rt = (R + 15) / 16, rows_pad = 16 * rt;
+  const int ch = chunk_steps(rt), kstep = wt == WT_F32 ? 16 : 32;
+  const int nch = K / (waves * ch * kstep);
+  const size_t red = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * rt * nb * 1024;
+  const size_t ssq = xsrc == XSRC_NORM ? (size_t)waves * rows_pad * 4 : 0;
+  GemmLds l{};
+  if (wt != WT_F32 && xsrc == XSRC_GLOBAL && rt <= 2) {
+    l.stage = 1;
+    l.row_bytes = ch * kstep * 2 + 16;
+    l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
+  } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt == 1 && nch == 1) {
+    l.stage = 2;
+    l.row_bytes = ch * kstep * 4 + 16;
+    l.xs_wave = (size_t)R * l.row_bytes + (size_t)ch * kstep * 2;
+  }
+  if (l.stage == 2) {
+    l.xs_off = 0;
+    const size_t xs = (size_t)waves * l.xs_wave;
+    l.ssq_off = ((xs > red ? xs : red) + 15) & ~(size_t)15;
+    l.total = l.ssq_off + ssq;
+  } else {
+    l.ssq_off = red;
+    l.xs_off = (red + ssq + 15) & ~(size_t)15;
+    l.total = l.xs_off + (size_t)waves * l.xs_wave;
+  }
+  l.total = (l.total + 15) & ~(size_t)15;
+  return l;
 }
-// Whole LDS of a GEMM work-group (today the part above for every weight type).
-size_t gemm_lds_bytes(int wt, int xsrc, int R, int waves, int nb, int K, int tiles_per_wg);
+// Whole LDS of a GEMM work-group.
+size_t gemm_lds_bytes(int wt, int xsrc, int split, int R, int waves, int nb, int K, int tiles_per_wg);
 
 // ---- small kernels --------------------------------------------------------------------
 struct AttnShape {
