@@ -19,7 +19,8 @@ DFLASH_F32, DFLASH_BF16, DFLASH_Q4G64 = 0, 1, 2
 _DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
 
 EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
-           "dflash_draft_block", "dflash_lm_head_argmax", "dflash_verify_greedy", "dflash_cache_state",
+           "dflash_draft_block", "dflash_lm_head_argmax", "dflash_time_next_argmax", "dflash_verify_greedy",
+           "dflash_cache_state",
            "dflash_cache_read", "dflash_last_error", "dflash_status_string")
 
 
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
         "dflash_cache_trim": (i32, [vp, i32]),
         "dflash_draft_block": (i32, [vp, i32, i32, vp, vp, vp]),
         "dflash_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
+        "dflash_time_next_argmax": (i32, [vp, vp, vp]),
         "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
         "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
         "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
@@ -222,6 +224,17 @@ class Drafter:
         self._dev(out, torch.int32)
         _check(lib().dflash_lm_head_argmax(self.ctx, _ptr(rows), n, _ptr(out), _stream(stream)), self.ctx)
         return out
+
+    def time_next_argmax(self, start: "torch.cuda.Event", end: "torch.cuda.Event") -> None:
+        """Have the next lm_head_argmax call record `start` and `end` (timing-enabled
+        torch.cuda.Event) right around its argmax kernel, so start.elapsed_time(end) is that
+        kernel's duration."""
+        handles = []
+        for ev in (start, end):
+            if not ev.cuda_event:
+                ev.record()  # torch creates the underlying event on its first record
+            handles.append(ctypes.c_void_p(ev.cuda_event))
+        _check(lib().dflash_time_next_argmax(self.ctx, *handles), self.ctx)
 
     def verify_greedy(self, draft: torch.Tensor, target: torch.Tensor, block: int,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

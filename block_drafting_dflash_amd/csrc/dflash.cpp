@@ -66,6 +66,10 @@ struct dflash_ctx {
   int cus = 256;        // compute units of the device the context was created on
   int64_t e = 0;        // committed context end (absolute position)
   int64_t pending = 0;  // rows appended since the last trim
+  // events around the first argmax GEMM launch of the next dflash_lm_head_argmax call
+  // (dflash_time_next_argmax); `active` while that call runs
+  hipEvent_t tev_start = nullptr, tev_end = nullptr;
+  bool tev_active = false;
   char err[512] = {0};
 };
 
@@ -112,12 +116,18 @@ bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
 }
 
 // Tiles per work-group of an argmax launch: small work-groups keep the dispatcher
-// balancing the vocabulary stream; with many rows, more tiles per work-group bound how
-// often the operand rows are re-read from L2.
-int argmax_tiles_per_wg(int ntiles, int rows) {
+// balancing the vocabulary stream; with more rows, more tiles per work-group bound how
+// often the operand rows are re-read from L2. Measured over a vocabulary-sized head
+// (202048 x 2048): bf16 single-plane rows run fastest at two tiles (four past 16 rows),
+// bf16 hi/lo pairs, with twice the operand loads and products, at four (eight past 8
+// rows); 4-bit heads, bound by dequantisation rather than bytes, at eight for hi/lo pairs
+// and four (eight past 16 rows) for single-plane rows.
+int argmax_tiles_per_wg(int wt, int split, int ntiles, int rows) {
   if (ntiles < 1024) return 1;
   if (ntiles < 8192) return 2;
-  return rows > 8 ? 16 : 4;
+  if (wt == WT_Q4) return split ? 8 : (rows > 16 ? 8 : 4);
+  if (!split) return rows > 16 ? 4 : 2;
+  return rows > 8 ? 8 : 4;
 }
 
 dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
@@ -360,14 +370,18 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     }
     if (gc.epi == EPI_ARGMAX) {
       p.part = (unsigned long long*)(ctx->ws + ctx->lay.argmax_part);
-      pl.tiles_per_wg = argmax_tiles_per_wg(p.ntiles, rc);
+      pl.tiles_per_wg = argmax_tiles_per_wg(wt, gc.split, p.ntiles, rc);
       pl.grid = (p.ntiles + pl.tiles_per_wg - 1) / pl.tiles_per_wg;
     } else {
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
       p.ylo = gc.ylo ? (unsigned char*)gc.ylo + (size_t)r0 * gc.ldy * y_elt : nullptr;
       p.ldy = gc.ldy;
     }
+    const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
+    if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
     const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, pl, p, st);
+    if (timed && le == hipSuccess && hipEventRecord(ctx->tev_end, st) != hipSuccess)
+      return dev(ctx, hipGetLastError(), "timing event");
     if (le != hipSuccess)
       return fail(ctx, DFLASH_E_DEVICE,
                   "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, ch %d x %d, tiles/wg %d, grid %d): %s",
@@ -671,7 +685,19 @@ dflash_status dflash_lm_head_argmax(dflash_ctx* ctx, const void* rows, int32_t n
   const dflash_config& c = ctx->cfg.c;
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, c.hidden, rows, c.hidden, nullptr, nullptr, 0,
               d_idx};
-  return run_gemm(ctx, lm, n, (hipStream_t)stream);
+  ctx->tev_active = ctx->tev_start != nullptr;
+  const dflash_status s = run_gemm(ctx, lm, n, (hipStream_t)stream);
+  ctx->tev_active = false;
+  ctx->tev_start = ctx->tev_end = nullptr;
+  return s;
+}
+
+dflash_status dflash_time_next_argmax(dflash_ctx* ctx, void* start, void* end) {
+  if (!ctx) return DFLASH_E_ARG;
+  if ((start == nullptr) != (end == nullptr)) return fail(ctx, DFLASH_E_ARG, "give both timing events or neither");
+  ctx->tev_start = (hipEvent_t)start;
+  ctx->tev_end = (hipEvent_t)end;
+  return DFLASH_OK;
 }
 
 dflash_status dflash_verify_greedy(dflash_ctx* ctx, const int32_t* d_draft, const int32_t* d_target, int32_t block,

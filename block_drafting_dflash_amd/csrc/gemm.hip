@@ -16,7 +16,8 @@ size_t gemm_lds_bytes(int wt, int xsrc, int split, int R, int waves, int nb, int
 bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc) {
   if (epi == EPI_ARGMAX)
     return xsrc == XSRC_LDS && pl.ch == 8 && (pl.nch == 1 || pl.nch == 2) &&
-           (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 16);
+           (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2 || pl.tiles_per_wg == 4 || pl.tiles_per_wg == 8 ||
+            pl.tiles_per_wg == 16);
   if (xsrc != XSRC_GLOBAL)
     return pl.ch == 8 && (pl.tiles_per_wg == 1 || pl.tiles_per_wg == 2) && (pl.nch == 1 || pl.nch == 2);
   return pl.ch == 8 && pl.tiles_per_wg == 1 &&

@@ -115,13 +115,16 @@ template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int ge
 // fragments; staged (LDS-source) operands every chunk; normed operands their raw rows while
 // the pairs are formed; and about 48 registers go to accumulators, addresses and sums. The
 // vocabulary argmax keeps shallow look-ahead: it runs thousands of work-groups, several per
-// CU, which keep the stream busy between them. f32 weights (the exact-arithmetic shapes)
+// CU, which keep the stream busy between them (three chunks for 4-bit single-plane rows,
+// whose chunks carry a quarter of the bytes). f32 weights (the exact-arithmetic shapes)
 // keep one chunk ahead.
 template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 constexpr int gemm_chunks_ahead() {
   constexpr bool Q4 = WT == WT_Q4, BF = WT != WT_F32;
   constexpr int nit = T * NCH;
-  if (EPI == EPI_ARGMAX || !BF) return nit < (Q4 ? 3 : 1) ? nit : (Q4 ? 3 : 1);
+  // 4-bit argmax over hi/lo pairs: the operand pairs and group sums leave no room (measured)
+  constexpr int argmax_ahead = Q4 && !SPLIT ? 3 : 1;
+  if (EPI == EPI_ARGMAX || !BF) return nit < argmax_ahead ? nit : argmax_ahead;
   constexpr int budget = 512 / gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>();
   constexpr int planes = SPLIT ? 2 : 1;
   constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
@@ -740,6 +743,7 @@ static hipError_t argmax_by_t(const GemmPlan& pl, const GemmParams& p, hipStream
     case 1: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 1, NCH, 8, SPLIT>(p, pl.grid, s);
     case 2: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 2, NCH, 8, SPLIT>(p, pl.grid, s);
     case 4: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 4, NCH, 8, SPLIT>(p, pl.grid, s);
+    case 8: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 8, NCH, 8, SPLIT>(p, pl.grid, s);
     case 16: return by_rt<WT, 1, EPI_ARGMAX, XSRC, 16, NCH, 8, SPLIT>(p, pl.grid, s);
     default: return hipErrorInvalidValue;
   }

@@ -175,6 +175,15 @@ dflash_status dflash_draft_block(dflash_ctx *ctx, int32_t anchor, int32_t block,
  * softcap). 1 <= n <= 4096. */
 dflash_status dflash_lm_head_argmax(dflash_ctx *ctx, const void *rows, int32_t n, int32_t *d_idx, void *stream);
 
+/* Kernel timing of the vocabulary argmax (profiling; no counterpart on the pages). The next
+ * dflash_lm_head_argmax call on ctx records `start` on its stream right before its first
+ * argmax GEMM launch (rows 0..31) and `end` right after it, before the per-row reduction
+ * of the work-group maxima, so the elapsed time between the two is that one kernel's
+ * duration; the call then forgets both. start and end are hipEvent_t handles created by
+ * the caller with timing enabled and owned by it. Passing two NULLs cancels a pending
+ * request. Errors: NULL ctx, or exactly one NULL event (DFLASH_E_ARG). */
+dflash_status dflash_time_next_argmax(dflash_ctx *ctx, void *start, void *end);
+
 /*
  * Greedy exact-match verify of one block (lablup/mlxcel #1751, Implementation Review
  * Summary: greedy exact-match verify rule, verify width = block + 1). d_draft: device

@@ -1,4 +1,6 @@
 """GPU parity: the HIP path through the C-ABI against the CPU oracle, element by element."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -167,3 +169,28 @@ def test_q4_lm_head_argmax_is_width_invariant(micro_q4_w):
     for w in (1, 5, 16, 17):
         part = torch.cat([g.lm_head_argmax(rows[i:i + w].contiguous()).cpu() for i in range(0, 40, w)])
         assert torch.equal(part, full), w
+
+
+def test_argmax_timing_hook(micro_bf16_w):
+    """dflash_time_next_argmax: the events bracket the argmax kernel of the next lm_head call
+    only (positive, and no longer than the whole call), leave its result unchanged, apply
+    to one call, and a single NULL event is rejected."""
+    sh = MICRO_BF16
+    g = binding.Drafter(sh, binding.to_device(sh, micro_bf16_w), max_block=4)
+    rows = torch.from_numpy(np.stack([synth.verify_hidden(sh, 5, r) for r in range(3)])).to(torch.bfloat16).cuda()
+    plain = g.lm_head_argmax(rows[0]).cpu()
+    stream = torch.cuda.current_stream()
+    k0, k1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    g.time_next_argmax(k0, k1)
+    c0.record(stream)
+    timed = g.lm_head_argmax(rows[0]).cpu()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, timed)
+    kernel_ms, call_ms = k0.elapsed_time(k1), c0.elapsed_time(c1)
+    assert 0.0 < kernel_ms <= call_ms
+    # the request is spent: the next call records nothing new
+    g.lm_head_argmax(rows[1])
+    torch.cuda.synchronize()
+    assert k0.elapsed_time(k1) == kernel_ms
+    assert binding.lib().dflash_time_next_argmax(g.ctx, ctypes.c_void_p(k0.cuda_event), None) == 1  # DFLASH_E_ARG
