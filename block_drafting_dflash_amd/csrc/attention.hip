@@ -12,11 +12,14 @@
 // Cs and the phase multiples of 8 (AttnShape cap / phase). Per layer, K is stored as
 // [kv head][slot][head dim] and V transposed, [kv head][head dim][slot], so that both MFMA
 // operands of the attention read consecutive elements: a key row for the scores, a run of
-// eight consecutive keys at one dim for the output. The draft writes the block's own k/v
-// into the slots of positions e..e+R-1 (past the committed window; the append of the
-// verified rows overwrites them), so all keys of a query, positions max(0, e-W)..e+R-1,
-// come from the ring. The ring is zeroed when the context is created, so every slot holds
-// finite values and keys outside a query's window can be read and given weight exactly 0.
+// eight consecutive keys at one dim for the output. The keys of a query are positions
+// max(0, e-W)..e+R-1: the committed context from the ring, then the block's own. The bf16
+// MFMA kernel forms the block's own keys and values itself from the raw projections and
+// uses them in place of the ring slots of positions e..e+R-1, which lie past the committed
+// window; the other paths (f32 shapes, long blocks) write them into those slots first (the
+// append of the verified rows overwrites them either way). The ring is zeroed when the
+// context is created, so every slot holds finite values and keys outside a query's window
+// can be read and given weight exactly 0.
 //
 // Work split: keys are cut into chunks of 64 absolute positions (aligned to multiples of
 // 64, so the cut never depends on the phase and every 8-key run is one aligned 16-byte
@@ -231,29 +234,49 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
 }
 
 // ---- attention on MFMA (bf16 operands): one work-group per (64-key chunk, kv head) ------
-// Each wave takes query tiles w, w+4, ... and reads its operands straight from the ring (no
-// LDS): scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16 key rows, B = 16 queries), then
-// O^T = V^T P^T (A = 16 dims x 32 keys from the transposed V, B = P). The key rows of the
-// two score tiles of each 32-key half are ordered so that lane (li, lg) ends up with keys
-// 8*lg .. 8*lg+7 of the half for query li, exactly its B operand of the output product,
-// and the matching V^T run is one aligned 16-byte load. Q (an f32 activation) and P (in
-// [0, 1]) enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16
-// already, products are exact and sums f32.
+// Each wave takes query tiles w, w+4, ... and reads its operands straight from the ring:
+// scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16 key rows, B = 16 queries), then O^T = V^T
+// P^T (A = 16 dims x 32 keys from the transposed V, B = P). The key rows of the two score
+// tiles of each 32-key half are ordered so that lane (li, lg) ends up with keys 8*lg ..
+// 8*lg+7 of the half for query li, exactly its B operand of the output product, and the
+// matching V^T run is one aligned 16-byte load. Q (an f32 activation) and P (in [0, 1])
+// enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16 already,
+// products are exact and sums f32.
+//
+// The kernel also does what the prep kernel does for the block rows. A query
+// fragment holds dims 32s + 8lg .. + 8 of one query, so the lane's four lanes lg together
+// hold the whole head (the RMSNorm sum is two shuffles) and each rotate-half partner, dim +
+// hd/2, sits in the same lane (s + DS/2). The block's own keys and values, at positions
+// e..e+R-1, are formed by the work-groups whose chunk holds them, one wave per position as
+// in the prep kernel, into LDS laid out like the chunk (keys by position, values by dim),
+// and replace the ring's values for those positions after the ring loads were issued (the
+// ring slots past the committed window are not written).
 template <int HD>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
-                                                        const uint16_t* __restrict__ qb, const uint16_t* __restrict__ qlo,
-                                                        int R, int64_t e, int nchunks, float* __restrict__ part) {
+                                                        const float* __restrict__ qkv, const uint16_t* __restrict__ qnorm,
+                                                        const uint16_t* __restrict__ knorm,
+                                                        const float2* __restrict__ rope, int R, int64_t e, int nchunks,
+                                                        float* __restrict__ part) {
   constexpr int KC = ATTN_CHUNK;  // 64 positions = two halves of 32
-  constexpr int DS = HD / 32, DT = HD / 16;
+  constexpr int DS = HD / 32, DT = HD / 16, HALF = HD / 2;
+  constexpr int KSTR = HD + 8;   // staged key row stride (elements)
+  constexpr int VSTR = KC + 8;   // staged V^T row stride (elements)
   static_assert(KC == 64, "two 32-key halves per work-group");
+  // the chunk's block keys [chunk position][KSTR] and values transposed [dim][VSTR]
+  __shared__ __align__(16) uint16_t kst[KC * KSTR];
+  __shared__ __align__(16) uint16_t vst[HD * VSTR];
   const int g = blockIdx.y, c = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int G = a.nq / a.nkv, NQ = R * G, nqt = (NQ + 15) / 16;
-  if (w >= nqt) return;  // no barrier below: an idle wave may leave
+  const bool active = w < nqt;  // waves past the last query tile only help staging
   const int64_t lo = attn_lo(a, e), hi = e + R;
   const int64_t p0 = (lo / KC + c) * KC;
   const int C = a.cap;
+  const size_t ldq = (size_t)(a.nq + 2 * a.nkv) * HD;  // raw projection row
+  // block positions of this chunk: b0 .. b1-1 (an empty range for most chunks)
+  const int64_t b0 = p0 > e ? p0 : e, b1 = p0 + KC < hi ? p0 + KC : hi;
+  const bool blk = b0 < b1;
   const uint16_t* Kp = ring_layer + (size_t)g * C * HD;
   const uint16_t* VTp = ring_layer + (size_t)(a.nkv + g) * HD * C;
   // slot of the chunk's first position: a multiple of 8 (p0, phase and Cs are), so the
@@ -261,23 +284,86 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   const int s0 = (int)ring_slot(a, p0);
   auto slot_at = [&](int kk) { const int sl = s0 + kk; return sl >= C ? sl - C : sl; };
 
-  // ---- K rows: half h, tile tb, row li <-> position p0 + 32h + 8*(li/4) + 4*tb + li%4 -----
+  // ---- ring operands first (their latency covers the block staging below) ---------------
+  // K rows: half h, tile tb, row li <-> position p0 + 32h + 8*(li/4) + 4*tb + li%4
   u32x4_t kf[2][2][DS];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const uint16_t* row = Kp + (size_t)slot_at(32 * h + 8 * (li >> 2) + 4 * tb + (li & 3)) * HD;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
-    }
-  // ---- V^T runs: half h, dim tile dt: dim dt*16 + li, positions p0 + 32h + 8*lg .. + 8 ----
+  // V^T runs: half h, dim tile dt: dim dt*16 + li, positions p0 + 32h + 8*lg .. + 8
   u32x4_t vf[2][DT];
+  if (active) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int sl = slot_at(32 * h + 8 * lg);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vf[h][dt] = *(const u32x4_t*)(VTp + (size_t)(dt * 16 + li) * C + sl);
+      for (int tb = 0; tb < 2; ++tb) {
+        const uint16_t* row = Kp + (size_t)slot_at(32 * h + 8 * (li >> 2) + 4 * tb + (li & 3)) * HD;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sl = slot_at(32 * h + 8 * lg);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vf[h][dt] = *(const u32x4_t*)(VTp + (size_t)(dt * 16 + li) * C + sl);
+    }
+  }
+
+  if (blk) {
+    // the block's own keys and values of this chunk, one wave per position as in the prep
+    // kernel: k RMSNorm, gain and RoPE, then bf16 (the ring's dtype); v cast to bf16
+    for (int64_t p = b0 + w; p < b1; p += 4) {
+      const int r = (int)(p - e), i = (int)(p - p0);
+      const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
+      const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
+      const bool act = lane < HALF;
+      float x1 = act ? kr[lane] : 0.f, x2 = act ? kr[lane + HALF] : 0.f;
+      const float ss = wave_sum(x1 * x1 + x2 * x2);
+      const float sc = rsqrtf(ss / (float)HD + a.eps);
+      if (act) {
+        x1 = x1 * sc * bf2f(knorm[lane]);
+        x2 = x2 * sc * bf2f(knorm[lane + HALF]);
+        const float2 cs = rope[(size_t)r * HALF + lane];
+        kst[i * KSTR + lane] = f2bf(x1 * cs.x - x2 * cs.y);
+        kst[i * KSTR + lane + HALF] = f2bf(x2 * cs.x + x1 * cs.y);
+        vst[lane * VSTR + i] = f2bf(vr[lane]);
+        vst[(lane + HALF) * VSTR + i] = f2bf(vr[lane + HALF]);
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;  // no barrier below: an idle wave may leave
+
+  if (blk) {
+    // replace the ring's values at the block positions
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int kk = 32 * h + 8 * (li >> 2) + 4 * tb + (li & 3);
+        const int64_t p = p0 + kk;
+        const bool inb = p >= b0 && p < b1;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const u32x4_t v = *(const u32x4_t*)(kst + kk * KSTR + 32 * s + 8 * lg);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) kf[h][tb][s][t] = inb ? v[t] : kf[h][tb][s][t];
+        }
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 32 * h + 8 * lg;
+      // which of the run's 8 positions are block positions: one mask per 16-bit half
+      uint32_t m[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t pa = p0 + kk + 2 * t, pb = pa + 1;
+        m[t] = ((pa >= b0 && pa < b1) ? 0x0000ffffu : 0u) | ((pb >= b0 && pb < b1) ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4_t v = *(const u32x4_t*)(vst + (dt * 16 + li) * VSTR + kk);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vf[h][dt][t] = (v[t] & m[t]) | (vf[h][dt][t] & ~m[t]);
+      }
+    }
   }
 
   const float scale = 1.0f / sqrtf((float)HD);
@@ -287,11 +373,55 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
     const int r = qok ? qv / G : 0, hh = qv - r * G;
     const int64_t qpos = e + r;
     u32x4_t qf[DS], qfl[DS];
-    const size_t qo = ((size_t)r * a.nq + (size_t)g * G + hh) * HD;
+    {
+      // raw q of (row r, head g*G + hh): RMSNorm over the head, gain, RoPE, hi/lo pairs
+      const float* src = qkv + (size_t)r * ldq + (size_t)(g * G + (qok ? hh : 0)) * HD;
+      float x[DS][8];
+      float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      qf[s] = *(const u32x4_t*)(qb + qo + 32 * s + 8 * lg);
-      qfl[s] = *(const u32x4_t*)(qlo + qo + 32 * s + 8 * lg);
+      for (int s = 0; s < DS; ++s) {
+        const float4 a0 = *(const float4*)(src + 32 * s + 8 * lg), a1 = *(const float4*)(src + 32 * s + 8 * lg + 4);
+        x[s][0] = a0.x; x[s][1] = a0.y; x[s][2] = a0.z; x[s][3] = a0.w;
+        x[s][4] = a1.x; x[s][5] = a1.y; x[s][6] = a1.z; x[s][7] = a1.w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(x[s][j], x[s][j], ss);
+      }
+      ss += __shfl_xor(ss, 16, 64);  // the four lanes of query li, in a fixed order
+      ss += __shfl_xor(ss, 32, 64);
+      const float sq = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const u32x4_t gq = *(const u32x4_t*)(qnorm + 32 * s + 8 * lg);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t gw = gq[j >> 1];
+          x[s][j] = x[s][j] * sq * __uint_as_float((j & 1) ? (gw & 0xffff0000u) : (gw << 16));
+        }
+      }
+      const float4* rrow = (const float4*)(rope + (size_t)r * HALF);  // two (cos, sin) per float4
+#pragma unroll
+      for (int s = 0; s < DS / 2; ++s)
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const float4 cs2 = rrow[(32 * s + 8 * lg) / 2 + j2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int j = 2 * j2 + u;
+            const float cc = u ? cs2.z : cs2.x, sn = u ? cs2.w : cs2.y;
+            const float x1 = x[s][j], x2 = x[s + DS / 2][j];
+            x[s][j] = x1 * cc - x2 * sn;
+            x[s + DS / 2][j] = x2 * cc + x1 * sn;
+          }
+        }
+#pragma unroll
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t hp, lp;
+          split2_bf16(x[s][2 * t], x[s][2 * t + 1], hp, lp);
+          qf[s][t] = hp;
+          qfl[s][t] = lp;
+        }
     }
     // scores: element i of tile (h, tb) is position p0 + 32h + 8*lg + 4*tb + i for query li
     float S[2][2][4];
@@ -414,7 +544,7 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
 }
 
 // ---- launchers ------------------------------------------------------------------------------
-hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
+static hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
                             int R, int64_t pos0, void* qb, void* qlo, void* ring_layer, hipStream_t s) {
   const int items = R * (a.nq + 2 * a.nkv);
   const int grid = (items + 3) / 4;
@@ -436,8 +566,6 @@ hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const 
   return hipGetLastError();
 }
 
-static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
-
 size_t attention_partial_floats(const AttnShape& a, int R) {
   // chunks of a launch: positions lo..e+R-1 (at most W + R of them) cut at multiples of 64
   const int nch = (a.window + R + 2 * ATTN_CHUNK - 2) / ATTN_CHUNK;
@@ -446,23 +574,31 @@ size_t attention_partial_floats(const AttnShape& a, int R) {
 
 int attention_max_chunks() { return COMBINE_MAX_CHUNKS; }
 
-hipError_t launch_attention(int bf, const AttnShape& a, const void* ring_layer, const void* qb, const void* qlo,
-                            int R, int64_t e, float* part, void* out, void* out_lo, hipStream_t s) {
+static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
+
+hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
+                                  const float2* rope, void* ring_layer, int R, int64_t e, void* qb, void* qlo,
+                                  float* part, void* out, void* out_lo, hipStream_t s) {
   const int nch = attn_nchunks(a, R, e);
-  if (nch > COMBINE_MAX_CHUNKS) return hipErrorInvalidValue;
+  if (nch > COMBINE_MAX_CHUNKS || R < 1) return hipErrorInvalidValue;
   dim3 grid(nch, a.nkv);
   if (use_mfma(bf, a)) {
+    if (!rope) return hipErrorInvalidValue;
     const uint16_t* rl = (const uint16_t*)ring_layer;
+    const uint16_t *qn = (const uint16_t*)qnorm, *kn = (const uint16_t*)knorm;
     if (a.hd == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
-                         R, e, nch, part);
+      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, part);
     else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, (const uint16_t*)qb, (const uint16_t*)qlo,
-                         R, e, nch, part);
+      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
     return hipGetLastError();
+  }
+  // queries as operands, the block's own k/v into the ring slots of positions e..e+R-1
+  {
+    const hipError_t pe = launch_attn_prep(bf, a, qkv, qnorm, knorm, R, e, qb, qlo, ring_layer, s);
+    if (pe != hipSuccess) return pe;
   }
   const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4;
   const void* fn = bf ? (const void*)attn_partial_kernel<true> : (const void*)attn_partial_kernel<false>;

@@ -31,7 +31,7 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, app_fc, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, rope, app_fc, app_kv, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -234,6 +234,7 @@ Layout make_layout(const Cfg& g) {
   L.mlp = take(4 * R * c.intermediate);
   L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
+  L.rope = take(sizeof(float2) * R * (c.head_dim / 2));  // rotary table of a draft's positions
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
   L.total = o;
@@ -453,12 +454,14 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
     if (g.wt == WT_Q4) return l.scales && l.biases && ((uintptr_t)l.scales & 1u) == 0 && ((uintptr_t)l.biases & 1u) == 0;
     return true;
   };
-  if (!wts->embed || !wts->enc_norm || !wts->final_norm || !lin_ok(wts->lm_head) || !lin_ok(wts->fc))
+  // norm gains are read 16 bytes at a time
+  auto gain_ok = [&](const void* p) { return p && aligned16(p); };
+  if (!wts->embed || !gain_ok(wts->enc_norm) || !gain_ok(wts->final_norm) || !lin_ok(wts->lm_head) || !lin_ok(wts->fc))
     return cfg_fail(g_create_err, DFLASH_E_ARG, "a top-level weight is NULL or not 16-byte aligned");
   for (int l = 0; l < g.c.layers; ++l) {
     const dflash_layer& L = wts->layers[l];
     if (!lin_ok(L.q) || !lin_ok(L.k) || !lin_ok(L.v) || !lin_ok(L.o) || !lin_ok(L.gate) || !lin_ok(L.up) ||
-        !lin_ok(L.down) || !L.in_norm || !L.post_norm || !L.q_norm || !L.k_norm)
+        !lin_ok(L.down) || !gain_ok(L.in_norm) || !gain_ok(L.post_norm) || !gain_ok(L.q_norm) || !gain_ok(L.k_norm))
       return cfg_fail(g_create_err, DFLASH_E_ARG, "layer %d has a NULL or misaligned weight", l);
   }
   dflash_ctx* ctx = new (std::nothrow) dflash_ctx();
@@ -632,7 +635,11 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   float* part = (float*)(ctx->ws + ctx->lay.part);
   const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * c.head_dim;
 
-  dflash_status s = dev(ctx, launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, x, st), "embed");
+  float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
+  dflash_status s = dev(ctx,
+                        launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, x, rope, ctx->e, c.rope_theta,
+                                     c.head_dim, st),
+                        "embed");
   if (s != DFLASH_OK) return s;
   for (int l = 0; l < c.layers; ++l) {
     const Layer& L = ctx->layers[l];
@@ -640,12 +647,9 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
                L.in_norm, qkv, qd + 2 * kvd, nullptr};
     q.split = g.bf;
     if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
-    // q as an operand; the block's own k/v into the ring slots of positions e..e+R-1
     s = dev(ctx,
-            launch_attn_prep(g.bf, g.a, qkv, L.q_norm, L.k_norm, R, ctx->e, qb, qb_lo, ctx->ring + l * ring_layer, st),
-            "attn prep");
-    if (s != DFLASH_OK) return s;
-    s = dev(ctx, launch_attention(g.bf, g.a, ctx->ring + l * ring_layer, qb, qb_lo, R, ctx->e, part, attn, attn_lo, st),
+            launch_block_attention(g.bf, g.a, qkv, L.q_norm, L.k_norm, rope, ctx->ring + l * ring_layer, R, ctx->e, qb,
+                                   qb_lo, part, attn, attn_lo, st),
             "attention");
     if (s != DFLASH_OK) return s;
     GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};

@@ -129,23 +129,25 @@ hipError_t launch_pack_q4(const void* codes, const void* scales, const void* bia
                           void* dst_scales, hipStream_t s);
 // idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
+// Embedding rows [anchor, mask x (R-1)] as f32 residual rows x; with rope != NULL also the
+// rotary table of positions pos0..pos0+R-1, rope[r][i] = (cos, sin), i < hd/2.
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
-                        float* x, hipStream_t s);
+                        float* x, float2* rope, int64_t pos0, float theta, int hd, hipStream_t s);
 // RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
                           void* out_lo, hipStream_t s);
-// q/k RMSNorm + RoPE: q as an operand (hi/lo planes qb/qlo, or f32); k and v of the block
-// rows into the ring slots of positions pos0.. (cache dtype).
-hipError_t launch_attn_prep(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
-                            const void* knorm, int R, int64_t pos0, void* qb, void* qlo, void* ring_layer,
-                            hipStream_t s);
 hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
                              int n, int64_t pos0, void* ring, hipStream_t s);
-// Attention of R block rows (positions e..e+R-1) over positions max(0, e-W)..e+R-1 of the
-// ring layer; writes the O-projection operand out/out_lo.
-hipError_t launch_attention(int act_bf16, const AttnShape& a, const void* ring_layer, const void* qb,
-                            const void* qlo, int R, int64_t e, float* part, void* out, void* out_lo,
-                            hipStream_t s);
+// Attention side of one layer of the block forward: q/k RMSNorm + RoPE of the R block rows
+// (positions e..e+R-1, raw projections qkv f32 [R][(nq + 2 nkv) hd]), then attention over
+// positions max(0, e-W)..e+R-1, writing the O-projection operand out/out_lo. The context
+// keys come from the ring layer; the block's own keys and values are formed where they are
+// used (bf16 shapes with head dim 64 or 128, reading the rotary table rope of launch_embed)
+// or written into the ring slots of positions e..e+R-1 first (other shapes, which also use
+// qb/qlo for the formed queries).
+hipError_t launch_block_attention(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
+                                  const void* knorm, const float2* rope, void* ring_layer, int R, int64_t e, void* qb,
+                                  void* qlo, float* part, void* out, void* out_lo, hipStream_t s);
 size_t attention_partial_floats(const AttnShape& a, int R);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);

@@ -39,17 +39,33 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
 
 // Block rows [anchor, mask x (R-1)] from the target's raw embedding table (not the
 // embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows.
+// The draft's first kernel also tabulates the rotary rotation of every block position
+// pos0 + r, (cos, sin) of (pos0 + r) * theta^(-2i/hd) for i < hd/2, evaluated in f64 and
+// rounded to f32 as the per-element RoPE of the prep kernel does; every layer's attention
+// reads it (rope may be NULL).
 template <bool BF>
-__global__ void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x) {
+__global__ void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
+                             float2* rope, int64_t pos0, float theta, int hd) {
   const int r = blockIdx.x;
   const int64_t tok = r == 0 ? anchor : mask_id;
   for (int i = threadIdx.x; i < hidden; i += blockDim.x) x[(size_t)r * hidden + i] = act_ld<BF>(table, tok * hidden + i);
+  if (rope)
+    for (int i = threadIdx.x; i < hd / 2; i += blockDim.x) {
+      const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
+      double sn, cs;
+      sincos((double)(pos0 + r) * inv, &sn, &cs);
+      rope[(size_t)r * (hd / 2) + i] = make_float2((float)cs, (float)sn);
+    }
 }
 
 hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
-                        hipStream_t s) {
-  if (bf) hipLaunchKernelGGL(embed_kernel<true>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x);
-  else hipLaunchKernelGGL(embed_kernel<false>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x);
+                        float2* rope, int64_t pos0, float theta, int hd, hipStream_t s) {
+  if (bf)
+    hipLaunchKernelGGL(embed_kernel<true>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x, rope, pos0,
+                       theta, hd);
+  else
+    hipLaunchKernelGGL(embed_kernel<false>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x, rope,
+                       pos0, theta, hd);
   return hipGetLastError();
 }
 

@@ -124,7 +124,8 @@ dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, s
  * becomes one contiguous kilobyte in the lane order of the MFMA operand, so that the
  * weight streams of every later call read whole contiguous kilobytes. The call
  * synchronises `stream`; afterwards the caller may free those row-major linears. The
- * embedding table and the norm gains are read in place and must stay alive. The ring
+ * embedding table and the norm gains are read in place and must stay alive; the linears
+ * and the norm gains must be 16-byte aligned (DFLASH_E_ARG otherwise). The ring is
  * zero-filled and starts empty: e = 0, no pending rows. */
 dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *weights, void *ring,
                             size_t ring_bytes, void *workspace, size_t workspace_bytes, void *packed,
@@ -158,10 +159,11 @@ dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
  * Draft one block: rows [anchor, mask x block] at absolute positions e..e+block are
  * embedded with the raw table, run through every layer over the ring's committed
  * context and the block's own keys, and rows 1..block go through final_norm and the
- * lm_head. Each layer writes the block's own k/v into the ring slots of positions
- * e..e+block, which lie past the committed window (dflash_cache_read never returns them
- * and the next append overwrites them). d_tokens (device int32 [block]) receives the first index of each row's
- * maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
+ * lm_head. The ring slots of positions e..e+block lie past the committed window: a layer
+ * may store the block's own k/v there (f32 shapes do; dflash_cache_read never returns
+ * those slots and the next append overwrites them), and
+ * the committed window is never written. d_tokens (device int32 [block]) receives the
+ * first index of each row's maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
  * residual stream after the last layer. Errors: block outside 1..max_block or anchor
  * outside [0, vocab) (DFLASH_E_RANGE); e == 0 (DFLASH_E_NO_CONTEXT); pending rows
  * (DFLASH_E_STATE).

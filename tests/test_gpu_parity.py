@@ -58,7 +58,10 @@ def test_micro_f32_synthetic_accept(micro_f32_w, block, phase):
     assert any(k > 0 for k in ks)
 
 
-@pytest.mark.parametrize("block,phase,context", [(4, 0, 50), (16, 3, 7), (17, 60, 33), (40, 0, 100)])
+# blocks 63 and 64 put the block's own keys into two or three 64-position chunks of the
+# attention (window 20), and the GEMMs into two launches of rows
+@pytest.mark.parametrize("block,phase,context",
+                         [(4, 0, 50), (16, 3, 7), (17, 60, 33), (40, 0, 100), (63, 8, 70), (64, 16, 130)])
 def test_micro_bf16_random_depth(micro_bf16_w, block, phase, context):
     ls = P.LockStep(MICRO_BF16, micro_bf16_w, max_block=block, phase=phase)
     P.run_random_depth_rounds(ls, context, block, 10, tag=block)
