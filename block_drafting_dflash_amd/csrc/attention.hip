@@ -284,7 +284,31 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   const int s0 = (int)ring_slot(a, p0);
   auto slot_at = [&](int kk) { const int sl = s0 + kk; return sl >= C ? sl - C : sl; };
 
-  // ---- ring operands first (their latency covers the block staging below) ---------------
+  // ---- loads: the block rows first, then the ring operands ---------------------------------
+  // The memory counter retires loads in issue order: the raw block k/v that the staging
+  // below needs go out before the ring operands, so the staging arithmetic overlaps the ring
+  // fetch. Wave w stages positions b0 + w + 4k; the first SK of them load up front.
+  constexpr int SK = 5;
+  const bool act = lane < HALF;
+  float kx1[SK], kx2[SK], vx1[SK], vx2[SK];
+  float2 rc[SK];
+  if (blk) {
+#pragma unroll
+    for (int k = 0; k < SK; ++k) {
+      const int64_t p = b0 + w + 4 * k;
+      if (p < b1) {  // uniform per wave
+        const int r = (int)(p - e);
+        const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
+        const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
+        const int l1 = act ? lane : 0;
+        kx1[k] = kr[l1];
+        kx2[k] = kr[l1 + HALF];
+        vx1[k] = vr[l1];
+        vx2[k] = vr[l1 + HALF];
+        rc[k] = rope[(size_t)r * HALF + l1];
+      }
+    }
+  }
   // K rows: half h, tile tb, row li <-> position p0 + 32h + 8*(li/4) + 4*tb + li%4
   u32x4_t kf[2][2][DS];
   // V^T runs: half h, dim tile dt: dim dt*16 + li, positions p0 + 32h + 8*lg .. + 8
@@ -309,23 +333,33 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   if (blk) {
     // the block's own keys and values of this chunk, one wave per position as in the prep
     // kernel: k RMSNorm, gain and RoPE, then bf16 (the ring's dtype); v cast to bf16
-    for (int64_t p = b0 + w; p < b1; p += 4) {
-      const int r = (int)(p - e), i = (int)(p - p0);
-      const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
-      const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
-      const bool act = lane < HALF;
-      float x1 = act ? kr[lane] : 0.f, x2 = act ? kr[lane + HALF] : 0.f;
+    const float g1 = bf2f(knorm[act ? lane : 0]), g2 = bf2f(knorm[(act ? lane : 0) + HALF]);
+    auto stage = [&](int64_t p, float x1, float x2, float v1, float v2, float2 cs) {
+      const int i = (int)(p - p0);
+      x1 = act ? x1 : 0.f;
+      x2 = act ? x2 : 0.f;
       const float ss = wave_sum(x1 * x1 + x2 * x2);
       const float sc = rsqrtf(ss / (float)HD + a.eps);
       if (act) {
-        x1 = x1 * sc * bf2f(knorm[lane]);
-        x2 = x2 * sc * bf2f(knorm[lane + HALF]);
-        const float2 cs = rope[(size_t)r * HALF + lane];
+        x1 = x1 * sc * g1;
+        x2 = x2 * sc * g2;
         kst[i * KSTR + lane] = f2bf(x1 * cs.x - x2 * cs.y);
         kst[i * KSTR + lane + HALF] = f2bf(x2 * cs.x + x1 * cs.y);
-        vst[lane * VSTR + i] = f2bf(vr[lane]);
-        vst[(lane + HALF) * VSTR + i] = f2bf(vr[lane + HALF]);
+        vst[lane * VSTR + i] = f2bf(v1);
+        vst[(lane + HALF) * VSTR + i] = f2bf(v2);
       }
+    };
+#pragma unroll
+    for (int k = 0; k < SK; ++k) {
+      const int64_t p = b0 + w + 4 * k;
+      if (p < b1) stage(p, kx1[k], kx2[k], vx1[k], vx2[k], rc[k]);
+    }
+    // positions past the first 4 * SK of the chunk (blocks of more than 20 rows)
+    for (int64_t p = b0 + w + 4 * SK; p < b1; p += 4) {
+      const int r = (int)(p - e), l1 = act ? lane : 0;
+      const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
+      const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
+      stage(p, kr[l1], kr[l1 + HALF], vr[l1], vr[l1 + HALF], rope[(size_t)r * HALF + l1]);
     }
     __syncthreads();
   }
