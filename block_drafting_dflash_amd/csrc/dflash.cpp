@@ -314,9 +314,13 @@ struct GemmCall {
 dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
   const Cfg& g = ctx->cfg;
   GemmCall gc = gc_in;
-  if (gc.xsrc == XSRC_NORM && gc.split && rows > 16) {
-    // hi/lo operand pairs of more than one row tile would not stay in registers: normalise
-    // the rows once into planes and stream them
+  const int wt = g.wt;
+  GemmPlan plan;
+  // normed hi/lo operands: up to GEMM_NORM_STAGED_ROWS rows run directly when each wave's k
+  // range is 256 elements (its raw rows are staged through LDS); more rows would not fit,
+  // so they are normalised once into planes and streamed
+  if (gc.xsrc == XSRC_NORM && gc.split && rows > 16 &&
+      !(rows <= GEMM_NORM_STAGED_ROWS && plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan) && plan.nch == 1)) {
     void* hn = ctx->ws + ctx->lay.hn;
     void* hn_lo = lo_plane(g, hn, hn_rows(g), gc.K);
     const dflash_status s0 =
@@ -328,9 +332,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     gc.ldx = gc.K;
     gc.gain = nullptr;
   }
-  const int wt = g.wt;
   const int nb = gc.epi == EPI_SWIGLU ? 2 : 1;
-  GemmPlan plan;
   if (!plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan)) return fail(ctx, DFLASH_E_SHAPE, "no GEMM plan for K = %d", gc.K);
   const int waves = plan.waves;
   const size_t x_elt = gc.xsrc == XSRC_NORM ? 4 : g.act_elt;  // a split operand is two bf16 planes
@@ -346,7 +348,8 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     if (gc.epi == EPI_ARGMAX) rc = std::min(rc, std::min(32, 16 * waves));  // one finishing wave per row tile
     // tiles per work-group that size the reduction buffers: two or more for the argmax, two
     // for normed hi/lo operands over an even tile count (the launch below)
-    const int tpw_lds = gc.epi == EPI_ARGMAX || (gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0) ? 2 : 1;
+    const bool norm_two = gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0 && (rc <= 16 || nb == 1);
+    const int tpw_lds = gc.epi == EPI_ARGMAX || norm_two ? 2 : 1;
     while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
     GemmParams p{};
     for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
@@ -363,9 +366,10 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     p.eps = g.c.rms_eps;
     GemmPlan pl = plan;
     pl.grid = p.ntiles;
-    if (gc.xsrc == XSRC_NORM && gc.split && p.ntiles % 2 == 0) {
+    if (norm_two) {
       // normed hi/lo operands: two tiles per work-group share the operand registers and
-      // halve the operand reads from L2
+      // halve the operand reads from L2 (two row tiles of the gate/up pair keep one: its
+      // weights of two tiles would not fit beside the operand pairs)
       pl.tiles_per_wg = 2;
       pl.grid = p.ntiles / 2;
     }

@@ -131,9 +131,14 @@ constexpr int gemm_chunks_ahead() {
   constexpr int raw = XSRC == XSRC_NORM ? RT * CH * 4 * 2 + CH * 4 : 0;
   constexpr int gupi = 64 / (CH * 32 * 2 / 16);  // staged rows per load instruction
   constexpr int staged = planes * ((16 * RT + gupi - 1) / gupi) * 4 + 32;
-  // normed rows of a later chunk are loaded while the earlier chunks' pairs are held
+  // normed rows of a later chunk are loaded while the earlier chunks' pairs are held, unless
+  // the raw rows of the wave's whole k range are staged through LDS first (then they are
+  // dead before the pairs are formed)
+  constexpr bool stg_n = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * 32 == 256;
+  constexpr int raw_stg = ((RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS) + 1) * 4;
   constexpr int opnd = XSRC == XSRC_GLOBAL ? (RT <= 2 ? staged : 2 * frag)
                        : XSRC == XSRC_LDS  ? NCH * frag
+                       : stg_n             ? (raw_stg > NCH * frag ? raw_stg : NCH * frag)
                        : NCH == 1          ? (raw > frag ? raw : frag)
                                            : NCH * frag + raw;
   constexpr int wreg = Q4 ? NB * (CH / 4) * 6 : NB * CH * 4;
@@ -174,13 +179,14 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   // staged operands: streamed rows (STG_G) of one chunk, [plane][row][CH * KSTEP] bf16; or the
   // normed raw rows (STG_N) of the wave's whole k range, [row][CH * KSTEP] f32 then the gains
   constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RT <= 2;
-  constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT == 1 && NCH == 1;
+  constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * Tr::KSTEP == 256;
+  constexpr int STG_N_ROWS = RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows a normed launch stages
   constexpr int SP = SPLIT ? 2 : 1;          // operand planes
   constexpr int LK = CH * Tr::KSTEP;          // k of one chunk
   constexpr int GU = LK * 2 / 16;             // lanes per staged bf16 row (32 or 16)
   constexpr int GUPI = 64 / GU;               // staged rows per load instruction
   constexpr int GIMAX = (16 * RT + GUPI - 1) / GUPI;
-  static_assert(!STG_N || LK * 4 == 1024, "a normed row of one chunk is one wave load");
+  static_assert(!STG_N || NCH * LK * 4 == 1024, "a normed row of the wave's k range is one wave load");
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues run with T dividing the tile count
@@ -506,7 +512,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   f32x4_t xa[STG_N ? 1 : RT][CH][XRAW];
   u32x4_t ga[CH];
   // STG_N: raw row i of the wave's k range in load i (64 lanes x 4 f32), the gains in the last
-  u32x4_t xn[STG_N ? 17 : 1];
+  u32x4_t xn[STG_N ? STG_N_ROWS + 1 : 1];
   auto kof = [&](int c, int st) { return w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL; };
   auto raw_ld = [&](int c, int rt, int st, int h) {
     return *(const f32x4_t*)((const float*)p.x + (size_t)xrow(rt) * p.ldx + kof(c, st) + 4 * h);
@@ -545,9 +551,9 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   } else if constexpr (STG_N) {
     const size_t k0 = (size_t)w * kw;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < STG_N_ROWS; ++i)
       if (i < R) xn[i] = *(const u32x4_t*)((const float*)p.x + (size_t)i * p.ldx + k0 + lane * 4);
-    xn[16] = *(const u32x4_t*)((const uint16_t*)p.gain + k0 + (lane & 31) * 8);
+    xn[STG_N_ROWS] = *(const u32x4_t*)((const uint16_t*)p.gain + k0 + (lane & 31) * 8);
   } else if constexpr (NORM_FIRST) {
 #pragma unroll
     for (int st = 0; st < CH; ++st) {
@@ -592,9 +598,9 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     for (int rt = 0; rt < RT; ++rt) ssl[rt] = 0.f;
     if constexpr (STG_N) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < STG_N_ROWS; ++i)
         if (i < R) *(u32x4_t*)(xs + (size_t)i * lds.row_bytes + lane * 16) = xn[i];
-      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (lane & 31) * 16) = xn[16];
+      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (lane & 31) * 16) = xn[STG_N_ROWS];
     }
     // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
 #pragma unroll
@@ -605,8 +611,9 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
         for (int st = 0; st < CH; ++st) {
           u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
           if constexpr (STG_N) {
-            const unsigned char* xrw = xs + (size_t)min(li, R - 1) * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 4;
-            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2);
+            const int kk = (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;  // within the wave's k range
+            const unsigned char* xrw = xs + (size_t)min(rt * 16 + li, R - 1) * lds.row_bytes + kk * 4;
+            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + kk * 2);
             form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
           } else if constexpr (NORM_FIRST) {
             form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
@@ -696,7 +703,12 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
   const int rt = (p.R + 15) / 16;
   if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
   if constexpr (XSRC == XSRC_NORM && SPLIT) {
-    return hipErrorInvalidValue;  // normed hi/lo operands of more rows go through planes (run_gemm)
+    // normed hi/lo operands of two row tiles: staged raw rows over a 256-element k range
+    // per wave (at most GEMM_NORM_STAGED_ROWS rows); larger launches go through planes
+    if constexpr (NCH == 1) {
+      if (rt == 2 && p.R <= GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
   } else {
     if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
     if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows

@@ -9,6 +9,8 @@ enum { WT_F32 = 0, WT_BF16 = 1, WT_Q4 = 2 };  // weight storage (matches dflash_
 
 constexpr int GEMM_MAXSEG = 12;
 constexpr int GEMM_MAX_ROWS = 48;  // rows per GEMM launch (3 MFMA row tiles)
+// normed hi/lo operands of two row tiles stage at most this many raw rows per wave in LDS
+constexpr int GEMM_NORM_STAGED_ROWS = 18;
 constexpr int ATTN_CHUNK = 64;     // keys per attention work-group
 constexpr int ATTN_QG = 64;        // query vectors per attention pass
 constexpr int MAX_WINDOW = 4096;   // attention chunks of one query stay within the combine's LDS
@@ -66,9 +68,10 @@ bool gemm_plan_supported(const GemmPlan& pl, int epi, int xsrc);
 hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const GemmParams& p, hipStream_t s);
 // LDS of a GEMM work-group: the cross-wave reduction buffers (double-buffered across tiles
 // when a work-group owns several), the per-wave row sums of squares of the RMSNorm operands
-// (XSRC_NORM), and, for bf16 and 4-bit weights, a per-wave slot that stages the operand
-// rows of one chunk of the wave's k range (XSRC_GLOBAL with at most two row tiles: R rows
-// of each plane; XSRC_NORM with one row tile and one chunk: R raw f32 rows and the gains).
+// (XSRC_NORM), and, for bf16 and 4-bit weights, a per-wave slot that stages operand rows:
+// XSRC_GLOBAL with at most two row tiles, the R rows of each plane for one chunk of the
+// wave's k range; XSRC_NORM with at most two row tiles and a 256-element k range per wave,
+// the R raw f32 rows of that range and its gains.
 // Staging loads only the R real rows with every lane busy, where the MFMA fragments would
 // load 16 rows per row tile; the fragments are then read from LDS. The normed slot is dead
 // once the operand pairs are formed and shares its bytes with the reduction buffers.
@@ -92,10 +95,10 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, 
     l.stage = 1;
     l.row_bytes = ch * kstep * 2 + 16;
     l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
-  } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt == 1 && nch == 1) {
-    l.stage = 2;
-    l.row_bytes = ch * kstep * 4 + 16;
-    l.xs_wave = (size_t)R * l.row_bytes + (size_t)ch * kstep * 2;
+  } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt <= 2 && nch * ch * kstep == 256) {
+    l.stage = 2;  // the raw rows of the wave's whole k range (256 f32) and its gains
+    l.row_bytes = 256 * 4 + 16;
+    l.xs_wave = (size_t)R * l.row_bytes + 256 * 2;
   }
   if (l.stage == 2) {
     l.xs_off = 0;
