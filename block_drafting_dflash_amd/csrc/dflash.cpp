@@ -117,11 +117,12 @@ bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
 
 // Tiles per work-group of an argmax launch: small work-groups keep the dispatcher
 // balancing the vocabulary stream; with more rows, more tiles per work-group bound how
-// often the operand rows are re-read from L2. Measured over a vocabulary-sized head
-// (202048 x 2048): bf16 single-plane rows run fastest at two tiles (four past 16 rows),
-// bf16 hi/lo pairs, with twice the operand loads and products, at four (eight past 8
-// rows); 4-bit heads, bound by dequantisation rather than bytes, at eight for hi/lo pairs
-// and four (eight past 16 rows) for single-plane rows.
+// often the operand rows are re-read. Measured over a vocabulary-sized head (202048 x
+// 2048, operand rows of one row tile staged through LDS): bf16 single-plane rows run
+// fastest at two tiles (four past 16 rows), bf16 hi/lo pairs, with twice the operand loads
+// and products, at four (eight past 8 rows, where whole-round runs favoured it); 4-bit
+// heads, bound by dequantisation rather than bytes, at eight for hi/lo pairs and four
+// (eight past 16 rows) for single-plane rows.
 int argmax_tiles_per_wg(int wt, int split, int ntiles, int rows) {
   if (ntiles < 1024) return 1;
   if (ntiles < 8192) return 2;

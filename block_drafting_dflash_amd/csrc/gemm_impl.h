@@ -567,10 +567,41 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) load_w(wbuf[i], sbuf[i], i);
   load_resid();
-  if constexpr (XSRC == XSRC_LDS) {
-    // LDS-source planes (the argmax rows): every chunk into the operand fragments, behind
-    // the first weight chunk and only for the real rows (measured faster for the
-    // vocabulary stream, where each work-group is one of many on its CU)
+  constexpr bool STG_L = BF && XSRC == XSRC_LDS && RT == 1 && NCH == 1;
+  if constexpr (STG_L) {
+    // LDS-source rows (the argmax rows), behind the first weight chunk: the R real rows of
+    // each plane over the wave's k range (512 bytes: 32 lanes, two rows per load) into the
+    // wave's staging slot, then the MFMA fragments from there
+    u32x4_t xc2[SP][8];
+    const int npairs = (R + 1) / 2;
+    const int half = lane >> 5, piece = lane & 31;
+#pragma unroll
+    for (int pl = 0; pl < SP; ++pl)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < npairs) {
+          const int r = min(2 * i + half, R - 1);
+          const unsigned char* src = (const unsigned char*)(pl ? p.xlo : p.x);
+          xc2[pl][i] = *(const u32x4_t*)(src + ((size_t)r * p.ldx + (size_t)w * kw) * 2 + piece * 16);
+        }
+#pragma unroll
+    for (int pl = 0; pl < SP; ++pl)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < npairs) {
+          const int r = min(2 * i + half, R - 1);
+          *(u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + piece * 16) = xc2[pl][i];
+        }
+#pragma unroll
+    for (int st = 0; st < CH; ++st) {
+      const int r = min(li, R - 1);
+      const size_t o = (size_t)r * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2;
+      xr[0][0][st] = *(const u32x4_t*)(xs + o);
+      if constexpr (SPLIT) xrl[0][0][st] = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + o);
+    }
+  } else if constexpr (XSRC == XSRC_LDS) {
+    // LDS-source planes of more row tiles or chunks: every chunk into the operand
+    // fragments, behind the first weight chunk and only for the real rows
 #pragma unroll
     for (int c = 0; c < XR; ++c)
 #pragma unroll

@@ -71,12 +71,13 @@ hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const Gemm
 // (XSRC_NORM), and, for bf16 and 4-bit weights, a per-wave slot that stages operand rows:
 // XSRC_GLOBAL with at most two row tiles, the R rows of each plane for one chunk of the
 // wave's k range; XSRC_NORM with at most two row tiles and a 256-element k range per wave,
-// the R raw f32 rows of that range and its gains.
+// the R raw f32 rows of that range and its gains; XSRC_LDS (the argmax rows) with one row
+// tile and one chunk per wave, the R rows of each plane, once per work-group.
 // Staging loads only the R real rows with every lane busy, where the MFMA fragments would
 // load 16 rows per row tile; the fragments are then read from LDS. The normed slot is dead
 // once the operand pairs are formed and shares its bytes with the reduction buffers.
 struct GemmLds {
-  int stage;       // 0 none, 1 streamed rows, 2 normed rows
+  int stage;       // 0 none, 1 streamed rows, 2 normed rows, 3 LDS-source rows
   int row_bytes;   // staged bytes per row and plane, padded by 16 against bank conflicts
   size_t ssq_off;  // byte offsets in the work-group's LDS
   size_t xs_off;
@@ -93,6 +94,10 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, 
   GemmLds l{};
   if (wt != WT_F32 && xsrc == XSRC_GLOBAL && rt <= 2) {
     l.stage = 1;
+    l.row_bytes = ch * kstep * 2 + 16;
+    l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
+  } else if (wt != WT_F32 && xsrc == XSRC_LDS && rt == 1 && nch == 1) {
+    l.stage = 3;  // the LDS-source rows of the wave's k range, once per work-group
     l.row_bytes = ch * kstep * 2 + 16;
     l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
   } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt <= 2 && nch * ch * kstep == 256) {
