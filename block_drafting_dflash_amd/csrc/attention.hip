@@ -233,50 +233,94 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
   }
 }
 
-// ---- attention on MFMA (bf16 operands): one work-group per (64-key chunk, kv head) ------
-// Each wave takes query tiles w, w+4, ... and reads its operands straight from the ring:
-// scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16 key rows, B = 16 queries), then O^T = V^T
-// P^T (A = 16 dims x 32 keys from the transposed V, B = P). The key rows of the two score
-// tiles of each 32-key half are ordered so that lane (li, lg) ends up with keys 8*lg ..
-// 8*lg+7 of the half for query li, exactly its B operand of the output product, and the
-// matching V^T run is one aligned 16-byte load. Q (an f32 activation) and P (in [0, 1])
-// enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16 already,
-// products are exact and sums f32.
+// N consecutive f32 (16-, 8- or 4-byte aligned for N = 4, 2, 1 per vector) and bf16 values
+template <int N>
+__device__ __forceinline__ void ld_f32(const float* p, float (&o)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 v = *(const float4*)(p + i);
+      o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      const float2 v = *(const float2*)(p + i);
+      o[i] = v.x; o[i + 1] = v.y;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void ld_bf16(const uint16_t* p, float (&o)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const uint32_t w = *(const uint32_t*)(p + i);
+    o[i] = __uint_as_float(w << 16);
+    o[i + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+template <int N>
+__device__ __forceinline__ void st_u16(uint16_t* p, const uint16_t (&v)[N]) {
+  if constexpr (N == 4) {
+    *(uint2*)p = make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) *(uint32_t*)(p + i) = (uint32_t)v[i] | ((uint32_t)v[i + 1] << 16);
+  }
+}
+
+// ---- attention on MFMA (bf16 operands): one work-group per (64-key chunk, kv head, query part)
+// The work-group copies the chunk's keys and transposed values from the ring into LDS once
+// (16-byte units spread over all its threads), and each wave takes at most one 16-query
+// tile, reading its MFMA operands from LDS: scores S^T = K Q^T (16x16x32 bf16 MFMA; A = 16
+// key rows, B = 16 queries), then O^T = V^T P^T (A = 16 dims x 32 keys of V^T, B = P). The
+// key rows of the two score tiles of each 32-key half are ordered so that lane (li, lg)
+// ends up with keys 8*lg .. 8*lg+7 of the half for query li, exactly its B operand of the
+// output product, and the matching V^T run is one 16-byte read. Q (an f32 activation) and
+// P (in [0, 1]) enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16
+// already, products are exact and sums f32. The launch splits the query tiles over
+// gridDim.z work-groups of at most 8 waves, so no wave runs two tiles in turn.
 //
-// The kernel also does what the prep kernel does for the block rows. A query
-// fragment holds dims 32s + 8lg .. + 8 of one query, so the lane's four lanes lg together
-// hold the whole head (the RMSNorm sum is two shuffles) and each rotate-half partner, dim +
-// hd/2, sits in the same lane (s + DS/2). The block's own keys and values, at positions
-// e..e+R-1, are formed by the work-groups whose chunk holds them, one wave per position as
-// in the prep kernel, into LDS laid out like the chunk (keys by position, values by dim),
-// and replace the ring's values for those positions after the ring loads were issued (the
+// The kernel also does what the prep kernel does for the block rows. A query fragment holds
+// dims 32s + 8lg .. + 8 of one query, so the lane's four lanes lg together hold the whole
+// head (the RMSNorm sum is two shuffles) and each rotate-half partner, dim + hd/2, sits in
+// the same lane (s + DS/2). The block's own keys and values, at positions e..e+R-1, are
+// formed by the work-groups whose chunk holds them, one wave per position as in the prep
+// kernel, and written into the LDS slots of those positions; the ring copy skips them (the
 // ring slots past the committed window are not written).
-template <int HD>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
-                                                        const float* __restrict__ qkv, const uint16_t* __restrict__ qnorm,
-                                                        const uint16_t* __restrict__ knorm,
-                                                        const float2* __restrict__ rope, int R, int64_t e, int nchunks,
-                                                        float* __restrict__ part) {
+//
+// Loads retire in issue order: the raw block rows go out first, then the wave's query tile,
+// then the ring copy, so the staging and the query arithmetic overlap the copy's fetch.
+// NW waves per work-group (4 or 8: the chunk copy divides evenly); BLK: the chunk holds block
+// positions. Every load is issued without a branch, so that each wait before the arithmetic
+// covers only the loads it needs.
+template <int HD, int NW, bool BLK>
+__device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_t* __restrict__ ring_layer,
+                                               const float* __restrict__ qkv, const uint16_t* __restrict__ qnorm,
+                                               const uint16_t* __restrict__ knorm, const float2* __restrict__ rope,
+                                               int R, int64_t e, int nchunks, int tpw, float* __restrict__ part,
+                                               uint16_t* __restrict__ kst, uint16_t* __restrict__ vst) {
   constexpr int KC = ATTN_CHUNK;  // 64 positions = two halves of 32
   constexpr int DS = HD / 32, DT = HD / 16, HALF = HD / 2;
-  constexpr int KSTR = HD + 8;   // staged key row stride (elements)
-  constexpr int VSTR = KC + 8;   // staged V^T row stride (elements)
-  static_assert(KC == 64, "two 32-key halves per work-group");
-  // the chunk's block keys [chunk position][KSTR] and values transposed [dim][VSTR]
-  __shared__ __align__(16) uint16_t kst[KC * KSTR];
-  __shared__ __align__(16) uint16_t vst[HD * VSTR];
+  constexpr int KSTR = HD + 8;      // LDS key row stride (elements)
+  constexpr int VSTR = KC + 8;      // LDS V^T row stride (elements)
+  constexpr int KU = KC * HD / 8;   // 16-byte units of the chunk's keys (and of its values)
+  constexpr int NIT = KU / (64 * NW);
+  constexpr int EPT = HALF / 16;    // staging: dims per lane and half, 16 lanes per position
+  static_assert(KC == 64 && KU % (64 * NW) == 0, "two 32-key halves, an even copy");
   const int g = blockIdx.y, c = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int G = a.nq / a.nkv, NQ = R * G, nqt = (NQ + 15) / 16;
-  const bool active = w < nqt;  // waves past the last query tile only help staging
+  const int G = a.nq / a.nkv, NQ = R * G;
+  const int qt = blockIdx.z * tpw + w;
+  const bool active = w < tpw && qt * 16 < NQ;  // other waves only copy and stage
   const int64_t lo = attn_lo(a, e), hi = e + R;
   const int64_t p0 = (lo / KC + c) * KC;
   const int C = a.cap;
   const size_t ldq = (size_t)(a.nq + 2 * a.nkv) * HD;  // raw projection row
-  // block positions of this chunk: b0 .. b1-1 (an empty range for most chunks)
+  // block positions of this chunk: b0 .. b1-1 (non-empty when BLK)
   const int64_t b0 = p0 > e ? p0 : e, b1 = p0 + KC < hi ? p0 + KC : hi;
-  const bool blk = b0 < b1;
   const uint16_t* Kp = ring_layer + (size_t)g * C * HD;
   const uint16_t* VTp = ring_layer + (size_t)(a.nkv + g) * HD * C;
   // slot of the chunk's first position: a multiple of 8 (p0, phase and Cs are), so the
@@ -284,240 +328,280 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnShape a, const uint1
   const int s0 = (int)ring_slot(a, p0);
   auto slot_at = [&](int kk) { const int sl = s0 + kk; return sl >= C ? sl - C : sl; };
 
-  // ---- loads: the block rows first, then the ring operands ---------------------------------
-  // The memory counter retires loads in issue order: the raw block k/v that the staging
-  // below needs go out before the ring operands, so the staging arithmetic overlaps the ring
-  // fetch. Wave w stages positions b0 + w + 4k; the first SK of them load up front.
-  constexpr int SK = 5;
-  const bool act = lane < HALF;
-  float kx1[SK], kx2[SK], vx1[SK], vx2[SK];
-  float2 rc[SK];
-  if (blk) {
-#pragma unroll
-    for (int k = 0; k < SK; ++k) {
-      const int64_t p = b0 + w + 4 * k;
-      if (p < b1) {  // uniform per wave
-        const int r = (int)(p - e);
-        const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
-        const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
-        const int l1 = act ? lane : 0;
-        kx1[k] = kr[l1];
-        kx2[k] = kr[l1 + HALF];
-        vx1[k] = vr[l1];
-        vx2[k] = vr[l1 + HALF];
-        rc[k] = rope[(size_t)r * HALF + l1];
-      }
-    }
+  // ---- (1) raw block rows: 16 lanes per position, four positions per wave and step; step k
+  // of wave w takes positions b0 + 4 (w + NW k) + lg, and lane t16 of a position holds dims
+  // EPT t16 .. + EPT and their rotate-half partners (+ HD/2). Step 0 loads up front, its
+  // rows clamped into the block range.
+  const int t16 = lane & 15;
+  float bk1[EPT], bk2[EPT], bv1[EPT], bv2[EPT], bcs[2 * EPT], kg1[EPT], kg2[EPT];
+  auto load_block_row = [&](int64_t p) {
+    const int rr = (int)((p < b1 ? p : b1 - 1) - e);
+    const float* kr = qkv + (size_t)rr * ldq + (size_t)(a.nq + g) * HD + EPT * t16;
+    const float* vr = qkv + (size_t)rr * ldq + (size_t)(a.nq + a.nkv + g) * HD + EPT * t16;
+    ld_f32<EPT>(kr, bk1);
+    ld_f32<EPT>(kr + HALF, bk2);
+    ld_f32<EPT>(vr, bv1);
+    ld_f32<EPT>(vr + HALF, bv2);
+    ld_f32<2 * EPT>((const float*)(rope + (size_t)rr * HALF + EPT * t16), bcs);
+  };
+  if constexpr (BLK) {
+    ld_bf16<EPT>(knorm + EPT * t16, kg1);
+    ld_bf16<EPT>(knorm + HALF + EPT * t16, kg2);
+    load_block_row(b0 + 4 * w + lg);
   }
-  // K rows: half h, tile tb, row li <-> position p0 + 32h + 8*(li/4) + 4*tb + li%4
-  u32x4_t kf[2][2][DS];
-  // V^T runs: half h, dim tile dt: dim dt*16 + li, positions p0 + 32h + 8*lg .. + 8
-  u32x4_t vf[2][DT];
-  if (active) {
+  // ---- (2) the wave's query tile: raw q of (row r, head g*G + hh), gains, rotary table; a
+  // wave without a tile loads row 0 and discards it ------------------------------------------
+  const int qv = qt * 16 + li;
+  const bool qok = active && qv < NQ;
+  const int rq = (int)((unsigned)qv / (unsigned)G);
+  const int r = qok ? rq : 0, hh = qok ? qv - rq * G : 0;
+  float x[DS][8];
+  u32x4_t gq[DS];
+  float4 cs2[DS / 2][4];  // two (cos, sin) per float4
+  {
+    const float* src = qkv + (size_t)r * ldq + (size_t)(g * G + hh) * HD;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int s = 0; s < DS; ++s) {
+      const float4 a0 = *(const float4*)(src + 32 * s + 8 * lg), a1 = *(const float4*)(src + 32 * s + 8 * lg + 4);
+      x[s][0] = a0.x; x[s][1] = a0.y; x[s][2] = a0.z; x[s][3] = a0.w;
+      x[s][4] = a1.x; x[s][5] = a1.y; x[s][6] = a1.z; x[s][7] = a1.w;
+    }
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const uint16_t* row = Kp + (size_t)slot_at(32 * h + 8 * (li >> 2) + 4 * tb + (li & 3)) * HD;
+    for (int s = 0; s < DS; ++s) gq[s] = *(const u32x4_t*)(qnorm + 32 * s + 8 * lg);
+    const float4* rrow = (const float4*)(rope + (size_t)r * HALF);
 #pragma unroll
-        for (int s = 0; s < DS; ++s) kf[h][tb][s] = *(const u32x4_t*)(row + 32 * s + 8 * lg);
+    for (int s = 0; s < DS / 2; ++s)
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) cs2[s][j2] = rrow[(32 * s + 8 * lg) / 2 + j2];
+  }
+  // ---- (3) the ring copy: unit u is key row u / (HD/8), dims 8 (u % (HD/8)) .. + 8, and
+  // V^T dim u / 8, chunk offsets 8 (u % 8) .. + 8 ---------------------------------------------
+  u32x4_t kr[NIT], vr[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int u = tid + 64 * NW * it;
+    kr[it] = *(const u32x4_t*)(Kp + (size_t)slot_at(u / (HD / 8)) * HD + 8 * (u % (HD / 8)));
+    vr[it] = *(const u32x4_t*)(VTp + (size_t)(u >> 3) * C + slot_at(8 * (u & 7)));
+  }
+  // every load above is issued before any of the arithmetic below
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- (4) the block's own keys of step 0: RMSNorm, gain and RoPE, then bf16 (the ring's
+  // dtype); values cast to bf16 --------------------------------------------------------------
+  uint32_t sk1[EPT / 2], sk2[EPT / 2];  // packed bf16 pairs
+  uint16_t sv1[EPT], sv2[EPT];
+  auto stage = [&]() {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) ss = fmaf(bk1[j], bk1[j], fmaf(bk2[j], bk2[j], ss));
+    ss = row16_sum(ss);
+    const float sc = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int j = 0; j < EPT; j += 2) {
+      float y1[2], y2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float x1 = bk1[j + u] * sc * kg1[j + u], x2 = bk2[j + u] * sc * kg2[j + u];
+        const float cc = bcs[2 * (j + u)], sn = bcs[2 * (j + u) + 1];
+        y1[u] = x1 * cc - x2 * sn;
+        y2[u] = x2 * cc + x1 * sn;
+      }
+      sk1[j / 2] = f2bf2(y1[0], y1[1]);
+      sk2[j / 2] = f2bf2(y2[0], y2[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      sv1[j] = f2bf(bv1[j]);
+      sv2[j] = f2bf(bv2[j]);
+    }
+  };
+  auto put = [&](int64_t p) {  // the staged position into its LDS slots
+    if (p < b1) {
+      const int i = (int)(p - p0);
+#pragma unroll
+      for (int j = 0; j < EPT / 2; ++j) {
+        *(uint32_t*)(kst + i * KSTR + EPT * t16 + 2 * j) = sk1[j];
+        *(uint32_t*)(kst + i * KSTR + HALF + EPT * t16 + 2 * j) = sk2[j];
       }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int sl = slot_at(32 * h + 8 * lg);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vf[h][dt] = *(const u32x4_t*)(VTp + (size_t)(dt * 16 + li) * C + sl);
+      for (int j = 0; j < EPT; ++j) {
+        vst[(EPT * t16 + j) * VSTR + i] = sv1[j];
+        vst[(HALF + EPT * t16 + j) * VSTR + i] = sv2[j];
+      }
     }
+  };
+  if constexpr (BLK) stage();
+
+  // ---- (5) the query tile as hi/lo operand pairs: RMSNorm over the head, gain, RoPE --------
+  u32x4_t qf[DS], qfl[DS];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(x[s][j], x[s][j], ss);
+    ss += __shfl_xor(ss, 16, 64);  // the four lanes of query li, in a fixed order
+    ss += __shfl_xor(ss, 32, 64);
+    const float sq = rsqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t gw = gq[s][j >> 1];
+        x[s][j] = x[s][j] * sq * __uint_as_float((j & 1) ? (gw & 0xffff0000u) : (gw << 16));
+      }
+#pragma unroll
+    for (int s = 0; s < DS / 2; ++s)
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * j2 + u;
+          const float cc = u ? cs2[s][j2].z : cs2[s][j2].x, sn = u ? cs2[s][j2].w : cs2[s][j2].y;
+          const float x1 = x[s][j], x2 = x[s + DS / 2][j];
+          x[s][j] = x1 * cc - x2 * sn;
+          x[s + DS / 2][j] = x2 * cc + x1 * sn;
+        }
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t hp, lp;
+        split2_bf16(x[s][2 * t], x[s][2 * t + 1], hp, lp);
+        qf[s][t] = hp;
+        qfl[s][t] = lp;
+      }
   }
 
-  if (blk) {
-    // the block's own keys and values of this chunk, one wave per position as in the prep
-    // kernel: k RMSNorm, gain and RoPE, then bf16 (the ring's dtype); v cast to bf16
-    const float g1 = bf2f(knorm[act ? lane : 0]), g2 = bf2f(knorm[(act ? lane : 0) + HALF]);
-    auto stage = [&](int64_t p, float x1, float x2, float v1, float v2, float2 cs) {
-      const int i = (int)(p - p0);
-      x1 = act ? x1 : 0.f;
-      x2 = act ? x2 : 0.f;
-      const float ss = wave_sum(x1 * x1 + x2 * x2);
-      const float sc = rsqrtf(ss / (float)HD + a.eps);
-      if (act) {
-        x1 = x1 * sc * g1;
-        x2 = x2 * sc * g2;
-        kst[i * KSTR + lane] = f2bf(x1 * cs.x - x2 * cs.y);
-        kst[i * KSTR + lane + HALF] = f2bf(x2 * cs.x + x1 * cs.y);
-        vst[lane * VSTR + i] = f2bf(v1);
-        vst[(lane + HALF) * VSTR + i] = f2bf(v2);
-      }
-    };
+  // the operands are formed here, while the ring copy is in flight: the compiler may not
+  // move their loads and arithmetic past the barrier below
 #pragma unroll
-    for (int k = 0; k < SK; ++k) {
-      const int64_t p = b0 + w + 4 * k;
-      if (p < b1) stage(p, kx1[k], kx2[k], vx1[k], vx2[k], rc[k]);
-    }
-    // positions past the first 4 * SK of the chunk (blocks of more than 20 rows)
-    for (int64_t p = b0 + w + 4 * SK; p < b1; p += 4) {
-      const int r = (int)(p - e), l1 = act ? lane : 0;
-      const float* kr = qkv + (size_t)r * ldq + (size_t)(a.nq + g) * HD;
-      const float* vr = qkv + (size_t)r * ldq + (size_t)(a.nq + a.nkv + g) * HD;
-      stage(p, kr[l1], kr[l1 + HALF], vr[l1], vr[l1 + HALF], rope[(size_t)r * HALF + l1]);
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[s]), "+v"(qfl[s]));
+  if constexpr (BLK) {
+#pragma unroll
+    for (int j = 0; j < EPT / 2; ++j) asm volatile("" : "+v"(sk1[j]), "+v"(sk2[j]));
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) asm volatile("" : "+v"(sv1[j]), "+v"(sv2[j]));
+  }
+
+  // ---- (6) the ring values into LDS; in a chunk with block positions the staged values
+  // then overwrite their slots (a barrier apart) ------------------------------------------------
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int u = tid + 64 * NW * it;
+    *(u32x4_t*)(kst + (u / (HD / 8)) * KSTR + 8 * (u % (HD / 8))) = kr[it];
+    *(u32x4_t*)(vst + (u >> 3) * VSTR + 8 * (u & 7)) = vr[it];
+  }
+  __syncthreads();
+  if constexpr (BLK) {
+    put(b0 + 4 * w + lg);
+    for (int64_t pb = b0 + 4 * (w + NW); pb < b1; pb += 4 * NW) {  // long blocks
+      load_block_row(pb + lg);
+      stage();
+      put(pb + lg);
     }
     __syncthreads();
   }
-  if (!active) return;  // no barrier below: an idle wave may leave
+  if (!active) return;  // no barrier below
 
-  if (blk) {
-    // replace the ring's values at the block positions
+  // ---- (7) scores, softmax over the chunk, output -----------------------------------------
+  // Logits are carried in base 2: t = (q . k) scale log2(e), p = 2^(t - m2); the partial
+  // stores m = m2 ln(2), the chunk maximum of the natural logits.
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+  // key offsets relative to e: the query is at e + r; visible keys lie in lo..e+R-1 with
+  // |query - key| <= W, all within int range (the chunk is within W + 64 of e)
+  const int kbase = (int)(p0 - e), klo = (int)(lo - e);
+  // key fragments: the A operand row li of tile (h, tb) is chunk offset 32h + 8*(li/4) +
+  // 4*tb + li%4; value fragments: dims dt*16 + li, chunk offsets 32h + 8*lg .. + 8
+  u32x4_t kf[2][2][DS], vf[2][DT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int kk = 32 * h + 8 * (li >> 2) + 4 * tb + (li & 3);
-        const int64_t p = p0 + kk;
-        const bool inb = p >= b0 && p < b1;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const u32x4_t v = *(const u32x4_t*)(kst + kk * KSTR + 32 * s + 8 * lg);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) kf[h][tb][s][t] = inb ? v[t] : kf[h][tb][s][t];
-        }
-      }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kk = 32 * h + 8 * lg;
-      // which of the run's 8 positions are block positions: one mask per 16-bit half
-      uint32_t m[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t pa = p0 + kk + 2 * t, pb = pa + 1;
-        m[t] = ((pa >= b0 && pa < b1) ? 0x0000ffffu : 0u) | ((pb >= b0 && pb < b1) ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4_t v = *(const u32x4_t*)(vst + (dt * 16 + li) * VSTR + kk);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) vf[h][dt][t] = (v[t] & m[t]) | (vf[h][dt][t] & ~m[t]);
-      }
-    }
-  }
-
-  const float scale = 1.0f / sqrtf((float)HD);
-  for (int qt = w; qt < nqt; qt += 4) {
-    const int qv = qt * 16 + li;
-    const bool qok = qv < NQ;
-    const int r = qok ? qv / G : 0, hh = qv - r * G;
-    const int64_t qpos = e + r;
-    u32x4_t qf[DS], qfl[DS];
-    {
-      // raw q of (row r, head g*G + hh): RMSNorm over the head, gain, RoPE, hi/lo pairs
-      const float* src = qkv + (size_t)r * ldq + (size_t)(g * G + (qok ? hh : 0)) * HD;
-      float x[DS][8];
-      float ss = 0.f;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const float4 a0 = *(const float4*)(src + 32 * s + 8 * lg), a1 = *(const float4*)(src + 32 * s + 8 * lg + 4);
-        x[s][0] = a0.x; x[s][1] = a0.y; x[s][2] = a0.z; x[s][3] = a0.w;
-        x[s][4] = a1.x; x[s][5] = a1.y; x[s][6] = a1.z; x[s][7] = a1.w;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(x[s][j], x[s][j], ss);
-      }
-      ss += __shfl_xor(ss, 16, 64);  // the four lanes of query li, in a fixed order
-      ss += __shfl_xor(ss, 32, 64);
-      const float sq = rsqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const u32x4_t gq = *(const u32x4_t*)(qnorm + 32 * s + 8 * lg);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t gw = gq[j >> 1];
-          x[s][j] = x[s][j] * sq * __uint_as_float((j & 1) ? (gw & 0xffff0000u) : (gw << 16));
-        }
-      }
-      const float4* rrow = (const float4*)(rope + (size_t)r * HALF);  // two (cos, sin) per float4
-#pragma unroll
-      for (int s = 0; s < DS / 2; ++s)
-#pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-          const float4 cs2 = rrow[(32 * s + 8 * lg) / 2 + j2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int j = 2 * j2 + u;
-            const float cc = u ? cs2.z : cs2.x, sn = u ? cs2.w : cs2.y;
-            const float x1 = x[s][j], x2 = x[s + DS / 2][j];
-            x[s][j] = x1 * cc - x2 * sn;
-            x[s + DS / 2][j] = x2 * cc + x1 * sn;
-          }
-        }
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int s = 0; s < DS; ++s)
+        kf[h][tb][s] = *(const u32x4_t*)(kst + (32 * h + 8 * (li >> 2) + 4 * tb + (li & 3)) * KSTR + 32 * s + 8 * lg);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint32_t hp, lp;
-          split2_bf16(x[s][2 * t], x[s][2 * t + 1], hp, lp);
-          qf[s][t] = hp;
-          qfl[s][t] = lp;
-        }
-    }
-    // scores: element i of tile (h, tb) is position p0 + 32h + 8*lg + 4*tb + i for query li
-    float S[2][2][4];
-    float m = -INFINITY;
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int dt = 0; dt < DT; ++dt) vf[h][dt] = *(const u32x4_t*)(vst + (dt * 16 + li) * VSTR + 32 * h + 8 * lg);
+  float S[2][2][4];
+  float m = -INFINITY;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          acc = mfma_bf16(kf[h][tb][s], qf[s], acc);
-          acc = mfma_bf16(kf[h][tb][s], qfl[s], acc);
-        }
+    for (int tb = 0; tb < 2; ++tb) {
+      // element i of tile (h, tb) is chunk offset 32h + 8*lg + 4*tb + i for query li
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t kp = p0 + 32 * h + 8 * lg + 4 * tb + i;
-          const int64_t dist = qpos > kp ? qpos - kp : kp - qpos;
-          const bool vis = qok && kp >= lo && kp < hi && dist <= a.window;
-          S[h][tb][i] = vis ? acc[i] * scale : -INFINITY;
-          m = fmaxf(m, S[h][tb][i]);
-        }
+      for (int s = 0; s < DS; ++s) {
+        acc = mfma_bf16(kf[h][tb][s], qf[s], acc);
+        acc = mfma_bf16(kf[h][tb][s], qfl[s], acc);
       }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    float l = 0.f;
-    u32x4_t phi[2], plo[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {  // word t holds keys 8*lg + 2t, 2t + 1 of the half
-        float pv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 2 * t + u, tb = j >> 2, i = j & 3;
-          const float sv = S[h][tb][i];
-          pv[u] = sv == -INFINITY ? 0.f : expf(sv - m);
-          l += pv[u];
-        }
-        uint32_t hp, lp;
-        split2_bf16(pv[0], pv[1], hp, lp);
-        phi[h][t] = hp;
-        plo[h][t] = lp;
+      for (int i = 0; i < 4; ++i) {
+        const int kp = kbase + 32 * h + 8 * lg + 4 * tb + i;
+        const int dist = r > kp ? r - kp : kp - r;
+        const bool vis = qok && kp >= klo && kp < R && dist <= a.window;
+        S[h][tb][i] = vis ? acc[i] * sl2 : -INFINITY;
+        m = fmaxf(m, S[h][tb][i]);
       }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    float* dst = part + (((size_t)g * nchunks + c) * NQ + qv) * PART_STRIDE(HD);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  float l = 0.f;
+  u32x4_t phi[2], plo[2];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        o = mfma_bf16(vf[h][dt], phi[h], o);
-        o = mfma_bf16(vf[h][dt], plo[h], o);
+    for (int t = 0; t < 4; ++t) {  // word t holds keys 8*lg + 2t, 2t + 1 of the half
+      float pv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * t + u, tb = j >> 2, i = j & 3;
+        const float sv = S[h][tb][i];
+        pv[u] = sv == -INFINITY ? 0.f : exp2f(sv - m);
+        l += pv[u];
       }
-      if (qok) *(f32x4_t*)&dst[dt * 16 + 4 * lg] = o;  // dims dt*16 + 4*lg .. + 4 of query qv
+      uint32_t hp, lp;
+      split2_bf16(pv[0], pv[1], hp, lp);
+      phi[h][t] = hp;
+      plo[h][t] = lp;
     }
-    if (qok && lg == 0) {
-      dst[HD] = m;
-      dst[HD + 1] = l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  float* dst = part + (((size_t)g * nchunks + c) * NQ + qv) * PART_STRIDE(HD);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      o = mfma_bf16(vf[h][dt], phi[h], o);
+      o = mfma_bf16(vf[h][dt], plo[h], o);
     }
+    if (qok) *(f32x4_t*)&dst[dt * 16 + 4 * lg] = o;  // dims dt*16 + 4*lg .. + 4 of query qv
   }
+  if (qok && lg == 0) {
+    dst[HD] = m * 0.6931471805599453f;
+    dst[HD + 1] = l;
+  }
+}
+
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
+                                                            const float* __restrict__ qkv,
+                                                            const uint16_t* __restrict__ qnorm,
+                                                            const uint16_t* __restrict__ knorm,
+                                                            const float2* __restrict__ rope, int R, int64_t e,
+                                                            int nchunks, int tpw, float* __restrict__ part) {
+  // the chunk's keys [chunk position][hd + 8] and values transposed [dim][64 + 8]
+  __shared__ __align__(16) uint16_t kst[ATTN_CHUNK * (HD + 8)];
+  __shared__ __align__(16) uint16_t vst[HD * (ATTN_CHUNK + 8)];
+  const int64_t p0 = (attn_lo(a, e) / ATTN_CHUNK + blockIdx.x) * ATTN_CHUNK;
+  if (p0 < e + R && e < p0 + ATTN_CHUNK)
+    attn_mfma_body<HD, NW, true>(a, ring_layer, qkv, qnorm, knorm, rope, R, e, nchunks, tpw, part, kst, vst);
+  else
+    attn_mfma_body<HD, NW, false>(a, ring_layer, qkv, qnorm, knorm, rope, R, e, nchunks, tpw, part, kst, vst);
 }
 
 // ---- combine chunks in chunk order --------------------------------------------------------
@@ -620,10 +704,13 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
     if (!rope) return hipErrorInvalidValue;
     const uint16_t* rl = (const uint16_t*)ring_layer;
     const uint16_t *qn = (const uint16_t*)qnorm, *kn = (const uint16_t*)knorm;
-    if (a.hd == 128)
-      hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, part);
-    else
-      hipLaunchKernelGGL(attn_mfma_kernel<64>, grid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, part);
+    // query tiles over z work-groups of 4 or 8 waves, at most one tile per wave
+    const int nqt = (R * (a.nq / a.nkv) + 15) / 16;
+    const int z = (nqt + 7) / 8, tpw = (nqt + z - 1) / z;
+    const dim3 mgrid(nch, a.nkv, z);
+    auto* fn = a.hd == 128 ? (tpw <= 4 ? attn_mfma_kernel<128, 4> : attn_mfma_kernel<128, 8>)
+                           : (tpw <= 4 ? attn_mfma_kernel<64, 4> : attn_mfma_kernel<64, 8>);
+    hipLaunchKernelGGL(fn, mgrid, dim3(tpw <= 4 ? 256 : 512), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, tpw, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);

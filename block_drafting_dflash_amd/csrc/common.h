@@ -74,6 +74,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Sum over each 16-lane row of the wave (DPP, no LDS): quad xor 1, quad xor 2, then the
+// two quads of each half-row (mirror) and the two halves (rotate by 8). Every lane of a row
+// ends with the same bits: each step adds two values that all lanes of a group share.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x128>(v);  // row_ror 8
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
