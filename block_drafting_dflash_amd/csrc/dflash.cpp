@@ -366,7 +366,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     p.gain = gc.gain;
     p.eps = g.c.rms_eps;
     GemmPlan pl = plan;
-    pl.grid = p.ntiles;
+    pl.grid = gemm_fold(wt, gc.xsrc) ? 2 * p.ntiles : p.ntiles;  // folded: 8-column tiles
     if (norm_two) {
       // normed hi/lo operands: two tiles per work-group share the operand registers and
       // halve the operand reads from L2 (two row tiles of the gate/up pair keep one: its

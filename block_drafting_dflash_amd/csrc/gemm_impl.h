@@ -121,6 +121,7 @@ template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int ge
 template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 constexpr int gemm_chunks_ahead() {
   constexpr bool Q4 = WT == WT_Q4, BF = WT != WT_F32;
+  constexpr bool fold = WT == WT_BF16 && XSRC == XSRC_GLOBAL;  // RT counts 8-row groups
   constexpr int nit = T * NCH;
   // 4-bit argmax over hi/lo pairs: the operand pairs and group sums leave no room (measured)
   constexpr int argmax_ahead = Q4 && !SPLIT ? 3 : 1;
@@ -130,18 +131,18 @@ constexpr int gemm_chunks_ahead() {
   constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
   constexpr int raw = XSRC == XSRC_NORM ? RT * CH * 4 * 2 + CH * 4 : 0;
   constexpr int gupi = 64 / (CH * 32 * 2 / 16);  // staged rows per load instruction
-  constexpr int staged = planes * ((16 * RT + gupi - 1) / gupi) * 4 + 32;
+  constexpr int staged = planes * (((fold ? 8 : 16) * RT + gupi - 1) / gupi) * 4 + 32;
   // normed rows of a later chunk are loaded while the earlier chunks' pairs are held, unless
   // the raw rows of the wave's whole k range are staged through LDS first (then they are
   // dead before the pairs are formed)
   constexpr bool stg_n = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * 32 == 256;
   constexpr int raw_stg = ((RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS) + 1) * 4;
-  constexpr int opnd = XSRC == XSRC_GLOBAL ? (RT <= 2 ? staged : 2 * frag)
+  constexpr int opnd = XSRC == XSRC_GLOBAL ? ((fold ? 8 : 16) * RT <= 32 ? staged : 2 * frag)
                        : XSRC == XSRC_LDS  ? NCH * frag
                        : stg_n             ? (raw_stg > NCH * frag ? raw_stg : NCH * frag)
                        : NCH == 1          ? (raw > frag ? raw : frag)
                                            : NCH * frag + raw;
-  constexpr int wreg = Q4 ? NB * (CH / 4) * 6 : NB * CH * 4;
+  constexpr int wreg = Q4 ? NB * (CH / 4) * 6 : NB * (fold ? CH / 2 : CH) * 4;
   constexpr int fit = (budget - opnd - 48) / wreg;
   // a launch with more chunks than fit streams the rest: one more chunk buffer is live
   return fit >= nit ? nit : (fit - 1 < 1 ? 1 : (fit - 1 > 8 ? 8 : fit - 1));
@@ -178,35 +179,47 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   unsigned char* xs = smem + lds.xs_off + (size_t)w * lds.xs_wave;
   // staged operands: streamed rows (STG_G) of one chunk, [plane][row][CH * KSTEP] bf16; or the
   // normed raw rows (STG_N) of the wave's whole k range, [row][CH * KSTEP] f32 then the gains
-  constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RT <= 2;
+  // FOLD (bf16 weights, streamed operands): a work-group owns 8 output columns, half h of
+  // a 16-row weight block, and RT counts groups of 8 operand rows. One MFMA takes two k
+  // steps s, s+1: lanes li < 8 supply weight rows 8h + li of step s and operand rows of step
+  // s, lanes li >= 8 the same rows of step s+1, so the product's top-left 8x8 block is step
+  // s, its bottom-right block step s+1 and the rest is discarded; the finishing wave adds
+  // the two blocks (lane l and lane l + 40).
+  constexpr bool FOLD = WT == WT_BF16 && XSRC == XSRC_GLOBAL;
+  constexpr int RROWS = FOLD ? 8 : 16;      // operand rows per MFMA row group
+  constexpr int WST = FOLD ? CH / 2 : CH;   // weight loads (and products) per chunk
+  static_assert(!FOLD || CH % 2 == 0, "a folded chunk pairs its k steps");
+  constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RROWS * RT <= 32;
   constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * Tr::KSTEP == 256;
   constexpr int STG_N_ROWS = RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows a normed launch stages
   constexpr int SP = SPLIT ? 2 : 1;          // operand planes
   constexpr int LK = CH * Tr::KSTEP;          // k of one chunk
   constexpr int GU = LK * 2 / 16;             // lanes per staged bf16 row (32 or 16)
   constexpr int GUPI = 64 / GU;               // staged rows per load instruction
-  constexpr int GIMAX = (16 * RT + GUPI - 1) / GUPI;
+  constexpr int GIMAX = (RROWS * RT + GUPI - 1) / GUPI;
   static_assert(!STG_N || NCH * LK * 4 == 1024, "a normed row of the wave's k range is one wave load");
 
   // tiles past the end repeat the last one: harmless for the argmax (max is idempotent);
   // the other epilogues run with T dividing the tile count
+  const int ntl = FOLD ? 2 * p.ntiles : p.ntiles;  // tiles of 8 (FOLD) or 16 columns
   auto tile_of = [&](int t) {
     const int j = (int)blockIdx.x * T + t;
-    return j < p.ntiles ? j : p.ntiles - 1;
+    return j < ntl ? j : ntl - 1;
   };
 
   // weights of (tile, chunk) it: the fragment-major blocks of every segment
   auto load_w = [&](u32x4_t (&wb)[NB][CH], u32x2_t (&sb)[NB][CB], int it) {
     const int j = tile_of(it / NCH), c = it % NCH;
+    const int j16 = FOLD ? j >> 1 : j;  // the 16-row weight block
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       SegSel sel;
       if constexpr (EPI == EPI_ARGMAX) {  // one matrix (checked at launch)
         sel = SegSel{(const unsigned char*)p.seg[0].w, (const unsigned char*)p.seg[0].scales, j};
       } else if constexpr (NB == 1) {
-        sel = select_seg(p, 16 * j);
+        sel = select_seg(p, 16 * j16);
       } else {
-        sel = SegSel{(const unsigned char*)p.seg[nb].w, (const unsigned char*)p.seg[nb].scales, j};
+        sel = SegSel{(const unsigned char*)p.seg[nb].w, (const unsigned char*)p.seg[nb].scales, j16};
       }
       const int tj = sel.tj;
       if constexpr (Q4) {
@@ -221,6 +234,15 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           wb[nb][b] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)b * 1024));
           sb[nb][b] = __builtin_nontemporal_load((const u32x2_t*)(sr + (size_t)b * 128));
         }
+      } else if constexpr (FOLD) {
+        // half h of the 16-row blocks of steps 2*st2 + li/8: 8 rows x 8 k per 128 bytes
+        const size_t kblocks = (size_t)K / Tr::KSTEP;
+        const size_t blk0 = (size_t)w * (kw / Tr::KSTEP) + (size_t)c * CH + (li >> 3);
+        const int fl = lg * 16 + 8 * (j & 1) + (li & 7);  // the lane of that row in the block
+        const unsigned char* wr = sel.w + ((size_t)tj * kblocks + blk0) * 1024 + fl * 16;
+#pragma unroll
+        for (int st2 = 0; st2 < WST; ++st2)
+          wb[nb][st2] = __builtin_nontemporal_load((const u32x4_t*)(wr + (size_t)st2 * 2048));
       } else {
         // fragment-major weights: one contiguous kilobyte per (16-row tile, KSTEP) block
         const size_t kblocks = (size_t)K / Tr::KSTEP;
@@ -293,6 +315,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   // MFMA fragment (row tile rt, step st) of plane pl from the staged rows
   auto frag_xs = [&](int rt, int st, int pl) {
     const int r = min(rt * 16 + li, R - 1);
+    return *(const u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2);
+  };
+  // FOLD: row group rt, step pair st2 (rows rt*8 + li%8 of step 2*st2 + li/8)
+  auto frag_xs_fold = [&](int rt, int st2, int pl) {
+    const int r = min(rt * 8 + (li & 7), R - 1);
+    const int st = 2 * st2 + (li >> 3);
     return *(const u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2);
   };
 
@@ -394,6 +422,23 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
       }
       return;
     }
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int st2 = 0; st2 < WST; ++st2) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const u32x4_t xf = frag_xs_fold(rt, st2, 0);
+          u32x4_t xl = xf;
+          if constexpr (SPLIT) xl = frag_xs_fold(rt, st2, 1);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            acc[rt][nb] = mfma_bf16(xf, wb[nb][st2], acc[rt][nb]);
+            if constexpr (SPLIT) acc[rt][nb] = mfma_bf16(xl, wb[nb][st2], acc[rt][nb]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int st = 0; st < CH; ++st) {
 #pragma unroll
@@ -417,10 +462,10 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   auto load_resid = [&]() {
     if constexpr (EPI == EPI_RESID) {
       if (w < RT) {
-        const int col = 16 * tile_of(0) + li;
+        const int col = FOLD ? 8 * tile_of(0) + (li & 7) : 16 * tile_of(0) + li;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int r = min(w * 16 + 4 * lg + q, R - 1);
+          const int r = min(w * RROWS + 4 * lg + q, R - 1);
           yres[q] = ((const float*)p.y)[(size_t)r * p.ldy + col];
         }
       }
@@ -445,6 +490,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
       for (int nb = 0; nb < NB; ++nb) {
         v[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int ww = 0; ww < nw; ++ww) v[nb] += *(const f32x4_t*)&rb[((size_t)((ww * RT + rt) * NB + nb) * 64 + lane) * 4];
+        if constexpr (FOLD) {  // the odd steps: lane l + 40 holds rows 4lg + 8 + q, column li + 8
+          f32x4_t v2 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int ww = 0; ww < nw; ++ww)
+            v2 += *(const f32x4_t*)&rb[((size_t)((ww * RT + rt) * NB + nb) * 64 + ((lane + 40) & 63)) * 4];
+          v[nb] += v2;
+        }
       }
       if constexpr (XSRC == XSRC_NORM) {
 #pragma unroll
@@ -457,7 +508,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           for (int nb = 0; nb < NB; ++nb) v[nb][q] *= rs;
         }
       }
-      const int col = 16 * j + li;
+      const int col = FOLD ? 8 * j + li : 16 * j + li;
       if constexpr (EPI == EPI_ARGMAX) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -473,8 +524,8 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int r = rt * 16 + 4 * lg + q;
-          if (r >= R) continue;
+          const int r = rt * RROWS + 4 * lg + q;
+          if (r >= R || (FOLD && (li >= 8 || lg >= 2))) continue;
           const size_t o = (size_t)r * p.ldy + col;
           if constexpr (EPI == EPI_STORE) {
             ((float*)p.y)[o] = v[0][q];
@@ -731,19 +782,31 @@ template <int WT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
 static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
   static_assert(CH == 8, "plans count 8-step chunks");
   static_assert(chunk_steps(1) == 8 && chunk_steps(2) == 4 && chunk_steps(3) == 4, "chunk depth by row tiles");
-  const int rt = (p.R + 15) / 16;
-  if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
-  if constexpr (XSRC == XSRC_NORM && SPLIT) {
-    // normed hi/lo operands of two row tiles: staged raw rows over a 256-element k range
-    // per wave (at most GEMM_NORM_STAGED_ROWS rows); larger launches go through planes
-    if constexpr (NCH == 1) {
-      if (rt == 2 && p.R <= GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
+  if constexpr (WT == WT_BF16 && XSRC == XSRC_GLOBAL) {
+    // folded launches (see gemm_kernel): groups of 8 operand rows, 4-step chunks past 16 rows
+    // (their staged rows would not fit beside 8-step chunks)
+    switch ((p.R + 7) / 8) {
+      case 1: return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+      case 2: return launch_t<WT, 2, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+      case 3: return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+      case 4: return launch_t<WT, 4, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+      default: return hipErrorInvalidValue;  // bf16 launches take at most 32 rows
     }
-    return hipErrorInvalidValue;
   } else {
-    if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
-    if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
-    else return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+    const int rt = (p.R + 15) / 16;
+    if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+    if constexpr (XSRC == XSRC_NORM && SPLIT) {
+      // normed hi/lo operands of two row tiles: staged raw rows over a 256-element k range
+      // per wave (at most GEMM_NORM_STAGED_ROWS rows); larger launches go through planes
+      if constexpr (NCH == 1) {
+        if (rt == 2 && p.R <= GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
+      }
+      return hipErrorInvalidValue;
+    } else {
+      if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+      if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
+      else return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
+    }
   }
 }
 

@@ -84,15 +84,27 @@ struct GemmLds {
   size_t xs_wave;  // staged bytes per wave
   size_t total;
 };
+// bf16 weights with streamed operands run folded: an MFMA takes 8 output columns over two
+// k steps (one per half of its 16 columns) against groups of 8 operand rows, so a 16-row
+// weight block serves two work-groups (see gemm_impl.h)
+__host__ __device__ inline bool gemm_fold(int wt, int xsrc) { return wt == WT_BF16 && xsrc == XSRC_GLOBAL; }
+// MFMA row groups of R operand rows (8 rows folded, else 16) and their k steps per chunk
+__host__ __device__ inline int gemm_row_groups(int wt, int xsrc, int R) {
+  return gemm_fold(wt, xsrc) ? (R + 7) / 8 : (R + 15) / 16;
+}
+__host__ __device__ inline int gemm_chunk_steps(int wt, int xsrc, int R) {
+  return gemm_fold(wt, xsrc) ? ((R + 7) / 8 <= 2 ? 8 : 4) : chunk_steps((R + 15) / 16);
+}
 __host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, int R, int waves, int nb, int K,
                                                    int tiles_per_wg) {
-  const int rt = (R + 15) / 16, rows_pad = 16 * rt;
-  const int ch = chunk_steps(rt), kstep = wt == WT_F32 ? 16 : 32;
+  const bool fold = gemm_fold(wt, xsrc);
+  const int rt = gemm_row_groups(wt, xsrc, R), rows_pad = (fold ? 8 : 16) * rt;
+  const int ch = gemm_chunk_steps(wt, xsrc, R), kstep = wt == WT_F32 ? 16 : 32;
   const int nch = K / (waves * ch * kstep);
   const size_t red = (size_t)(tiles_per_wg > 1 ? 2 : 1) * waves * rt * nb * 1024;
   const size_t ssq = xsrc == XSRC_NORM ? (size_t)waves * rows_pad * 4 : 0;
   GemmLds l{};
-  if (wt != WT_F32 && xsrc == XSRC_GLOBAL && rt <= 2) {
+  if (wt != WT_F32 && xsrc == XSRC_GLOBAL && rows_pad <= 32) {
     l.stage = 1;
     l.row_bytes = ch * kstep * 2 + 16;
     l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
