@@ -213,7 +213,7 @@ size_t hn_rows(const Cfg& g) { return std::max<size_t>((size_t)g.R, (size_t)GEMM
 
 Layout make_layout(const Cfg& g) {
   const dflash_config& c = g.c;
-  const size_t H = c.hidden, R = g.R, ae = g.act_elt;
+  const size_t H = c.hidden, R = g.R;
   const size_t qd = (size_t)c.q_heads * c.head_dim, kvd = (size_t)c.kv_heads * c.head_dim;
   Layout L{};
   size_t o = 0;

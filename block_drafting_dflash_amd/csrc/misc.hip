@@ -6,90 +6,181 @@
 namespace dflash {
 
 // One work-group per row: the largest (value, index) key over the lm_head work-groups'
-// partial keys; the key order puts the larger logit first and then the lower index.
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const unsigned long long* __restrict__ part, int groups,
-                                                             int32_t* idx) {
-  __shared__ unsigned long long red[4];
+// partial keys; the key order puts the larger logit first and then the lower index. Each
+// thread loads its first FIN_PER keys at once (indices clamped: max is idempotent).
+constexpr int FIN_THREADS = 1024, FIN_PER = 8;
+__global__ __launch_bounds__(FIN_THREADS) void argmax_finalize_kernel(const unsigned long long* __restrict__ part,
+                                                                      int groups, int32_t* idx) {
+  __shared__ unsigned long long red[FIN_THREADS / 64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const unsigned long long* row = part + (size_t)r * groups;
+  unsigned long long k[FIN_PER];
+#pragma unroll
+  for (int i = 0; i < FIN_PER; ++i) k[i] = row[min(tid + FIN_THREADS * i, groups - 1)];
   unsigned long long best = 0ull;
-#pragma unroll 4
-  for (int g = tid; g < groups; g += 256) {
-    const unsigned long long k = row[g];
-    best = k > best ? k : best;
-  }
+#pragma unroll
+  for (int i = 0; i < FIN_PER; ++i) best = k[i] > best ? k[i] : best;
+  for (int g = tid + FIN_THREADS * FIN_PER; g < groups; g += FIN_THREADS) best = row[g] > best ? row[g] : best;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long k = shfl_xor_u64(best, o);
-    best = k > best ? k : best;
+    const unsigned long long kk = shfl_xor_u64(best, o);
+    best = kk > best ? kk : best;
   }
   if (lane == 0) red[w] = best;
   __syncthreads();
   if (tid == 0) {
     unsigned long long b = red[0];
-    for (int i = 1; i < 4; ++i) b = red[i] > b ? red[i] : b;
+    for (int i = 1; i < FIN_THREADS / 64; ++i) b = red[i] > b ? red[i] : b;
     idx[r] = argmax_key_index(b);
   }
 }
 
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(R), dim3(256), 0, s, part, groups, idx);
+  if (groups < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_finalize_kernel, dim3(R), dim3(FIN_THREADS), 0, s, part, groups, idx);
   return hipGetLastError();
 }
 
 // Block rows [anchor, mask x (R-1)] from the target's raw embedding table (not the
-// embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows.
-// The draft's first kernel also tabulates the rotary rotation of every block position
-// pos0 + r, (cos, sin) of (pos0 + r) * theta^(-2i/hd) for i < hd/2, evaluated in f64 and
-// rounded to f32 as the per-element RoPE of the prep kernel does; every layer's attention
-// reads it (rope may be NULL).
-template <bool BF>
-__global__ void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
-                             float2* rope, int64_t pos0, float theta, int hd) {
+// embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows: work-group
+// (r, 0) gathers row r, with 16-byte loads when the table is 16-byte aligned (every row
+// then is: hidden is a multiple of 16). The draft's first kernel also tabulates the rotary
+// rotation of every block position pos0 + r in work-group (r, 1): (cos, sin) of (pos0 + r) *
+// theta^(-2i/hd) for i < hd/2, evaluated in f64 and rounded to f32 as the per-element RoPE
+// of the prep kernel does; every layer's attention reads it (rope may be NULL).
+template <bool BF, bool VEC>
+__global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id,
+                                                    float* x, float2* rope, int64_t pos0, float theta, int hd) {
   const int r = blockIdx.x;
-  const int64_t tok = r == 0 ? anchor : mask_id;
-  for (int i = threadIdx.x; i < hidden; i += blockDim.x) x[(size_t)r * hidden + i] = act_ld<BF>(table, tok * hidden + i);
-  if (rope)
+  if (blockIdx.y == 1) {
     for (int i = threadIdx.x; i < hd / 2; i += blockDim.x) {
       const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
       double sn, cs;
       sincos((double)(pos0 + r) * inv, &sn, &cs);
       rope[(size_t)r * (hd / 2) + i] = make_float2((float)cs, (float)sn);
     }
+    return;
+  }
+  const int64_t tok = r == 0 ? anchor : mask_id;
+  float* xr = x + (size_t)r * hidden;
+  if constexpr (VEC) {
+    constexpr int EPV = BF ? 8 : 4;  // elements per 16-byte load
+    constexpr int U = 4;             // loads in flight per thread
+    const int nv = hidden / EPV;
+    const u32x4_t* src = (const u32x4_t*)table + (size_t)tok * nv;
+    for (int v0 = threadIdx.x; v0 < nv; v0 += 256 * U) {
+      u32x4_t t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = src[min(v0 + 256 * u, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + 256 * u;
+        if (v >= nv) break;
+        if constexpr (BF) {
+          float4* d = (float4*)(xr + (size_t)v * 8);
+          d[0] = make_float4(__uint_as_float(t[u][0] << 16), __uint_as_float(t[u][0] & 0xffff0000u),
+                             __uint_as_float(t[u][1] << 16), __uint_as_float(t[u][1] & 0xffff0000u));
+          d[1] = make_float4(__uint_as_float(t[u][2] << 16), __uint_as_float(t[u][2] & 0xffff0000u),
+                             __uint_as_float(t[u][3] << 16), __uint_as_float(t[u][3] & 0xffff0000u));
+        } else {
+          *(u32x4_t*)(xr + (size_t)v * 4) = t[u];
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < hidden; i += blockDim.x) xr[i] = act_ld<BF>(table, tok * hidden + i);
+  }
 }
 
 hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
                         float2* rope, int64_t pos0, float theta, int hd, hipStream_t s) {
-  if (bf)
-    hipLaunchKernelGGL(embed_kernel<true>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x, rope, pos0,
+  const bool vec = ((uintptr_t)table & 15u) == 0 && hidden % 8 == 0;
+  const dim3 grid(R, rope ? 2 : 1);
+  if (bf && vec)
+    hipLaunchKernelGGL((embed_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope, pos0,
                        theta, hd);
+  else if (bf)
+    hipLaunchKernelGGL((embed_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
+                       pos0, theta, hd);
+  else if (vec)
+    hipLaunchKernelGGL((embed_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
+                       pos0, theta, hd);
   else
-    hipLaunchKernelGGL(embed_kernel<false>, dim3(R), dim3(256), 0, s, table, hidden, anchor, mask_id, R, x, rope,
+    hipLaunchKernelGGL((embed_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
                        pos0, theta, hd);
   return hipGetLastError();
 }
 
 // out[r] = RMSNorm(in[r]) * g as a GEMM operand (hi/lo bf16 planes for bf16 shapes, f32
-// otherwise); one 256-thread group per row. The sum of squares is accumulated per lane in
-// a fixed stride, then reduced wave by wave in order.
+// otherwise); one 256-thread group per row. Each thread holds its first RN_V groups of four
+// values in registers (rows up to 4096 wide: one read), accumulates their squares, and the
+// wave sums are added in wave order.
+constexpr int RN_V = 4;
 template <bool BF>
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ in, const void* gain, float eps, int H,
                                                       void* out, void* out_lo) {
   __shared__ float part[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* x = in + (size_t)r * H;
+  const int nv = H / 4;  // H is a multiple of 16
+  const float4* x = (const float4*)(in + (size_t)r * H);
+  float4 xv[RN_V];
+  float gv[RN_V][4];
+  auto load_gain = [&](int v, float (&g)[4]) {
+    if constexpr (BF) {
+      const uint2 gw = *((const uint2*)gain + v);
+      g[0] = __uint_as_float(gw.x << 16); g[1] = __uint_as_float(gw.x & 0xffff0000u);
+      g[2] = __uint_as_float(gw.y << 16); g[3] = __uint_as_float(gw.y & 0xffff0000u);
+    } else {
+      const float4 gf = *((const float4*)gain + v);
+      g[0] = gf.x; g[1] = gf.y; g[2] = gf.z; g[3] = gf.w;
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j) {
+    const int v = min(tid + 256 * j, nv - 1);
+    xv[j] = x[v];
+    load_gain(v, gv[j]);
+  }
   float ss = 0.f;
-  for (int k = tid; k < H; k += 256) ss = fmaf(x[k], x[k], ss);
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j)
+    if (tid + 256 * j < nv)
+      ss = fmaf(xv[j].w, xv[j].w, fmaf(xv[j].z, xv[j].z, fmaf(xv[j].y, xv[j].y, fmaf(xv[j].x, xv[j].x, ss))));
+  for (int v = tid + 256 * RN_V; v < nv; v += 256) {
+    const float4 a = x[v];
+    ss = fmaf(a.w, a.w, fmaf(a.z, a.z, fmaf(a.y, a.y, fmaf(a.x, a.x, ss))));
+  }
   ss = wave_sum(ss);
   if (lane == 0) part[w] = ss;
   __syncthreads();
   const float tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float s = rsqrtf(tot / (float)H + eps);
-  for (int k = tid; k < H; k += 256) op_st<BF>(out, out_lo, (size_t)r * H + k, x[k] * s * act_ld<BF>(gain, k));
+  auto put = [&](int v, const float4 a, const float (&g)[4]) {
+    const float y[4] = {a.x * s * g[0], a.y * s * g[1], a.z * s * g[2], a.w * s * g[3]};
+    const size_t o = (size_t)r * H + 4 * (size_t)v;
+    if constexpr (BF) {
+      uint32_t h0, l0, h1, l1;
+      split2_bf16(y[0], y[1], h0, l0);
+      split2_bf16(y[2], y[3], h1, l1);
+      *(uint2*)((uint16_t*)out + o) = make_uint2(h0, h1);
+      *(uint2*)((uint16_t*)out_lo + o) = make_uint2(l0, l1);
+    } else {
+      *(float4*)((float*)out + o) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < RN_V; ++j)
+    if (tid + 256 * j < nv) put(tid + 256 * j, xv[j], gv[j]);
+  for (int v = tid + 256 * RN_V; v < nv; v += 256) {
+    float g[4];
+    load_gain(v, g);
+    put(v, x[v], g);
+  }
 }
 
 hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, int R, int H, void* out,
                           void* out_lo, hipStream_t s) {
+  if (H % 16) return hipErrorInvalidValue;
   if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
   else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
   return hipGetLastError();
