@@ -108,12 +108,17 @@ template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int ge
   return NCH == 1 ? 4 : 2;
 }
 
-// Weight chunks a wave issues before its first product. The layer GEMMs put every chunk of
-// the launch in flight at once (a launch is one round trip, not a pipeline) as far as the
-// registers beside the operands allow: streamed operands staged through LDS hold one chunk
-// of compact rows plus the fragments read back; unstaged streamed operands two chunks of
-// fragments; staged (LDS-source) operands every chunk; normed operands their raw rows while
-// the pairs are formed; and about 48 registers go to accumulators, addresses and sums. The
+// Weight chunks a wave issues before its first product. The layer GEMMs with streamed
+// operands put every chunk of the launch in flight at once (a launch is one round trip, not
+// a pipeline) as far as the registers beside the operands allow: streamed operands staged
+// through LDS hold one chunk of compact rows plus the fragments read back; unstaged
+// streamed operands two chunks of fragments; staged (LDS-source) operands every chunk; and
+// about 48 registers go to accumulators, addresses and sums; normed operands of two row
+// tiles hold their raw rows while the pairs are formed. Normed operands of one row tile
+// issue one chunk, form their pairs, then issue the rest: a wave stalls while the memory
+// pipeline refuses its loads, and with every chunk issued first the norm prologue waited
+// behind that stall (gate/up 13.2 -> 12.5 us, QKV 8.6 -> 8.4 us at 5 rows; two row tiles,
+// whose prologue is longer, measured slower that way). The
 // vocabulary argmax keeps shallow look-ahead: it runs thousands of work-groups, several per
 // CU, which keep the stream busy between them (three chunks for 4-bit single-plane rows,
 // whose chunks carry a quarter of the bytes). f32 weights (the exact-arithmetic shapes)
@@ -126,6 +131,7 @@ constexpr int gemm_chunks_ahead() {
   // 4-bit argmax over hi/lo pairs: the operand pairs and group sums leave no room (measured)
   constexpr int argmax_ahead = Q4 && !SPLIT ? 3 : 1;
   if (EPI == EPI_ARGMAX || !BF) return nit < argmax_ahead ? nit : argmax_ahead;
+  if (XSRC == XSRC_NORM && RT == 1) return 1;
   constexpr int budget = 512 / gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>();
   constexpr int planes = SPLIT ? 2 : 1;
   constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
@@ -135,8 +141,8 @@ constexpr int gemm_chunks_ahead() {
   // normed rows of a later chunk are loaded while the earlier chunks' pairs are held, unless
   // the raw rows of the wave's whole k range are staged through LDS first (then they are
   // dead before the pairs are formed)
-  constexpr bool stg_n = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * 32 == 256;
-  constexpr int raw_stg = ((RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS) + 1) * 4;
+  constexpr bool stg_n = XSRC == XSRC_NORM && RT <= 2 && NCH * CH * 32 == 256;
+  constexpr int raw_stg = (GEMM_NORM_STAGED_ROWS + 1) * 4;
   constexpr int opnd = XSRC == XSRC_GLOBAL ? ((fold ? 8 : 16) * RT <= 32 ? staged : 2 * frag)
                        : XSRC == XSRC_LDS  ? NCH * frag
                        : stg_n             ? (raw_stg > NCH * frag ? raw_stg : NCH * frag)
