@@ -118,9 +118,9 @@ template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int ge
 // issue one chunk, form their pairs, then issue the rest: a wave stalls while the memory
 // pipeline refuses its loads, and with every chunk issued first the norm prologue waited
 // behind that stall (gate/up 13.2 -> 12.5 us, QKV 8.6 -> 8.4 us at 5 rows; two row tiles,
-// whose prologue is longer, measured slower that way). Folded launches also keep one chunk
-// ahead, so that staging a chunk's operand rows does not wait behind the whole stream (O
-// 7.2 -> 6.9 us, down 8.9 -> 8.4 us at 5 rows). The
+// whose prologue is longer, measured slower that way). Streamed operands (folded bf16 and
+// 4-bit) also keep one chunk ahead, so that staging a chunk's operand rows does not wait
+// behind the whole stream (bf16 O 7.2 -> 6.9 us, down 8.9 -> 8.4 us at 5 rows). The
 // vocabulary argmax keeps shallow look-ahead: it runs thousands of work-groups, several per
 // CU, which keep the stream busy between them (three chunks for 4-bit single-plane rows,
 // whose chunks carry a quarter of the bytes). f32 weights (the exact-arithmetic shapes)
@@ -133,7 +133,7 @@ constexpr int gemm_chunks_ahead() {
   // 4-bit argmax over hi/lo pairs: the operand pairs and group sums leave no room (measured)
   constexpr int argmax_ahead = Q4 && !SPLIT ? 3 : 1;
   if (EPI == EPI_ARGMAX || !BF) return nit < argmax_ahead ? nit : argmax_ahead;
-  if ((XSRC == XSRC_NORM && RT == 1) || fold) return 1;
+  if ((XSRC == XSRC_NORM && RT == 1) || XSRC == XSRC_GLOBAL) return 1;
   constexpr int budget = 512 / gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>();
   constexpr int planes = SPLIT ? 2 : 1;
   constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
