@@ -174,13 +174,19 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, 1000 * (tag + 1) + r) for r in range(n)]))
     resid = resid.to(torch.bfloat16).to(dev)
     u = torch.from_numpy(np.stack([synth.accept_draws(B, r, tag) for r in range(n)])).to(dev)  # f64 [n, 3, B+1]
+    V = sh.vocab
+    # the stand-in target's draws that do not depend on the draft, made before timing: accept
+    # flags, the offset of a rejected row's token, and the bonus row's token
+    acc = u[:, 0, :B] < p
+    off = (1 + torch.floor(u[:, 1, :B] * (V - 1))).int()
+    tgt_all = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+    tgt_all[:, B] = (torch.floor(u[:, 2, B] * V) % V).int()
+    other = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty(B, dtype=torch.int32, device=dev)
-    tgt = torch.empty(B + 1, dtype=torch.int32, device=dev)
     vout = torch.empty(3, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     anchor = synth.anchor_token(sh, tag=tag)
-    V = sh.vocab
     ks = []
     torch.cuda.synchronize()
     t0 = None
@@ -192,11 +198,12 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         if e: e[0].record(stream)
         g.draft_block(anchor, B, tokens=toks)
         if e: e[1].record(stream)
-        # stand-in for the target's verify-row argmaxes (the target model is out of scope)
-        d = toks.long()
-        other = (d + 1 + torch.floor(u[r, 1, :B] * (V - 1)).long()) % V
-        tgt[:B] = torch.where(u[r, 0, :B] < p, d, other).int()
-        tgt[B] = torch.floor(u[r, 2, B] * V).int() % V
+        # stand-in for the target's verify-row argmaxes (the target model is out of scope):
+        # row i keeps the draft token with probability p, else (token + offset) mod V
+        tgt = tgt_all[r]
+        torch.add(toks, off[r], out=other)
+        torch.remainder(other, V, out=other)
+        torch.where(acc[r], toks, other, out=tgt[:B])
         g.verify_greedy(toks, tgt, B, out=vout)
         if e: e[2].record(stream)
         g.cache_append(resid[r])
