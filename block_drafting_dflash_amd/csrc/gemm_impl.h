@@ -19,8 +19,9 @@
 // prologue y = x * rsqrt(mean(x^2) + eps) * g. With bf16 weights an f32 activation enters
 // as a bf16 pair hi + lo and costs two MFMA products (SPLIT); activations given in bf16
 // (the residual slab, verify rows) take one. Epilogues: store,
-// residual add, SwiGLU, and the fused lm_head argmax, which reduces (value, index) keys
-// with wavefront shuffles and stores one key per row and work-group; a finalize kernel
+// residual add, SwiGLU, and the fused lm_head argmax, which keeps each lane's best
+// (value, index) key over the work-group's tiles, reduces a row's 16 lanes with wavefront
+// shuffles once at the end and stores one key per row and work-group; a finalize kernel
 // reduces those (no fence or atomic in the streaming kernel: a device-scope fence per
 // work-group cost a third of the lm_head's time).
 #pragma once
@@ -518,15 +519,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
       }
       const int col = FOLD ? 8 * j + li : 16 * j + li;
       if constexpr (EPI == EPI_ARGMAX) {
+        // each lane keeps the best key of its own columns over the tiles; the 16 columns of
+        // a row are reduced once, after the last tile (max is exact and order-free)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rt * 16 + 4 * lg + q;
-          unsigned long long key = (r < R) ? argmax_key(v[0][q], col) : 0ull;
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) {
-            unsigned long long other = shfl_xor_u64(key, o);
-            key = other > key ? other : key;
-          }
+          const unsigned long long key = (r < R) ? argmax_key(v[0][q], col) : 0ull;
           best[q] = key > best[q] ? key : best[q];
         }
       } else {
@@ -758,11 +756,21 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   }
 
   if constexpr (EPI == EPI_ARGMAX) {
-    if (w < RT && li == 0) {
+    if (w < RT) {  // the finishing wave of row tile w: its 16 columns per row, then one key
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = w * 16 + 4 * lg + q;
-        if (r < R) p.part[(size_t)r * gridDim.x + blockIdx.x] = best[q];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = shfl_xor_u64(best[q], o);
+          best[q] = other > best[q] ? other : best[q];
+        }
+      }
+      if (li == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = w * 16 + 4 * lg + q;
+          if (r < R) p.part[(size_t)r * gridDim.x + blockIdx.x] = best[q];
+        }
       }
     }
   }
