@@ -279,7 +279,7 @@ __device__ __forceinline__ void st_u16(uint16_t* p, const uint16_t (&v)[N]) {
 // output product, and the matching V^T run is one 16-byte read. Q (an f32 activation) and
 // P (in [0, 1]) enter as bf16 pairs hi + lo, about 16 significant bits; K and V are bf16
 // already, products are exact and sums f32. The launch splits the query tiles over
-// gridDim.z work-groups of at most 8 waves, so no wave runs two tiles in turn.
+// gridDim.z work-groups of 4 waves, so no wave runs two tiles in turn.
 //
 // The kernel also does what the prep kernel does for the block rows. A query fragment holds
 // dims 32s + 8lg .. + 8 of one query, so the lane's four lanes lg together hold the whole
@@ -291,7 +291,7 @@ __device__ __forceinline__ void st_u16(uint16_t* p, const uint16_t (&v)[N]) {
 //
 // Loads retire in issue order: the raw block rows go out first, then the wave's query tile,
 // then the ring copy, so the staging and the query arithmetic overlap the copy's fetch.
-// NW waves per work-group (4 or 8: the chunk copy divides evenly); BLK: the chunk holds block
+// NW waves per work-group (the chunk copy divides evenly over them); BLK: the chunk holds block
 // positions. Every load is issued without a branch, so that each wait before the arithmetic
 // covers only the loads it needs.
 template <int HD, int NW, bool BLK>
@@ -704,13 +704,13 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
     if (!rope) return hipErrorInvalidValue;
     const uint16_t* rl = (const uint16_t*)ring_layer;
     const uint16_t *qn = (const uint16_t*)qnorm, *kn = (const uint16_t*)knorm;
-    // query tiles over z work-groups of 4 or 8 waves, at most one tile per wave
+    // query tiles over z work-groups of 4 waves, at most one tile per wave: two such
+    // work-groups fit a CU, where an 8-wave one (150 registers) leaves room for no second
     const int nqt = (R * (a.nq / a.nkv) + 15) / 16;
-    const int z = (nqt + 7) / 8, tpw = (nqt + z - 1) / z;
+    const int z = (nqt + 3) / 4, tpw = (nqt + z - 1) / z;
     const dim3 mgrid(nch, a.nkv, z);
-    auto* fn = a.hd == 128 ? (tpw <= 4 ? attn_mfma_kernel<128, 4> : attn_mfma_kernel<128, 8>)
-                           : (tpw <= 4 ? attn_mfma_kernel<64, 4> : attn_mfma_kernel<64, 8>);
-    hipLaunchKernelGGL(fn, mgrid, dim3(tpw <= 4 ? 256 : 512), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, tpw, part);
+    auto* fn = a.hd == 128 ? attn_mfma_kernel<128, 4> : attn_mfma_kernel<64, 4>;
+    hipLaunchKernelGGL(fn, mgrid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, tpw, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
