@@ -109,14 +109,14 @@ def run_gpu(args):
             t_start = time.perf_counter()
         e = ev[r - args.warmup] if r >= args.warmup else None
         if e: e[0].record(stream)
-        g.draft_block(anchor, B, tokens=toks)
+        g.draft_block(anchor, B, tokens=toks, stream=stream)
         if e: e[1].record(stream)
         if e: g.time_next_argmax(*evk[r - args.warmup])
-        g.lm_head_argmax(vrows[r], out=a)
+        g.lm_head_argmax(vrows[r], out=a, stream=stream)
         if e: e[2].record(stream)
-        g.verify_greedy(toks, a, B, out=vout)
+        g.verify_greedy(toks, a, B, out=vout, stream=stream)
         if e: e[3].record(stream)
-        g.cache_append(resid[r])
+        g.cache_append(resid[r], stream=stream)
         if e: e[4].record(stream)
         host.copy_(vout, non_blocking=True)
         stream.synchronize()
@@ -196,7 +196,7 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
             t0 = time.perf_counter()
         e = ev[r - warmup] if r >= warmup else None
         if e: e[0].record(stream)
-        g.draft_block(anchor, B, tokens=toks)
+        g.draft_block(anchor, B, tokens=toks, stream=stream)
         if e: e[1].record(stream)
         # stand-in for the target's verify-row argmaxes (the target model is out of scope):
         # row i keeps the draft token with probability p, else (token + offset) mod V
@@ -204,9 +204,9 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         torch.add(toks, off[r], out=other)
         torch.remainder(other, V, out=other)
         torch.where(acc[r], toks, other, out=tgt[:B])
-        g.verify_greedy(toks, tgt, B, out=vout)
+        g.verify_greedy(toks, tgt, B, out=vout, stream=stream)
         if e: e[2].record(stream)
-        g.cache_append(resid[r])
+        g.cache_append(resid[r], stream=stream)
         if e: e[3].record(stream)
         host.copy_(vout, non_blocking=True)
         stream.synchronize()
