@@ -93,6 +93,7 @@ def run_gpu(args):
     a = torch.empty(B + 1, dtype=torch.int32, device=dev)
     vout = torch.empty(3, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    done = torch.cuda.Event()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     # events around the argmax kernel alone (the library records them on the call's stream)
     evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -119,7 +120,9 @@ def run_gpu(args):
         g.cache_append(resid[r], stream=stream)
         if e: e[4].record(stream)
         host.copy_(vout, non_blocking=True)
-        stream.synchronize()
+        done.record(stream)
+        while not done.query():  # spin: the round's one host round trip, without a blocking wait
+            pass
         k, bonus, status = host.tolist()
         assert status == 0
         g.cache_trim(B - k)
@@ -185,6 +188,7 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     toks = torch.empty(B, dtype=torch.int32, device=dev)
     vout = torch.empty(3, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    done = torch.cuda.Event()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     anchor = synth.anchor_token(sh, tag=tag)
     ks = []
@@ -209,7 +213,9 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         g.cache_append(resid[r], stream=stream)
         if e: e[3].record(stream)
         host.copy_(vout, non_blocking=True)
-        stream.synchronize()
+        done.record(stream)
+        while not done.query():  # spin: the round's one host round trip, without a blocking wait
+            pass
         k, bonus, status = host.tolist()
         assert status == 0
         g.cache_trim(B - k)
