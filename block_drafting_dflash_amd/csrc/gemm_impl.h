@@ -291,7 +291,11 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 
   // STG_G: the R rows of each plane for chunk it, GU lanes of 16 bytes per row, rows past
   // R-1 repeating row R-1 in the last instruction; then stored to the staging slot
-  u32x4_t xc[STG_G ? SP : 1][STG_G ? GIMAX : 1];
+  // XCD chunks of operand rows in flight: with one row group, every chunk of a short launch
+  // up front and a ring of three ahead for longer ones (one chunk ahead made each chunk's
+  // staging wait a round trip); more row groups have no registers to spare
+  constexpr int XCD = STG_G && RT == 1 ? (NIT < 3 ? NIT : 3) : 1;
+  u32x4_t xc[XCD][STG_G ? SP : 1][STG_G ? GIMAX : 1];
   const int gipp = (R + GUPI - 1) / GUPI;  // load instructions per plane
   auto load_xc = [&](int it) {
     if constexpr (STG_G) {
@@ -304,11 +308,11 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           if (i < gipp) {
             const int r = min(i * GUPI + lane / GU, R - 1);
             const unsigned char* src = (const unsigned char*)(pl ? p.xlo : p.x);
-            xc[pl][i] = *(const u32x4_t*)(src + ((size_t)r * p.ldx + k0) * 2 + piece * 16);
+            xc[it % XCD][pl][i] = *(const u32x4_t*)(src + ((size_t)r * p.ldx + k0) * 2 + piece * 16);
           }
     }
   };
-  auto stage_xc = [&]() {
+  auto stage_xc = [&](int it) {
     if constexpr (STG_G) {
       const int piece = lane % GU;
 #pragma unroll
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
         for (int i = 0; i < GIMAX; ++i)
           if (i < gipp) {
             const int r = min(i * GUPI + lane / GU, R - 1);
-            *(u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + piece * 16) = xc[pl][i];
+            *(u32x4_t*)(xs + ((size_t)pl * R + r) * lds.row_bytes + piece * 16) = xc[it % XCD][pl][i];
           }
     }
   };
@@ -602,7 +606,8 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
     }
   };
   if constexpr (STG_G) {
-    load_xc(0);
+#pragma unroll
+    for (int c = 0; c < XCD; ++c) load_xc(c);
   } else if constexpr (XSRC == XSRC_GLOBAL) {
     load_x(xbuf[0], xlbuf[0], 0);
   } else if constexpr (STG_N) {
@@ -744,10 +749,10 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   for (int it = 0; it < NIT; ++it) {
     if (it + PDW - 1 < NIT) load_w(wbuf[(it + PDW - 1) % PDW], sbuf[(it + PDW - 1) % PDW], it + PDW - 1);
     if constexpr (STG_G) {
-      // this chunk's rows into the staging slot, then the next chunk's loads into the
+      // this chunk's rows into the staging slot, then a later chunk's loads into the
       // registers they free (behind the weights in flight)
-      stage_xc();
-      if (it + 1 < NIT) load_xc(it + 1);
+      stage_xc(it);
+      if (it + XCD < NIT) load_xc(it + XCD);
     } else if constexpr (XSRC == XSRC_GLOBAL) {
       if (it + 1 < NIT) load_x(xbuf[(it + 1) & 1], xlbuf[(it + 1) & 1], it + 1);
     }
