@@ -88,7 +88,102 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(AttnShape a, const float
   }
 }
 
-// ---- context K/V into the ring ----------------------------------------------------------
+// ---- one key row, 16 lanes per row ------------------------------------------------------
+// Lane t16 of a 16-lane row holds dims EPT t16 .. + EPT (k1) and their rotate-half
+// partners (k2), the gains of those dims and their (cos, sin) pairs. RMSNorm over the head
+// (each lane's squares in dim order, then the 16 lanes' sums in a fixed order), gain, RoPE,
+// then bf16 pairs. The attention's own block rows and the ring write of appended rows both
+// form keys here, so a key has the same bits whichever of them wrote it.
+template <int HD>
+__device__ __forceinline__ void form_key16(const float (&k1)[HD / 32], const float (&k2)[HD / 32],
+                                           const float (&g1)[HD / 32], const float (&g2)[HD / 32],
+                                           const float (&cs)[HD / 16], float eps, uint32_t (&o1)[HD / 64],
+                                           uint32_t (&o2)[HD / 64]) {
+  constexpr int EPT = HD / 32;
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) ss = fmaf(k1[j], k1[j], fmaf(k2[j], k2[j], ss));
+  ss = row16_sum(ss);
+  const float sc = rsqrtf(ss / (float)HD + eps);
+#pragma unroll
+  for (int j = 0; j < EPT; j += 2) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float x1 = k1[j + u] * sc * g1[j + u], x2 = k2[j + u] * sc * g2[j + u];
+      const float cc = cs[2 * (j + u)], sn = cs[2 * (j + u) + 1];
+      y1[u] = fmaf(x1, cc, -(x2 * sn));
+      y2[u] = fmaf(x2, cc, x1 * sn);
+    }
+    o1[j / 2] = f2bf2(y1[0], y1[1]);
+    o2[j / 2] = f2bf2(y2[0], y2[1]);
+  }
+}
+
+// ---- context K/V into the ring, bf16 shapes with head dim 64 or 128 -----------------------
+// kv: f32 [n, L, 2, nkv, hd] (k then v per layer). Work-group (row r, y): 16 lanes per
+// (layer, kv head) item 16 y .. 16 y + 15 of the row, in the lane layout of form_key16. The
+// items' loads are issued first; the row's rotary pairs are computed meanwhile into LDS (as
+// the embedding kernel's table computes them).
+template <int HD>
+__global__ __launch_bounds__(256) void ring_write16_kernel(AttnShape a, const float* __restrict__ kv,
+                                                           const void* const* knorms, int64_t pos0,
+                                                           uint16_t* ring) {
+  constexpr int HALF = HD / 2, EPT = HD / 32;
+  __shared__ float2 rot[HALF];
+  const int r = blockIdx.x;
+  const int64_t pos = pos0 + r;
+  const int t16 = threadIdx.x & 15;
+  const int per_row = a.L * a.nkv;
+  const int item = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int it = item < per_row ? item : per_row - 1;  // a whole 16-lane row shares its item
+  const int l = it / a.nkv, h = it - l * a.nkv;
+  const float* kr = kv + (((size_t)(r * a.L + l) * 2) * a.nkv + h) * HD + EPT * t16;
+  const float* vr = kr + (size_t)a.nkv * HD;
+  const uint16_t* g = (const uint16_t*)knorms[l] + EPT * t16;
+  float k1[EPT], k2[EPT], v1[EPT], v2[EPT], g1[EPT], g2[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    k1[j] = kr[j];
+    k2[j] = kr[HALF + j];
+    v1[j] = vr[j];
+    v2[j] = vr[HALF + j];
+    g1[j] = bf2f(g[j]);
+    g2[j] = bf2f(g[HALF + j]);
+  }
+  for (int i = threadIdx.x; i < HALF; i += blockDim.x) {
+    const double inv = pow((double)a.theta, -2.0 * (double)i / (double)HD);
+    double sn, c;
+    sincos((double)pos * inv, &sn, &c);
+    rot[i] = make_float2((float)c, (float)sn);
+  }
+  __syncthreads();
+  float cs[2 * EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const float2 v = rot[EPT * t16 + j];
+    cs[2 * j] = v.x;
+    cs[2 * j + 1] = v.y;
+  }
+  uint32_t o1[EPT / 2], o2[EPT / 2];
+  form_key16<HD>(k1, k2, g1, g2, cs, a.eps, o1, o2);
+  if (item >= per_row) return;
+  const size_t slot = (size_t)ring_slot(a, pos);
+  uint16_t* K = ring + (((size_t)l * 2) * a.nkv + h) * (size_t)a.cap * HD + slot * HD + EPT * t16;
+  uint16_t* VT = ring + (((size_t)l * 2 + 1) * a.nkv + h) * (size_t)a.cap * HD + slot;
+#pragma unroll
+  for (int j = 0; j < EPT / 2; ++j) {
+    *(uint32_t*)(K + 2 * j) = o1[j];
+    *(uint32_t*)(K + HALF + 2 * j) = o2[j];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    VT[(size_t)(EPT * t16 + j) * a.cap] = f2bf(v1[j]);
+    VT[(size_t)(HALF + EPT * t16 + j) * a.cap] = f2bf(v2[j]);
+  }
+}
+
+// ---- context K/V into the ring, other shapes --------------------------------------------
 // kv: f32 [n, L, 2, nkv, hd] (k then v per layer). One wave per (row, layer, kv slot).
 // ring: act, per layer K [nkv][Cs][hd] then V^T [nkv][hd][Cs].
 template <bool BF>
@@ -295,11 +390,12 @@ __device__ __forceinline__ void st_u16(uint16_t* p, const uint16_t (&v)[N]) {
 // positions. Every load is issued without a branch, so that each wait before the arithmetic
 // covers only the loads it needs.
 template <int HD, int NW, bool BLK>
-__device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_t* __restrict__ ring_layer,
+__device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* ring_layer,
                                                const float* __restrict__ qkv, const uint16_t* __restrict__ qnorm,
                                                const uint16_t* __restrict__ knorm, const float2* __restrict__ rope,
-                                               int R, int64_t e, int nchunks, int tpw, float* __restrict__ part,
-                                               uint16_t* __restrict__ kst, uint16_t* __restrict__ vst) {
+                                               int R, int n, int64_t e, int nchunks, int tpw,
+                                               float* __restrict__ part, uint16_t* __restrict__ kst,
+                                               uint16_t* __restrict__ vst) {
   constexpr int KC = ATTN_CHUNK;  // 64 positions = two halves of 32
   constexpr int DS = HD / 32, DT = HD / 16, HALF = HD / 2;
   constexpr int KSTR = HD + 8;      // LDS key row stride (elements)
@@ -319,8 +415,12 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_
   const int64_t p0 = (lo / KC + c) * KC;
   const int C = a.cap;
   const size_t ldq = (size_t)(a.nq + 2 * a.nkv) * HD;  // raw projection row
-  // block positions of this chunk: b0 .. b1-1 (non-empty when BLK)
-  const int64_t b0 = p0 > e ? p0 : e, b1 = p0 + KC < hi ? p0 + KC : hi;
+  // positions formed from the raw projections: the n committed rows e-n..e-1 (projection
+  // rows R..R+n-1, also written into their ring slots here) and the block e..e+R-1 (rows
+  // 0..R-1); this chunk's share b0 .. b1-1 (non-empty when BLK)
+  const int64_t bs = e - n;
+  const int64_t b0 = p0 > bs ? p0 : bs, b1 = p0 + KC < hi ? p0 + KC : hi;
+  auto row_of = [&](int64_t p) { return p >= e ? (int)(p - e) : R + (int)(p - bs); };
   const uint16_t* Kp = ring_layer + (size_t)g * C * HD;
   const uint16_t* VTp = ring_layer + (size_t)(a.nkv + g) * HD * C;
   // slot of the chunk's first position: a multiple of 8 (p0, phase and Cs are), so the
@@ -335,7 +435,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_
   const int t16 = lane & 15;
   float bk1[EPT], bk2[EPT], bv1[EPT], bv2[EPT], bcs[2 * EPT], kg1[EPT], kg2[EPT];
   auto load_block_row = [&](int64_t p) {
-    const int rr = (int)((p < b1 ? p : b1 - 1) - e);
+    const int rr = row_of(p < b1 ? p : b1 - 1);
     const float* kr = qkv + (size_t)rr * ldq + (size_t)(a.nq + g) * HD + EPT * t16;
     const float* vr = qkv + (size_t)rr * ldq + (size_t)(a.nq + a.nkv + g) * HD + EPT * t16;
     ld_f32<EPT>(kr, bk1);
@@ -391,24 +491,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_
   uint32_t sk1[EPT / 2], sk2[EPT / 2];  // packed bf16 pairs
   uint16_t sv1[EPT], sv2[EPT];
   auto stage = [&]() {
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) ss = fmaf(bk1[j], bk1[j], fmaf(bk2[j], bk2[j], ss));
-    ss = row16_sum(ss);
-    const float sc = rsqrtf(ss / (float)HD + a.eps);
-#pragma unroll
-    for (int j = 0; j < EPT; j += 2) {
-      float y1[2], y2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float x1 = bk1[j + u] * sc * kg1[j + u], x2 = bk2[j + u] * sc * kg2[j + u];
-        const float cc = bcs[2 * (j + u)], sn = bcs[2 * (j + u) + 1];
-        y1[u] = x1 * cc - x2 * sn;
-        y2[u] = x2 * cc + x1 * sn;
-      }
-      sk1[j / 2] = f2bf2(y1[0], y1[1]);
-      sk2[j / 2] = f2bf2(y2[0], y2[1]);
-    }
+    form_key16<HD>(bk1, bk2, kg1, kg2, bcs, a.eps, sk1, sk2);
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       sv1[j] = f2bf(bv1[j]);
@@ -427,6 +510,20 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_
       for (int j = 0; j < EPT; ++j) {
         vst[(EPT * t16 + j) * VSTR + i] = sv1[j];
         vst[(HALF + EPT * t16 + j) * VSTR + i] = sv2[j];
+      }
+      if (p < e && blockIdx.z == 0) {  // a committed row: also into its ring slots
+        uint16_t* Kw = ring_layer + (size_t)g * C * HD + (size_t)slot_at(i) * HD + EPT * t16;
+        uint16_t* VTw = ring_layer + (size_t)(a.nkv + g) * HD * C + slot_at(i);
+#pragma unroll
+        for (int j = 0; j < EPT / 2; ++j) {
+          *(uint32_t*)(Kw + 2 * j) = sk1[j];
+          *(uint32_t*)(Kw + HALF + 2 * j) = sk2[j];
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          VTw[(size_t)(EPT * t16 + j) * C] = sv1[j];
+          VTw[(size_t)(HALF + EPT * t16 + j) * C] = sv2[j];
+        }
       }
     }
   };
@@ -588,20 +685,20 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, const uint16_
 }
 
 template <int HD, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnShape a, const uint16_t* __restrict__ ring_layer,
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnShape a, uint16_t* ring_layer,
                                                             const float* __restrict__ qkv,
                                                             const uint16_t* __restrict__ qnorm,
                                                             const uint16_t* __restrict__ knorm,
-                                                            const float2* __restrict__ rope, int R, int64_t e,
+                                                            const float2* __restrict__ rope, int R, int n, int64_t e,
                                                             int nchunks, int tpw, float* __restrict__ part) {
   // the chunk's keys [chunk position][hd + 8] and values transposed [dim][64 + 8]
   __shared__ __align__(16) uint16_t kst[ATTN_CHUNK * (HD + 8)];
   __shared__ __align__(16) uint16_t vst[HD * (ATTN_CHUNK + 8)];
   const int64_t p0 = (attn_lo(a, e) / ATTN_CHUNK + blockIdx.x) * ATTN_CHUNK;
-  if (p0 < e + R && e < p0 + ATTN_CHUNK)
-    attn_mfma_body<HD, NW, true>(a, ring_layer, qkv, qnorm, knorm, rope, R, e, nchunks, tpw, part, kst, vst);
+  if (p0 < e + R && e - n < p0 + ATTN_CHUNK)
+    attn_mfma_body<HD, NW, true>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, part, kst, vst);
   else
-    attn_mfma_body<HD, NW, false>(a, ring_layer, qkv, qnorm, knorm, rope, R, e, nchunks, tpw, part, kst, vst);
+    attn_mfma_body<HD, NW, false>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, part, kst, vst);
 }
 
 // ---- combine chunks in chunk order --------------------------------------------------------
@@ -675,8 +772,15 @@ static hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv,
   return hipGetLastError();
 }
 
+static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
+
 hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const void* const* knorms, int n,
                              int64_t pos0, void* ring, hipStream_t s) {
+  if (use_mfma(bf, a)) {  // keys formed as the attention forms its own
+    auto* fn = a.hd == 128 ? ring_write16_kernel<128> : ring_write16_kernel<64>;
+    hipLaunchKernelGGL(fn, dim3(n, (a.L * a.nkv + 15) / 16), dim3(256), 0, s, a, kv, knorms, pos0, (uint16_t*)ring);
+    return hipGetLastError();
+  }
   const int items = n * a.L * 2 * a.nkv;
   const int grid = (items + 3) / 4;
   if (bf) hipLaunchKernelGGL(ring_write_kernel<true>, dim3(grid), dim3(256), 0, s, a, kv, knorms, n, pos0, ring);
@@ -692,17 +796,18 @@ size_t attention_partial_floats(const AttnShape& a, int R) {
 
 int attention_max_chunks() { return COMBINE_MAX_CHUNKS; }
 
-static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
+bool attention_forms_committed_rows(int bf, const AttnShape& a) { return use_mfma(bf, a); }
 
 hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,
-                                  const float2* rope, void* ring_layer, int R, int64_t e, void* qb, void* qlo,
+                                  const float2* rope, void* ring_layer, int R, int n, int64_t e, void* qb, void* qlo,
                                   float* part, void* out, void* out_lo, hipStream_t s) {
   const int nch = attn_nchunks(a, R, e);
-  if (nch > COMBINE_MAX_CHUNKS || R < 1) return hipErrorInvalidValue;
+  if (nch > COMBINE_MAX_CHUNKS || R < 1 || n < 0 || n > e || n > a.window) return hipErrorInvalidValue;
+  if (n > 0 && !use_mfma(bf, a)) return hipErrorInvalidValue;
   dim3 grid(nch, a.nkv);
   if (use_mfma(bf, a)) {
     if (!rope) return hipErrorInvalidValue;
-    const uint16_t* rl = (const uint16_t*)ring_layer;
+    uint16_t* rl = (uint16_t*)ring_layer;
     const uint16_t *qn = (const uint16_t*)qnorm, *kn = (const uint16_t*)knorm;
     // query tiles over z work-groups of 4 waves, at most one tile per wave: two such
     // work-groups fit a CU, where an 8-wave one (150 registers) leaves room for no second
@@ -710,7 +815,7 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
     const int z = (nqt + 3) / 4, tpw = (nqt + z - 1) / z;
     const dim3 mgrid(nch, a.nkv, z);
     auto* fn = a.hd == 128 ? attn_mfma_kernel<128, 4> : attn_mfma_kernel<64, 4>;
-    hipLaunchKernelGGL(fn, mgrid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, e, nch, tpw, part);
+    hipLaunchKernelGGL(fn, mgrid, dim3(256), 0, s, a, rl, qkv, qn, kn, rope, R, n, e, nch, tpw, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);

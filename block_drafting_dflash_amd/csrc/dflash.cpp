@@ -66,6 +66,13 @@ struct dflash_ctx {
   int cus = 256;        // compute units of the device the context was created on
   int64_t e = 0;        // committed context end (absolute position)
   int64_t pending = 0;  // rows appended since the last trim
+  // rows at positions kv_pos .. kv_pos + kv_rows - 1 whose encoder rows (fc output) sit in
+  // the append buffer while their K/V are not yet in the ring: the next draft projects them
+  // in its own per-layer QKV launches and its attention writes them into the ring; any
+  // other call that needs the ring projects them first (flush_kv)
+  int64_t kv_pos = 0;
+  int32_t kv_rows = 0;
+  int fold_rows = 0;  // rows of a QKV launch that may carry such rows (0: never deferred)
   // events around the first argmax GEMM launch of the next dflash_lm_head_argmax call
   // (dflash_time_next_argmax); `active` while that call runs
   hipEvent_t tev_start = nullptr, tev_end = nullptr;
@@ -98,6 +105,9 @@ dflash_status cfg_fail(char* buf, dflash_status st, const char* fmt, ...) {
 int kstep(int wt) { return wt == WT_F32 ? 16 : 32; }
 
 constexpr int CHUNK_STEPS = 8;
+// rows of a QKV launch with committed rows folded in: draft rows plus committed rows in one
+// MFMA row tile
+constexpr int FOLD_ROWS = 16;
 
 // Launch plan of a GEMM with contraction length K. Waves and chunking depend on K only.
 bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
@@ -227,15 +237,16 @@ Layout make_layout(const Cfg& g) {
   L.knorm_ptrs = take(sizeof(void*) * c.layers);
   // operand buffers (q, attention output, SwiGLU output, normed rows) hold 4 bytes per
   // element: f32, or for bf16 shapes a hi plane followed by a lo plane (see lo_plane)
-  L.x = take(4 * R * H);
+  const size_t RQ = std::max<size_t>(R, FOLD_ROWS);  // draft rows and folded committed rows
+  L.x = take(4 * RQ * H);
   L.hn = take(4 * hn_rows(g) * H);  // normed rows of launches past one row tile
-  L.qkv = take(4 * R * (qd + 2 * kvd));
+  L.qkv = take(4 * RQ * (qd + 2 * kvd));
   L.qb = take(4 * R * qd);
   L.attn = take(4 * R * qd);
   L.mlp = take(4 * R * c.intermediate);
   L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
-  L.rope = take(sizeof(float2) * R * (c.head_dim / 2));  // rotary table of a draft's positions
+  L.rope = take(sizeof(float2) * RQ * (c.head_dim / 2));  // rotary table of a draft's positions
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
   L.total = o;
@@ -310,6 +321,10 @@ struct GemmCall {
   int split = 0;  // operands are hi/lo bf16 pairs (x/xlo planes, or formed by the norm prologue)
   const void* xlo = nullptr;
   void* ylo = nullptr;
+  // normed operands only: rows r2 and up take the gains gain2, in one launch of one row
+  // tile whose raw rows are staged through LDS
+  const void* gain2 = nullptr;
+  int r2 = 0;
 };
 
 dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
@@ -317,6 +332,9 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   GemmCall gc = gc_in;
   const int wt = g.wt;
   GemmPlan plan;
+  if (gc.gain2 && (gc.xsrc != XSRC_NORM || !gc.split || rows > 16 || gc.r2 < 0 || gc.r2 > rows))
+    return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows, split at %d) need one staged normed launch",
+                rows, gc.r2);
   // normed hi/lo operands: up to GEMM_NORM_STAGED_ROWS rows run directly when each wave's k
   // range is 256 elements (its raw rows are staged through LDS); more rows would not fit,
   // so they are normalised once into planes and streamed
@@ -352,6 +370,9 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     const bool norm_two = gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0 && (rc <= 16 || nb == 1);
     const int tpw_lds = gc.epi == EPI_ARGMAX || norm_two ? 2 : 1;
     while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
+    if (gc.gain2 && (rc < rows || gemm_lds_layout(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds).stage != 2 ||
+                     gemm_lds_bytes(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES))
+      return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows) do not fit one staged launch", rows);
     GemmParams p{};
     for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
     p.nseg = (int)gc.segs.size();
@@ -364,6 +385,8 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     p.xlo = gc.xlo ? (const unsigned char*)gc.xlo + (size_t)r0 * gc.ldx * x_elt : nullptr;
     p.ldx = gc.ldx;
     p.gain = gc.gain;
+    p.gain2 = gc.gain2 ? gc.gain2 : gc.gain;
+    p.r2 = gc.gain2 ? gc.r2 : rc;
     p.eps = g.c.rms_eps;
     GemmPlan pl = plan;
     pl.grid = gemm_fold(wt, gc.xsrc) ? 2 * p.ntiles : p.ntiles;  // folded: 8-column tiles
@@ -385,7 +408,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
-    const hipError_t le = launch_gemm(wt, gc.epi, gc.xsrc, pl, p, st);
+    const hipError_t le = launch_gemm(wt, gc.epi, gc.gain2 ? XSRC_NORM2 : gc.xsrc, pl, p, st);
     if (timed && le == hipSuccess && hipEventRecord(ctx->tev_end, st) != hipSuccess)
       return dev(ctx, hipGetLastError(), "timing event");
     if (le != hipSuccess)
@@ -403,6 +426,57 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
 }
 
 GemmSeg seg(const Lin& l, int col0, int rows) { return GemmSeg{l.w, l.s, l.b, col0, rows}; }
+
+// Rows of a QKV launch that may carry committed rows beside the draft rows (0: none): bf16
+// activations on the MFMA attention (which forms and writes those rows), and a normed
+// launch of one row tile that stages its raw rows through LDS.
+int fold_rows_of(const Cfg& g) {
+  const dflash_config& c = g.c;
+  if (!g.bf || !attention_forms_committed_rows(g.bf, g.a)) return 0;
+  GemmPlan pl;
+  if (!plan_gemm(g.wt, EPI_STORE, XSRC_NORM, c.hidden, &pl)) return 0;
+  const int tiles = (c.q_heads + 2 * c.kv_heads) * c.head_dim / 16;
+  const int tpw = tiles % 2 == 0 ? 2 : 1;
+  if (gemm_lds_layout(g.wt, XSRC_NORM2, 1, FOLD_ROWS, pl.waves, 1, c.hidden, tpw).stage != 2 ||
+      gemm_lds_bytes(g.wt, XSRC_NORM2, 1, FOLD_ROWS, pl.waves, 1, c.hidden, tpw) > (size_t)LDS_BYTES)
+    return 0;
+  return FOLD_ROWS;
+}
+
+// K/V of rc encoder rows (the fc output in the append buffer) at positions pos.. into the
+// ring: the per-layer k/v projections with the encoder norm fused as the operand norm, six
+// layers per launch, then the ring write (k RMSNorm, RoPE, cache dtype)
+dflash_status project_kv(dflash_ctx* ctx, int rc, int64_t pos, hipStream_t st) {
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  const int kvd = c.kv_heads * c.head_dim;
+  const int kv_cols = c.layers * 2 * kvd;
+  const float* fc_out = (const float*)(ctx->ws + ctx->lay.app_fc);
+  float* kv = (float*)(ctx->ws + ctx->lay.app_kv);
+  for (int l0 = 0; l0 < c.layers; l0 += GEMM_MAXSEG / 2) {
+    const int l1 = std::min(c.layers, l0 + GEMM_MAXSEG / 2);
+    GemmCall kvc{EPI_STORE, XSRC_NORM, {}, c.hidden, fc_out, c.hidden, ctx->enc_norm,
+                 kv + (size_t)l0 * 2 * kvd, kv_cols, nullptr};
+    kvc.split = g.bf;
+    for (int l = l0; l < l1; ++l) {
+      kvc.segs.push_back(seg(ctx->layers[l].k, (l - l0) * 2 * kvd, kvd));
+      kvc.segs.push_back(seg(ctx->layers[l].v, (l - l0) * 2 * kvd + kvd, kvd));
+    }
+    const dflash_status s = run_gemm(ctx, kvc, rc, st);
+    if (s != DFLASH_OK) return s;
+  }
+  return dev(ctx, launch_ring_write(g.bf, g.a, kv, (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), rc, pos,
+                                    ctx->ring, st),
+             "ring write");
+}
+
+// the deferred rows' K/V into the ring now
+dflash_status flush_kv(dflash_ctx* ctx, hipStream_t st) {
+  if (ctx->kv_rows <= 0) return DFLASH_OK;
+  const dflash_status s = project_kv(ctx, ctx->kv_rows, ctx->kv_pos, st);
+  if (s == DFLASH_OK) ctx->kv_rows = 0;
+  return s;
+}
 
 }  // namespace
 
@@ -473,6 +547,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   if (!ctx) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
   ctx->cfg = g;
   ctx->lay = lay;
+  ctx->fold_rows = fold_rows_of(g);
   auto cv = [](const dflash_linear& l) { return Lin{l.w, l.scales, l.biases}; };
   ctx->lm_head = cv(wts->lm_head);
   ctx->fc = cv(wts->fc);
@@ -564,6 +639,9 @@ dflash_status dflash_cache_trim(dflash_ctx* ctx, int32_t m) {
                 (long long)ctx->pending, (long long)ctx->cfg.S);
   ctx->e += ctx->pending - m;
   ctx->pending = 0;
+  // deferred rows past the new end are dropped with the rest
+  if (ctx->kv_rows > 0)
+    ctx->kv_rows = (int32_t)std::max<int64_t>(0, std::min<int64_t>(ctx->kv_rows, ctx->e - ctx->kv_pos));
   return DFLASH_OK;
 }
 
@@ -573,38 +651,30 @@ dflash_status dflash_cache_append(dflash_ctx* ctx, const void* resid, int32_t n,
   const Cfg& g = ctx->cfg;
   const dflash_config& c = g.c;
   hipStream_t st = (hipStream_t)stream;
+  dflash_status s = flush_kv(ctx, st);
+  if (s != DFLASH_OK) return s;
   const int64_t start = ctx->e + ctx->pending, end = start + n;
   const int64_t keep_from = commit ? end - c.window : end - g.C;
   const int64_t first = std::max<int64_t>(0, keep_from - start);
   const int64_t F = (int64_t)c.target_streams * c.target_width;
-  const int kvd = c.kv_heads * c.head_dim;
-  const int kv_cols = c.layers * 2 * kvd;
+  // a few uncommitted rows (the verified rows of a round) are deferred: encoder rows now,
+  // their K/V with the next draft's QKV launches (at least two draft rows beside them)
+  const bool defer = !commit && first == 0 && n + 2 <= ctx->fold_rows && n <= c.window;
   for (int64_t r0 = first; r0 < n; r0 += GEMM_MAX_ROWS) {
     const int rc = (int)std::min<int64_t>(GEMM_MAX_ROWS, n - r0);
     float* fc_out = (float*)(ctx->ws + ctx->lay.app_fc);
-    float* kv = (float*)(ctx->ws + ctx->lay.app_kv);
     GemmCall f{EPI_STORE, XSRC_GLOBAL, {seg(ctx->fc, 0, c.hidden)}, (int)F,
                (const unsigned char*)resid + (size_t)r0 * F * g.act_elt, F, nullptr, fc_out, c.hidden, nullptr};
-    dflash_status s = run_gemm(ctx, f, rc, st);
+    s = run_gemm(ctx, f, rc, st);
     if (s != DFLASH_OK) return s;
-    // per-layer k/v projections of the encoder rows (output_norm_enc fused as the operand
-    // norm), six layers per launch
-    for (int l0 = 0; l0 < c.layers; l0 += GEMM_MAXSEG / 2) {
-      const int l1 = std::min(c.layers, l0 + GEMM_MAXSEG / 2);
-      GemmCall kvc{EPI_STORE, XSRC_NORM, {}, c.hidden, fc_out, c.hidden, ctx->enc_norm,
-                   kv + (size_t)l0 * 2 * kvd, kv_cols, nullptr};
-      kvc.split = g.bf;
-      for (int l = l0; l < l1; ++l) {
-        kvc.segs.push_back(seg(ctx->layers[l].k, (l - l0) * 2 * kvd, kvd));
-        kvc.segs.push_back(seg(ctx->layers[l].v, (l - l0) * 2 * kvd + kvd, kvd));
-      }
-      s = run_gemm(ctx, kvc, rc, st);
+    if (!defer) {
+      s = project_kv(ctx, rc, start + r0, st);
       if (s != DFLASH_OK) return s;
     }
-    s = dev(ctx, launch_ring_write(g.bf, g.a, kv, (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), rc,
-                                   start + r0, ctx->ring, st),
-            "ring write");
-    if (s != DFLASH_OK) return s;
+  }
+  if (defer) {
+    ctx->kv_pos = start;
+    ctx->kv_rows = n;
   }
   if (commit) {
     ctx->e = end;
@@ -628,6 +698,14 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   hipStream_t st = (hipStream_t)stream;
   const int R = block + 1;
   const int H = c.hidden;
+  // committed rows whose K/V are deferred: projected with this draft's QKV launches (rows
+  // R..R+nf-1) and written into the ring by its attention, or first on their own
+  int nf = ctx->kv_rows;
+  if (nf > 0 && (R + nf > ctx->fold_rows || ctx->kv_pos + nf != ctx->e)) {
+    const dflash_status s0 = flush_kv(ctx, st);
+    if (s0 != DFLASH_OK) return s0;
+    nf = 0;
+  }
   const int qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim;
   float* x = (float*)(ctx->ws + ctx->lay.x);
   float* qkv = (float*)(ctx->ws + ctx->lay.qkv);
@@ -642,7 +720,8 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
 
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   dflash_status s = dev(ctx,
-                        launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, x, rope, ctx->e, c.rope_theta,
+                        launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, nf,
+                                     (const float*)(ctx->ws + ctx->lay.app_fc), x, rope, ctx->e, c.rope_theta,
                                      c.head_dim, st),
                         "embed");
   if (s != DFLASH_OK) return s;
@@ -651,10 +730,14 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     GemmCall q{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
                L.in_norm, qkv, qd + 2 * kvd, nullptr};
     q.split = g.bf;
-    if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
+    if (nf > 0) {  // the committed encoder rows behind the draft rows (copied by the embedding)
+      q.gain2 = ctx->enc_norm;
+      q.r2 = R;
+    }
+    if ((s = run_gemm(ctx, q, R + nf, st)) != DFLASH_OK) return s;
     s = dev(ctx,
-            launch_block_attention(g.bf, g.a, qkv, L.q_norm, L.k_norm, rope, ctx->ring + l * ring_layer, R, ctx->e, qb,
-                                   qb_lo, part, attn, attn_lo, st),
+            launch_block_attention(g.bf, g.a, qkv, L.q_norm, L.k_norm, rope, ctx->ring + l * ring_layer, R, nf,
+                                   ctx->e, qb, qb_lo, part, attn, attn_lo, st),
             "attention");
     if (s != DFLASH_OK) return s;
     GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
@@ -672,6 +755,7 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     dn.xlo = mlp_lo;
     if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
   }
+  ctx->kv_rows = 0;  // every layer's ring now holds them
   if (d_hidden) {
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
@@ -728,6 +812,8 @@ dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, voi
   const int n = (int)(ctx->e - lo);
   *n_out = n;
   if (n == 0) return DFLASH_OK;
+  const dflash_status s = flush_kv(ctx, (hipStream_t)stream);
+  if (s != DFLASH_OK) return s;
   if (!k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL window output");
   const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
   return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),

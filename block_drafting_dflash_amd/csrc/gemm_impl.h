@@ -158,9 +158,10 @@ constexpr int gemm_chunks_ahead() {
 }
 
 // T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
-template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
-__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>())) void gemm_kernel(
-    const GemmParams p) {
+template <int WT, int RT, int NB, int EPI, int XSRC_IN, int T, int NCH, int CH, bool SPLIT>
+__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, xsrc_base(XSRC_IN), T, NCH, SPLIT>())) void
+gemm_kernel(const GemmParams p) {
+  constexpr int XSRC = xsrc_base(XSRC_IN);
   using Tr = WTr<WT>;
   constexpr bool BF = Tr::BF;
   static_assert(!SPLIT || BF, "hi/lo operand pairs feed bf16 MFMA only");
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   const int K = p.K, R = p.R;
   const int kw = K / nw;  // k owned by this wave in every tile (= NCH * CH * KSTEP)
 
-  const GemmLds lds = gemm_lds_layout(WT, XSRC, SPLIT ? 1 : 0, R, nw, NB, K, T);
+  const GemmLds lds = gemm_lds_layout(WT, XSRC_IN, SPLIT ? 1 : 0, R, nw, NB, K, T);
   float* red = (float*)smem;  // [NRED][nw][RT][NB][64 lanes][4]
   // XSRC_NORM: per wave, the sum of squares of each row over the wave's k range [nw][RT*16]
   float* ssq = (float*)(smem + lds.ssq_off);
@@ -573,7 +574,12 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
   f32x4_t xa[STG_N ? 1 : RT][CH][XRAW];
   u32x4_t ga[CH];
   // STG_N: raw row i of the wave's k range in load i (64 lanes x 4 f32), the gains in the last
+  // (one row tile: lanes 0-31 the gains of rows below r2, lanes 32-63 those of rows r2 and up)
   u32x4_t xn[STG_N ? STG_N_ROWS + 1 : 1];
+  constexpr bool GAIN2 = XSRC_IN == XSRC_NORM2;
+  static_assert(!GAIN2 || (STG_N && RT == 1), "two gain rows: one row tile of staged raw rows");
+  // LDS offset of the gain row of this lane's operand row (row li, clamped to the real rows)
+  const int g2off = GAIN2 && min(li, R - 1) >= p.r2 ? 512 : 0;
   auto kof = [&](int c, int st) { return w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL; };
   auto raw_ld = [&](int c, int rt, int st, int h) {
     return *(const f32x4_t*)((const float*)p.x + (size_t)xrow(rt) * p.ldx + kof(c, st) + 4 * h);
@@ -615,7 +621,8 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 #pragma unroll
     for (int i = 0; i < STG_N_ROWS; ++i)
       if (i < R) xn[i] = *(const u32x4_t*)((const float*)p.x + (size_t)i * p.ldx + k0 + lane * 4);
-    xn[STG_N_ROWS] = *(const u32x4_t*)((const uint16_t*)p.gain + k0 + (lane & 31) * 8);
+    xn[STG_N_ROWS] =
+        *(const u32x4_t*)((const uint16_t*)(GAIN2 && lane >= 32 ? p.gain2 : p.gain) + k0 + (lane & 31) * 8);
   } else if constexpr (NORM_FIRST) {
 #pragma unroll
     for (int st = 0; st < CH; ++st) {
@@ -693,7 +700,7 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
 #pragma unroll
       for (int i = 0; i < STG_N_ROWS; ++i)
         if (i < R) *(u32x4_t*)(xs + (size_t)i * lds.row_bytes + lane * 16) = xn[i];
-      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (lane & 31) * 16) = xn[STG_N_ROWS];
+      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (GAIN2 ? lane : lane & 31) * 16) = xn[STG_N_ROWS];
     }
     // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
 #pragma unroll
@@ -705,8 +712,9 @@ __global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH,
           u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
           if constexpr (STG_N) {
             const int kk = (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;  // within the wave's k range
-            const unsigned char* xrw = xs + (size_t)min(rt * 16 + li, R - 1) * lds.row_bytes + kk * 4;
-            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + kk * 2);
+            const int row = min(rt * 16 + li, R - 1);
+            const unsigned char* xrw = xs + (size_t)row * lds.row_bytes + kk * 4;
+            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + (GAIN2 ? g2off : 0) + kk * 2);
             form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
           } else if constexpr (NORM_FIRST) {
             form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
@@ -816,7 +824,9 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
   } else {
     const int rt = (p.R + 15) / 16;
     if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
-    if constexpr (XSRC == XSRC_NORM && SPLIT) {
+    if constexpr (XSRC == XSRC_NORM2) {
+      return hipErrorInvalidValue;
+    } else if constexpr (XSRC == XSRC_NORM && SPLIT) {
       // normed hi/lo operands of two row tiles: staged raw rows over a 256-element k range
       // per wave (at most GEMM_NORM_STAGED_ROWS rows); larger launches go through planes
       if constexpr (NCH == 1) {
@@ -835,7 +845,11 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
 // every chunk in registers, so they stop at two chunks)
 template <int WT, int NB, int EPI, int XSRC, bool SPLIT>
 static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  if constexpr (XSRC != XSRC_GLOBAL) {
+  if constexpr (XSRC == XSRC_NORM2) {  // one chunk per wave (raw rows staged), one row tile
+    if (pl.nch != 1) return hipErrorInvalidValue;
+    return pl.tiles_per_wg == 2 ? by_rt<WT, NB, EPI, XSRC, 2, 1, 8, SPLIT>(p, pl.grid, s)
+                                : by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
+  } else if constexpr (XSRC != XSRC_GLOBAL) {
     // normed operands: one tile per work-group, or two (the registers holding the
     // operand pairs then serve both tiles)
     if (pl.tiles_per_wg == 2) {
@@ -908,6 +922,7 @@ static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParam
                      : by_nch<WT, 1, EPI_STORE, XSRC_GLOBAL, false>(pl, p, s);
     if (!p.split) return hipErrorInvalidValue;
     if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, true>(pl, p, s);
+    if (epi == EPI_STORE && xsrc == XSRC_NORM2) return by_nch<WT, 1, EPI_STORE, XSRC_NORM2, true>(pl, p, s);
     if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_GLOBAL) return by_nch<WT, 2, EPI_SWIGLU, XSRC_GLOBAL, true>(pl, p, s);

@@ -15,7 +15,10 @@ constexpr int ATTN_CHUNK = 64;     // keys per attention work-group
 constexpr int ATTN_QG = 64;        // query vectors per attention pass
 constexpr int MAX_WINDOW = 4096;   // attention chunks of one query stay within the combine's LDS
 
-enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2 };
+// XSRC_NORM2: XSRC_NORM whose rows r2 and up take the gains gain2 (one row tile, raw rows
+// staged through LDS); plans, LDS layouts and the kernel body treat it as XSRC_NORM
+enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2, XSRC_NORM2 = 3 };
+__host__ __device__ constexpr int xsrc_base(int xsrc) { return xsrc == XSRC_NORM2 ? XSRC_NORM : xsrc; }
 
 // MFMA steps per pipelined chunk (16-byte weight loads per lane per chunk): deeper for one
 // row tile, shallower when 2-3 row tiles of activations also sit in registers.
@@ -51,6 +54,9 @@ struct GemmParams {
   const void* xlo;
   int64_t ldx;
   const void* gain;  // XSRC_NORM: act-dtype storage [K]
+  // XSRC_NORM2: rows r2..R-1 are normalised with gains gain2 (the same storage as gain)
+  const void* gain2;
+  int32_t r2;
   float eps;
   void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: hi/lo planes (split) or f32
   void* ylo;
@@ -95,8 +101,9 @@ __host__ __device__ inline int gemm_row_groups(int wt, int xsrc, int R) {
 __host__ __device__ inline int gemm_chunk_steps(int wt, int xsrc, int R) {
   return gemm_fold(wt, xsrc) ? ((R + 7) / 8 <= 2 ? 8 : 4) : chunk_steps((R + 15) / 16);
 }
-__host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, int R, int waves, int nb, int K,
+__host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc_in, int split, int R, int waves, int nb, int K,
                                                    int tiles_per_wg) {
+  const int xsrc = xsrc_base(xsrc_in);
   const bool fold = gemm_fold(wt, xsrc);
   const int rt = gemm_row_groups(wt, xsrc, R), rows_pad = (fold ? 8 : 16) * rt;
   const int ch = gemm_chunk_steps(wt, xsrc, R), kstep = wt == WT_F32 ? 16 : 32;
@@ -113,9 +120,9 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc, int split, 
     l.row_bytes = ch * kstep * 2 + 16;
     l.xs_wave = (size_t)(split ? 2 : 1) * R * l.row_bytes;
   } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt <= 2 && nch * ch * kstep == 256) {
-    l.stage = 2;  // the raw rows of the wave's whole k range (256 f32) and its gains
+    l.stage = 2;  // the raw rows of the wave's whole k range (256 f32) and its gain row(s)
     l.row_bytes = 256 * 4 + 16;
-    l.xs_wave = (size_t)R * l.row_bytes + 256 * 2;
+    l.xs_wave = (size_t)R * l.row_bytes + (xsrc_in == XSRC_NORM2 ? 2 : 1) * 256 * 2;
   }
   if (l.stage == 2) {
     l.xs_off = 0;
@@ -150,9 +157,12 @@ hipError_t launch_pack_q4(const void* codes, const void* scales, const void* bia
 // idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
 // Embedding rows [anchor, mask x (R-1)] as f32 residual rows x; with rope != NULL also the
-// rotary table of positions pos0..pos0+R-1, rope[r][i] = (cos, sin), i < hd/2.
+// rotary table rope[r][i] = (cos, sin), i < hd/2, of positions pos0..pos0+R-1 (rows 0..R-1)
+// and pos0-nprev..pos0-1 (rows R..R+nprev-1). With nprev > 0, the f32 rows prev [nprev][hidden]
+// are copied into x rows R..R+nprev-1.
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
-                        float* x, float2* rope, int64_t pos0, float theta, int hd, hipStream_t s);
+                        int nprev, const float* prev, float* x, float2* rope, int64_t pos0, float theta, int hd,
+                        hipStream_t s);
 // RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
                           void* out_lo, hipStream_t s);
@@ -164,10 +174,14 @@ hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, 
 // keys come from the ring layer; the block's own keys and values are formed where they are
 // used (bf16 shapes with head dim 64 or 128, reading the rotary table rope of launch_embed)
 // or written into the ring slots of positions e..e+R-1 first (other shapes, which also use
-// qb/qlo for the formed queries).
+// qb/qlo for the formed queries). With n > 0 (bf16 MFMA shapes only, n <= W), projection
+// rows R..R+n-1 are the committed positions e-n..e-1 whose keys and values are not yet in
+// the ring: they are formed like the block's own, used, and written into their ring slots.
 hipError_t launch_block_attention(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
-                                  const void* knorm, const float2* rope, void* ring_layer, int R, int64_t e, void* qb,
-                                  void* qlo, float* part, void* out, void* out_lo, hipStream_t s);
+                                  const void* knorm, const float2* rope, void* ring_layer, int R, int n, int64_t e,
+                                  void* qb, void* qlo, float* part, void* out, void* out_lo, hipStream_t s);
+// whether launch_block_attention takes committed rows (n > 0) for this shape
+bool attention_forms_committed_rows(int act_bf16, const AttnShape& a);
 size_t attention_partial_floats(const AttnShape& a, int R);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);

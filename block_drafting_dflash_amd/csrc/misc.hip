@@ -50,15 +50,23 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
 // of the prep kernel does; every layer's attention reads it (rope may be NULL).
 template <bool BF, bool VEC>
 __global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id,
-                                                    float* x, float2* rope, int64_t pos0, float theta, int hd) {
+                                                    int R, int nprev, const float* prev, float* x, float2* rope,
+                                                    int64_t pos0, float theta, int hd) {
   const int r = blockIdx.x;
   if (blockIdx.y == 1) {
+    const int64_t pos = r < R ? pos0 + r : pos0 - nprev + (r - R);
     for (int i = threadIdx.x; i < hd / 2; i += blockDim.x) {
       const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
       double sn, cs;
-      sincos((double)(pos0 + r) * inv, &sn, &cs);
+      sincos((double)pos * inv, &sn, &cs);
       rope[(size_t)r * (hd / 2) + i] = make_float2((float)cs, (float)sn);
     }
+    return;
+  }
+  if (r >= R) {  // rows carried behind the embedded ones
+    const float4* src = (const float4*)(prev + (size_t)(r - R) * hidden);
+    float4* dst = (float4*)(x + (size_t)r * hidden);
+    for (int v = threadIdx.x; v < hidden / 4; v += blockDim.x) dst[v] = src[v];
     return;
   }
   const int64_t tok = r == 0 ? anchor : mask_id;
@@ -92,22 +100,24 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidde
   }
 }
 
-hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, float* x,
-                        float2* rope, int64_t pos0, float theta, int hd, hipStream_t s) {
+hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, int nprev,
+                        const float* prev, float* x, float2* rope, int64_t pos0, float theta, int hd, hipStream_t s) {
+  if (nprev < 0 || (nprev > 0 && (!rope || !prev || hidden % 4 || ((uintptr_t)prev & 15u) || ((uintptr_t)x & 15u))))
+    return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)table & 15u) == 0 && hidden % 8 == 0;
-  const dim3 grid(R, rope ? 2 : 1);
+  const dim3 grid(R + nprev, rope ? 2 : 1);
   if (bf && vec)
-    hipLaunchKernelGGL((embed_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope, pos0,
-                       theta, hd);
+    hipLaunchKernelGGL((embed_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
+                       x, rope, pos0, theta, hd);
   else if (bf)
-    hipLaunchKernelGGL((embed_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
-                       pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
+                       x, rope, pos0, theta, hd);
   else if (vec)
-    hipLaunchKernelGGL((embed_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
-                       pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
+                       x, rope, pos0, theta, hd);
   else
-    hipLaunchKernelGGL((embed_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, x, rope,
-                       pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
+                       x, rope, pos0, theta, hd);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ class Stats:
 
 class LockStep:
     def __init__(self, shape, weights_np, max_block: int, phase: int = 0, dev_weights=None,
-                 check_windows: bool = True):
+                 check_windows: bool = True, window_period: int = 1):
         self.sh = shape
         self.dev = dev_weights if dev_weights is not None else binding.to_device(shape, weights_np)
         self.gpu = binding.Drafter(shape, self.dev, max_block, phase)
@@ -50,6 +50,10 @@ class LockStep:
         self.dt = binding.act_torch_dtype(shape)
         self.stats = Stats()
         self.check_windows = check_windows
+        # the live window is read back after every window_period-th trim; between reads the
+        # verified rows' K/V travel with the next draft (read-back projects them first)
+        self.window_period = window_period
+        self.trims = 0
 
     def _t(self, a: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(self.dt).to(self.gpu.device)
@@ -88,7 +92,8 @@ class LockStep:
         self.gpu.cache_trim(m)
         self.orc.trim(m)
         self.check_state()
-        if self.check_windows:
+        self.trims += 1
+        if self.check_windows and self.trims % self.window_period == 0:
             torch.cuda.synchronize()
             self.check_window()
 

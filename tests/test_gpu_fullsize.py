@@ -44,6 +44,19 @@ def test_block4_ctx1024_lm_head_verify(muse):
     assert ls.stats.rows_checked == wl.rounds * (4 + 5)
 
 
+def test_block4_ctx1024_deferred_kv(muse):
+    """The bench's round sequence at block 4: the verified rows' K/V travel with the next
+    draft's QKV launches and attention; the live window of all layers is read back every
+    fourth trim and at the end."""
+    w64, dev = muse
+    wl = synth.WORKLOADS["muse-bf16-b4-ctx1024"]
+    ls = P.LockStep(SH, w64, max_block=4, dev_weights=dev, window_period=4)
+    ks = P.run_lm_head_rounds(ls, wl.context, 4, 8, anchor_tag=3)
+    torch.cuda.synchronize()
+    ls.check_window()
+    _report(wl.name + " deferred", ls, ks)
+
+
 def test_block16_ctx4096_synthetic_accept(muse):
     """Block 16 after a 4096-row prefill (2048 kept); p = 0.6 prefix-broken stand-in target."""
     w64, dev = muse

@@ -154,6 +154,54 @@ def test_outputs_do_not_depend_on_ring_phase(micro_bf16_w):
             assert torch.equal(k0, k1) and torch.equal(v0, v1), phase
 
 
+# the verified rows' K/V travel with the next draft (its QKV launches project them beside
+# the draft rows, its attention writes them into the ring) while draft rows + committed rows
+# fit one row tile (16); the window is read back only every third trim, so most rounds take
+# that path, and block 13 takes it only when at most two rows were committed
+@pytest.mark.parametrize("block,phase,context", [(1, 0, 21), (4, 5, 50), (8, 16, 40), (13, 3, 64)])
+def test_micro_bf16_deferred_kv_rounds(micro_bf16_w, block, phase, context):
+    ls = P.LockStep(MICRO_BF16, micro_bf16_w, max_block=block, phase=phase, window_period=3)
+    P.run_random_depth_rounds(ls, context, block, 14, tag=200 + block)
+    torch.cuda.synchronize()
+    ls.check_window()
+    print("micro-bf16 deferred stats", block, ls.stats)
+
+
+@pytest.mark.parametrize("block", [4, 8])
+def test_deferred_kv_matches_immediate_projection(micro_bf16_w, block):
+    """The same rounds with the window read after every trim (the verified rows' K/V
+    projected on their own, by the append path's kernels) and never (projected inside the
+    next draft): drafted tokens, hidden rows and the final window are bit-identical."""
+    sh, context, rounds = MICRO_BF16, 45, 12
+    dev = binding.to_device(sh, micro_bf16_w)
+    runs = []
+    for read_back in (True, False):
+        g = binding.Drafter(sh, dev, max_block=block, phase=8)
+        g.cache_append(torch.from_numpy(synth.resid_rows(sh, context, 0)).to(torch.bfloat16).cuda(), commit=True)
+        anchor, outs = synth.anchor_token(sh), []
+        for r in range(rounds):
+            h = torch.empty((block + 1, sh.hidden), dtype=torch.float32, device="cuda")
+            d = g.draft_block(anchor, block, hidden=h).cpu().numpy()
+            a = P.target_with_accept_length(d, synth.random_depth_k(block, r, 7), sh.vocab, tail=r)
+            out = g.verify_greedy(torch.from_numpy(d).cuda(), torch.from_numpy(a.astype(np.int32)).cuda(), block)
+            k, bonus, _ = out.cpu().tolist()
+            g.cache_append(torch.from_numpy(synth.resid_rows(sh, block + 1, 300 + r)).to(torch.bfloat16).cuda())
+            g.cache_trim(block - k)
+            if read_back:
+                for l in range(sh.layers):
+                    g.cache_read(l)
+            outs.append((d, h.cpu(), k))
+            anchor = bonus
+        kv = [g.cache_read(l) for l in range(sh.layers)]
+        runs.append((outs, [(k.cpu(), v.cpu()) for k, v in kv], g.cache_state()))
+    (o0, kv0, st0), (o1, kv1, st1) = runs
+    assert st0 == st1
+    for (d0, h0, k0), (d1, h1, k1) in zip(o0, o1):
+        assert np.array_equal(d0, d1) and k0 == k1 and torch.equal(h0, h1)
+    for (k0, v0), (k1, v1) in zip(kv0, kv1):
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+
+
 @pytest.mark.parametrize("block,phase,context", [(4, 0, 50), (16, 7, 30), (17, 0, 9), (40, 3, 64)])
 def test_micro_q4_random_depth(micro_q4_w, block, phase, context):
     """4-bit fc, layer linears and lm_head (group 64): the codes enter the MFMA as exact
@@ -162,6 +210,17 @@ def test_micro_q4_random_depth(micro_q4_w, block, phase, context):
     P.run_random_depth_rounds(ls, context, block, 10, tag=block)
     assert ls.stats.max_hidden_rel <= 2e-3, ls.stats
     print("micro-q4 stats", block, ls.stats)
+
+
+@pytest.mark.parametrize("block,phase,context", [(4, 0, 50), (8, 24, 33)])
+def test_micro_q4_deferred_kv_rounds(micro_q4_w, block, phase, context):
+    """4-bit layers with the verified rows' K/V projected inside the next draft (window read
+    back every third trim and at the end)."""
+    ls = P.LockStep(MICRO_Q4, micro_q4_w, max_block=block, phase=phase, window_period=3)
+    P.run_random_depth_rounds(ls, context, block, 12, tag=300 + block)
+    torch.cuda.synchronize()
+    ls.check_window()
+    assert ls.stats.max_hidden_rel <= 2e-3, ls.stats
 
 
 def test_q4_lm_head_argmax_is_width_invariant(micro_q4_w):
