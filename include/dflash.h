@@ -140,7 +140,12 @@ void dflash_destroy(dflash_ctx *ctx);
  * its position, and is written to its ring slot. commit = 0: the rows are pending until
  * dflash_cache_trim. commit != 0: all pending rows and these are committed now, and rows
  * that the committed window can no longer see are dropped before the encoder
- * (lablup/mlxcel #1762, Pre-merge review round, third finding). Errors: n <= 0 or a NULL
+ * (lablup/mlxcel #1762, Pre-merge review round, third finding). A pending append of a few
+ * rows (bf16 shapes with head_dim 64 or 128, at most 14 rows) runs only encoder.fc here and
+ * leaves the rest of the projection to the next call that needs the ring: the next
+ * dflash_draft_block does it inside its own launches when its rows and the committed ones
+ * fit, else that call, dflash_cache_read or the next append does it first, on its own
+ * stream. The ring then holds the same values either way. Errors: n <= 0 or a NULL
  * slab ("no residual stream captured", lablup/mlxcel #1762, Pre-merge review round,
  * second finding).
  */
@@ -162,7 +167,8 @@ dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
  * lm_head. The ring slots of positions e..e+block lie past the committed window: a layer
  * may store the block's own k/v there (f32 shapes do; dflash_cache_read never returns
  * those slots and the next append overwrites them), and
- * the committed window is never written. d_tokens (device int32 [block]) receives the
+ * of the committed window only rows whose projection an append left to this call are
+ * written (their ring slots, once). d_tokens (device int32 [block]) receives the
  * first index of each row's maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
  * residual stream after the last layer. Errors: block outside 1..max_block or anchor
  * outside [0, vocab) (DFLASH_E_RANGE); e == 0 (DFLASH_E_NO_CONTEXT); pending rows
