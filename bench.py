@@ -4,7 +4,10 @@ A step is one whole round over one block of synthetic input: the drafter's block
 (dflash_draft_block), the target verify rows through the shared lm_head
 (dflash_lm_head_argmax), greedy verify (dflash_verify_greedy), the append of the B+1
 verify residual rows (dflash_cache_append), one device->host copy of (k, bonus) and the
-trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts.
+trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
+timed rounds record no timing events (a HIP event record holds the stream for a few
+microseconds); a pass of up to 100 more rounds after them records events around the draft,
+the append and the lm_head argmax kernel for the per-call breakdown and `roofline`.
 
 Workload (timed as `value`): muse-bf16-b4-ctx1024 -- Muse-assistant-shaped bf16 drafter
 (hidden 2048, 5 layers, 32/4 heads x 128, intermediate 6144, vocab 202048, untied lm_head,
@@ -31,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BREAKDOWN_ROUNDS = 100  # event-timed rounds after the timed ones (per-call breakdown, kernel timing)
 
 
 def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
@@ -86,7 +90,10 @@ def run_gpu(args):
     B = 4
     g = binding.Drafter(sh, dw, max_block=B)
     g.cache_append(torch.from_numpy(synth.resid_rows(sh, wl.context, 0)).to(torch.bfloat16).to(dev), commit=True)
-    n = args.warmup + args.steps
+    # timed rounds carry no timing events (each event record costs the stream a few
+    # microseconds); a shorter pass after them, with events, gives the breakdown
+    nb = min(args.steps, BREAKDOWN_ROUNDS)
+    n = args.warmup + args.steps + nb
     vrows = torch.from_numpy(np.stack([synth.verify_hidden(sh, B + 1, r) for r in range(n)])).to(torch.bfloat16).to(dev)
     resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, r + 1) for r in range(n)])).to(torch.bfloat16).to(dev)
     toks = torch.empty(B, dtype=torch.int32, device=dev)
@@ -94,25 +101,29 @@ def run_gpu(args):
     vout = torch.empty(3, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)
     done = torch.cuda.Event()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
     # events around the argmax kernel alone (the library records them on the call's stream)
-    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)]
     for pair in evk:
         for x in pair:
             x.record(stream)  # creates the underlying events before the timed region
     anchor = synth.anchor_token(sh)
     ks = []
     torch.cuda.synchronize()
-    t_start = None
+    t_start = elapsed = None
+    b0 = args.warmup + args.steps  # first breakdown round
     for r in range(n):
         if r == args.warmup:
             torch.cuda.synchronize()
             t_start = time.perf_counter()
-        e = ev[r - args.warmup] if r >= args.warmup else None
+        if r == b0:
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t_start
+        e = ev[r - b0] if r >= b0 else None
         if e: e[0].record(stream)
         g.draft_block(anchor, B, tokens=toks, stream=stream)
         if e: e[1].record(stream)
-        if e: g.time_next_argmax(*evk[r - args.warmup])
+        if e: g.time_next_argmax(*evk[r - b0])
         g.lm_head_argmax(vrows[r], out=a, stream=stream)
         if e: e[2].record(stream)
         g.verify_greedy(toks, a, B, out=vout, stream=stream)
@@ -129,7 +140,6 @@ def run_gpu(args):
         anchor = bonus
         ks.append(k)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
     ms_draft = [x[0].elapsed_time(x[1]) for x in ev]
     ms_lm_call = [x[1].elapsed_time(x[2]) for x in ev]
     ms_lm = [x[0].elapsed_time(x[1]) for x in evk]
@@ -148,7 +158,7 @@ def run_gpu(args):
         "draft_ms": float(np.mean(ms_draft)), "append_ms": float(np.mean(ms_append)),
         "lm_head_ms": lm_ms, "lm_head_gbs": by["lm_head"] / (lm_ms * 1e-3) / 1e9,
         "lm_head_call_ms": float(np.mean(ms_lm_call)),
-        "mean_accepted": float(np.mean(ks[args.warmup:])), "bytes": by,
+        "mean_accepted": float(np.mean(ks[args.warmup:b0])), "bytes": by, "breakdown_rounds": nb,
     }
 
     # ---------------- block 16, p = 0.6 synthetic target --------------------------------
@@ -173,7 +183,8 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     stream = torch.cuda.current_stream()
     g = binding.Drafter(sh, dw, max_block=B)
     g.cache_append(torch.from_numpy(synth.resid_rows(sh, context, 0)).to(torch.bfloat16).to(dev), commit=True)
-    n = warmup + steps
+    nb = min(steps, BREAKDOWN_ROUNDS)  # event-timed rounds after the timed ones
+    n = warmup + steps + nb
     resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, 1000 * (tag + 1) + r) for r in range(n)]))
     resid = resid.to(torch.bfloat16).to(dev)
     u = torch.from_numpy(np.stack([synth.accept_draws(B, r, tag) for r in range(n)])).to(dev)  # f64 [n, 3, B+1]
@@ -189,16 +200,20 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     vout = torch.empty(3, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)
     done = torch.cuda.Event()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
     anchor = synth.anchor_token(sh, tag=tag)
     ks = []
     torch.cuda.synchronize()
-    t0 = None
+    t0 = el = None
+    b0 = warmup + steps
     for r in range(n):
         if r == warmup:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-        e = ev[r - warmup] if r >= warmup else None
+        if r == b0:
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+        e = ev[r - b0] if r >= b0 else None
         if e: e[0].record(stream)
         g.draft_block(anchor, B, tokens=toks, stream=stream)
         if e: e[1].record(stream)
@@ -222,7 +237,6 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         anchor = bonus
         ks.append(k)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
     by = alg_bytes(sh, B, g.cache_state()[0])
     rs = steps / el
     fwd = float(np.mean([x[0].elapsed_time(x[1]) + x[2].elapsed_time(x[3]) for x in ev]))
@@ -230,7 +244,7 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
             "round_hbm_frac": round(by["block_forward"] * rs / (HBM_PEAK_GBS * 1e9), 4),
             "block_forward_ms": round(fwd, 4),
             "block_forward_hbm_frac": round(by["block_forward"] / (fwd * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-            "mean_accepted": round(float(np.mean(ks[warmup:])), 4), "steps": steps}
+            "mean_accepted": round(float(np.mean(ks[warmup:b0])), 4), "steps": steps}
 
 
 def run_q4(args) -> dict:
