@@ -2,9 +2,9 @@
 
 A step is one whole round over one block of synthetic input: the drafter's block forward
 (dflash_draft_block), the target verify rows through the shared lm_head
-(dflash_lm_head_argmax), greedy verify (dflash_verify_greedy), the append of the B+1
-verify residual rows (dflash_cache_append), one device->host copy of (k, bonus) and the
-trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
+(dflash_lm_head_argmax), greedy verify (dflash_verify_greedy, whose kernel writes (k,
+bonus, status) into pinned host memory), the append of the B+1 verify residual rows
+(dflash_cache_append), the host's wait for that result and the trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
 timed rounds record no timing events (a HIP event record holds the stream for a few
 microseconds); a pass of up to 100 more rounds after them records events around the draft,
 the append and the lm_head argmax kernel for the per-call breakdown and `roofline`.
@@ -98,8 +98,7 @@ def run_gpu(args):
     resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, r + 1) for r in range(n)])).to(torch.bfloat16).to(dev)
     toks = torch.empty(B, dtype=torch.int32, device=dev)
     a = torch.empty(B + 1, dtype=torch.int32, device=dev)
-    vout = torch.empty(3, dtype=torch.int32, device=dev)
-    host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
     done = torch.cuda.Event()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
     # events around the argmax kernel alone (the library records them on the call's stream)
@@ -126,11 +125,10 @@ def run_gpu(args):
         if e: g.time_next_argmax(*evk[r - b0])
         g.lm_head_argmax(vrows[r], out=a, stream=stream)
         if e: e[2].record(stream)
-        g.verify_greedy(toks, a, B, out=vout, stream=stream)
+        g.verify_greedy(toks, a, B, out=host, stream=stream)
         if e: e[3].record(stream)
         g.cache_append(resid[r], stream=stream)
         if e: e[4].record(stream)
-        host.copy_(vout, non_blocking=True)
         done.record(stream)
         while not done.query():  # spin: the round's one host round trip, without a blocking wait
             pass
@@ -173,8 +171,9 @@ def run_gpu(args):
 
 def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: float, tag: int) -> dict:
     """Rounds of block B whose verify-row argmaxes come from the p-accept stand-in target
-    (computed on the device from pre-drawn uniforms): draft, verify, append, one D2H copy of
-    (k, bonus), trim. The block forward is the event-timed draft plus append."""
+    (computed on the device from pre-drawn uniforms): draft, verify (result written into
+    pinned host memory), append, the host's wait for (k, bonus), trim. The block forward is
+    the event-timed draft plus append."""
     import torch
 
     from block_drafting_dflash_amd import binding, synth
@@ -197,8 +196,7 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     tgt_all[:, B] = (torch.floor(u[:, 2, B] * V) % V).int()
     other = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty(B, dtype=torch.int32, device=dev)
-    vout = torch.empty(3, dtype=torch.int32, device=dev)
-    host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
     done = torch.cuda.Event()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
     anchor = synth.anchor_token(sh, tag=tag)
@@ -223,11 +221,10 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         torch.add(toks, off[r], out=other)
         torch.remainder(other, V, out=other)
         torch.where(acc[r], toks, other, out=tgt[:B])
-        g.verify_greedy(toks, tgt, B, out=vout, stream=stream)
+        g.verify_greedy(toks, tgt, B, out=host, stream=stream)
         if e: e[2].record(stream)
         g.cache_append(resid[r], stream=stream)
         if e: e[3].record(stream)
-        host.copy_(vout, non_blocking=True)
         done.record(stream)
         while not done.query():  # spin: the round's one host round trip, without a blocking wait
             pass

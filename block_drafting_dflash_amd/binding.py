@@ -244,7 +244,13 @@ class Drafter:
             raise ValueError("draft needs block rows and target block + 1")
         if out is None:
             out = torch.empty(3, dtype=torch.int32, device=self.device)
-        self._dev(out, torch.int32)
+        if out.device.type == "cpu":
+            # pinned host memory: the verify kernel writes the result there itself, readable
+            # once the stream has passed the call (no device->host copy)
+            if not (out.is_pinned() and out.dtype == torch.int32 and out.is_contiguous() and out.numel() >= 3):
+                raise ValueError("a host output must be a pinned, contiguous int32 tensor of 3 elements")
+        else:
+            self._dev(out, torch.int32)
         _check(lib().dflash_verify_greedy(self.ctx, _ptr(draft), _ptr(target), int(block), _ptr(out),
                                           _stream(stream)), self.ctx)
         return out

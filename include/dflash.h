@@ -196,7 +196,8 @@ dflash_status dflash_time_next_argmax(dflash_ctx *ctx, void *start, void *end);
  * Greedy exact-match verify of one block (lablup/mlxcel #1751, Implementation Review
  * Summary: greedy exact-match verify rule, verify width = block + 1). d_draft: device
  * int32 [block] = d_1..d_block; d_target: device int32 [block+1] = the target's argmax
- * at verify rows e..e+block. d_out (device int32 [3]) receives k = the number of leading
+ * at verify rows e..e+block. d_out (int32 [3]: device memory, or pinned host memory from
+ * hipHostMalloc, which the kernel then writes directly) receives k = the number of leading
  * rows with d_{i+1} == a_i (0..block), the bonus token a_k, and a status word: 0, or 1
  * if any target id lies outside [0, vocab) (then k = 0 and bonus = -1).
  */

@@ -93,6 +93,26 @@ def test_draft_is_bit_reproducible(micro_bf16_w):
     assert torch.equal(outs[0][1], outs[1][1])
 
 
+def test_verify_result_into_pinned_host_memory(micro_f32_w):
+    """The verify kernel writes (k, bonus, status) straight into pinned host memory: the same
+    words as a device buffer, for accepted lengths 0..B and an out-of-range target id."""
+    sh, B = MICRO_F32, 5
+    g = binding.Drafter(sh, binding.to_device(sh, micro_f32_w), max_block=B)
+    host = torch.full((3,), -7, dtype=torch.int32).pin_memory()
+    d = torch.tensor([3, 1, 4, 1, 5], dtype=torch.int32, device="cuda")
+    cases = [P.target_with_accept_length(d.cpu().numpy(), k, sh.vocab, tail=11 + k) for k in range(B + 1)]
+    cases.append(np.array([3, sh.vocab + 2, 0, 0, 0, 0]))
+    for a in cases:
+        t = torch.from_numpy(a.astype(np.int32)).cuda()
+        want = g.verify_greedy(d, t, B).cpu().tolist()
+        host.fill_(-7)
+        g.verify_greedy(d, t, B, out=host)
+        torch.cuda.synchronize()
+        assert host.tolist() == want, (a, want)
+    with pytest.raises(ValueError):
+        g.verify_greedy(d, t, B, out=torch.empty(3, dtype=torch.int32))  # not pinned
+
+
 def test_boundary_errors_leave_state_unchanged(micro_f32_w):
     sh = MICRO_F32
     g = binding.Drafter(sh, binding.to_device(sh, micro_f32_w), max_block=4)
