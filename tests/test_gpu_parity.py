@@ -187,6 +187,39 @@ def test_micro_bf16_deferred_kv_rounds(micro_bf16_w, block, phase, context):
     print("micro-bf16 deferred stats", block, ls.stats)
 
 
+def test_deferred_kv_call_sequences(micro_bf16_w):
+    """Sequences the round loop never makes, in lock-step with the oracle: a read-back
+    between an append and its trim, two pending appends before one trim, a committing
+    append over deferred rows, and a draft whose rows and the committed ones do not fit one
+    row tile (the rows are projected on their own first)."""
+    sh = MICRO_BF16
+    ls = P.LockStep(sh, micro_bf16_w, max_block=14, phase=16, check_windows=False)
+    ls.append(synth.resid_rows(sh, 27, 0), commit=True)
+    anchor = synth.anchor_token(sh, tag=9)
+    ls.draft(anchor, 4)
+    ls.append(synth.resid_rows(sh, 5, 1))   # deferred
+    ls.check_window()                         # read-back projects the pending rows
+    ls.trim(2)
+    ls.draft((anchor + 1) % sh.vocab, 4)  # nothing left to fold
+    ls.append(synth.resid_rows(sh, 5, 2))   # deferred
+    ls.append(synth.resid_rows(sh, 3, 3))   # projects the first five, defers these three
+    ls.trim(4)                                # keeps 5 + 3 - 4 = 4 rows, of them 0 deferred
+    ls.draft((anchor + 2) % sh.vocab, 8)
+    ls.append(synth.resid_rows(sh, 9, 4))   # deferred
+    ls.trim(1)                                # 8 committed rows
+    ls.draft((anchor + 3) % sh.vocab, 13)  # 14 + 8 rows > one tile: projected first
+    ls.append(synth.resid_rows(sh, 3, 5))   # deferred
+    ls.trim(0)
+    ls.append(synth.resid_rows(sh, 6, 6), commit=True)  # projects them, then these six
+    ls.draft((anchor + 4) % sh.vocab, 1)
+    ls.append(synth.resid_rows(sh, 2, 7))   # deferred
+    ls.trim(1)
+    ls.draft((anchor + 5) % sh.vocab, 6)  # folds the one committed row
+    torch.cuda.synchronize()
+    ls.check_window()
+    print("deferred sequences stats", ls.stats)
+
+
 @pytest.mark.parametrize("block", [4, 8])
 def test_deferred_kv_matches_immediate_projection(micro_bf16_w, block):
     """The same rounds with the window read after every trim (the verified rows' K/V
