@@ -197,22 +197,22 @@ def test_deferred_kv_call_sequences(micro_bf16_w):
     ls.append(synth.resid_rows(sh, 27, 0), commit=True)
     anchor = synth.anchor_token(sh, tag=9)
     ls.draft(anchor, 4)
-    ls.append(synth.resid_rows(sh, 5, 1))   # deferred
-    ls.check_window()                         # read-back projects the pending rows
+    ls.append(synth.resid_rows(sh, 5, 1))  # deferred
+    ls.check_window()  # read-back projects the pending rows
     ls.trim(2)
     ls.draft((anchor + 1) % sh.vocab, 4)  # nothing left to fold
-    ls.append(synth.resid_rows(sh, 5, 2))   # deferred
-    ls.append(synth.resid_rows(sh, 3, 3))   # projects the first five, defers these three
-    ls.trim(4)                                # keeps 5 + 3 - 4 = 4 rows, of them 0 deferred
+    ls.append(synth.resid_rows(sh, 5, 2))  # deferred
+    ls.append(synth.resid_rows(sh, 3, 3))  # projects the first five, defers these three
+    ls.trim(4)  # keeps 5 + 3 - 4 = 4 rows, of them 0 deferred
     ls.draft((anchor + 2) % sh.vocab, 8)
-    ls.append(synth.resid_rows(sh, 9, 4))   # deferred
-    ls.trim(1)                                # 8 committed rows
+    ls.append(synth.resid_rows(sh, 9, 4))  # deferred
+    ls.trim(1)  # 8 committed rows
     ls.draft((anchor + 3) % sh.vocab, 13)  # 14 + 8 rows > one tile: projected first
-    ls.append(synth.resid_rows(sh, 3, 5))   # deferred
+    ls.append(synth.resid_rows(sh, 3, 5))  # deferred
     ls.trim(0)
     ls.append(synth.resid_rows(sh, 6, 6), commit=True)  # projects them, then these six
     ls.draft((anchor + 4) % sh.vocab, 1)
-    ls.append(synth.resid_rows(sh, 2, 7))   # deferred
+    ls.append(synth.resid_rows(sh, 2, 7))  # deferred
     ls.trim(1)
     ls.draft((anchor + 5) % sh.vocab, 6)  # folds the one committed row
     torch.cuda.synchronize()
