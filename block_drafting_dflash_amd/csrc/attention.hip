@@ -17,7 +17,9 @@
 // MFMA kernel forms the block's own keys and values itself from the raw projections and
 // uses them in place of the ring slots of positions e..e+R-1, which lie past the committed
 // window; the other paths (f32 shapes, long blocks) write them into those slots first (the
-// append of the verified rows overwrites them either way). The ring is zeroed when the
+// append of the verified rows overwrites them either way). The MFMA kernel also takes the
+// last n committed rows, e-n..e-1, from the raw projections when an append left their K/V
+// to this draft: it forms them the same way, uses them, and writes them into their slots. The ring is zeroed when the
 // context is created, so every slot holds finite values and keys outside a query's window
 // can be read and given weight exactly 0.
 //
