@@ -131,12 +131,13 @@ bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
 // 2048, operand rows of one row tile staged through LDS): bf16 single-plane rows run
 // fastest at two tiles (four past 16 rows), bf16 hi/lo pairs, with twice the operand loads
 // and products, at four (eight past 8 rows, where whole-round runs favoured it); 4-bit
-// heads, bound by dequantisation rather than bytes, at eight for hi/lo pairs and four
-// (eight past 16 rows) for single-plane rows.
+// heads at eight for hi/lo pairs (four up to 5 rows, where that launch reads its lo
+// fragments from LDS and fits two work-groups per CU) and four (eight past 16 rows) for
+// single-plane rows.
 int argmax_tiles_per_wg(int wt, int split, int ntiles, int rows) {
   if (ntiles < 1024) return 1;
   if (ntiles < 8192) return 2;
-  if (wt == WT_Q4) return split ? 8 : (rows > 16 ? 8 : 4);
+  if (wt == WT_Q4) return split ? (rows <= 5 ? 4 : 8) : (rows > 16 ? 8 : 4);
   if (!split) return rows > 16 ? 4 : 2;
   return rows > 8 ? 8 : 4;
 }

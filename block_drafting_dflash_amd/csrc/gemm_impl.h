@@ -102,7 +102,11 @@ __device__ __forceinline__ SegSel select_seg(const GemmParams& p, int col) {
 // and get two per CU (<= 128 VGPRs); launches with more row tiles, normed operands, or
 // hi/lo operand pairs across several chunks or weight blocks take the full budget and
 // fewer, larger work-groups; the multi-tile argmax launches three.
-template <int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int gemm_min_waves_per_simd() {
+template <int WT, int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexpr int gemm_min_waves_per_simd() {
+  // 4-bit heads over a few hi/lo rows, four tiles per work-group, read their lo fragments
+  // from LDS at each step (gemm_kernel), which brings them to four waves per SIMD: two
+  // 8-wave work-groups per CU
+  if (WT == WT_Q4 && SPLIT && XSRC == XSRC_LDS && RT == 1 && NCH == 1 && T == 4) return 4;
   if (RT > 1 || XSRC == XSRC_NORM) return 2;
   if (T > 1) return 3;
   if (SPLIT && (NCH > 1 || NB > 1)) return 2;
@@ -135,7 +139,7 @@ constexpr int gemm_chunks_ahead() {
   constexpr int argmax_ahead = Q4 && !SPLIT ? 3 : 1;
   if (EPI == EPI_ARGMAX || !BF) return nit < argmax_ahead ? nit : argmax_ahead;
   if ((XSRC == XSRC_NORM && RT == 1) || XSRC == XSRC_GLOBAL) return 1;
-  constexpr int budget = 512 / gemm_min_waves_per_simd<RT, NB, XSRC, T, NCH, SPLIT>();
+  constexpr int budget = 512 / gemm_min_waves_per_simd<WT, RT, NB, XSRC, T, NCH, SPLIT>();
   constexpr int planes = SPLIT ? 2 : 1;
   constexpr int frag = RT * CH * 4 * planes;  // operand VGPRs of one chunk's fragments
   constexpr int raw = XSRC == XSRC_NORM ? RT * CH * 4 * 2 + CH * 4 : 0;
@@ -159,7 +163,7 @@ constexpr int gemm_chunks_ahead() {
 
 // T tiles per work-group, NCH chunks of CH steps per wave per tile, all compile-time.
 template <int WT, int RT, int NB, int EPI, int XSRC_IN, int T, int NCH, int CH, bool SPLIT>
-__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<RT, NB, xsrc_base(XSRC_IN), T, NCH, SPLIT>())) void
+__global__ __launch_bounds__(512, (gemm_min_waves_per_simd<WT, RT, NB, xsrc_base(XSRC_IN), T, NCH, SPLIT>())) void
 gemm_kernel(const GemmParams p) {
   constexpr int XSRC = xsrc_base(XSRC_IN);
   using Tr = WTr<WT>;
@@ -202,6 +206,12 @@ gemm_kernel(const GemmParams p) {
   constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RROWS * RT <= 32;
   constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * Tr::KSTEP == 256;
   constexpr int STG_N_ROWS = RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows a normed launch stages
+  constexpr bool STG_L = BF && XSRC == XSRC_LDS && RT == 1 && NCH == 1;
+  // 4-bit weights over hi/lo rows staged once per work-group, four tiles per work-group: each
+  // step's lo fragment is read from the staged rows where it is used instead of being held
+  // with the hi fragments (vocabulary argmax at 4 and 5 rows 65 -> 58 us; at 8 and 16 rows
+  // it measured slower, and those launches keep eight tiles and held fragments)
+  constexpr bool LO_LDS = Q4 && SPLIT && STG_L && T == 4;
   constexpr int SP = SPLIT ? 2 : 1;          // operand planes
   constexpr int LK = CH * Tr::KSTEP;          // k of one chunk
   constexpr int GU = LK * 2 / 16;             // lanes per staged bf16 row (32 or 16)
@@ -348,7 +358,7 @@ gemm_kernel(const GemmParams p) {
   // operand fragments of this wave's K slice, built once (staged sources only)
   constexpr int XR = XSRC == XSRC_GLOBAL ? 1 : NCH;
   u32x4_t xr[XR][RT][CH];
-  u32x4_t xrl[SPLIT ? XR : 1][SR][CH];  // lo halves of staged pairs
+  u32x4_t xrl[SPLIT && !LO_LDS ? XR : 1][SR][LO_LDS ? 1 : CH];  // lo halves of staged pairs
   // q4: per 64-k group, the sum of the operand values of each accumulator row (staged
   // sources: built once from the staged fragments)
   constexpr int NG = (Q4 && XSRC != XSRC_GLOBAL) ? XR * CH / 2 : 1;
@@ -366,7 +376,8 @@ gemm_kernel(const GemmParams p) {
         if constexpr (SPLIT) xl = xlb[rt][st];
       } else {
         xf = xr[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
-        if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
+        if constexpr (LO_LDS) xl = frag_xs(rt, st, 1);
+        else if constexpr (SPLIT) xl = xrl[XSRC == XSRC_GLOBAL ? 0 : c][rt][st];
       }
     };
     if constexpr (Q4) {
@@ -636,7 +647,6 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) load_w(wbuf[i], sbuf[i], i);
   load_resid();
-  constexpr bool STG_L = BF && XSRC == XSRC_LDS && RT == 1 && NCH == 1;
   if constexpr (STG_L) {
     // LDS-source rows (the argmax rows), behind the first weight chunk: the R real rows of
     // each plane over the wave's k range (512 bytes: 32 lanes, two rows per load) into the
@@ -666,7 +676,7 @@ gemm_kernel(const GemmParams p) {
       const int r = min(li, R - 1);
       const size_t o = (size_t)r * lds.row_bytes + (st * Tr::KSTEP + lg * Tr::EPL) * 2;
       xr[0][0][st] = *(const u32x4_t*)(xs + o);
-      if constexpr (SPLIT) xrl[0][0][st] = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + o);
+      if constexpr (SPLIT && !LO_LDS) xrl[0][0][st] = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + o);
     }
   } else if constexpr (XSRC == XSRC_LDS) {
     // LDS-source planes of more row tiles or chunks: every chunk into the operand
@@ -744,7 +754,8 @@ gemm_kernel(const GemmParams p) {
         for (int tt = 0; tt < 2; ++tt) {
           const int st = 2 * gi + tt;
           a = mfma_bf16(xr[st / CH][rt][st % CH], ones, a);
-          if constexpr (SPLIT) a = mfma_bf16(xrl[st / CH][rt][st % CH], ones, a);
+          if constexpr (LO_LDS) a = mfma_bf16(frag_xs(rt, st % CH, 1), ones, a);
+          else if constexpr (SPLIT) a = mfma_bf16(xrl[st / CH][rt][st % CH], ones, a);
         }
         xg[gi][rt] = a;
       }
