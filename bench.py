@@ -188,13 +188,13 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     resid = resid.to(torch.bfloat16).to(dev)
     u = torch.from_numpy(np.stack([synth.accept_draws(B, r, tag) for r in range(n)])).to(dev)  # f64 [n, 3, B+1]
     V = sh.vocab
-    # the stand-in target's draws that do not depend on the draft, made before timing: accept
-    # flags, the offset of a rejected row's token, and the bonus row's token
-    acc = u[:, 0, :B] < p
-    off = (1 + torch.floor(u[:, 1, :B] * (V - 1))).int()
+    # the stand-in target's draws that do not depend on the draft, made before timing: per
+    # row a 0/1 word that rejects the row (its token then differs from the draft token in the
+    # lowest bit, a valid id since the vocabulary size is even), and the bonus row's token
+    assert V % 2 == 0, "the stand-in target flips the lowest bit of a token id"
+    flip = (u[:, 0, :B] >= p).int()
     tgt_all = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
     tgt_all[:, B] = (torch.floor(u[:, 2, B] * V) % V).int()
-    other = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty(B, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
     done = torch.cuda.Event()
@@ -216,11 +216,9 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         g.draft_block(anchor, B, tokens=toks, stream=stream)
         if e: e[1].record(stream)
         # stand-in for the target's verify-row argmaxes (the target model is out of scope):
-        # row i keeps the draft token with probability p, else (token + offset) mod V
+        # row i keeps the draft token with probability p, else another token (one kernel)
         tgt = tgt_all[r]
-        torch.add(toks, off[r], out=other)
-        torch.remainder(other, V, out=other)
-        torch.where(acc[r], toks, other, out=tgt[:B])
+        torch.bitwise_xor(toks, flip[r], out=tgt[:B])
         g.verify_greedy(toks, tgt, B, out=host, stream=stream)
         if e: e[2].record(stream)
         g.cache_append(resid[r], stream=stream)
