@@ -4,7 +4,9 @@ A step is one whole round over one block of synthetic input: the drafter's block
 (dflash_draft_block), the target verify rows through the shared lm_head
 (dflash_lm_head_argmax), greedy verify (dflash_verify_greedy, whose kernel writes (k,
 bonus, status) into pinned host memory), the append of the B+1 verify residual rows
-(dflash_cache_append), the host's wait for that result and the trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
+(dflash_cache_append), the host's wait for that result (polled in pinned memory, so the
+append still runs while the host trims and enqueues the next round) and the trim
+(dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
 timed rounds record no timing events (a HIP event record holds the stream for a few
 microseconds); a pass of up to 100 more rounds after them records events around the draft,
 the append and the lm_head argmax kernel for the per-call breakdown and `roofline`.
@@ -35,6 +37,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BREAKDOWN_ROUNDS = 100  # event-timed rounds after the timed ones (per-call breakdown, kernel timing)
+
+
+def await_verify(hv, timeout_s: float = 10.0):
+    """Spin until the verify kernel has written (k, bonus, status) into the pinned words hv
+    (each preset to -1). Each word changes once, from -1 to its value; k and status are
+    never -1 once written, bonus only with status 1. The append enqueued after the verify may
+    still run: the next round's launches queue behind it on the stream."""
+    t0 = time.perf_counter()
+    while True:
+        k, bonus, status = int(hv[0]), int(hv[1]), int(hv[2])
+        if k != -1 and status != -1 and (bonus != -1 or status == 1):
+            return k, bonus, status
+        if time.perf_counter() - t0 > timeout_s:
+            raise RuntimeError("the verify result did not arrive in pinned host memory")
 
 
 def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
@@ -99,7 +115,7 @@ def run_gpu(args):
     toks = torch.empty(B, dtype=torch.int32, device=dev)
     a = torch.empty(B + 1, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
-    done = torch.cuda.Event()
+    hv = host.numpy()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
     # events around the argmax kernel alone (the library records them on the call's stream)
     evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)]
@@ -125,14 +141,12 @@ def run_gpu(args):
         if e: g.time_next_argmax(*evk[r - b0])
         g.lm_head_argmax(vrows[r], out=a, stream=stream)
         if e: e[2].record(stream)
+        hv[:] = -1
         g.verify_greedy(toks, a, B, out=host, stream=stream)
         if e: e[3].record(stream)
         g.cache_append(resid[r], stream=stream)
         if e: e[4].record(stream)
-        done.record(stream)
-        while not done.query():  # spin: the round's one host round trip, without a blocking wait
-            pass
-        k, bonus, status = host.tolist()
+        k, bonus, status = await_verify(hv)  # the round's one host round trip
         assert status == 0
         g.cache_trim(B - k)
         anchor = bonus
@@ -197,7 +211,7 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
     tgt_all[:, B] = (torch.floor(u[:, 2, B] * V) % V).int()
     toks = torch.empty(B, dtype=torch.int32, device=dev)
     host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
-    done = torch.cuda.Event()
+    hv = host.numpy()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
     anchor = synth.anchor_token(sh, tag=tag)
     ks = []
@@ -219,14 +233,12 @@ def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: f
         # row i keeps the draft token with probability p, else another token (one kernel)
         tgt = tgt_all[r]
         torch.bitwise_xor(toks, flip[r], out=tgt[:B])
+        hv[:] = -1
         g.verify_greedy(toks, tgt, B, out=host, stream=stream)
         if e: e[2].record(stream)
         g.cache_append(resid[r], stream=stream)
         if e: e[3].record(stream)
-        done.record(stream)
-        while not done.query():  # spin: the round's one host round trip, without a blocking wait
-            pass
-        k, bonus, status = host.tolist()
+        k, bonus, status = await_verify(hv)  # the round's one host round trip
         assert status == 0
         g.cache_trim(B - k)
         anchor = bonus
