@@ -113,3 +113,16 @@ def test_q4_ctx2048_width_sweep(muse_q4, block):
     ks = P.run_synthetic_rounds(ls, wl.context, block, 24, p=p, tag=block)
     _report(f"{wl.name} block {block} p {p:.3f}", ls, ks)
     assert ls.stats.max_hidden_rel <= 2e-3
+
+
+def test_q4_ctx2048_deferred_kv(muse_q4):
+    """4-bit Muse-shaped drafter at block 4 with the verified rows' K/V projected inside the
+    next draft (window read back every third trim and at the end)."""
+    w, dev = muse_q4
+    wl = synth.WORKLOADS["muse-q4-sweep-ctx2048"]
+    ls = P.LockStep(wl.shape, w, max_block=4, dev_weights=dev, window_period=3)
+    ks = P.run_random_depth_rounds(ls, wl.context, 4, 8, tag=41)
+    torch.cuda.synchronize()
+    ls.check_window()
+    _report(f"{wl.name} block 4 deferred", ls, ks)
+    assert ls.stats.max_hidden_rel <= 2e-3
