@@ -830,13 +830,9 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
   }
   const size_t lds = (size_t)(ATTN_CHUNK * (a.hd + 1) + ATTN_CHUNK * a.hd + ATTN_QG * a.hd + ATTN_QG * ATTN_CHUNK) * 4;
   const void* fn = bf ? (const void*)attn_partial_kernel<true> : (const void*)attn_partial_kernel<false>;
-  static bool attr_set[2] = {false, false};
-  hipError_t err = hipSuccess;
-  if (!attr_set[bf ? 1 : 0]) {
-    err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set[bf ? 1 : 0] = true;
-  }
+  static std::atomic<bool> cleared[2][MAX_DEVICES];
+  hipError_t err = clear_dynamic_lds(fn, lds, cleared[bf ? 1 : 0]);
+  if (err != hipSuccess) return err;
   if (bf)
     hipLaunchKernelGGL(attn_partial_kernel<true>, grid, dim3(256), lds, s, a, ring_layer, qb, qlo, R, e, nch, part);
   else

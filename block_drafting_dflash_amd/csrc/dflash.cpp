@@ -808,14 +808,16 @@ dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, voi
   if (!ctx) return DFLASH_E_ARG;
   const Cfg& g = ctx->cfg;
   if (layer < 0 || layer >= g.c.layers) return fail(ctx, DFLASH_E_RANGE, "layer %d outside 0..%d", layer, g.c.layers - 1);
-  if (!n_out) return fail(ctx, DFLASH_E_ARG, "NULL count output");
+  if (!n_out || !k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL count or window output");
   const int64_t lo = std::max<int64_t>(0, ctx->e - g.c.window);
   const int n = (int)(ctx->e - lo);
-  *n_out = n;
-  if (n == 0) return DFLASH_OK;
+  if (n == 0) {
+    *n_out = 0;
+    return DFLASH_OK;
+  }
   const dflash_status s = flush_kv(ctx, (hipStream_t)stream);
   if (s != DFLASH_OK) return s;
-  if (!k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL window output");
+  *n_out = n;
   const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
   return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),
              "cache read");

@@ -805,12 +805,9 @@ template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, boo
 static hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
   const size_t lds = gemm_lds_layout(WT, XSRC, SPLIT ? 1 : 0, p.R, p.waves, NB, p.K, T).total;
   auto fn = gemm_kernel<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>;
-  static size_t attr_lds = 64 * 1024;  // dynamic LDS this kernel is cleared for
-  if (lds > attr_lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_lds = lds;
-  }
+  static std::atomic<bool> cleared[MAX_DEVICES];
+  const hipError_t e = clear_dynamic_lds((const void*)fn, lds, cleared);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(p.waves * 64), lds, s, p);
   return hipGetLastError();
 }

@@ -3,7 +3,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace dflash {
+
+constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per compute unit
+
+// A kernel may take more than 64 KiB of dynamic LDS only once it has been cleared for it,
+// and the clearance holds per device. `cleared` is the kernel's own per-device flag array:
+// the first launch past 64 KiB on a device clears the kernel for the whole LDS of a compute
+// unit there (one value, so racing host threads agree on it).
+constexpr int MAX_DEVICES = 64;
+inline hipError_t clear_dynamic_lds(const void* fn, size_t lds, std::atomic<bool>* cleared) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  if (cleared[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  if (e == hipSuccess) cleared[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 enum { WT_F32 = 0, WT_BF16 = 1, WT_Q4 = 2 };  // weight storage (matches dflash_dtype)
 
@@ -23,7 +44,6 @@ __host__ __device__ constexpr int xsrc_base(int xsrc) { return xsrc == XSRC_NORM
 // MFMA steps per pipelined chunk (16-byte weight loads per lane per chunk): deeper for one
 // row tile, shallower when 2-3 row tiles of activations also sit in registers.
 __host__ __device__ constexpr int chunk_steps(int rt) { return rt == 1 ? 8 : 4; }
-constexpr int LDS_BYTES = 160 * 1024;  // gfx950 LDS per compute unit
 enum { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ARGMAX = 3 };
 
 // One weight matrix [rows, K] in fragment-major blocks (launch_pack) whose outputs occupy

@@ -19,8 +19,15 @@
  *    context is.
  *  - `stream` is a hipStream_t (NULL = the default stream). Device calls only enqueue
  *    work; outputs are valid once the caller has synchronised the stream.
- *  - Every call returns a status. On error nothing is enqueued and the context is
- *    unchanged; dflash_last_error() describes the failure. Nothing throws or aborts.
+ *  - Every call returns a status and dflash_last_error() describes a failure. Arguments
+ *    and the context's state are checked on the host before anything is enqueued: on
+ *    DFLASH_E_ARG, _SHAPE, _RANGE, _NO_CONTEXT, _REWIND or _STATE nothing is enqueued and
+ *    the context is unchanged. DFLASH_E_DEVICE means a HIP call failed part way: launches
+ *    enqueued before it stay enqueued (for instance the K/V projection of deferred rows,
+ *    after which the context no longer counts them as deferred), the committed offsets are
+ *    unchanged, and the stream should be treated as failed. Nothing throws or aborts
+ *    (lablup/mlxcel #1751, Security fixes: an exception crossing the bridge aborts the
+ *    process instead of failing the request).
  *  - A context is used by one host thread and one stream at a time.
  *  - Weight matrices are [out, in] row-major (y = x W^T). bf16 is raw 16-bit storage.
  */
@@ -118,7 +125,10 @@ dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, s
                                  size_t *packed_bytes);
 
 /* Validate cfg and the weight pointers, bind the caller's buffers and initialise the
- * workspace on `stream`. ring, workspace and packed must be at least the queried sizes and
+ * workspace on `stream`. The drafter shares the target's raw embedding table and untied
+ * lm_head by pointer (lablup/mlxcel #1762, What changed: the Drafter adapter binds the
+ * target's raw embedding table and untied lm_head); config dimensions are bounded before
+ * any device call (same page, Pre-merge review round, third finding). ring, workspace and packed must be at least the queried sizes and
  * 256-byte aligned. Every linear (fc, lm_head and the layer linears) is copied once into
  * `packed` in a fragment-major order: each 16-row x 16-byte-per-lane block of the matrix
  * becomes one contiguous kilobyte in the lane order of the MFMA operand, so that the
@@ -162,17 +172,21 @@ dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
 
 /*
  * Draft one block: rows [anchor, mask x block] at absolute positions e..e+block are
- * embedded with the raw table, run through every layer over the ring's committed
- * context and the block's own keys, and rows 1..block go through final_norm and the
- * lm_head. The ring slots of positions e..e+block lie past the committed window: a layer
- * may store the block's own k/v there (f32 shapes do; dflash_cache_read never returns
- * those slots and the next append overwrites them), and
- * of the committed window only rows whose projection an append left to this call are
- * written (their ring slots, once). d_tokens (device int32 [block]) receives the
- * first index of each row's maximum f32 logit. d_hidden (device f32 [block+1, hidden], or NULL) receives the
- * residual stream after the last layer. Errors: block outside 1..max_block or anchor
- * outside [0, vocab) (DFLASH_E_RANGE); e == 0 (DFLASH_E_NO_CONTEXT); pending rows
- * (DFLASH_E_STATE).
+ * embedded with the raw table, run through every layer over the ring's committed context
+ * and the block's own keys, and rows 1..block go through final_norm and the lm_head. The
+ * layers are Qwen3-shaped and bidirectional (z-lab/dflash #168, Why: is_causal False);
+ * each attends under |q - k| <= W over absolute positions, with per-head q/k norms, and the
+ * embedding table and lm_head are the target's (lablup/mlxcel #1762, What changed); the
+ * context K/V come from the cache with the block's own K/V after them (lablup/mlxcel
+ * #1751, Implementation Review Summary).
+ * The ring slots of positions e..e+block lie past the committed window: a layer may store
+ * the block's own k/v there (f32 shapes do; dflash_cache_read never returns those slots and
+ * the next append overwrites them), and of the committed window only rows whose projection
+ * an append left to this call are written (their ring slots, once). d_tokens (device int32
+ * [block]) receives the first index of each row's maximum f32 logit. d_hidden (device f32
+ * [block+1, hidden], or NULL) receives the residual stream after the last layer. Errors:
+ * block outside 1..max_block or anchor outside [0, vocab) (DFLASH_E_RANGE); NULL d_tokens
+ * (DFLASH_E_ARG); e == 0 (DFLASH_E_NO_CONTEXT); pending rows (DFLASH_E_STATE).
  */
 dflash_status dflash_draft_block(dflash_ctx *ctx, int32_t anchor, int32_t block, int32_t *d_tokens,
                                  float *d_hidden, void *stream);
@@ -209,7 +223,10 @@ dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pen
                                  int32_t *capacity);
 
 /* Copy one layer's live window, positions max(0, e-W)..e-1 in position order, into
- * k_out and v_out (device, act_dtype [kv_heads, n, head_dim]); *n_out = n (host). */
+ * k_out and v_out (device, act_dtype [kv_heads, n, head_dim], at least kv_heads * min(e, W)
+ * * head_dim elements each); *n_out = n (host). Rows whose K/V an append deferred are
+ * projected into the ring first. Errors: NULL n_out, k_out or v_out, or a layer outside
+ * 0..layers-1 (nothing enqueued). */
 dflash_status dflash_cache_read(dflash_ctx *ctx, int32_t layer, void *k_out, void *v_out, int32_t *n_out,
                                 void *stream);
 

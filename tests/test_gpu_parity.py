@@ -309,3 +309,94 @@ def test_argmax_timing_hook(micro_bf16_w):
     torch.cuda.synchronize()
     assert k0.elapsed_time(k1) == kernel_ms
     assert binding.lib().dflash_time_next_argmax(g.ctx, ctypes.c_void_p(k0.cuda_event), None) == 1  # DFLASH_E_ARG
+
+
+def test_lm_head_exact_tie_goes_to_the_lowest_index(micro_bf16_w):
+    """Two bit-identical lm_head rows give bit-identical logits, and the argmax takes the lower
+    index (the first maximum), on the verify-row path (one bf16 operand plane) and on the
+    drafted rows (final norm, hi/lo operand pairs); the oracle agrees with margin exactly 0."""
+    from oracle import dflash_oracle as O
+
+    sh = MICRO_BF16
+    lm0 = micro_bf16_w["lm_head"]
+    # verify rows: row 0 points along lm_head row t, whose copy sits at the end of the table
+    t, s = 7, sh.vocab - 5
+    lm = lm0.copy()
+    lm[s] = lm[t]
+    w = dict(micro_bf16_w, lm_head=lm)
+    rows = synth.verify_hidden(sh, 6, 11)
+    rows[0] = synth.to_bf16_values(lm[t] / np.float32(0.02))
+    g = binding.Drafter(sh, binding.to_device(sh, w), max_block=4)
+    got = g.lm_head_argmax(torch.from_numpy(rows).to(torch.bfloat16).cuda()).cpu().numpy()
+    oi, om = O.OracleDrafter(sh, w, 4).lm_head_argmax(rows)
+    assert om[0] == 0.0 and oi[0] == t and got[0] == t
+    for i in range(1, len(rows)):
+        assert om[i] <= P.MARGIN or got[i] == oi[i]
+    # drafted rows: copy the winner v of a clearly decided drafted row into a lower, unused row
+    prefill = synth.resid_rows(sh, 30, 0)
+    anchor = 5
+    od = O.OracleDrafter(sh, micro_bf16_w, 4)
+    od.append(prefill, commit=True)
+    ref = od.draft(anchor, 4)
+    g0 = binding.Drafter(sh, binding.to_device(sh, micro_bf16_w), max_block=4)
+    g0.cache_append(torch.from_numpy(prefill).to(torch.bfloat16).cuda(), commit=True)
+    d0 = g0.draft_block(anchor, 4).cpu().numpy()
+    j = next(j for j in range(4) if ref.margins[j] > P.MARGIN and d0[j] == ref.tokens[j] and d0[j] > 8)
+    v = int(d0[j])
+    m = min(set(range(v)) - set(int(x) for x in d0))
+    lm2 = lm0.copy()
+    lm2[m] = lm2[v]
+    w2 = dict(micro_bf16_w, lm_head=lm2)
+    g2 = binding.Drafter(sh, binding.to_device(sh, w2), max_block=4)
+    g2.cache_append(torch.from_numpy(prefill).to(torch.bfloat16).cuda(), commit=True)
+    d2 = g2.draft_block(anchor, 4).cpu().numpy()
+    od2 = O.OracleDrafter(sh, w2, 4)
+    od2.append(prefill, commit=True)
+    r2 = od2.draft(anchor, 4)
+    assert r2.tokens[j] == m and r2.margins[j] == 0.0
+    assert d2[j] == m
+    for i in range(4):
+        assert d2[i] == (m if d0[i] == v else d0[i]), (i, d0, d2)
+
+
+def test_append_without_a_residual_stream_is_refused(micro_f32_w):
+    """dflash_cache_append through the C-ABI with a NULL slab, zero rows or a negative count:
+    DFLASH_E_ARG ("no residual stream captured"), nothing enqueued, offsets unchanged; a real
+    append afterwards still matches the oracle."""
+    sh = MICRO_F32
+    ls = P.LockStep(sh, micro_f32_w, max_block=4)
+    L = binding.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = torch.from_numpy(synth.resid_rows(sh, 4, 0)).cuda()
+    st0 = ls.gpu.cache_state()
+    for ptr, n in [(None, 4), (None, 0), (rows.data_ptr(), 0), (rows.data_ptr(), -2)]:
+        for commit in (0, 1):
+            assert L.dflash_cache_append(ls.gpu.ctx, ptr, n, commit, stream) == 1  # DFLASH_E_ARG
+            assert b"no residual stream captured" in L.dflash_last_error(ls.gpu.ctx)
+            assert ls.gpu.cache_state() == st0
+    ls.append(synth.resid_rows(sh, 13, 0), commit=True)
+    torch.cuda.synchronize()
+    ls.check_window()
+
+
+def test_micro_bf16_block129_deepest_rewind(micro_bf16_w):
+    """Block 129: the slack is 129 rows (the block floor past the 128 cap). Rounds that accept
+    nothing rewind 129 of the 130 appended rows, the deepest rewind a round makes; after
+    every trim the live window is read back and compared with the oracle, and the next
+    draft sees no corrupted key."""
+    sh, B = MICRO_BF16, 129
+    ls = P.LockStep(sh, micro_bf16_w, max_block=B, phase=8)
+    assert ls.gpu.cache_state()[2] == B
+    ls.append(synth.resid_rows(sh, 40, 0), commit=True)
+    torch.cuda.synchronize()
+    ls.check_window()
+    anchor = synth.anchor_token(sh, tag=129)
+    for r, kk in enumerate([0, 0, 5, B, 0]):
+        d = ls.draft(anchor, B)
+        a = P.target_with_accept_length(d, kk, sh.vocab, tail=anchor + r)
+        k, bonus = ls.verify(d, a)
+        assert k == kk
+        ls.append(synth.resid_rows(sh, B + 1, 700 + r))
+        ls.trim(B - k)
+        anchor = bonus
+    print("block 129 stats", ls.stats)

@@ -1,0 +1,143 @@
+"""Planted mistakes in a copy of the oracle must fail its pins.
+
+Each mutant rewrites one passage of oracle/dflash_oracle.py's source text with a plausible
+mistake (a dropped term, a wrong sign or index, a transposed operand, an off-by-one
+position, a missing floor) and loads the result as a module of its own. The pins of
+tests/test_oracle_pins.py then run against that module in place of the oracle, cheapest
+first; a mutant is caught when one of them fails (an assertion or any error). The real
+oracle file is never modified.
+"""
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+from block_drafting_dflash_amd import synth
+from tests import test_oracle_pins as pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dflash_oracle.py")
+
+# (name, passage of the oracle, mistaken replacement)
+MUTANTS = [
+    ("verify rows through final_norm before the lm_head",
+     "logits = self.lm_head_logits(self._act(np.asarray(rows, dtype=F64)))",
+     "logits = self.lm_head_logits(rms_norm(self._act(np.asarray(rows, dtype=F64)), self._gain('final_norm'), "
+     "self.sh.rms_eps))"),
+    ("verify-row logits from the embedding table",
+     "logits = self.lm_head_logits(self._act(np.asarray(rows, dtype=F64)))",
+     "logits = self._act(np.asarray(rows, dtype=F64)) @ np.asarray(self.w['embed'], dtype=F64).T"),
+    ("RoPE rotation sign", "return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)",
+     "return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)"),
+    ("RoPE interleaved pairing", "x1, x2 = x[..., :half], x[..., half:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
+    ("RoPE frequency exponent", "inv = theta ** (-2.0 * np.arange(half, dtype=F64) / hd)",
+     "inv = theta ** (-1.0 * np.arange(half, dtype=F64) / hd)"),
+    ("RMSNorm without eps", "(np.mean(x * x, axis=-1, keepdims=True) + eps)", "(np.mean(x * x, axis=-1, keepdims=True))"),
+    ("RMSNorm sum instead of mean", "np.mean(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-1, keepdims=True)"),
+    ("SiLU without its input factor", "return x / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(-x))"),
+    ("slack without the block floor", "return max(min(max(8 * block, 32), 128), block)",
+     "return min(max(8 * block, 32), 128)"),
+    ("bonus token one row late", "return k, int(target[k])", "return k, int(target[min(k + 1, B)])"),
+    ("verify compares against the next target row", "while k < B and int(draft[k]) == int(target[k]):",
+     "while k < B and int(draft[k]) == int(target[k + 1]):"),
+    ("argmax takes the last maximum", "idx = np.argmax(logits, axis=1)",
+     "idx = logits.shape[1] - 1 - np.argmax(logits[:, ::-1], axis=1)"),
+    ("argmax margin sign", "return idx, top2[:, 1] - top2[:, 0]", "return idx, top2[:, 0] - top2[:, 1]"),
+    ("q4 nibbles highest first", "codes[:, j::8] = (packed >> np.uint32(4 * j)) & np.uint32(0xF)",
+     "codes[:, j::8] = (packed >> np.uint32(28 - 4 * j)) & np.uint32(0xF)"),
+    ("window edge exclusive", "vis = np.abs(qpos[:, None] - kpos[None, :]) <= self.W",
+     "vis = np.abs(qpos[:, None] - kpos[None, :]) < self.W"),
+    ("attention scale 1/hd", "scale = 1.0 / np.sqrt(sh.head_dim)", "scale = 1.0 / sh.head_dim"),
+    ("GQA heads interleaved", "g = h // group", "g = h % sh.kv_heads"),
+    ("lm_head reads rows 0..B-1", "z = rms_norm(x[1:], self._gain(\"final_norm\"), sh.rms_eps)",
+     "z = rms_norm(x[:-1], self._gain(\"final_norm\"), sh.rms_eps)"),
+    ("attention without its residual", "x = x + o @ self._lin(p + \"o\").T", "x = o @ self._lin(p + \"o\").T"),
+    ("W_o transposed", "x = x + o @ self._lin(p + \"o\").T", "x = x + o @ self._lin(p + \"o\")"),
+    ("gate and up swapped",
+     "a = silu(h2 @ self._lin(p + \"gate\").T) * (h2 @ self._lin(p + \"up\").T)",
+     "a = silu(h2 @ self._lin(p + \"up\").T) * (h2 @ self._lin(p + \"gate\").T)"),
+    ("trim ignores the rewind", "self.e += self.span - m", "self.e += self.span"),
+    ("block positions one late", "qpos = self.e + np.arange(R, dtype=np.int64)",
+     "qpos = self.e + 1 + np.arange(R, dtype=np.int64)"),
+    ("cached K/V not rounded to the cache dtype", "return self._act(k), self._act(v)", "return k, v"),
+    ("anchor embedded as a mask row", "x = self.embed([anchor] + [sh.mask_id] * block)",
+     "x = self.embed([sh.mask_id] * (block + 1))"),
+    ("committing append keeps one row too few", "keep_from = end - self.W if commit else end - self.C",
+     "keep_from = end - self.W + 1 if commit else end - self.C"),
+    ("context includes the position at e", "(self.slot_pos >= 0) & (self.slot_pos <= self.e - 1)",
+     "(self.slot_pos >= 0) & (self.slot_pos <= self.e)"),
+    ("q_norm gain dropped", "q = rope_neox(rms_norm(q, self._gain(p + \"q_norm\"), sh.rms_eps), qpos, sh.rope_theta)",
+     "q = rope_neox(rms_norm(q, 1.0, sh.rms_eps), qpos, sh.rope_theta)"),
+    ("k_norm on context rows dropped", "k = rms_norm(k, self._gain(f\"layers.{layer}.k_norm\"), sh.rms_eps)",
+     "k = k"),
+    ("pending append placed at e", "start = self.e + self.span", "start = self.e"),
+    ("encoder norm dropped", "return rms_norm(h, self._gain(\"enc_norm\"), self.sh.rms_eps)", "return h"),
+    ("MLP reads the pre-attention norm", "h2 = rms_norm(x, self._gain(p + \"post_norm\"), sh.rms_eps)",
+     "h2 = h"),
+]
+
+
+def load_mutant(old: str, new: str) -> types.ModuleType:
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"passage not found exactly once: {old!r}"
+    name = "dflash_oracle_mutant"
+    mod = types.ModuleType(name)
+    mod.__file__ = ORACLE_SRC
+    sys.modules[name] = mod  # dataclasses resolve their annotations through sys.modules
+    try:
+        exec(compile(src.replace(old, new), ORACLE_SRC + " (mutant)", "exec"), mod.__dict__)
+    finally:
+        del sys.modules[name]
+    return mod
+
+
+@pytest.fixture(scope="module")
+def pin_calls():
+    """Every pin of test_oracle_pins as a call, cheapest first."""
+    mw = synth.make_weights(pins.MICRO, threads=2)
+    mbw = synth.make_weights(pins.MICRO_BF16, threads=2)
+    P = pins
+    calls = [
+        P.test_slack_rule_matches_page_table, P.test_round_bf16_hand_values,
+        P.test_rms_norm_and_silu_match_torch, P.test_rope_hand_values_fix_pairing_and_sign, P.test_rope_identities,
+        P.test_q4_pack_hand_values_and_quantizer_round_trip, P.test_argmax_first_max_and_margin,
+        lambda: P.test_verify_row_lm_head_argmax_hand_values("f32"),
+        lambda: P.test_verify_row_lm_head_argmax_hand_values("bf16"),
+        lambda: P.test_verify_row_lm_head_argmax_matches_torch_linear(mw, mbw, "f32"),
+        lambda: P.test_verify_row_lm_head_argmax_matches_torch_linear(mw, mbw, "bf16"),
+        lambda: P.test_verify_exhaustive_over_binary_blocks(4),
+        lambda: P.test_boundary_errors_leave_state_unchanged(mw),
+        lambda: P.test_uniform_query_attention_counts_the_inclusive_window(mw),
+        lambda: P.test_zero_layers_reduce_to_lm_head_of_the_embedding(mw),
+        lambda: P.test_full_window_reduces_to_unmasked_attention(mw),
+        lambda: P.test_forward_matches_torch_formulation_over_rounds(mw, 5, 12, 3, 4),
+        lambda: P.test_forward_bf16_matches_torch_formulation(mbw),
+        lambda: P.test_dropping_rows_before_the_encoder_changes_nothing(mw),
+        lambda: P.test_post_trim_window_equals_cache_rebuilt_from_committed_prefix(mw, 3),
+        lambda: P.test_pending_appends_equal_one_append(mw),
+        lambda: P.test_outputs_do_not_depend_on_ring_phase(mw),
+        lambda: P.test_slack_below_the_block_corrupts_the_window_and_the_rewind_is_refused(mw),
+        P.test_q4_drafter_equals_the_dequantized_f64_drafter,
+        lambda: P.test_forward_matches_torch_formulation_over_rounds(mw, 3, 20, 4, 1),
+        P.test_counter_definitions_reproduce_page_arithmetic,
+    ]
+    return calls
+
+
+def test_real_oracle_passes_every_pin_call(pin_calls):
+    for call in pin_calls:
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_fails_a_pin(pin_calls, monkeypatch, name, old, new):
+    mod = load_mutant(old, new)
+    monkeypatch.setattr(pins, "O", mod)
+    for call in pin_calls:
+        try:
+            with np.errstate(all="ignore"):
+                call()
+        except Exception:
+            return  # caught
+    pytest.fail(f"no pin fails with the planted mistake: {name}")

@@ -143,6 +143,53 @@ def test_argmax_first_max_and_margin():
 
 
 # ---------------------------------------------------------------------------------------
+# the verify rows through the shared lm_head
+# ---------------------------------------------------------------------------------------
+
+def _hand_lm_head_drafter(g, act):
+    sh = synth.Shape(hidden=g["hidden"], layers=1, q_heads=1, kv_heads=1, head_dim=4, intermediate=4,
+                     vocab=len(g["lm_head"]), target_streams=1, target_width=4, window=2,
+                     weight_dtype=act, act_dtype=act)
+    w = {k: np.array(g[k], dtype=np.float32) for k in ("lm_head", "embed", "final_norm")}
+    return O.OracleDrafter(sh, w, 1)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_verify_row_lm_head_argmax_hand_values(act):
+    """Hand-worked logits of bf16-exact rows through a 5-row lm_head: plain dot products (no
+    norm, no scale), the first index of the maximum on exact ties, and the top-2 margins."""
+    g = gold("lm_head_argmax_hand.json")
+    od = _hand_lm_head_drafter(g, act)
+    rows = np.array(g["rows"], dtype=np.float32)
+    np.testing.assert_array_equal(od.lm_head_logits(rows), np.array(g["logits"], dtype=np.float64))
+    idx, margin = od.lm_head_argmax(rows)
+    assert idx.tolist() == g["argmax"]
+    np.testing.assert_array_equal(margin, np.array(g["margin"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_verify_row_lm_head_argmax_matches_torch_linear(micro_w, micro_bf16_w, act):
+    """The verify rows (storage dtype) through torch's F.linear with the shared lm_head, then
+    torch.argmax (first maximum) and torch.topk margins, all in float64."""
+    sh, w = (MICRO, micro_w) if act == "f32" else (MICRO_BF16, micro_bf16_w)
+    rows = synth.verify_hidden(sh, 11, 3)
+    od = O.OracleDrafter(sh, w, 4)
+    idx, margin = od.lm_head_argmax(rows)
+    logits = F.linear(torch.from_numpy(rows.astype(np.float64)), torch.from_numpy(w["lm_head"].astype(np.float64)))
+    assert idx.tolist() == torch.argmax(logits, dim=1).tolist()
+    top = torch.topk(logits, 2, dim=1).values
+    np.testing.assert_allclose(margin, (top[:, 0] - top[:, 1]).numpy(), rtol=1e-12, atol=1e-14)
+    # a tie planted by duplicating the winning lm_head row below itself goes to the lower row
+    w2 = dict(w)
+    lm = w["lm_head"].copy()
+    lm[2] = lm[idx[0]]
+    w2["lm_head"] = lm
+    idx2, margin2 = O.OracleDrafter(sh, w2, 4).lm_head_argmax(rows[:1])
+    if idx[0] > 2:
+        assert idx2[0] == 2 and margin2[0] == 0.0
+
+
+# ---------------------------------------------------------------------------------------
 # verify, synthetic target and counters
 # ---------------------------------------------------------------------------------------
 
@@ -339,6 +386,31 @@ def test_post_trim_window_equals_cache_rebuilt_from_committed_prefix(micro_w, bl
     r1, r2 = od.draft(anchor, block), fresh.draft(anchor, block)
     assert np.array_equal(r1.tokens, r2.tokens)
     np.testing.assert_allclose(r1.hidden, r2.hidden, rtol=1e-12)
+
+
+def test_pending_appends_equal_one_append(micro_w):
+    """Two pending appends before one trim place their rows at consecutive positions: the
+    same offsets, window and next draft as one append of both row sets."""
+    sh = MICRO.with_(window=6)
+    a = O.OracleDrafter(sh, micro_w, 4)
+    b = O.OracleDrafter(sh, micro_w, 4)
+    for od in (a, b):
+        od.append(synth.resid_rows(sh, 9, 0), commit=True)
+    r1, r2 = synth.resid_rows(sh, 3, 1), synth.resid_rows(sh, 2, 2)
+    a.append(r1)
+    a.append(r2)
+    b.append(np.concatenate([r1, r2]))
+    assert a.state() == b.state() == (9, 5, a.S, a.C)
+    a.trim(1)
+    b.trim(1)
+    assert a.state()[:2] == b.state()[:2] == (13, 0)
+    for l in range(sh.layers):
+        pa, ka, va = a.live_window(l)
+        pb, kb, vb = b.live_window(l)
+        assert np.array_equal(pa, pb)
+        np.testing.assert_array_equal(ka, kb)
+        np.testing.assert_array_equal(va, vb)
+    np.testing.assert_array_equal(a.draft(7, 4).hidden, b.draft(7, 4).hidden)
 
 
 def test_outputs_do_not_depend_on_ring_phase(micro_w):
