@@ -19,7 +19,8 @@ DFLASH_F32, DFLASH_BF16, DFLASH_Q4G64 = 0, 1, 2
 _DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
 
 EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
-           "dflash_draft_block", "dflash_lm_head_argmax", "dflash_time_next_argmax", "dflash_verify_greedy",
+           "dflash_draft_block", "dflash_lm_head_argmax", "dflash_lm_head_argmax_noalloc", "dflash_time_next_argmax",
+           "dflash_verify_greedy",
            "dflash_cache_state",
            "dflash_cache_read", "dflash_last_error", "dflash_status_string")
 
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         "dflash_cache_trim": (i32, [vp, i32]),
         "dflash_draft_block": (i32, [vp, i32, i32, vp, vp, vp]),
         "dflash_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
+        "dflash_lm_head_argmax_noalloc": (i32, [vp, vp, i32, vp, vp]),
         "dflash_time_next_argmax": (i32, [vp, vp, vp]),
         "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
         "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
@@ -223,6 +225,19 @@ class Drafter:
             out = torch.empty(n, dtype=torch.int32, device=self.device)
         self._dev(out, torch.int32)
         _check(lib().dflash_lm_head_argmax(self.ctx, _ptr(rows), n, _ptr(out), _stream(stream)), self.ctx)
+        return out
+
+    def lm_head_argmax_noalloc(self, rows: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """lm_head_argmax whose scratch is the library's fixed per-GPU array (no allocation:
+        the caller provides the output too)."""
+        self._dev(rows, self.act_dtype)
+        if rows.dim() != 2 or rows.shape[1] != self.shape.hidden:
+            raise ValueError("rows must be [n, hidden]")
+        self._dev(out, torch.int32)
+        if out.numel() < rows.shape[0]:
+            raise ValueError("output too small")
+        _check(lib().dflash_lm_head_argmax_noalloc(self.ctx, _ptr(rows), rows.shape[0], _ptr(out), _stream(stream)),
+               self.ctx)
         return out
 
     def time_next_argmax(self, start: "torch.cuda.Event", end: "torch.cuda.Event") -> None:

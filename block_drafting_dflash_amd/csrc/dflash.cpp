@@ -15,6 +15,7 @@
 
 #include "../../include/dflash.h"
 #include "kernels.h"
+#include "noalloc.h"
 
 using namespace dflash;
 
@@ -64,6 +65,9 @@ struct dflash_ctx {
   unsigned char* ring;
   unsigned char* ws;
   int cus = 256;        // compute units of the device the context was created on
+  int device = 0;       // that device
+  // that device's copy of the fixed argmax key array (dflash_lm_head_argmax_noalloc)
+  unsigned long long* noalloc_keys = nullptr;
   int64_t e = 0;        // committed context end (absolute position)
   int64_t pending = 0;  // rows appended since the last trim
   // rows at positions kv_pos .. kv_pos + kv_rows - 1 whose encoder rows (fc output) sit in
@@ -326,6 +330,9 @@ struct GemmCall {
   // tile whose raw rows are staged through LDS
   const void* gain2 = nullptr;
   int r2 = 0;
+  // argmax only: per-work-group keys go here (part_bytes long) instead of the workspace
+  unsigned long long* part = nullptr;
+  size_t part_bytes = 0;
 };
 
 dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
@@ -399,9 +406,15 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
       pl.grid = p.ntiles / 2;
     }
     if (gc.epi == EPI_ARGMAX) {
-      p.part = (unsigned long long*)(ctx->ws + ctx->lay.argmax_part);
       pl.tiles_per_wg = argmax_tiles_per_wg(wt, gc.split, p.ntiles, rc);
       pl.grid = (p.ntiles + pl.tiles_per_wg - 1) / pl.tiles_per_wg;
+      p.part = (unsigned long long*)(ctx->ws + ctx->lay.argmax_part);
+      if (gc.part) {  // callers check the bound before the first launch (argmax_key_bytes)
+        if ((size_t)rc * pl.grid * sizeof(unsigned long long) > gc.part_bytes)
+          return fail(ctx, DFLASH_E_SHAPE, "argmax keys of %d rows x %d work-groups exceed %zu bytes", rc, pl.grid,
+                      gc.part_bytes);
+        p.part = gc.part;
+      }
     } else {
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
       p.ylo = gc.ylo ? (unsigned char*)gc.ylo + (size_t)r0 * gc.ldy * y_elt : nullptr;
@@ -479,7 +492,49 @@ dflash_status flush_kv(dflash_ctx* ctx, hipStream_t st) {
   return s;
 }
 
+// Bound on the per-work-group key bytes of one vocabulary argmax launch over rows given in
+// the activation dtype (at most 32 rows per launch; fewer tiles per work-group, so more
+// work-groups, at fewer rows).
+size_t argmax_key_bytes(const Cfg& g, int n) {
+  const int ntiles = g.c.vocab / 16;
+  const int tpw = argmax_tiles_per_wg(g.wt, 0, ntiles, 1);
+  return (size_t)std::min(n, 32) * (size_t)((ntiles + tpw - 1) / tpw) * sizeof(unsigned long long);
+}
+
 }  // namespace
+
+namespace dflash {
+
+// dflash_lm_head_argmax with the per-work-group argmax keys in `keys` (keys_bytes long) in
+// place of the context's workspace; nothing is enqueued unless every launch fits.
+dflash_status lm_head_argmax_into(dflash_ctx* ctx, const void* rows, int32_t n, int32_t* d_idx,
+                                  unsigned long long* keys, size_t keys_bytes, hipStream_t st) {
+  if (!ctx) return DFLASH_E_ARG;
+  if (!rows || !d_idx) return fail(ctx, DFLASH_E_ARG, "NULL rows or output");
+  if (n < 1 || n > 4096) return fail(ctx, DFLASH_E_RANGE, "row count %d outside 1..4096", n);
+  if (!keys) return fail(ctx, DFLASH_E_DEVICE, "no argmax key scratch on this device");
+  const size_t need = argmax_key_bytes(ctx->cfg, n);
+  if (need > keys_bytes)
+    return fail(ctx, DFLASH_E_SHAPE, "vocabulary %d needs %zu bytes of argmax keys, above the %zu-byte scratch",
+                ctx->cfg.c.vocab, need, keys_bytes);
+  const dflash_config& c = ctx->cfg.c;
+  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, c.hidden, rows, c.hidden, nullptr, nullptr, 0,
+              d_idx};
+  lm.part = keys;
+  lm.part_bytes = keys_bytes;
+  return run_gemm(ctx, lm, n, st);
+}
+
+dflash_status noalloc_keys_for_call(dflash_ctx* ctx, unsigned long long** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device)
+    return fail(ctx, DFLASH_E_ARG, "the context's device %d is not current", ctx->device);
+  if (!ctx->noalloc_keys) return fail(ctx, DFLASH_E_DEVICE, "no argmax key array on device %d", ctx->device);
+  *out = ctx->noalloc_keys;
+  return DFLASH_OK;
+}
+
+}  // namespace dflash
 
 // ======================================================================================
 extern "C" {
@@ -565,15 +620,21 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   }
   ctx->ring = (unsigned char*)ring;
   ctx->ws = (unsigned char*)workspace;
+  hipError_t e = hipGetDevice(&ctx->device);
   {
-    int dev_id = 0, cus = 0;
-    if (hipGetDevice(&dev_id) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev_id) == hipSuccess && cus > 0)
+    int cus = 0;
+    if (e == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ctx->device) == hipSuccess &&
+        cus > 0)
       ctx->cus = cus;
+  }
+  // the device address of this device's fixed argmax key array, for the allocation-free argmax
+  if (e == hipSuccess) {
+    void* keys = nullptr;
+    e = noalloc_scratch_address(ctx->device, &keys);
+    ctx->noalloc_keys = (unsigned long long*)keys;
   }
   hipStream_t st = (hipStream_t)stream;
   // repack every linear into fragment-major blocks; the context reads only the packed copies
-  hipError_t e = hipSuccess;
   {
     const dflash_config& c = g.c;
     const int H = c.hidden, qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim;

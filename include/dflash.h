@@ -197,6 +197,18 @@ dflash_status dflash_draft_block(dflash_ctx *ctx, int32_t anchor, int32_t block,
  * softcap). 1 <= n <= 4096. */
 dflash_status dflash_lm_head_argmax(dflash_ctx *ctx, const void *rows, int32_t n, int32_t *d_idx, void *stream);
 
+/* dflash_lm_head_argmax without any device allocation, for callers that cannot allocate
+ * device memory at the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it). Same rows, output and result as dflash_lm_head_argmax; its per-work-group
+ * argmax keys go to a fixed 4 MiB device array of the library (one copy per GPU, held until
+ * the process ends) instead of the context's workspace, so nothing is allocated or freed.
+ * Every call on one GPU shares that array: calls that overlap on one GPU (several streams or
+ * host threads) race on it. Call with the context's device current. Errors: as
+ * dflash_lm_head_argmax; DFLASH_E_SHAPE (nothing enqueued) if the vocabulary needs more keys
+ * than the array holds (above 524288 rows); DFLASH_E_ARG if another device is current. */
+dflash_status dflash_lm_head_argmax_noalloc(dflash_ctx *ctx, const void *rows, int32_t n, int32_t *d_idx,
+                                            void *stream);
+
 /* Kernel timing of the vocabulary argmax (profiling; no counterpart on the pages). The next
  * dflash_lm_head_argmax call on ctx records `start` on its stream right before its first
  * argmax GEMM launch (rows 0..31) and `end` right after it, before the per-row reduction
