@@ -1,22 +1,28 @@
 """Throughput of one DFlash speculative round at batch 1 on one MI355X.
 
 A step is one whole round over one block of synthetic input: the drafter's block forward
-(dflash_draft_block), the target verify rows through the shared lm_head
-(dflash_lm_head_argmax), greedy verify (dflash_verify_greedy, whose kernel writes (k,
-bonus, status) into pinned host memory), the append of the B+1 verify residual rows
-(dflash_cache_append), the host's wait for that result (polled in pinned memory, so the
-append still runs while the host trims and enqueues the next round) and the trim
-(dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
+(dflash_draft_block), the target's verify-row argmaxes (through the shared lm_head with
+dflash_lm_head_argmax, or a stand-in target), greedy verify (dflash_verify_greedy, whose
+kernel writes (k, bonus, status) into pinned host memory), the append of the B+1 verify
+residual rows (dflash_cache_append), the host's wait for that result (polled in pinned
+memory, so the append still runs while the host trims and enqueues the next round) and the
+trim (dflash_cache_trim). Inputs are resident in HBM before the timed region starts. The
 timed rounds record no timing events (a HIP event record holds the stream for a few
-microseconds); a pass of up to 100 more rounds after them records events around the draft,
-the append and the lm_head argmax kernel for the per-call breakdown and `roofline`.
+microseconds); the host stamps the arrival of each round's verify result, whose spacing gives
+the per-round time distribution, and a pass of up to 100 more rounds after them records
+events around the draft, the append and the lm_head argmax kernel for the per-call
+breakdown and `roofline`.
 
 Workload (timed as `value`): muse-bf16-b4-ctx1024 -- Muse-assistant-shaped bf16 drafter
 (hidden 2048, 5 layers, 32/4 heads x 128, intermediate 6144, vocab 202048, untied lm_head,
 fc 20480 -> 2048), context 1024, window 2048, block 4, verify rows N(0,1) through the
-lm_head. Also reported: the block-16 round (muse-bf16-b16-ctx4096, p = 0.6 synthetic
-target), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16) and the CPU oracle
-timed on the host cores.
+lm_head. Also reported, each with the round counters the pages print (draft_rounds, draft_n,
+draft_n_accepted, mean accepted with and without the bonus, committed tok/s, accept
+histogram, SHA-256 of the committed token stream): the block-16 round (muse-bf16-b16-ctx4096,
+p = 0.6 stand-in target), the 16384-row context with ring wraps at blocks 8 and 32 (prefill
+timed on its own), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16), the tiny
+f32 round (tiny-f32-b4-ctx64), an HBM streaming-read probe, and the CPU oracle on the host
+cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -56,10 +62,11 @@ def await_verify(hv, timeout_s: float = 10.0):
 def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
     """Algorithmic bytes of one round: every weight read once, live K/V window, inputs.
 
-    Weights cost 2 bytes per parameter in bf16 and 9/16 in q4 (a 4-bit code plus a bf16
-    scale and bias per 64 inputs); activations, the ring and the embedding rows are bf16."""
-    e = 2  # bf16
-    we = 9 / 16 if sh.weight_dtype == "q4" else 2
+    Weights cost 4 bytes per parameter in f32, 2 in bf16 and 9/16 in q4 (a 4-bit code plus
+    a bf16 scale and bias per 64 inputs); activations, the ring and the embedding rows take
+    the activation dtype."""
+    e = 4 if sh.act_dtype == "f32" else 2
+    we = {"f32": 4, "bf16": 2, "q4": 9 / 16}[sh.weight_dtype]
     H, I, V, F = sh.hidden, sh.intermediate, sh.vocab, sh.fc_in
     qd, kvd = sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim
     layer = (qd * H + 2 * kvd * H + H * qd + 2 * I * H + H * I) * we
@@ -83,175 +90,242 @@ def counted_traffic():
     return d["traffic_bytes"] if d.get("kernel_source_sha256") == hashlib.sha256(src).hexdigest() else None
 
 
-def run_gpu(args):
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+class Leg:
+    """Rounds of one drafter context: block B, a verify source, timed without events, then a
+    breakdown pass with events; round counters and the committed token stream."""
+
+    def __init__(self, sh, dw, B: int, context: int, phase: int = 0):
+        import torch
+
+        from block_drafting_dflash_amd import binding, synth
+
+        self.torch, self.synth, self.binding = torch, synth, binding
+        self.sh, self.B = sh, B
+        self.dev = torch.device("cuda", 0)
+        self.stream = torch.cuda.current_stream()
+        self.act = binding.act_torch_dtype(sh)
+        self.g = binding.Drafter(sh, dw, max_block=B, phase=phase)
+        slab = torch.from_numpy(synth.resid_rows(sh, context, 0)).to(self.act).to(self.dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        self.g.cache_append(slab, commit=True, stream=self.stream)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        self.prefill_ms = e0.elapsed_time(e1)
+        del slab
+
+    def run(self, warmup: int, steps: int, verify, resid_tag: int, anchor_tag: int, lm_timing: bool = False) -> dict:
+        """verify(r, toks_r, out_r): enqueue the target's argmaxes of round r into out_r;
+        verify.prepare(tgt), if present, fills what does not depend on the draft beforehand."""
+        torch, synth = self.torch, self.synth
+        g, sh, B, dev, stream = self.g, self.sh, self.B, self.dev, self.stream
+        nb = min(steps, BREAKDOWN_ROUNDS)
+        n = warmup + steps + nb
+        resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, resid_tag + r) for r in range(n)]))
+        resid = resid.to(self.act).to(dev)
+        toks = torch.empty((n, B), dtype=torch.int32, device=dev)  # each round's drafted tokens stay
+        tgt = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+        host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes here
+        hv = host.numpy()
+        if hasattr(verify, "prepare"):
+            verify.prepare(tgt)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
+        evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)] if lm_timing else None
+        for pair in evk or []:
+            for x in pair:
+                x.record(stream)  # creates the underlying events before the timed region
+        anchor = synth.anchor_token(sh, tag=anchor_tag)
+        ks, bonuses, stamps = [], [], []
+        torch.cuda.synchronize()
+        t0 = el = None
+        b0 = warmup + steps
+        for r in range(n):
+            if r == warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                stamps.append(t0)
+            if r == b0:
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+            e = ev[r - b0] if r >= b0 else None
+            if e: e[0].record(stream)
+            g.draft_block(anchor, B, tokens=toks[r], stream=stream)
+            if e: e[1].record(stream)
+            if e and evk: g.time_next_argmax(*evk[r - b0])
+            verify(r, toks[r], tgt[r])
+            if e: e[2].record(stream)
+            hv[:] = -1
+            g.verify_greedy(toks[r], tgt[r], B, out=host, stream=stream)
+            if e: e[3].record(stream)
+            g.cache_append(resid[r], stream=stream)
+            if e: e[4].record(stream)
+            k, bonus, status = await_verify(hv)  # the round's one host round trip
+            if warmup <= r < b0:
+                stamps.append(time.perf_counter())
+            assert status == 0
+            g.cache_trim(B - k)
+            anchor = bonus
+            ks.append(k)
+            bonuses.append(bonus)
+        torch.cuda.synchronize()
+        from block_drafting_dflash_amd.counters import RoundCounters
+
+        d = toks.cpu().numpy()
+        stream_toks = []
+        cnt = RoundCounters()
+        for r in range(n):
+            stream_toks.extend(int(x) for x in d[r, :ks[r]])
+            stream_toks.append(bonuses[r])
+            if warmup <= r < b0:
+                cnt.record(B, ks[r])
+        rs = steps / el
+        gaps_ms = np.diff(np.asarray(stamps)) * 1e3
+        by = alg_bytes(sh, B, g.cache_state()[0])
+        fwd = [x[0].elapsed_time(x[1]) + x[3].elapsed_time(x[4]) for x in ev]
+        out = {
+            "block": B, "rounds_per_s": round(rs, 2), "drafted_tok_s": round(rs * B, 1),
+            "committed_tok_s": round(cnt.emitted / el, 1),
+            "round_ms": {"mean": round(1e3 * el / steps, 4), "median": round(pct(gaps_ms, 50), 4),
+                         "p90": round(pct(gaps_ms, 90), 4)},
+            "rounds_per_s_median": round(1e3 / pct(gaps_ms, 50), 2),
+            "block_forward_ms": round(float(np.mean(fwd)), 4),
+            "block_forward_hbm_frac": round(by["block_forward"] / (float(np.mean(fwd)) * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "draft_ms": round(float(np.mean([x[0].elapsed_time(x[1]) for x in ev])), 4),
+            "append_ms": round(float(np.mean([x[3].elapsed_time(x[4]) for x in ev])), 4),
+            **cnt.as_dict(),
+            "committed_token_sha256": hashlib.sha256(np.asarray(stream_toks, dtype="<i4").tobytes()).hexdigest(),
+            "committed_tokens": len(stream_toks), "steps": steps, "breakdown_rounds": nb,
+            "_bytes": by, "_elapsed_s": el,
+        }
+        if evk:
+            out["_lm_ms"] = float(np.mean([x[0].elapsed_time(x[1]) for x in evk]))
+            out["_lm_call_ms"] = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
+        return out
+
+
+def lm_head_verify(leg, n_rounds: int, seed_tag: int = 0):
+    """Verify rows N(0,1) [B+1, hidden] of each round through the shared lm_head."""
+    torch, synth = leg.torch, leg.synth
+    rows = torch.from_numpy(np.stack([synth.verify_hidden(leg.sh, leg.B + 1, seed_tag + r) for r in range(n_rounds)]))
+    rows = rows.to(leg.act).to(leg.dev)
+
+    def verify(r, toks_r, out_r):
+        leg.g.lm_head_argmax(rows[r], out=out_r, stream=leg.stream)
+    return verify
+
+
+def flip_verify(leg, flip, last):
+    """Stand-in target (the target model is not built): row i < B takes the draft token with
+    its lowest bit flipped where flip[r, i] is 1 (a valid, different id since the vocabulary
+    size is even), the draft token itself elsewhere; row B is last[r]. One kernel per round."""
+    torch = leg.torch
+    assert leg.sh.vocab % 2 == 0, "the stand-in target flips the lowest bit of a token id"
+    flip = flip.to(torch.int32).to(leg.dev)
+    last = last.to(torch.int32).to(leg.dev)
+
+    def verify(r, toks_r, out_r):
+        torch.bitwise_xor(toks_r, flip[r], out=out_r[:leg.B])
+
+    def prepare(tgt):
+        tgt[:, leg.B] = last[:tgt.shape[0]]
+    verify.prepare = prepare
+    return verify
+
+
+def accept_p_verify(leg, n_rounds: int, p: float, tag: int):
+    """p-accept stand-in: row i keeps the draft token with probability p (pre-drawn uniforms)."""
+    torch, synth = leg.torch, leg.synth
+    u = torch.from_numpy(np.stack([synth.accept_draws(leg.B, r, tag) for r in range(n_rounds)]))
+    flip = (u[:, 0, :leg.B] >= p).int()
+    last = torch.floor(u[:, 2, leg.B] * leg.sh.vocab) % leg.sh.vocab
+    return flip_verify(leg, flip, last)
+
+
+def random_depth_verify(leg, n_rounds: int, tag: int):
+    """Accepted length drawn uniformly from 0..B each round: the draft token is flipped at
+    row k only (trims of random depth B - k)."""
+    torch, synth = leg.torch, leg.synth
+    B = leg.B
+    flip = torch.zeros((n_rounds, B), dtype=torch.int32)
+    for r in range(n_rounds):
+        k = synth.random_depth_k(B, r, tag)
+        if k < B:
+            flip[r, k] = 1
+    last = torch.tensor([synth.anchor_token(leg.sh, tag=90_000 + r) for r in range(n_rounds)])
+    return flip_verify(leg, flip, last)
+
+
+def public(d: dict) -> dict:
+    return {k: v for k, v in d.items() if not k.startswith("_")}
+
+
+def run_c1(args, sh, dw) -> dict:
+    leg = Leg(sh, dw, 4, 1024)
+    n = args.warmup + args.steps + min(args.steps, BREAKDOWN_ROUNDS)
+    res = leg.run(args.warmup, args.steps, lm_head_verify(leg, n), resid_tag=1, anchor_tag=0, lm_timing=True)
+    by = res["_bytes"]
+    rs = res["rounds_per_s"]
+    res["round_hbm_frac"] = round(by["round_lm_verify"] * rs / (HBM_PEAK_GBS * 1e9), 4)
+    res["drafted_tok_s_hbm_frac"] = res["round_hbm_frac"]
+    return res
+
+
+def run_synthetic_p(args, sh, dw, B, context, steps, p, tag) -> dict:
+    leg = Leg(sh, dw, B, context)
+    n = args.warmup + steps + min(steps, BREAKDOWN_ROUNDS)
+    res = leg.run(args.warmup, steps, accept_p_verify(leg, n, p, tag), resid_tag=1000 * (tag + 1), anchor_tag=tag)
+    res["accept_p"] = round(p, 4)
+    res["round_hbm_frac"] = round(res["_bytes"]["block_forward"] * res["rounds_per_s"] / (HBM_PEAK_GBS * 1e9), 4)
+    return res
+
+
+def run_c3(args, sh, dw) -> dict:
+    """16384-row prefill slab (rows the window cannot see dropped before the encoder; the
+    prefill is timed on its own), then random-depth rounds with the ring phase set so that
+    the first round's append straddles the ring's last slot."""
+    from block_drafting_dflash_amd import synth
+
+    wl = synth.WORKLOADS["muse-bf16-ctx16384-wrap"]
+    out = {"workload": wl.name, "context": wl.context, "widths": []}
+    for B in wl.blocks:
+        S = max(min(max(8 * B, 32), 128), B)
+        Cs = (max(sh.window + S, sh.window + B + 1, 64) + 7) // 8 * 8
+        phase = (Cs - 8 - wl.context) % Cs
+        leg = Leg(sh, dw, B, wl.context, phase=phase)
+        n = args.warmup + args.c3_steps + min(args.c3_steps, BREAKDOWN_ROUNDS)
+        res = leg.run(args.warmup, args.c3_steps, random_depth_verify(leg, n, tag=B), resid_tag=5000 * B,
+                      anchor_tag=B)
+        slab_bytes = wl.context * sh.fc_in * 2
+        kept = min(wl.context, sh.window)
+        pre_alg = kept * sh.fc_in * 2 + sh.hidden * sh.fc_in * 2 + sh.layers * 2 * sh.kv_heads * sh.head_dim * (
+            sh.hidden * 2 + kept * 2)
+        res["prefill"] = {"ms": round(leg.prefill_ms, 3), "slab_bytes": slab_bytes, "rows_projected": kept,
+                          "alg_bytes": pre_alg,
+                          "gbs": round(pre_alg / (leg.prefill_ms * 1e-3) / 1e9, 1)}
+        res["round_hbm_frac"] = round(res["_bytes"]["block_forward"] * res["rounds_per_s"] / (HBM_PEAK_GBS * 1e9), 4)
+        out["widths"].append(public(res))
+        del leg
+    return out
+
+
+def run_c0(args) -> dict:
+    """The tiny f32 round: weights and ring fit the caches, so it is launch-latency bound."""
     import torch
 
     from block_drafting_dflash_amd import binding, synth
 
-    if not os.path.exists(binding.LIB_PATH):
-        from block_drafting_dflash_amd import build as _b
-        _b.build()
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
-    wl = synth.WORKLOADS["muse-bf16-b4-ctx1024"]
-    sh = wl.shape
-    t0 = time.time()
-    weights = synth.make_weights(sh)
-    dw = binding.to_device(sh, weights)
+    wl = synth.WORKLOADS["tiny-f32-b4-ctx64"]
+    dw = binding.to_device(wl.shape, synth.make_weights(wl.shape))
+    leg = Leg(wl.shape, dw, 4, wl.context)
+    n = args.warmup + args.c0_steps + min(args.c0_steps, BREAKDOWN_ROUNDS)
+    res = leg.run(args.warmup, args.c0_steps, lm_head_verify(leg, n), resid_tag=1, anchor_tag=0)
     torch.cuda.synchronize()
-    print(f"[bench] weights generated and resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream()
-
-    # ---------------- block 4, verify rows through the shared lm_head ------------------
-    B = 4
-    g = binding.Drafter(sh, dw, max_block=B)
-    g.cache_append(torch.from_numpy(synth.resid_rows(sh, wl.context, 0)).to(torch.bfloat16).to(dev), commit=True)
-    # timed rounds carry no timing events (each event record costs the stream a few
-    # microseconds); a shorter pass after them, with events, gives the breakdown
-    nb = min(args.steps, BREAKDOWN_ROUNDS)
-    n = args.warmup + args.steps + nb
-    vrows = torch.from_numpy(np.stack([synth.verify_hidden(sh, B + 1, r) for r in range(n)])).to(torch.bfloat16).to(dev)
-    resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, r + 1) for r in range(n)])).to(torch.bfloat16).to(dev)
-    toks = torch.empty(B, dtype=torch.int32, device=dev)
-    a = torch.empty(B + 1, dtype=torch.int32, device=dev)
-    host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
-    hv = host.numpy()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nb)]
-    # events around the argmax kernel alone (the library records them on the call's stream)
-    evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)]
-    for pair in evk:
-        for x in pair:
-            x.record(stream)  # creates the underlying events before the timed region
-    anchor = synth.anchor_token(sh)
-    ks = []
-    torch.cuda.synchronize()
-    t_start = elapsed = None
-    b0 = args.warmup + args.steps  # first breakdown round
-    for r in range(n):
-        if r == args.warmup:
-            torch.cuda.synchronize()
-            t_start = time.perf_counter()
-        if r == b0:
-            torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t_start
-        e = ev[r - b0] if r >= b0 else None
-        if e: e[0].record(stream)
-        g.draft_block(anchor, B, tokens=toks, stream=stream)
-        if e: e[1].record(stream)
-        if e: g.time_next_argmax(*evk[r - b0])
-        g.lm_head_argmax(vrows[r], out=a, stream=stream)
-        if e: e[2].record(stream)
-        hv[:] = -1
-        g.verify_greedy(toks, a, B, out=host, stream=stream)
-        if e: e[3].record(stream)
-        g.cache_append(resid[r], stream=stream)
-        if e: e[4].record(stream)
-        k, bonus, status = await_verify(hv)  # the round's one host round trip
-        assert status == 0
-        g.cache_trim(B - k)
-        anchor = bonus
-        ks.append(k)
-    torch.cuda.synchronize()
-    ms_draft = [x[0].elapsed_time(x[1]) for x in ev]
-    ms_lm_call = [x[1].elapsed_time(x[2]) for x in ev]
-    ms_lm = [x[0].elapsed_time(x[1]) for x in evk]
-    ms_append = [x[3].elapsed_time(x[4]) for x in ev]
-    e_end = g.cache_state()[0]
-    by = alg_bytes(sh, B, e_end)
-    rounds_s = args.steps / elapsed
-    lm_ms = float(np.mean(ms_lm))
-    fwd_ms = float(np.mean(ms_draft) + np.mean(ms_append))
-    res = {
-        "rounds_per_s": rounds_s, "ms_per_step": 1e3 * elapsed / args.steps, "drafted_tok_s": rounds_s * B,
-        "round_hbm_frac": by["round_lm_verify"] * rounds_s / (HBM_PEAK_GBS * 1e9),
-        "drafted_tok_s_hbm_frac": by["round_lm_verify"] * rounds_s / (HBM_PEAK_GBS * 1e9),
-        "block_forward_ms": fwd_ms, "block_forward_per_s": 1e3 / fwd_ms,
-        "block_forward_hbm_frac": by["block_forward"] / (fwd_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
-        "draft_ms": float(np.mean(ms_draft)), "append_ms": float(np.mean(ms_append)),
-        "lm_head_ms": lm_ms, "lm_head_gbs": by["lm_head"] / (lm_ms * 1e-3) / 1e9,
-        "lm_head_call_ms": float(np.mean(ms_lm_call)),
-        "mean_accepted": float(np.mean(ks[args.warmup:b0])), "bytes": by, "breakdown_rounds": nb,
-    }
-
-    # ---------------- block 16, p = 0.6 synthetic target --------------------------------
-    b16 = None
-    if args.block16_steps > 0:
-        del g
-        wl2 = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
-        b16 = synthetic_rounds(sh, dw, 16, wl2.context, args.warmup, args.block16_steps, wl2.accept_p, tag=0)
-        b16 = {"workload": wl2.name, **b16}
-    return sh, weights, dw, res, b16
-
-
-def synthetic_rounds(sh, dw, B: int, context: int, warmup: int, steps: int, p: float, tag: int) -> dict:
-    """Rounds of block B whose verify-row argmaxes come from the p-accept stand-in target
-    (computed on the device from pre-drawn uniforms): draft, verify (result written into
-    pinned host memory), append, the host's wait for (k, bonus), trim. The block forward is
-    the event-timed draft plus append."""
-    import torch
-
-    from block_drafting_dflash_amd import binding, synth
-
-    dev = torch.device("cuda", 0)
-    stream = torch.cuda.current_stream()
-    g = binding.Drafter(sh, dw, max_block=B)
-    g.cache_append(torch.from_numpy(synth.resid_rows(sh, context, 0)).to(torch.bfloat16).to(dev), commit=True)
-    nb = min(steps, BREAKDOWN_ROUNDS)  # event-timed rounds after the timed ones
-    n = warmup + steps + nb
-    resid = torch.from_numpy(np.stack([synth.resid_rows(sh, B + 1, 1000 * (tag + 1) + r) for r in range(n)]))
-    resid = resid.to(torch.bfloat16).to(dev)
-    u = torch.from_numpy(np.stack([synth.accept_draws(B, r, tag) for r in range(n)])).to(dev)  # f64 [n, 3, B+1]
-    V = sh.vocab
-    # the stand-in target's draws that do not depend on the draft, made before timing: per
-    # row a 0/1 word that rejects the row (its token then differs from the draft token in the
-    # lowest bit, a valid id since the vocabulary size is even), and the bonus row's token
-    assert V % 2 == 0, "the stand-in target flips the lowest bit of a token id"
-    flip = (u[:, 0, :B] >= p).int()
-    tgt_all = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
-    tgt_all[:, B] = (torch.floor(u[:, 2, B] * V) % V).int()
-    toks = torch.empty(B, dtype=torch.int32, device=dev)
-    host = torch.empty(3, dtype=torch.int32, pin_memory=True)  # the verify kernel writes (k, bonus, status) here
-    hv = host.numpy()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
-    anchor = synth.anchor_token(sh, tag=tag)
-    ks = []
-    torch.cuda.synchronize()
-    t0 = el = None
-    b0 = warmup + steps
-    for r in range(n):
-        if r == warmup:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-        if r == b0:
-            torch.cuda.synchronize()
-            el = time.perf_counter() - t0
-        e = ev[r - b0] if r >= b0 else None
-        if e: e[0].record(stream)
-        g.draft_block(anchor, B, tokens=toks, stream=stream)
-        if e: e[1].record(stream)
-        # stand-in for the target's verify-row argmaxes (the target model is out of scope):
-        # row i keeps the draft token with probability p, else another token (one kernel)
-        tgt = tgt_all[r]
-        torch.bitwise_xor(toks, flip[r], out=tgt[:B])
-        hv[:] = -1
-        g.verify_greedy(toks, tgt, B, out=host, stream=stream)
-        if e: e[2].record(stream)
-        g.cache_append(resid[r], stream=stream)
-        if e: e[3].record(stream)
-        k, bonus, status = await_verify(hv)  # the round's one host round trip
-        assert status == 0
-        g.cache_trim(B - k)
-        anchor = bonus
-        ks.append(k)
-    torch.cuda.synchronize()
-    by = alg_bytes(sh, B, g.cache_state()[0])
-    rs = steps / el
-    fwd = float(np.mean([x[0].elapsed_time(x[1]) + x[2].elapsed_time(x[3]) for x in ev]))
-    return {"block": B, "accept_p": round(p, 4), "rounds_per_s": round(rs, 2), "drafted_tok_s": round(rs * B, 1),
-            "round_hbm_frac": round(by["block_forward"] * rs / (HBM_PEAK_GBS * 1e9), 4),
-            "block_forward_ms": round(fwd, 4),
-            "block_forward_hbm_frac": round(by["block_forward"] / (fwd * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-            "mean_accepted": round(float(np.mean(ks[warmup:b0])), 4), "steps": steps}
+    return {"workload": wl.name, **public(res)}
 
 
 def run_q4(args) -> dict:
@@ -268,9 +342,31 @@ def run_q4(args) -> dict:
     torch.cuda.synchronize()
     print(f"[bench] q4 weights generated and resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     ps = synth.width_accept_p(wl.blocks)
-    widths = [synthetic_rounds(sh, dw, B, wl.context, args.warmup, args.q4_steps, ps[B], tag=B) for B in wl.blocks]
+    widths = [public(run_synthetic_p(args, sh, dw, B, wl.context, args.q4_steps, ps[B], tag=B)) for B in wl.blocks]
     return {"workload": wl.name, "widths": widths}
 
+
+def stream_probe(mib: int, reps: int = 10) -> dict:
+    """The in-repo HBM streaming-read probe: mib MiB read `reps` times, event-timed."""
+    import torch
+
+    from block_drafting_dflash_amd import binding
+
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    best = None
+    for groups in (1024, 2048, 4096):
+        sink = torch.empty(groups, dtype=torch.int32, device="cuda")
+        binding.hbm_read_probe(src, sink, groups)  # warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            binding.hbm_read_probe(src, sink, groups)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "groups": groups}
+    return {"mib": mib, "reps": reps, **best, "frac_of_peak": round(best["gbs"] / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(sh, weights, budget_s: float) -> dict:
@@ -317,7 +413,10 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--block16-steps", type=int, default=320)
+    ap.add_argument("--c3-steps", type=int, default=128, help="timed rounds per width at 16384 context (0 = skip)")
     ap.add_argument("--q4-steps", type=int, default=200, help="timed rounds per width of the q4 sweep (0 = skip)")
+    ap.add_argument("--c0-steps", type=int, default=500, help="timed rounds of the tiny f32 round (0 = skip)")
+    ap.add_argument("--probe-mib", type=int, default=1024, help="HBM streaming-read probe size (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -337,33 +436,75 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the round at batch 1 is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
-    sh, weights, dw, res, b16 = run_gpu(args)
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    if not os.path.exists(binding.LIB_PATH):
+        from block_drafting_dflash_amd import build as _b
+        _b.build()
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS["muse-bf16-b4-ctx1024"]
+    sh = wl.shape
+    t0 = time.time()
+    weights = synth.make_weights(sh)
+    dw = binding.to_device(sh, weights)
+    torch.cuda.synchronize()
+    print(f"[bench] weights generated and resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    res = run_c1(args, sh, dw)
+    print(f"[bench] block 4: {res['rounds_per_s']} rounds/s", file=sys.stderr, flush=True)
+    b16 = None
+    if args.block16_steps > 0:
+        wl2 = synth.WORKLOADS["muse-bf16-b16-ctx4096"]
+        b16 = {"workload": wl2.name, **public(run_synthetic_p(args, sh, dw, 16, wl2.context, args.block16_steps,
+                                                               wl2.accept_p, tag=0))}
+        print(f"[bench] block 16: {b16['rounds_per_s']} rounds/s", file=sys.stderr, flush=True)
+    c3 = run_c3(args, sh, dw) if args.c3_steps > 0 else None
+    if c3:
+        print("[bench] 16384 context done", file=sys.stderr, flush=True)
     del dw
+    torch.cuda.empty_cache()
     q4 = run_q4(args) if args.q4_steps > 0 else None
+    c0 = run_c0(args) if args.c0_steps > 0 else None
+    probe = stream_probe(args.probe_mib) if args.probe_mib > 0 else None
     cpu = None if args.no_cpu_baseline else cpu_baseline(sh, weights, args.cpu_budget)
     traffic = counted_traffic()
+    by = res["_bytes"]
+    lm_ms = res["_lm_ms"]
+    fwd_ms = res["block_forward_ms"]
     line = {
         "metric": "DFlash rounds/s at block 4 (B=1), with drafted tok/s and % of HBM roofline",
-        "value": round(res["rounds_per_s"], 2), "unit": "rounds/s",
+        "value": res["rounds_per_s"], "unit": "rounds/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": res["round_ms"]["mean"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) weights, N(0,1) residual/verify rows)",
         "config": {"workload": "muse-bf16-b4-ctx1024", "block": 4, "context": 1024, "window": 2048,
                    "hidden": 2048, "layers": 5, "vocab": 202048},
-        "drafted_tok_s": round(res["drafted_tok_s"], 1),
-        "round_hbm_frac": round(res["round_hbm_frac"], 4),
-        "block_forward": {"ms": round(res["block_forward_ms"], 4), "per_s": round(res["block_forward_per_s"], 1),
-                          "hbm_frac": round(res["block_forward_hbm_frac"], 4),
-                          "draft_ms": round(res["draft_ms"], 4), "append_ms": round(res["append_ms"], 4)},
+        "drafted_tok_s": res["drafted_tok_s"],
+        "round_hbm_frac": res["round_hbm_frac"],
+        "round_ms": res["round_ms"], "rounds_per_s_median": res["rounds_per_s_median"],
+        "counters": {k: res[k] for k in ("draft_rounds", "draft_n", "draft_n_accepted", "mean_accepted",
+                                         "mean_accepted_with_bonus", "accept_hist", "committed_tok_s",
+                                         "committed_token_sha256", "committed_tokens")},
+        "block_forward": {"ms": fwd_ms, "per_s": round(1e3 / fwd_ms, 1), "hbm_frac": res["block_forward_hbm_frac"],
+                          "draft_ms": res["draft_ms"], "append_ms": res["append_ms"]},
         "roofline": {"bound": "hbm", "kernel": "lm_head argmax GEMM (202048x2048 bf16, 5 verify rows)",
-                     "achieved": round(res["lm_head_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["lm_head_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": (round(traffic / (res["lm_head_ms"] * 1e-3) / 1e9, 1) if traffic else None),
-                     "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": res["bytes"]["lm_head"],
-                     "avg_launch_ms": round(res["lm_head_ms"], 5),
-                     "avg_call_ms": round(res["lm_head_call_ms"], 5)},
+                     "achieved": round(by["lm_head"] / (lm_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(by["lm_head"] / (lm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic / (lm_ms * 1e-3) / 1e9, 1) if traffic else None),
+                     "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": by["lm_head"],
+                     "avg_launch_ms": round(lm_ms, 5), "avg_call_ms": round(res["_lm_call_ms"], 5)},
+        "roofline_block_forward": {"bound": "hbm", "span": "drafter + lm_head block forward (append fc + draft)",
+                                   "achieved": round(by["block_forward"] / (fwd_ms * 1e-3) / 1e9, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": res["block_forward_hbm_frac"],
+                                   "algorithmic_bytes": by["block_forward"], "avg_ms": fwd_ms},
+        "hbm_stream_probe": probe,
         "block16": b16,
+        "ctx16384": c3,
         "q4": q4,
+        "tiny_f32": c0,
         "cpu_baseline": cpu,
         "mean_accepted": res["mean_accepted"],
     }

@@ -20,7 +20,7 @@ _DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
 
 EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
            "dflash_draft_block", "dflash_lm_head_argmax", "dflash_lm_head_argmax_noalloc", "dflash_time_next_argmax",
-           "dflash_verify_greedy",
+           "dflash_verify_greedy", "dflash_hbm_read_probe",
            "dflash_cache_state",
            "dflash_cache_read", "dflash_last_error", "dflash_status_string")
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         "dflash_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
         "dflash_lm_head_argmax_noalloc": (i32, [vp, vp, i32, vp, vp]),
         "dflash_time_next_argmax": (i32, [vp, vp, vp]),
+        "dflash_hbm_read_probe": (i32, [vp, sz, vp, i32, vp]),
         "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
         "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
         "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
@@ -290,3 +291,13 @@ class Drafter:
     def _dev(self, t: torch.Tensor, dtype: torch.dtype) -> None:
         if t.device != self.device or t.dtype != dtype or not t.is_contiguous():
             raise ValueError(f"expected a contiguous {dtype} tensor on {self.device}, got {t.dtype} on {t.device}")
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, groups: int, stream=None) -> None:
+    """dflash_hbm_read_probe over the bytes of src (sink: int32 [groups] on the same device)."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32 and
+            sink.numel() >= groups):
+        raise ValueError("src and sink must be contiguous device tensors, sink int32 [groups]")
+    _check(lib().dflash_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(groups),
+                                       _stream(stream)), None)
+

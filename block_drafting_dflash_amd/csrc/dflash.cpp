@@ -847,6 +847,14 @@ dflash_status dflash_lm_head_argmax(dflash_ctx* ctx, const void* rows, int32_t n
   return s;
 }
 
+dflash_status dflash_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t groups, void* stream) {
+  if (!src || !sink || groups < 1 || ((uintptr_t)src & 15u) || bytes % 16 || bytes / 16 < (size_t)groups * 256)
+    return cfg_fail(g_create_err, DFLASH_E_ARG, "probe needs a 16-byte aligned source of at least groups * 4096 bytes");
+  const hipError_t e = launch_hbm_read_probe(src, bytes, sink, groups, (hipStream_t)stream);
+  if (e != hipSuccess) return cfg_fail(g_create_err, DFLASH_E_DEVICE, "probe launch: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
 dflash_status dflash_time_next_argmax(dflash_ctx* ctx, void* start, void* end) {
   if (!ctx) return DFLASH_E_ARG;
   if ((start == nullptr) != (end == nullptr)) return fail(ctx, DFLASH_E_ARG, "give both timing events or neither");

@@ -205,6 +205,9 @@ bool attention_forms_committed_rows(int act_bf16, const AttnShape& a);
 size_t attention_partial_floats(const AttnShape& a, int R);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);
+// Streaming read of `bytes` (a multiple of 16, at least groups * 4096) by `groups` work-groups
+// of contiguous shares; sink [groups] receives an XOR of what each read (misc.hip).
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int groups, hipStream_t s);
 hipError_t launch_cache_read(int act_bf16, const AttnShape& a, const void* ring_layer, int64_t lo, int n,
                              void* kout, void* vout, hipStream_t s);
 

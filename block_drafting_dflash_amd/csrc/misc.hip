@@ -321,3 +321,43 @@ hipError_t launch_pack_q4(const void* codes, const void* scales, const void* bia
 }
 
 }  // namespace dflash
+
+namespace dflash {
+
+// Streaming read of `bytes` from src: work-group g reads its contiguous share with 16-byte
+// non-temporal loads, eight in flight per thread, and stores the XOR of everything it read
+// to sink[g] (so the loads cannot be dropped). The practical HBM read ceiling the weight
+// streams of the round are compared with.
+constexpr int PROBE_THREADS = 256, PROBE_UNROLL = 8;
+__global__ __launch_bounds__(PROBE_THREADS) void hbm_read_probe_kernel(const u32x4_t* __restrict__ src, size_t n16,
+                                                                      uint32_t* __restrict__ sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per, hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  for (size_t i = lo + threadIdx.x; i < hi; i += (size_t)PROBE_THREADS * PROBE_UNROLL) {
+    u32x4_t v[PROBE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) {
+      const size_t j = i + (size_t)u * PROBE_THREADS;
+      v[u] = __builtin_nontemporal_load(src + (j < hi ? j : hi - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < PROBE_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+  __shared__ uint32_t part[PROBE_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int groups, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 < (size_t)groups * PROBE_THREADS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(hbm_read_probe_kernel, dim3(groups), dim3(PROBE_THREADS), 0, s, (const u32x4_t*)src, n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace dflash
+

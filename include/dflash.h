@@ -218,6 +218,14 @@ dflash_status dflash_lm_head_argmax_noalloc(dflash_ctx *ctx, const void *rows, i
  * request. Errors: NULL ctx, or exactly one NULL event (DFLASH_E_ARG). */
 dflash_status dflash_time_next_argmax(dflash_ctx *ctx, void *start, void *end);
 
+/* HBM streaming-read probe (measurement; no counterpart on the pages): `groups` work-groups
+ * each read a contiguous share of `bytes` from src (device, 16-byte aligned, bytes a multiple
+ * of 16 and at least groups * 4096) with 16-byte non-temporal loads and write the XOR of what
+ * they read to sink (device uint32 [groups]). Timed by the caller, it gives the practical read
+ * bandwidth the weight streams are compared with. Context-free; errors go to
+ * dflash_last_error(NULL): DFLASH_E_ARG for the conditions above, DFLASH_E_DEVICE. */
+dflash_status dflash_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, int32_t groups, void *stream);
+
 /*
  * Greedy exact-match verify of one block (lablup/mlxcel #1751, Implementation Review
  * Summary: greedy exact-match verify rule, verify width = block + 1). d_draft: device
