@@ -20,7 +20,8 @@ lm_head. Also reported, each with the round counters the pages print (draft_roun
 draft_n_accepted, mean accepted with and without the bonus, committed tok/s, accept
 histogram, SHA-256 of the committed token stream): the block-16 round (muse-bf16-b16-ctx4096,
 p = 0.6 stand-in target), the 16384-row context with ring wraps at blocks 8 and 32 (prefill
-timed on its own), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16), the tiny
+timed on its own), the adaptive verify width (the library's controller between blocks 4 and 16
+against both fixed widths), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16), the tiny
 f32 round (tiny-f32-b4-ctx64), an HBM streaming-read probe, and the CPU oracle on the host
 cores.
 
@@ -346,6 +347,75 @@ def run_q4(args) -> dict:
     return {"workload": wl.name, "widths": widths}
 
 
+def run_adaptive(args, sh, dw) -> dict:
+    """Rounds whose block the library's width controller picks between the declared depth 4 and
+    the ceiling 16 (windows of 32 rounds, a challenge after every 3; shorter windows are too
+    noisy under geometric accept lengths), fed with the rounds' real periods (spacing of the
+    verify results' arrivals) and committed tokens, beside the same rounds at fixed widths 4
+    and 16; p-accept stand-in target at p = 0.6 and 0.9, 2048-row context. The ring is sized
+    for the ceiling."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    D, C, WIN, EVERY = 4, 16, 32, 3
+    n = args.warmup + args.adaptive_steps
+    out = {"depth": D, "ceiling": C, "window": WIN, "challenge_every": EVERY, "context": 2048, "runs": []}
+    prefill = torch.from_numpy(synth.resid_rows(sh, 2048, 0)).to(torch.bfloat16).to(dev)
+    resid = torch.from_numpy(np.stack([synth.resid_rows(sh, C + 1, 7000 + r) for r in range(n)]))
+    resid = resid.to(torch.bfloat16).to(dev)
+    u = torch.from_numpy(np.stack([synth.accept_draws(C, r, 33) for r in range(n)]))
+    for p in (0.6, 0.9):
+        for mode in ("fixed-4", "fixed-16", "adaptive"):
+            g = binding.Drafter(sh, dw, max_block=C)
+            g.cache_append(prefill, commit=True)
+            flip = (u[:, 0, :C] >= p).int().to(dev)
+            tgt = (torch.floor(u[:, 2, C] * sh.vocab) % sh.vocab).int()[:, None].repeat(1, C + 1).contiguous().to(dev)
+            toks = torch.empty((n, C), dtype=torch.int32, device=dev)
+            host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+            hv = host.numpy()
+            ctl = binding.WidthController(D, C, WIN, EVERY) if mode == "adaptive" else None
+            fixed = {"fixed-4": D, "fixed-16": C}.get(mode)
+            anchor = synth.anchor_token(sh, tag=33)
+            torch.cuda.synchronize()
+            last = time.perf_counter()
+            tokens, widths, t0 = 0, [], None
+            for r in range(n):
+                if r == args.warmup:
+                    t0 = time.perf_counter()
+                b = ctl.width() if ctl else fixed
+                g.draft_block(anchor, b, tokens=toks[r, :b], stream=stream)
+                torch.bitwise_xor(toks[r, :b], flip[r, :b], out=tgt[r, :b])
+                hv[:] = -1
+                g.verify_greedy(toks[r, :b], tgt[r, :b + 1], b, out=host, stream=stream)
+                g.cache_append(resid[r, :b + 1], stream=stream)
+                k, bonus, status = await_verify(hv)
+                now = time.perf_counter()
+                assert status == 0
+                g.cache_trim(b - k)
+                if ctl:
+                    ctl.record(b, k + 1, (now - last) * 1e3)
+                last = now
+                anchor = bonus
+                if r >= args.warmup:
+                    tokens += k + 1
+                    widths.append(b)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            run = {"p": p, "mode": mode, "rounds": len(widths), "committed_tok_s": round(tokens / el, 1),
+                   "rounds_per_s": round(len(widths) / el, 1),
+                   "rounds_at_ceiling": int(sum(1 for w in widths if w == C))}
+            if ctl:
+                st = ctl.state()
+                run.update({"final_width": st["incumbent"], "challenges": st["challenges"],
+                            "adoptions": st["adoptions"], "tok_per_ms_incumbent": round(st["incumbent_rate"], 3)})
+            out["runs"].append(run)
+            del g
+    return out
+
+
 def stream_probe(mib: int, reps: int = 10) -> dict:
     """The in-repo HBM streaming-read probe: mib MiB read `reps` times, event-timed."""
     import torch
@@ -416,6 +486,8 @@ def main():
     ap.add_argument("--c3-steps", type=int, default=128, help="timed rounds per width at 16384 context (0 = skip)")
     ap.add_argument("--q4-steps", type=int, default=200, help="timed rounds per width of the q4 sweep (0 = skip)")
     ap.add_argument("--c0-steps", type=int, default=500, help="timed rounds of the tiny f32 round (0 = skip)")
+    ap.add_argument("--adaptive-steps", type=int, default=768,
+                    help="rounds per run of the adaptive-width comparison (0 = skip)")
     ap.add_argument("--probe-mib", type=int, default=1024, help="HBM streaming-read probe size (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -463,6 +535,7 @@ def main():
     c3 = run_c3(args, sh, dw) if args.c3_steps > 0 else None
     if c3:
         print("[bench] 16384 context done", file=sys.stderr, flush=True)
+    adaptive = run_adaptive(args, sh, dw) if args.adaptive_steps > 0 else None
     del dw
     torch.cuda.empty_cache()
     q4 = run_q4(args) if args.q4_steps > 0 else None
@@ -503,6 +576,7 @@ def main():
         "hbm_stream_probe": probe,
         "block16": b16,
         "ctx16384": c3,
+        "adaptive_width": adaptive,
         "q4": q4,
         "tiny_f32": c0,
         "cpu_baseline": cpu,

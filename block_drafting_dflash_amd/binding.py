@@ -20,7 +20,8 @@ _DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
 
 EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
            "dflash_draft_block", "dflash_lm_head_argmax", "dflash_lm_head_argmax_noalloc", "dflash_time_next_argmax",
-           "dflash_verify_greedy", "dflash_hbm_read_probe",
+           "dflash_verify_greedy", "dflash_hbm_read_probe", "dflash_width_ctl_create", "dflash_width_ctl_width",
+           "dflash_width_ctl_record", "dflash_width_ctl_state", "dflash_width_ctl_destroy",
            "dflash_cache_state",
            "dflash_cache_read", "dflash_last_error", "dflash_status_string")
 
@@ -72,6 +73,12 @@ def lib() -> ctypes.CDLL:
         "dflash_lm_head_argmax_noalloc": (i32, [vp, vp, i32, vp, vp]),
         "dflash_time_next_argmax": (i32, [vp, vp, vp]),
         "dflash_hbm_read_probe": (i32, [vp, sz, vp, i32, vp]),
+        "dflash_width_ctl_create": (i32, [i32, i32, i32, i32, P(vp)]),
+        "dflash_width_ctl_width": (i32, [vp]),
+        "dflash_width_ctl_record": (i32, [vp, i32, i32, ctypes.c_double]),
+        "dflash_width_ctl_state": (i32, [vp, P(i32), P(i32), P(i32), P(ctypes.c_double), P(ctypes.c_double),
+                                         P(i64), P(i64)]),
+        "dflash_width_ctl_destroy": (None, [vp]),
         "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
         "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
         "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
@@ -300,4 +307,35 @@ def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, groups: int, stream=No
         raise ValueError("src and sink must be contiguous device tensors, sink int32 [groups]")
     _check(lib().dflash_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), int(groups),
                                        _stream(stream)), None)
+
+
+class WidthController:
+    """dflash_width_ctl: the adaptive verify width of the round loop (host code in the library)."""
+
+    def __init__(self, depth: int, ceiling: int, window: int, challenge_every: int):
+        h = ctypes.c_void_p()
+        _check(lib().dflash_width_ctl_create(depth, ceiling, window, challenge_every, ctypes.byref(h)), None)
+        self.h = h
+
+    def __del__(self):
+        h = getattr(self, "h", None)
+        if h and _lib is not None:
+            _lib.dflash_width_ctl_destroy(h)
+            self.h = None
+
+    def width(self) -> int:
+        return lib().dflash_width_ctl_width(self.h)
+
+    def record(self, block: int, committed: int, ms: float) -> None:
+        st = lib().dflash_width_ctl_record(self.h, int(block), int(committed), float(ms))
+        if st != 0:
+            raise DFlashError(st, lib().dflash_status_string(st).decode())
+
+    def state(self) -> dict:
+        i, c, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        ir, cr = ctypes.c_double(), ctypes.c_double()
+        n, a = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().dflash_width_ctl_state(self.h, *(ctypes.byref(x) for x in (i, c, ch, ir, cr, n, a))), None)
+        return {"incumbent": i.value, "challenger": c.value, "challenging": bool(ch.value),
+                "incumbent_rate": ir.value, "challenge_rate": cr.value, "challenges": n.value, "adoptions": a.value}
 

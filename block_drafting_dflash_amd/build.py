@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 SOURCES = ["gemm_bf16.hip", "gemm_q4.hip", "gemm_f32.hip", "gemm.hip", "attention.hip", "misc.hip", "noalloc.hip",
-           "dflash.cpp"]
+           "dflash.cpp", "controller.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -238,6 +238,37 @@ dflash_status dflash_hbm_read_probe(const void *src, size_t bytes, uint32_t *sin
 dflash_status dflash_verify_greedy(dflash_ctx *ctx, const int32_t *d_draft, const int32_t *d_target,
                                    int32_t block, int32_t *d_out, void *stream);
 
+/*
+ * Adaptive verify width (host only). A drafter whose declared depth lies below the requested
+ * width runs the round loop under a throughput controller between the two: it warms up at the
+ * depth and widens to the ceiling only when a measured window pays for it; the widths a run
+ * can settle on are the depth and the ceiling (lablup/mlxcel #1762, What changed, "Round
+ * loop"; Pre-merge review round, first finding). The measure is committed tokens per
+ * millisecond over a window of rounds (same page, Real-checkpoint validation, item 5).
+ * Schedule: windows of `window` rounds at the incumbent width (first the depth); after every
+ * `challenge_every` of them one window at the other width, adopted (the two swap roles) only
+ * if its rate is strictly above the incumbent's rate over its whole measurement period since
+ * the last challenge; a new period then starts from the adopted window, or empty. A drafter context
+ * serving these widths needs max_block >= ceiling (its slack is sized for the ceiling).
+ *   create: 1 <= depth <= ceiling, window >= 1, challenge_every >= 1 (DFLASH_E_RANGE).
+ *   width: the block of the next round (0 for a NULL controller).
+ *   record: one finished round at `block` (must equal width(), else DFLASH_E_STATE) that
+ *     committed `committed` >= 1 tokens (accepted + bonus) in `ms` > 0 milliseconds
+ *     (DFLASH_E_RANGE otherwise); on error the controller is unchanged.
+ *   state: the incumbent and challenger widths, whether the next round is a challenge, the
+ *     incumbent's period rate and the latest challenge rate (-1 before the first), and
+ *     how many challenges ran and were adopted. Any output may be NULL.
+ */
+typedef struct dflash_width_ctl dflash_width_ctl;
+dflash_status dflash_width_ctl_create(int32_t depth, int32_t ceiling, int32_t window, int32_t challenge_every,
+                                      dflash_width_ctl **out);
+int32_t dflash_width_ctl_width(const dflash_width_ctl *ctl);
+dflash_status dflash_width_ctl_record(dflash_width_ctl *ctl, int32_t block, int32_t committed, double ms);
+dflash_status dflash_width_ctl_state(const dflash_width_ctl *ctl, int32_t *incumbent, int32_t *challenger,
+                                     int32_t *challenging, double *incumbent_rate, double *challenge_rate,
+                                     int64_t *challenges, int64_t *adoptions);
+void dflash_width_ctl_destroy(dflash_width_ctl *ctl);
+
 /* Committed end e, pending rows, slack S and capacity C. Host only. */
 dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pending, int32_t *slack,
                                  int32_t *capacity);

@@ -400,3 +400,39 @@ def test_micro_bf16_block129_deepest_rewind(micro_bf16_w):
         ls.trim(B - k)
         anchor = bonus
     print("block 129 stats", ls.stats)
+
+
+@pytest.mark.parametrize("p,widens", [(0.95, True), (0.3, False)])
+def test_adaptive_width_rounds_match_oracle(micro_bf16_w, p, widens):
+    """Rounds whose block the library's width controller picks (depth 4, ceiling 16, windows of
+    4 rounds, a challenge after every 2): drafts at both widths in lock-step with the oracle
+    drafter (the ring sized for the ceiling), and the controller's decisions replayed through
+    the oracle controller. Round times are a fixed model (0.1 + 0.02 * block ms), so a high
+    accept probability makes the ceiling pay and a low one does not."""
+    from oracle.width_controller import WidthController as OracleController
+
+    sh = MICRO_BF16
+    ctl = binding.WidthController(4, 16, 4, 2)
+    orc = OracleController(4, 16, 4, 2)
+    ls = P.LockStep(sh, micro_bf16_w, max_block=16, phase=24, window_period=5)
+    ls.append(synth.resid_rows(sh, 48, 0), commit=True)
+    anchor = synth.anchor_token(sh, tag=77)
+    used = set()
+    for r in range(48):
+        b = ctl.width()
+        assert b == orc.width()
+        used.add(b)
+        d = ls.draft(anchor, b)
+        a = synth.synthetic_target_argmax(d, synth.accept_draws(b, r, 77), p, sh.vocab)
+        k, bonus = ls.verify(d, a)
+        ls.append(synth.resid_rows(sh, b + 1, 9000 + r))
+        ls.trim(b - k)
+        ms = 0.1 + 0.02 * b
+        ctl.record(b, k + 1, ms)
+        orc.record(b, k + 1, ms)
+        anchor = bonus
+    st = ctl.state()
+    assert st["incumbent"] == orc.incumbent and st["adoptions"] == sum(x[3] for x in orc.decisions)
+    assert used == {4, 16}
+    assert (st["incumbent"] == 16) == widens
+    print("adaptive", p, st, ls.stats)
