@@ -35,6 +35,8 @@ SEED_ACCEPT = 4
 SEED_WIDTH_P = 5
 SEED_TRIM = 6
 SEED_PHASE = 7
+SEED_TARGET = 8  # the synthetic target's own layers (its embedding table and lm_head are the drafter's)
+SEED_PROMPT = 9
 
 ROW_BLOCK = 2048  # rows per independent RNG block of a weight tensor
 
@@ -79,6 +81,84 @@ MUSE_BF16 = Shape(hidden=2048, layers=5, q_heads=32, kv_heads=4, head_dim=128, i
                   vocab=202048, target_streams=5, target_width=4096, window=2048,
                   weight_dtype="bf16", act_dtype="bf16")
 MUSE_Q4 = MUSE_BF16.with_(weight_dtype="q4")
+
+
+@dataclasses.dataclass(frozen=True)
+class TargetShape:
+    """Synthetic causal target: Qwen3-shaped layers, each with a sliding window of `window`
+    positions or full attention, and the layers whose residual stream is captured for the
+    drafter (hidden = the drafter's hidden, so both share the embedding table and lm_head)."""
+
+    hidden: int
+    layers: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    intermediate: int
+    vocab: int
+    window: int
+    full_layers: Tuple[int, ...]
+    capture_layers: Tuple[int, ...]
+    weight_dtype: str
+    act_dtype: str
+    rms_eps: float = 1e-6
+    rope_theta: float = 1e6
+    max_context: int = 4096
+
+    def layer_kind(self, l: int) -> str:
+        return "full" if l in self.full_layers else "sliding"
+
+    @property
+    def streams(self) -> int:
+        return len(self.capture_layers)
+
+    def with_(self, **kw) -> "TargetShape":
+        return dataclasses.replace(self, **kw)
+
+
+def drafter_for(target: TargetShape, drafter: Shape) -> Shape:
+    """The drafter paired with a target: fc takes the target's captured streams."""
+    return drafter.with_(target_streams=target.streams, target_width=target.hidden)
+
+
+# Targets of the two drafter sizes: hidden equal to the drafter's, mixed sliding/full layers
+# (every fifth layer full), residual streams captured at every other layer.
+TINY_F32_TARGET = TargetShape(hidden=256, layers=6, q_heads=4, kv_heads=2, head_dim=64, intermediate=512,
+                              vocab=4096, window=32, full_layers=(2, 5), capture_layers=(1, 3, 5),
+                              weight_dtype="f32", act_dtype="f32", max_context=512)
+MUSE_BF16_TARGET = TargetShape(hidden=2048, layers=10, q_heads=32, kv_heads=4, head_dim=128, intermediate=6144,
+                               vocab=202048, window=2048, full_layers=(4, 9), capture_layers=(1, 3, 5, 7, 9),
+                               weight_dtype="bf16", act_dtype="bf16", max_context=4096)
+
+
+def target_weight_names(t: TargetShape) -> List[str]:
+    names = ["final_norm"]
+    for l in range(t.layers):
+        names += [f"layers.{l}.{n}" for n in
+                  ("q", "k", "v", "o", "gate", "up", "down", "in_norm", "post_norm", "q_norm", "k_norm")]
+    return names
+
+
+def make_target_weights(t: TargetShape, drafter_weights: Dict[str, object], seed: int = SEED_TARGET,
+                        threads: Optional[int] = None) -> Dict[str, object]:
+    """The target's weights in storage form: its own layers and final norm drawn from their
+    own stream (N(0, 0.02), gains 1 + 0.02 N(0, 1)), and the drafter's embedding table and
+    lm_head (shared)."""
+    proxy = Shape(hidden=t.hidden, layers=t.layers, q_heads=t.q_heads, kv_heads=t.kv_heads, head_dim=t.head_dim,
+                  intermediate=t.intermediate, vocab=t.vocab, target_streams=1, target_width=t.hidden,
+                  window=t.window, weight_dtype=t.weight_dtype, act_dtype=t.act_dtype)
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    out: Dict[str, object] = {"embed": drafter_weights["embed"], "lm_head": drafter_weights["lm_head"]}
+    with _cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        for name in target_weight_names(t):
+            w = draw_tensor(proxy, name, seed, pool)
+            out[name] = w if t.weight_dtype == "f32" else _bf16_parallel(w, pool)
+    return out
+
+
+def prompt_tokens(vocab: int, n: int, tag: int = 0, seed: int = SEED_PROMPT) -> np.ndarray:
+    """A prompt of uniform token ids."""
+    return _rng(seed, tag).integers(0, vocab, n).astype(np.int64)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -1,11 +1,11 @@
 """Planted mistakes in a copy of the oracle must fail its pins.
 
-Each mutant rewrites one passage of oracle/dflash_oracle.py's source text with a plausible
-mistake (a dropped term, a wrong sign or index, a transposed operand, an off-by-one
-position, a missing floor) and loads the result as a module of its own. The pins of
-tests/test_oracle_pins.py then run against that module in place of the oracle, cheapest
-first; a mutant is caught when one of them fails (an assertion or any error). The real
-oracle file is never modified.
+Each mutant rewrites one passage of oracle/dflash_oracle.py's (or oracle/target_oracle.py's)
+source text with a plausible mistake (a dropped term, a wrong sign or index, a transposed
+operand, an off-by-one position or window edge, a missing floor) and loads the result as a
+module of its own. The pins of tests/test_oracle_pins.py (tests/test_target_oracle.py) then
+run against that module in place of the oracle, cheapest first; a mutant is caught when one
+of them fails (an assertion or any error). The real oracle files are never modified.
 """
 import os
 import sys
@@ -16,6 +16,7 @@ import pytest
 
 from block_drafting_dflash_amd import synth
 from tests import test_oracle_pins as pins
+from tests import test_target_oracle as tpins
 
 ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "dflash_oracle.py")
 
@@ -78,15 +79,40 @@ MUTANTS = [
 ]
 
 
-def load_mutant(old: str, new: str) -> types.ModuleType:
-    src = open(ORACLE_SRC).read()
+TARGET_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "target_oracle.py")
+
+# mistakes in the target oracle (the verify forward of the round's target)
+TARGET_MUTANTS = [
+    ("target attention not causal inside the block", "K = self.K[l][self.first_key(l, qp):qp + 1]",
+     "K = self.K[l][self.first_key(l, qp):self.e + R]"),
+    ("target sliding window one key wider", "else max(0, q - self.sh.window + 1)", "else max(0, q - self.sh.window)"),
+    ("target full layers treated as sliding",
+     'return 0 if self.sh.layer_kind(layer) == "full" else max(0, q - self.sh.window + 1)',
+     "return max(0, q - self.sh.window + 1)"),
+    ("streams captured after the final norm", "caps.append((sh.capture_layers.index(l), x.copy()))",
+     'caps.append((sh.capture_layers.index(l), rms_norm(x, self._lin("final_norm"), sh.rms_eps)))'),
+    ("captured streams in reverse order", "caps.sort(key=lambda c: c[0])", "caps.sort(key=lambda c: -c[0])"),
+    ("target trim ignores the rewind", "self.e = self.e + self.pending - m", "self.e = self.e + self.pending"),
+    ("captured streams not in the activation dtype",
+     "capture = self._act(np.concatenate([c[1] for c in caps], axis=1))",
+     "capture = np.concatenate([c[1] for c in caps], axis=1)"),
+    ("target positions one late", "pos = self.e + np.arange(R)", "pos = self.e + 1 + np.arange(R)"),
+    ("target MLP without its residual",
+     'x = x + (silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)) @ self._lin(p + "down").T',
+     'x = (silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)) @ self._lin(p + "down").T'),
+    ("target verify rows skip the final norm", 'z = rms_norm(x, self._lin("final_norm"), sh.rms_eps)', "z = x"),
+]
+
+
+def load_mutant(old: str, new: str, path: str = ORACLE_SRC) -> types.ModuleType:
+    src = open(path).read()
     assert src.count(old) == 1, f"passage not found exactly once: {old!r}"
-    name = "dflash_oracle_mutant"
+    name = "oracle_mutant"
     mod = types.ModuleType(name)
-    mod.__file__ = ORACLE_SRC
+    mod.__file__ = path
     sys.modules[name] = mod  # dataclasses resolve their annotations through sys.modules
     try:
-        exec(compile(src.replace(old, new), ORACLE_SRC + " (mutant)", "exec"), mod.__dict__)
+        exec(compile(src.replace(old, new), path + " (mutant)", "exec"), mod.__dict__)
     finally:
         del sys.modules[name]
     return mod
@@ -141,3 +167,38 @@ def test_planted_mistake_fails_a_pin(pin_calls, monkeypatch, name, old, new):
         except Exception:
             return  # caught
     pytest.fail(f"no pin fails with the planted mistake: {name}")
+
+
+@pytest.fixture(scope="module")
+def target_pin_calls():
+    micro = tpins.weights(tpins.MICRO_T)
+    micro_bf16 = tpins.weights(tpins.MICRO_T.with_(weight_dtype="bf16", act_dtype="bf16"))
+    T = tpins
+    return [
+        lambda: T.test_target_trim_legality_and_the_slack_floor(micro),
+        lambda: T.test_capture_is_the_residual_stream_before_the_final_norm(micro),
+        lambda: T.test_sliding_window_past_the_context_equals_full_attention(micro),
+        lambda: T.test_verify_forward_matches_torch_formulation(micro, micro_bf16, "f32"),
+        lambda: T.test_verify_forward_matches_torch_formulation(micro, micro_bf16, "bf16"),
+        lambda: T.test_post_trim_caches_equal_a_target_rebuilt_from_the_committed_tokens(micro),
+        lambda: T.test_speculative_decoding_is_token_identical_to_greedy_decoding(micro, 0.7),
+    ]
+
+
+def test_real_target_oracle_passes_every_pin_call(target_pin_calls):
+    for call in target_pin_calls:
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", TARGET_MUTANTS, ids=[m[0] for m in TARGET_MUTANTS])
+def test_planted_target_mistake_fails_a_pin(target_pin_calls, monkeypatch, name, old, new):
+    mod = load_mutant(old, new, TARGET_SRC)
+    monkeypatch.setattr(tpins, "OracleTarget", mod.OracleTarget)
+    for call in target_pin_calls:
+        try:
+            with np.errstate(all="ignore"):
+                call()
+        except Exception:
+            return  # caught
+    pytest.fail(f"no pin fails with the planted mistake: {name}")
+
