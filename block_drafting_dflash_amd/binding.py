@@ -22,6 +22,8 @@ EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cach
            "dflash_draft_block", "dflash_lm_head_argmax", "dflash_lm_head_argmax_noalloc", "dflash_time_next_argmax",
            "dflash_verify_greedy", "dflash_hbm_read_probe", "dflash_width_ctl_create", "dflash_width_ctl_width",
            "dflash_width_ctl_record", "dflash_width_ctl_state", "dflash_width_ctl_destroy",
+           "dflash_target_query_sizes", "dflash_target_create", "dflash_target_destroy", "dflash_target_forward",
+           "dflash_target_trim", "dflash_target_state", "dflash_target_cache_read", "dflash_target_last_error",
            "dflash_cache_state",
            "dflash_cache_read", "dflash_last_error", "dflash_status_string")
 
@@ -43,9 +45,23 @@ class dflash_layer(ctypes.Structure):
         (n, ctypes.c_void_p) for n in ("in_norm", "post_norm", "q_norm", "k_norm")]
 
 
+class dflash_target_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden", "layers", "q_heads", "kv_heads", "head_dim", "intermediate", "vocab",
+        "window", "max_context", "max_block")] + [
+        ("full_mask", ctypes.c_uint64), ("n_capture", ctypes.c_int32), ("capture_layers", ctypes.c_int32 * 8),
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+        ("weight_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+
+
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("lm_head", dflash_linear), ("fc", dflash_linear),
                 ("enc_norm", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(dflash_layer))]
+
+
+class dflash_target_weights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", dflash_linear), ("final_norm", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(dflash_layer))]
 
 
@@ -79,6 +95,15 @@ def lib() -> ctypes.CDLL:
         "dflash_width_ctl_state": (i32, [vp, P(i32), P(i32), P(i32), P(ctypes.c_double), P(ctypes.c_double),
                                          P(i64), P(i64)]),
         "dflash_width_ctl_destroy": (None, [vp]),
+        "dflash_target_query_sizes": (i32, [P(dflash_target_config), P(sz), P(sz), P(sz)]),
+        "dflash_target_create": (i32, [P(dflash_target_config), P(dflash_target_weights), vp, sz, vp, sz, vp, sz, vp,
+                                       P(vp)]),
+        "dflash_target_destroy": (None, [vp]),
+        "dflash_target_forward": (i32, [vp, i32, vp, i32, vp, vp, vp]),
+        "dflash_target_trim": (i32, [vp, i32]),
+        "dflash_target_state": (i32, [vp, P(i64), P(i32), P(i32)]),
+        "dflash_target_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
+        "dflash_target_last_error": (ctypes.c_char_p, [vp]),
         "dflash_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
         "dflash_cache_state": (i32, [vp, P(i64), P(i32), P(i32), P(i32)]),
         "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
@@ -338,4 +363,108 @@ class WidthController:
         _check(lib().dflash_width_ctl_state(self.h, *(ctypes.byref(x) for x in (i, c, ch, ir, cr, n, a))), None)
         return {"incumbent": i.value, "challenger": c.value, "challenging": bool(ch.value),
                 "incumbent_rate": ir.value, "challenge_rate": cr.value, "challenges": n.value, "adoptions": a.value}
+
+
+def make_target_config(t, max_block: int) -> dflash_target_config:
+    cfg = dflash_target_config(
+        hidden=t.hidden, layers=t.layers, q_heads=t.q_heads, kv_heads=t.kv_heads, head_dim=t.head_dim,
+        intermediate=t.intermediate, vocab=t.vocab, window=t.window, max_context=t.max_context, max_block=max_block,
+        full_mask=sum(1 << l for l in t.full_layers), n_capture=len(t.capture_layers),
+        rms_eps=t.rms_eps, rope_theta=t.rope_theta, weight_dtype=_DTYPE[t.weight_dtype], act_dtype=_DTYPE[t.act_dtype])
+    for i, l in enumerate(t.capture_layers):
+        cfg.capture_layers[i] = l
+    return cfg
+
+
+def _check_target(status: int, t) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.dflash_target_last_error(t).decode() or L.dflash_status_string(status).decode()
+        raise DFlashError(status, msg)
+
+
+class Target:
+    """One dflash_target: the round's target (verify forward, caches, trim) bound to device
+    weights; `dev_weights` holds its layers, final_norm, and the embedding table and lm_head
+    it shares with the drafter."""
+
+    def __init__(self, tshape, dev_weights: Dict[str, object], max_block: int, device="cuda", stream=None):
+        L = lib()
+        self.shape = tshape
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.cfg = make_target_config(tshape, max_block)
+        self._w = dev_weights
+
+        def lin(name):
+            t = dev_weights[name]
+            if isinstance(t, tuple):
+                return dflash_linear(_ptr(t[0]), _ptr(t[1]), _ptr(t[2]))
+            return dflash_linear(_ptr(t), None, None)
+
+        layers = (dflash_layer * tshape.layers)()
+        for l in range(tshape.layers):
+            p = f"layers.{l}."
+            layers[l] = dflash_layer(*[lin(p + n) for n in ("q", "k", "v", "o", "gate", "up", "down")],
+                                     *[_ptr(dev_weights[p + n]) for n in ("in_norm", "post_norm", "q_norm", "k_norm")])
+        self._layers = layers
+        self.weights = dflash_target_weights(_ptr(dev_weights["embed"]), lin("lm_head"), _ptr(dev_weights["final_norm"]),
+                                             ctypes.cast(layers, ctypes.POINTER(dflash_layer)))
+        cb, wb, pb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.dflash_target_query_sizes(ctypes.byref(self.cfg), ctypes.byref(cb), ctypes.byref(wb), ctypes.byref(pb)),
+               None)
+        self.cache = torch.empty(max(cb.value, 256), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(wb.value, 256), dtype=torch.uint8, device=self.device)
+        self.packed = torch.empty(max(pb.value, 256), dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(L.dflash_target_create(ctypes.byref(self.cfg), ctypes.byref(self.weights), _ptr(self.cache), cb.value,
+                                      _ptr(self.workspace), wb.value, _ptr(self.packed), pb.value, _stream(stream),
+                                      ctypes.byref(h)), None)
+        self.t = h
+        self.act_dtype = torch.float32 if tshape.act_dtype == "f32" else torch.bfloat16
+        self.rows_max = max(max_block + 1, 32)
+
+    def __del__(self):
+        t = getattr(self, "t", None)
+        if t and _lib is not None:
+            _lib.dflash_target_destroy(t)
+            self.t = None
+
+    def forward(self, anchor: int, tokens: Optional[torch.Tensor], n: int, argmax: Optional[torch.Tensor] = None,
+                capture: Optional[torch.Tensor] = None, stream=None):
+        """Rows [anchor, tokens[0..n-2]]: returns (argmax int32 [n], capture or None)."""
+        if argmax is None:
+            argmax = torch.empty(n, dtype=torch.int32, device=self.device)
+        for t_, dt in ((tokens, torch.int32), (argmax, torch.int32), (capture, self.act_dtype)):
+            if t_ is not None and (t_.device != self.device or t_.dtype != dt or not t_.is_contiguous()):
+                raise ValueError(f"expected a contiguous {dt} tensor on {self.device}")
+        if tokens is not None and tokens.numel() < n - 1:
+            raise ValueError("tokens too short")
+        if capture is not None and capture.numel() < n * len(self.shape.capture_layers) * self.shape.hidden:
+            raise ValueError("capture output too small")
+        _check_target(lib().dflash_target_forward(self.t, int(anchor), _ptr(tokens), int(n), _ptr(argmax),
+                                                  _ptr(capture), _stream(stream)), self.t)
+        return argmax, capture
+
+    def trim(self, m: int) -> None:
+        _check_target(lib().dflash_target_trim(self.t, int(m)), self.t)
+
+    def state(self) -> Tuple[int, int, int]:
+        e, p, s = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check_target(lib().dflash_target_state(self.t, ctypes.byref(e), ctypes.byref(p), ctypes.byref(s)), self.t)
+        return e.value, p.value, s.value
+
+    def cache_read(self, layer: int, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """The committed keys and values the next query sees on `layer`: [kv_heads, n, head_dim]
+        each (the library writes them packed; n <= e)."""
+        e = self.state()[0]
+        kv, hd = self.shape.kv_heads, self.shape.head_dim
+        k = torch.empty(max(1, e) * kv * hd, dtype=self.act_dtype, device=self.device)
+        v = torch.empty_like(k)
+        n = ctypes.c_int32()
+        _check_target(lib().dflash_target_cache_read(self.t, int(layer), _ptr(k), _ptr(v), ctypes.byref(n),
+                                                     _stream(stream)), self.t)
+        m = n.value
+        return k[:kv * m * hd].view(kv, m, hd), v[:kv * m * hd].view(kv, m, hd)
 

@@ -23,6 +23,12 @@
 // context is created, so every slot holds finite values and keys outside a query's window
 // can be read and given weight exactly 0.
 //
+// The same kernels serve a target's verify forward (AttnShape causal): each query sees the
+// keys q - W < p <= q (every earlier position on full-attention layers), and the block's own
+// keys and values become cache rows: the MFMA kernel writes the ones it forms into their
+// slots, the other paths write them first, as for the drafter (lablup/mlxcel #1762, What
+// changed, "Muse target": trim rollback over mixed sliding and full caches).
+//
 // Work split: keys are cut into chunks of 64 absolute positions (aligned to multiples of
 // 64, so the cut never depends on the phase and every 8-key run is one aligned 16-byte
 // load). One work-group per (chunk, kv head) computes, for the kv group's query vectors,
@@ -237,7 +243,10 @@ __global__ __launch_bounds__(256) void ring_write_kernel(AttnShape a, const floa
 
 // Keys of a query: absolute positions lo..e+R-1 (lo = max(0, e - W)); chunk c of a launch
 // covers positions (lo/64 + c)*64 .. + 64.
-__host__ __device__ inline int64_t attn_lo(const AttnShape& a, int64_t e) { return e > a.window ? e - a.window : 0; }
+__host__ __device__ inline int64_t attn_lo(const AttnShape& a, int64_t e) {
+  if (a.causal) return e > a.window - 1 ? e - (a.window - 1) : 0;  // the query at e sees e-W+1..e
+  return e > a.window ? e - a.window : 0;
+}
 __host__ __device__ inline int attn_nchunks(const AttnShape& a, int R, int64_t e) {
   return (int)((e + R - 1) / ATTN_CHUNK - attn_lo(a, e) / ATTN_CHUNK + 1);
 }
@@ -294,7 +303,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnShape a, const vo
         float sc = -INFINITY;
         const int64_t qp = e + (q0 + qi) / G;
         const int64_t dist = qp > kp ? qp - kp : kp - qp;
-        if (kp >= lo && kp < hi && dist <= a.window) {
+        const bool in_window = a.causal ? (kp <= qp && qp - kp < a.window) : dist <= a.window;
+        if (kp >= lo && kp < hi && in_window) {
           float s = 0.f;
           const float* qv = Qs + qi * hd;
           const float* kv = Ks + kj * KS;
@@ -513,7 +523,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* rin
         vst[(EPT * t16 + j) * VSTR + i] = sv1[j];
         vst[(HALF + EPT * t16 + j) * VSTR + i] = sv2[j];
       }
-      if (p < e && blockIdx.z == 0) {  // a committed row: also into its ring slots
+      if ((p < e || a.causal) && blockIdx.z == 0) {  // a committed (or target block) row: also into its slots
         uint16_t* Kw = ring_layer + (size_t)g * C * HD + (size_t)slot_at(i) * HD + EPT * t16;
         uint16_t* VTw = ring_layer + (size_t)(a.nkv + g) * HD * C + slot_at(i);
 #pragma unroll
@@ -641,7 +651,8 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* rin
       for (int i = 0; i < 4; ++i) {
         const int kp = kbase + 32 * h + 8 * lg + 4 * tb + i;
         const int dist = r > kp ? r - kp : kp - r;
-        const bool vis = qok && kp >= klo && kp < R && dist <= a.window;
+        const bool in_window = a.causal ? (kp <= r && r - kp < a.window) : dist <= a.window;
+        const bool vis = qok && kp >= klo && kp < R && in_window;
         S[h][tb][i] = vis ? acc[i] * sl2 : -INFINITY;
         m = fmaxf(m, S[h][tb][i]);
       }
@@ -790,11 +801,13 @@ hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const 
   return hipGetLastError();
 }
 
-size_t attention_partial_floats(const AttnShape& a, int R) {
-  // chunks of a launch: positions lo..e+R-1 (at most W + R of them) cut at multiples of 64
-  const int nch = (a.window + R + 2 * ATTN_CHUNK - 2) / ATTN_CHUNK;
+size_t attention_partial_floats_span(const AttnShape& a, int R, int span) {
+  // chunks of a launch: positions lo..e+R-1 (at most span + R of them) cut at multiples of 64
+  const int nch = (span + R + 2 * ATTN_CHUNK - 2) / ATTN_CHUNK;
   return (size_t)a.nkv * nch * R * (a.nq / a.nkv) * PART_STRIDE(a.hd);
 }
+
+size_t attention_partial_floats(const AttnShape& a, int R) { return attention_partial_floats_span(a, R, a.window); }
 
 int attention_max_chunks() { return COMBINE_MAX_CHUNKS; }
 

@@ -333,6 +333,9 @@ struct GemmCall {
   // argmax only: per-work-group keys go here (part_bytes long) instead of the workspace
   unsigned long long* part = nullptr;
   size_t part_bytes = 0;
+  // residual only: also store the finished rows here ([rows, ldy2], act dtype)
+  void* y2 = nullptr;
+  int64_t ldy2 = 0;
 };
 
 dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
@@ -419,6 +422,9 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
       p.y = (unsigned char*)gc.y + (size_t)r0 * gc.ldy * y_elt;
       p.ylo = gc.ylo ? (unsigned char*)gc.ylo + (size_t)r0 * gc.ldy * y_elt : nullptr;
       p.ldy = gc.ldy;
+      p.y2 = gc.y2 ? (unsigned char*)gc.y2 + (size_t)r0 * gc.ldy2 * g.act_elt : nullptr;
+      p.ldy2 = gc.ldy2;
+      p.y2_bf16 = g.bf ? 1 : 0;
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
@@ -782,7 +788,7 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
 
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   dflash_status s = dev(ctx,
-                        launch_embed(g.bf, ctx->embed, H, anchor, c.mask_token_id, R, nf,
+                        launch_embed(g.bf, ctx->embed, H, c.vocab, anchor, c.mask_token_id, nullptr, R, nf,
                                      (const float*)(ctx->ws + ctx->lay.app_fc), x, rope, ctx->e, c.rope_theta,
                                      c.head_dim, st),
                         "embed");
@@ -889,6 +895,359 @@ dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, voi
   *n_out = n;
   const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
   return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),
+             "cache read");
+}
+
+}  // extern "C"
+
+// ======================================================================================
+// The target's verify forward (dflash_target_*). A target context embeds a drafter-style
+// engine (`core`): the same GEMM driver, packed-weight layout, workspace layout and launch
+// plans, with the target's layers in place of the drafter's; per layer its own cache (a
+// sliding ring of window + slack slots, or a full-attention buffer of max_context slots) and
+// attention shape (causal: the block's own keys and values become cache rows).
+// ======================================================================================
+
+struct dflash_target {
+  dflash_ctx core;
+  dflash_target_config tc;
+  int R = 0;                      // rows per forward at most
+  std::vector<AttnShape> shape;   // per layer
+  std::vector<size_t> cache_off;  // per layer byte offset of its K [nkv][cap][hd] and V^T [nkv][hd][cap]
+  std::vector<int> capture_slot;  // per layer: its place in the captured row, or -1
+  size_t cache_total = 0;
+  bool has_full = false;
+};
+
+namespace {
+
+constexpr int TARGET_MAX_BLOCK = 64;
+constexpr int TARGET_CHUNK_ROWS = 32;  // rows of a prompt chunk a forward may take
+
+bool target_full(const dflash_target_config& c, int l) { return l < 64 && ((c.full_mask >> l) & 1ull); }
+
+// Validate the target config and derive the engine's Cfg plus per-layer shapes and offsets.
+dflash_status check_target(const dflash_target_config* c, dflash_target* t, char* err) {
+  if (!c) return cfg_fail(err, DFLASH_E_ARG, "target config is NULL");
+  if (c->layers < 1 || c->layers > 64) return cfg_fail(err, DFLASH_E_SHAPE, "target layers must be 1..64");
+  if (c->window < 1 || c->window > MAX_WINDOW) return cfg_fail(err, DFLASH_E_SHAPE, "window must be 1..%d", MAX_WINDOW);
+  if (c->max_context < 64 || c->max_context > MAX_WINDOW)
+    return cfg_fail(err, DFLASH_E_SHAPE, "max_context must be 64..%d", MAX_WINDOW);
+  if (c->max_block < 1 || c->max_block > TARGET_MAX_BLOCK)
+    return cfg_fail(err, DFLASH_E_RANGE, "target max_block must be 1..%d", TARGET_MAX_BLOCK);
+  if (c->n_capture < 1 || c->n_capture > 8) return cfg_fail(err, DFLASH_E_SHAPE, "1..8 capture layers");
+  for (int i = 0; i < c->n_capture; ++i)
+    if (c->capture_layers[i] < 0 || c->capture_layers[i] >= c->layers || (i && c->capture_layers[i] <= c->capture_layers[i - 1]))
+      return cfg_fail(err, DFLASH_E_SHAPE, "capture layers must be strictly increasing layer ids");
+  const int R = std::max(c->max_block + 1, TARGET_CHUNK_ROWS);
+  // the engine's shape: the drafter checks with fc = one stream of hidden (unused), the
+  // widest attention span, and the rows of a forward
+  dflash_config d{};
+  d.hidden = c->hidden;
+  d.layers = c->layers;
+  d.q_heads = c->q_heads;
+  d.kv_heads = c->kv_heads;
+  d.head_dim = c->head_dim;
+  d.intermediate = c->intermediate;
+  d.vocab = c->vocab;
+  d.target_streams = 1;
+  d.target_width = c->hidden;
+  d.window = std::max(c->window, c->max_context);
+  d.max_block = R - 1;
+  d.mask_token_id = 0;
+  d.ring_phase = 0;
+  d.rms_eps = c->rms_eps;
+  d.rope_theta = c->rope_theta;
+  d.weight_dtype = c->weight_dtype;
+  d.act_dtype = c->act_dtype;
+  Cfg g;
+  const dflash_status s = check_cfg(&d, &g, err);
+  if (s != DFLASH_OK) return s;
+  g.S = slack_rows(c->max_block);  // the sliding caches' slack follows the verify block
+  t->core.cfg = g;
+  t->tc = *c;
+  t->R = R;
+  t->shape.assign(c->layers, g.a);
+  t->cache_off.assign(c->layers, 0);
+  t->capture_slot.assign(c->layers, -1);
+  for (int i = 0; i < c->n_capture; ++i) t->capture_slot[c->capture_layers[i]] = i;
+  size_t off = 0;
+  for (int l = 0; l < c->layers; ++l) {
+    AttnShape& a = t->shape[l];
+    a.causal = 1;
+    a.phase = 0;
+    int64_t cap;
+    if (target_full(*c, l)) {
+      t->has_full = true;
+      a.window = 1 << 30;  // past every distance
+      cap = c->max_context;
+    } else {
+      a.window = c->window;
+      cap = std::max<int64_t>({(int64_t)c->window + g.S, (int64_t)c->window + R, (int64_t)64});
+    }
+    a.cap = (int32_t)((cap + 7) & ~(int64_t)7);
+    t->cache_off[l] = off;
+    off = align256(off + (size_t)g.act_elt * 2 * c->kv_heads * (size_t)a.cap * c->head_dim);
+  }
+  t->cache_total = off;
+  return DFLASH_OK;
+}
+
+Layout target_layout(const dflash_target* t) {
+  Layout L = make_layout(t->core.cfg);
+  // attention partials for the widest span: a full layer's whole context
+  const Cfg& g = t->core.cfg;
+  const size_t need = 4 * attention_partial_floats_span(g.a, t->R, t->tc.max_context);
+  if (need > L.total - L.part) {
+    L.part = L.total;
+    L.total = align256(L.total + need);
+  }
+  return L;
+}
+
+size_t target_packed_bytes(const dflash_target* t, std::vector<size_t>* offs) {
+  const Cfg& g = t->core.cfg;
+  const dflash_target_config& c = t->tc;
+  const int64_t H = c.hidden, qd = (int64_t)c.q_heads * c.head_dim, kvd = (int64_t)c.kv_heads * c.head_dim;
+  size_t total = 0;
+  auto add = [&](int64_t N, int64_t K) {
+    if (offs) offs->push_back(total);
+    total = align256(total + linear_bytes(g, N, K));
+  };
+  add(c.vocab, H);
+  for (int l = 0; l < c.layers; ++l) {
+    add(qd, H);
+    add(kvd, H);
+    add(kvd, H);
+    add(H, qd);
+    add(c.intermediate, H);
+    add(c.intermediate, H);
+    add(H, c.intermediate);
+  }
+  return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_target_query_sizes(const dflash_target_config* cfg, size_t* cache_bytes, size_t* workspace_bytes,
+                                        size_t* packed_bytes) {
+  dflash_target t;
+  const dflash_status s = check_target(cfg, &t, g_create_err);
+  if (s != DFLASH_OK) return s;
+  if (!cache_bytes || !workspace_bytes || !packed_bytes) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL size output");
+  *cache_bytes = t.cache_total;
+  *workspace_bytes = target_layout(&t).total;
+  *packed_bytes = target_packed_bytes(&t, nullptr);
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_create(const dflash_target_config* cfg, const dflash_target_weights* wts, void* cache,
+                                   size_t cache_bytes, void* workspace, size_t workspace_bytes, void* packed,
+                                   size_t packed_bytes, void* stream, dflash_target** out) {
+  g_create_err[0] = 0;
+  if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
+  *out = nullptr;
+  dflash_target* t = new (std::nothrow) dflash_target();
+  if (!t) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
+  auto bail = [&](dflash_status st) {
+    delete t;
+    return st;
+  };
+  dflash_status s = check_target(cfg, t, g_create_err);
+  if (s != DFLASH_OK) return bail(s);
+  if (!wts || !wts->layers || !wts->embed) return bail(cfg_fail(g_create_err, DFLASH_E_ARG, "weights, layers or embed NULL"));
+  if (!cache || !workspace || !packed) return bail(cfg_fail(g_create_err, DFLASH_E_ARG, "cache, workspace or packed is NULL"));
+  if (((uintptr_t)cache & 255u) || ((uintptr_t)workspace & 255u) || ((uintptr_t)packed & 255u))
+    return bail(cfg_fail(g_create_err, DFLASH_E_ARG, "cache, workspace and packed must be 256-byte aligned"));
+  const Layout lay = target_layout(t);
+  std::vector<size_t> poff;
+  const size_t pk = target_packed_bytes(t, &poff);
+  if (cache_bytes < t->cache_total || workspace_bytes < lay.total || packed_bytes < pk)
+    return bail(cfg_fail(g_create_err, DFLASH_E_SHAPE, "cache, workspace or packed smaller than the queried sizes"));
+  const Cfg& g = t->core.cfg;
+  auto lin_ok = [&](const dflash_linear& l) {
+    if (!l.w || !aligned16(l.w)) return false;
+    if (g.wt == WT_Q4) return l.scales && l.biases;
+    return true;
+  };
+  auto gain_ok = [&](const void* p) { return p && aligned16(p); };
+  if (!lin_ok(wts->lm_head) || !gain_ok(wts->final_norm))
+    return bail(cfg_fail(g_create_err, DFLASH_E_ARG, "lm_head or final_norm NULL or misaligned"));
+  for (int l = 0; l < g.c.layers; ++l) {
+    const dflash_layer& L = wts->layers[l];
+    if (!lin_ok(L.q) || !lin_ok(L.k) || !lin_ok(L.v) || !lin_ok(L.o) || !lin_ok(L.gate) || !lin_ok(L.up) ||
+        !lin_ok(L.down) || !gain_ok(L.in_norm) || !gain_ok(L.post_norm) || !gain_ok(L.q_norm) || !gain_ok(L.k_norm))
+      return bail(cfg_fail(g_create_err, DFLASH_E_ARG, "target layer %d has a NULL or misaligned weight", l));
+  }
+  dflash_ctx& ctx = t->core;
+  ctx.lay = lay;
+  ctx.ws = (unsigned char*)workspace;
+  ctx.ring = (unsigned char*)cache;
+  ctx.embed = wts->embed;
+  ctx.final_norm = wts->final_norm;
+  auto cv = [](const dflash_linear& l) { return Lin{l.w, l.scales, l.biases}; };
+  ctx.lm_head = cv(wts->lm_head);
+  ctx.layers.resize(g.c.layers);
+  for (int l = 0; l < g.c.layers; ++l) {
+    const dflash_layer& L = wts->layers[l];
+    ctx.layers[l] = Layer{cv(L.q), cv(L.k), cv(L.v), cv(L.o), cv(L.gate), cv(L.up), cv(L.down),
+                          L.in_norm, L.post_norm, L.q_norm, L.k_norm};
+  }
+  hipError_t e = hipGetDevice(&ctx.device);
+  hipStream_t st = (hipStream_t)stream;
+  {
+    const dflash_config& c = g.c;
+    const int H = c.hidden, qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim, I = c.intermediate;
+    unsigned char* base = (unsigned char*)packed;
+    size_t idx = 0;
+    auto pack = [&](Lin& l, int N, int K) {
+      unsigned char* dst = base + poff[idx++];
+      if (g.wt == WT_Q4) {
+        unsigned char* sdst = dst + q4_code_bytes(N, K);
+        if (e == hipSuccess) e = launch_pack_q4(l.w, l.s, l.b, N, K, dst, sdst, st);
+        l.s = sdst;
+        l.b = nullptr;
+      } else if (e == hipSuccess) {
+        e = launch_pack(g.wt, l.w, N, K, dst, st);
+      }
+      l.w = dst;
+    };
+    pack(ctx.lm_head, c.vocab, H);
+    for (int l = 0; l < c.layers; ++l) {
+      Layer& L = ctx.layers[l];
+      pack(L.q, qd, H);
+      pack(L.k, kvd, H);
+      pack(L.v, kvd, H);
+      pack(L.o, H, qd);
+      pack(L.gate, I, H);
+      pack(L.up, I, H);
+      pack(L.down, H, I);
+    }
+  }
+  // every slot starts finite (zero): attention reads whole aligned runs of slots
+  if (e == hipSuccess) e = hipMemsetAsync(cache, 0, t->cache_total, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return bail(cfg_fail(g_create_err, DFLASH_E_DEVICE, "target init: %s", hipGetErrorString(e)));
+  *out = t;
+  return DFLASH_OK;
+}
+
+void dflash_target_destroy(dflash_target* t) { delete t; }
+
+const char* dflash_target_last_error(const dflash_target* t) { return t ? t->core.err : g_create_err; }
+
+dflash_status dflash_target_forward(dflash_target* t, int32_t anchor, const int32_t* d_tokens, int32_t n,
+                                    int32_t* d_argmax, void* d_capture, void* stream) {
+  if (!t) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &t->core;
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  const dflash_target_config& tc = t->tc;
+  if (n < 1 || n > t->R) return fail(ctx, DFLASH_E_RANGE, "forward of %d rows outside 1..%d", n, t->R);
+  if (anchor < 0 || anchor >= c.vocab) return fail(ctx, DFLASH_E_RANGE, "anchor %d outside [0, %d)", anchor, c.vocab);
+  if (!d_argmax || (n > 1 && !d_tokens)) return fail(ctx, DFLASH_E_ARG, "NULL argmax output or block tokens");
+  if (ctx->pending) return fail(ctx, DFLASH_E_STATE, "%lld rows pending: trim first", (long long)ctx->pending);
+  if (t->has_full && ctx->e + n > tc.max_context)
+    return fail(ctx, DFLASH_E_RANGE, "positions past max_context %d", tc.max_context);
+  hipStream_t st = (hipStream_t)stream;
+  const int R = n, H = c.hidden;
+  const int qd = c.q_heads * c.head_dim, kvd = c.kv_heads * c.head_dim;
+  float* x = (float*)(ctx->ws + ctx->lay.x);
+  float* qkv = (float*)(ctx->ws + ctx->lay.qkv);
+  void* qb = ctx->ws + ctx->lay.qb;
+  void* attn = ctx->ws + ctx->lay.attn;
+  void* mlp = ctx->ws + ctx->lay.mlp;
+  void* qb_lo = lo_plane(g, qb, g.R, qd);
+  void* attn_lo = lo_plane(g, attn, g.R, qd);
+  void* mlp_lo = lo_plane(g, mlp, g.R, c.intermediate);
+  float* part = (float*)(ctx->ws + ctx->lay.part);
+  float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
+  const int64_t ldcap = (int64_t)tc.n_capture * H;
+  dflash_status s = dev(ctx,
+                        launch_embed(g.bf, ctx->embed, H, c.vocab, anchor, 0, d_tokens, R, 0, nullptr, x, rope, ctx->e,
+                                     c.rope_theta, c.head_dim, st),
+                        "embed");
+  if (s != DFLASH_OK) return s;
+  for (int l = 0; l < c.layers; ++l) {
+    const Layer& L = ctx->layers[l];
+    GemmCall q{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
+               L.in_norm, qkv, qd + 2 * kvd, nullptr};
+    q.split = g.bf;
+    if ((s = run_gemm(ctx, q, R, st)) != DFLASH_OK) return s;
+    s = dev(ctx,
+            launch_block_attention(g.bf, t->shape[l], qkv, L.q_norm, L.k_norm, rope, ctx->ring + t->cache_off[l], R, 0,
+                                   ctx->e, qb, qb_lo, part, attn, attn_lo, st),
+            "attention");
+    if (s != DFLASH_OK) return s;
+    GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
+    o.split = g.bf;
+    o.xlo = attn_lo;
+    if ((s = run_gemm(ctx, o, R, st)) != DFLASH_OK) return s;
+    GemmCall gu{EPI_SWIGLU, XSRC_NORM, {seg(L.gate, 0, c.intermediate), seg(L.up, 0, c.intermediate)}, H, x, H,
+                L.post_norm, mlp, c.intermediate, nullptr};
+    gu.split = g.bf;
+    gu.ylo = mlp_lo;
+    if ((s = run_gemm(ctx, gu, R, st)) != DFLASH_OK) return s;
+    GemmCall dn{EPI_RESID, XSRC_GLOBAL, {seg(L.down, 0, H)}, c.intermediate, mlp, c.intermediate, nullptr, x, H,
+                nullptr};
+    dn.split = g.bf;
+    dn.xlo = mlp_lo;
+    if (d_capture && t->capture_slot[l] >= 0) {  // the residual stream after this layer
+      dn.y2 = (unsigned char*)d_capture + (size_t)t->capture_slot[l] * H * g.act_elt;
+      dn.ldy2 = ldcap;
+    }
+    if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
+  }
+  // final RMSNorm of every row, then the lm_head argmax
+  void* zrows = ctx->ws + ctx->lay.zrows;
+  void* zrows_lo = lo_plane(g, zrows, R, H);
+  s = dev(ctx, launch_rownorm(g.bf, x, ctx->final_norm, c.rms_eps, R, H, zrows, zrows_lo, st), "final norm");
+  if (s != DFLASH_OK) return s;
+  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_argmax};
+  lm.split = g.bf;
+  lm.xlo = zrows_lo;
+  s = run_gemm(ctx, lm, R, st);
+  if (s != DFLASH_OK) return s;
+  ctx->pending = R;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_trim(dflash_target* t, int32_t m) {
+  if (!t) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &t->core;
+  if (m < 0 || m > ctx->pending || m > ctx->cfg.S)
+    return fail(ctx, DFLASH_E_REWIND, "rewind of %d rows with %lld pending and slack %lld", m, (long long)ctx->pending,
+                (long long)ctx->cfg.S);
+  ctx->e += ctx->pending - m;
+  ctx->pending = 0;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_state(const dflash_target* t, int64_t* e, int32_t* pending, int32_t* slack) {
+  if (!t) return DFLASH_E_ARG;
+  if (e) *e = t->core.e;
+  if (pending) *pending = (int32_t)t->core.pending;
+  if (slack) *slack = (int32_t)t->core.cfg.S;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_cache_read(dflash_target* t, int32_t layer, void* k_out, void* v_out, int32_t* n_out,
+                                       void* stream) {
+  if (!t) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &t->core;
+  if (layer < 0 || layer >= ctx->cfg.c.layers) return fail(ctx, DFLASH_E_RANGE, "layer %d out of range", layer);
+  if (!n_out || !k_out || !v_out) return fail(ctx, DFLASH_E_ARG, "NULL count or window output");
+  const AttnShape& a = t->shape[layer];
+  const int64_t e = ctx->e;
+  const int64_t lo = target_full(t->tc, layer) ? 0 : std::max<int64_t>(0, e - (a.window - 1));
+  const int n = (int)(e - lo);
+  *n_out = n;
+  if (n == 0) return DFLASH_OK;
+  return dev(ctx,
+             launch_cache_read(ctx->cfg.bf, a, ctx->ring + t->cache_off[layer], lo, n, k_out, v_out,
+                               (hipStream_t)stream),
              "cache read");
 }
 

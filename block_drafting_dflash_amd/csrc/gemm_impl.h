@@ -552,7 +552,13 @@ gemm_kernel(const GemmParams p) {
           if constexpr (EPI == EPI_STORE) {
             ((float*)p.y)[o] = v[0][q];
           } else if constexpr (EPI == EPI_RESID) {
-            ((float*)p.y)[o] = (rt == w ? yres[q] : ((const float*)p.y)[o]) + v[0][q];
+            const float nv = (rt == w ? yres[q] : ((const float*)p.y)[o]) + v[0][q];
+            ((float*)p.y)[o] = nv;
+            if (p.y2) {  // a target's captured residual stream
+              const size_t o2 = (size_t)r * p.ldy2 + col;
+              if (p.y2_bf16) ((uint16_t*)p.y2)[o2] = f2bf(nv);
+              else ((float*)p.y2)[o2] = nv;
+            }
           } else if constexpr (EPI == EPI_SWIGLU) {
             const float g = v[0][q], u = v[NB - 1][q];
             op_st<SPLIT>(p.y, p.ylo, o, g / (1.0f + expf(-g)) * u);

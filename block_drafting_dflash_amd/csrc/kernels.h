@@ -81,6 +81,11 @@ struct GemmParams {
   void* y;          // STORE/RESID: f32 [R, ldy]; SWIGLU: hi/lo planes (split) or f32
   void* ylo;
   int64_t ldy;
+  // RESID: when y2 is set, the finished rows are also stored there, [R, ldy2], in bf16
+  // (y2_bf16) or f32 (a target's captured residual stream)
+  void* y2;
+  int64_t ldy2;
+  int32_t y2_bf16;
   unsigned long long* part;  // ARGMAX: per-work-group best keys, [R][grid]
 };
 
@@ -166,6 +171,11 @@ struct AttnShape {
   int32_t window;
   int32_t cap, phase;  // ring slots stored (a multiple of 8, >= 64) and phase (a multiple of 8)
   float eps, theta;
+  // 0 (the drafter): a query at q sees keys with |q - p| <= window, both directions, and the
+  // block's own rows stay out of the cache. 1 (a target's verify forward): it sees keys
+  // q - window < p <= q (a window past every distance on full-attention layers), and the
+  // block's own keys and values are written into their cache slots.
+  int32_t causal = 0;
 };
 
 // Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip).
@@ -176,13 +186,14 @@ hipError_t launch_pack_q4(const void* codes, const void* scales, const void* bia
                           void* dst_scales, hipStream_t s);
 // idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
-// Embedding rows [anchor, mask x (R-1)] as f32 residual rows x; with rope != NULL also the
+// Embedding rows [anchor, t_1 .. t_{R-1}] as f32 residual rows x, where t_i = toks[i-1]
+// (device int32, clamped into [0, vocab)) or the mask token when toks is NULL; with rope != NULL also the
 // rotary table rope[r][i] = (cos, sin), i < hd/2, of positions pos0..pos0+R-1 (rows 0..R-1)
 // and pos0-nprev..pos0-1 (rows R..R+nprev-1). With nprev > 0, the f32 rows prev [nprev][hidden]
 // are copied into x rows R..R+nprev-1.
-hipError_t launch_embed(int act_bf16, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R,
-                        int nprev, const float* prev, float* x, float2* rope, int64_t pos0, float theta, int hd,
-                        hipStream_t s);
+hipError_t launch_embed(int act_bf16, const void* table, int hidden, int vocab, int32_t anchor, int32_t mask_id,
+                        const int32_t* toks, int R, int nprev, const float* prev, float* x, float2* rope, int64_t pos0,
+                        float theta, int hd, hipStream_t s);
 // RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
                           void* out_lo, hipStream_t s);
@@ -203,6 +214,8 @@ hipError_t launch_block_attention(int act_bf16, const AttnShape& a, const float*
 // whether launch_block_attention takes committed rows (n > 0) for this shape
 bool attention_forms_committed_rows(int act_bf16, const AttnShape& a);
 size_t attention_partial_floats(const AttnShape& a, int R);
+// the same for queries whose keys span at most `span` positions before the block
+size_t attention_partial_floats_span(const AttnShape& a, int R, int span);
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
                          hipStream_t s);
 // Streaming read of `bytes` (a multiple of 16, at least groups * 4096) by `groups` work-groups

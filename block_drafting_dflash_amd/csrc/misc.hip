@@ -49,9 +49,10 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
 // theta^(-2i/hd) for i < hd/2, evaluated in f64 and rounded to f32 as the per-element RoPE
 // of the prep kernel does; every layer's attention reads it (rope may be NULL).
 template <bool BF, bool VEC>
-__global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int32_t anchor, int32_t mask_id,
-                                                    int R, int nprev, const float* prev, float* x, float2* rope,
-                                                    int64_t pos0, float theta, int hd) {
+__global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int vocab, int32_t anchor,
+                                                    int32_t mask_id, const int32_t* toks, int R, int nprev,
+                                                    const float* prev, float* x, float2* rope, int64_t pos0,
+                                                    float theta, int hd) {
   const int r = blockIdx.x;
   if (blockIdx.y == 1) {
     const int64_t pos = r < R ? pos0 + r : pos0 - nprev + (r - R);
@@ -69,7 +70,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidde
     for (int v = threadIdx.x; v < hidden / 4; v += blockDim.x) dst[v] = src[v];
     return;
   }
-  const int64_t tok = r == 0 ? anchor : mask_id;
+  // block tokens from device memory (a target's verify rows) are clamped into the table: an
+  // id past the last row would read whatever follows the table (lablup/mlxcel #1751, Review
+  // fixes); the verify kernel reports out-of-range ids in its status word
+  const int64_t tok = r == 0 ? anchor : (toks ? (int64_t)min(max(toks[r - 1], 0), vocab - 1) : mask_id);
   float* xr = x + (size_t)r * hidden;
   if constexpr (VEC) {
     constexpr int EPV = BF ? 8 : 4;  // elements per 16-byte load
@@ -100,24 +104,25 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidde
   }
 }
 
-hipError_t launch_embed(int bf, const void* table, int hidden, int32_t anchor, int32_t mask_id, int R, int nprev,
-                        const float* prev, float* x, float2* rope, int64_t pos0, float theta, int hd, hipStream_t s) {
+hipError_t launch_embed(int bf, const void* table, int hidden, int vocab, int32_t anchor, int32_t mask_id,
+                        const int32_t* toks, int R, int nprev, const float* prev, float* x, float2* rope, int64_t pos0,
+                        float theta, int hd, hipStream_t s) {
   if (nprev < 0 || (nprev > 0 && (!rope || !prev || hidden % 4 || ((uintptr_t)prev & 15u) || ((uintptr_t)x & 15u))))
     return hipErrorInvalidValue;
   const bool vec = ((uintptr_t)table & 15u) == 0 && hidden % 8 == 0;
   const dim3 grid(R + nprev, rope ? 2 : 1);
   if (bf && vec)
-    hipLaunchKernelGGL((embed_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
-                       x, rope, pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, vocab, anchor, mask_id, toks, R,
+                       nprev, prev, x, rope, pos0, theta, hd);
   else if (bf)
-    hipLaunchKernelGGL((embed_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
-                       x, rope, pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, vocab, anchor, mask_id, toks, R,
+                       nprev, prev, x, rope, pos0, theta, hd);
   else if (vec)
-    hipLaunchKernelGGL((embed_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
-                       x, rope, pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, vocab, anchor, mask_id, toks, R,
+                       nprev, prev, x, rope, pos0, theta, hd);
   else
-    hipLaunchKernelGGL((embed_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, anchor, mask_id, R, nprev, prev,
-                       x, rope, pos0, theta, hd);
+    hipLaunchKernelGGL((embed_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, vocab, anchor, mask_id, toks, R,
+                       nprev, prev, x, rope, pos0, theta, hd);
   return hipGetLastError();
 }
 

@@ -269,6 +269,91 @@ dflash_status dflash_width_ctl_state(const dflash_width_ctl *ctl, int32_t *incum
                                      int64_t *challenges, int64_t *adoptions);
 void dflash_width_ctl_destroy(dflash_width_ctl *ctl);
 
+/*
+ * The target side of the round: the verify forward of a causal target that shares its raw
+ * embedding table and untied lm_head with the drafter and hands the drafter its residual
+ * streams (lablup/mlxcel #1762, What changed, "Muse target": residual-stream capture before
+ * the final norm, trim rollback over the mixed caches, sliding caches armed with the
+ * drafter's slack rule; lablup/mlxcel #1751, opening paragraph: the verify forward with
+ * residual-stream capture, a drafter fed five of the target's residual streams).
+ *
+ * Layers are Qwen3-shaped (RMSNorm, q/k/v, per-head q/k RMSNorm, neox RoPE, attention, o +
+ * residual, RMSNorm, SwiGLU, down + residual); a final RMSNorm and the lm_head follow. A
+ * query at absolute position q sees the keys p <= q, and on a sliding layer only q - window <
+ * p (the last `window` positions, itself included). Sliding caches hold window + S slots with
+ * S = max(clamp(8*max_block, 32, 128), max_block); full-attention caches hold max_context.
+ *   hidden, intermediate, q_heads*head_dim, vocab, head_dim, dtypes: as dflash_config.
+ *   full_mask: bit l set = layer l attends to every earlier position (layers <= 64).
+ *   capture_layers[0..n_capture-1]: strictly increasing layer ids (1..8 of them) whose
+ *     residual stream, after the layer and before the final norm, is captured; the captured
+ *     row is the concatenation in this order, [n_capture * hidden], in act_dtype.
+ *   window 1..4096; max_context 64..4096 (positions a full layer can hold; every forward
+ *     must end at or before it when a full layer exists); max_block 1..64 (forwards take at
+ *     most max(max_block + 1, 32) rows).
+ */
+typedef struct {
+  int32_t hidden, layers, q_heads, kv_heads, head_dim, intermediate, vocab;
+  int32_t window, max_context, max_block;
+  uint64_t full_mask;
+  int32_t n_capture, capture_layers[8];
+  float rms_eps, rope_theta;
+  int32_t weight_dtype, act_dtype;
+} dflash_target_config;
+
+/* embed and lm_head: the table and lm_head the drafter binds (the same device buffers may
+ * serve both); layers: a host array of cfg.layers entries (copied at create). */
+typedef struct {
+  const void *embed;
+  dflash_linear lm_head;
+  const void *final_norm;
+  const dflash_layer *layers;
+} dflash_target_weights;
+
+typedef struct dflash_target dflash_target; /* opaque */
+
+/* Bytes of caches, workspace and packed weights a target with this config needs. */
+dflash_status dflash_target_query_sizes(const dflash_target_config *cfg, size_t *cache_bytes,
+                                        size_t *workspace_bytes, size_t *packed_bytes);
+
+/* As dflash_create: validate, bind the caller's buffers (256-byte aligned, at least the
+ * queried sizes), repack the lm_head and layer linears into `packed`, zero the caches, and
+ * synchronise `stream`. The target starts empty: e = 0, no pending rows. */
+dflash_status dflash_target_create(const dflash_target_config *cfg, const dflash_target_weights *weights,
+                                   void *cache, size_t cache_bytes, void *workspace, size_t workspace_bytes,
+                                   void *packed, size_t packed_bytes, void *stream, dflash_target **out);
+void dflash_target_destroy(dflash_target *t);
+
+/*
+ * One forward over n rows [anchor, d_tokens[0], .., d_tokens[n-2]] at absolute positions
+ * e..e+n-1: the verify rows of a round (anchor and the drafted tokens), or a chunk of a prompt.
+ * Their keys and values are appended to every layer's cache as pending rows. d_tokens:
+ * device int32 [n-1] (ids are clamped into [0, vocab)); d_argmax (device int32 [n]) receives
+ * the first index of each row's maximum f32 logit through final_norm and the lm_head;
+ * d_capture (device act_dtype [n, n_capture * hidden], or NULL) the captured residual
+ * streams, which dflash_cache_append takes as the drafter's input rows. Errors: n outside
+ * 1..max rows or anchor outside [0, vocab) (DFLASH_E_RANGE), a full layer that would pass
+ * max_context (DFLASH_E_RANGE), pending rows (DFLASH_E_STATE), NULL d_argmax or a NULL
+ * d_tokens with n > 1 (DFLASH_E_ARG).
+ */
+dflash_status dflash_target_forward(dflash_target *t, int32_t anchor, const int32_t *d_tokens, int32_t n,
+                                    int32_t *d_argmax, void *d_capture, void *stream);
+
+/* Commit the pending rows except the last m (attention caches trim by block - n with n =
+ * accepted + 1: lablup/mlxcel #1751, Implementation Review Summary). Host bookkeeping;
+ * DFLASH_E_REWIND unless 0 <= m <= min(pending, S). */
+dflash_status dflash_target_trim(dflash_target *t, int32_t m);
+
+/* Committed end e, pending rows and slack S. Host only. */
+dflash_status dflash_target_state(const dflash_target *t, int64_t *e, int32_t *pending, int32_t *slack);
+
+/* The committed keys and values the next query (at e) sees on one layer, in position order:
+ * positions max(0, e - window + 1)..e-1 on a sliding layer, 0..e-1 on a full one, into k_out
+ * and v_out (device act_dtype [kv_heads, n, head_dim]); *n_out = n. */
+dflash_status dflash_target_cache_read(dflash_target *t, int32_t layer, void *k_out, void *v_out, int32_t *n_out,
+                                       void *stream);
+
+const char *dflash_target_last_error(const dflash_target *t);
+
 /* Committed end e, pending rows, slack S and capacity C. Host only. */
 dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pending, int32_t *slack,
                                  int32_t *capacity);
