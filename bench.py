@@ -21,7 +21,8 @@ draft_n_accepted, mean accepted with and without the bonus, committed tok/s, acc
 histogram, SHA-256 of the committed token stream): the block-16 round (muse-bf16-b16-ctx4096,
 p = 0.6 stand-in target), the 16384-row context with ring wraps at blocks 8 and 32 (prefill
 timed on its own), the adaptive verify width (the library's controller between blocks 4 and 16
-against both fixed widths), the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16), the tiny
+against both fixed widths), speculative decoding through a synthetic Muse-shaped target
+against classic greedy decoding of it, the 4-bit width sweep (muse-q4-sweep-ctx2048, blocks 4/5/8/16), the tiny
 f32 round (tiny-f32-b4-ctx64), an HBM streaming-read probe, and the CPU oracle on the host
 cores.
 
@@ -416,6 +417,128 @@ def run_adaptive(args, sh, dw) -> dict:
     return out
 
 
+def run_target(args) -> dict:
+    """Speculative decoding against classic greedy decoding of the same synthetic target (the
+    pages' comparison, on synthetic weights): the Muse-shaped target (10 layers, window 2048,
+    full layers 4 and 9, streams captured at layers 1, 3, 5, 7, 9) and the drafter it feeds
+    (fc 5 x 2048 -> 2048), sharing one device copy of the embedding table and lm_head. A
+    1024-token prompt goes through the target in 32-row forwards, its captured streams into
+    the drafter. Classic decode: one target forward per token, its argmax read back. A
+    speculative round at block 4: draft, target verify forward over [anchor, drafts] (its
+    captured streams kept), greedy verify into pinned host memory, the drafter's append of
+    the captured rows, both trims. With random weights the drafter's proposals are rarely
+    the target's tokens, so the rounds mostly commit one token each; the committed stream
+    equals the classic one."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    t = synth.MUSE_BF16_TARGET
+    dsh = synth.drafter_for(t, synth.MUSE_BF16)
+    t0 = time.time()
+    dw = synth.make_weights(dsh)
+    tw = synth.make_target_weights(t, dw)
+    ddev = binding.to_device(dsh, dw)
+    tdev = binding.to_device(t, {k: v for k, v in tw.items() if k not in ("embed", "lm_head")})
+    tdev["embed"], tdev["lm_head"] = ddev["embed"], ddev["lm_head"]
+    del dw, tw
+    torch.cuda.synchronize()
+    print(f"[bench] target pair resident in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    prompt = torch.from_numpy(synth.prompt_tokens(t.vocab, 1024, tag=13).astype(np.int32)).to(dev)
+    ncap = t.streams * t.hidden
+
+    def prefill(tg, dr):
+        a = None
+        for s0 in range(0, 1024, tg.rows_max):
+            n = min(tg.rows_max, 1024 - s0)
+            cap = torch.empty((n, ncap), dtype=torch.bfloat16, device=dev) if dr else None
+            a, _ = tg.forward(int(prompt[s0].item()), prompt[s0 + 1:s0 + n], n, capture=cap, stream=stream)
+            tg.trim(0)
+            if dr:
+                dr.cache_append(cap, commit=True, stream=stream)
+        return int(a[-1].item())
+
+    # classic greedy decode
+    tc = binding.Target(t, tdev, max_block=1)
+    tok = prefill(tc, None)
+    n_classic = args.target_steps
+    classic = [tok]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    for i in range(n_classic):
+        a, _ = tc.forward(classic[-1], None, 1, stream=stream)
+        tc.trim(0)
+        classic.append(int(a[0].item()))
+    classic_s = time.perf_counter() - t0
+    e0.record(stream)
+    tc.forward(classic[-1], None, 1, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd1_ms = e0.elapsed_time(e1)
+    del tc
+    # speculative rounds
+    B = 4
+    tg = binding.Target(t, tdev, max_block=B)
+    dr = binding.Drafter(dsh, ddev, max_block=B)
+    first = prefill(tg, dr)
+    assert first == classic[0]
+    n = args.warmup + args.target_steps
+    toks = torch.empty((n, B), dtype=torch.int32, device=dev)
+    av = torch.empty((n, B + 1), dtype=torch.int32, device=dev)
+    cap = torch.empty((B + 1, ncap), dtype=torch.bfloat16, device=dev)
+    host = torch.empty(3, dtype=torch.int32, pin_memory=True)
+    hv = host.numpy()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ks, bonuses = [], []
+    anchor = first
+    torch.cuda.synchronize()
+    t0 = None
+    for r in range(n):
+        if r == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        timed = r == n - 1
+        if timed: ev[0].record(stream)
+        dr.draft_block(anchor, B, tokens=toks[r], stream=stream)
+        if timed: ev[1].record(stream)
+        tg.forward(anchor, toks[r], B + 1, argmax=av[r], capture=cap, stream=stream)
+        if timed: ev[2].record(stream)
+        hv[:] = -1
+        dr.verify_greedy(toks[r], av[r], B, out=host, stream=stream)
+        dr.cache_append(cap, stream=stream)
+        if timed: ev[3].record(stream)
+        k, bonus, status = await_verify(hv)
+        assert status == 0
+        dr.cache_trim(B - k)
+        tg.trim(B - k)
+        ks.append(k)
+        bonuses.append(bonus)
+        anchor = bonus
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    rounds = args.target_steps
+    d = toks.cpu().numpy()
+    out = [first]
+    for r in range(n):
+        out += [int(x) for x in d[r, :ks[r]]] + [bonuses[r]]
+    committed = sum(k + 1 for k in ks[args.warmup:])
+    m = min(len(out), len(classic))
+    tb = t.layers * (2 * (t.q_heads + 2 * t.kv_heads) * t.head_dim * t.hidden + 2 * 3 * t.intermediate * t.hidden) \
+        + 2 * t.vocab * t.hidden
+    return {"workload": "muse-bf16-target-b4-prompt1024", "block": B, "target_layers": t.layers,
+            "classic_tok_s": round(n_classic / classic_s, 1), "classic_forward_ms": round(fwd1_ms, 4),
+            "classic_forward_hbm_frac": round(tb / (fwd1_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "speculative_rounds_per_s": round(rounds / el, 1), "speculative_committed_tok_s": round(committed / el, 1),
+            "speedup_vs_classic": round((committed / el) / (n_classic / classic_s), 3),
+            "mean_accepted": round(float(np.mean(ks[args.warmup:])), 4),
+            "round_ms": {"draft": round(ev[0].elapsed_time(ev[1]), 4), "target_verify_forward": round(ev[1].elapsed_time(ev[2]), 4),
+                         "verify_and_append": round(ev[2].elapsed_time(ev[3]), 4)},
+            "committed_equals_classic": out[:m] == classic[:m], "tokens_compared": m, "rounds": rounds}
+
+
 def stream_probe(mib: int, reps: int = 10) -> dict:
     """The in-repo HBM streaming-read probe: mib MiB read `reps` times, event-timed."""
     import torch
@@ -486,6 +609,8 @@ def main():
     ap.add_argument("--c3-steps", type=int, default=128, help="timed rounds per width at 16384 context (0 = skip)")
     ap.add_argument("--q4-steps", type=int, default=200, help="timed rounds per width of the q4 sweep (0 = skip)")
     ap.add_argument("--c0-steps", type=int, default=500, help="timed rounds of the tiny f32 round (0 = skip)")
+    ap.add_argument("--target-steps", type=int, default=96,
+                    help="rounds (and classic decode tokens) against the synthetic target (0 = skip)")
     ap.add_argument("--adaptive-steps", type=int, default=768,
                     help="rounds per run of the adaptive-width comparison (0 = skip)")
     ap.add_argument("--probe-mib", type=int, default=1024, help="HBM streaming-read probe size (0 = skip)")
@@ -538,6 +663,8 @@ def main():
     adaptive = run_adaptive(args, sh, dw) if args.adaptive_steps > 0 else None
     del dw
     torch.cuda.empty_cache()
+    target = run_target(args) if args.target_steps > 0 else None
+    torch.cuda.empty_cache()
     q4 = run_q4(args) if args.q4_steps > 0 else None
     c0 = run_c0(args) if args.c0_steps > 0 else None
     probe = stream_probe(args.probe_mib) if args.probe_mib > 0 else None
@@ -577,6 +704,7 @@ def main():
         "block16": b16,
         "ctx16384": c3,
         "adaptive_width": adaptive,
+        "target": target,
         "q4": q4,
         "tiny_f32": c0,
         "cpu_baseline": cpu,

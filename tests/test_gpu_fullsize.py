@@ -127,3 +127,68 @@ def test_q4_ctx2048_deferred_kv(muse_q4):
     ls.check_window()
     _report(f"{wl.name} block 4 deferred", ls, ks)
     assert ls.stats.max_hidden_rel <= 2e-3
+
+
+@pytest.fixture(scope="module")
+def muse_pair():
+    """The Muse-shaped target (10 layers, window 2048, full layers 4 and 9, streams captured
+    at layers 1, 3, 5, 7, 9) and the drafter it feeds (fc 5 x 2048 -> 2048), sharing the
+    embedding table and lm_head."""
+    t = synth.MUSE_BF16_TARGET
+    dsh = synth.drafter_for(t, SH)
+    dw = synth.make_weights(dsh)
+    tw = synth.make_target_weights(t, dw)
+    ddev = binding.to_device(dsh, dw)
+    tdev = binding.to_device(t, {k: v for k, v in tw.items() if k not in ("embed", "lm_head")})
+    tdev["embed"], tdev["lm_head"] = ddev["embed"], ddev["lm_head"]  # one device copy, shared
+    f64 = lambda w: {k: (np.asarray(v, dtype=np.float64) if k != "embed" and getattr(v, "ndim", 0) == 2 else v)
+                     for k, v in w.items()}
+    dw64 = f64(dw)
+    tw64 = {k: (dw64[k] if k in ("embed", "lm_head") else v) for k, v in f64(tw).items()}
+    return t, dsh, dw64, tw64, ddev, tdev
+
+
+def test_muse_target_rounds_match_oracles(muse_pair):
+    """A 256-token prompt through the target in 32-row forwards (captured streams committed to
+    the drafter), then rounds at block 4 with the drafter's own proposals: the target's
+    verify argmaxes and captured streams, the drafter's tokens and hidden rows, the verify
+    result and both caches' offsets in lock-step with the oracles; every target cache window
+    and the drafter's live window at the end."""
+    from oracle.target_oracle import OracleTarget
+    from tests.test_gpu_target import TargetLockStep
+
+    t, dsh, dw64, tw64, ddev, tdev = muse_pair
+    B = 4
+    tls = TargetLockStep(t, tw64, max_block=B, dev=tdev)
+    dls = P.LockStep(dsh, dw64, max_block=B, dev_weights=ddev, check_windows=False)
+    prompt = [int(x) for x in synth.prompt_tokens(t.vocab, 256, tag=11)]
+    for s in range(0, len(prompt), tls.gpu.rows_max):
+        a, cap = tls.forward(prompt[s:s + tls.gpu.rows_max])
+        tls.trim(0)
+        # the drafter takes the oracle's captured rows: the same bits the GPU's are compared to
+        dls.append(tls.orc_last_capture, commit=True)
+    anchor = int(a[-1])
+    for r in range(8):
+        d = dls.draft(anchor, B)
+        a, cap = tls.forward([anchor] + [int(x) for x in d])
+        k, bonus = dls.verify(d, a)
+        dls.append(tls.orc_last_capture)
+        dls.trim(B - k)
+        tls.trim(B - k)
+        anchor = bonus
+    tls.check_caches()
+    torch.cuda.synchronize()
+    dls.check_window()
+    print("muse target rounds: near ties", tls.near_ties, "drafter", dls.stats)
+
+
+def test_muse_speculative_loop_commits_the_tokens_of_classic_decoding(muse_pair):
+    """The identity property at the Muse-shaped sizes, on the GPU alone: the speculative round
+    loop commits bit-for-bit the tokens of classic greedy decoding of the same target."""
+    from tests.test_gpu_target import run_classic, run_speculative
+
+    t, dsh, _, _, ddev, tdev = muse_pair
+    prompt = [int(x) for x in synth.prompt_tokens(t.vocab, 300, tag=12)]
+    want = run_classic(t, tdev, prompt, 24)
+    got, ks = run_speculative(t, dsh, tdev, ddev, prompt, 24, 4)
+    assert got == want

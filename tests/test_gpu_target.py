@@ -53,6 +53,7 @@ class TargetLockStep:
         assert P.rel_rows(cg, res.capture).max() <= self.tol
         assert P.elem_excess(cg, res.capture, self.tol, self.bf16) <= 1.0
         assert self.gpu.state()[:2] == self.orc.state()[:2]
+        self.orc_last_capture = res.capture
         return res.argmax, cap
 
     def trim(self, m):
