@@ -61,6 +61,12 @@ class Shape:
     rope_theta: float = 1e6
     group: int = 64  # q4 group size along the input dim
     mask_token_id: Optional[int] = None
+    # the DSpark form of the drafter (lablup/mlxcel #1751 "LFM2 / LFM2.5 DSpark drafter on
+    # the DFlash loop", opening paragraph): every block row proposes a token through a
+    # low-rank Markov token-transition head, and RoPE may pair adjacent elements
+    variant: str = "dflash"  # "dflash" | "dspark"
+    rope_style: str = "neox"  # "neox" (rotate-half) | "traditional" (adjacent pairs)
+    markov_rank: int = 0
 
     @property
     def mask_id(self) -> int:
@@ -81,6 +87,10 @@ MUSE_BF16 = Shape(hidden=2048, layers=5, q_heads=32, kv_heads=4, head_dim=128, i
                   vocab=202048, target_streams=5, target_width=4096, window=2048,
                   weight_dtype="bf16", act_dtype="bf16")
 MUSE_Q4 = MUSE_BF16.with_(weight_dtype="q4")
+# The Muse-shaped backbone in the DSpark form: a rank-256 Markov head, adjacent-pair RoPE and
+# a window as long as the longest context served (DSpark attends to every context row).
+MUSE_DSPARK_BF16 = MUSE_BF16.with_(variant="dspark", rope_style="traditional", markov_rank=256, window=4096)
+TINY_DSPARK_F32 = TINY_F32.with_(variant="dspark", rope_style="traditional", markov_rank=64, window=256)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -172,7 +182,7 @@ class Workload:
     accept_p: Optional[float] = None
 
 
-# The five round workloads (sizes as named; the bench times the Muse-shaped block-4 one).
+# The round workloads (sizes as named; the bench times the Muse-shaped block-4 one).
 WORKLOADS: Dict[str, Workload] = {
     w.name: w
     for w in [
@@ -181,6 +191,9 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("muse-bf16-b16-ctx4096", MUSE_BF16, 4096, (16,), 64, "synthetic", 0.6),
         Workload("muse-bf16-ctx16384-wrap", MUSE_BF16, 16384, (8, 32), 128, "random_depth"),
         Workload("muse-q4-sweep-ctx2048", MUSE_Q4, 2048, (4, 5, 8, 16), 256, "synthetic"),
+        # DSpark proposals per block at the pages' verify widths 8 and 10 (lablup/mlxcel
+        # #1751, Real-checkpoint validation)
+        Workload("muse-dspark-bf16-w8-w10-ctx1024", MUSE_DSPARK_BF16, 1024, (7, 9), 16, "lm_head"),
     ]
 }
 
@@ -258,6 +271,8 @@ def weight_names(shape: Shape) -> List[str]:
         names += [f"layers.{l}.{t}" for t in
                   ("q", "k", "v", "o", "gate", "up", "down",
                    "in_norm", "post_norm", "q_norm", "k_norm")]
+    if shape.markov_rank > 0:  # last, so that every other tensor keeps its stream
+        names += ["markov_w1", "markov_w2"]
     return names
 
 
@@ -277,6 +292,8 @@ def weight_shape(shape: Shape, name: str) -> Tuple[int, ...]:
         "gate": (shape.intermediate, H),
         "up": (shape.intermediate, H),
         "down": (H, shape.intermediate),
+        "markov_w1": (shape.vocab, shape.markov_rank),
+        "markov_w2": (shape.vocab, shape.markov_rank),
     }[t]
 
 
@@ -284,17 +301,32 @@ def is_gain(name: str) -> bool:
     return name.split(".")[-1] in ("enc_norm", "final_norm", "in_norm", "post_norm", "q_norm", "k_norm")
 
 
+def is_markov(name: str) -> bool:
+    return name.startswith("markov_")
+
+
 def is_quantized(shape: Shape, name: str) -> bool:
-    """q4 applies to fc, every layer linear and the lm_head; embed and gains stay bf16."""
-    return shape.weight_dtype == "q4" and not is_gain(name) and name != "embed"
+    """q4 applies to fc, every layer linear and the lm_head; embed, gains and the Markov
+    factors stay bf16."""
+    return shape.weight_dtype == "q4" and not is_gain(name) and name != "embed" and not is_markov(name)
 
 
-def _draw_block(seed: int, idx: int, blk: int, rows: int, cols: int, gain: bool) -> np.ndarray:
+# Draw scale of the Markov factors: with rank r their transition logits have standard
+# deviation 0.25^2 sqrt(r) (1.0 at rank 256), the size of the Muse-shaped backbone's logits
+# (0.02 sqrt(2048) ~ 0.9), so both terms of a chain step move its argmax.
+MARKOV_SCALE = 0.25
+
+
+def _draw_block(seed: int, idx: int, blk: int, rows: int, cols: int, gain: bool, scale: float = 0.02) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(idx, blk))))
     z = rng.standard_normal((rows, cols), dtype=np.float32)
     if gain:
         return np.float32(1.0) + np.float32(0.02) * z
-    return np.float32(0.02) * z
+    return np.float32(scale) * z
+
+
+def _scale(name: str) -> float:
+    return MARKOV_SCALE if is_markov(name) else 0.02
 
 
 def draw_tensor(shape: Shape, name: str, seed: int = SEED_WEIGHTS,
@@ -312,7 +344,7 @@ def draw_tensor(shape: Shape, name: str, seed: int = SEED_WEIGHTS,
 
     def fill(item):
         b, r0, r1 = item
-        out[r0:r1] = _draw_block(seed, idx, b, r1 - r0, cols, gain)
+        out[r0:r1] = _draw_block(seed, idx, b, r1 - r0, cols, gain, _scale(name))
 
     if pool is None or len(blocks) == 1:
         for it in blocks:
@@ -335,7 +367,7 @@ def draw_rows(shape: Shape, name: str, rows: Iterable[int], seed: int = SEED_WEI
         b = r // ROW_BLOCK
         if b not in cache:
             r0, r1 = b * ROW_BLOCK, min(nrows, (b + 1) * ROW_BLOCK)
-            cache[b] = _draw_block(seed, idx, b, r1 - r0, cols, is_gain(name))
+            cache[b] = _draw_block(seed, idx, b, r1 - r0, cols, is_gain(name), _scale(name))
         out[i] = cache[b][r - b * ROW_BLOCK]
     return out
 

@@ -23,8 +23,8 @@ What the round computes (readings where the pages are silent are marked READING)
     round, third finding]. READING: each layer's K/V of a context row are
     k = RoPE(k_norm(c W_k^T), p), v = c W_v^T with c the encoder output, and are
     written to a ring slot (p + phase) mod C; the draft's own block K/V are transient
-    and attended after the context K/V [dspark, Verified against the issue: "Context K/V
-    only in the drafter cache with proposal K/V concatenated after"].
+    and attended after the context K/V (the cache holds context rows only) [dspark,
+    Implementation Review Summary, Verified against the issue].
   * draft: rows [anchor, mask x B] at absolute positions e..e+B embedded with the
     target's raw table [muse, What changed: raw table, not the embed_norm lookup], then
     five Qwen3-shaped layers [dflash, Why] with per-head q/k RMSNorm and bidirectional
@@ -35,8 +35,8 @@ What the round computes (readings where the pages are silent are marked READING)
     [muse, What changed]; the drafted token of row j (j = 1..B) is the first index of
     the maximum logit.
   * verify: greedy exact match; k = longest prefix with d_{i+1} == a_i, bonus a_k,
-    n = k + 1 rows committed [dspark, Short-conv rollback: "n = accepted + 1", attention
-    trim(block_size - n)].
+    n = k + 1 rows committed and the attention caches rewound by block - n [dspark,
+    Implementation Review Summary, Short-conv rollback].
   * ring slack S = max(clamp(8 B, 32, 128), B) and trim = offset rewind with no restore
     [muse, What changed; Pre-merge review round, second finding].
   * READING (precision): activations are real numbers (f64 here). bf16 shapes round to
@@ -110,11 +110,80 @@ def rope_neox(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def rope_traditional(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary embedding, adjacent pairing (2i, 2i + 1), at absolute positions.
+
+    The DSpark checkpoint's pairing: its config turns the rotate-half form off, and every
+    rotary call site of the backbone then pairs neighbouring elements [dspark, opening
+    paragraph; Implementation Review Summary, Verified against the issue]. Pair i at
+    position p turns by p * theta^(-2i/hd), the angle of pair i of the rotate-half form.
+    x: [n, heads, hd]; pos: [n].
+    """
+    hd = x.shape[-1]
+    inv = theta ** (-np.arange(0, hd, 2, dtype=F64) / hd)  # pair i: theta^(-2i/hd)
+    ang = np.asarray(pos, dtype=F64)[:, None] * inv[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty(x.shape, dtype=F64)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xo * c + xe * s
+    return out
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float, style: str) -> np.ndarray:
+    """RoPE in the named pairing: "neox" (rotate-half) or "traditional" (adjacent)."""
+    if style == "neox":
+        return rope_neox(x, pos, theta)
+    if style == "traditional":
+        return rope_traditional(x, pos, theta)
+    raise ValueError(f"unknown rope style {style!r}")
+
+
+def markov_transition(w1: np.ndarray, w2: np.ndarray, prev: int) -> np.ndarray:
+    """Transition logits of the low-rank token-transition head after token `prev`.
+
+    markov_w1 [vocab, rank] is gathered at the previous token and markov_w2 [vocab, rank]
+    maps the rank-r row to a logit per vocabulary entry [dspark, opening paragraph: a
+    rank-256 Markov token-transition head; Security fixes: markov_w1 is indexed by a token
+    id once per chain step, rank lies along the last axis of both factors, the transition
+    logits span the vocabulary].
+    """
+    return np.asarray(w2, dtype=F64) @ np.asarray(w1[int(prev)], dtype=F64)
+
+
+def markov_chain(backbone_logits: np.ndarray, w1, w2, anchor: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """DSpark proposals d_1..d_gamma from the gamma backbone logit rows.
+
+    The chain starts from the anchor and each step's argmax is the token the next step
+    gathers [dspark, Implementation Review Summary, Verified against the issue]: step i
+    scores row i of the backbone logits plus the transition logits of token t_i (t_0 =
+    anchor, t_{i+1} = d_{i+1}) and proposes the first index of the maximum. READING: the
+    pages do not spell out how the two logit vectors combine; they are added (both span
+    the vocabulary, and the pages check one against the other's size), unscaled.
+    Returns (tokens [gamma], margins [gamma], winning scores [gamma]).
+    """
+    L = np.asarray(backbone_logits, dtype=F64)
+    prev = int(anchor)
+    toks, margins, tops = [], [], []
+    for i in range(L.shape[0]):
+        score = L[i] + markov_transition(w1, w2, prev)
+        idx, margin = argmax_with_margin(score[None, :])
+        prev = int(idx[0])
+        toks.append(prev)
+        margins.append(float(margin[0]))
+        tops.append(float(score[prev]))
+    return np.array(toks, dtype=np.int64), np.array(margins), np.array(tops)
+
+
+DSPARK_MAX_VERIFY_WIDTH = 32  # [dspark, Security fixes, the HIGH finding: verify width clamp]
+
+
 def speculative_slack(block: int) -> int:
     """Rows of ring slack past the window: clamp(8 B, 32, 128), floored at B.
 
-    [muse, What changed: "clamp(block * 8, 32, 128) rows of speculative buffer floored at
-    the block size"; Pre-merge review round, second finding: the floor].
+    [muse, What changed: eight rows per block, clamped to 32..128, never fewer than the
+    block; Pre-merge review round, second finding: the floor].
     """
     return max(min(max(8 * block, 32), 128), block)
 
@@ -123,8 +192,8 @@ def dequant_q4(packed: np.ndarray, scales: np.ndarray, biases: np.ndarray, group
     """4-bit affine dequantization w = s * q + b, exact in f64.
 
     packed: uint32 [out, in/8], eight codes per word along the input dim, lowest nibble
-    first, so the packed width is in * 4 / 32 [dspark, Security fixes: "The packed width
-    is rank * bits / 32"]. scales/biases: [out, in/group].
+    first, so the packed width is in * 4 / 32 [dspark, Security fixes: a packed factor's
+    width is its unpacked width times the bit depth over 32]. scales/biases: [out, in/group].
     """
     out, words = packed.shape
     codes = np.empty((out, words * 8), dtype=F64)
@@ -175,6 +244,7 @@ class DraftResult:
     hidden: np.ndarray  # [B+1, H] f64: residual stream after the last layer
     margins: np.ndarray  # [B] f64: top-1 minus top-2 logit of rows 1..B
     logits_top: np.ndarray  # [B] f64: the winning logit
+    logits: Optional[np.ndarray] = None  # DSpark: the backbone logits [gamma, V] the chain scores
 
 
 class OracleDrafter:
@@ -205,6 +275,15 @@ class OracleDrafter:
         self.V = np.zeros((L, nkv, self.C, hd), dtype=F64)
         self._cache: Dict[str, np.ndarray] = {}
         self._cache_f64 = cache_f64
+        self.variant = getattr(shape, "variant", "dflash")
+        self.rope_style = getattr(shape, "rope_style", "neox")
+        if self.variant == "dspark":
+            if getattr(shape, "markov_rank", 0) < 1:
+                raise OracleError("a DSpark drafter needs its Markov head")
+            if max_block + 1 > DSPARK_MAX_VERIFY_WIDTH:
+                raise OracleError(f"verify width {max_block + 1} above {DSPARK_MAX_VERIFY_WIDTH}")
+        elif self.variant != "dflash":
+            raise OracleError(f"unknown drafter variant {self.variant!r}")
 
     # -- weights -------------------------------------------------------------------------
     def _lin(self, name: str, rows: Optional[slice] = None) -> np.ndarray:
@@ -241,7 +320,7 @@ class OracleDrafter:
         k = (c @ self._lin(f"layers.{layer}.k").T).reshape(n, sh.kv_heads, sh.head_dim)
         v = (c @ self._lin(f"layers.{layer}.v").T).reshape(n, sh.kv_heads, sh.head_dim)
         k = rms_norm(k, self._gain(f"layers.{layer}.k_norm"), sh.rms_eps)
-        k = rope_neox(k, pos, sh.rope_theta)
+        k = rope(k, pos, sh.rope_theta, self.rope_style)
         return self._act(k), self._act(v)
 
     def lm_head_logits(self, rows: np.ndarray, chunk: int = 16384) -> np.ndarray:
@@ -344,8 +423,31 @@ class OracleDrafter:
             out[:, h] = (p / p.sum(axis=1, keepdims=True)) @ vals
         return out
 
-    def draft(self, anchor: int, block: int) -> DraftResult:
-        """One block forward: rows [anchor, mask x B] -> drafted tokens d_1..d_B."""
+    def _backbone(self, ids, qpos: np.ndarray) -> np.ndarray:
+        """Rows `ids` at absolute positions qpos through every layer over the ring's
+        committed context and their own keys: the residual stream after the last layer."""
+        sh = self.sh
+        R = len(ids)
+        x = self.embed(ids)
+        nq, nkv, hd = sh.q_heads, sh.kv_heads, sh.head_dim
+        for l in range(sh.layers):
+            p = f"layers.{l}."
+            h = rms_norm(x, self._gain(p + "in_norm"), sh.rms_eps)
+            q = (h @ self._lin(p + "q").T).reshape(R, nq, hd)
+            kb = (h @ self._lin(p + "k").T).reshape(R, nkv, hd)
+            vb = (h @ self._lin(p + "v").T).reshape(R, nkv, hd)
+            q = rope(rms_norm(q, self._gain(p + "q_norm"), sh.rms_eps), qpos, sh.rope_theta, self.rope_style)
+            kb = self._act(rope(rms_norm(kb, self._gain(p + "k_norm"), sh.rms_eps), qpos, sh.rope_theta,
+                                self.rope_style))
+            vb = self._act(vb)
+            o = self._attention(l, q, kb, vb, qpos).reshape(R, nq * hd)
+            x = x + o @ self._lin(p + "o").T
+            h2 = rms_norm(x, self._gain(p + "post_norm"), sh.rms_eps)
+            a = silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)
+            x = x + a @ self._lin(p + "down").T
+        return x
+
+    def _check_draft(self, anchor: int, block: int) -> None:
         sh = self.sh
         if not (1 <= block <= self.max_block):
             raise OracleError("block out of range")
@@ -355,29 +457,42 @@ class OracleDrafter:
             raise OracleError("empty context")
         if self.span != 0:
             raise OracleError("uncommitted rows pending: trim first")
-        R = block + 1
-        qpos = self.e + np.arange(R, dtype=np.int64)
-        x = self.embed([anchor] + [sh.mask_id] * block)
-        nq, nkv, hd = sh.q_heads, sh.kv_heads, sh.head_dim
-        for l in range(sh.layers):
-            p = f"layers.{l}."
-            h = rms_norm(x, self._gain(p + "in_norm"), sh.rms_eps)
-            q = (h @ self._lin(p + "q").T).reshape(R, nq, hd)
-            kb = (h @ self._lin(p + "k").T).reshape(R, nkv, hd)
-            vb = (h @ self._lin(p + "v").T).reshape(R, nkv, hd)
-            q = rope_neox(rms_norm(q, self._gain(p + "q_norm"), sh.rms_eps), qpos, sh.rope_theta)
-            kb = self._act(rope_neox(rms_norm(kb, self._gain(p + "k_norm"), sh.rms_eps), qpos, sh.rope_theta))
-            vb = self._act(vb)
-            o = self._attention(l, q, kb, vb, qpos).reshape(R, nq * hd)
-            x = x + o @ self._lin(p + "o").T
-            h2 = rms_norm(x, self._gain(p + "post_norm"), sh.rms_eps)
-            a = silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)
-            x = x + a @ self._lin(p + "down").T
+
+    def draft(self, anchor: int, block: int) -> DraftResult:
+        """One block forward: rows [anchor, mask x B] -> drafted tokens d_1..d_B (DFlash),
+        or the DSpark form (draft_dspark) for a DSpark shape."""
+        if self.variant == "dspark":
+            return self.draft_dspark(anchor, block)
+        sh = self.sh
+        self._check_draft(anchor, block)
+        qpos = self.e + np.arange(block + 1, dtype=np.int64)
+        x = self._backbone([anchor] + [sh.mask_id] * block, qpos)
         z = rms_norm(x[1:], self._gain("final_norm"), sh.rms_eps)
         logits = self.lm_head_logits(z)
         idx, margin = argmax_with_margin(logits)
         return DraftResult(tokens=idx.astype(np.int64), hidden=x, margins=margin,
                            logits_top=logits[np.arange(block), idx])
+
+    def draft_dspark(self, anchor: int, gamma: int) -> DraftResult:
+        """DSpark block: gamma rows [anchor, mask x (gamma - 1)] at positions e..e+gamma-1,
+        every row's logits consumed, position 0 included, then the Markov chain
+        [dspark, Implementation Review Summary, Verified against the issue].
+
+        The DSpark backbone attends without a mask (same section: context K/V in the
+        cache, the proposal K/V after them, no mask). READING: with the window rule
+        |q - p| <= W that is exact while every context row lies within W of every query,
+        e + gamma - 1 <= W; longer contexts are refused rather than cut.
+        """
+        sh = self.sh
+        self._check_draft(anchor, gamma)
+        if self.e + gamma - 1 > self.W:
+            raise OracleError("context past the window: the unmasked DSpark attention would be cut")
+        qpos = self.e + np.arange(gamma, dtype=np.int64)
+        x = self._backbone([anchor] + [sh.mask_id] * (gamma - 1), qpos)
+        z = rms_norm(x, self._gain("final_norm"), sh.rms_eps)
+        logits = self.lm_head_logits(z)
+        toks, margins, tops = markov_chain(logits, self.w["markov_w1"], self.w["markov_w2"], anchor)
+        return DraftResult(tokens=toks, hidden=x, margins=margins, logits_top=tops, logits=logits)
 
     def lm_head_argmax(self, rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
         """argmax over the vocabulary of rows (given in the storage dtype) through the shared

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 from block_drafting_dflash_amd import synth
+from tests import test_dspark_oracle as dpins
 from tests import test_oracle_pins as pins
 from tests import test_target_oracle as tpins
 
@@ -59,17 +60,17 @@ MUTANTS = [
      "a = silu(h2 @ self._lin(p + \"gate\").T) * (h2 @ self._lin(p + \"up\").T)",
      "a = silu(h2 @ self._lin(p + \"up\").T) * (h2 @ self._lin(p + \"gate\").T)"),
     ("trim ignores the rewind", "self.e += self.span - m", "self.e += self.span"),
-    ("block positions one late", "qpos = self.e + np.arange(R, dtype=np.int64)",
-     "qpos = self.e + 1 + np.arange(R, dtype=np.int64)"),
+    ("block positions one late", "qpos = self.e + np.arange(block + 1, dtype=np.int64)",
+     "qpos = self.e + 1 + np.arange(block + 1, dtype=np.int64)"),
     ("cached K/V not rounded to the cache dtype", "return self._act(k), self._act(v)", "return k, v"),
-    ("anchor embedded as a mask row", "x = self.embed([anchor] + [sh.mask_id] * block)",
-     "x = self.embed([sh.mask_id] * (block + 1))"),
+    ("anchor embedded as a mask row", "x = self._backbone([anchor] + [sh.mask_id] * block, qpos)",
+     "x = self._backbone([sh.mask_id] * (block + 1), qpos)"),
     ("committing append keeps one row too few", "keep_from = end - self.W if commit else end - self.C",
      "keep_from = end - self.W + 1 if commit else end - self.C"),
     ("context includes the position at e", "(self.slot_pos >= 0) & (self.slot_pos <= self.e - 1)",
      "(self.slot_pos >= 0) & (self.slot_pos <= self.e)"),
-    ("q_norm gain dropped", "q = rope_neox(rms_norm(q, self._gain(p + \"q_norm\"), sh.rms_eps), qpos, sh.rope_theta)",
-     "q = rope_neox(rms_norm(q, 1.0, sh.rms_eps), qpos, sh.rope_theta)"),
+    ("q_norm gain dropped", "q = rope(rms_norm(q, self._gain(p + \"q_norm\"), sh.rms_eps), qpos,",
+     "q = rope(rms_norm(q, 1.0, sh.rms_eps), qpos,"),
     ("k_norm on context rows dropped", "k = rms_norm(k, self._gain(f\"layers.{layer}.k_norm\"), sh.rms_eps)",
      "k = k"),
     ("pending append placed at e", "start = self.e + self.span", "start = self.e"),
@@ -101,6 +102,37 @@ TARGET_MUTANTS = [
      'x = x + (silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)) @ self._lin(p + "down").T',
      'x = (silu(h2 @ self._lin(p + "gate").T) * (h2 @ self._lin(p + "up").T)) @ self._lin(p + "down").T'),
     ("target verify rows skip the final norm", 'z = rms_norm(x, self._lin("final_norm"), sh.rms_eps)', "z = x"),
+]
+
+# planted mistakes in the DSpark form, against the DSpark pins
+DSPARK_MUTANTS = [
+    ("chain seeded with the mask token",
+     'toks, margins, tops = markov_chain(logits, self.w["markov_w1"], self.w["markov_w2"], anchor)',
+     'toks, margins, tops = markov_chain(logits, self.w["markov_w1"], self.w["markov_w2"], sh.mask_id)'),
+    ("chain gathers the anchor at every step", "        prev = int(idx[0])\n        toks.append(prev)",
+     "        toks.append(int(idx[0]))"),
+    ("transition factors swapped",
+     "return np.asarray(w2, dtype=F64) @ np.asarray(w1[int(prev)], dtype=F64)",
+     "return np.asarray(w1, dtype=F64) @ np.asarray(w2[int(prev)], dtype=F64)"),
+    ("transition logits subtracted", "score = L[i] + markov_transition(w1, w2, prev)",
+     "score = L[i] - markov_transition(w1, w2, prev)"),
+    ("DSpark logits of the rows after each position",
+     'z = rms_norm(x, self._gain("final_norm"), sh.rms_eps)\n        logits = self.lm_head_logits(z)\n        toks',
+     'z = rms_norm(np.concatenate([x[1:], x[-1:]]), self._gain("final_norm"), sh.rms_eps)\n'
+     '        logits = self.lm_head_logits(z)\n        toks'),
+    ("DSpark block one mask row longer",
+     "x = self._backbone([anchor] + [sh.mask_id] * (gamma - 1), qpos)",
+     "x = self._backbone([anchor] + [sh.mask_id] * gamma, self.e + np.arange(gamma + 1))"),
+    ("adjacent-pair RoPE rotates the wrong way", "out[..., 0::2] = xe * c - xo * s", "out[..., 0::2] = xe * c + xo * s"),
+    ("adjacent-pair RoPE frequency per element",
+     "inv = theta ** (-np.arange(0, hd, 2, dtype=F64) / hd)", "inv = theta ** (-np.arange(0, hd // 2, dtype=F64) / hd)"),
+    ("DSpark layers keep the rotate-half pairing", 'self.rope_style = getattr(shape, "rope_style", "neox")',
+     'self.rope_style = "neox"'),
+    ("context K/V keep the rotate-half pairing", "k = rope(k, pos, sh.rope_theta, self.rope_style)",
+     "k = rope_neox(k, pos, sh.rope_theta)"),
+    ("DSpark context check one row early", "if self.e + gamma - 1 > self.W:", "if self.e + gamma > self.W:"),
+    ("verify width clamp one row late", "if max_block + 1 > DSPARK_MAX_VERIFY_WIDTH:",
+     "if max_block > DSPARK_MAX_VERIFY_WIDTH:"),
 ]
 
 
@@ -164,7 +196,7 @@ def test_planted_mistake_fails_a_pin(pin_calls, monkeypatch, name, old, new):
         try:
             with np.errstate(all="ignore"):
                 call()
-        except Exception:
+        except (Exception, pytest.fail.Exception):  # an assertion, an error, or pytest.raises unmet
             return  # caught
     pytest.fail(f"no pin fails with the planted mistake: {name}")
 
@@ -198,7 +230,40 @@ def test_planted_target_mistake_fails_a_pin(target_pin_calls, monkeypatch, name,
         try:
             with np.errstate(all="ignore"):
                 call()
-        except Exception:
+        except (Exception, pytest.fail.Exception):  # an assertion, an error, or pytest.raises unmet
             return  # caught
     pytest.fail(f"no pin fails with the planted mistake: {name}")
 
+
+
+@pytest.fixture(scope="module")
+def dspark_pin_calls():
+    w = dpins.dspark_weights()
+    D = dpins
+    return [
+        D.test_traditional_rope_hand_values, D.test_traditional_rope_matches_torch_complex_view,
+        D.test_traditional_rope_is_rotate_half_on_deinterleaved_elements, D.test_markov_chain_hand_values,
+        D.test_markov_chain_matches_brute_force_over_tiny_vocab,
+        lambda: D.test_dspark_limits(w),
+        lambda: D.test_dspark_backbone_is_the_dflash_backbone_on_the_same_rows(w),
+        lambda: D.test_dspark_chain_feeds_its_own_tokens(w),
+        lambda: D.test_dspark_draft_matches_torch_formulation_over_rounds(w, "traditional"),
+    ]
+
+
+def test_real_oracle_passes_every_dspark_pin_call(dspark_pin_calls):
+    for call in dspark_pin_calls:
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", DSPARK_MUTANTS, ids=[m[0] for m in DSPARK_MUTANTS])
+def test_planted_dspark_mistake_fails_a_pin(dspark_pin_calls, monkeypatch, name, old, new):
+    mod = load_mutant(old, new)
+    monkeypatch.setattr(dpins, "O", mod)
+    for call in dspark_pin_calls:
+        try:
+            with np.errstate(all="ignore"):
+                call()
+        except (Exception, pytest.fail.Exception):  # an assertion, an error, or pytest.raises unmet
+            return  # caught
+    pytest.fail(f"no pin fails with the planted mistake: {name}")
