@@ -33,7 +33,11 @@ class dflash_config(ctypes.Structure):
         "hidden", "layers", "q_heads", "kv_heads", "head_dim", "intermediate", "vocab",
         "target_streams", "target_width", "window", "max_block", "mask_token_id", "ring_phase")] + [
         ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-        ("weight_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32)]
+        ("weight_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+        ("variant", ctypes.c_int32), ("rope_traditional", ctypes.c_int32), ("markov_rank", ctypes.c_int32)]
+
+
+VARIANT = {"dflash": 0, "dspark": 1}
 
 
 class dflash_linear(ctypes.Structure):
@@ -57,7 +61,8 @@ class dflash_target_config(ctypes.Structure):
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("lm_head", dflash_linear), ("fc", dflash_linear),
                 ("enc_norm", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(dflash_layer))]
+                ("layers", ctypes.POINTER(dflash_layer)),
+                ("markov_w1", ctypes.c_void_p), ("markov_w2", ctypes.c_void_p)]
 
 
 class dflash_target_weights(ctypes.Structure):
@@ -151,7 +156,10 @@ def make_config(shape, max_block: int, phase: int = 0) -> dflash_config:
         head_dim=shape.head_dim, intermediate=shape.intermediate, vocab=shape.vocab,
         target_streams=shape.target_streams, target_width=shape.target_width, window=shape.window,
         max_block=max_block, mask_token_id=shape.mask_id, ring_phase=phase, rms_eps=shape.rms_eps,
-        rope_theta=shape.rope_theta, weight_dtype=_DTYPE[shape.weight_dtype], act_dtype=_DTYPE[shape.act_dtype])
+        rope_theta=shape.rope_theta, weight_dtype=_DTYPE[shape.weight_dtype], act_dtype=_DTYPE[shape.act_dtype],
+        variant=VARIANT[getattr(shape, "variant", "dflash")],
+        rope_traditional=int(getattr(shape, "rope_style", "neox") == "traditional"),
+        markov_rank=getattr(shape, "markov_rank", 0))
 
 
 def act_torch_dtype(shape) -> torch.dtype:
@@ -205,7 +213,9 @@ class Drafter:
         self._layers = layers
         self.weights = dflash_weights(_ptr(dev_weights["embed"]), lin("lm_head"), lin("fc"),
                                       _ptr(dev_weights["enc_norm"]), _ptr(dev_weights["final_norm"]),
-                                      ctypes.cast(layers, ctypes.POINTER(dflash_layer)))
+                                      ctypes.cast(layers, ctypes.POINTER(dflash_layer)),
+                                      _ptr(dev_weights.get("markov_w1")), _ptr(dev_weights.get("markov_w2")))
+        self.dspark = getattr(shape, "variant", "dflash") == "dspark"
         ring_b, ws_b, pk_b = query_sizes(self.cfg)
         self.ring = torch.empty(max(ring_b, 256), dtype=torch.uint8, device=self.device)
         self.workspace = torch.empty(max(ws_b, 256), dtype=torch.uint8, device=self.device)
@@ -241,7 +251,8 @@ class Drafter:
         self._dev(tokens, torch.int32)
         if hidden is not None:
             self._dev(hidden, torch.float32)
-            if hidden.numel() < (block + 1) * self.shape.hidden:
+            rows = block if self.dspark else block + 1  # DSpark blocks have gamma rows
+            if hidden.numel() < rows * self.shape.hidden:
                 raise ValueError("hidden output too small")
         if tokens.numel() < block:
             raise ValueError("token output too small")

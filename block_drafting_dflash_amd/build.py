@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
-SOURCES = ["gemm_bf16.hip", "gemm_q4.hip", "gemm_f32.hip", "gemm.hip", "attention.hip", "misc.hip", "noalloc.hip",
+SOURCES = ["gemm_bf16.hip", "gemm_q4.hip", "gemm_f32.hip", "gemm.hip", "attention.hip", "misc.hip", "markov.hip",
+           "noalloc.hip",
            "dflash.cpp", "controller.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -750,7 +750,8 @@ __global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part,
 
 // ---- live window read-back (parity checks) -----------------------------------------------
 template <bool BF>
-__global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t lo, int n, void* kout, void* vout) {
+__global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t lo, int n, void* kout, void* vout,
+                                  int deint) {
   const int hd = a.hd;
   const size_t total = (size_t)a.nkv * n * hd;
   const size_t plane = (size_t)a.cap * hd;
@@ -759,7 +760,9 @@ __global__ void cache_read_kernel(AttnShape a, const void* ring_layer, int64_t l
     const size_t t = i / hd;
     const int j = (int)(t % n), h = (int)(t / n);
     const size_t slot = (size_t)ring_slot(a, lo + j);
-    const size_t ko = (size_t)h * plane + slot * hd + d;                       // K [h][slot][d]
+    // K [h][slot][d], element d of the original order at d/2 or hd/2 + d/2 when deinterleaved
+    const int dk = deint ? (d & 1 ? hd / 2 + (d >> 1) : d >> 1) : d;
+    const size_t ko = (size_t)h * plane + slot * hd + dk;
     const size_t vo = (size_t)(a.nkv + h) * plane + (size_t)d * a.cap + slot;  // V^T [h][d][slot]
     if constexpr (BF) {
       ((uint16_t*)kout)[i] = ((const uint16_t*)ring_layer)[ko];
@@ -858,12 +861,14 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
 }
 
 hipError_t launch_cache_read(int bf, const AttnShape& a, const void* ring_layer, int64_t lo, int n, void* kout,
-                             void* vout, hipStream_t s) {
+                             void* vout, hipStream_t s, int deint) {
   if (n <= 0) return hipSuccess;
   const size_t total = (size_t)a.nkv * n * a.hd;
   const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-  if (bf) hipLaunchKernelGGL(cache_read_kernel<true>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout);
-  else hipLaunchKernelGGL(cache_read_kernel<false>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout);
+  if (bf)
+    hipLaunchKernelGGL(cache_read_kernel<true>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout, deint);
+  else
+    hipLaunchKernelGGL(cache_read_kernel<false>, dim3(grid), dim3(256), 0, s, a, ring_layer, lo, n, kout, vout, deint);
   return hipGetLastError();
 }
 

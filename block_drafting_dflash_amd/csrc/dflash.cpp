@@ -32,7 +32,9 @@ struct Layer {
 };
 
 struct Layout {  // byte offsets into the workspace
-  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, rope, app_fc, app_kv, total;
+  size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, rope, app_fc, app_kv;
+  size_t logits, mk_part, mk_ticket;  // DSpark: backbone logits of a block, chain keys, chain counter
+  size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -51,6 +53,8 @@ struct Cfg {
   int R;        // max rows of a block forward = max_block + 1
   int64_t S, C;  // slack and capacity of the window (C = W + S)
   int64_t Cs;    // slots stored: C rounded up to a multiple of 8, at least W + R and 64
+  bool dspark;   // the DSpark form (gamma rows, every row's logits, the Markov chain)
+  bool trad;     // adjacent-pair RoPE, run as rotate-half over deinterleaved q/k elements
   AttnShape a;
 };
 
@@ -61,6 +65,8 @@ struct dflash_ctx {
   Layout lay;
   Lin embed_lin, lm_head, fc;
   const void *embed, *enc_norm, *final_norm;
+  const void *markov_w1 = nullptr, *markov_w2 = nullptr;
+  int mk_groups = 0;  // work-groups of a Markov chain step
   std::vector<Layer> layers;
   unsigned char* ring;
   unsigned char* ws;
@@ -170,6 +176,20 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   if (c->vocab % 16) return cfg_fail(err, DFLASH_E_SHAPE, "vocab must be a multiple of 16");
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 0.f) || !std::isfinite(c->rms_eps) || !std::isfinite(c->rope_theta))
     return cfg_fail(err, DFLASH_E_ARG, "rms_eps and rope_theta must be positive and finite");
+  if (c->rope_traditional != 0 && c->rope_traditional != 1)
+    return cfg_fail(err, DFLASH_E_ARG, "rope_traditional must be 0 or 1");
+  if (c->variant == DFLASH_VARIANT_DSPARK) {
+    // the verify width (block + 1 rows) is clamped at 32 (lablup/mlxcel #1751, Security fixes)
+    if (c->max_block + 1 > 32)
+      return cfg_fail(err, DFLASH_E_RANGE, "a DSpark verify width of %d rows is above 32", c->max_block + 1);
+    if (!markov_rank_supported(bf, c->markov_rank))
+      return cfg_fail(err, DFLASH_E_SHAPE, "markov_rank %d is not one of 64, 128, 256%s", c->markov_rank,
+                      bf ? ", 512" : "");
+  } else if (c->variant != DFLASH_VARIANT_DFLASH) {
+    return cfg_fail(err, DFLASH_E_ARG, "unknown variant %d", c->variant);
+  } else if (c->markov_rank != 0) {
+    return cfg_fail(err, DFLASH_E_ARG, "markov_rank is for DSpark contexts only");
+  }
   // every extent and element count handed to a kernel fits an int32
   const int64_t qd = (int64_t)c->q_heads * c->head_dim, kvd = (int64_t)c->kv_heads * c->head_dim;
   const int64_t fin = (int64_t)c->target_streams * c->target_width;
@@ -203,6 +223,8 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   g.bf = bf;
   g.act_elt = bf ? 2 : 4;
   g.R = c->max_block + 1;
+  g.dspark = c->variant == DFLASH_VARIANT_DSPARK;
+  g.trad = c->rope_traditional != 0;
   g.S = slack_rows(c->max_block);
   g.C = c->window + g.S;
   // storage: the block's own keys (positions e..e+R-1) get slots of their own past the
@@ -254,6 +276,11 @@ Layout make_layout(const Cfg& g) {
   L.rope = take(sizeof(float2) * RQ * (c.head_dim / 2));  // rotary table of a draft's positions
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
+  if (g.dspark) {
+    L.logits = take(4 * (size_t)c.max_block * c.vocab);
+    L.mk_part = take(sizeof(unsigned long long) * MK_MAX_GROUPS);
+    L.mk_ticket = take(sizeof(unsigned int));
+  }
   L.total = o;
   return L;
 }
@@ -263,10 +290,13 @@ size_t ring_bytes_of(const Cfg& g) {
 }
 
 // Fragment-major copies of every linear live in the caller's packed buffer, in this order:
-// fc, lm_head, then per layer q, k, v, o, gate, up, down.
+// fc, lm_head, then per layer q, k, v, o, gate, up, down; with adjacent-pair RoPE the
+// deinterleaved copies of every layer's q_norm and k_norm follow.
 struct PackedLayout {
   size_t total = 0;
   std::vector<size_t> off;  // byte offset of each linear, in the order above
+  size_t gains = 0;         // offset of the deinterleaved gains: per layer q_norm, k_norm
+  size_t gain_stride = 0;   // bytes per gain copy
 };
 
 // f32/bf16: the fragment-major matrix; q4: code blocks (K/2 bytes per row) followed by
@@ -296,6 +326,11 @@ PackedLayout make_packed_layout(const Cfg& g) {
     add(I, H);
     add(I, H);
     add(H, I);
+  }
+  if (g.trad) {
+    P.gains = P.total;
+    P.gain_stride = align256((size_t)c.head_dim * (g.wt == WT_F32 ? 4 : 2));
+    P.total += P.gain_stride * 2 * c.layers;
   }
   return P;
 }
@@ -605,6 +640,11 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
         !lin_ok(L.down) || !gain_ok(L.in_norm) || !gain_ok(L.post_norm) || !gain_ok(L.q_norm) || !gain_ok(L.k_norm))
       return cfg_fail(g_create_err, DFLASH_E_ARG, "layer %d has a NULL or misaligned weight", l);
   }
+  // the Markov factors are read 16 bytes per lane in place
+  if (g.dspark ? !gain_ok(wts->markov_w1) || !gain_ok(wts->markov_w2) : wts->markov_w1 || wts->markov_w2)
+    return cfg_fail(g_create_err, DFLASH_E_ARG,
+                    g.dspark ? "the Markov factors are NULL or not 16-byte aligned"
+                             : "Markov factors given to a DFlash context");
   dflash_ctx* ctx = new (std::nothrow) dflash_ctx();
   if (!ctx) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
   ctx->cfg = g;
@@ -616,6 +656,8 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   ctx->embed = wts->embed;
   ctx->enc_norm = wts->enc_norm;
   ctx->final_norm = wts->final_norm;
+  ctx->markov_w1 = wts->markov_w1;
+  ctx->markov_w2 = wts->markov_w2;
   ctx->layers.resize(g.c.layers);
   std::vector<const void*> knorms(g.c.layers);
   for (int l = 0; l < g.c.layers; ++l) {
@@ -633,6 +675,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
         cus > 0)
       ctx->cus = cus;
   }
+  if (g.dspark) ctx->mk_groups = markov_step_groups(g.c.vocab, g.c.markov_rank, g.bf, ctx->cus);
   // the device address of this device's fixed argmax key array, for the allocation-free argmax
   if (e == hipSuccess) {
     void* keys = nullptr;
@@ -647,29 +690,41 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
     const int F = c.target_streams * c.target_width, I = c.intermediate;
     unsigned char* base = (unsigned char*)packed;
     size_t idx = 0;
-    auto pack = [&](Lin& l, int N, int K) {
+    // adjacent-pair RoPE: q and k rows (and their norm gains) in deinterleaved order per head
+    auto pack = [&](Lin& l, int N, int K, int perm_hd = 0) {
       unsigned char* dst = base + pk.off[idx++];
       if (g.wt == WT_Q4) {
         unsigned char* sdst = dst + q4_code_bytes(N, K);
-        if (e == hipSuccess) e = launch_pack_q4(l.w, l.s, l.b, N, K, dst, sdst, st);
+        if (e == hipSuccess) e = launch_pack_q4(l.w, l.s, l.b, N, K, dst, sdst, st, perm_hd);
         l.s = sdst;
         l.b = nullptr;
       } else if (e == hipSuccess) {
-        e = launch_pack(g.wt, l.w, N, K, dst, st);
+        e = launch_pack(g.wt, l.w, N, K, dst, st, perm_hd);
       }
       l.w = dst;
     };
+    const int perm = g.trad ? c.head_dim : 0;
     pack(ctx->fc, H, F);
     pack(ctx->lm_head, c.vocab, H);
     for (int l = 0; l < c.layers; ++l) {
       Layer& L = ctx->layers[l];
-      pack(L.q, qd, H);
-      pack(L.k, kvd, H);
+      pack(L.q, qd, H, perm);
+      pack(L.k, kvd, H, perm);
       pack(L.v, kvd, H);
       pack(L.o, H, qd);
       pack(L.gate, I, H);
       pack(L.up, I, H);
       pack(L.down, H, I);
+      if (g.trad) {
+        unsigned char* qn = base + pk.gains + pk.gain_stride * 2 * l;
+        unsigned char* kn = qn + pk.gain_stride;
+        const int gelt = g.wt == WT_F32 ? 4 : 2;
+        if (e == hipSuccess) e = launch_deinterleave(L.q_norm, qn, c.head_dim, gelt, st);
+        if (e == hipSuccess) e = launch_deinterleave(L.k_norm, kn, c.head_dim, gelt, st);
+        L.q_norm = qn;
+        L.k_norm = kn;
+        knorms[l] = kn;
+      }
     }
   }
   if (e == hipSuccess)
@@ -678,6 +733,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   // every slot starts finite (zero): attention reads whole aligned runs of slots, including
   // keys outside a query's window that then get weight 0
   if (e == hipSuccess) e = hipMemsetAsync(ring, 0, ring_bytes_of(g), st);
+  if (e == hipSuccess && g.dspark) e = hipMemsetAsync(ctx->ws + lay.mk_ticket, 0, sizeof(unsigned int), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
   if (e != hipSuccess) {
     cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
@@ -763,8 +819,12 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   if (!d_tokens) return fail(ctx, DFLASH_E_ARG, "NULL token output");
   if (ctx->e <= 0) return fail(ctx, DFLASH_E_NO_CONTEXT, "draft with an empty context");
   if (ctx->pending) return fail(ctx, DFLASH_E_STATE, "%lld appended rows are not committed", (long long)ctx->pending);
+  // DSpark attends to every context row; the window rule agrees while it cuts nothing
+  if (g.dspark && ctx->e + block - 1 > c.window)
+    return fail(ctx, DFLASH_E_RANGE, "DSpark block at context %lld + %d rows reaches past the window %d",
+                (long long)ctx->e, block, c.window);
   hipStream_t st = (hipStream_t)stream;
-  const int R = block + 1;
+  const int R = g.dspark ? block : block + 1;  // DSpark: [anchor, mask x (gamma-1)]
   const int H = c.hidden;
   // committed rows whose K/V are deferred: projected with this draft's QKV launches (rows
   // R..R+nf-1) and written into the ring by its attention, or first on their own
@@ -828,15 +888,37 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
   }
-  // final RMSNorm of rows 1..B once, then the lm_head argmax over the operand rows
+  // final RMSNorm of the proposing rows once (DFlash: rows 1..B; DSpark: all gamma rows),
+  // then the lm_head over the operand rows
   void* zrows = ctx->ws + ctx->lay.zrows;
   void* zrows_lo = lo_plane(g, zrows, block, H);
-  s = dev(ctx, launch_rownorm(g.bf, x + H, ctx->final_norm, c.rms_eps, block, H, zrows, zrows_lo, st), "final norm");
+  s = dev(ctx, launch_rownorm(g.bf, g.dspark ? x : x + H, ctx->final_norm, c.rms_eps, block, H, zrows, zrows_lo, st),
+          "final norm");
   if (s != DFLASH_OK) return s;
-  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
+  if (!g.dspark) {
+    GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
+    lm.split = g.bf;
+    lm.xlo = zrows_lo;
+    return run_gemm(ctx, lm, block, st);
+  }
+  // DSpark: every row's f32 logits, then the Markov chain, one launch per step, each step
+  // gathering the token the previous one wrote (the anchor first)
+  float* logits = (float*)(ctx->ws + ctx->lay.logits);
+  GemmCall lm{EPI_STORE, XSRC_GLOBAL, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, logits, c.vocab, nullptr};
   lm.split = g.bf;
   lm.xlo = zrows_lo;
-  return run_gemm(ctx, lm, block, st);
+  if ((s = run_gemm(ctx, lm, block, st)) != DFLASH_OK) return s;
+  unsigned long long* mk_part = (unsigned long long*)(ctx->ws + ctx->lay.mk_part);
+  unsigned int* mk_ticket = (unsigned int*)(ctx->ws + ctx->lay.mk_ticket);
+  for (int i = 0; i < block; ++i) {
+    s = dev(ctx,
+            launch_markov_step(g.bf, c.markov_rank, ctx->markov_w1, ctx->markov_w2, c.vocab,
+                               logits + (size_t)i * c.vocab, i ? d_tokens + i - 1 : nullptr, anchor, mk_part,
+                               mk_ticket, d_tokens + i, ctx->mk_groups, st),
+            "markov step");
+    if (s != DFLASH_OK) return s;
+  }
+  return DFLASH_OK;
 }
 
 dflash_status dflash_lm_head_argmax(dflash_ctx* ctx, const void* rows, int32_t n, int32_t* d_idx, void* stream) {
@@ -894,7 +976,9 @@ dflash_status dflash_cache_read(dflash_ctx* ctx, int32_t layer, void* k_out, voi
   if (s != DFLASH_OK) return s;
   *n_out = n;
   const size_t ring_layer = (size_t)g.act_elt * 2 * g.c.kv_heads * (size_t)g.Cs * g.c.head_dim;
-  return dev(ctx, launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream),
+  return dev(ctx,
+             launch_cache_read(g.bf, g.a, ctx->ring + layer * ring_layer, lo, n, k_out, v_out, (hipStream_t)stream,
+                               g.trad ? 1 : 0),
              "cache read");
 }
 

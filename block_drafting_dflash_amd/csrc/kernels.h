@@ -178,12 +178,21 @@ struct AttnShape {
   int32_t causal = 0;
 };
 
-// Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip).
-hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s);
+// Row-major [N, K] linear -> fragment-major 1 KiB blocks (see misc.hip). perm_hd > 0 takes
+// the rows of each run of perm_hd (one attention head) in the order 0, 2, 4, .., 1, 3, 5, ..
+// (deinterleaved_row below).
+hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s, int perm_hd = 0);
 // 4-bit linear (codes uint32 [N, K/8], bf16 scales/biases [N, K/64]) -> fragment-major
-// code blocks (N*K/2 bytes) and scale blocks (N*K/16 bytes), see misc.hip.
+// code blocks (N*K/2 bytes) and scale blocks (N*K/16 bytes), see misc.hip; perm_hd as above.
 hipError_t launch_pack_q4(const void* codes, const void* scales, const void* biases, int N, int K, void* dst_codes,
-                          void* dst_scales, hipStream_t s);
+                          void* dst_scales, hipStream_t s, int perm_hd = 0);
+// Source element of stored element j of a head of hd elements held in deinterleaved order:
+// the evens first, then the odds. The rotate-half RoPE of that order pairs (2i, 2i + 1).
+__host__ __device__ constexpr int deinterleaved_row(int j, int hd) {
+  return j < hd / 2 ? 2 * j : 2 * (j - hd / 2) + 1;
+}
+// dst[j] = src[deinterleaved_row(j, hd)] for one vector of hd elements of elt bytes.
+hipError_t launch_deinterleave(const void* src, void* dst, int hd, int elt, hipStream_t s);
 // idx[r] = index of the largest key among part[r][0..groups) (lm_head argmax finish).
 hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, int R, int32_t* idx, hipStream_t s);
 // Embedding rows [anchor, t_1 .. t_{R-1}] as f32 residual rows x, where t_i = toks[i-1]
@@ -221,7 +230,21 @@ hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int
 // Streaming read of `bytes` (a multiple of 16, at least groups * 4096) by `groups` work-groups
 // of contiguous shares; sink [groups] receives an XOR of what each read (misc.hip).
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int groups, hipStream_t s);
+// Live window read-back; deint: the ring holds keys in deinterleaved order, restored here.
 hipError_t launch_cache_read(int act_bf16, const AttnShape& a, const void* ring_layer, int64_t lo, int n,
-                             void* kout, void* vout, hipStream_t s);
+                             void* kout, void* vout, hipStream_t s, int deint = 0);
+
+// ---- the DSpark Markov head (markov.hip) ---------------------------------------------------
+constexpr int MK_WG_PER_CU = 4;     // work-groups per compute unit of a chain step
+constexpr int MK_MAX_GROUPS = 4096;  // bound on a step's work-groups (its key array)
+bool markov_rank_supported(int act_bf16, int rank);
+// work-groups of one chain step on a device of `cus` compute units
+int markov_step_groups(int vocab, int rank, int act_bf16, int cus);
+// One chain step: out[0] = first argmax over v of logits[v] + w2[v] . w1[t], t = prev[0]
+// (anchor when prev is NULL); part holds `groups` keys and ticket one zeroed counter, which
+// the step leaves zeroed.
+hipError_t launch_markov_step(int act_bf16, int rank, const void* w1, const void* w2, int vocab, const float* logits,
+                              const int32_t* prev, int32_t anchor, unsigned long long* part, unsigned int* ticket,
+                              int32_t* out, int groups, hipStream_t s);
 
 }  // namespace dflash

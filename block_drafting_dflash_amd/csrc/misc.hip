@@ -250,25 +250,50 @@ namespace dflash {
 // offset, lg = 0..3) owns the 16 bytes W[16j + li][s*KSTEP + lg*EPL .. + EPL). Blocks of a
 // row tile are consecutive, so every 16-byte-per-lane wave load of the GEMM reads one
 // contiguous kilobyte and lands directly in the MFMA B-operand layout.
+// Row r of the packed matrix takes source row src_row(r): itself, or with perm_hd > 0 the
+// deinterleaved order inside each run of perm_hd rows.
+__device__ __forceinline__ int64_t src_row(int64_t r, int perm_hd) {
+  if (perm_hd <= 0) return r;
+  const int64_t h = r / perm_hd;
+  return h * perm_hd + deinterleaved_row((int)(r - h * perm_hd), perm_hd);
+}
+
 __global__ void pack_kernel(const unsigned char* __restrict__ src, int64_t nblocks, int kblocks, int K, int elt,
-                            int epl, u32x4_t* __restrict__ dst) {
+                            int epl, int perm_hd, u32x4_t* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte lane slot
   if (i >= nblocks * 64) return;
   const int64_t blk = i >> 6;
   const int lane = (int)(i & 63), li = lane & 15, lg = lane >> 4;
   const int64_t j = blk / kblocks, s = blk - j * kblocks;
   const int kstep = 4 * epl;
-  const size_t off = ((size_t)(16 * j + li) * K + (size_t)s * kstep + (size_t)lg * epl) * elt;
+  const size_t off = ((size_t)src_row(16 * j + li, perm_hd) * K + (size_t)s * kstep + (size_t)lg * epl) * elt;
   dst[i] = *(const u32x4_t*)(src + off);
 }
 
-hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s) {
+hipError_t launch_pack(int wt, const void* src, int N, int K, void* dst, hipStream_t s, int perm_hd) {
+  if (perm_hd < 0 || (perm_hd > 0 && (perm_hd % 2 || N % perm_hd))) return hipErrorInvalidValue;
   const int elt = wt == WT_F32 ? 4 : 2, epl = 16 / elt;
   const int kblocks = K / (4 * epl);
   const int64_t nblocks = (int64_t)(N / 16) * kblocks;
   const int64_t slots = nblocks * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, (const unsigned char*)src,
-                     nblocks, kblocks, K, elt, epl, (u32x4_t*)dst);
+                     nblocks, kblocks, K, elt, epl, perm_hd, (u32x4_t*)dst);
+  return hipGetLastError();
+}
+
+__global__ void deinterleave_kernel(const unsigned char* __restrict__ src, unsigned char* __restrict__ dst, int hd,
+                                    int elt) {
+  const int j = threadIdx.x;
+  if (j >= hd) return;
+  const int from = deinterleaved_row(j, hd);
+  if (elt == 4) ((float*)dst)[j] = ((const float*)src)[from];
+  else ((uint16_t*)dst)[j] = ((const uint16_t*)src)[from];
+}
+
+hipError_t launch_deinterleave(const void* src, void* dst, int hd, int elt, hipStream_t s) {
+  if (hd < 2 || hd > 1024 || hd % 2 || (elt != 2 && elt != 4)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(deinterleave_kernel, dim3(1), dim3(hd), 0, s, (const unsigned char*)src, (unsigned char*)dst, hd,
+                     elt);
   return hipGetLastError();
 }
 
@@ -292,14 +317,14 @@ __device__ __forceinline__ uint32_t q4_reorder(uint32_t w) {
 }
 
 __global__ void pack_q4_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                               const uint16_t* __restrict__ biases, int64_t nblocks, int kblocks, int K,
+                               const uint16_t* __restrict__ biases, int64_t nblocks, int kblocks, int K, int perm_hd,
                                u32x4_t* __restrict__ dst_codes, uint32_t* __restrict__ dst_scales) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte lane slot
   if (i >= nblocks * 64) return;
   const int64_t blk = i >> 6;
   const int lane = (int)(i & 63), li = lane & 15, lg = lane >> 4;
   const int64_t j = blk / kblocks, s4 = blk - j * kblocks;
-  const int64_t row = 16 * j + li;
+  const int64_t row = src_row(16 * j + li, perm_hd);
   const uint32_t* src = codes + row * (K / 8) + (128 * s4 + 8 * lg) / 8;
   u32x4_t v;
 #pragma unroll
@@ -315,13 +340,14 @@ __global__ void pack_q4_kernel(const uint32_t* __restrict__ codes, const uint16_
 }
 
 hipError_t launch_pack_q4(const void* codes, const void* scales, const void* biases, int N, int K, void* dst_codes,
-                          void* dst_scales, hipStream_t s) {
+                          void* dst_scales, hipStream_t s, int perm_hd) {
+  if (perm_hd < 0 || (perm_hd > 0 && (perm_hd % 2 || N % perm_hd))) return hipErrorInvalidValue;
   const int kblocks = K / 128;
   const int64_t nblocks = (int64_t)(N / 16) * kblocks;
   const int64_t slots = nblocks * 64;
   hipLaunchKernelGGL(pack_q4_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, (const uint32_t*)codes,
-                     (const uint16_t*)scales, (const uint16_t*)biases, nblocks, kblocks, K, (u32x4_t*)dst_codes,
-                     (uint32_t*)dst_scales);
+                     (const uint16_t*)scales, (const uint16_t*)biases, nblocks, kblocks, K, perm_hd,
+                     (u32x4_t*)dst_codes, (uint32_t*)dst_scales);
   return hipGetLastError();
 }
 

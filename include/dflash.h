@@ -85,6 +85,16 @@ typedef enum {
  *     the embedding table and the norm gains are bf16; otherwise they use weight_dtype.
  *   act_dtype: DFLASH_F32 with f32 weights, DFLASH_BF16 otherwise. It is the dtype of
  *     the residual slab, of every GEMM operand, of the ring and of lm_head input rows.
+ *   variant: DFLASH_VARIANT_DFLASH (0) or DFLASH_VARIANT_DSPARK, the DSpark form of the
+ *     drafter (lablup/mlxcel #1751, opening paragraph; Implementation Review Summary,
+ *     Verified against the issue): a block of gamma rows [anchor, mask x (gamma-1)] whose
+ *     every row proposes a token through a low-rank Markov token-transition head chained
+ *     from the anchor (dflash_draft_block). A DSpark context takes max_block + 1 <= 32
+ *     (the verify width clamp of the same page, Security fixes) and markov_rank in {64,
+ *     128, 256} (also 512 with bf16 activations); a DFlash one takes markov_rank 0.
+ *   rope_traditional: 0 pairs each head's elements (i, i + head_dim/2) in RoPE (the
+ *     rotate-half form); 1 pairs neighbours (2i, 2i + 1), the DSpark checkpoints' form
+ *     (same page, opening paragraph). Pair i turns by p * theta^(-2i/head_dim) either way.
  */
 typedef struct {
   int32_t hidden, layers, q_heads, kv_heads, head_dim, intermediate, vocab;
@@ -93,7 +103,12 @@ typedef struct {
   float rms_eps, rope_theta;
   int32_t weight_dtype; /* dflash_dtype */
   int32_t act_dtype;    /* dflash_dtype */
+  int32_t variant;      /* dflash_variant */
+  int32_t rope_traditional;
+  int32_t markov_rank;
 } dflash_config;
+
+typedef enum { DFLASH_VARIANT_DFLASH = 0, DFLASH_VARIANT_DSPARK = 1 } dflash_variant;
 
 /* A linear layer [out, in]. For DFLASH_Q4G64: w is uint32 [out, in/8] holding eight
  * 4-bit codes per word along the input dim, lowest nibble first; scales and biases are
@@ -111,12 +126,18 @@ typedef struct {
 /* embed and lm_head are the target's raw embedding table [vocab, hidden] and untied
  * lm_head, shared with the drafter (lablup/mlxcel #1762, What changed). fc is
  * encoder.fc [hidden, target_streams*target_width]; enc_norm is encoder.output_norm_enc.
- * `layers` is a host array of cfg.layers entries; it is copied at create. */
+ * `layers` is a host array of cfg.layers entries; it is copied at create.
+ * markov_w1 and markov_w2 (DSpark only, else NULL) are the Markov head's factors, both
+ * [vocab, markov_rank] row-major in the embedding table's dtype: w1 is gathered at the
+ * previous token and w2 maps that rank-r row to one logit per vocabulary entry
+ * (lablup/mlxcel #1751, Security fixes). They are read in place (16-byte aligned, alive
+ * while the context is). */
 typedef struct {
   const void *embed;
   dflash_linear lm_head, fc;
   const void *enc_norm, *final_norm;
   const dflash_layer *layers;
+  const void *markov_w1, *markov_w2;
 } dflash_weights;
 
 /* Bytes of ring (layers * 2 * kv_heads * Cs * head_dim * act element size), of workspace
@@ -136,7 +157,12 @@ dflash_status dflash_query_sizes(const dflash_config *cfg, size_t *ring_bytes, s
  * synchronises `stream`; afterwards the caller may free those row-major linears. The
  * embedding table and the norm gains are read in place and must stay alive; the linears
  * and the norm gains must be 16-byte aligned (DFLASH_E_ARG otherwise). The ring is
- * zero-filled and starts empty: e = 0, no pending rows. */
+ * zero-filled and starts empty: e = 0, no pending rows. With rope_traditional the packed
+ * q and k projections, and copies of q_norm and k_norm in `packed`, hold each head's
+ * elements in the order (0, 2, 4, ..., 1, 3, 5, ...): the rotate-half rotation of that
+ * order is the adjacent-pair rotation of the original one, and attention scores are
+ * unchanged by a permutation shared by queries and keys, so every kernel runs one RoPE
+ * form; the ring keeps keys in that order and dflash_cache_read restores the original. */
 dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *weights, void *ring,
                             size_t ring_bytes, void *workspace, size_t workspace_bytes, void *packed,
                             size_t packed_bytes, void *stream, dflash_ctx **out);
@@ -187,6 +213,16 @@ dflash_status dflash_cache_trim(dflash_ctx *ctx, int32_t m);
  * [block+1, hidden], or NULL) receives the residual stream after the last layer. Errors:
  * block outside 1..max_block or anchor outside [0, vocab) (DFLASH_E_RANGE); NULL d_tokens
  * (DFLASH_E_ARG); e == 0 (DFLASH_E_NO_CONTEXT); pending rows (DFLASH_E_STATE).
+ *
+ * DSpark contexts (lablup/mlxcel #1751, Implementation Review Summary, Verified against the
+ * issue): block = gamma proposals from gamma rows [anchor, mask x (gamma-1)] at positions
+ * e..e+gamma-1, every row through final_norm and the lm_head (row 0 included), then the
+ * Markov chain on the device: step i adds markov_w2 . markov_w1[t_i] to row i's logits
+ * (t_0 = anchor, t_{i+1} = the step's token) and d_tokens[i] receives the first index of
+ * the maximum, which the next step gathers; no host round trip inside the chain. The
+ * DSpark backbone attends to every context row (no mask), which the window rule matches
+ * while e + gamma - 1 <= window: a longer context is refused (DFLASH_E_RANGE) rather than
+ * cut. d_hidden then has gamma rows.
  */
 dflash_status dflash_draft_block(dflash_ctx *ctx, int32_t anchor, int32_t block, int32_t *d_tokens,
                                  float *d_hidden, void *stream);
@@ -360,9 +396,10 @@ dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pen
 
 /* Copy one layer's live window, positions max(0, e-W)..e-1 in position order, into
  * k_out and v_out (device, act_dtype [kv_heads, n, head_dim], at least kv_heads * min(e, W)
- * * head_dim elements each); *n_out = n (host). Rows whose K/V an append deferred are
- * projected into the ring first. Errors: NULL n_out, k_out or v_out, or a layer outside
- * 0..layers-1 (nothing enqueued). */
+ * * head_dim elements each); *n_out = n (host). Keys come out in the original element
+ * order whatever the RoPE form. Rows whose K/V an append deferred are projected into the
+ * ring first. Errors: NULL n_out, k_out or v_out, or a layer outside 0..layers-1 (nothing
+ * enqueued). */
 dflash_status dflash_cache_read(dflash_ctx *ctx, int32_t layer, void *k_out, void *v_out, int32_t *n_out,
                                 void *stream);
 

@@ -130,7 +130,9 @@ class LockStep:
             self.check_window()
 
     def draft(self, anchor: int, block: int) -> np.ndarray:
-        hidden = torch.empty((block + 1, self.sh.hidden), dtype=torch.float32, device=self.gpu.device)
+        dspark = getattr(self.sh, "variant", "dflash") == "dspark"
+        rows = block if dspark else block + 1
+        hidden = torch.empty((rows, self.sh.hidden), dtype=torch.float32, device=self.gpu.device)
         toks = self.gpu.draft_block(anchor, block, hidden=hidden)
         res = self.orc.draft(anchor, block)
         torch.cuda.synchronize()
@@ -141,8 +143,28 @@ class LockStep:
         x = elem_excess(hg, res.hidden, self.tol, False)
         self.stats.max_hidden_elem = max(self.stats.max_hidden_elem, x)
         assert x <= 1.0, f"hidden element error {x:.3g} x its bound"
+        if dspark:
+            return self._agree_chain(toks.cpu().numpy(), res, anchor)
         self._agree(toks.cpu().numpy(), res.tokens, res.margins, "draft token")
         return res.tokens
+
+    def _agree_chain(self, got: np.ndarray, res, anchor: int) -> np.ndarray:
+        """DSpark chain: each step's token against the oracle's step taken from the GPU's own
+        previous token (the anchor first), exact above the near-tie margin, so a near tie the
+        two sides break differently still leaves every later step checked."""
+        w1, w2 = self.orc.w["markov_w1"], self.orc.w["markov_w2"]
+        prev = int(anchor)
+        for i in range(len(got)):
+            score = res.logits[i] + O.markov_transition(w1, w2, prev)
+            idx, margin = O.argmax_with_margin(score[None, :])
+            self.stats.rows_checked += 1
+            if margin[0] <= self.margin:
+                self.stats.near_ties += 1
+                self.stats.near_tie_flips += int(got[i] != idx[0])
+            else:
+                assert got[i] == idx[0], f"chain step {i}: gpu {got[i]} oracle {idx[0]} (margin {margin[0]:.4g})"
+            prev = int(got[i])
+        return got.astype(np.int64)
 
     def target_argmax(self, rows: np.ndarray) -> np.ndarray:
         idx = self.gpu.lm_head_argmax(self._t(rows))

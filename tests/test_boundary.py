@@ -128,3 +128,28 @@ def test_status_strings():
     for s in range(8):
         assert L.dflash_status_string(s)
     assert L.dflash_status_string(99) == b"unknown status"
+
+
+def test_dspark_config_validation_and_sizes():
+    """DSpark contexts (lablup/mlxcel #1751, Security fixes): the verify width max_block + 1 is
+    clamped at 32, the Markov rank is one the chain kernel tiles, a DFlash context takes no
+    Markov rank; the workspace holds the block's backbone logits, and adjacent-pair RoPE adds
+    one deinterleaved copy of each layer's q_norm and k_norm to the packed weights."""
+    E_ARG, E_SHAPE, E_RANGE = 1, 2, 3
+    ds = synth.TINY_DSPARK_F32
+    assert status_of(ds, max_block=31) == 0
+    assert status_of(ds, max_block=32) == E_RANGE
+    assert status_of(ds, max_block=31, markov_rank=100) == E_SHAPE
+    assert status_of(ds, max_block=31, markov_rank=512) == E_SHAPE  # f32 factors: at most 256
+    assert status_of(synth.MUSE_DSPARK_BF16, max_block=9, markov_rank=512) == 0
+    assert status_of(ds, max_block=31, markov_rank=0) == E_SHAPE
+    assert status_of(synth.TINY_F32, markov_rank=64) == E_ARG
+    assert status_of(synth.TINY_F32, variant=2) == E_ARG
+    assert status_of(synth.TINY_F32, rope_traditional=2) == E_ARG
+    r0, w0, p0 = sizes(synth.TINY_F32, 9)
+    r1, w1, p1 = sizes(ds.with_(window=synth.TINY_F32.window), 9)
+    assert r1 == r0
+    assert w0 + 4 * 9 * ds.vocab <= w1 <= w0 + 4 * 9 * ds.vocab + 8 * 4096 + 3 * 256
+    assert p1 == p0 + ds.layers * 2 * 256  # head_dim 64 f32 gains: one 256-byte block each
+    _, _, p2 = sizes(synth.TINY_F32.with_(rope_style="traditional"), 9)
+    assert p2 == p1
