@@ -75,10 +75,19 @@ def alg_bytes(sh, block: int, ctx_visible: int) -> dict:
     fc = H * F * we
     lm = V * H * we
     kv = sh.layers * 2 * min(ctx_visible, sh.window) * kvd * e
-    inputs = (block + 1) * F * e + (block + 1) * H * e
+    dspark = getattr(sh, "variant", "dflash") == "dspark"
+    rows = block if dspark else block + 1  # DSpark: gamma block rows
+    inputs = (block + 1) * F * e + rows * H * e
     fwd = fc + sh.layers * layer + lm + kv + inputs
-    return {"fc": fc, "layers": sh.layers * layer, "lm_head": lm, "kv": kv, "block_forward": fwd,
-            "round_lm_verify": fwd + lm + (block + 1) * H * e}
+    out = {"fc": fc, "layers": sh.layers * layer, "lm_head": lm, "kv": kv}
+    if dspark:
+        # every row's f32 logits written once and read once by its chain step, and per step
+        # the whole markov_w2 plus one markov_w1 row (the factors take the activation dtype)
+        step = V * sh.markov_rank * e + V * 4 + sh.markov_rank * e
+        out.update(markov_step=step, chain=block * step, logits=2 * block * V * 4)
+        fwd += block * step + block * V * 4
+    out.update(block_forward=fwd, round_lm_verify=fwd + lm + (block + 1) * H * e)
+    return out
 
 
 def counted_traffic():
@@ -121,7 +130,8 @@ class Leg:
         self.prefill_ms = e0.elapsed_time(e1)
         del slab
 
-    def run(self, warmup: int, steps: int, verify, resid_tag: int, anchor_tag: int, lm_timing: bool = False) -> dict:
+    def run(self, warmup: int, steps: int, verify, resid_tag: int, anchor_tag: int, lm_timing: bool = False,
+            chain_timing: bool = False) -> dict:
         """verify(r, toks_r, out_r): enqueue the target's argmaxes of round r into out_r;
         verify.prepare(tgt), if present, fills what does not depend on the draft beforehand."""
         torch, synth = self.torch, self.synth
@@ -138,7 +148,8 @@ class Leg:
             verify.prepare(tgt)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
         evk = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)] if lm_timing else None
-        for pair in evk or []:
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)] if chain_timing else None
+        for pair in (evk or []) + (evc or []):
             for x in pair:
                 x.record(stream)  # creates the underlying events before the timed region
         anchor = synth.anchor_token(sh, tag=anchor_tag)
@@ -156,6 +167,7 @@ class Leg:
                 el = time.perf_counter() - t0
             e = ev[r - b0] if r >= b0 else None
             if e: e[0].record(stream)
+            if e and evc: g.time_next_chain(*evc[r - b0])
             g.draft_block(anchor, B, tokens=toks[r], stream=stream)
             if e: e[1].record(stream)
             if e and evk: g.time_next_argmax(*evk[r - b0])
@@ -207,6 +219,8 @@ class Leg:
         if evk:
             out["_lm_ms"] = float(np.mean([x[0].elapsed_time(x[1]) for x in evk]))
             out["_lm_call_ms"] = float(np.mean([x[1].elapsed_time(x[2]) for x in ev]))
+        if evc:
+            out["_chain_ms"] = float(np.mean([x[0].elapsed_time(x[1]) for x in evc]))
         return out
 
 
@@ -539,6 +553,49 @@ def run_target(args) -> dict:
             "committed_equals_classic": out[:m] == classic[:m], "tokens_compared": m, "rounds": rounds}
 
 
+def run_dspark(args, weights, dw) -> dict:
+    """The DSpark form of the Muse-shaped drafter (rank-256 Markov head, adjacent-pair RoPE,
+    window 4096) at the pages' verify widths 8 and 10 (7 and 9 proposals per round), after a
+    1024-row context, verify rows through the shared lm_head. The drafter's other tensors are
+    the block-4 workload's (same seeds); the Markov factors are drawn for it. The chain's
+    gamma step launches are event-timed in the breakdown rounds: per step the kernel streams
+    markov_w2 once."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+
+    wl = synth.WORKLOADS["muse-dspark-bf16-w8-w10-ctx1024"]
+    sh = wl.shape
+    dd = dict(dw)
+    for name in ("markov_w1", "markov_w2"):
+        dd[name] = torch.from_numpy(synth.to_bf16_values(synth.draw_tensor(sh, name))).to(torch.bfloat16).cuda()
+    torch.cuda.synchronize()
+    widths = []
+    for B in wl.blocks:
+        leg = Leg(sh, dd, B, wl.context)
+        n = args.warmup + args.dspark_steps + min(args.dspark_steps, BREAKDOWN_ROUNDS)
+        res = leg.run(args.warmup, args.dspark_steps, lm_head_verify(leg, n, seed_tag=500 * B), resid_tag=7000 + B,
+                      anchor_tag=B, chain_timing=True)
+        by = res["_bytes"]
+        step_ms = res["_chain_ms"] / B
+        res.update(verify_width=B + 1, round_hbm_frac=round(by["round_lm_verify"] * res["rounds_per_s"] /
+                                                              (HBM_PEAK_GBS * 1e9), 4),
+                   chain_ms=round(res["_chain_ms"], 5), markov_step_us=round(1e3 * step_ms, 3),
+                   markov_step_gbs=round(by["markov_step"] / (step_ms * 1e-3) / 1e9, 1))
+        widths.append(public(res))
+        del leg
+        torch.cuda.empty_cache()
+    best = max(widths, key=lambda w: w["markov_step_gbs"])
+    step_bytes = alg_bytes(sh, 1, 0)["markov_step"]
+    return {"workload": wl.name, "markov_rank": sh.markov_rank, "rope": sh.rope_style, "widths": widths,
+            "roofline_markov_step": {"bound": "hbm", "kernel": "Markov chain step (markov_w2 202048x256 bf16 + "
+                                                               "one f32 logit row)",
+                                     "achieved": best["markov_step_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(best["markov_step_gbs"] / HBM_PEAK_GBS, 4),
+                                     "algorithmic_bytes_per_launch": step_bytes,
+                                     "avg_launch_us": best["markov_step_us"], "traffic": None}}
+
+
 def stream_probe(mib: int, reps: int = 10) -> dict:
     """The in-repo HBM streaming-read probe: mib MiB read `reps` times, event-timed."""
     import torch
@@ -611,6 +668,8 @@ def main():
     ap.add_argument("--c0-steps", type=int, default=500, help="timed rounds of the tiny f32 round (0 = skip)")
     ap.add_argument("--target-steps", type=int, default=96,
                     help="rounds (and classic decode tokens) against the synthetic target (0 = skip)")
+    ap.add_argument("--dspark-steps", type=int, default=200,
+                    help="timed rounds per verify width of the DSpark drafter (0 = skip)")
     ap.add_argument("--adaptive-steps", type=int, default=768,
                     help="rounds per run of the adaptive-width comparison (0 = skip)")
     ap.add_argument("--probe-mib", type=int, default=1024, help="HBM streaming-read probe size (0 = skip)")
@@ -661,6 +720,10 @@ def main():
     if c3:
         print("[bench] 16384 context done", file=sys.stderr, flush=True)
     adaptive = run_adaptive(args, sh, dw) if args.adaptive_steps > 0 else None
+    dspark = run_dspark(args, weights, dw) if args.dspark_steps > 0 else None
+    if dspark:
+        print("[bench] dspark: " + ", ".join(f"width {w['verify_width']} {w['rounds_per_s']} rounds/s"
+                                             for w in dspark["widths"]), file=sys.stderr, flush=True)
     del dw
     torch.cuda.empty_cache()
     target = run_target(args) if args.target_steps > 0 else None
@@ -704,6 +767,7 @@ def main():
         "block16": b16,
         "ctx16384": c3,
         "adaptive_width": adaptive,
+        "dspark": dspark,
         "target": target,
         "q4": q4,
         "tiny_f32": c0,

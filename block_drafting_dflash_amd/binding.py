@@ -20,6 +20,7 @@ _DTYPE = {"f32": DFLASH_F32, "bf16": DFLASH_BF16, "q4": DFLASH_Q4G64}
 
 EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cache_append", "dflash_cache_trim",
            "dflash_draft_block", "dflash_lm_head_argmax", "dflash_lm_head_argmax_noalloc", "dflash_time_next_argmax",
+           "dflash_time_next_chain",
            "dflash_verify_greedy", "dflash_hbm_read_probe", "dflash_width_ctl_create", "dflash_width_ctl_width",
            "dflash_width_ctl_record", "dflash_width_ctl_state", "dflash_width_ctl_destroy",
            "dflash_target_query_sizes", "dflash_target_create", "dflash_target_destroy", "dflash_target_forward",
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
         "dflash_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
         "dflash_lm_head_argmax_noalloc": (i32, [vp, vp, i32, vp, vp]),
         "dflash_time_next_argmax": (i32, [vp, vp, vp]),
+        "dflash_time_next_chain": (i32, [vp, vp, vp]),
         "dflash_hbm_read_probe": (i32, [vp, sz, vp, i32, vp]),
         "dflash_width_ctl_create": (i32, [i32, i32, i32, i32, P(vp)]),
         "dflash_width_ctl_width": (i32, [vp]),
@@ -294,6 +296,16 @@ class Drafter:
                 ev.record()  # torch creates the underlying event on its first record
             handles.append(ctypes.c_void_p(ev.cuda_event))
         _check(lib().dflash_time_next_argmax(self.ctx, *handles), self.ctx)
+
+    def time_next_chain(self, start: "torch.cuda.Event", end: "torch.cuda.Event") -> None:
+        """Have the next draft_block of a DSpark context record `start` and `end` right around
+        its Markov chain (gamma step launches)."""
+        handles = []
+        for ev in (start, end):
+            if not ev.cuda_event:
+                ev.record()
+            handles.append(ctypes.c_void_p(ev.cuda_event))
+        _check(lib().dflash_time_next_chain(self.ctx, *handles), self.ctx)
 
     def verify_greedy(self, draft: torch.Tensor, target: torch.Tensor, block: int,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -33,7 +33,7 @@ struct Layer {
 
 struct Layout {  // byte offsets into the workspace
   size_t argmax_part, knorm_ptrs, x, hn, qkv, qb, attn, mlp, zrows, part, rope, app_fc, app_kv;
-  size_t logits, mk_part, mk_ticket;  // DSpark: backbone logits of a block, chain keys, chain counter
+  size_t logits, mk_part;  // DSpark: backbone logits of a block, the chain's keys (two steps' worth)
   size_t total;
 };
 
@@ -87,6 +87,8 @@ struct dflash_ctx {
   // (dflash_time_next_argmax); `active` while that call runs
   hipEvent_t tev_start = nullptr, tev_end = nullptr;
   bool tev_active = false;
+  // events around the Markov chain of the next DSpark draft (dflash_time_next_chain)
+  hipEvent_t cev_start = nullptr, cev_end = nullptr;
   char err[512] = {0};
 };
 
@@ -278,8 +280,7 @@ Layout make_layout(const Cfg& g) {
   L.app_kv = take(4 * (size_t)GEMM_MAX_ROWS * c.layers * 2 * kvd);
   if (g.dspark) {
     L.logits = take(4 * (size_t)c.max_block * c.vocab);
-    L.mk_part = take(sizeof(unsigned long long) * MK_MAX_GROUPS);
-    L.mk_ticket = take(sizeof(unsigned int));
+    L.mk_part = take(sizeof(unsigned long long) * 2 * MK_MAX_GROUPS);
   }
   L.total = o;
   return L;
@@ -733,7 +734,6 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
   // every slot starts finite (zero): attention reads whole aligned runs of slots, including
   // keys outside a query's window that then get weight 0
   if (e == hipSuccess) e = hipMemsetAsync(ring, 0, ring_bytes_of(g), st);
-  if (e == hipSuccess && g.dspark) e = hipMemsetAsync(ctx->ws + lay.mk_ticket, 0, sizeof(unsigned int), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
   if (e != hipSuccess) {
     cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
@@ -901,23 +901,31 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     lm.xlo = zrows_lo;
     return run_gemm(ctx, lm, block, st);
   }
-  // DSpark: every row's f32 logits, then the Markov chain, one launch per step, each step
-  // gathering the token the previous one wrote (the anchor first)
+  // DSpark: every row's f32 logits, then the Markov chain: one launch per step, each taking
+  // its token from the keys the previous step left (the anchor first) and storing it as the
+  // previous step's output, then the reduction of the last step's keys
   float* logits = (float*)(ctx->ws + ctx->lay.logits);
   GemmCall lm{EPI_STORE, XSRC_GLOBAL, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, logits, c.vocab, nullptr};
   lm.split = g.bf;
   lm.xlo = zrows_lo;
   if ((s = run_gemm(ctx, lm, block, st)) != DFLASH_OK) return s;
-  unsigned long long* mk_part = (unsigned long long*)(ctx->ws + ctx->lay.mk_part);
-  unsigned int* mk_ticket = (unsigned int*)(ctx->ws + ctx->lay.mk_ticket);
+  unsigned long long* keys[2] = {(unsigned long long*)(ctx->ws + ctx->lay.mk_part),
+                                 (unsigned long long*)(ctx->ws + ctx->lay.mk_part) + MK_MAX_GROUPS};
+  const int ng = ctx->mk_groups;
+  hipEvent_t cs = ctx->cev_start, ce = ctx->cev_end;
+  ctx->cev_start = ctx->cev_end = nullptr;
+  if (cs && (s = dev(ctx, hipEventRecord(cs, st), "timing event")) != DFLASH_OK) return s;
   for (int i = 0; i < block; ++i) {
     s = dev(ctx,
             launch_markov_step(g.bf, c.markov_rank, ctx->markov_w1, ctx->markov_w2, c.vocab,
-                               logits + (size_t)i * c.vocab, i ? d_tokens + i - 1 : nullptr, anchor, mk_part,
-                               mk_ticket, d_tokens + i, ctx->mk_groups, st),
+                               logits + (size_t)i * c.vocab, i ? keys[(i - 1) & 1] : nullptr, ng, anchor,
+                               i ? d_tokens + i - 1 : nullptr, keys[i & 1], ng, st),
             "markov step");
     if (s != DFLASH_OK) return s;
   }
+  s = dev(ctx, launch_argmax_finalize(keys[(block - 1) & 1], ng, 1, d_tokens + block - 1, st), "markov finish");
+  if (s != DFLASH_OK) return s;
+  if (ce) return dev(ctx, hipEventRecord(ce, st), "timing event");
   return DFLASH_OK;
 }
 
@@ -948,6 +956,15 @@ dflash_status dflash_time_next_argmax(dflash_ctx* ctx, void* start, void* end) {
   if ((start == nullptr) != (end == nullptr)) return fail(ctx, DFLASH_E_ARG, "give both timing events or neither");
   ctx->tev_start = (hipEvent_t)start;
   ctx->tev_end = (hipEvent_t)end;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_time_next_chain(dflash_ctx* ctx, void* start, void* end) {
+  if (!ctx) return DFLASH_E_ARG;
+  if ((start == nullptr) != (end == nullptr)) return fail(ctx, DFLASH_E_ARG, "give both timing events or neither");
+  if (!ctx->cfg.dspark) return fail(ctx, DFLASH_E_ARG, "a DFlash context has no Markov chain");
+  ctx->cev_start = (hipEvent_t)start;
+  ctx->cev_end = (hipEvent_t)end;
   return DFLASH_OK;
 }
 

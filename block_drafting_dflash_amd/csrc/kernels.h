@@ -240,11 +240,12 @@ constexpr int MK_MAX_GROUPS = 4096;  // bound on a step's work-groups (its key a
 bool markov_rank_supported(int act_bf16, int rank);
 // work-groups of one chain step on a device of `cus` compute units
 int markov_step_groups(int vocab, int rank, int act_bf16, int cus);
-// One chain step: out[0] = first argmax over v of logits[v] + w2[v] . w1[t], t = prev[0]
-// (anchor when prev is NULL); part holds `groups` keys and ticket one zeroed counter, which
-// the step leaves zeroed.
+// One chain step over the vocabulary: keys[g] (g < groups) = the largest (score, index) key of
+// work-group g, score[v] = logits[v] + w2[v] . w1[t]. t is the anchor when prev_keys is NULL,
+// else the index of the largest of the previous step's prev_groups keys, which work-group 0
+// also stores to prev_out[0]. The last step's keys are reduced by launch_argmax_finalize.
 hipError_t launch_markov_step(int act_bf16, int rank, const void* w1, const void* w2, int vocab, const float* logits,
-                              const int32_t* prev, int32_t anchor, unsigned long long* part, unsigned int* ticket,
-                              int32_t* out, int groups, hipStream_t s);
+                              const unsigned long long* prev_keys, int prev_groups, int32_t anchor, int32_t* prev_out,
+                              unsigned long long* keys, int groups, hipStream_t s);
 
 }  // namespace dflash

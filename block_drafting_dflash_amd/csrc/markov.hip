@@ -11,9 +11,15 @@
 // the same 16 bytes of u = w1[t] for the whole launch); the LPR lanes of a row read its
 // rank * elt bytes as one contiguous run, a wave load reads 64 / LPR whole rows (1 KiB
 // contiguous), and each wave keeps MK_LOADS such loads in flight. The per-row sums finish
-// with DPP row operations. The work-groups leave (score, index) keys; the last work-group
-// to finish (a ticket counter: no work-group waits on another) reduces them, writes the
-// token where the next step reads it, and re-arms the counter.
+// with DPP row operations, and each work-group leaves one (score, index) key.
+//
+// The steps pass the token on through kernel boundaries, with no device-wide fence: every
+// work-group of step i reduces the keys step i-1 left (a few KiB, read while its first w2
+// loads, which do not depend on the token, are in flight) to the token t_i itself, and
+// work-group 0 also stores it as the previous step's output. A last one-work-group launch
+// reduces the final step's keys. (A fence per work-group, to let the last one finish the
+// reduction in the same launch, writes back and invalidates the L2 each time: it measured
+// four times slower than the whole stream.)
 #include "common.h"
 #include "kernels.h"
 
@@ -55,20 +61,68 @@ template <bool BF, int RANK>
 __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __restrict__ w1,
                                                                  const u32x4_t* __restrict__ w2, int vocab,
                                                                  const float* __restrict__ logits,
-                                                                 const int32_t* __restrict__ prev, int32_t anchor,
-                                                                 unsigned long long* __restrict__ part,
-                                                                 unsigned int* __restrict__ ticket,
-                                                                 int32_t* __restrict__ out) {
+                                                                 const unsigned long long* __restrict__ prev_keys,
+                                                                 int prev_groups, int32_t anchor,
+                                                                 int32_t* __restrict__ prev_out,
+                                                                 unsigned long long* __restrict__ keys) {
   constexpr int EPL = BF ? 8 : 4;        // elements per 16-byte slice
   constexpr int LPR = RANK / EPL;        // lanes per row
   static_assert(LPR >= 2 && LPR <= 64 && 64 % LPR == 0, "rank slices must tile a wave");
   constexpr int RPL = 64 / LPR;          // rows per wave load
   constexpr int GROUP = RPL * MK_LOADS;  // rows per wave pass
   constexpr int SLICES = RANK / EPL;     // 16-byte slices per row
+  constexpr int KPT = MK_MAX_GROUPS / MK_THREADS;  // previous keys per thread, at most
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int sub = lane % LPR, rsub = lane / LPR;
+  const int ngroups = (vocab + GROUP - 1) / GROUP;
+  __shared__ unsigned long long red[MK_WAVES];
+  __shared__ int32_t tok;
 
-  const int32_t t = prev ? prev[0] : anchor;  // in [0, vocab): the previous step clamps it
+  // the first pass's loads (rows past the vocabulary re-read the last one, unused)
+  int g = blockIdx.x * MK_WAVES + w;
+  u32x4_t v[MK_LOADS];
+  float lg[MK_LOADS];
+  auto issue = [&](int gg) {
+    const int r0 = gg * GROUP + rsub;
+#pragma unroll
+    for (int j = 0; j < MK_LOADS; ++j) {
+      const int row = min(r0 + j * RPL, vocab - 1);
+      v[j] = __builtin_nontemporal_load(w2 + (size_t)row * SLICES + sub);
+      lg[j] = logits[row];
+    }
+  };
+  if (g < ngroups) issue(g);
+
+  // the previous token: the anchor, or the largest key step i-1 left
+  if (prev_keys) {
+    unsigned long long b = 0ull;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int k = tid + i * MK_THREADS;
+      const unsigned long long kk = k < prev_groups ? prev_keys[k] : 0ull;
+      b = kk > b ? kk : b;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long kk = shfl_xor_u64(b, o);
+      b = kk > b ? kk : b;
+    }
+    if (lane == 0) red[w] = b;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int i = 1; i < MK_WAVES; ++i) b = red[i] > b ? red[i] : b;
+      const int32_t idx = argmax_key_index(b);
+      tok = idx >= 0 && idx < vocab ? idx : 0;  // a vocabulary row whatever the keys held
+      if (blockIdx.x == 0) prev_out[0] = tok;
+    }
+    __syncthreads();
+  } else if (tid == 0) {
+    tok = anchor;
+  }
+  if (!prev_keys) __syncthreads();
+  const int32_t t = tok;
+
   float u[EPL];
   {
     const u32x4_t uw = ((const u32x4_t*)w1)[(size_t)t * SLICES + sub];
@@ -85,17 +139,8 @@ __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __r
   }
 
   unsigned long long best = 0ull;  // below every real key
-  const int ngroups = (vocab + GROUP - 1) / GROUP;
-  for (int g = blockIdx.x * MK_WAVES + w; g < ngroups; g += gridDim.x * MK_WAVES) {
+  for (; g < ngroups; g += gridDim.x * MK_WAVES) {
     const int r0 = g * GROUP + rsub;
-    u32x4_t v[MK_LOADS];
-    float lg[MK_LOADS];
-#pragma unroll
-    for (int j = 0; j < MK_LOADS; ++j) {  // rows past the vocabulary re-read the last one, unused
-      const int row = min(r0 + j * RPL, vocab - 1);
-      v[j] = __builtin_nontemporal_load(w2 + (size_t)row * SLICES + sub);
-      lg[j] = logits[row];
-    }
 #pragma unroll
     for (int j = 0; j < MK_LOADS; ++j) {
       const float d = row_lanes_sum<LPR>(dot16<BF>(v[j], u));
@@ -105,50 +150,23 @@ __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __r
       const unsigned long long k = argmax_key(lg[j] + d, row) & (0ull - (unsigned long long)(row < vocab));
       best = k > best ? k : best;
     }
+    const int gn = g + gridDim.x * MK_WAVES;
+    if (gn < ngroups) issue(gn);
   }
 
-  __shared__ unsigned long long red[MK_WAVES];
-  __shared__ int last;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long k = shfl_xor_u64(best, o);
     best = k > best ? k : best;
   }
+  __syncthreads();  // every wave is past its read of red (the previous-token reduction)
   if (lane == 0) red[w] = best;
   __syncthreads();
   if (tid == 0) {
     unsigned long long b = red[0];
 #pragma unroll
     for (int i = 1; i < MK_WAVES; ++i) b = red[i] > b ? red[i] : b;
-    part[blockIdx.x] = b;
-    __threadfence();  // the key is visible device-wide before the ticket counts it
-    last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!last) return;
-
-  // the last work-group: every other key has been published
-  __threadfence();
-  unsigned long long b = 0ull;
-  for (int i = tid; i < (int)gridDim.x; i += MK_THREADS) {
-    const unsigned long long k = __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    b = k > b ? k : b;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long k = shfl_xor_u64(b, o);
-    b = k > b ? k : b;
-  }
-  __syncthreads();  // every wave has read `red` above
-  if (lane == 0) red[w] = b;
-  __syncthreads();
-  if (tid == 0) {
-#pragma unroll
-    for (int i = 1; i < MK_WAVES; ++i) b = red[i] > b ? red[i] : b;
-    b = red[0] > b ? red[0] : b;
-    const int32_t idx = argmax_key_index(b);
-    out[0] = idx >= 0 && idx < vocab ? idx : 0;  // a vocabulary row whatever the scores held
-    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // re-armed for the next step
+    keys[blockIdx.x] = b;
   }
 }
 
@@ -165,14 +183,16 @@ int markov_step_groups(int vocab, int rank, int bf, int cus) {
 }
 
 hipError_t launch_markov_step(int bf, int rank, const void* w1, const void* w2, int vocab, const float* logits,
-                              const int32_t* prev, int32_t anchor, unsigned long long* part, unsigned int* ticket,
-                              int32_t* out, int groups, hipStream_t s) {
-  if (!markov_rank_supported(bf, rank) || groups < 1 || groups > MK_MAX_GROUPS || vocab < 1)
+                              const unsigned long long* prev_keys, int prev_groups, int32_t anchor, int32_t* prev_out,
+                              unsigned long long* keys, int groups, hipStream_t s) {
+  if (!markov_rank_supported(bf, rank) || groups < 1 || groups > MK_MAX_GROUPS || vocab < 1 ||
+      (prev_keys && (prev_groups < 1 || prev_groups > MK_MAX_GROUPS || !prev_out)))
     return hipErrorInvalidValue;
   const dim3 grid(groups), block(MK_THREADS);
   const u32x4_t* w2v = (const u32x4_t*)w2;
-#define MK_LAUNCH(B, R) \
-  hipLaunchKernelGGL((markov_step_kernel<B, R>), grid, block, 0, s, w1, w2v, vocab, logits, prev, anchor, part, ticket, out)
+#define MK_LAUNCH(B, R)                                                                                         \
+  hipLaunchKernelGGL((markov_step_kernel<B, R>), grid, block, 0, s, w1, w2v, vocab, logits, prev_keys, prev_groups, \
+                     anchor, prev_out, keys)
   if (bf) {
     if (rank == 64) MK_LAUNCH(true, 64);
     else if (rank == 128) MK_LAUNCH(true, 128);

@@ -254,6 +254,14 @@ dflash_status dflash_lm_head_argmax_noalloc(dflash_ctx *ctx, const void *rows, i
  * request. Errors: NULL ctx, or exactly one NULL event (DFLASH_E_ARG). */
 dflash_status dflash_time_next_argmax(dflash_ctx *ctx, void *start, void *end);
 
+/* Kernel timing of the DSpark Markov chain (profiling; no counterpart on the pages). The
+ * next dflash_draft_block call on a DSpark context records `start` on its stream right
+ * before the first chain step and `end` right after the last, so the elapsed time is the
+ * gamma step launches back to back; the call then forgets both. Events as for
+ * dflash_time_next_argmax. Errors: NULL ctx, exactly one NULL event, or a DFlash context
+ * (DFLASH_E_ARG). */
+dflash_status dflash_time_next_chain(dflash_ctx *ctx, void *start, void *end);
+
 /* HBM streaming-read probe (measurement; no counterpart on the pages): `groups` work-groups
  * each read a contiguous share of `bytes` from src (device, 16-byte aligned, bytes a multiple
  * of 16 and at least groups * 4096) with 16-byte non-temporal loads and write the XOR of what

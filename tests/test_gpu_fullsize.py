@@ -192,3 +192,25 @@ def test_muse_speculative_loop_commits_the_tokens_of_classic_decoding(muse_pair)
     want = run_classic(t, tdev, prompt, 24)
     got, ks = run_speculative(t, dsh, tdev, ddev, prompt, 24, 4)
     assert got == want
+
+
+@pytest.mark.parametrize("gamma", [7, 9])
+def test_dspark_w8_w10_ctx1024_lm_head_verify(muse, gamma):
+    """The DSpark form of the Muse-shaped drafter (rank-256 Markov head over the 202048-row
+    vocabulary, adjacent-pair RoPE, window 4096) at verify widths 8 and 10, after a 1024-row
+    context, verify rows through the shared lm_head: every chain step (from the GPU's own
+    previous token), the hidden rows, the verify result, the offsets and the live window of
+    all five layers after every trim."""
+    w64, dev = muse
+    wl = synth.WORKLOADS["muse-dspark-bf16-w8-w10-ctx1024"]
+    sh = wl.shape
+    w = dict(w64)
+    dd = dict(dev)
+    for name in ("markov_w1", "markov_w2"):
+        m = synth.to_bf16_values(synth.draw_tensor(sh, name))
+        w[name] = m.astype(np.float64)
+        dd[name] = torch.from_numpy(m).to(torch.bfloat16).cuda()
+    ls = P.LockStep(sh, w, max_block=gamma, dev_weights=dd)
+    ks = P.run_lm_head_rounds(ls, wl.context, gamma, 6, anchor_tag=gamma)
+    _report(f"{wl.name} gamma {gamma}", ls, ks)
+    assert ls.stats.rows_checked == 6 * (gamma + gamma + 1)
