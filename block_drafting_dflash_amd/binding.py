@@ -26,7 +26,10 @@ EXPORTS = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_cach
            "dflash_target_query_sizes", "dflash_target_create", "dflash_target_destroy", "dflash_target_forward",
            "dflash_target_trim", "dflash_target_state", "dflash_target_cache_read", "dflash_target_last_error",
            "dflash_cache_state",
-           "dflash_cache_read", "dflash_last_error", "dflash_status_string")
+           "dflash_cache_read", "dflash_last_error", "dflash_status_string",
+           "dflash_batch_query_sizes", "dflash_batch_create", "dflash_batch_destroy", "dflash_batch_append",
+           "dflash_batch_trim", "dflash_batch_draft", "dflash_batch_lm_head_argmax", "dflash_batch_verify_greedy",
+           "dflash_batch_state", "dflash_batch_cache_read", "dflash_batch_last_error")
 
 
 class dflash_config(ctypes.Structure):
@@ -116,6 +119,17 @@ def lib() -> ctypes.CDLL:
         "dflash_cache_read": (i32, [vp, i32, vp, vp, P(i32), vp]),
         "dflash_last_error": (ctypes.c_char_p, [vp]),
         "dflash_status_string": (ctypes.c_char_p, [i32]),
+        "dflash_batch_query_sizes": (i32, [P(dflash_config), i32, P(sz), P(sz), P(sz)]),
+        "dflash_batch_create": (i32, [P(dflash_config), i32, P(dflash_weights), vp, sz, vp, sz, vp, sz, vp, P(vp)]),
+        "dflash_batch_destroy": (None, [vp]),
+        "dflash_batch_append": (i32, [vp, vp, P(i32), i32, vp]),
+        "dflash_batch_trim": (i32, [vp, P(i32)]),
+        "dflash_batch_draft": (i32, [vp, P(i32), i32, vp, vp, vp]),
+        "dflash_batch_lm_head_argmax": (i32, [vp, vp, i32, vp, vp]),
+        "dflash_batch_verify_greedy": (i32, [vp, vp, vp, i32, vp, vp]),
+        "dflash_batch_state": (i32, [vp, i32, P(i64), P(i32)]),
+        "dflash_batch_cache_read": (i32, [vp, i32, i32, vp, vp, P(i32), vp]),
+        "dflash_batch_last_error": (ctypes.c_char_p, [vp]),
     }
     for name, (res, args) in sig.items():  # every symbol include/dflash.h declares
         fn = getattr(L, name)
@@ -491,3 +505,143 @@ class Target:
         m = n.value
         return k[:kv * m * hd].view(kv, m, hd), v[:kv * m * hd].view(kv, m, hd)
 
+
+
+def _check_batch(status: int, b) -> None:
+    if status != 0:
+        L = lib()
+        msg = L.dflash_batch_last_error(b).decode() or L.dflash_status_string(status).decode()
+        raise DFlashError(status, msg)
+
+
+def _i32_array(vals) -> "ctypes.Array":
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+class Batch:
+    """One dflash_batch: n_seq independent sequences of one drafter, drafted together."""
+
+    def __init__(self, shape, dev_weights: Dict[str, object], n_seq: int, max_block: int, phase: int = 0,
+                 device="cuda", stream=None):
+        L = lib()
+        self.shape, self.n_seq = shape, n_seq
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.cfg = make_config(shape, max_block, phase)
+        self._w = dev_weights
+
+        def lin(name):
+            t = dev_weights[name]
+            if isinstance(t, tuple):
+                return dflash_linear(_ptr(t[0]), _ptr(t[1]), _ptr(t[2]))
+            return dflash_linear(_ptr(t), None, None)
+
+        layers = (dflash_layer * shape.layers)()
+        for l in range(shape.layers):
+            p = f"layers.{l}."
+            layers[l] = dflash_layer(*[lin(p + n) for n in ("q", "k", "v", "o", "gate", "up", "down")],
+                                     *[_ptr(dev_weights[p + n]) for n in ("in_norm", "post_norm", "q_norm", "k_norm")])
+        self._layers = layers
+        self.weights = dflash_weights(_ptr(dev_weights["embed"]), lin("lm_head"), lin("fc"),
+                                      _ptr(dev_weights["enc_norm"]), _ptr(dev_weights["final_norm"]),
+                                      ctypes.cast(layers, ctypes.POINTER(dflash_layer)), None, None)
+        rb, wb, pb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.dflash_batch_query_sizes(ctypes.byref(self.cfg), n_seq, ctypes.byref(rb), ctypes.byref(wb),
+                                          ctypes.byref(pb)), None)
+        self.ring = torch.empty(max(rb.value, 256), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(wb.value, 256), dtype=torch.uint8, device=self.device)
+        self.packed = torch.empty(max(pb.value, 256), dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(L.dflash_batch_create(ctypes.byref(self.cfg), n_seq, ctypes.byref(self.weights), _ptr(self.ring),
+                                     rb.value, _ptr(self.workspace), wb.value, _ptr(self.packed), pb.value,
+                                     _stream(stream), ctypes.byref(h)), None)
+        self.b = h
+        self.act_dtype = act_torch_dtype(shape)
+
+    def __del__(self):
+        b = getattr(self, "b", None)
+        if b and _lib is not None:
+            _lib.dflash_batch_destroy(b)
+            self.b = None
+
+    def append(self, resid: torch.Tensor, counts, commit: bool = False, stream=None) -> None:
+        """resid: [sum(counts), fc_in], sequence 0's rows first."""
+        self._dev(resid, self.act_dtype)
+        if len(counts) != self.n_seq or resid.dim() != 2 or resid.shape[0] != sum(counts) or \
+                resid.shape[1] != self.shape.fc_in:
+            raise ValueError("residual rows must be [sum(counts), target_streams*target_width], one count per sequence")
+        _check_batch(lib().dflash_batch_append(self.b, _ptr(resid), _i32_array(counts), int(bool(commit)),
+                                               _stream(stream)), self.b)
+
+    def trim(self, m) -> None:
+        if len(m) != self.n_seq:
+            raise ValueError("one rewind count per sequence")
+        _check_batch(lib().dflash_batch_trim(self.b, _i32_array(m)), self.b)
+
+    def draft(self, anchors, block: int, tokens: Optional[torch.Tensor] = None,
+              hidden: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if len(anchors) != self.n_seq:
+            raise ValueError("one anchor per sequence")
+        if tokens is None:
+            tokens = torch.empty((self.n_seq, block), dtype=torch.int32, device=self.device)
+        self._dev(tokens, torch.int32)
+        if tokens.numel() < self.n_seq * block:
+            raise ValueError("token output too small")
+        if hidden is not None:
+            self._dev(hidden, torch.float32)
+            if hidden.numel() < self.n_seq * (block + 1) * self.shape.hidden:
+                raise ValueError("hidden output too small")
+        _check_batch(lib().dflash_batch_draft(self.b, _i32_array(anchors), int(block), _ptr(tokens), _ptr(hidden),
+                                              _stream(stream)), self.b)
+        return tokens
+
+    def lm_head_argmax(self, rows: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        self._dev(rows, self.act_dtype)
+        if rows.dim() != 2 or rows.shape[1] != self.shape.hidden:
+            raise ValueError("rows must be [n, hidden]")
+        if out is None:
+            out = torch.empty(rows.shape[0], dtype=torch.int32, device=self.device)
+        self._dev(out, torch.int32)
+        _check_batch(lib().dflash_batch_lm_head_argmax(self.b, _ptr(rows), rows.shape[0], _ptr(out), _stream(stream)),
+                     self.b)
+        return out
+
+    def verify_greedy(self, draft: torch.Tensor, target: torch.Tensor, block: int,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        self._dev(draft, torch.int32)
+        self._dev(target, torch.int32)
+        if draft.numel() < self.n_seq * block or target.numel() < self.n_seq * (block + 1):
+            raise ValueError("draft needs [n_seq, block] and target [n_seq, block + 1]")
+        if out is None:
+            out = torch.empty((self.n_seq, 3), dtype=torch.int32, device=self.device)
+        if out.device.type == "cpu":
+            if not (out.is_pinned() and out.dtype == torch.int32 and out.is_contiguous() and
+                    out.numel() >= 3 * self.n_seq):
+                raise ValueError("a host output must be a pinned, contiguous int32 tensor of 3 * n_seq elements")
+        else:
+            self._dev(out, torch.int32)
+        _check_batch(lib().dflash_batch_verify_greedy(self.b, _ptr(draft), _ptr(target), int(block), _ptr(out),
+                                                      _stream(stream)), self.b)
+        return out
+
+    def state(self, seq: int) -> Tuple[int, int]:
+        e, pend = ctypes.c_int64(), ctypes.c_int32()
+        _check_batch(lib().dflash_batch_state(self.b, int(seq), ctypes.byref(e), ctypes.byref(pend)), self.b)
+        return e.value, pend.value
+
+    def cache_read(self, seq: int, layer: int, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+        e, _ = self.state(seq)
+        n_max = min(e, self.shape.window)
+        sh = (self.shape.kv_heads, max(n_max, 1), self.shape.head_dim)
+        k = torch.empty(sh, dtype=self.act_dtype, device=self.device)
+        v = torch.empty(sh, dtype=self.act_dtype, device=self.device)
+        n = ctypes.c_int32()
+        _check_batch(lib().dflash_batch_cache_read(self.b, int(seq), int(layer), _ptr(k), _ptr(v), ctypes.byref(n),
+                                                   _stream(stream)), self.b)
+        return k[:, :n.value], v[:, :n.value]
+
+    def _dev(self, t: torch.Tensor, dtype: torch.dtype) -> None:
+        if t.device != self.device or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {dtype} tensor on {self.device}, got {t.dtype} on {t.device}")

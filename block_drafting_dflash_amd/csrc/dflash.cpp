@@ -502,7 +502,8 @@ int fold_rows_of(const Cfg& g) {
 // K/V of rc encoder rows (the fc output in the append buffer) at positions pos.. into the
 // ring: the per-layer k/v projections with the encoder norm fused as the operand norm, six
 // layers per launch, then the ring write (k RMSNorm, RoPE, cache dtype)
-dflash_status project_kv(dflash_ctx* ctx, int rc, int64_t pos, hipStream_t st) {
+// the raw per-layer K/V (app_kv, f32 [rc][layers * 2 * kvd]) of the rc encoder rows in app_fc
+dflash_status kv_gemms(dflash_ctx* ctx, int rc, hipStream_t st) {
   const Cfg& g = ctx->cfg;
   const dflash_config& c = g.c;
   const int kvd = c.kv_heads * c.head_dim;
@@ -521,9 +522,23 @@ dflash_status project_kv(dflash_ctx* ctx, int rc, int64_t pos, hipStream_t st) {
     const dflash_status s = run_gemm(ctx, kvc, rc, st);
     if (s != DFLASH_OK) return s;
   }
-  return dev(ctx, launch_ring_write(g.bf, g.a, kv, (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), rc, pos,
-                                    ctx->ring, st),
+  return DFLASH_OK;
+}
+
+// k_norm, RoPE and the cache-dtype cast of n rows of app_kv starting at row r0, at positions
+// pos.., into `ring`
+dflash_status ring_write_rows(dflash_ctx* ctx, int r0, int n, int64_t pos, unsigned char* ring, hipStream_t st) {
+  const Cfg& g = ctx->cfg;
+  const size_t kv_cols = (size_t)g.c.layers * 2 * g.c.kv_heads * g.c.head_dim;
+  const float* kv = (const float*)(ctx->ws + ctx->lay.app_kv) + (size_t)r0 * kv_cols;
+  return dev(ctx, launch_ring_write(g.bf, g.a, kv, (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), n, pos, ring,
+                                    st),
              "ring write");
+}
+
+dflash_status project_kv(dflash_ctx* ctx, int rc, int64_t pos, hipStream_t st) {
+  const dflash_status s = kv_gemms(ctx, rc, st);
+  return s != DFLASH_OK ? s : ring_write_rows(ctx, 0, rc, pos, ctx->ring, st);
 }
 
 // the deferred rows' K/V into the ring now
@@ -609,23 +624,25 @@ dflash_status dflash_query_sizes(const dflash_config* cfg, size_t* ring_bytes, s
   return DFLASH_OK;
 }
 
-dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts, void* ring, size_t ring_bytes,
-                            void* workspace, size_t workspace_bytes, void* packed, size_t packed_bytes, void* stream,
-                            dflash_ctx** out) {
-  g_create_err[0] = 0;
-  if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
-  *out = nullptr;
-  Cfg g;
-  dflash_status s = check_cfg(cfg, &g, g_create_err);
-  if (s != DFLASH_OK) return s;
+}  // extern "C"
+
+namespace {
+
+// Binds a context to validated buffers and weights and initialises it on `st` (the body of
+// dflash_create, shared with the batch context): packs every linear, fills the k_norm
+// table, zero-fills the first ring_need ring bytes and synchronises the stream. fold_rows:
+// whether committed rows' K/V may travel with the next draft.
+dflash_status init_engine(dflash_ctx* ctx, const Cfg& g, const dflash_weights* wts, void* ring, size_t ring_need,
+                          size_t ring_bytes, void* workspace, size_t workspace_bytes, void* packed,
+                          size_t packed_bytes, bool fold_rows, hipStream_t st) {
   if (!wts || !wts->layers) return cfg_fail(g_create_err, DFLASH_E_ARG, "weights or layer array is NULL");
   if (!ring || !workspace || !packed) return cfg_fail(g_create_err, DFLASH_E_ARG, "ring, workspace or packed is NULL");
   if (((uintptr_t)ring & 255u) || ((uintptr_t)workspace & 255u) || ((uintptr_t)packed & 255u))
     return cfg_fail(g_create_err, DFLASH_E_ARG, "ring, workspace and packed must be 256-byte aligned");
   const Layout lay = make_layout(g);
   const PackedLayout pk = make_packed_layout(g);
-  if (ring_bytes < ring_bytes_of(g) || workspace_bytes < lay.total || packed_bytes < pk.total)
-    return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring, workspace or packed smaller than dflash_query_sizes");
+  if (ring_bytes < ring_need || workspace_bytes < lay.total || packed_bytes < pk.total)
+    return cfg_fail(g_create_err, DFLASH_E_SHAPE, "ring, workspace or packed smaller than the queried sizes");
   auto lin_ok = [&](const dflash_linear& l) {
     if (!l.w || !aligned16(l.w)) return false;
     if (g.wt == WT_Q4) return l.scales && l.biases && ((uintptr_t)l.scales & 1u) == 0 && ((uintptr_t)l.biases & 1u) == 0;
@@ -646,11 +663,9 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
     return cfg_fail(g_create_err, DFLASH_E_ARG,
                     g.dspark ? "the Markov factors are NULL or not 16-byte aligned"
                              : "Markov factors given to a DFlash context");
-  dflash_ctx* ctx = new (std::nothrow) dflash_ctx();
-  if (!ctx) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
   ctx->cfg = g;
   ctx->lay = lay;
-  ctx->fold_rows = fold_rows_of(g);
+  ctx->fold_rows = fold_rows ? fold_rows_of(g) : 0;
   auto cv = [](const dflash_linear& l) { return Lin{l.w, l.scales, l.biases}; };
   ctx->lm_head = cv(wts->lm_head);
   ctx->fc = cv(wts->fc);
@@ -683,7 +698,6 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
     e = noalloc_scratch_address(ctx->device, &keys);
     ctx->noalloc_keys = (unsigned long long*)keys;
   }
-  hipStream_t st = (hipStream_t)stream;
   // repack every linear into fragment-major blocks; the context reads only the packed copies
   {
     const dflash_config& c = g.c;
@@ -733,12 +747,33 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts,
                        hipMemcpyHostToDevice, st);
   // every slot starts finite (zero): attention reads whole aligned runs of slots, including
   // keys outside a query's window that then get weight 0
-  if (e == hipSuccess) e = hipMemsetAsync(ring, 0, ring_bytes_of(g), st);
+  if (e == hipSuccess) e = hipMemsetAsync(ring, 0, ring_need, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);  // the host copy source dies with this call
-  if (e != hipSuccess) {
-    cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return cfg_fail(g_create_err, DFLASH_E_DEVICE, "workspace init: %s", hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* wts, void* ring, size_t ring_bytes,
+                            void* workspace, size_t workspace_bytes, void* packed, size_t packed_bytes, void* stream,
+                            dflash_ctx** out) {
+  g_create_err[0] = 0;
+  if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
+  *out = nullptr;
+  Cfg g;
+  dflash_status s = check_cfg(cfg, &g, g_create_err);
+  if (s != DFLASH_OK) return s;
+  dflash_ctx* ctx = new (std::nothrow) dflash_ctx();
+  if (!ctx) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
+  s = init_engine(ctx, g, wts, ring, ring_bytes_of(g), ring_bytes, workspace, workspace_bytes, packed, packed_bytes,
+                  true, (hipStream_t)stream);
+  if (s != DFLASH_OK) {
     delete ctx;
-    return DFLASH_E_DEVICE;
+    return s;
   }
   *out = ctx;
   return DFLASH_OK;
@@ -1350,6 +1385,302 @@ dflash_status dflash_target_cache_read(dflash_target* t, int32_t layer, void* k_
              launch_cache_read(ctx->cfg.bf, a, ctx->ring + t->cache_off[layer], lo, n, k_out, v_out,
                                (hipStream_t)stream),
              "cache read");
+}
+
+}  // extern "C"
+
+// ======================================================================================
+// Independent sequences drafted together (dflash_batch_*): one engine (packed weights,
+// workspace sized for every sequence's block) and one ring per sequence. Every GEMM of a
+// round runs once over the rows of all sequences, so each weight byte is read once per
+// round for the whole batch; embedding, attention, the final norm and the ring writes run
+// per sequence, on its own positions and ring; verify runs one wave per sequence.
+// ======================================================================================
+struct dflash_batch {
+  dflash_ctx core;  // the engine; core.ring is sequence 0's ring, core.e/pending are unused
+  int n_seq = 0;
+  size_t ring_seq = 0;  // bytes of one sequence's ring
+  std::vector<int64_t> e, pending;
+};
+
+namespace {
+
+constexpr int BATCH_MAX_SEQ = 64;
+constexpr int BATCH_MAX_ROWS = 512;  // n_seq * (max_block + 1)
+
+dflash_status check_batch(const dflash_config* c, int32_t n_seq, Cfg* g, char* err) {
+  dflash_status s = check_cfg(c, g, err);
+  if (s != DFLASH_OK) return s;
+  if (n_seq < 1 || n_seq > BATCH_MAX_SEQ) return cfg_fail(err, DFLASH_E_RANGE, "n_seq %d outside 1..%d", n_seq, BATCH_MAX_SEQ);
+  if (g->dspark) return cfg_fail(err, DFLASH_E_ARG, "a batch drafts in the DFlash form only");
+  if ((int64_t)n_seq * (c->max_block + 1) > BATCH_MAX_ROWS)
+    return cfg_fail(err, DFLASH_E_RANGE, "n_seq * (max_block + 1) = %lld rows above %d",
+                    (long long)n_seq * (c->max_block + 1), BATCH_MAX_ROWS);
+  // buffers of a round hold every sequence's block rows; the ring geometry (Cs) stays the
+  // one of a single sequence, computed by check_cfg above
+  g->R = n_seq * (c->max_block + 1);
+  return DFLASH_OK;
+}
+
+unsigned char* seq_ring(dflash_batch* b, int s) { return b->core.ring + (size_t)s * b->ring_seq; }
+
+// Runs f with the engine's committed state set to sequence s's (the single-sequence paths
+// read ctx->ring, ctx->e and ctx->pending), then stores that state back.
+template <class F>
+dflash_status as_sequence(dflash_batch* b, int s, F&& f) {
+  dflash_ctx& c = b->core;
+  unsigned char* ring0 = c.ring;
+  c.ring = seq_ring(b, s);
+  c.e = b->e[s];
+  c.pending = b->pending[s];
+  const dflash_status st = f();
+  b->e[s] = c.e;
+  b->pending[s] = c.pending;
+  c.ring = ring0;
+  c.e = c.pending = 0;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_batch_query_sizes(const dflash_config* cfg, int32_t n_seq, size_t* ring_bytes,
+                                       size_t* workspace_bytes, size_t* packed_bytes) {
+  Cfg g;
+  dflash_status s = check_batch(cfg, n_seq, &g, g_create_err);
+  if (s != DFLASH_OK) return s;
+  if (!ring_bytes || !workspace_bytes || !packed_bytes) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL size output");
+  *ring_bytes = (size_t)n_seq * ring_bytes_of(g);
+  *workspace_bytes = make_layout(g).total;
+  *packed_bytes = make_packed_layout(g).total;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_batch_create(const dflash_config* cfg, int32_t n_seq, const dflash_weights* wts, void* ring,
+                                  size_t ring_bytes, void* workspace, size_t workspace_bytes, void* packed,
+                                  size_t packed_bytes, void* stream, dflash_batch** out) {
+  g_create_err[0] = 0;
+  if (!out) return cfg_fail(g_create_err, DFLASH_E_ARG, "NULL output handle");
+  *out = nullptr;
+  Cfg g;
+  dflash_status s = check_batch(cfg, n_seq, &g, g_create_err);
+  if (s != DFLASH_OK) return s;
+  dflash_batch* b = new (std::nothrow) dflash_batch();
+  if (!b) return cfg_fail(g_create_err, DFLASH_E_ARG, "out of host memory");
+  b->n_seq = n_seq;
+  b->ring_seq = ring_bytes_of(g);
+  b->e.assign(n_seq, 0);
+  b->pending.assign(n_seq, 0);
+  // no deferred K/V: an append projects its rows at once, so a draft never carries
+  // committed rows beside the block rows of several sequences
+  s = init_engine(&b->core, g, wts, ring, (size_t)n_seq * b->ring_seq, ring_bytes, workspace, workspace_bytes, packed,
+                  packed_bytes, false, (hipStream_t)stream);
+  if (s != DFLASH_OK) {
+    delete b;
+    return s;
+  }
+  *out = b;
+  return DFLASH_OK;
+}
+
+void dflash_batch_destroy(dflash_batch* b) { delete b; }
+
+const char* dflash_batch_last_error(const dflash_batch* b) { return b ? b->core.err : g_create_err; }
+
+dflash_status dflash_batch_state(const dflash_batch* b, int32_t seq, int64_t* e, int32_t* pending) {
+  if (!b) return DFLASH_E_ARG;
+  if (seq < 0 || seq >= b->n_seq) return DFLASH_E_RANGE;
+  if (e) *e = b->e[seq];
+  if (pending) *pending = (int32_t)b->pending[seq];
+  return DFLASH_OK;
+}
+
+dflash_status dflash_batch_append(dflash_batch* b, const void* resid, const int32_t* counts, int32_t commit,
+                                  void* stream) {
+  if (!b) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &b->core;
+  if (!resid || !counts) return fail(ctx, DFLASH_E_ARG, "NULL residual rows or counts: no residual stream captured");
+  int64_t total = 0;
+  bool fits = !commit;  // rows of one call all land in the ring: every sequence's count <= C
+  for (int s = 0; s < b->n_seq; ++s) {
+    if (counts[s] < 0) return fail(ctx, DFLASH_E_ARG, "sequence %d: negative row count %d", s, counts[s]);
+    total += counts[s];
+    fits = fits && counts[s] <= ctx->cfg.C;
+  }
+  if (total <= 0) return fail(ctx, DFLASH_E_ARG, "append of zero rows: no residual stream captured");
+  if (total > INT32_MAX) return fail(ctx, DFLASH_E_RANGE, "append of %lld rows", (long long)total);
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  const int64_t F = (int64_t)c.target_streams * c.target_width;
+  hipStream_t st = (hipStream_t)stream;
+  const unsigned char* base = (const unsigned char*)resid;
+  if (!fits) {
+    // committing appends (prompts) go sequence by sequence: each drops the rows its window
+    // can no longer see before the encoder
+    int64_t r = 0;
+    for (int s = 0; s < b->n_seq; ++s) {
+      const int n = counts[s];
+      if (n > 0) {
+        const unsigned char* rows = base + (size_t)r * F * g.act_elt;
+        const dflash_status st_s =
+            as_sequence(b, s, [&] { return dflash_cache_append(ctx, rows, n, commit, stream); });
+        if (st_s != DFLASH_OK) return st_s;
+      }
+      r += n;
+    }
+    return DFLASH_OK;
+  }
+  // pending rows of every sequence (a round's verify rows): the encoder and the K/V
+  // projections run over all sequences' rows at once, the ring writes per sequence
+  std::vector<int64_t> start(b->n_seq), first(b->n_seq + 1, 0);
+  for (int s = 0; s < b->n_seq; ++s) {
+    start[s] = b->e[s] + b->pending[s];
+    first[s + 1] = first[s] + counts[s];
+  }
+  float* fc_out = (float*)(ctx->ws + ctx->lay.app_fc);
+  for (int64_t r0 = 0; r0 < total; r0 += GEMM_MAX_ROWS) {
+    const int rc = (int)std::min<int64_t>(GEMM_MAX_ROWS, total - r0);
+    GemmCall f{EPI_STORE, XSRC_GLOBAL, {seg(ctx->fc, 0, c.hidden)}, (int)F, base + (size_t)r0 * F * g.act_elt, F,
+               nullptr, fc_out, c.hidden, nullptr};
+    dflash_status s = run_gemm(ctx, f, rc, st);
+    if (s == DFLASH_OK) s = kv_gemms(ctx, rc, st);
+    for (int q = 0; q < b->n_seq && s == DFLASH_OK; ++q) {
+      const int64_t lo = std::max<int64_t>(first[q], r0), hi = std::min<int64_t>(first[q + 1], r0 + rc);
+      if (lo < hi) s = ring_write_rows(ctx, (int)(lo - r0), (int)(hi - lo), start[q] + (lo - first[q]), seq_ring(b, q), st);
+    }
+    if (s != DFLASH_OK) return s;
+  }
+  for (int s = 0; s < b->n_seq; ++s) b->pending[s] += counts[s];
+  return DFLASH_OK;
+}
+
+dflash_status dflash_batch_trim(dflash_batch* b, const int32_t* m) {
+  if (!b) return DFLASH_E_ARG;
+  if (!m) return fail(&b->core, DFLASH_E_ARG, "NULL rewind counts");
+  for (int s = 0; s < b->n_seq; ++s)
+    if (m[s] < 0 || m[s] > b->pending[s] || m[s] > b->core.cfg.S)
+      return fail(&b->core, DFLASH_E_REWIND, "sequence %d: rewind of %d rows with %lld pending and slack %lld", s,
+                  m[s], (long long)b->pending[s], (long long)b->core.cfg.S);
+  for (int s = 0; s < b->n_seq; ++s) {
+    b->e[s] += b->pending[s] - m[s];
+    b->pending[s] = 0;
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_t block, int32_t* d_tokens,
+                                 float* d_hidden, void* stream) {
+  if (!b) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &b->core;
+  const Cfg& g = ctx->cfg;
+  const dflash_config& c = g.c;
+  if (!anchors || !d_tokens) return fail(ctx, DFLASH_E_ARG, "NULL anchors or token output");
+  if (block < 1 || block > c.max_block) return fail(ctx, DFLASH_E_RANGE, "block %d outside 1..%d", block, c.max_block);
+  for (int s = 0; s < b->n_seq; ++s) {
+    if (anchors[s] < 0 || anchors[s] >= c.vocab)
+      return fail(ctx, DFLASH_E_RANGE, "sequence %d: anchor %d outside [0, %d)", s, anchors[s], c.vocab);
+    if (b->e[s] <= 0) return fail(ctx, DFLASH_E_NO_CONTEXT, "sequence %d: draft with an empty context", s);
+    if (b->pending[s])
+      return fail(ctx, DFLASH_E_STATE, "sequence %d: %lld appended rows are not committed", s, (long long)b->pending[s]);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int S = b->n_seq, R1 = block + 1, rows = S * R1;
+  const int H = c.hidden, hd = c.head_dim;
+  const int qd = c.q_heads * hd, kvd = c.kv_heads * hd;
+  float* x = (float*)(ctx->ws + ctx->lay.x);
+  float* qkv = (float*)(ctx->ws + ctx->lay.qkv);
+  unsigned char* qb = ctx->ws + ctx->lay.qb;
+  unsigned char* attn = ctx->ws + ctx->lay.attn;
+  void* mlp = ctx->ws + ctx->lay.mlp;
+  unsigned char* qb_lo = (unsigned char*)lo_plane(g, qb, g.R, qd);
+  unsigned char* attn_lo = (unsigned char*)lo_plane(g, attn, g.R, qd);
+  void* mlp_lo = lo_plane(g, mlp, g.R, c.intermediate);
+  float* part = (float*)(ctx->ws + ctx->lay.part);
+  float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
+  const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * hd;
+  const size_t op_row = (size_t)qd * g.act_elt;  // bytes of one row of an operand plane
+  dflash_status s = DFLASH_OK;
+  for (int q = 0; q < S && s == DFLASH_OK; ++q)
+    s = dev(ctx,
+            launch_embed(g.bf, ctx->embed, H, c.vocab, anchors[q], c.mask_token_id, nullptr, R1, 0, nullptr,
+                         x + (size_t)q * R1 * H, rope + (size_t)q * R1 * (hd / 2), b->e[q], c.rope_theta, hd, st),
+            "embed");
+  for (int l = 0; l < c.layers && s == DFLASH_OK; ++l) {
+    const Layer& L = ctx->layers[l];
+    GemmCall qc{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
+                L.in_norm, qkv, qd + 2 * kvd, nullptr};
+    qc.split = g.bf;
+    if ((s = run_gemm(ctx, qc, rows, st)) != DFLASH_OK) return s;
+    for (int q = 0; q < S && s == DFLASH_OK; ++q) {
+      const size_t r0 = (size_t)q * R1;
+      s = dev(ctx,
+              launch_block_attention(g.bf, g.a, qkv + r0 * (qd + 2 * kvd), L.q_norm, L.k_norm, rope + r0 * (hd / 2),
+                                     seq_ring(b, q) + l * ring_layer, R1, 0, b->e[q], qb + r0 * op_row,
+                                     g.bf ? qb_lo + r0 * op_row : nullptr, part, attn + r0 * op_row,
+                                     g.bf ? attn_lo + r0 * op_row : nullptr, st),
+              "attention");
+    }
+    if (s != DFLASH_OK) return s;
+    GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
+    o.split = g.bf;
+    o.xlo = attn_lo;
+    if ((s = run_gemm(ctx, o, rows, st)) != DFLASH_OK) return s;
+    GemmCall gu{EPI_SWIGLU, XSRC_NORM, {seg(L.gate, 0, c.intermediate), seg(L.up, 0, c.intermediate)}, H, x, H,
+                L.post_norm, mlp, c.intermediate, nullptr};
+    gu.split = g.bf;
+    gu.ylo = mlp_lo;
+    if ((s = run_gemm(ctx, gu, rows, st)) != DFLASH_OK) return s;
+    GemmCall dn{EPI_RESID, XSRC_GLOBAL, {seg(L.down, 0, H)}, c.intermediate, mlp, c.intermediate, nullptr, x, H,
+                nullptr};
+    dn.split = g.bf;
+    dn.xlo = mlp_lo;
+    if ((s = run_gemm(ctx, dn, rows, st)) != DFLASH_OK) return s;
+  }
+  if (s != DFLASH_OK) return s;
+  if (d_hidden) {
+    s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * rows * H, hipMemcpyDeviceToDevice, st), "hidden copy");
+    if (s != DFLASH_OK) return s;
+  }
+  // final RMSNorm of each sequence's rows 1..B into consecutive operand rows, then one
+  // lm_head argmax over all of them: d_tokens [n_seq][block]
+  void* zrows = ctx->ws + ctx->lay.zrows;
+  void* zrows_lo = lo_plane(g, zrows, S * block, H);
+  const size_t z_row = (size_t)H * (g.bf ? 2 : 4);
+  for (int q = 0; q < S && s == DFLASH_OK; ++q)
+    s = dev(ctx,
+            launch_rownorm(g.bf, x + ((size_t)q * R1 + 1) * H, ctx->final_norm, c.rms_eps, block, H,
+                           (unsigned char*)zrows + (size_t)q * block * z_row,
+                           g.bf ? (unsigned char*)zrows_lo + (size_t)q * block * z_row : nullptr, st),
+            "final norm");
+  if (s != DFLASH_OK) return s;
+  GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
+  lm.split = g.bf;
+  lm.xlo = zrows_lo;
+  return run_gemm(ctx, lm, S * block, st);
+}
+
+dflash_status dflash_batch_lm_head_argmax(dflash_batch* b, const void* rows, int32_t n, int32_t* d_idx, void* stream) {
+  if (!b) return DFLASH_E_ARG;
+  return dflash_lm_head_argmax(&b->core, rows, n, d_idx, stream);
+}
+
+dflash_status dflash_batch_verify_greedy(dflash_batch* b, const int32_t* d_draft, const int32_t* d_target,
+                                         int32_t block, int32_t* d_out, void* stream) {
+  if (!b) return DFLASH_E_ARG;
+  dflash_ctx* ctx = &b->core;
+  if (!d_draft || !d_target || !d_out) return fail(ctx, DFLASH_E_ARG, "NULL verify buffer");
+  if (block < 1 || block > ctx->cfg.c.max_block)
+    return fail(ctx, DFLASH_E_RANGE, "block %d outside 1..%d", block, ctx->cfg.c.max_block);
+  return dev(ctx, launch_verify(d_draft, d_target, block, ctx->cfg.c.vocab, d_out, (hipStream_t)stream, b->n_seq),
+             "verify");
+}
+
+dflash_status dflash_batch_cache_read(dflash_batch* b, int32_t seq, int32_t layer, void* k_out, void* v_out,
+                                      int32_t* n_out, void* stream) {
+  if (!b) return DFLASH_E_ARG;
+  if (seq < 0 || seq >= b->n_seq) return fail(&b->core, DFLASH_E_RANGE, "sequence %d outside 0..%d", seq, b->n_seq - 1);
+  return as_sequence(b, seq, [&] { return dflash_cache_read(&b->core, layer, k_out, v_out, n_out, stream); });
 }
 
 }  // extern "C"

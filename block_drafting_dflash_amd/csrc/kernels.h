@@ -225,8 +225,9 @@ bool attention_forms_committed_rows(int act_bf16, const AttnShape& a);
 size_t attention_partial_floats(const AttnShape& a, int R);
 // the same for queries whose keys span at most `span` positions before the block
 size_t attention_partial_floats_span(const AttnShape& a, int R, int span);
+// greedy verify of n_seq sequences, one wave each: draft [n_seq][B], target [n_seq][B+1], out [n_seq][3]
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out,
-                         hipStream_t s);
+                         hipStream_t s, int n_seq = 1);
 // Streaming read of `bytes` (a multiple of 16, at least groups * 4096) by `groups` work-groups
 // of contiguous shares; sink [groups] receives an XOR of what each read (misc.hip).
 hipError_t launch_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int groups, hipStream_t s);

@@ -206,6 +206,10 @@ hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, 
 // (lablup/mlxcel #1751, Implementation Review Summary: greedy exact-match verify rule).
 __global__ void verify_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ target, int B,
                               int vocab, int32_t* out) {
+  // one wave per sequence of a batch: its draft [B], target [B+1] and result [3]
+  draft += (size_t)blockIdx.x * B;
+  target += (size_t)blockIdx.x * (B + 1);
+  out += (size_t)blockIdx.x * 3;
   const int lane = threadIdx.x;
   bool bad = false;
   for (int i = lane; i <= B; i += 64) {
@@ -236,8 +240,10 @@ __global__ void verify_kernel(const int32_t* __restrict__ draft, const int32_t* 
   }
 }
 
-hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(64), 0, s, draft, target, B, vocab, out);
+hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out, hipStream_t s,
+                         int n_seq) {
+  if (n_seq < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(verify_kernel, dim3(n_seq), dim3(64), 0, s, draft, target, B, vocab, out);
   return hipGetLastError();
 }
 

@@ -411,6 +411,68 @@ dflash_status dflash_cache_state(const dflash_ctx *ctx, int64_t *e, int32_t *pen
 dflash_status dflash_cache_read(dflash_ctx *ctx, int32_t layer, void *k_out, void *v_out, int32_t *n_out,
                                 void *stream);
 
+/*
+ * Independent sequences drafted together (B > 1 requests; the pages' Muse pairing declines
+ * them, lablup/mlxcel #1762, Not in this PR, and the LFM2 pairing is batch 1 as well,
+ * lablup/mlxcel #1751, Review fixes). A batch holds n_seq sequences of one drafter config,
+ * each with its own ring, committed end e_s and pending rows; nothing couples two
+ * sequences, so sequence s computes exactly what a dflash_ctx fed the same calls computes.
+ * One round drafts every sequence at the same block width; accept lengths, and so trims
+ * and contexts, differ per sequence. Every GEMM of a round runs once over the rows of all
+ * sequences (each weight byte is read once per round for the batch); the rest runs per
+ * sequence. The DFlash form only (variant 0); 1 <= n_seq <= 64 and n_seq * (max_block + 1)
+ * <= 512 (DFLASH_E_RANGE otherwise). Conventions as for dflash_ctx; per-sequence host
+ * arrays have n_seq entries.
+ */
+typedef struct dflash_batch dflash_batch; /* opaque */
+
+/* Ring bytes for all sequences (n_seq rings of the single-sequence size, back to back),
+ * workspace and packed bytes. Host only. */
+dflash_status dflash_batch_query_sizes(const dflash_config *cfg, int32_t n_seq, size_t *ring_bytes,
+                                       size_t *workspace_bytes, size_t *packed_bytes);
+
+/* As dflash_create, for n_seq sequences (every ring empty). */
+dflash_status dflash_batch_create(const dflash_config *cfg, int32_t n_seq, const dflash_weights *weights,
+                                  void *ring, size_t ring_bytes, void *workspace, size_t workspace_bytes, void *packed,
+                                  size_t packed_bytes, void *stream, dflash_batch **out);
+void dflash_batch_destroy(dflash_batch *b);
+
+/* Append captured residual rows: resid (device, act_dtype [sum(counts), F]) holds sequence
+ * 0's counts[0] rows, then sequence 1's, ...; counts (host) may hold zeros. Per sequence as
+ * dflash_cache_append (commit, drop before the encoder); pending appends of at most C rows
+ * per sequence run the encoder and K/V projections once over all rows. Errors: NULL resid
+ * or counts, a negative count, or no rows at all (DFLASH_E_ARG). */
+dflash_status dflash_batch_append(dflash_batch *b, const void *resid, const int32_t *counts, int32_t commit,
+                                  void *stream);
+
+/* Per sequence: commit the pending rows except the last m[s] (host array). All legal or
+ * nothing changes (DFLASH_E_REWIND). */
+dflash_status dflash_batch_trim(dflash_batch *b, const int32_t *m);
+
+/* One block of `block` drafted tokens for every sequence: sequence s runs rows [anchors[s],
+ * mask x block] at its positions e_s..e_s+block over its own ring (dflash_draft_block).
+ * anchors: host int32 [n_seq]; d_tokens: device int32 [n_seq][block]; d_hidden: device f32
+ * [n_seq][block+1][hidden] or NULL. Errors as dflash_draft_block, for any sequence. */
+dflash_status dflash_batch_draft(dflash_batch *b, const int32_t *anchors, int32_t block, int32_t *d_tokens,
+                                 float *d_hidden, void *stream);
+
+/* dflash_lm_head_argmax on the batch's lm_head (rows of any sequences, 1 <= n <= 4096). */
+dflash_status dflash_batch_lm_head_argmax(dflash_batch *b, const void *rows, int32_t n, int32_t *d_idx, void *stream);
+
+/* dflash_verify_greedy of every sequence in one launch: d_draft [n_seq][block], d_target
+ * [n_seq][block+1], d_out [n_seq][3] (device or pinned host memory). */
+dflash_status dflash_batch_verify_greedy(dflash_batch *b, const int32_t *d_draft, const int32_t *d_target,
+                                         int32_t block, int32_t *d_out, void *stream);
+
+/* Sequence seq's committed end and pending rows (host only; DFLASH_E_RANGE for a bad seq). */
+dflash_status dflash_batch_state(const dflash_batch *b, int32_t seq, int64_t *e, int32_t *pending);
+
+/* dflash_cache_read of sequence seq's ring. */
+dflash_status dflash_batch_cache_read(dflash_batch *b, int32_t seq, int32_t layer, void *k_out, void *v_out,
+                                      int32_t *n_out, void *stream);
+
+const char *dflash_batch_last_error(const dflash_batch *b);
+
 /* Description of the last error on ctx (never NULL), and of a status code. */
 const char *dflash_last_error(const dflash_ctx *ctx);
 const char *dflash_status_string(dflash_status s);

@@ -149,7 +149,36 @@ def test_dspark_config_validation_and_sizes():
     r0, w0, p0 = sizes(synth.TINY_F32, 9)
     r1, w1, p1 = sizes(ds.with_(window=synth.TINY_F32.window), 9)
     assert r1 == r0
-    assert w0 + 4 * 9 * ds.vocab <= w1 <= w0 + 4 * 9 * ds.vocab + 8 * 4096 + 3 * 256
+    assert w0 + 4 * 9 * ds.vocab <= w1 <= w0 + 4 * 9 * ds.vocab + 2 * 8 * 4096 + 2 * 256  # logits, two steps of keys
     assert p1 == p0 + ds.layers * 2 * 256  # head_dim 64 f32 gains: one 256-byte block each
     _, _, p2 = sizes(synth.TINY_F32.with_(rope_style="traditional"), 9)
     assert p2 == p1
+
+
+def test_batch_sizes_and_validation():
+    """A batch of n sequences: n rings of the single-sequence size back to back, the same
+    packed weights, a workspace for n blocks; n in 1..64, n * (max_block + 1) <= 512, DFlash
+    form only."""
+    L = binding.lib()
+    sh = synth.MUSE_BF16
+    r1, w1, p1 = sizes(sh, 4)
+
+    def bsizes(shape, n, max_block=4, **over):
+        cfg = binding.make_config(shape, max_block)
+        for k, v in over.items():
+            setattr(cfg, k, v)
+        rb, wb, pb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+        st = L.dflash_batch_query_sizes(ctypes.byref(cfg), n, ctypes.byref(rb), ctypes.byref(wb), ctypes.byref(pb))
+        return st, rb.value, wb.value, pb.value
+
+    st, rb, wb, pb = bsizes(sh, 4)
+    assert st == 0 and rb == 4 * r1 and pb == p1 and wb > w1
+    assert bsizes(sh, 1)[1:] == (r1, bsizes(sh, 1)[2], p1)
+    assert bsizes(sh, 0)[0] == 3 and bsizes(sh, 65)[0] == 3
+    assert bsizes(sh, 64, max_block=7)[0] == 0  # 512 rows
+    assert bsizes(sh, 64, max_block=8)[0] == 3  # 576 rows
+    assert bsizes(synth.MUSE_DSPARK_BF16, 2, max_block=7)[0] == 1
+    h = ctypes.c_void_p()
+    cfg = binding.make_config(sh, 4)
+    assert L.dflash_batch_create(ctypes.byref(cfg), 2, None, None, 0, None, 0, None, 0, None, ctypes.byref(h)) == 1
+    assert not h.value
