@@ -596,6 +596,91 @@ def run_dspark(args, weights, dw) -> dict:
                                      "avg_launch_us": best["markov_step_us"], "traffic": None}}
 
 
+def run_batch(args, sh, dw) -> dict:
+    """Independent sequences drafted together (dflash_batch_*): n sequences, each after its own
+    1024-row context, block 4, verify rows N(0,1) of all sequences through the shared lm_head
+    in one call, one verify launch, one append of every sequence's 5 rows, per-sequence trims;
+    the host waits for the n verify results in pinned memory. One sequence alone is the
+    block-4 round of the main leg through the batch entry points."""
+    import torch
+
+    from block_drafting_dflash_amd import binding, synth
+    from block_drafting_dflash_amd.counters import RoundCounters
+
+    B, ctx_rows = 4, 1024
+    out = {"workload": "muse-bf16-b4-ctx1024-batch", "block": B, "context": ctx_rows, "sizes": []}
+    stream = torch.cuda.current_stream()
+    for n in args.batch_sizes:
+        bt = binding.Batch(sh, dw, n, B)
+        slab = torch.cat([torch.from_numpy(synth.resid_rows(sh, ctx_rows, 5000 + s)) for s in range(n)])
+        bt.append(slab.to(binding.act_torch_dtype(sh)).cuda(), [ctx_rows] * n, commit=True)
+        del slab
+        steps, warm = args.batch_steps, args.warmup
+        nb = min(steps, BREAKDOWN_ROUNDS)
+        total = warm + steps + nb
+        rows = torch.from_numpy(np.stack([np.concatenate([synth.verify_hidden(sh, B + 1, 20000 + 100 * r + s)
+                                                          for s in range(n)]) for r in range(min(total, 64))]))
+        rows = rows.to(binding.act_torch_dtype(sh)).cuda()
+        resid = torch.from_numpy(np.stack([np.concatenate([synth.resid_rows(sh, B + 1, 30000 + 100 * r + s)
+                                                           for s in range(n)]) for r in range(min(total, 64))]))
+        resid = resid.to(binding.act_torch_dtype(sh)).cuda()
+        toks = torch.empty((total, n, B), dtype=torch.int32, device="cuda")
+        tgt = torch.empty((total, n, B + 1), dtype=torch.int32, device="cuda")
+        host = torch.empty((n, 3), dtype=torch.int32, pin_memory=True)
+        hv = host.numpy()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)]
+        anchors = [synth.anchor_token(sh, tag=s) for s in range(n)]
+        cnt = RoundCounters()
+        stream_toks = []
+        torch.cuda.synchronize()
+        t0 = el = None
+        for r in range(total):
+            if r == warm:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+            if r == warm + steps:
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+            e = ev[r - warm - steps] if r >= warm + steps else None
+            if e: e[0].record(stream)
+            bt.draft(anchors, B, tokens=toks[r], stream=stream)
+            if e: e[1].record(stream)
+            bt.lm_head_argmax(rows[r % 64].view(n * (B + 1), -1), out=tgt[r].view(-1), stream=stream)
+            hv[:] = -1
+            bt.verify_greedy(toks[r], tgt[r], B, out=host, stream=stream)
+            bt.append(resid[r % 64].view(n * (B + 1), -1), [B + 1] * n, stream=stream)
+            if e: e[2].record(stream)
+            t_wait = time.perf_counter()
+            while (hv[:, 0] == -1).any() or (hv[:, 2] == -1).any() or ((hv[:, 1] == -1) & (hv[:, 2] != 1)).any():
+                if time.perf_counter() - t_wait > 10.0:
+                    raise RuntimeError("the batch verify results did not arrive")
+            res = hv.copy()
+            assert (res[:, 2] == 0).all()
+            bt.trim([B - int(k) for k in res[:, 0]])
+            if warm <= r < warm + steps:
+                for s in range(n):
+                    cnt.record(B, int(res[s, 0]))
+            anchors = [int(b) for b in res[:, 1]]
+        torch.cuda.synchronize()
+        rs = steps / el
+        d_ms = float(np.mean([x[0].elapsed_time(x[1]) for x in ev]))
+        by = alg_bytes(sh, B, ctx_rows)
+        weights = by["fc"] + by["layers"] + by["lm_head"]
+        per_seq = by["block_forward"] - weights
+        fwd_bytes = weights + n * per_seq
+        out["sizes"].append({
+            "n_seq": n, "rows_per_gemm": n * (B + 1), "rounds_per_s": round(rs, 2),
+            "sequence_rounds_per_s": round(n * rs, 2), "drafted_tok_s": round(n * B * rs, 1),
+            "round_ms": round(1e3 * el / steps, 4), "draft_ms": round(d_ms, 4),
+            "round_ms_with_events": round(float(np.mean([x[0].elapsed_time(x[2]) for x in ev])), 4),
+            "draft_hbm_frac": round(fwd_bytes / (d_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "mean_accepted": round(cnt.as_dict()["mean_accepted"], 4), "steps": steps})
+        print(f"[bench] batch of {n}: {n * rs:.1f} sequence-rounds/s", file=sys.stderr, flush=True)
+        del bt, rows, resid, toks, tgt
+        torch.cuda.empty_cache()
+    return out
+
+
 def stream_probe(mib: int, reps: int = 10) -> dict:
     """The in-repo HBM streaming-read probe: mib MiB read `reps` times, event-timed."""
     import torch
@@ -670,6 +755,9 @@ def main():
                     help="rounds (and classic decode tokens) against the synthetic target (0 = skip)")
     ap.add_argument("--dspark-steps", type=int, default=200,
                     help="timed rounds per verify width of the DSpark drafter (0 = skip)")
+    ap.add_argument("--batch-steps", type=int, default=200,
+                    help="timed rounds per batch size of the batched-sequence leg (0 = skip)")
+    ap.add_argument("--batch-sizes", type=lambda t: [int(x) for x in t.split(",")], default=[1, 2, 4, 8])
     ap.add_argument("--adaptive-steps", type=int, default=768,
                     help="rounds per run of the adaptive-width comparison (0 = skip)")
     ap.add_argument("--probe-mib", type=int, default=1024, help="HBM streaming-read probe size (0 = skip)")
@@ -721,6 +809,7 @@ def main():
         print("[bench] 16384 context done", file=sys.stderr, flush=True)
     adaptive = run_adaptive(args, sh, dw) if args.adaptive_steps > 0 else None
     dspark = run_dspark(args, weights, dw) if args.dspark_steps > 0 else None
+    batch = run_batch(args, sh, dw) if args.batch_steps > 0 else None
     if dspark:
         print("[bench] dspark: " + ", ".join(f"width {w['verify_width']} {w['rounds_per_s']} rounds/s"
                                              for w in dspark["widths"]), file=sys.stderr, flush=True)
@@ -768,6 +857,7 @@ def main():
         "ctx16384": c3,
         "adaptive_width": adaptive,
         "dspark": dspark,
+        "batch": batch,
         "target": target,
         "q4": q4,
         "tiny_f32": c0,

@@ -405,7 +405,7 @@ template <int HD, int NW, bool BLK>
 __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* ring_layer,
                                                const float* __restrict__ qkv, const uint16_t* __restrict__ qnorm,
                                                const uint16_t* __restrict__ knorm, const float2* __restrict__ rope,
-                                               int R, int n, int64_t e, int nchunks, int tpw,
+                                               int R, int n, int64_t e, int nchunks, int tpw, int zi,
                                                float* __restrict__ part, uint16_t* __restrict__ kst,
                                                uint16_t* __restrict__ vst) {
   constexpr int KC = ATTN_CHUNK;  // 64 positions = two halves of 32
@@ -421,7 +421,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* rin
   const int lane = tid & 63, w = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int G = a.nq / a.nkv, NQ = R * G;
-  const int qt = blockIdx.z * tpw + w;
+  const int qt = zi * tpw + w;  // zi: this work-group's share of the query tiles
   const bool active = w < tpw && qt * 16 < NQ;  // other waves only copy and stage
   const int64_t lo = attn_lo(a, e), hi = e + R;
   const int64_t p0 = (lo / KC + c) * KC;
@@ -523,7 +523,7 @@ __device__ __forceinline__ void attn_mfma_body(const AttnShape& a, uint16_t* rin
         vst[(EPT * t16 + j) * VSTR + i] = sv1[j];
         vst[(HALF + EPT * t16 + j) * VSTR + i] = sv2[j];
       }
-      if ((p < e || a.causal) && blockIdx.z == 0) {  // a committed (or target block) row: also into its slots
+      if ((p < e || a.causal) && zi == 0) {  // a committed (or target block) row: also into its slots
         uint16_t* Kw = ring_layer + (size_t)g * C * HD + (size_t)slot_at(i) * HD + EPT * t16;
         uint16_t* VTw = ring_layer + (size_t)(a.nkv + g) * HD * C + slot_at(i);
 #pragma unroll
@@ -709,9 +709,41 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnShape a, uint16_
   __shared__ __align__(16) uint16_t vst[HD * (ATTN_CHUNK + 8)];
   const int64_t p0 = (attn_lo(a, e) / ATTN_CHUNK + blockIdx.x) * ATTN_CHUNK;
   if (p0 < e + R && e - n < p0 + ATTN_CHUNK)
-    attn_mfma_body<HD, NW, true>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, part, kst, vst);
+    attn_mfma_body<HD, NW, true>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, blockIdx.z, part, kst,
+                                 vst);
   else
-    attn_mfma_body<HD, NW, false>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, part, kst, vst);
+    attn_mfma_body<HD, NW, false>(a, ring_layer, qkv, qnorm, knorm, rope, R, n, e, nchunks, tpw, blockIdx.z, part, kst,
+                                  vst);
+}
+
+// Independent sequences in one launch (a batch round): blockIdx.z = sequence * zq + query
+// part. Sequence s has its own committed end, ring (ring_seq elements after s - 1's), R
+// rows of raw projections and rotary table after s - 1's, and a partial region of
+// part_seq floats laid out as a single sequence's with its own chunk count; chunks past
+// that count return at once. No committed rows travel with a batch draft (n = 0).
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_batch_kernel(AttnShape a, AttnSeqs seqs, uint16_t* ring0,
+                                                                  size_t ring_seq, const float* __restrict__ qkv,
+                                                                  const uint16_t* __restrict__ qnorm,
+                                                                  const uint16_t* __restrict__ knorm,
+                                                                  const float2* __restrict__ rope, int R, int zq,
+                                                                  int tpw, size_t part_seq, float* __restrict__ part) {
+  __shared__ __align__(16) uint16_t kst[ATTN_CHUNK * (HD + 8)];
+  __shared__ __align__(16) uint16_t vst[HD * (ATTN_CHUNK + 8)];
+  const int s = blockIdx.z / zq, zi = blockIdx.z - s * zq;
+  const int64_t e = seqs.e[s];
+  const int nch = attn_nchunks(a, R, e);
+  if ((int)blockIdx.x >= nch) return;
+  const size_t ldq = (size_t)(a.nq + 2 * a.nkv) * HD;
+  uint16_t* ring_layer = ring0 + (size_t)s * ring_seq;
+  const float* q_s = qkv + (size_t)s * R * ldq;
+  const float2* rope_s = rope + (size_t)s * R * (HD / 2);
+  float* part_s = part + (size_t)s * part_seq;
+  const int64_t p0 = (attn_lo(a, e) / ATTN_CHUNK + blockIdx.x) * ATTN_CHUNK;
+  if (p0 < e + R && e < p0 + ATTN_CHUNK)  // the chunk holds block positions
+    attn_mfma_body<HD, NW, true>(a, ring_layer, q_s, qnorm, knorm, rope_s, R, 0, e, nch, tpw, zi, part_s, kst, vst);
+  else
+    attn_mfma_body<HD, NW, false>(a, ring_layer, q_s, qnorm, knorm, rope_s, R, 0, e, nch, tpw, zi, part_s, kst, vst);
 }
 
 // ---- combine chunks in chunk order --------------------------------------------------------
@@ -746,6 +778,39 @@ __global__ void attn_combine_kernel(AttnShape a, const float* __restrict__ part,
     O += base[c * stride + d] * f;
   }
   op_st<BF>(out, out_lo, (size_t)r * a.nq * hd + (size_t)h * hd + d, O / L);
+}
+
+// The same for a batch round: blockIdx.x = sequence * R * nq + item, each sequence with its
+// own chunk count, partial region (part_seq floats) and output rows s * R ..
+template <bool BF>
+__global__ void attn_combine_batch_kernel(AttnShape a, AttnSeqs seqs, const float* __restrict__ part, size_t part_seq,
+                                          int R, void* out, void* out_lo) {
+  __shared__ float sm_m[COMBINE_MAX_CHUNKS], sm_l[COMBINE_MAX_CHUNKS];
+  const int per = R * a.nq;
+  const int s = blockIdx.x / per, item = blockIdx.x - s * per;
+  const int nchunks = attn_nchunks(a, R, seqs.e[s]);
+  const int r = item / a.nq, h = item - r * a.nq;
+  const int G = a.nq / a.nkv, g = h / G, hh = h - g * G;
+  const int NQ = R * G, qi = r * G + hh;
+  const int d = threadIdx.x, hd = a.hd;
+  const size_t stride = (size_t)NQ * PART_STRIDE(hd);
+  const float* base = part + (size_t)s * part_seq + ((size_t)g * nchunks * NQ + qi) * PART_STRIDE(hd);
+  for (int c = d; c < nchunks; c += blockDim.x) {
+    sm_m[c] = base[c * stride + hd];
+    sm_l[c] = base[c * stride + hd + 1];
+  }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, sm_m[c]);
+  float L = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < nchunks; ++c) {
+    const float m = sm_m[c];
+    const float f = m == -INFINITY ? 0.f : expf(m - M);
+    L += sm_l[c] * f;
+    O += base[c * stride + d] * f;
+  }
+  op_st<BF>(out, out_lo, ((size_t)s * R + r) * a.nq * hd + (size_t)h * hd + d, O / L);
 }
 
 // ---- live window read-back (parity checks) -----------------------------------------------
@@ -858,6 +923,50 @@ hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, 
   if (bf) hipLaunchKernelGGL(attn_combine_kernel<true>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
   else hipLaunchKernelGGL(attn_combine_kernel<false>, dim3(R * a.nq), dim3(a.hd), 0, s, a, part, R, nch, out, out_lo);
   return hipGetLastError();
+}
+
+hipError_t launch_block_attention_batch(int bf, const AttnShape& a, const AttnSeqs& seqs, const float* qkv,
+                                        const void* qnorm, const void* knorm, const float2* rope, void* ring0,
+                                        size_t ring_seq_bytes, int R, void* qb, void* qlo, float* part, void* out,
+                                        void* out_lo, hipStream_t s) {
+  if (seqs.n < 1 || seqs.n > ATTN_MAX_SEQS || R < 1) return hipErrorInvalidValue;
+  const size_t elt = bf ? 2 : 4;
+  if (!use_mfma(bf, a)) {  // f32 shapes: one launch pair per sequence
+    const size_t ldq = (size_t)(a.nq + 2 * a.nkv) * a.hd, op_row = (size_t)a.nq * a.hd * elt;
+    for (int q = 0; q < seqs.n; ++q) {
+      const size_t r0 = (size_t)q * R;
+      const hipError_t err = launch_block_attention(
+          bf, a, qkv + r0 * ldq, qnorm, knorm, rope ? rope + r0 * (a.hd / 2) : nullptr,
+          (unsigned char*)ring0 + (size_t)q * ring_seq_bytes, R, 0, seqs.e[q], (unsigned char*)qb + r0 * op_row,
+          qlo ? (unsigned char*)qlo + r0 * op_row : nullptr, part, (unsigned char*)out + r0 * op_row,
+          out_lo ? (unsigned char*)out_lo + r0 * op_row : nullptr, s);
+      if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
+  if (!rope || ring_seq_bytes % 2) return hipErrorInvalidValue;
+  int nch_max = 1;
+  for (int q = 0; q < seqs.n; ++q) {
+    const int nch = attn_nchunks(a, R, seqs.e[q]);
+    if (nch > COMBINE_MAX_CHUNKS || seqs.e[q] < 1) return hipErrorInvalidValue;
+    nch_max = nch > nch_max ? nch : nch_max;
+  }
+  const size_t part_seq = (size_t)a.nkv * nch_max * R * (a.nq / a.nkv) * PART_STRIDE(a.hd);
+  const int nqt = (R * (a.nq / a.nkv) + 15) / 16;
+  const int zq = (nqt + 3) / 4, tpw = (nqt + zq - 1) / zq;
+  const dim3 grid(nch_max, a.nkv, zq * seqs.n);
+  auto* fn = a.hd == 128 ? attn_mfma_batch_kernel<128, 4> : attn_mfma_batch_kernel<64, 4>;
+  hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, a, seqs, (uint16_t*)ring0, ring_seq_bytes / 2, qkv,
+                     (const uint16_t*)qnorm, (const uint16_t*)knorm, rope, R, zq, tpw, part_seq, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(attn_combine_batch_kernel<true>, dim3(seqs.n * R * a.nq), dim3(a.hd), 0, s, a, seqs, part,
+                     part_seq, R, out, out_lo);
+  return hipGetLastError();
+}
+
+size_t attention_partial_floats_batch(const AttnShape& a, int R, int n_seq) {
+  return (size_t)n_seq * attention_partial_floats(a, R);
 }
 
 hipError_t launch_cache_read(int bf, const AttnShape& a, const void* ring_layer, int64_t lo, int n, void* kout,

@@ -1393,8 +1393,9 @@ dflash_status dflash_target_cache_read(dflash_target* t, int32_t layer, void* k_
 // Independent sequences drafted together (dflash_batch_*): one engine (packed weights,
 // workspace sized for every sequence's block) and one ring per sequence. Every GEMM of a
 // round runs once over the rows of all sequences, so each weight byte is read once per
-// round for the whole batch; embedding, attention, the final norm and the ring writes run
-// per sequence, on its own positions and ring; verify runs one wave per sequence.
+// round for the whole batch; the embedding, attention (bf16 MFMA shapes), final norm and
+// verify also take every sequence in one launch, each on its own positions and ring; the
+// ring writes of appended rows run per sequence.
 // ======================================================================================
 struct dflash_batch {
   dflash_ctx core;  // the engine; core.ring is sequence 0's ring, core.e/pending are unused
@@ -1599,28 +1600,27 @@ dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_
   float* part = (float*)(ctx->ws + ctx->lay.part);
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * hd;
-  const size_t op_row = (size_t)qd * g.act_elt;  // bytes of one row of an operand plane
-  dflash_status s = DFLASH_OK;
-  for (int q = 0; q < S && s == DFLASH_OK; ++q)
-    s = dev(ctx,
-            launch_embed(g.bf, ctx->embed, H, c.vocab, anchors[q], c.mask_token_id, nullptr, R1, 0, nullptr,
-                         x + (size_t)q * R1 * H, rope + (size_t)q * R1 * (hd / 2), b->e[q], c.rope_theta, hd, st),
-            "embed");
+  EmbedSeqs es{};
+  AttnSeqs as{};
+  es.n = as.n = S;
+  for (int q = 0; q < S; ++q) {
+    es.anchor[q] = anchors[q];
+    es.pos0[q] = as.e[q] = b->e[q];
+  }
+  dflash_status s = dev(ctx,
+                        launch_embed_batch(g.bf, ctx->embed, H, es, R1, c.mask_token_id, x, rope, c.rope_theta, hd, st),
+                        "embed");
   for (int l = 0; l < c.layers && s == DFLASH_OK; ++l) {
     const Layer& L = ctx->layers[l];
     GemmCall qc{EPI_STORE, XSRC_NORM, {seg(L.q, 0, qd), seg(L.k, qd, kvd), seg(L.v, qd + kvd, kvd)}, H, x, H,
                 L.in_norm, qkv, qd + 2 * kvd, nullptr};
     qc.split = g.bf;
     if ((s = run_gemm(ctx, qc, rows, st)) != DFLASH_OK) return s;
-    for (int q = 0; q < S && s == DFLASH_OK; ++q) {
-      const size_t r0 = (size_t)q * R1;
-      s = dev(ctx,
-              launch_block_attention(g.bf, g.a, qkv + r0 * (qd + 2 * kvd), L.q_norm, L.k_norm, rope + r0 * (hd / 2),
-                                     seq_ring(b, q) + l * ring_layer, R1, 0, b->e[q], qb + r0 * op_row,
-                                     g.bf ? qb_lo + r0 * op_row : nullptr, part, attn + r0 * op_row,
-                                     g.bf ? attn_lo + r0 * op_row : nullptr, st),
-              "attention");
-    }
+    s = dev(ctx,
+            launch_block_attention_batch(g.bf, g.a, as, qkv, L.q_norm, L.k_norm, rope, ctx->ring + l * ring_layer,
+                                         b->ring_seq, R1, qb, g.bf ? qb_lo : nullptr, part, attn,
+                                         g.bf ? attn_lo : nullptr, st),
+            "attention");
     if (s != DFLASH_OK) return s;
     GemmCall o{EPI_RESID, XSRC_GLOBAL, {seg(L.o, 0, H)}, qd, attn, qd, nullptr, x, H, nullptr};
     o.split = g.bf;
@@ -1646,13 +1646,8 @@ dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_
   // lm_head argmax over all of them: d_tokens [n_seq][block]
   void* zrows = ctx->ws + ctx->lay.zrows;
   void* zrows_lo = lo_plane(g, zrows, S * block, H);
-  const size_t z_row = (size_t)H * (g.bf ? 2 : 4);
-  for (int q = 0; q < S && s == DFLASH_OK; ++q)
-    s = dev(ctx,
-            launch_rownorm(g.bf, x + ((size_t)q * R1 + 1) * H, ctx->final_norm, c.rms_eps, block, H,
-                           (unsigned char*)zrows + (size_t)q * block * z_row,
-                           g.bf ? (unsigned char*)zrows_lo + (size_t)q * block * z_row : nullptr, st),
-            "final norm");
+  s = dev(ctx, launch_rownorm(g.bf, x, ctx->final_norm, c.rms_eps, S * block, H, zrows, zrows_lo, st, block),
+          "final norm");
   if (s != DFLASH_OK) return s;
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
   lm.split = g.bf;

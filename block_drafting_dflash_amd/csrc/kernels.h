@@ -203,9 +203,10 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int vocab, int32_t anchor, int32_t mask_id,
                         const int32_t* toks, int R, int nprev, const float* prev, float* x, float2* rope, int64_t pos0,
                         float theta, int hd, hipStream_t s);
-// RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
+// RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out. skip_every =
+// B > 0 reads rows 1..B of each group of B + 1 input rows (a batch's proposing rows).
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          void* out_lo, hipStream_t s);
+                          void* out_lo, hipStream_t s, int skip_every = 0);
 hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
                              int n, int64_t pos0, void* ring, hipStream_t s);
 // Attention side of one layer of the block forward: q/k RMSNorm + RoPE of the R block rows
@@ -220,6 +221,32 @@ hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, 
 hipError_t launch_block_attention(int act_bf16, const AttnShape& a, const float* qkv, const void* qnorm,
                                   const void* knorm, const float2* rope, void* ring_layer, int R, int n, int64_t e,
                                   void* qb, void* qlo, float* part, void* out, void* out_lo, hipStream_t s);
+// Committed ends of the sequences of a batch round, passed by value.
+constexpr int ATTN_MAX_SEQS = 64;
+struct AttnSeqs {
+  int32_t n;
+  int64_t e[ATTN_MAX_SEQS];
+};
+// Anchors and first positions of a batch round's sequences, passed by value.
+struct EmbedSeqs {
+  int32_t n;
+  int32_t anchor[ATTN_MAX_SEQS];
+  int64_t pos0[ATTN_MAX_SEQS];
+};
+// launch_embed for a batch: rows [anchor_q, mask x (R1 - 1)] of every sequence, sequence
+// after sequence, at positions pos0_q.., with their rotary table (required).
+hipError_t launch_embed_batch(int act_bf16, const void* table, int hidden, const EmbedSeqs& seqs, int R1,
+                              int32_t mask_id, float* x, float2* rope, float theta, int hd, hipStream_t s);
+// launch_block_attention for n sequences at once (no committed rows): sequence s's R rows of
+// raw projections and of the rotary table follow s - 1's, its ring sits ring_seq_bytes after
+// s - 1's, and its output rows follow s - 1's in out/out_lo; part holds
+// attention_partial_floats_batch floats. bf16 MFMA shapes run one launch pair for all
+// sequences, other shapes one per sequence.
+hipError_t launch_block_attention_batch(int act_bf16, const AttnShape& a, const AttnSeqs& seqs, const float* qkv,
+                                        const void* qnorm, const void* knorm, const float2* rope, void* ring0,
+                                        size_t ring_seq_bytes, int R, void* qb, void* qlo, float* part, void* out,
+                                        void* out_lo, hipStream_t s);
+size_t attention_partial_floats_batch(const AttnShape& a, int R, int n_seq);
 // whether launch_block_attention takes committed rows (n > 0) for this shape
 bool attention_forms_committed_rows(int act_bf16, const AttnShape& a);
 size_t attention_partial_floats(const AttnShape& a, int R);

@@ -41,40 +41,10 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
   return hipGetLastError();
 }
 
-// Block rows [anchor, mask x (R-1)] from the target's raw embedding table (not the
-// embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows: work-group
-// (r, 0) gathers row r, with 16-byte loads when the table is 16-byte aligned (every row
-// then is: hidden is a multiple of 16). The draft's first kernel also tabulates the rotary
-// rotation of every block position pos0 + r in work-group (r, 1): (cos, sin) of (pos0 + r) *
-// theta^(-2i/hd) for i < hd/2, evaluated in f64 and rounded to f32 as the per-element RoPE
-// of the prep kernel does; every layer's attention reads it (rope may be NULL).
+// one embedding row (gathered from the table in its storage dtype) as f32: 16-byte loads
+// when the table is 16-byte aligned (every row then is: hidden is a multiple of 16)
 template <bool BF, bool VEC>
-__global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int vocab, int32_t anchor,
-                                                    int32_t mask_id, const int32_t* toks, int R, int nprev,
-                                                    const float* prev, float* x, float2* rope, int64_t pos0,
-                                                    float theta, int hd) {
-  const int r = blockIdx.x;
-  if (blockIdx.y == 1) {
-    const int64_t pos = r < R ? pos0 + r : pos0 - nprev + (r - R);
-    for (int i = threadIdx.x; i < hd / 2; i += blockDim.x) {
-      const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
-      double sn, cs;
-      sincos((double)pos * inv, &sn, &cs);
-      rope[(size_t)r * (hd / 2) + i] = make_float2((float)cs, (float)sn);
-    }
-    return;
-  }
-  if (r >= R) {  // rows carried behind the embedded ones
-    const float4* src = (const float4*)(prev + (size_t)(r - R) * hidden);
-    float4* dst = (float4*)(x + (size_t)r * hidden);
-    for (int v = threadIdx.x; v < hidden / 4; v += blockDim.x) dst[v] = src[v];
-    return;
-  }
-  // block tokens from device memory (a target's verify rows) are clamped into the table: an
-  // id past the last row would read whatever follows the table (lablup/mlxcel #1751, Review
-  // fixes); the verify kernel reports out-of-range ids in its status word
-  const int64_t tok = r == 0 ? anchor : (toks ? (int64_t)min(max(toks[r - 1], 0), vocab - 1) : mask_id);
-  float* xr = x + (size_t)r * hidden;
+__device__ __forceinline__ void embed_row(const void* table, int hidden, int64_t tok, float* xr) {
   if constexpr (VEC) {
     constexpr int EPV = BF ? 8 : 4;  // elements per 16-byte load
     constexpr int U = 4;             // loads in flight per thread
@@ -104,6 +74,59 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidde
   }
 }
 
+// the rotary rotation of position pos: (cos, sin) of pos * theta^(-2i/hd) for i < hd/2,
+// evaluated in f64 and rounded to f32 as the per-element RoPE of the prep kernel does
+__device__ __forceinline__ void rope_row(int64_t pos, float theta, int hd, float2* dst) {
+  for (int i = threadIdx.x; i < hd / 2; i += blockDim.x) {
+    const double inv = pow((double)theta, -2.0 * (double)i / (double)hd);
+    double sn, cs;
+    sincos((double)pos * inv, &sn, &cs);
+    dst[i] = make_float2((float)cs, (float)sn);
+  }
+}
+
+// Block rows [anchor, mask x (R-1)] from the target's raw embedding table (not the
+// embed_norm lookup: lablup/mlxcel #1762, What changed), as f32 residual rows: work-group
+// (r, 0) gathers row r. The draft's first kernel also tabulates the rotary rotation of
+// every block position pos0 + r in work-group (r, 1); every layer's attention reads it
+// (rope may be NULL).
+template <bool BF, bool VEC>
+__global__ __launch_bounds__(256) void embed_kernel(const void* table, int hidden, int vocab, int32_t anchor,
+                                                    int32_t mask_id, const int32_t* toks, int R, int nprev,
+                                                    const float* prev, float* x, float2* rope, int64_t pos0,
+                                                    float theta, int hd) {
+  const int r = blockIdx.x;
+  if (blockIdx.y == 1) {
+    rope_row(r < R ? pos0 + r : pos0 - nprev + (r - R), theta, hd, rope + (size_t)r * (hd / 2));
+    return;
+  }
+  if (r >= R) {  // rows carried behind the embedded ones
+    const float4* src = (const float4*)(prev + (size_t)(r - R) * hidden);
+    float4* dst = (float4*)(x + (size_t)r * hidden);
+    for (int v = threadIdx.x; v < hidden / 4; v += blockDim.x) dst[v] = src[v];
+    return;
+  }
+  // block tokens from device memory (a target's verify rows) are clamped into the table: an
+  // id past the last row would read whatever follows the table (lablup/mlxcel #1751, Review
+  // fixes); the verify kernel reports out-of-range ids in its status word
+  const int64_t tok = r == 0 ? anchor : (toks ? (int64_t)min(max(toks[r - 1], 0), vocab - 1) : mask_id);
+  embed_row<BF, VEC>(table, hidden, tok, x + (size_t)r * hidden);
+}
+
+// Rows [anchor_q, mask x (R1 - 1)] of every sequence q of a batch, sequence after sequence,
+// at positions pos0_q + j, with their rotary table (work-group (r, 1)).
+template <bool BF, bool VEC>
+__global__ __launch_bounds__(256) void embed_batch_kernel(const void* table, int hidden, EmbedSeqs seqs, int R1,
+                                                          int32_t mask_id, float* x, float2* rope, float theta,
+                                                          int hd) {
+  const int r = blockIdx.x, q = r / R1, j = r - q * R1;
+  if (blockIdx.y == 1) {
+    rope_row(seqs.pos0[q] + j, theta, hd, rope + (size_t)r * (hd / 2));
+    return;
+  }
+  embed_row<BF, VEC>(table, hidden, j == 0 ? seqs.anchor[q] : mask_id, x + (size_t)r * hidden);
+}
+
 hipError_t launch_embed(int bf, const void* table, int hidden, int vocab, int32_t anchor, int32_t mask_id,
                         const int32_t* toks, int R, int nprev, const float* prev, float* x, float2* rope, int64_t pos0,
                         float theta, int hd, hipStream_t s) {
@@ -126,6 +149,26 @@ hipError_t launch_embed(int bf, const void* table, int hidden, int vocab, int32_
   return hipGetLastError();
 }
 
+hipError_t launch_embed_batch(int bf, const void* table, int hidden, const EmbedSeqs& seqs, int R1, int32_t mask_id,
+                              float* x, float2* rope, float theta, int hd, hipStream_t s) {
+  if (seqs.n < 1 || seqs.n > ATTN_MAX_SEQS || R1 < 1 || !rope) return hipErrorInvalidValue;
+  const bool vec = ((uintptr_t)table & 15u) == 0 && hidden % 8 == 0;
+  const dim3 grid(seqs.n * R1, 2);
+  if (bf && vec)
+    hipLaunchKernelGGL((embed_batch_kernel<true, true>), grid, dim3(256), 0, s, table, hidden, seqs, R1, mask_id, x, rope,
+                       theta, hd);
+  else if (bf)
+    hipLaunchKernelGGL((embed_batch_kernel<true, false>), grid, dim3(256), 0, s, table, hidden, seqs, R1, mask_id, x,
+                       rope, theta, hd);
+  else if (vec)
+    hipLaunchKernelGGL((embed_batch_kernel<false, true>), grid, dim3(256), 0, s, table, hidden, seqs, R1, mask_id, x,
+                       rope, theta, hd);
+  else
+    hipLaunchKernelGGL((embed_batch_kernel<false, false>), grid, dim3(256), 0, s, table, hidden, seqs, R1, mask_id, x,
+                       rope, theta, hd);
+  return hipGetLastError();
+}
+
 // out[r] = RMSNorm(in[r]) * g as a GEMM operand (hi/lo bf16 planes for bf16 shapes, f32
 // otherwise); one 256-thread group per row. Each thread holds its first RN_V groups of four
 // values in registers (rows up to 4096 wide: one read), accumulates their squares, and the
@@ -133,11 +176,14 @@ hipError_t launch_embed(int bf, const void* table, int hidden, int vocab, int32_
 constexpr int RN_V = 4;
 template <bool BF>
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ in, const void* gain, float eps, int H,
-                                                      void* out, void* out_lo) {
+                                                      void* out, void* out_lo, int skip_every) {
   __shared__ float part[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nv = H / 4;  // H is a multiple of 16
-  const float4* x = (const float4*)(in + (size_t)r * H);
+  // skip_every = B > 0: output row r reads input row (r / B) (B + 1) + 1 + r % B (rows 1..B of
+  // each sequence's B + 1)
+  const int ri = skip_every > 0 ? (r / skip_every) * (skip_every + 1) + 1 + r % skip_every : r;
+  const float4* x = (const float4*)(in + (size_t)ri * H);
   float4 xv[RN_V];
   float gv[RN_V][4];
   auto load_gain = [&](int v, float (&g)[4]) {
@@ -194,10 +240,10 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          void* out_lo, hipStream_t s) {
-  if (H % 16) return hipErrorInvalidValue;
-  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
-  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
+                          void* out_lo, hipStream_t s, int skip_every) {
+  if (H % 16 || skip_every < 0) return hipErrorInvalidValue;
+  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo, skip_every);
+  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo, skip_every);
   return hipGetLastError();
 }
 
