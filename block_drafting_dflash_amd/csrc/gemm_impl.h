@@ -536,12 +536,15 @@ gemm_kernel(const GemmParams p) {
       const int col = FOLD ? 8 * j + li : 16 * j + li;
       if constexpr (EPI == EPI_ARGMAX) {
         // each lane keeps the best key of its own columns over the tiles; the 16 columns of
-        // a row are reduced once, after the last tile (max is exact and order-free)
+        // a row are reduced once, after the last tile (max is exact and order-free). With
+        // p.y the f32 logits are stored as well (a DSpark block's rows, which its Markov
+        // chain scores)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rt * 16 + 4 * lg + q;
           const unsigned long long key = (r < R) ? argmax_key(v[0][q], col) : 0ull;
           best[q] = key > best[q] ? key : best[q];
+          if (p.y && r < R) ((float*)p.y)[(size_t)r * p.ldy + col] = v[0][q];
         }
       } else {
 #pragma unroll

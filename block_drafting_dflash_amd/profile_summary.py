@@ -40,7 +40,9 @@ def read_csv(path: Optional[str]) -> List[dict]:
         return list(csv.DictReader(f))
 
 
-def gemm_role(name: str) -> Optional[str]:
+def gemm_role(name: str, wgs: int = 0) -> Optional[str]:
+    """The GEMM's role from its template arguments (wgs: its work-groups, which tell the
+    DSpark lm_head's logit store from the projections that share its arguments)."""
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (true|false)>", name)
     if not m:
         return None
@@ -57,6 +59,8 @@ def gemm_role(name: str) -> Optional[str]:
         return "QKV or K/V projection"
     if epi == 0 and xsrc == 0 and k_per_wave * 8 == F:
         return "fc"
+    if epi == 0 and xsrc == 0 and wgs >= V // 16:
+        return "lm_head"  # every row's logits stored (DSpark)
     if epi == 0 and xsrc == 0:
         return "QKV or K/V projection"  # normed rows streamed from planes (long blocks)
     return None
@@ -76,12 +80,12 @@ def split_legs(rows: List[dict]) -> List[List[dict]]:
     in_pack = False
     started = False
     for r in rows:
-        is_pack = "pack_kernel" in r["Kernel_Name"] or "pack_q4_kernel" in r["Kernel_Name"]
+        is_pack = any(k in r["Kernel_Name"] for k in ("pack_kernel", "pack_q4_kernel", "deinterleave_kernel"))
         if is_pack and not in_pack:
             legs.append([])
             started = False
         in_pack = is_pack
-        started = started or "embed_kernel" in r["Kernel_Name"]
+        started = started or re.search(r"embed(_batch)?_kernel", r["Kernel_Name"]) is not None
         if legs and started:
             legs[-1].append(r)
     return legs
@@ -160,14 +164,24 @@ def summarize(args) -> str:
                      "(fetch+write) | counted/alg | MfmaUtil % | VALUBusy % | MFMA inst | VALU inst |")
         lines.append("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
         per: Dict[str, List[float]] = collections.defaultdict(list)
+        wgs: Dict[str, int] = {}
         for r in leg:
             per[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            try:
+                wgs[r["Kernel_Name"]] = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            except (KeyError, ValueError):
+                wgs[r["Kernel_Name"]] = 0
         total = sum(sum(v) for v in per.values())
         rows = []
         for k, ds in per.items():
-            role = gemm_role(k)
+            role = gemm_role(k, wgs.get(k, 0))
             alg = ELEMS[role] * (9 / 16 if short(k).startswith("gemm_kernel<2") else 2) if role else None
-            if "attn_mfma" in k:
+            mk = re.search(r"markov_step_kernel<(true|false), (\d+)>", k)
+            if mk:  # markov_w2 [V, rank] once plus one f32 logit row
+                role, alg = "Markov chain step", V * int(mk.group(2)) * (2 if mk.group(1) == "true" else 4) + V * 4
+            if "attn_mfma_batch" in k:
+                role, alg = "attention (every sequence of a batch)", None
+            elif "attn_mfma" in k:
                 kv = [int(x) for x in str(args.kv_rows).split(",")]
                 role, alg = "attention (live K/V of one layer)", kv[min(li, len(kv) - 1)] * KVD * 2 * 2
             med = statistics.median(ds)

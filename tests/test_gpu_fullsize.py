@@ -214,3 +214,31 @@ def test_dspark_w8_w10_ctx1024_lm_head_verify(muse, gamma):
     ks = P.run_lm_head_rounds(ls, wl.context, gamma, 6, anchor_tag=gamma)
     _report(f"{wl.name} gamma {gamma}", ls, ks)
     assert ls.stats.rows_checked == 6 * (gamma + gamma + 1)
+
+
+def test_batch_of_four_ctx1024_lm_head_verify(muse):
+    """Four independent Muse-shaped sequences drafted together at block 4 (20 rows per GEMM:
+    the normed operands go through the row-norm planes), after contexts of 1024, 1000, 977 and
+    1031 rows; verify rows through the shared lm_head; each sequence in lock-step with its
+    own copy of the oracle (tokens, hidden rows, verify result, offsets, live windows)."""
+    from tests.test_gpu_batch import BatchLockStep
+
+    w64, dev = muse
+    n, B = 4, 4
+    ls = BatchLockStep(SH, w64, n, B, dev=dev)
+    ls.append([synth.resid_rows(SH, c, 40 + s) for s, c in enumerate((1024, 1000, 977, 1031))], commit=True)
+    anchors = [synth.anchor_token(SH, tag=60 + s) for s in range(n)]
+    for r in range(4):
+        d = ls.draft(anchors, B)
+        rows = np.concatenate([synth.verify_hidden(SH, B + 1, 700 + 10 * r + s) for s in range(n)])
+        a_gpu = ls.gpu.lm_head_argmax(ls._t(rows)).cpu().numpy().reshape(n, B + 1)
+        a = []
+        for s in range(n):
+            oi, om = ls.orc.seqs[s].lm_head_argmax(rows[s * (B + 1):(s + 1) * (B + 1)])
+            ls._agree(a_gpu[s], oi, om, f"sequence {s} verify argmax")
+            a.append(oi)
+        res = ls.verify(d, np.stack(a), B)
+        ls.append([synth.resid_rows(SH, B + 1, 800 + 10 * r + s) for s in range(n)])
+        ls.trim([B - k for k, _ in res])
+        anchors = [bonus for _, bonus in res]
+    print("batch of four: near ties", ls.near_ties)
