@@ -113,11 +113,12 @@ def run_batch_rounds(ls, contexts, B, rounds, tag):
 
 
 @pytest.mark.parametrize("kind,n,B,phase", [("bf16", 3, 4, 0), ("bf16", 5, 4, 8), ("bf16", 8, 7, 0), ("f32", 2, 3, 16),
-                                            ("bf16", 1, 16, 0)])
+                                            ("bf16", 1, 16, 0), ("q4", 4, 4, 24)])
 def test_batch_rounds_match_oracle(kind, n, B, phase):
     """Ragged prefills and accept lengths; 15, 25 and 64 rows per GEMM (one launch with the
-    norm staged in LDS, one through the row-norm planes, two launches), f32, one sequence."""
-    sh = MICRO_BF16 if kind == "bf16" else MICRO_F32
+    norm staged in LDS, one through the row-norm planes, two launches), f32, one sequence,
+    4-bit weights."""
+    sh = {"bf16": MICRO_BF16, "f32": MICRO_F32, "q4": MICRO_BF16.with_(weight_dtype="q4")}[kind]
     w = synth.make_weights(sh)
     ls = BatchLockStep(sh, w, n, B, phase)
     contexts = [7 + 13 * s for s in range(n)]

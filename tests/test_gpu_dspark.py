@@ -67,11 +67,13 @@ def run_varying_rounds(ls, context, max_block, rounds, tag):
     return ks
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_dspark_rounds_match_oracle(name):
+@pytest.mark.parametrize("name,phase", [(n, 0) for n in CASES] + [("bf16-r256-trad", 208), ("f32-r64-trad", 168)])
+def test_dspark_rounds_match_oracle(name, phase):
+    """Every case at ring phase 0; two with a phase that puts the ring's wrap point inside the
+    rounds' positions."""
     sh = CASES[name]
-    ls = P.LockStep(sh, weights(name), max_block=9)
-    ks = run_varying_rounds(ls, 37, 9, 10, tag=len(name))
+    ls = P.LockStep(sh, weights(name), max_block=9, phase=phase)
+    ks = run_varying_rounds(ls, 37, 9, 10, tag=len(name) + phase)
     print(name, "stats", ls.stats, "ks", ks)
     assert ls.stats.rows_checked > 0
 
