@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -192,14 +193,21 @@ dflash_status check_cfg(const dflash_config* c, Cfg* out, char* err) {
   } else if (c->markov_rank != 0) {
     return cfg_fail(err, DFLASH_E_ARG, "markov_rank is for DSpark contexts only");
   }
-  // every extent and element count handed to a kernel fits an int32
+  // every extent and element count handed to a kernel fits an int32; the products are
+  // bounded factor by factor (every factor is positive and below 2^31 + 512), so that no
+  // partial product can pass the int64 range either
   const int64_t qd = (int64_t)c->q_heads * c->head_dim, kvd = (int64_t)c->kv_heads * c->head_dim;
   const int64_t fin = (int64_t)c->target_streams * c->target_width;
   const int64_t H = c->hidden;
-  const int64_t products[] = {qd, kvd, fin, H * c->vocab, H * c->intermediate, H * fin, H * qd,
-                              (int64_t)c->layers * 2 * kvd * (c->window + 128 + c->max_block + 72)};
-  for (int64_t v : products)
-    if (v > INT32_MAX) return cfg_fail(err, DFLASH_E_SHAPE, "a dimension product would wrap an int32");
+  const int64_t slots = (int64_t)c->window + 128 + c->max_block + 72;
+  const std::initializer_list<int64_t> products[] = {
+      {qd}, {kvd}, {fin}, {H, c->vocab}, {H, c->intermediate}, {H, fin}, {H, qd}, {c->layers, 2, kvd, slots}};
+  for (const auto& f : products) {
+    int64_t v = 1;
+    for (int64_t x : f)
+      if (x > INT32_MAX || (v *= x) > INT32_MAX)
+        return cfg_fail(err, DFLASH_E_SHAPE, "a dimension product would wrap an int32");
+  }
   const int unit = chunk_steps(1) * kstep(wt);
   const int64_t ks[] = {H, c->intermediate, qd, fin};
   for (int64_t k : ks)
