@@ -87,7 +87,7 @@ __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __r
 #pragma unroll
     for (int j = 0; j < MK_LOADS; ++j) {
       const int row = min(r0 + j * RPL, vocab - 1);
-      v[j] = __builtin_nontemporal_load(w2 + (size_t)row * SLICES + sub);
+      v[j] = w2[(size_t)row * SLICES + sub];
       lg[j] = logits[row];
     }
   };
