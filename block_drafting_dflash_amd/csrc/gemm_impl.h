@@ -56,10 +56,13 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // Eight reordered 4-bit codes -> the bf16 values 128 + q in MFMA operand order (element
 // 2e in the low half of word e): bf16 0x4300 is 128 and its 7 mantissa bits count units.
-__device__ __forceinline__ u32x4_t q4_expand(uint32_t w) {
+// m = 0x000F000F and c = 0x43004300 come in as register values the compiler cannot see
+// through (the kernel hides them once): with literal constants it emits an AND and an OR
+// per word (gfx9 three-operand encodings take no literal), with registers one AND-OR.
+__device__ __forceinline__ u32x4_t q4_expand(uint32_t w, uint32_t m, uint32_t c) {
   u32x4_t f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) f[e] = ((w >> (4 * e)) & 0x000F000Fu) | 0x43004300u;
+  for (int e = 0; e < 4; ++e) f[e] = ((w >> (4 * e)) & m) | c;
   return f;
 }
 
@@ -173,6 +176,12 @@ gemm_kernel(const GemmParams p) {
   constexpr int CB = Q4 ? CH / 4 : 1;  // 128-k code blocks per chunk
   static_assert(!Q4 || CH % 4 == 0, "a q4 chunk is whole code blocks");
   const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  // q4_expand's mask (a scalar register) and bf16 128 pair (a vector register), opaque
+  uint32_t q4m = 0x000F000Fu, q4c = 0x43004300u;
+  if constexpr (Q4) {
+    asm volatile("" : "+s"(q4m));
+    asm volatile("" : "+v"(q4c));
+  }
   static_assert(!(BF && XSRC == XSRC_NORM && !SPLIT), "a normed bf16 operand is always a hi/lo pair");
   constexpr int SR = SPLIT ? RT : 1;  // row tiles of lo fragments held (1 = unused)
   constexpr int NIT = T * NCH;
@@ -408,7 +417,7 @@ gemm_kernel(const GemmParams p) {
             const int t = 2 * g2 + tt, st = 4 * b + t;
             u32x4_t fr[NB];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) fr[nb] = q4_expand(wb[nb][b][t]);
+            for (int nb = 0; nb < NB; ++nb) fr[nb] = q4_expand(wb[nb][b][t], q4m, q4c);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
               u32x4_t xf, xl;
