@@ -10,7 +10,7 @@ emits its accepted tokens plus one bonus token.
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List
+from typing import Dict
 
 
 @dataclasses.dataclass

@@ -877,8 +877,6 @@ size_t attention_partial_floats_span(const AttnShape& a, int R, int span) {
 
 size_t attention_partial_floats(const AttnShape& a, int R) { return attention_partial_floats_span(a, R, a.window); }
 
-int attention_max_chunks() { return COMBINE_MAX_CHUNKS; }
-
 bool attention_forms_committed_rows(int bf, const AttnShape& a) { return use_mfma(bf, a); }
 
 hipError_t launch_block_attention(int bf, const AttnShape& a, const float* qkv, const void* qnorm, const void* knorm,

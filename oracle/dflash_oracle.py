@@ -52,7 +52,7 @@ What the round computes (readings where the pages are silent are marked READING)
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional, Tuple
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 

@@ -17,7 +17,7 @@ oracle's to about 1e-6, use 1e-4.
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional
+from typing import List
 
 import numpy as np
 import torch

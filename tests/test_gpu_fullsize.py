@@ -154,7 +154,6 @@ def test_muse_target_rounds_match_oracles(muse_pair):
     verify argmaxes and captured streams, the drafter's tokens and hidden rows, the verify
     result and both caches' offsets in lock-step with the oracles; every target cache window
     and the drafter's live window at the end."""
-    from oracle.target_oracle import OracleTarget
     from tests.test_gpu_target import TargetLockStep
 
     t, dsh, dw64, tw64, ddev, tdev = muse_pair

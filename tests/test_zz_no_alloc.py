@@ -2,7 +2,6 @@
 dflash_lm_head_argmax (keys in the context's workspace), through the C-ABI: the indices are
 bit-identical, over two calls in a row whose second takes fewer rows, on bf16, 4-bit and f32
 shapes; argument errors are refused before anything is enqueued."""
-import numpy as np
 import pytest
 import torch
 
