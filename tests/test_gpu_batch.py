@@ -126,6 +126,16 @@ def test_batch_rounds_match_oracle(kind, n, B, phase):
     print(kind, n, B, "near ties", ls.near_ties, "ks", ks)
 
 
+def test_batch_at_its_limits():
+    """64 sequences (the most a batch takes) at block 7: 512 rows per GEMM, the row limit,
+    with ragged contexts from a few rows to far past the window and ragged accept lengths."""
+    sh, n, B = MICRO_BF16, 64, 7
+    ls = BatchLockStep(sh, synth.make_weights(sh), n, B, phase=8)
+    contexts = [1 + 5 * s for s in range(n)]
+    ks = run_batch_rounds(ls, contexts, B, 3, tag=64)
+    print("64 sequences: near ties", ls.near_ties, "ks", ks)
+
+
 def test_batch_equals_single_contexts_bit_for_bit():
     sh = MICRO_BF16
     w = synth.make_weights(sh)

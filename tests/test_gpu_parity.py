@@ -402,6 +402,29 @@ def test_micro_bf16_block129_deepest_rewind(micro_bf16_w):
     print("block 129 stats", ls.stats)
 
 
+def test_micro_bf16_block256_widest_block(micro_bf16_w):
+    """Block 256, the widest a context takes: 257 draft rows (nine row launches per GEMM, the
+    normed operands through the row-norm planes, 65 query tiles per kv head, eight argmax
+    launches of 32 rows), slack 256; rounds that accept nothing, everything and a few rows,
+    with the live window read back after every trim."""
+    sh, B = MICRO_BF16, 256
+    ls = P.LockStep(sh, micro_bf16_w, max_block=B, phase=16)
+    assert ls.gpu.cache_state()[2] == B
+    ls.append(synth.resid_rows(sh, 33, 0), commit=True)
+    torch.cuda.synchronize()
+    ls.check_window()
+    anchor = synth.anchor_token(sh, tag=256)
+    for r, kk in enumerate([0, B, 17]):
+        d = ls.draft(anchor, B)
+        a = P.target_with_accept_length(d, kk, sh.vocab, tail=anchor + r)
+        k, bonus = ls.verify(d, a)
+        assert k == kk
+        ls.append(synth.resid_rows(sh, B + 1, 900 + r))
+        ls.trim(B - k)
+        anchor = bonus
+    print("block 256 stats", ls.stats)
+
+
 @pytest.mark.parametrize("p,widens", [(0.95, True), (0.3, False)])
 def test_adaptive_width_rounds_match_oracle(micro_bf16_w, p, widens):
     """Rounds whose block the library's width controller picks (depth 4, ceiling 16, windows of
