@@ -425,6 +425,30 @@ def test_micro_bf16_block256_widest_block(micro_bf16_w):
     print("block 256 stats", ls.stats)
 
 
+def test_micro_bf16_widest_window(micro_bf16_w):
+    """Window 4096, the widest a context takes, full after a 4400-row prefill (the rows before
+    the window dropped ahead of the encoder): a query's keys span 66-67 chunks of 64, so the
+    combine merges the most partials it takes; block 16, rounds of random accept length with
+    the whole live window read back after every trim, across the ring's wrap point."""
+    sh, B = MICRO_BF16.with_(window=4096), 16
+    ls = P.LockStep(sh, micro_bf16_w, max_block=B, phase=4000)
+    ls.append(synth.resid_rows(sh, 4400, 0), commit=True)
+    torch.cuda.synchronize()
+    ls.check_window()
+    anchor = synth.anchor_token(sh, tag=4096)
+    rng = np.random.default_rng(4096)
+    for r in range(3):
+        d = ls.draft(anchor, B)
+        kk = int(rng.integers(0, B + 1))
+        a = P.target_with_accept_length(d, kk, sh.vocab, tail=anchor + r)
+        k, bonus = ls.verify(d, a)
+        assert k == kk
+        ls.append(synth.resid_rows(sh, B + 1, 4500 + r))
+        ls.trim(B - k)
+        anchor = bonus
+    print("window 4096 stats", ls.stats)
+
+
 @pytest.mark.parametrize("p,widens", [(0.95, True), (0.3, False)])
 def test_adaptive_width_rounds_match_oracle(micro_bf16_w, p, widens):
     """Rounds whose block the library's width controller picks (depth 4, ceiling 16, windows of

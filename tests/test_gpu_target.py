@@ -111,6 +111,29 @@ def test_target_prefill_and_verify_rounds_match_oracle(bf16_pair, f32_target, ki
     print(kind, "near ties", ls.near_ties)
 
 
+def test_target_widest_verify_forward(bf16_pair):
+    """Block 64, the widest verify a target takes (65-row forwards, slack 128): the prompt in
+    65-row forwards, then rounds of 65 rows with trims of random depth, argmaxes, captures,
+    offsets and every cache window (sliding and full) against the oracle after every trim."""
+    tshape, tw, block = T_BF16.with_(max_context=1024), bf16_pair[1], 64
+    ls = TargetLockStep(tshape, tw, max_block=block)
+    assert ls.gpu.rows_max == block + 1
+    prompt = [int(x) for x in synth.prompt_tokens(tshape.vocab, 100, tag=64)]
+    for s in range(0, len(prompt), ls.gpu.rows_max):
+        ls.forward(prompt[s:s + ls.gpu.rows_max])
+        ls.trim(0)
+    ls.check_caches()
+    rng = np.random.default_rng(64)
+    anchor = int(prompt[-1])
+    for k in (0, block, 23, 5):
+        block_toks = [anchor] + [int(x) for x in rng.integers(0, tshape.vocab, block)]
+        a, _ = ls.forward(block_toks)
+        ls.trim(block - k)
+        ls.check_caches()
+        anchor = int(a[k])
+    print("block 64 near ties", ls.near_ties)
+
+
 def test_target_boundary_errors(bf16_pair):
     t = binding.Target(T_BF16, binding.to_device(T_BF16, bf16_pair[1]), max_block=4)
     toks = torch.zeros(40, dtype=torch.int32, device="cuda")
