@@ -267,3 +267,97 @@ def test_planted_dspark_mistake_fails_a_pin(dspark_pin_calls, monkeypatch, name,
         except (Exception, pytest.fail.Exception):  # an assertion, an error, or pytest.raises unmet
             return  # caught
     pytest.fail(f"no pin fails with the planted mistake: {name}")
+
+
+WIDTH_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "width_controller.py")
+
+# mistakes in the adaptive-width controller, against its hand-worked schedules and invariants
+WIDTH_MUTANTS = [
+    ("challenger adopted on a tie", "adopted = rate > self.incumbent_rate", "adopted = rate >= self.incumbent_rate"),
+    ("incumbent rated on its latest window only", "self.incumbent_rate = self.period_tokens / self.period_ms",
+     "self.incumbent_rate = w_tokens / w_ms"),
+    ("period kept after a rejected challenge", "self.period_tokens, self.period_ms = 0, 0.0",
+     "self.period_tokens, self.period_ms = self.period_tokens, self.period_ms"),
+    ("adopted window not the new period", "self.period_tokens, self.period_ms = w_tokens, w_ms",
+     "self.period_tokens, self.period_ms = 0, 0.0"),
+    ("challenge one window late", "self.windows_since_challenge >= self.challenge_every",
+     "self.windows_since_challenge > self.challenge_every"),
+    ("rate counts rounds, not committed tokens", "self.tokens += committed", "self.tokens += 1"),
+    ("window closes one round late", "if self.rounds < self.window:", "if self.rounds <= self.window:"),
+    ("a single width challenges itself",
+     "if self.depth != self.ceiling and self.windows_since_challenge >= self.challenge_every:",
+     "if self.windows_since_challenge >= self.challenge_every:"),
+]
+
+
+@pytest.fixture(scope="module")
+def width_pin_calls():
+    from tests import test_width_controller as W
+    return [W.test_oracle_starts_at_the_declared_depth_and_probes_depth_and_ceiling,
+            W.test_oracle_never_leaves_the_two_widths_and_challenges_on_schedule] + \
+        [(lambda c=c: W.test_oracle_follows_the_hand_worked_schedules(c)) for c in W.cases()]
+
+
+def test_real_width_controller_passes_every_pin_call(width_pin_calls):
+    for call in width_pin_calls:
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", WIDTH_MUTANTS, ids=[m[0] for m in WIDTH_MUTANTS])
+def test_planted_width_controller_mistake_fails_a_pin(width_pin_calls, monkeypatch, name, old, new):
+    from tests import test_width_controller as W
+    mod = load_mutant(old, new, WIDTH_SRC)
+    monkeypatch.setattr(W, "OracleController", mod.WidthController)
+    for call in width_pin_calls:
+        try:
+            call()
+        except (Exception, pytest.fail.Exception):
+            return  # caught
+    pytest.fail(f"no pin fails with the planted mistake: {name}")
+
+
+BATCH_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "batch_oracle.py")
+
+# mistakes in the batch oracle's own logic (the split of ragged rows, the trim, the anchors),
+# against the batch pins (n independent copies of the pinned single-sequence oracle)
+BATCH_MUTANTS = [
+    ("every sequence takes the first rows", "self.seqs[s].append(resid[r:r + n], commit=commit)",
+     "self.seqs[s].append(resid[:n], commit=commit)"),
+    ("offset not advanced past an empty sequence", "            r += n\n", "            r += n if n else 1\n"),
+    ("rewinds rotated between sequences", "        for od, mm in zip(self.seqs, m):\n            od.trim(mm)",
+     "        for od, mm in zip(self.seqs, m[1:] + m[:1]):\n            od.trim(mm)"),
+    ("trim checked one sequence at a time",
+     "            if mm < 0 or mm > min(span, S):\n                raise OracleError",
+     "            if False:\n                raise OracleError"),
+    ("every sequence drafts from the first anchor",
+     "return [od.draft(int(a), block) for od, a in zip(self.seqs, anchors)]",
+     "return [od.draft(int(anchors[0]), block) for od in self.seqs]"),
+]
+
+
+@pytest.fixture(scope="module")
+def batch_pin_calls():
+    from tests import test_batch_oracle as B
+    w = synth.make_weights(B.MICRO, threads=2)
+    return [lambda: B.test_batch_refusals(w), lambda: B.test_trim_is_all_or_nothing(w),
+            lambda: B.test_a_sequence_ignores_the_others(w),
+            lambda: B.test_batch_equals_independent_sequences_with_ragged_rows(w)]
+
+
+def test_real_batch_oracle_passes_every_pin_call(batch_pin_calls):
+    for call in batch_pin_calls:
+        call()
+
+
+@pytest.mark.parametrize("name,old,new", BATCH_MUTANTS, ids=[m[0] for m in BATCH_MUTANTS])
+def test_planted_batch_mistake_fails_a_pin(batch_pin_calls, monkeypatch, name, old, new):
+    from tests import test_batch_oracle as B
+    mod = load_mutant(old, new, BATCH_SRC)
+    monkeypatch.setattr(B, "OracleBatch", mod.OracleBatch)
+    for call in batch_pin_calls:
+        try:
+            with np.errstate(all="ignore"):
+                call()
+        except (Exception, pytest.fail.Exception):
+            return  # caught
+    pytest.fail(f"no pin fails with the planted mistake: {name}")
