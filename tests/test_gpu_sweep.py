@@ -1,0 +1,82 @@
+"""A seeded sweep of lock-step parity runs over random micro configurations, through the C-ABI:
+the shape family (f32, bf16, 4-bit; DFlash and DSpark with either RoPE pairing and ranks 64
+to 256), the window (8 to 1000), the widest block, the ring phase, the context length and,
+per round, the block width and the accepted length; a third of the DFlash runs are batches
+of up to 8 sequences with ragged contexts. Every run checks what the fixed cases check: the
+drafted tokens (exact above the near-tie margin), hidden rows, the verify result, offsets
+after every call and the live window after every trim."""
+import numpy as np
+import pytest
+import torch
+
+from block_drafting_dflash_amd import binding, synth
+from tests import parity as P
+from tests.test_gpu_batch import BatchLockStep, run_batch_rounds
+from tests.test_gpu_dspark import DS_BF16, DS_F32
+from tests.test_gpu_parity import MICRO_BF16, MICRO_F32
+
+pytestmark = pytest.mark.gpu
+
+BASES = {
+    "f32": MICRO_F32, "bf16": MICRO_BF16, "q4": MICRO_BF16.with_(weight_dtype="q4"),
+    "ds_f32": DS_F32, "ds_bf16": DS_BF16, "ds_q4": DS_BF16.with_(weight_dtype="q4", markov_rank=128),
+    "ds_bf16_neox": DS_BF16.with_(rope_style="neox", markov_rank=64),
+}
+CONFIGS = 300
+
+
+def draw(rng):
+    name = str(rng.choice(list(BASES)))
+    base = BASES[name]
+    dspark = base.variant == "dspark"
+    batch = (not dspark) and rng.random() < 0.3
+    if dspark:  # a DSpark context stays within its window: 300 + 4 rounds of <= 32 rows
+        window, mb = int(rng.choice([512, 1000])), int(rng.integers(1, 32))
+    else:
+        window = int(rng.choice([8, 9, 17, 20, 33, 64, 100, 257, 600]))
+        mb = int(rng.integers(1, 9)) if batch else int(rng.integers(1, 65))
+    return name, base.with_(window=window), batch, mb, int(rng.integers(0, 400)), int(rng.integers(0, 1 << 20))
+
+
+def test_random_configurations_match_the_oracle():
+    rng = np.random.default_rng(20261202)
+    weights = {}
+    done = 0
+    while done < CONFIGS:
+        name, sh, batch, mb, phase, tag = draw(rng)
+        binding.query_sizes(binding.make_config(sh, mb, phase))  # every drawn configuration is valid
+        if name not in weights:
+            weights[name] = synth.make_weights(BASES[name])
+        w = weights[name]
+        label = f"configuration {done}: {name} W={sh.window} max_block={mb} phase={phase} tag={tag} batch={batch}"
+        try:
+            run_one(rng, sh, w, batch, mb, phase, tag)
+        except AssertionError as ex:
+            raise AssertionError(f"{label}: {ex}") from ex
+        done += 1
+    print(f"{done} random configurations matched the oracle")
+
+
+def run_one(rng, sh, w, batch, mb, phase, tag):
+    if batch:
+        n = int(rng.integers(1, min(8, 512 // (mb + 1)) + 1))
+        contexts = [int(x) for x in rng.integers(1, 300, n)]
+        ls = BatchLockStep(sh, w, n, mb, phase)
+        run_batch_rounds(ls, contexts, mb, 3, tag=tag)
+    else:
+        context = int(rng.integers(1, 300))
+        ls = P.LockStep(sh, w, max_block=mb, phase=phase)
+        ls.append(synth.resid_rows(sh, context, tag % 1000), commit=True)
+        torch.cuda.synchronize()
+        ls.check_window()
+        anchor = synth.anchor_token(sh, tag=tag % 97)
+        for r in range(4):
+            g = int(rng.integers(1, mb + 1))
+            d = ls.draft(anchor, g)
+            kk = int(rng.integers(0, g + 1))
+            a = P.target_with_accept_length(d, kk, sh.vocab, tail=anchor + 7 * r)
+            k, bonus = ls.verify(d, a)
+            assert k == kk
+            ls.append(synth.resid_rows(sh, g + 1, tag % 1000 + 10 * r + 1))
+            ls.trim(g - k)
+            anchor = bonus
