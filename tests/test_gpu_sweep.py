@@ -80,3 +80,50 @@ def run_one(rng, sh, w, batch, mb, phase, tag):
             ls.append(synth.resid_rows(sh, g + 1, tag % 1000 + 10 * r + 1))
             ls.trim(g - k)
             anchor = bonus
+
+
+TARGET_CONFIGS = 150
+
+
+def test_random_target_configurations_match_the_oracle():
+    """The target's verify forward over seeded random micro configurations: window (1-119),
+    max_context (512, 1024), which layers attend to everything, which streams are captured,
+    the widest block (1-64), the prompt length (in forwards of the widest width) and rounds
+    of random width with trims of random depth; argmaxes, captures, offsets and every cache
+    window against the target oracle after every call."""
+    from tests.test_gpu_target import D_BF16, T_BF16, T_F32, TargetLockStep
+
+    rng = np.random.default_rng(20261203)
+    d32 = synth.Shape(hidden=256, layers=1, q_heads=4, kv_heads=2, head_dim=64, intermediate=384, vocab=1040,
+                      target_streams=2, target_width=256, window=9, weight_dtype="f32", act_dtype="f32")
+    tw = {"bf16": synth.make_target_weights(T_BF16, synth.make_weights(D_BF16)),
+          "f32": synth.make_target_weights(T_F32, synth.make_weights(d32))}
+    bases = {"bf16": T_BF16, "f32": T_F32}
+    for i in range(TARGET_CONFIGS):
+        kind = str(rng.choice(["bf16", "f32"]))
+        base = bases[kind]
+        L = base.layers
+        full = tuple(int(l) for l in range(L) if rng.random() < 0.35)
+        caps = tuple(sorted(int(x) for x in rng.choice(L, int(rng.integers(1, L + 1)), replace=False)))
+        sh = base.with_(window=int(rng.integers(1, 120)), max_context=int(rng.choice([512, 1024])),
+                        full_layers=full, capture_layers=caps)
+        mb, prompt_len, tag = int(rng.integers(1, 65)), int(rng.integers(1, 200)), int(rng.integers(0, 1 << 20))
+        label = f"configuration {i}: {kind} W={sh.window} full={full} caps={caps} max_block={mb} prompt={prompt_len}"
+        try:
+            ls = TargetLockStep(sh, tw[kind], max_block=mb)
+            prompt = [int(x) for x in synth.prompt_tokens(sh.vocab, prompt_len, tag=tag % 1000)]
+            for s in range(0, prompt_len, ls.gpu.rows_max):
+                ls.forward(prompt[s:s + ls.gpu.rows_max])
+                ls.trim(0)
+            ls.check_caches()
+            anchor = int(prompt[-1])
+            for r in range(4):
+                g = int(rng.integers(1, mb + 1))
+                a, _ = ls.forward([anchor] + [int(x) for x in rng.integers(0, sh.vocab, g)])
+                k = int(rng.integers(0, g + 1))
+                ls.trim(g - k)
+                ls.check_caches()
+                anchor = int(a[k])
+        except AssertionError as ex:
+            raise AssertionError(f"{label}: {ex}") from ex
+    print(f"{TARGET_CONFIGS} random target configurations matched the oracle")
