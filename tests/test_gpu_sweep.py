@@ -127,3 +127,60 @@ def test_random_target_configurations_match_the_oracle():
         except AssertionError as ex:
             raise AssertionError(f"{label}: {ex}") from ex
     print(f"{TARGET_CONFIGS} random target configurations matched the oracle")
+
+
+SHAPE_CONFIGS = 80
+
+
+def draw_shape(rng):
+    """A random drafter shape: weight dtype, head dim and GQA grouping, hidden / intermediate /
+    fc widths in whole tile units, vocabulary, layers, window; and the widest block."""
+    wt = str(rng.choice(["f32", "bf16", "q4"]))
+    nkv = int(rng.choice([1, 2, 4]))
+    unit = 128 if wt == "f32" else 256
+    sh = synth.Shape(hidden=unit * int(rng.integers(1, 9)), layers=int(rng.integers(1, 4)),
+                     q_heads=nkv * int(rng.choice([1, 2, 4, 8])), kv_heads=nkv, head_dim=int(rng.choice([64, 128])),
+                     intermediate=unit * int(rng.integers(1, 17)), vocab=16 * int(rng.integers(40, 1500)),
+                     target_streams=int(rng.integers(1, 6)), target_width=unit * int(rng.integers(1, 5)),
+                     window=int(rng.choice([9, 33, 64, 200])), weight_dtype=wt,
+                     act_dtype="f32" if wt == "f32" else "bf16")
+    return sh, int(rng.integers(1, 33))
+
+
+def test_random_shapes_match_the_oracle():
+    """Drafter dimensions decide the GEMM launch plans (waves, chunks, tile and fold forms, the
+    4-bit code paths) and the attention's query tiling. Every seeded random shape the library
+    accepts (it refuses, before any device call, contraction lengths it has no plan for) runs
+    a prefill and three rounds of random width and accepted length in lock-step with the oracle."""
+    rng = np.random.default_rng(20261204)
+    done = refused = 0
+    while done < SHAPE_CONFIGS:
+        sh, mb = draw_shape(rng)
+        try:
+            binding.query_sizes(binding.make_config(sh, mb, 0))
+        except binding.DFlashError:
+            refused += 1
+            continue
+        label = (f"shape {done}: {sh.weight_dtype} H={sh.hidden} L={sh.layers} q/kv={sh.q_heads}/{sh.kv_heads} "
+                 f"hd={sh.head_dim} I={sh.intermediate} V={sh.vocab} F={sh.target_streams}x{sh.target_width} "
+                 f"W={sh.window} max_block={mb}")
+        try:
+            ls = P.LockStep(sh, synth.make_weights(sh), max_block=mb, phase=int(rng.integers(0, 300)))
+            tag = int(rng.integers(0, 1 << 20))
+            ls.append(synth.resid_rows(sh, int(rng.integers(1, 120)), tag % 1000), commit=True)
+            torch.cuda.synchronize()
+            ls.check_window()
+            anchor = synth.anchor_token(sh, tag=tag % 97)
+            for r in range(3):
+                g = int(rng.integers(1, mb + 1))
+                d = ls.draft(anchor, g)
+                kk = int(rng.integers(0, g + 1))
+                k, bonus = ls.verify(d, P.target_with_accept_length(d, kk, sh.vocab, tail=anchor + 7 * r))
+                assert k == kk
+                ls.append(synth.resid_rows(sh, g + 1, tag % 1000 + 10 * r + 1))
+                ls.trim(g - k)
+                anchor = bonus
+        except AssertionError as ex:
+            raise AssertionError(f"{label}: {ex}") from ex
+        done += 1
+    print(f"{done} random shapes matched the oracle ({refused} drawn shapes refused at validation)")
