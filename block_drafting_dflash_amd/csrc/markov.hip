@@ -10,7 +10,8 @@
 // runs on the vector ALUs. Every lane owns a fixed 16-byte slice of the rank axis (and so
 // the same 16 bytes of u = w1[t] for the whole launch); the LPR lanes of a row read its
 // rank * elt bytes as one contiguous run, a wave load reads 64 / LPR whole rows (1 KiB
-// contiguous), and each wave keeps MK_LOADS such loads in flight. The per-row sums finish
+// contiguous), and each wave keeps MK_LOADS such loads in flight (a pass) and issues the
+// next pass after reducing this one: more requests queued per wave measured slower. The per-row sums finish
 // with DPP row operations, and each work-group leaves one (score, index) key.
 //
 // The steps pass the token on through kernel boundaries, with no device-wide fence: every
@@ -27,7 +28,7 @@ namespace dflash {
 
 constexpr int MK_THREADS = 256;
 constexpr int MK_WAVES = MK_THREADS / 64;
-constexpr int MK_LOADS = 8;  // 16-byte loads in flight per lane
+constexpr int MK_LOADS = 7;  // 16-byte loads in flight per lane (5-7 measured alike, 8 and more slower)
 
 // sum over the LPR consecutive lanes that share a row (every one of them ends with the sum)
 template <int LPR>
@@ -78,7 +79,15 @@ __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __r
   __shared__ unsigned long long red[MK_WAVES];
   __shared__ int32_t tok;
 
-  // the first pass's loads (rows past the vocabulary re-read the last one, unused)
+  // the previous step's keys first (a few KiB from L2: indices past them re-read the last
+  // one, as max is idempotent), all in flight together, so that the token's reduction waits
+  // for them alone
+  unsigned long long kk[KPT];
+  if (prev_keys) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) kk[i] = prev_keys[min(tid + i * MK_THREADS, prev_groups - 1)];
+  }
+  // then the first pass's loads (rows past the vocabulary re-read the last one, unused)
   int g = blockIdx.x * MK_WAVES + w;
   u32x4_t v[MK_LOADS];
   float lg[MK_LOADS];
@@ -91,17 +100,13 @@ __global__ __launch_bounds__(MK_THREADS) void markov_step_kernel(const void* __r
       lg[j] = logits[row];
     }
   };
-  if (g < ngroups) issue(g);
+  issue(min(g, ngroups - 1));  // unconditional: no merge between the keys and their use
 
   // the previous token: the anchor, or the largest key step i-1 left
   if (prev_keys) {
     unsigned long long b = 0ull;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int k = tid + i * MK_THREADS;
-      const unsigned long long kk = k < prev_groups ? prev_keys[k] : 0ull;
-      b = kk > b ? kk : b;
-    }
+    for (int i = 0; i < KPT; ++i) b = kk[i] > b ? kk[i] : b;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const unsigned long long kk = shfl_xor_u64(b, o);
