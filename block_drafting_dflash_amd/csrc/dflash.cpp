@@ -390,11 +390,11 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   if (gc.gain2 && (gc.xsrc != XSRC_NORM || !gc.split || rows > 16 || gc.r2 < 0 || gc.r2 > rows))
     return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows, split at %d) need one staged normed launch",
                 rows, gc.r2);
-  // normed hi/lo operands: up to GEMM_NORM_STAGED_ROWS rows run directly when each wave's k
-  // range is 256 elements (its raw rows are staged through LDS); more rows would not fit,
-  // so they are normalised once into planes and streamed
-  if (gc.xsrc == XSRC_NORM && gc.split && rows > 16 &&
-      !(rows <= GEMM_NORM_STAGED_ROWS && plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan) && plan.nch == 1)) {
+  // normed hi/lo operands run directly when each wave's k range is 256 elements (their raw
+  // rows are staged through LDS: one staging up to GEMM_NORM_STAGED_ROWS rows, two phases up
+  // to a launch's 32); otherwise rows past one row tile are normalised once into planes and
+  // streamed
+  if (gc.xsrc == XSRC_NORM && gc.split && rows > 16 && !(plan_gemm(wt, gc.epi, gc.xsrc, gc.K, &plan) && plan.nch == 1)) {
     void* hn = ctx->ws + ctx->lay.hn;
     void* hn_lo = lo_plane(g, hn, hn_rows(g), gc.K);
     const dflash_status s0 =
@@ -424,7 +424,11 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     // for normed hi/lo operands over an even tile count (the launch below)
     const bool norm_two = gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0 && (rc <= 16 || nb == 1);
     const int tpw_lds = gc.epi == EPI_ARGMAX || norm_two ? 2 : 1;
-    while (rc > 1 && gemm_lds_bytes(wt, gc.xsrc, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
+    // staged normed rows past one staging take two phases
+    auto xsrc_for = [&](int r) {
+      return gc.xsrc == XSRC_NORM && gc.split && r > GEMM_NORM_STAGED_ROWS ? (int)XSRC_NORMP : gc.xsrc;
+    };
+    while (rc > 1 && gemm_lds_bytes(wt, xsrc_for(rc), gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
     if (gc.gain2 && (rc < rows || gemm_lds_layout(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds).stage != 2 ||
                      gemm_lds_bytes(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES))
       return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows) do not fit one staged launch", rows);
@@ -476,7 +480,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
-    const hipError_t le = launch_gemm(wt, gc.epi, gc.gain2 ? XSRC_NORM2 : gc.xsrc, pl, p, st);
+    const hipError_t le = launch_gemm(wt, gc.epi, gc.gain2 ? (int)XSRC_NORM2 : xsrc_for(rc), pl, p, st);
     if (timed && le == hipSuccess && hipEventRecord(ctx->tev_end, st) != hipSuccess)
       return dev(ctx, hipGetLastError(), "timing event");
     if (le != hipSuccess)

@@ -133,8 +133,9 @@ template <int WT, int RT, int NB, int XSRC, int T, int NCH, bool SPLIT> constexp
 // CU, which keep the stream busy between them (three chunks for 4-bit single-plane rows,
 // whose chunks carry a quarter of the bytes). f32 weights (the exact-arithmetic shapes)
 // keep one chunk ahead.
-template <int WT, int RT, int NB, int EPI, int XSRC, int T, int NCH, int CH, bool SPLIT>
+template <int WT, int RT, int NB, int EPI, int XSRC_IN, int T, int NCH, int CH, bool SPLIT>
 constexpr int gemm_chunks_ahead() {
+  constexpr int XSRC = xsrc_base(XSRC_IN);
   constexpr bool Q4 = WT == WT_Q4, BF = WT != WT_F32;
   constexpr bool fold = WT == WT_BF16 && XSRC == XSRC_GLOBAL;  // RT counts 8-row groups
   constexpr int nit = T * NCH;
@@ -153,9 +154,12 @@ constexpr int gemm_chunks_ahead() {
   // dead before the pairs are formed)
   constexpr bool stg_n = XSRC == XSRC_NORM && RT <= 2 && NCH * CH * 32 == 256;
   constexpr int raw_stg = (GEMM_NORM_STAGED_ROWS + 1) * 4;
+  // two-phase staging (XSRC_NORMP) loads its later rows, eight at a time, beside the first
+  // row tile's pairs
+  constexpr int raw_p2 = XSRC_IN == XSRC_NORMP ? 8 * 4 : 0;
   constexpr int opnd = XSRC == XSRC_GLOBAL ? ((fold ? 8 : 16) * RT <= 32 ? staged : 2 * frag)
                        : XSRC == XSRC_LDS  ? NCH * frag
-                       : stg_n             ? (raw_stg > NCH * frag ? raw_stg : NCH * frag)
+                       : stg_n             ? (raw_stg > NCH * frag + raw_p2 ? raw_stg : NCH * frag + raw_p2)
                        : NCH == 1          ? (raw > frag ? raw : frag)
                                            : NCH * frag + raw;
   constexpr int wreg = Q4 ? NB * (CH / 4) * 6 : NB * (fold ? CH / 2 : CH) * 4;
@@ -214,7 +218,10 @@ gemm_kernel(const GemmParams p) {
   static_assert(!FOLD || CH % 2 == 0, "a folded chunk pairs its k steps");
   constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RROWS * RT <= 32;
   constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * Tr::KSTEP == 256;
-  constexpr int STG_N_ROWS = RT == 1 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows a normed launch stages
+  // two-phase staging (XSRC_NORMP): rows 0-15, then rows 16.. over the same slot
+  constexpr bool STG_N2 = XSRC_IN == XSRC_NORMP;
+  static_assert(!STG_N2 || (STG_N && RT == 2), "two-phase staging: two row tiles of staged raw rows");
+  constexpr int STG_N_ROWS = RT == 1 || STG_N2 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows one staging holds
   constexpr bool STG_L = BF && XSRC == XSRC_LDS && RT == 1 && NCH == 1;
   // 4-bit weights over hi/lo rows staged once per work-group, four tiles per work-group: each
   // step's lo fragment is read from the staged rows where it is used instead of being held
@@ -587,7 +594,7 @@ gemm_kernel(const GemmParams p) {
   // first and the weights right behind them, before any arithmetic: the normed operands
   // are ready when their own loads land, and every weight chunk the register budget holds
   // (all of them for the layer GEMMs) is in flight from the start.
-  constexpr int AHEAD = gemm_chunks_ahead<WT, RT, NB, EPI, XSRC, T, NCH, CH, SPLIT>();
+  constexpr int AHEAD = gemm_chunks_ahead<WT, RT, NB, EPI, XSRC_IN, T, NCH, CH, SPLIT>();
   constexpr int PDW = AHEAD + 1;
   u32x4_t wbuf[PDW][NB][CH];
   u32x2_t sbuf[PDW][NB][CB];
@@ -724,35 +731,65 @@ gemm_kernel(const GemmParams p) {
     float ssl[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) ssl[rt] = 0.f;
+    // the gain row sits after the staged rows (after the first phase's 16 with two phases)
+    const int grow = STG_N2 ? 16 : R;
     if constexpr (STG_N) {
 #pragma unroll
       for (int i = 0; i < STG_N_ROWS; ++i)
         if (i < R) *(u32x4_t*)(xs + (size_t)i * lds.row_bytes + lane * 16) = xn[i];
-      *(u32x4_t*)(xs + (size_t)R * lds.row_bytes + (GAIN2 ? lane : lane & 31) * 16) = xn[STG_N_ROWS];
+      *(u32x4_t*)(xs + (size_t)grow * lds.row_bytes + (GAIN2 ? lane : lane & 31) * 16) = xn[STG_N_ROWS];
     }
     // lane (li, lg) of step st holds row rt*16+li, k = w*kw + st*KSTEP + lg*EPL .. + EPL
+    auto form_at = [&](int c, int rt, int st) {
+      u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
+      if constexpr (STG_N) {
+        const int kk = (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;  // within the wave's k range
+        // the slot holds rows 0.. (one phase), or the row tile's own rows (two phases)
+        const int row = STG_N2 ? min(li, R - 1 - 16 * rt) : min(rt * 16 + li, R - 1);
+        const unsigned char* xrw = xs + (size_t)row * lds.row_bytes + kk * 4;
+        const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)grow * lds.row_bytes + (GAIN2 ? g2off : 0) + kk * 2);
+        form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
+      } else if constexpr (NORM_FIRST) {
+        form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
+      } else if (rt * 16 + li < R) {
+        const float* src = (const float*)p.x + (size_t)(rt * 16 + li) * p.ldx + kof(c, st);
+        form(*(const f32x4_t*)src, *(const f32x4_t*)(src + 4 * (XRAW - 1)), gain_ld(c, st), ssl[rt], f, fl);
+      }
+      xr[c][rt][st] = f;
+      if constexpr (SPLIT) xrl[c][rt][st] = fl;
+    };
+    if constexpr (STG_N2) {
+      // the first row tile forms; then rows 16.., eight at a time in the registers the first
+      // phase freed (more beside the first tile's pairs and the weights in flight spill),
+      // overwrite the slot (a wave's LDS operations complete in order) and the second row
+      // tile forms; every row's sums keep the order of one phase (chunk, then step)
 #pragma unroll
-    for (int c = 0; c < XR; ++c) {
+      for (int c = 0; c < XR; ++c)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int st = 0; st < CH; ++st) form_at(c, 0, st);
+      const size_t k0 = (size_t)w * kw;
 #pragma unroll
-        for (int st = 0; st < CH; ++st) {
-          u32x4_t f = {0u, 0u, 0u, 0u}, fl = {0u, 0u, 0u, 0u};
-          if constexpr (STG_N) {
-            const int kk = (c * CH + st) * Tr::KSTEP + lg * Tr::EPL;  // within the wave's k range
-            const int row = min(rt * 16 + li, R - 1);
-            const unsigned char* xrw = xs + (size_t)row * lds.row_bytes + kk * 4;
-            const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)R * lds.row_bytes + (GAIN2 ? g2off : 0) + kk * 2);
-            form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
-          } else if constexpr (NORM_FIRST) {
-            form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
-          } else if (rt * 16 + li < R) {
-            const float* src = (const float*)p.x + (size_t)(rt * 16 + li) * p.ldx + kof(c, st);
-            form(*(const f32x4_t*)src, *(const f32x4_t*)(src + 4 * (XRAW - 1)), gain_ld(c, st), ssl[rt], f, fl);
-          }
-          xr[c][rt][st] = f;
-          if constexpr (SPLIT) xrl[c][rt][st] = fl;
-        }
+      for (int h = 0; h < 2; ++h) {
+        if (16 + 8 * h >= R) break;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 + 8 * h + i < R)
+            xn[i] = *(const u32x4_t*)((const float*)p.x + (size_t)(16 + 8 * h + i) * p.ldx + k0 + lane * 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 + 8 * h + i < R) *(u32x4_t*)(xs + (size_t)(8 * h + i) * lds.row_bytes + lane * 16) = xn[i];
+      }
+#pragma unroll
+      for (int c = 0; c < XR; ++c)
+#pragma unroll
+        for (int st = 0; st < CH; ++st) form_at(c, 1, st);
+    } else {
+#pragma unroll
+      for (int c = 0; c < XR; ++c)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int st = 0; st < CH; ++st) form_at(c, rt, st);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -849,12 +886,22 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
     }
   } else {
     const int rt = (p.R + 15) / 16;
-    if (rt == 1) return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
-    if constexpr (XSRC == XSRC_NORM2) {
+    if constexpr (XSRC == XSRC_NORMP) {
+      // normed hi/lo operands of two row tiles past one staging: two phases (up to 32 rows)
+      if constexpr (NCH == 1 && SPLIT) {
+        if (rt == 2 && p.R > GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
+      }
+      return hipErrorInvalidValue;
+    } else if (rt == 1) {
+      return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
+    }
+    if constexpr (XSRC == XSRC_NORMP) {
+      return hipErrorInvalidValue;
+    } else if constexpr (XSRC == XSRC_NORM2) {
       return hipErrorInvalidValue;
     } else if constexpr (XSRC == XSRC_NORM && SPLIT) {
       // normed hi/lo operands of two row tiles: staged raw rows over a 256-element k range
-      // per wave (at most GEMM_NORM_STAGED_ROWS rows); larger launches go through planes
+      // per wave (at most GEMM_NORM_STAGED_ROWS rows; up to 32 as XSRC_NORMP)
       if constexpr (NCH == 1) {
         if (rt == 2 && p.R <= GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
       }
@@ -949,6 +996,8 @@ static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParam
     if (!p.split) return hipErrorInvalidValue;
     if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, true>(pl, p, s);
     if (epi == EPI_STORE && xsrc == XSRC_NORM2) return by_nch<WT, 1, EPI_STORE, XSRC_NORM2, true>(pl, p, s);
+    if (epi == EPI_STORE && xsrc == XSRC_NORMP) return by_nch<WT, 1, EPI_STORE, XSRC_NORMP, true>(pl, p, s);
+    if (epi == EPI_SWIGLU && xsrc == XSRC_NORMP) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORMP, true>(pl, p, s);
     if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_GLOBAL) return by_nch<WT, 2, EPI_SWIGLU, XSRC_GLOBAL, true>(pl, p, s);

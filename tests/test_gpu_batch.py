@@ -116,8 +116,8 @@ def run_batch_rounds(ls, contexts, B, rounds, tag):
                                             ("bf16", 1, 16, 0), ("q4", 4, 4, 24)])
 def test_batch_rounds_match_oracle(kind, n, B, phase):
     """Ragged prefills and accept lengths; 15, 25 and 64 rows per GEMM (one launch with the
-    norm staged in LDS, one through the row-norm planes, two launches), f32, one sequence,
-    4-bit weights."""
+    norm staged in LDS in one phase, one staged in two phases, two launches), f32, one
+    sequence, 4-bit weights."""
     sh = {"bf16": MICRO_BF16, "f32": MICRO_F32, "q4": MICRO_BF16.with_(weight_dtype="q4")}[kind]
     w = synth.make_weights(sh)
     ls = BatchLockStep(sh, w, n, B, phase)
@@ -136,11 +136,15 @@ def test_batch_at_its_limits():
     print("64 sequences: near ties", ls.near_ties, "ks", ks)
 
 
-def test_batch_equals_single_contexts_bit_for_bit():
+@pytest.mark.parametrize("n", [3, 5, 8])
+def test_batch_equals_single_contexts_bit_for_bit(n):
+    """15, 25 and 40 rows per GEMM: the normed launches stage their raw rows in one phase,
+    in two (19-32 rows), and as a two-phase launch of 32 rows plus one of 8; a sequence's
+    tokens, hidden rows and ring windows are bit for bit those of a single context."""
     sh = MICRO_BF16
     w = synth.make_weights(sh)
     dev = binding.to_device(sh, w)
-    n, B = 3, 4
+    B = 4
     batch = binding.Batch(sh, dev, n, B)
     singles = [binding.Drafter(sh, dev, B) for _ in range(n)]
     rows = [synth.resid_rows(sh, 9 + 11 * s, 70 + s) for s in range(n)]
@@ -148,7 +152,7 @@ def test_batch_equals_single_contexts_bit_for_bit():
     for d, r in zip(singles, rows):
         d.cache_append(torch.from_numpy(r).to(torch.bfloat16).cuda(), commit=True)
     rng = np.random.default_rng(5)
-    anchors = [3, 500, 2000]
+    anchors = [3, 500, 2000, 7, 911, 1234, 42, 2999][:n]
     for r in range(6):
         hb = torch.empty((n, B + 1, sh.hidden), dtype=torch.float32, device="cuda")
         tb = batch.draft(anchors, B, hidden=hb)
