@@ -480,13 +480,14 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
-    const hipError_t le = launch_gemm(wt, gc.epi, gc.gain2 ? (int)XSRC_NORM2 : xsrc_for(rc), pl, p, st);
+    const int xsrc_launch = gc.gain2 ? (int)XSRC_NORM2 : xsrc_for(rc);
+    const hipError_t le = launch_gemm(wt, gc.epi, xsrc_launch, pl, p, st);
     if (timed && le == hipSuccess && hipEventRecord(ctx->tev_end, st) != hipSuccess)
       return dev(ctx, hipGetLastError(), "timing event");
     if (le != hipSuccess)
       return fail(ctx, DFLASH_E_DEVICE,
                   "gemm launch (epi %d, xsrc %d, K %d, rows %d, tiles %d, waves %d, ch %d x %d, tiles/wg %d, grid %d): %s",
-                  gc.epi, gc.xsrc, gc.K, rc, p.ntiles, waves, pl.ch, pl.nch, pl.tiles_per_wg, pl.grid,
+                  gc.epi, xsrc_launch, gc.K, rc, p.ntiles, waves, pl.ch, pl.nch, pl.tiles_per_wg, pl.grid,
                   hipGetErrorString(le));
     if (gc.epi == EPI_ARGMAX && gc.idx) {  // no index output: the logits were the point
       const hipError_t fe = launch_argmax_finalize(p.part, pl.grid, rc, gc.idx + r0, st);
