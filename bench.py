@@ -777,7 +777,7 @@ def main():
         print(json.dumps({"copy_probe_mib": args.copy_probe_mib, "launches": 5}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the round at batch 1 is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     import torch
