@@ -119,8 +119,9 @@ int kstep(int wt) { return wt == WT_F32 ? 16 : 32; }
 
 constexpr int CHUNK_STEPS = 8;
 // rows of a QKV launch with committed rows folded in: draft rows plus committed rows in one
-// MFMA row tile
+// MFMA row tile, or in two row tiles staged in two phases
 constexpr int FOLD_ROWS = 16;
+constexpr int FOLD_ROWS_TWO = 32;
 
 // Launch plan of a GEMM with contraction length K. Waves and chunking depend on K only.
 bool plan_gemm(int wt, int epi, int xsrc, int K, GemmPlan* pl) {
@@ -274,7 +275,7 @@ Layout make_layout(const Cfg& g) {
   L.knorm_ptrs = take(sizeof(void*) * c.layers);
   // operand buffers (q, attention output, SwiGLU output, normed rows) hold 4 bytes per
   // element: f32, or for bf16 shapes a hi plane followed by a lo plane (see lo_plane)
-  const size_t RQ = std::max<size_t>(R, FOLD_ROWS);  // draft rows and folded committed rows
+  const size_t RQ = std::max<size_t>(R, FOLD_ROWS_TWO);  // draft rows and folded committed rows
   L.x = take(4 * RQ * H);
   L.hn = take(4 * hn_rows(g) * H);  // normed rows of launches past one row tile
   L.qkv = take(4 * RQ * (qd + 2 * kvd));
@@ -387,7 +388,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
   GemmCall gc = gc_in;
   const int wt = g.wt;
   GemmPlan plan;
-  if (gc.gain2 && (gc.xsrc != XSRC_NORM || !gc.split || rows > 16 || gc.r2 < 0 || gc.r2 > rows))
+  if (gc.gain2 && (gc.xsrc != XSRC_NORM || !gc.split || rows > 32 || gc.r2 < 0 || gc.r2 > rows))
     return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows, split at %d) need one staged normed launch",
                 rows, gc.r2);
   // normed hi/lo operands run directly when each wave's k range is 256 elements (their raw
@@ -424,13 +425,14 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     // for normed hi/lo operands over an even tile count (the launch below)
     const bool norm_two = gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0 && (rc <= 16 || nb == 1);
     const int tpw_lds = gc.epi == EPI_ARGMAX || norm_two ? 2 : 1;
-    // staged normed rows past one staging take two phases
+    // staged normed rows past one staging (past one row tile with two gain rows) take two
+    // phases
     auto xsrc_for = [&](int r) {
+      if (gc.gain2) return r > 16 ? (int)XSRC_NORM2P : (int)XSRC_NORM2;
       return gc.xsrc == XSRC_NORM && gc.split && r > GEMM_NORM_STAGED_ROWS ? (int)XSRC_NORMP : gc.xsrc;
     };
     while (rc > 1 && gemm_lds_bytes(wt, xsrc_for(rc), gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES) --rc;
-    if (gc.gain2 && (rc < rows || gemm_lds_layout(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds).stage != 2 ||
-                     gemm_lds_bytes(wt, XSRC_NORM2, gc.split, rc, waves, nb, gc.K, tpw_lds) > (size_t)LDS_BYTES))
+    if (gc.gain2 && (rc < rows || gemm_lds_layout(wt, xsrc_for(rc), gc.split, rc, waves, nb, gc.K, tpw_lds).stage != 2))
       return fail(ctx, DFLASH_E_SHAPE, "operand rows with two gains (%d rows) do not fit one staged launch", rows);
     GemmParams p{};
     for (size_t i = 0; i < gc.segs.size(); ++i) p.seg[i] = gc.segs[i];
@@ -480,7 +482,7 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
-    const int xsrc_launch = gc.gain2 ? (int)XSRC_NORM2 : xsrc_for(rc);
+    const int xsrc_launch = xsrc_for(rc);
     const hipError_t le = launch_gemm(wt, gc.epi, xsrc_launch, pl, p, st);
     if (timed && le == hipSuccess && hipEventRecord(ctx->tev_end, st) != hipSuccess)
       return dev(ctx, hipGetLastError(), "timing event");
@@ -502,18 +504,22 @@ GemmSeg seg(const Lin& l, int col0, int rows) { return GemmSeg{l.w, l.s, l.b, co
 
 // Rows of a QKV launch that may carry committed rows beside the draft rows (0: none): bf16
 // activations on the MFMA attention (which forms and writes those rows), and a normed
-// launch of one row tile that stages its raw rows through LDS.
+// launch that stages its raw rows through LDS: two row tiles in two phases where that
+// fits, else one.
 int fold_rows_of(const Cfg& g) {
   const dflash_config& c = g.c;
   if (!g.bf || !attention_forms_committed_rows(g.bf, g.a)) return 0;
   GemmPlan pl;
-  if (!plan_gemm(g.wt, EPI_STORE, XSRC_NORM, c.hidden, &pl)) return 0;
+  if (!plan_gemm(g.wt, EPI_STORE, XSRC_NORM, c.hidden, &pl) || pl.nch != 1) return 0;
   const int tiles = (c.q_heads + 2 * c.kv_heads) * c.head_dim / 16;
   const int tpw = tiles % 2 == 0 ? 2 : 1;
-  if (gemm_lds_layout(g.wt, XSRC_NORM2, 1, FOLD_ROWS, pl.waves, 1, c.hidden, tpw).stage != 2 ||
-      gemm_lds_bytes(g.wt, XSRC_NORM2, 1, FOLD_ROWS, pl.waves, 1, c.hidden, tpw) > (size_t)LDS_BYTES)
-    return 0;
-  return FOLD_ROWS;
+  for (const int rows : {FOLD_ROWS_TWO, FOLD_ROWS}) {
+    const int xs = rows > 16 ? XSRC_NORM2P : XSRC_NORM2;
+    if (gemm_lds_layout(g.wt, xs, 1, rows, pl.waves, 1, c.hidden, tpw).stage == 2 &&
+        gemm_lds_bytes(g.wt, xs, 1, rows, pl.waves, 1, c.hidden, tpw) <= (size_t)LDS_BYTES)
+      return rows;
+  }
+  return 0;
 }
 
 // K/V of rc encoder rows (the fc output in the append buffer) at positions pos.. into the

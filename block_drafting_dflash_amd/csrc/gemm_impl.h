@@ -156,7 +156,7 @@ constexpr int gemm_chunks_ahead() {
   constexpr int raw_stg = (GEMM_NORM_STAGED_ROWS + 1) * 4;
   // two-phase staging (XSRC_NORMP) loads its later rows, eight at a time, beside the first
   // row tile's pairs
-  constexpr int raw_p2 = XSRC_IN == XSRC_NORMP ? 8 * 4 : 0;
+  constexpr int raw_p2 = xsrc_two_phase(XSRC_IN) ? 8 * 4 : 0;
   constexpr int opnd = XSRC == XSRC_GLOBAL ? ((fold ? 8 : 16) * RT <= 32 ? staged : 2 * frag)
                        : XSRC == XSRC_LDS  ? NCH * frag
                        : stg_n             ? (raw_stg > NCH * frag + raw_p2 ? raw_stg : NCH * frag + raw_p2)
@@ -219,7 +219,7 @@ gemm_kernel(const GemmParams p) {
   constexpr bool STG_G = BF && XSRC == XSRC_GLOBAL && RROWS * RT <= 32;
   constexpr bool STG_N = BF && XSRC == XSRC_NORM && RT <= 2 && NCH * CH * Tr::KSTEP == 256;
   // two-phase staging (XSRC_NORMP): rows 0-15, then rows 16.. over the same slot
-  constexpr bool STG_N2 = XSRC_IN == XSRC_NORMP;
+  constexpr bool STG_N2 = xsrc_two_phase(XSRC_IN);
   static_assert(!STG_N2 || (STG_N && RT == 2), "two-phase staging: two row tiles of staged raw rows");
   constexpr int STG_N_ROWS = RT == 1 || STG_N2 ? 16 : GEMM_NORM_STAGED_ROWS;  // rows one staging holds
   constexpr bool STG_L = BF && XSRC == XSRC_LDS && RT == 1 && NCH == 1;
@@ -612,10 +612,11 @@ gemm_kernel(const GemmParams p) {
   // STG_N: raw row i of the wave's k range in load i (64 lanes x 4 f32), the gains in the last
   // (one row tile: lanes 0-31 the gains of rows below r2, lanes 32-63 those of rows r2 and up)
   u32x4_t xn[STG_N ? STG_N_ROWS + 1 : 1];
-  constexpr bool GAIN2 = XSRC_IN == XSRC_NORM2;
-  static_assert(!GAIN2 || (STG_N && RT == 1), "two gain rows: one row tile of staged raw rows");
-  // LDS offset of the gain row of this lane's operand row (row li, clamped to the real rows)
-  const int g2off = GAIN2 && min(li, R - 1) >= p.r2 ? 512 : 0;
+  constexpr bool GAIN2 = xsrc_gain2(XSRC_IN);
+  static_assert(!GAIN2 || (STG_N && (RT == 1 || STG_N2)), "two gain rows: staged raw rows");
+  // LDS offset of the gain row of this lane's operand row in row tile rt (row rt*16+li,
+  // clamped to the real rows)
+  auto g2off = [&](int rt) { return GAIN2 && min(rt * 16 + li, R - 1) >= p.r2 ? 512 : 0; };
   auto kof = [&](int c, int st) { return w * kw + (c * CH + st) * Tr::KSTEP + lg * Tr::EPL; };
   auto raw_ld = [&](int c, int rt, int st, int h) {
     return *(const f32x4_t*)((const float*)p.x + (size_t)xrow(rt) * p.ldx + kof(c, st) + 4 * h);
@@ -747,7 +748,7 @@ gemm_kernel(const GemmParams p) {
         // the slot holds rows 0.. (one phase), or the row tile's own rows (two phases)
         const int row = STG_N2 ? min(li, R - 1 - 16 * rt) : min(rt * 16 + li, R - 1);
         const unsigned char* xrw = xs + (size_t)row * lds.row_bytes + kk * 4;
-        const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)grow * lds.row_bytes + (GAIN2 ? g2off : 0) + kk * 2);
+        const u32x4_t gb = *(const u32x4_t*)(xs + (size_t)grow * lds.row_bytes + g2off(rt) + kk * 2);
         form(*(const f32x4_t*)xrw, *(const f32x4_t*)(xrw + 16), gb, ssl[rt], f, fl);
       } else if constexpr (NORM_FIRST) {
         form(xa[rt][st][0], xa[rt][st][XRAW - 1], ga[st], ssl[rt], f, fl);
@@ -886,16 +887,16 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
     }
   } else {
     const int rt = (p.R + 15) / 16;
-    if constexpr (XSRC == XSRC_NORMP) {
-      // normed hi/lo operands of two row tiles past one staging: two phases (up to 32 rows)
+    if constexpr (xsrc_two_phase(XSRC)) {
+      // normed hi/lo operands of two row tiles staged in two phases (up to 32 rows)
       if constexpr (NCH == 1 && SPLIT) {
-        if (rt == 2 && p.R > GEMM_NORM_STAGED_ROWS) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
+        if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2, 4, SPLIT>(p, grid, s);
       }
       return hipErrorInvalidValue;
     } else if (rt == 1) {
       return launch_t<WT, 1, NB, EPI, XSRC, T, NCH, 8, SPLIT>(p, grid, s);
     }
-    if constexpr (XSRC == XSRC_NORMP) {
+    if constexpr (xsrc_two_phase(XSRC)) {
       return hipErrorInvalidValue;
     } else if constexpr (XSRC == XSRC_NORM2) {
       return hipErrorInvalidValue;
@@ -918,7 +919,7 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
 // every chunk in registers, so they stop at two chunks)
 template <int WT, int NB, int EPI, int XSRC, bool SPLIT>
 static hipError_t by_nch(const GemmPlan& pl, const GemmParams& p, hipStream_t s) {
-  if constexpr (XSRC == XSRC_NORM2) {  // one chunk per wave (raw rows staged), one row tile
+  if constexpr (xsrc_gain2(XSRC)) {  // one chunk per wave (raw rows staged)
     if (pl.nch != 1) return hipErrorInvalidValue;
     return pl.tiles_per_wg == 2 ? by_rt<WT, NB, EPI, XSRC, 2, 1, 8, SPLIT>(p, pl.grid, s)
                                 : by_rt<WT, NB, EPI, XSRC, 1, 1, 8, SPLIT>(p, pl.grid, s);
@@ -997,6 +998,7 @@ static hipError_t by_kind(const GemmPlan& pl, int epi, int xsrc, const GemmParam
     if (epi == EPI_STORE && xsrc == XSRC_NORM) return by_nch<WT, 1, EPI_STORE, XSRC_NORM, true>(pl, p, s);
     if (epi == EPI_STORE && xsrc == XSRC_NORM2) return by_nch<WT, 1, EPI_STORE, XSRC_NORM2, true>(pl, p, s);
     if (epi == EPI_STORE && xsrc == XSRC_NORMP) return by_nch<WT, 1, EPI_STORE, XSRC_NORMP, true>(pl, p, s);
+    if (epi == EPI_STORE && xsrc == XSRC_NORM2P) return by_nch<WT, 1, EPI_STORE, XSRC_NORM2P, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_NORMP) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORMP, true>(pl, p, s);
     if (epi == EPI_RESID && xsrc == XSRC_GLOBAL) return by_nch<WT, 1, EPI_RESID, XSRC_GLOBAL, true>(pl, p, s);
     if (epi == EPI_SWIGLU && xsrc == XSRC_NORM) return by_nch<WT, 2, EPI_SWIGLU, XSRC_NORM, true>(pl, p, s);

@@ -39,12 +39,14 @@ constexpr int MAX_WINDOW = 4096;   // attention chunks of one query stay within 
 // XSRC_NORM2: XSRC_NORM whose rows r2 and up take the gains gain2 (one row tile, raw rows
 // staged through LDS). XSRC_NORMP: XSRC_NORM over two row tiles of more rows than one
 // staging of GEMM_NORM_STAGED_ROWS holds (up to 32), staged in two phases of at most 16
-// rows, one per row tile. Plans, LDS layouts and the kernel body otherwise treat both as
-// XSRC_NORM.
-enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2, XSRC_NORM2 = 3, XSRC_NORMP = 4 };
+// rows, one per row tile. XSRC_NORM2P: XSRC_NORM2 over two row tiles (17-32 rows), staged
+// the same way. Plans, LDS layouts and the kernel body otherwise treat them as XSRC_NORM.
+enum { XSRC_GLOBAL = 0, XSRC_LDS = 1, XSRC_NORM = 2, XSRC_NORM2 = 3, XSRC_NORMP = 4, XSRC_NORM2P = 5 };
 __host__ __device__ constexpr int xsrc_base(int xsrc) {
-  return xsrc == XSRC_NORM2 || xsrc == XSRC_NORMP ? XSRC_NORM : xsrc;
+  return xsrc == XSRC_NORM2 || xsrc == XSRC_NORMP || xsrc == XSRC_NORM2P ? XSRC_NORM : xsrc;
 }
+__host__ __device__ constexpr bool xsrc_two_phase(int xsrc) { return xsrc == XSRC_NORMP || xsrc == XSRC_NORM2P; }
+__host__ __device__ constexpr bool xsrc_gain2(int xsrc) { return xsrc == XSRC_NORM2 || xsrc == XSRC_NORM2P; }
 
 // MFMA steps per pipelined chunk (16-byte weight loads per lane per chunk): deeper for one
 // row tile, shallower when 2-3 row tiles of activations also sit in registers.
@@ -152,8 +154,8 @@ __host__ __device__ inline GemmLds gemm_lds_layout(int wt, int xsrc_in, int spli
   } else if (wt != WT_F32 && xsrc == XSRC_NORM && rt <= 2 && nch * ch * kstep == 256) {
     l.stage = 2;  // the raw rows of the wave's whole k range (256 f32) and its gain row(s)
     l.row_bytes = 256 * 4 + 16;
-    const int rows = xsrc_in == XSRC_NORMP ? 16 : R;  // two phases of at most 16 rows
-    l.xs_wave = (size_t)rows * l.row_bytes + (xsrc_in == XSRC_NORM2 ? 2 : 1) * 256 * 2;
+    const int rows = xsrc_two_phase(xsrc_in) ? 16 : R;  // two phases of at most 16 rows
+    l.xs_wave = (size_t)rows * l.row_bytes + (xsrc_gain2(xsrc_in) ? 2 : 1) * 256 * 2;
   }
   if (l.stage == 2) {
     l.xs_off = 0;

@@ -176,9 +176,11 @@ def test_outputs_do_not_depend_on_ring_phase(micro_bf16_w):
 
 # the verified rows' K/V travel with the next draft (its QKV launches project them beside
 # the draft rows, its attention writes them into the ring) while draft rows + committed rows
-# fit one row tile (16); the window is read back only every third trim, so most rounds take
-# that path, and block 13 takes it only when at most two rows were committed
-@pytest.mark.parametrize("block,phase,context", [(1, 0, 21), (4, 5, 50), (8, 16, 40), (13, 3, 64)])
+# fit a launch's two row tiles (32; past 16 staged in two phases); the window is read back
+# only every third trim, so most rounds take that path, and block 24 takes it only when at
+# most seven rows were committed
+@pytest.mark.parametrize("block,phase,context", [(1, 0, 21), (4, 5, 50), (8, 16, 40), (13, 3, 64), (16, 7, 30),
+                                                 (24, 0, 45)])
 def test_micro_bf16_deferred_kv_rounds(micro_bf16_w, block, phase, context):
     ls = P.LockStep(MICRO_BF16, micro_bf16_w, max_block=block, phase=phase, window_period=3)
     P.run_random_depth_rounds(ls, context, block, 14, tag=200 + block)
@@ -190,10 +192,11 @@ def test_micro_bf16_deferred_kv_rounds(micro_bf16_w, block, phase, context):
 def test_deferred_kv_call_sequences(micro_bf16_w):
     """Sequences the round loop never makes, in lock-step with the oracle: a read-back
     between an append and its trim, two pending appends before one trim, a committing
-    append over deferred rows, and a draft whose rows and the committed ones do not fit one
-    row tile (the rows are projected on their own first)."""
+    append over deferred rows, a draft whose rows and the committed ones take two row tiles
+    (folded, staged in two phases) and one where they pass a launch's 32 rows (the rows are
+    projected on their own first)."""
     sh = MICRO_BF16
-    ls = P.LockStep(sh, micro_bf16_w, max_block=14, phase=16, check_windows=False)
+    ls = P.LockStep(sh, micro_bf16_w, max_block=30, phase=16, check_windows=False)
     ls.append(synth.resid_rows(sh, 27, 0), commit=True)
     anchor = synth.anchor_token(sh, tag=9)
     ls.draft(anchor, 4)
@@ -207,20 +210,23 @@ def test_deferred_kv_call_sequences(micro_bf16_w):
     ls.draft((anchor + 2) % sh.vocab, 8)
     ls.append(synth.resid_rows(sh, 9, 4))  # deferred
     ls.trim(1)  # 8 committed rows
-    ls.draft((anchor + 3) % sh.vocab, 13)  # 14 + 8 rows > one tile: projected first
+    ls.draft((anchor + 3) % sh.vocab, 13)  # 14 + 8 rows: two row tiles, folded in two phases
     ls.append(synth.resid_rows(sh, 3, 5))  # deferred
     ls.trim(0)
     ls.append(synth.resid_rows(sh, 6, 6), commit=True)  # projects them, then these six
     ls.draft((anchor + 4) % sh.vocab, 1)
-    ls.append(synth.resid_rows(sh, 2, 7))  # deferred
+    ls.append(synth.resid_rows(sh, 9, 7))  # deferred
+    ls.trim(1)  # 8 committed rows
+    ls.draft((anchor + 5) % sh.vocab, 27)  # 28 + 8 rows > 32: projected first
+    ls.append(synth.resid_rows(sh, 2, 8))  # deferred
     ls.trim(1)
-    ls.draft((anchor + 5) % sh.vocab, 6)  # folds the one committed row
+    ls.draft((anchor + 6) % sh.vocab, 6)  # folds the one committed row
     torch.cuda.synchronize()
     ls.check_window()
     print("deferred sequences stats", ls.stats)
 
 
-@pytest.mark.parametrize("block", [4, 8])
+@pytest.mark.parametrize("block", [4, 8, 16])
 def test_deferred_kv_matches_immediate_projection(micro_bf16_w, block):
     """The same rounds with the window read after every trim (the verified rows' K/V
     projected on their own, by the append path's kernels) and never (projected inside the
