@@ -133,14 +133,13 @@ __device__ __forceinline__ void form_key16(const float (&k1)[HD / 32], const flo
 // (layer, kv head) item 16 y .. 16 y + 15 of the row, in the lane layout of form_key16. The
 // items' loads are issued first; the row's rotary pairs are computed meanwhile into LDS (as
 // the embedding kernel's table computes them).
+// One row r of kv at position pos (this work-group's 16 (layer, kv head) items) into `ring`;
+// rot: the work-group's LDS for the row's rotation table.
 template <int HD>
-__global__ __launch_bounds__(256) void ring_write16_kernel(AttnShape a, const float* __restrict__ kv,
-                                                           const void* const* knorms, int64_t pos0,
-                                                           uint16_t* ring) {
+__device__ __forceinline__ void ring_write16_row(const AttnShape& a, const float* __restrict__ kv,
+                                                 const void* const* knorms, int r, int64_t pos, uint16_t* ring,
+                                                 float2* rot) {
   constexpr int HALF = HD / 2, EPT = HD / 32;
-  __shared__ float2 rot[HALF];
-  const int r = blockIdx.x;
-  const int64_t pos = pos0 + r;
   const int t16 = threadIdx.x & 15;
   const int per_row = a.L * a.nkv;
   const int item = blockIdx.y * 16 + (threadIdx.x >> 4);
@@ -189,6 +188,30 @@ __global__ __launch_bounds__(256) void ring_write16_kernel(AttnShape a, const fl
     VT[(size_t)(EPT * t16 + j) * a.cap] = f2bf(v1[j]);
     VT[(size_t)(HALF + EPT * t16 + j) * a.cap] = f2bf(v2[j]);
   }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void ring_write16_kernel(AttnShape a, const float* __restrict__ kv,
+                                                           const void* const* knorms, int64_t pos0,
+                                                           uint16_t* ring) {
+  __shared__ float2 rot[HD / 2];
+  ring_write16_row<HD>(a, kv, knorms, (int)blockIdx.x, pos0 + blockIdx.x, ring, rot);
+}
+
+// The rows of several sequences in one launch: row r belongs to the sequence whose rows
+// first[q]..first[q+1]-1 hold it (one search per work-group over the by-value table), at
+// position start[q] + r - first[q], into that sequence's ring.
+template <int HD>
+__global__ __launch_bounds__(256) void ring_write16_batch_kernel(AttnShape a, RingSeqs seqs,
+                                                                 const float* __restrict__ kv,
+                                                                 const void* const* knorms, uint16_t* ring0,
+                                                                 size_t ring_stride) {
+  __shared__ float2 rot[HD / 2];
+  const int r = blockIdx.x;
+  int q = 0;
+  while (q + 1 < seqs.n && r >= seqs.first[q + 1]) ++q;
+  uint16_t* ring = (uint16_t*)((unsigned char*)ring0 + (size_t)q * ring_stride);
+  ring_write16_row<HD>(a, kv, knorms, r, seqs.start[q] + (r - seqs.first[q]), ring, rot);
 }
 
 // ---- context K/V into the ring, other shapes --------------------------------------------
@@ -854,6 +877,19 @@ static hipError_t launch_attn_prep(int bf, const AttnShape& a, const float* qkv,
 }
 
 static bool use_mfma(int bf, const AttnShape& a) { return bf && (a.hd == 64 || a.hd == 128); }
+
+hipError_t launch_ring_write_batch(int bf, const AttnShape& a, const float* kv, const void* const* knorms,
+                                   const RingSeqs& seqs, void* ring0, size_t ring_stride, hipStream_t s) {
+  if (!use_mfma(bf, a)) return hipErrorNotSupported;
+  if (seqs.n < 1 || seqs.n > ATTN_MAX_SEQS || seqs.first[0] != 0 || seqs.first[seqs.n] < 1)
+    return hipErrorInvalidValue;
+  for (int q = 0; q < seqs.n; ++q)
+    if (seqs.first[q + 1] < seqs.first[q]) return hipErrorInvalidValue;
+  auto* fn = a.hd == 128 ? ring_write16_batch_kernel<128> : ring_write16_batch_kernel<64>;
+  hipLaunchKernelGGL(fn, dim3(seqs.first[seqs.n], (a.L * a.nkv + 15) / 16), dim3(256), 0, s, a, seqs, kv, knorms,
+                     (uint16_t*)ring0, ring_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_ring_write(int bf, const AttnShape& a, const float* kv, const void* const* knorms, int n,
                              int64_t pos0, void* ring, hipStream_t s) {

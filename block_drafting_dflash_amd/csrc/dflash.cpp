@@ -1557,8 +1557,9 @@ dflash_status dflash_batch_append(dflash_batch* b, const void* resid, const int3
     }
     return DFLASH_OK;
   }
-  // pending rows of every sequence (a round's verify rows): the encoder and the K/V
-  // projections run over all sequences' rows at once, the ring writes per sequence
+  // pending rows of every sequence (a round's verify rows): the encoder, the K/V
+  // projections and the ring writes run over all sequences' rows at once (the ring writes
+  // per sequence where the attention does not form keys itself)
   std::vector<int64_t> start(b->n_seq), first(b->n_seq + 1, 0);
   for (int s = 0; s < b->n_seq; ++s) {
     start[s] = b->e[s] + b->pending[s];
@@ -1571,9 +1572,23 @@ dflash_status dflash_batch_append(dflash_batch* b, const void* resid, const int3
                nullptr, fc_out, c.hidden, nullptr};
     dflash_status s = run_gemm(ctx, f, rc, st);
     if (s == DFLASH_OK) s = kv_gemms(ctx, rc, st);
-    for (int q = 0; q < b->n_seq && s == DFLASH_OK; ++q) {
-      const int64_t lo = std::max<int64_t>(first[q], r0), hi = std::min<int64_t>(first[q + 1], r0 + rc);
-      if (lo < hi) s = ring_write_rows(ctx, (int)(lo - r0), (int)(hi - lo), start[q] + (lo - first[q]), seq_ring(b, q), st);
+    if (s == DFLASH_OK && attention_forms_committed_rows(g.bf, g.a)) {
+      // rows r0..r0+rc-1 of the call: sequence q's share is [max(first[q], r0), first[q+1])
+      RingSeqs rs{};
+      rs.n = b->n_seq;
+      for (int q = 0; q <= b->n_seq; ++q) rs.first[q] = (int)std::clamp<int64_t>(first[q] - r0, 0, rc);
+      for (int q = 0; q < b->n_seq; ++q) rs.start[q] = start[q] + std::max<int64_t>(r0 - first[q], 0);
+      s = dev(ctx,
+              launch_ring_write_batch(g.bf, g.a, (const float*)(ctx->ws + ctx->lay.app_kv),
+                                      (const void* const*)(ctx->ws + ctx->lay.knorm_ptrs), rs, seq_ring(b, 0),
+                                      b->ring_seq, st),
+              "ring write");
+    } else {
+      for (int q = 0; q < b->n_seq && s == DFLASH_OK; ++q) {
+        const int64_t lo = std::max<int64_t>(first[q], r0), hi = std::min<int64_t>(first[q + 1], r0 + rc);
+        if (lo < hi)
+          s = ring_write_rows(ctx, (int)(lo - r0), (int)(hi - lo), start[q] + (lo - first[q]), seq_ring(b, q), st);
+      }
     }
     if (s != DFLASH_OK) return s;
   }

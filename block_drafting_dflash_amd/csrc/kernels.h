@@ -235,6 +235,18 @@ struct AttnSeqs {
   int32_t n;
   int64_t e[ATTN_MAX_SEQS];
 };
+// Rows of one ring write over several sequences: rows first[q]..first[q+1]-1 of kv belong
+// to sequence q, at positions start[q].., into the ring at ring0 + q * ring_stride bytes
+// (first[0] = 0, non-decreasing; empty ranges allowed).
+struct RingSeqs {
+  int32_t n;
+  int32_t first[ATTN_MAX_SEQS + 1];
+  int64_t start[ATTN_MAX_SEQS];
+};
+// launch_ring_write over several sequences in one launch: the bf16 MFMA shapes (otherwise
+// hipErrorNotSupported, and callers write sequence by sequence).
+hipError_t launch_ring_write_batch(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
+                                   const RingSeqs& seqs, void* ring0, size_t ring_stride, hipStream_t s);
 // Anchors and first positions of a batch round's sequences, passed by value.
 struct EmbedSeqs {
   int32_t n;
