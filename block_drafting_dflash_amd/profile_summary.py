@@ -55,7 +55,7 @@ def gemm_role(name: str, wgs: int = 0) -> Optional[str]:
         return "gate/up"
     if epi == 1:
         return "down" if k_per_wave * 8 == I else "O"
-    if epi == 0 and xsrc in (2, 3, 4):  # normed rows: one staging, a second gain row, two phases
+    if epi == 0 and xsrc in (2, 3, 4, 5):  # normed rows: one staging, a second gain row, two phases
         return "QKV or K/V projection"
     if epi == 0 and xsrc == 0 and k_per_wave * 8 == F:
         return "fc"
