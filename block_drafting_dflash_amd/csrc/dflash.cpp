@@ -270,8 +270,8 @@ Layout make_layout(const Cfg& g) {
     o = align256(o + bytes);
     return at;
   };
-  // per-work-group argmax keys of one lm_head launch: <= 32 rows x <= V/16 work-groups
-  L.argmax_part = take(sizeof(unsigned long long) * 32 * (size_t)(c.vocab / 16));
+  // per-work-group argmax keys of one lm_head launch: <= 48 rows x <= V/16 work-groups
+  L.argmax_part = take(sizeof(unsigned long long) * GEMM_MAX_ROWS * (size_t)(c.vocab / 16));
   L.knorm_ptrs = take(sizeof(void*) * c.layers);
   // operand buffers (q, attention output, SwiGLU output, normed rows) hold 4 bytes per
   // element: f32, or for bf16 shapes a hi plane followed by a lo plane (see lo_plane)
@@ -420,7 +420,12 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
     // staged through LDS there, while a three-tile launch loads 48-row fragments per wave
     // (measured slower than two staged launches over the same rows)
     int rc = std::min(rows - r0, g.bf ? 32 : GEMM_MAX_ROWS);
-    if (gc.epi == EPI_ARGMAX) rc = std::min(rc, std::min(32, 16 * waves));  // one finishing wave per row tile
+    if (gc.epi == EPI_ARGMAX) {
+      // one finishing wave per row tile; single-plane rows over bf16 or 4-bit weights (the
+      // verify rows) take three row tiles, so 48 verify rows stream the head once
+      const int cap = g.bf && !gc.split ? GEMM_MAX_ROWS : 32;
+      rc = std::min(rows - r0, std::min(cap, 16 * waves));
+    }
     // tiles per work-group that size the reduction buffers: two or more for the argmax, two
     // for normed hi/lo operands over an even tile count (the launch below)
     const bool norm_two = gc.xsrc == XSRC_NORM && gc.split && (N / 16) % 2 == 0 && (rc <= 16 || nb == 1);
@@ -573,12 +578,17 @@ dflash_status flush_kv(dflash_ctx* ctx, hipStream_t st) {
 }
 
 // Bound on the per-work-group key bytes of one vocabulary argmax launch over rows given in
-// the activation dtype (at most 32 rows per launch; fewer tiles per work-group, so more
-// work-groups, at fewer rows).
+// the activation dtype (at most 48 rows per launch over bf16 or 4-bit weights, 32 over f32;
+// fewer tiles per work-group, so more work-groups, at fewer rows).
 size_t argmax_key_bytes(const Cfg& g, int n) {
   const int ntiles = g.c.vocab / 16;
-  const int tpw = argmax_tiles_per_wg(g.wt, 0, ntiles, 1);
-  return (size_t)std::min(n, 32) * (size_t)((ntiles + tpw - 1) / tpw) * sizeof(unsigned long long);
+  size_t most = 0;
+  // the largest launch of n rows, and the largest of 16 rows or fewer (more work-groups)
+  for (const int rc : {std::min(n, g.bf ? GEMM_MAX_ROWS : 32), std::min(n, 16)}) {
+    const int tpw = argmax_tiles_per_wg(g.wt, 0, ntiles, rc);
+    most = std::max(most, (size_t)rc * (size_t)((ntiles + tpw - 1) / tpw) * sizeof(unsigned long long));
+  }
+  return most;
 }
 
 }  // namespace

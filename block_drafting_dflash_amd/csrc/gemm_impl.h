@@ -909,7 +909,9 @@ static hipError_t by_rt(const GemmParams& p, int grid, hipStream_t s) {
       return hipErrorInvalidValue;
     } else {
       if (rt == 2) return launch_t<WT, 2, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
-      if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;  // argmax launches take <= 32 rows
+      // the vocabulary argmax over hi/lo pairs takes at most 32 rows; over single-plane rows
+      // (bf16 and 4-bit weights, T as argmax_tiles_per_wg picks them) 48
+      if constexpr (EPI == EPI_ARGMAX && (SPLIT || WT == WT_F32 || T > 8)) return hipErrorInvalidValue;
       else return launch_t<WT, 3, NB, EPI, XSRC, T, 2 * NCH, 4, SPLIT>(p, grid, s);
     }
   }

@@ -8,9 +8,10 @@
 
 namespace dflash {
 
-// Bytes of the fixed argmax key array per device: 8-byte keys of 32 rows from up to 16384
-// work-groups, which covers every vocabulary up to 524288 rows (two or more 16-column tiles
-// per work-group there).
+// Bytes of the fixed argmax key array per device: 8-byte keys of a launch's rows from its
+// work-groups: up to 16 rows from 16384 work-groups, 32 or 48 rows from 8192 (rows past 16
+// take four 16-column tiles per work-group), which covers every vocabulary up to 524288 rows
+// (the bound is computed per call and checked against this size).
 constexpr size_t NOALLOC_KEY_BYTES = (size_t)4 << 20;
 
 // Device address of `device`'s copy of the array (looked up once per device; that device
