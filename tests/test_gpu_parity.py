@@ -68,15 +68,31 @@ def test_micro_bf16_random_depth(micro_bf16_w, block, phase, context):
     print("micro-bf16 stats", block, ls.stats)
 
 
+def check_argmax_against_oracle(sh, w, got, rows):
+    """Verify-row argmaxes against the oracle's, exact above the near-tie margin."""
+    from oracle import dflash_oracle as O
+
+    oi, om = O.OracleDrafter(sh, w, 4).lm_head_argmax(rows)
+    got = got.numpy()
+    for i in range(len(rows)):
+        assert om[i] <= P.MARGIN or got[i] == oi[i], (i, got[i], oi[i], om[i])
+
+
 def test_lm_head_argmax_is_width_invariant(micro_bf16_w):
+    """The verify-row argmax over 40, 48 and 49 rows (one, two and three 16-row tiles per
+    launch, and a second launch past 48 rows) against the oracle, and bit-identical to the
+    same rows taken in narrower calls."""
     sh = MICRO_BF16
     dev = binding.to_device(sh, micro_bf16_w)
     g = binding.Drafter(sh, dev, max_block=4)
-    rows = torch.from_numpy(synth.verify_hidden(sh, 40, 0)).to(torch.bfloat16).cuda()
-    full = g.lm_head_argmax(rows).cpu()
-    for w in (1, 4, 5, 16, 17, 33):
-        part = torch.cat([g.lm_head_argmax(rows[i:i + w].contiguous()).cpu() for i in range(0, 40, w)])
-        assert torch.equal(part, full), w
+    for n in (40, 48, 49):
+        rows_np = synth.verify_hidden(sh, n, n)
+        rows = torch.from_numpy(rows_np).to(torch.bfloat16).cuda()
+        full = g.lm_head_argmax(rows).cpu()
+        check_argmax_against_oracle(sh, micro_bf16_w, full, rows_np)
+        for wd in (1, 4, 5, 16, 17, 33):
+            part = torch.cat([g.lm_head_argmax(rows[i:i + wd].contiguous()).cpu() for i in range(0, n, wd)])
+            assert torch.equal(part, full), (n, wd)
 
 
 def test_draft_is_bit_reproducible(micro_bf16_w):
@@ -285,11 +301,14 @@ def test_micro_q4_deferred_kv_rounds(micro_q4_w, block, phase, context):
 def test_q4_lm_head_argmax_is_width_invariant(micro_q4_w):
     sh = MICRO_Q4
     g = binding.Drafter(sh, binding.to_device(sh, micro_q4_w), max_block=4)
-    rows = torch.from_numpy(synth.verify_hidden(sh, 40, 0)).to(torch.bfloat16).cuda()
-    full = g.lm_head_argmax(rows).cpu()
-    for w in (1, 5, 16, 17):
-        part = torch.cat([g.lm_head_argmax(rows[i:i + w].contiguous()).cpu() for i in range(0, 40, w)])
-        assert torch.equal(part, full), w
+    for n in (40, 49):
+        rows_np = synth.verify_hidden(sh, n, n)
+        rows = torch.from_numpy(rows_np).to(torch.bfloat16).cuda()
+        full = g.lm_head_argmax(rows).cpu()
+        check_argmax_against_oracle(sh, micro_q4_w, full, rows_np)
+        for wd in (1, 5, 16, 17):
+            part = torch.cat([g.lm_head_argmax(rows[i:i + wd].contiguous()).cpu() for i in range(0, n, wd)])
+            assert torch.equal(part, full), (n, wd)
 
 
 def test_argmax_timing_hook(micro_bf16_w):
@@ -330,12 +349,14 @@ def test_lm_head_exact_tie_goes_to_the_lowest_index(micro_bf16_w):
     lm = lm0.copy()
     lm[s] = lm[t]
     w = dict(micro_bf16_w, lm_head=lm)
-    rows = synth.verify_hidden(sh, 6, 11)
+    rows = synth.verify_hidden(sh, 45, 11)
     rows[0] = synth.to_bf16_values(lm[t] / np.float32(0.02))
+    rows[41] = rows[0]  # the same tie in the third row tile of the launch
     g = binding.Drafter(sh, binding.to_device(sh, w), max_block=4)
     got = g.lm_head_argmax(torch.from_numpy(rows).to(torch.bfloat16).cuda()).cpu().numpy()
     oi, om = O.OracleDrafter(sh, w, 4).lm_head_argmax(rows)
-    assert om[0] == 0.0 and oi[0] == t and got[0] == t
+    for i in (0, 41):
+        assert om[i] == 0.0 and oi[i] == t and got[i] == t, i
     for i in range(1, len(rows)):
         assert om[i] <= P.MARGIN or got[i] == oi[i]
     # drafted rows: copy the winner v of a clearly decided drafted row into a lower, unused row
