@@ -282,7 +282,7 @@ Layout make_layout(const Cfg& g) {
   L.qb = take(4 * R * qd);
   L.attn = take(4 * R * qd);
   L.mlp = take(4 * R * c.intermediate);
-  L.zrows = take(4 * R * H);  // final-normed drafted rows (lm_head operand)
+  L.zrows = take(4 * R * H);  // drafted rows through the final norm (or its gain alone): lm_head operand
   L.part = take(4 * attention_partial_floats(g.a, (int)R));
   L.rope = take(sizeof(float2) * RQ * (c.head_dim / 2));  // rotary table of a draft's positions
   L.app_fc = take(4 * (size_t)GEMM_MAX_ROWS * H);
@@ -381,6 +381,12 @@ struct GemmCall {
   // residual only: also store the finished rows here ([rows, ldy2], act dtype)
   void* y2 = nullptr;
   int64_t ldy2 = 0;
+  // residual only: the finished rows times zgain as operand rows (GemmParams::z)
+  const void* zgain = nullptr;
+  void* z = nullptr;
+  void* zlo = nullptr;
+  int64_t ldz = 0;
+  int zper = 0;
 };
 
 dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStream_t st) {
@@ -484,6 +490,12 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
       p.y2 = gc.y2 ? (unsigned char*)gc.y2 + (size_t)r0 * gc.ldy2 * g.act_elt : nullptr;
       p.ldy2 = gc.ldy2;
       p.y2_bf16 = g.bf ? 1 : 0;
+      p.zgain = gc.zgain;
+      p.z = gc.z;
+      p.zlo = gc.zlo;
+      p.ldz = gc.ldz;
+      p.zper = gc.zper;
+      p.zrow0 = r0;
     }
     const bool timed = gc.epi == EPI_ARGMAX && ctx->tev_active && r0 == 0;
     if (timed && hipEventRecord(ctx->tev_start, st) != hipSuccess) return dev(ctx, hipGetLastError(), "timing event");
@@ -506,6 +518,19 @@ dflash_status run_gemm(dflash_ctx* ctx, const GemmCall& gc_in, int rows, hipStre
 }
 
 GemmSeg seg(const Lin& l, int col0, int rows) { return GemmSeg{l.w, l.s, l.b, col0, rows}; }
+
+// A DFlash draft ranks rows 1..B of each run of B + 1 (per = B + 1), a target forward every
+// row (per = 0), through the final RMSNorm and the lm_head. The norm's per-row factor 1/rms
+// is positive, so it leaves each row's argmax as it is: the last down launch stores its
+// finished rows times the norm's gain alone as the lm_head's operand rows, in place of a
+// separate norm pass over them.
+void gain_rows_for_argmax(const dflash_ctx* ctx, GemmCall& dn, void* z, void* zlo, int per) {
+  dn.zgain = ctx->final_norm;
+  dn.z = z;
+  dn.zlo = zlo;
+  dn.ldz = ctx->cfg.c.hidden;
+  dn.zper = per;
+}
 
 // Rows of a QKV launch that may carry committed rows beside the draft rows (0: none): bf16
 // activations on the MFMA attention (which forms and writes those rows), and a normed
@@ -914,6 +939,9 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
   float* part = (float*)(ctx->ws + ctx->lay.part);
   const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * c.head_dim;
 
+  // the proposing rows' operands of the lm_head (DFlash: rows 1..B; DSpark: all gamma rows)
+  void* zrows = ctx->ws + ctx->lay.zrows;
+  void* zrows_lo = lo_plane(g, zrows, block, H);
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   dflash_status s = dev(ctx,
                         launch_embed(g.bf, ctx->embed, H, c.vocab, anchor, c.mask_token_id, nullptr, R, nf,
@@ -949,6 +977,7 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
                 nullptr};
     dn.split = g.bf;
     dn.xlo = mlp_lo;
+    if (!g.dspark && l == c.layers - 1) gain_rows_for_argmax(ctx, dn, zrows, zrows_lo, R);
     if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
   }
   ctx->kv_rows = 0;  // every layer's ring now holds them
@@ -956,24 +985,20 @@ dflash_status dflash_draft_block(dflash_ctx* ctx, int32_t anchor, int32_t block,
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * R * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
   }
-  // final RMSNorm of the proposing rows once (DFlash: rows 1..B; DSpark: all gamma rows),
-  // then the lm_head over the operand rows
-  void* zrows = ctx->ws + ctx->lay.zrows;
-  void* zrows_lo = lo_plane(g, zrows, block, H);
-  s = dev(ctx, launch_rownorm(g.bf, g.dspark ? x : x + H, ctx->final_norm, c.rms_eps, block, H, zrows, zrows_lo, st),
-          "final norm");
-  if (s != DFLASH_OK) return s;
-  if (!g.dspark) {
+  if (!g.dspark) {  // the last down launch left rows 1..B times the final norm's gain
     GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
     lm.split = g.bf;
     lm.xlo = zrows_lo;
     return run_gemm(ctx, lm, block, st);
   }
-  // DSpark: every row's f32 logits, then the Markov chain: one launch per step, each taking
+  // DSpark: the final RMSNorm of all gamma rows (their logits are scored, not only ranked),
+  // every row's f32 logits, then the Markov chain: one launch per step, each taking
   // its token from the keys the previous step left (the anchor first) and storing it as the
   // previous step's output, then the reduction of the last step's keys
   // (the vocabulary argmax GEMM with its logit store: the store GEMM's folded 8-column
   // tiles measured 192 / 317 us against 122 us at 7 / 9 rows)
+  s = dev(ctx, launch_rownorm(g.bf, x, ctx->final_norm, c.rms_eps, block, H, zrows, zrows_lo, st), "final norm");
+  if (s != DFLASH_OK) return s;
   float* logits = (float*)(ctx->ws + ctx->lay.logits);
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, logits, c.vocab, nullptr};
   lm.split = g.bf;
@@ -1336,6 +1361,8 @@ dflash_status dflash_target_forward(dflash_target* t, int32_t anchor, const int3
   float* part = (float*)(ctx->ws + ctx->lay.part);
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   const int64_t ldcap = (int64_t)tc.n_capture * H;
+  void* zrows = ctx->ws + ctx->lay.zrows;  // the lm_head's operand rows
+  void* zrows_lo = lo_plane(g, zrows, R, H);
   dflash_status s = dev(ctx,
                         launch_embed(g.bf, ctx->embed, H, c.vocab, anchor, 0, d_tokens, R, 0, nullptr, x, rope, ctx->e,
                                      c.rope_theta, c.head_dim, st),
@@ -1369,13 +1396,10 @@ dflash_status dflash_target_forward(dflash_target* t, int32_t anchor, const int3
       dn.y2 = (unsigned char*)d_capture + (size_t)t->capture_slot[l] * H * g.act_elt;
       dn.ldy2 = ldcap;
     }
+    if (l == c.layers - 1) gain_rows_for_argmax(ctx, dn, zrows, zrows_lo, 0);
     if ((s = run_gemm(ctx, dn, R, st)) != DFLASH_OK) return s;
   }
-  // final RMSNorm of every row, then the lm_head argmax
-  void* zrows = ctx->ws + ctx->lay.zrows;
-  void* zrows_lo = lo_plane(g, zrows, R, H);
-  s = dev(ctx, launch_rownorm(g.bf, x, ctx->final_norm, c.rms_eps, R, H, zrows, zrows_lo, st), "final norm");
-  if (s != DFLASH_OK) return s;
+  // the last down launch left every row times the final norm's gain: the lm_head argmax
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_argmax};
   lm.split = g.bf;
   lm.xlo = zrows_lo;
@@ -1650,6 +1674,8 @@ dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_
   float* part = (float*)(ctx->ws + ctx->lay.part);
   float2* rope = (float2*)(ctx->ws + ctx->lay.rope);
   const size_t ring_layer = (size_t)g.act_elt * 2 * c.kv_heads * (size_t)g.Cs * hd;
+  void* zrows = ctx->ws + ctx->lay.zrows;  // each sequence's rows 1..B, consecutive
+  void* zrows_lo = lo_plane(g, zrows, S * block, H);
   EmbedSeqs es{};
   AttnSeqs as{};
   es.n = as.n = S;
@@ -1685,6 +1711,7 @@ dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_
                 nullptr};
     dn.split = g.bf;
     dn.xlo = mlp_lo;
+    if (l == c.layers - 1) gain_rows_for_argmax(ctx, dn, zrows, zrows_lo, R1);
     if ((s = run_gemm(ctx, dn, rows, st)) != DFLASH_OK) return s;
   }
   if (s != DFLASH_OK) return s;
@@ -1692,13 +1719,8 @@ dflash_status dflash_batch_draft(dflash_batch* b, const int32_t* anchors, int32_
     s = dev(ctx, hipMemcpyAsync(d_hidden, x, sizeof(float) * rows * H, hipMemcpyDeviceToDevice, st), "hidden copy");
     if (s != DFLASH_OK) return s;
   }
-  // final RMSNorm of each sequence's rows 1..B into consecutive operand rows, then one
-  // lm_head argmax over all of them: d_tokens [n_seq][block]
-  void* zrows = ctx->ws + ctx->lay.zrows;
-  void* zrows_lo = lo_plane(g, zrows, S * block, H);
-  s = dev(ctx, launch_rownorm(g.bf, x, ctx->final_norm, c.rms_eps, S * block, H, zrows, zrows_lo, st, block),
-          "final norm");
-  if (s != DFLASH_OK) return s;
+  // the last down launch left each sequence's rows 1..B times the final norm's gain in
+  // consecutive operand rows; one lm_head argmax over all of them: d_tokens [n_seq][block]
   GemmCall lm{EPI_ARGMAX, XSRC_LDS, {seg(ctx->lm_head, 0, c.vocab)}, H, zrows, H, nullptr, nullptr, 0, d_tokens};
   lm.split = g.bf;
   lm.xlo = zrows_lo;

@@ -29,6 +29,8 @@ hipError_t launch_gemm(int wt, int epi, int xsrc, const GemmPlan& pl, const Gemm
     return hipErrorInvalidValue;
   if (p.nseg < 1 || p.nseg > GEMM_MAXSEG || (epi == EPI_ARGMAX && (p.nseg != 1 || p.seg[0].col0 != 0)))
     return hipErrorInvalidValue;  // the argmax kernel reads one matrix
+  if (p.z && (epi != EPI_RESID || p.zper < 0 || p.zper == 1 || p.zrow0 < 0 || !p.zgain || (p.split && !p.zlo)))
+    return hipErrorInvalidValue;  // gained rows come from a residual launch: all, or runs of 2 or more
   if (wt == WT_F32) return launch_gemm_f32(pl, epi, xsrc, p, s);
   if (wt == WT_BF16) return launch_gemm_bf16(pl, epi, xsrc, p, s);
   if (wt == WT_Q4) return launch_gemm_q4(pl, epi, xsrc, p, s);

@@ -500,15 +500,20 @@ gemm_kernel(const GemmParams p) {
   // that the epilogue only stores; every output is read and written by one lane
   static_assert(EPI != EPI_RESID || T == 1, "residual launches own one tile per work-group");
   float yres[4] = {0.f, 0.f, 0.f, 0.f};
+  float zg = 0.f;  // the gain of this lane's output column for the z rows
   auto load_resid = [&]() {
     if constexpr (EPI == EPI_RESID) {
+      const int col = FOLD ? 8 * tile_of(0) + (li & 7) : 16 * tile_of(0) + li;
       if (w < RT) {
-        const int col = FOLD ? 8 * tile_of(0) + (li & 7) : 16 * tile_of(0) + li;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = min(w * RROWS + 4 * lg + q, R - 1);
           yres[q] = ((const float*)p.y)[(size_t)r * p.ldy + col];
         }
+      }
+      if (p.z) {
+        if constexpr (BF) zg = bf2f(((const uint16_t*)p.zgain)[col]);
+        else zg = ((const float*)p.zgain)[col];
       }
     }
   };
@@ -577,6 +582,12 @@ gemm_kernel(const GemmParams p) {
               const size_t o2 = (size_t)r * p.ldy2 + col;
               if (p.y2_bf16) ((uint16_t*)p.y2)[o2] = f2bf(nv);
               else ((float*)p.y2)[o2] = nv;
+            }
+            if (p.z) {  // gained rows for the vocabulary argmax (every row, or runs of zper
+                        // with the first row of each left out)
+              const int ar = p.zrow0 + r, run = p.zper ? ar / p.zper : 0, i = ar - run * p.zper;
+              if (!p.zper || i > 0)
+                op_st<SPLIT>(p.z, p.zlo, (int64_t)(p.zper ? run * (p.zper - 1) + i - 1 : ar) * p.ldz + col, nv * zg);
             }
           } else if constexpr (EPI == EPI_SWIGLU) {
             const float g = v[0][q], u = v[NB - 1][q];

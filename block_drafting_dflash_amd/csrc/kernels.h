@@ -93,6 +93,16 @@ struct GemmParams {
   void* y2;
   int64_t ldy2;
   int32_t y2_bf16;
+  // RESID: when z is set, the finished rows times zgain (act-dtype storage [ldy]) are also
+  // stored as operand rows of the next GEMM (hi/lo planes z/zlo when split, else f32 at z),
+  // [.., ldz]: every row (zper 0), or runs of zper rows with the first of each left out;
+  // launch row r is row zrow0 + r of the whole call
+  const void* zgain;
+  void* z;
+  void* zlo;
+  int64_t ldz;
+  int32_t zper;
+  int32_t zrow0;
   unsigned long long* part;  // ARGMAX: per-work-group best keys, [R][grid]
 };
 
@@ -211,10 +221,9 @@ hipError_t launch_argmax_finalize(const unsigned long long* part, int groups, in
 hipError_t launch_embed(int act_bf16, const void* table, int hidden, int vocab, int32_t anchor, int32_t mask_id,
                         const int32_t* toks, int R, int nprev, const float* prev, float* x, float2* rope, int64_t pos0,
                         float theta, int hd, hipStream_t s);
-// RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out. skip_every =
-// B > 0 reads rows 1..B of each group of B + 1 input rows (a batch's proposing rows).
+// RMSNorm rows of in: act_bf16 -> hi/lo bf16 planes out/out_lo, else f32 out.
 hipError_t launch_rownorm(int act_bf16, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          void* out_lo, hipStream_t s, int skip_every = 0);
+                          void* out_lo, hipStream_t s);
 hipError_t launch_ring_write(int act_bf16, const AttnShape& a, const float* kv, const void* const* knorms,
                              int n, int64_t pos0, void* ring, hipStream_t s);
 // Attention side of one layer of the block forward: q/k RMSNorm + RoPE of the R block rows

@@ -176,14 +176,11 @@ hipError_t launch_embed_batch(int bf, const void* table, int hidden, const Embed
 constexpr int RN_V = 4;
 template <bool BF>
 __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ in, const void* gain, float eps, int H,
-                                                      void* out, void* out_lo, int skip_every) {
+                                                      void* out, void* out_lo) {
   __shared__ float part[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nv = H / 4;  // H is a multiple of 16
-  // skip_every = B > 0: output row r reads input row (r / B) (B + 1) + 1 + r % B (rows 1..B of
-  // each sequence's B + 1)
-  const int ri = skip_every > 0 ? (r / skip_every) * (skip_every + 1) + 1 + r % skip_every : r;
-  const float4* x = (const float4*)(in + (size_t)ri * H);
+  const float4* x = (const float4*)(in + (size_t)r * H);
   float4 xv[RN_V];
   float gv[RN_V][4];
   auto load_gain = [&](int v, float (&g)[4]) {
@@ -240,10 +237,10 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const float* __restrict__ 
 }
 
 hipError_t launch_rownorm(int bf, const float* in, const void* gain, float eps, int R, int H, void* out,
-                          void* out_lo, hipStream_t s, int skip_every) {
-  if (H % 16 || skip_every < 0) return hipErrorInvalidValue;
-  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo, skip_every);
-  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo, skip_every);
+                          void* out_lo, hipStream_t s) {
+  if (H % 16) return hipErrorInvalidValue;
+  if (bf) hipLaunchKernelGGL(rownorm_kernel<true>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
+  else hipLaunchKernelGGL(rownorm_kernel<false>, dim3(R), dim3(256), 0, s, in, gain, eps, H, out, out_lo);
   return hipGetLastError();
 }
 
