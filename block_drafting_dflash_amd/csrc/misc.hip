@@ -285,7 +285,7 @@ __global__ void verify_kernel(const int32_t* __restrict__ draft, const int32_t* 
 
 hipError_t launch_verify(const int32_t* draft, const int32_t* target, int B, int vocab, int32_t* out, hipStream_t s,
                          int n_seq) {
-  if (n_seq < 1) return hipErrorInvalidValue;
+  if (n_seq < 1 || B < 1) return hipErrorInvalidValue;  // a block drafts at least one row
   hipLaunchKernelGGL(verify_kernel, dim3(n_seq), dim3(64), 0, s, draft, target, B, vocab, out);
   return hipGetLastError();
 }

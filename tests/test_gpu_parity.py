@@ -129,6 +129,32 @@ def test_verify_result_into_pinned_host_memory(micro_f32_w):
         g.verify_greedy(d, t, B, out=torch.empty(3, dtype=torch.int32))  # not pinned
 
 
+def test_verify_kernel_matches_oracle_across_widths(micro_f32_w):
+    """Greedy verify through the C-ABI against the oracle's rule at widths on both sides of
+    one wave's 64 rows (one ballot below 64 draft rows, several 64-row passes from 64 on):
+    every accepted length 0..B at the small widths, sampled ones past them, and an
+    out-of-range target id at the first, a middle and the bonus row, which refuses the
+    whole block."""
+    from oracle import dflash_oracle as O
+
+    sh = MICRO_F32
+    g = binding.Drafter(sh, binding.to_device(sh, micro_f32_w), max_block=200)
+    rng = np.random.default_rng(77)
+    for B in (1, 2, 5, 31, 63, 64, 65, 127, 128, 200):
+        ks = range(B + 1) if B <= 8 else sorted({0, 1, B // 2, B - 1, B, int(rng.integers(0, B + 1))})
+        for k in ks:
+            d = rng.integers(0, sh.vocab, B).astype(np.int32)
+            a = P.target_with_accept_length(d, k, sh.vocab, tail=int(rng.integers(0, sh.vocab))).astype(np.int32)
+            got = g.verify_greedy(torch.from_numpy(d).cuda(), torch.from_numpy(a).cuda(), B).cpu().tolist()
+            want = list(O.verify_greedy(d, a))
+            assert got == want + [0], (B, k, got, want)
+        for pos, bad in ((0, sh.vocab), (B // 2, -1), (B, sh.vocab + 3)):
+            a = rng.integers(0, sh.vocab, B + 1).astype(np.int32)
+            a[pos] = bad
+            got = g.verify_greedy(torch.from_numpy(d).cuda(), torch.from_numpy(a).cuda(), B).cpu().tolist()
+            assert got == [0, -1, 1], (B, pos, got)
+
+
 def test_boundary_errors_leave_state_unchanged(micro_f32_w):
     sh = MICRO_F32
     g = binding.Drafter(sh, binding.to_device(sh, micro_f32_w), max_block=4)
